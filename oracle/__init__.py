@@ -1,0 +1,107 @@
+"""fp64 CPU oracle for the selective scan (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. The product path (the HIP library and its binding) never does.
+
+``scan`` is the sequential definition written out in ``ssm_oracle.c``:
+  a_t[n] = exp(delta_t * A[e, n]);  h_t = a_t * h_{t-1} + (delta_t * x_t) * B_t[n]
+  y_t = sum_n C_t[n] h_t[n] + D[e] x_t
+(plus the reverse-time scan for the bidirectional variant), in fp64.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_SO = os.path.join(_HERE, "libssm_oracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build():
+    """Compile the oracle with gcc (no fast-math: IEEE fp64 throughout)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+           "-ffp-contract=off", _SRC, "-o", _SO + ".tmp", "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(_SO + ".tmp", _SO)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.oracle_scan.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                  i64, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
+        L.oracle_scan.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _threads(nthreads):
+    if nthreads is None:
+        nthreads = min(16, os.cpu_count() or 1)
+    return int(nthreads)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def scan(x, delta, A, B, C, D=None, *, bidir=False, chans=None, want_h_last=False,
+         want_g_first=False, nthreads=None):
+    """Run the oracle.
+
+    x, delta: (Bs, L, ED); B, C: (Bs, L, N) -- float32, or uint16 bf16 bit
+    patterns (all four the same dtype). A: (ED, N) float32; D: (ED,) float32
+    or None. chans: optional int64 array of channel ids b*ED + e.
+
+    Returns (y, h_last, g_first): y is (Bs, L, ED) float64 when chans is None,
+    else (len(chans), L) channel-major; h_last / g_first are (Bs, ED, N) or
+    (len(chans), N), or None when not requested.
+    """
+    x = np.ascontiguousarray(x)
+    delta = np.ascontiguousarray(delta)
+    B = np.ascontiguousarray(B)
+    C = np.ascontiguousarray(C)
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
+    if x.dtype == np.uint16:
+        dtype = BF16
+    elif x.dtype == np.float32:
+        dtype = F32
+    else:
+        raise TypeError("x must be float32 or uint16 (bf16 bits)")
+    for t in (delta, B, C):
+        if t.dtype != x.dtype:
+            raise TypeError("x, delta, B, C must share a dtype")
+    Bs, L, ED = x.shape
+    N = A.shape[1]
+    assert delta.shape == x.shape and B.shape == (Bs, L, N) and C.shape == (Bs, L, N)
+    assert A.shape == (ED, N) and (D is None or D.shape == (ED,))
+    if chans is not None:
+        chans = np.ascontiguousarray(chans, dtype=np.int64)
+        nch = chans.size
+    else:
+        nch = Bs * ED
+    y = np.empty((nch, L), dtype=np.float64)
+    h = np.empty((nch, N), dtype=np.float64) if want_h_last else None
+    g = np.empty((nch, N), dtype=np.float64) if (want_g_first and bidir) else None
+    rc = lib().oracle_scan(dtype, int(bool(bidir)), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                           _ptr(D), Bs, L, ED, N, _ptr(chans), nch, _ptr(y), _ptr(h), _ptr(g),
+                           _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan failed with code %d" % rc)
+    if chans is None:
+        y = y.reshape(Bs, ED, L).transpose(0, 2, 1)
+        if h is not None:
+            h = h.reshape(Bs, ED, N)
+        if g is not None:
+            g = g.reshape(Bs, ED, N)
+    return y, h, g

@@ -1,0 +1,170 @@
+/*
+ * Selective-scan oracle: the plain, slow, fp64 CPU definition.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do. It shares no code, header, table or helper with the HIP
+ * library.
+ *
+ * What it computes (for every batch row b and channel e; n = 0..N-1):
+ *   API and shapes: "scan output is different between sequential and
+ *   parallel versions" (mamba.py issue 26), first reply, the API comment of
+ *   the test script: x, delta (Bs, L, ED); A (ED, N); B, C (Bs, L, N);
+ *   D (ED); y (Bs, L, ED). The sequential form is that page's
+ *   selective_scan_seq.
+ *   Recurrence (zero initial state, raw delta, Euler-style input term):
+ *     a_t[n] = exp(delta[b,t,e] * A[e,n])
+ *     h_t[n] = a_t[n] * h_{t-1}[n] + (delta[b,t,e] * x[b,t,e]) * B[b,t,n],  h_{-1} = 0
+ *     y[b,t,e] = sum_n C[b,t,n] * h_t[n] + D[e] * x[b,t,e]
+ *   Final state h_last[b,e,n] = h_{L-1}[n] (the forward scan's final state,
+ *   as the Bi-Mamba2 forward returns per direction: "Some questions of
+ *   Bi-Mamba2 and Hydra", the MambaChunkScanCombinedFn.forward listing).
+ *   Bidirectional variant (same page, Hprairie's first reply, point 1 and 3:
+ *   two SSMs with shared weights added together, plus D x, read in place):
+ *     g_t[n] = a_t[n] * g_{t+1}[n] + (delta x)[t] * B[b,t,n],  g_L = 0
+ *     y[b,t,e] = sum_n C[b,t,n] * (h_t[n] + g_t[n]) + D[e] * x[b,t,e]
+ *   with the same a_t, inputs read in place (no shift, no flipped copy).
+ *
+ * Every product of two fp32 (or bf16) inputs is exact in fp64; exp is the
+ * host libm's. Threads split only the independent (b, e) channels; the
+ * arithmetic of each channel runs in the order written above.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+static double load(const void* p, int64_t i, int dtype) {
+  if (dtype == ORACLE_BF16) {
+    uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+  }
+  return (double)((const float*)p)[i];
+}
+
+typedef struct {
+  int dtype, bidir;
+  const void *x, *delta, *B, *C;
+  const float *A, *D;
+  int64_t Bs, L, ED, N;
+  const int64_t* chans; /* channel ids c = b*ED + e, or NULL for all */
+  int64_t nchans;
+  double* y;      /* (nchans, L): y of channel k at row k */
+  double* h_last; /* (nchans, N) or NULL */
+  double* g_first;/* (nchans, N) or NULL: reverse state at t = 0 (bidir only) */
+  int64_t k0, k1; /* this worker's range of k */
+} work_t;
+
+/* One channel: the forward recurrence, then (bidir) the reverse one. */
+static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
+  const int64_t c = w->chans ? w->chans[k] : k;
+  const int64_t b = c / w->ED, e = c % w->ED;
+  const int64_t L = w->L, ED = w->ED, N = w->N;
+  double* y = w->y + k * L;
+
+  for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t ix = (b * L + t) * ED + e; /* x, delta index */
+    const int64_t ib = (b * L + t) * N;      /* B, C row index */
+    const double dt = load(w->delta, ix, w->dtype);
+    const double xv = load(w->x, ix, w->dtype);
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = exp(dt * (double)w->A[e * N + n]);
+      h[n] = a * h[n] + (dt * xv) * load(w->B, ib + n, w->dtype);
+      acc += load(w->C, ib + n, w->dtype) * h[n];
+    }
+    y[t] = acc;
+  }
+  if (w->h_last)
+    for (int64_t n = 0; n < N; ++n) w->h_last[k * N + n] = h[n];
+
+  if (w->bidir) {
+    for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+      const int64_t ix = (b * L + t) * ED + e;
+      const int64_t ib = (b * L + t) * N;
+      const double dt = load(w->delta, ix, w->dtype);
+      const double xv = load(w->x, ix, w->dtype);
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double a = exp(dt * (double)w->A[e * N + n]);
+        g[n] = a * g[n] + (dt * xv) * load(w->B, ib + n, w->dtype);
+        acc += load(w->C, ib + n, w->dtype) * g[n];
+      }
+      y[t] += acc;
+    }
+    if (w->g_first)
+      for (int64_t n = 0; n < N; ++n) w->g_first[k * N + n] = g[n];
+  }
+
+  /* the skip term D x, added once */
+  for (int64_t t = 0; t < L; ++t) {
+    const double xv = load(w->x, (b * L + t) * ED + e, w->dtype);
+    const double d = w->D ? (double)w->D[e] : 0.0;
+    y[t] += d * xv;
+  }
+}
+
+static void* worker(void* p) {
+  work_t* w = (work_t*)p;
+  double* h = (double*)malloc(sizeof(double) * (size_t)w->N * 2);
+  if (!h) return (void*)1;
+  for (int64_t k = w->k0; k < w->k1; ++k) scan_channel(w, k, h, h + w->N);
+  free(h);
+  return NULL;
+}
+
+/*
+ * Run the oracle over the listed channels (or all Bs*ED channels when chans
+ * is NULL, in order c = b*ED + e). Outputs are channel-major:
+ * y[k*L + t], h_last[k*N + n], g_first[k*N + n]. Returns 0 on success,
+ * -1 on bad arguments, -2 when memory for a worker could not be allocated.
+ */
+int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const float* A, const void* B,
+                const void* C, const float* D, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                const int64_t* chans, int64_t nchans, double* y, double* h_last, double* g_first,
+                int nthreads) {
+  if (!x || !delta || !A || !B || !C || !y) return -1;
+  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (!chans) nchans = Bs * ED;
+  if (nchans < 0) return -1;
+  for (int64_t k = 0; chans && k < nchans; ++k)
+    if (chans[k] < 0 || chans[k] >= Bs * ED) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > nchans) nthreads = (int)(nchans > 0 ? nchans : 1);
+
+  work_t base = {dtype, bidir, x, delta, B, C, A, D, Bs, L, ED, N, chans, nchans, y, h_last,
+                 bidir ? g_first : NULL, 0, 0};
+  work_t* ws = (work_t*)malloc(sizeof(work_t) * (size_t)nthreads);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!ws || !th) {
+    free(ws);
+    free(th);
+    return -2;
+  }
+  int64_t per = (nchans + nthreads - 1) / nthreads;
+  for (int i = 0; i < nthreads; ++i) {
+    ws[i] = base;
+    ws[i].k0 = per * i < nchans ? per * i : nchans;
+    ws[i].k1 = per * (i + 1) < nchans ? per * (i + 1) : nchans;
+  }
+  int rc = 0;
+  for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, worker, &ws[i]);
+  if (worker(&ws[0])) rc = -2;
+  for (int i = 1; i < nthreads; ++i) {
+    void* r = NULL;
+    pthread_join(th[i], &r);
+    if (r) rc = -2;
+  }
+  free(ws);
+  free(th);
+  return rc;
+}
