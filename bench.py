@@ -1,0 +1,236 @@
+"""Benchmark of the fused selective scan on one MI355X.
+
+One step = one full pass of the scan (discretise, scan over L, C-contraction,
+D skip term, final state) over one batch of synthetic input already resident in
+device memory. Three input sets are rotated so that consecutive steps do not
+re-read a working set left in the 256 MB last-level cache.
+
+Prints ONE JSON line. `value` is scan elements (Bs*L*ED*N) per second;
+`roofline` describes the dominant kernel (its per-launch time is measured with
+HIP events on the stream it is launched on); `cpu_baseline` is the fp64 oracle
+on the host cores over the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "fwd_f32_Bs8_L1024_ED1536_N16"
+METRIC = "scan elements (Bs·L·ED·N)/s and achieved HBM GB/s vs MI355X peak"
+
+# MI355X published figures
+HBM_PEAK_GBPS = 8000.0
+CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
+# fp32 VALU issue slots per second (one non-packed lane-op per lane per clock)
+VALU_SLOTS_PER_S = CUS * SIMDS * LANES * CLOCK_GHZ * 1e9
+# algorithmic VALU cost of one scan element: delta*A, (delta x)*B, the state
+# FMA, the C FMA (4 full-rate slots) + one v_exp_f32 (half rate on gfx950: 2)
+SLOTS_PER_ELEMENT = 6.0
+SLOTS_PER_ELEMENT_BIDIR = 8.0
+
+
+def alg_bytes(w):
+    s = 4 if w["dtype"] == "f32" else 2
+    Bs, L, ED, N = w["Bs"], w["L"], w["ED"], w["N"]
+    b = Bs * L * ED * (2 * s + s) + 2 * Bs * L * N * s + 4 * ED * N + 4 * ED
+    if w.get("h_last"):
+        b += 4 * Bs * ED * N
+    return b
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    import state_space_model_selective_amd as ssm
+    for p in ssm.SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, budget_s=20.0):
+    import numpy as np
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    Bs, ED = w["Bs"], w["ED"]
+    E_per_channel = w["L"] * w["N"] * (2 if w["bidir"] else 1)
+    # time a small sample first, then size the measured sample to the budget
+    probe = np.arange(0, min(Bs * ED, threads * 4), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.scan(**inp, bidir=w["bidir"], chans=probe, nthreads=threads)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    per_ch = dt / probe.size
+    nch = int(min(Bs * ED, max(probe.size, budget_s / per_ch)))
+    chans = None if nch >= Bs * ED else np.linspace(0, Bs * ED - 1, nch).astype(np.int64)
+    t0 = time.perf_counter()
+    y_ref, _, _ = oracle.scan(**inp, bidir=w["bidir"], chans=chans, nthreads=threads)
+    dt = time.perf_counter() - t0
+    n_eff = Bs * ED if chans is None else chans.size
+    rate = n_eff * E_per_channel / dt / (2 if w["bidir"] else 1)
+    sample = ("all %d channels" % n_eff) if chans is None else ("%d of %d channels, every time step" % (n_eff, Bs * ED))
+    return dict(value=rate, unit="scan elements/s", cores=threads, kind="oracle",
+                sample=sample + " (fp64 sequential recurrence, %.2f s)" % dt), y_ref, chans
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU-baseline leg")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan shards along batch rows and channels without "
+              "communication, so a multi-GPU figure would be N copies of this one. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import state_space_model_selective_amd as ssm
+    import synth
+    from synth import WORKLOADS
+
+    w = dict(WORKLOADS[args.workload])
+    Bs, L, ED, N = w["Bs"], w["L"], w["ED"], w["N"]
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if w["dtype"] == "f32" else torch.bfloat16
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    nsets = 3
+    host_sets, sets = [], []
+    for i in range(nsets):
+        inp = synth.make_inputs(Bs, L, ED, N, w["dtype"], seed=i)
+        host_sets.append(inp if i == 0 else None)
+        t = {k: to_dev(v) for k, v in inp.items()}
+        t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
+        t["h"] = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev) if w["h_last"] else None
+        need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16,
+                                            w["bidir"])
+        t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        sets.append(t)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        if w["bidir"]:
+            ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], h_last=t["h"],
+                                   workspace=t["ws"], stream=stream)
+        else:
+            ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], h_last=t["h"],
+                             workspace=t["ws"], stream=stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # timed region: K steps, one launch sequence each, events around each step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(sets[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall * 1e3 / args.steps
+
+    E = Bs * L * ED * N
+    value = E / (wall / args.steps)
+    bytes_alg = alg_bytes(w)
+    kernel_elem_rate = E / avg_launch_s
+    # bidirectional: the exp and the two multiplies are shared by both
+    # directions; algorithmic cost 2 mul + exp + 2 x (state FMA + C FMA) = 8
+    slots = SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT
+    achieved_slots = kernel_elem_rate * slots
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(args.workload, src_hash)
+
+    # parity check of step 0's input set against the oracle (also the CPU baseline)
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        cpu, y_ref, chans = cpu_baseline(host_sets[0], w)
+        step(sets[0])
+        torch.cuda.synchronize()
+        y0 = sets[0]["y"].float().cpu().numpy().astype(np.float64)
+        if chans is None:
+            got = y0
+        else:
+            b_i, e_i = np.divmod(chans, ED)
+            got = y0[b_i, :, e_i]
+        tol = 1e-4 if w["dtype"] == "f32" else 2e-2
+        rel = float(np.max(np.abs(got - y_ref) / (1 + np.abs(y_ref))))
+        parity = dict(max_rel_err=rel, tol=tol, passed=bool(rel <= tol))
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "scan elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded counter-based generator; x,B,C,D ~ N(0,1), delta log-uniform [1e-3,1e-1], "
+                "A[e,n] = -(n+1)); 3 input sets rotated",
+        "config": {"workload": args.workload, "Bs": Bs, "L": L, "ED": ED, "N": N, "bidir": w["bidir"],
+                   "h_last": w["h_last"], "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved_slots / 1e12,
+            "peak": VALU_SLOTS_PER_S / 1e12,
+            "unit": "T VALU-slot/s",
+            "frac": achieved_slots / VALU_SLOTS_PER_S,
+            "traffic": traffic,
+            "kernel_avg_us": avg_launch_s * 1e6,
+            "slots_per_element": slots,
+        },
+        "hbm": {
+            "alg_bytes_per_launch": bytes_alg,
+            "achieved_GBps": bytes_alg / avg_launch_s / 1e9,
+            "peak_GBps": HBM_PEAK_GBPS,
+            "frac": bytes_alg / avg_launch_s / 1e9 / HBM_PEAK_GBPS,
+        },
+        "kernel_source_sha256_16": src_hash,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

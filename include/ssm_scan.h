@@ -1,0 +1,115 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * The operation is the selective state-space scan of Mamba as the page
+ * "scan output is different between sequential and parallel versions"
+ * (alxndrTL/mamba.py issue 26) states its API in the test script's API
+ * comment: x and delta of shape (Bs, L, ED), A (ED, N), B and C (Bs, L, N),
+ * D (ED) and the output y (Bs, L, ED), computed by selective_scan /
+ * selective_scan_seq. For every batch row b, channel e and state n:
+ *
+ *   a_t[n]   = exp(delta[b,t,e] * A[e,n])
+ *   h_t[n]   = a_t[n] * h_{t-1}[n] + (delta[b,t,e] * x[b,t,e]) * B[b,t,n],   h_{-1} = 0
+ *   y[b,t,e] = sum_n C[b,t,n] * h_t[n] + D[e] * x[b,t,e]
+ *
+ * delta is used as given (no softplus, bias or clamp) and the initial state is
+ * zero; the pages pass neither.
+ *
+ * The bidirectional variant follows "Some questions of Bi-Mamba2 and Hydra"
+ * (Hprairie/Bi-Mamba2 issue 1), the author's first reply: the sum of two SSMs
+ * with shared weights (A, B, C, delta), one over increasing and one over
+ * decreasing time, plus D x once, with the inputs read in place (no flipped
+ * copy) and no shift:
+ *
+ *   g_t[n]   = a_t[n] * g_{t+1}[n] + (delta x)[b,t,e] * B[b,t,n],   g_L = 0
+ *   y[b,t,e] = sum_n C[b,t,n] * (h_t[n] + g_t[n]) + D[e] * x[b,t,e]
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers (memory from hipMalloc or any allocator on
+ *    the device the stream belongs to). The caller owns every buffer,
+ *    including the workspace. The library allocates nothing, keeps no pointer
+ *    after returning and holds no global state, so calls are reentrant; two
+ *    calls that run at the same time need separate workspaces.
+ *  - Layout: dense row-major in the shapes above (last index fastest), no
+ *    strides. h_last and g_first are (Bs, ED, N) float32.
+ *  - dtype (ssm_dtype) applies to x, delta, B, C and y. A, D, h_last and
+ *    g_first are float32 always. Internal state and accumulation are float32;
+ *    bfloat16 outputs are rounded to nearest even.
+ *  - Alignment: every pointer must be aligned to 16 bytes.
+ *  - Asynchrony: each call validates its arguments on the host before any
+ *    HIP call, enqueues its kernels on `stream` (a hipStream_t; NULL means
+ *    the null stream) and returns. Faults inside a kernel surface at the
+ *    caller's next synchronisation on that stream.
+ *  - Numerics: inputs whose state overflows float32 (a > 1, i.e. delta*A > 0
+ *    over long spans) propagate inf/NaN; no error code is returned for them.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_F32 = 0,  /* float32 x, delta, B, C, y */
+  SSM_BF16 = 1  /* bfloat16 x, delta, B, C, y (bit patterns, uint16) */
+} ssm_dtype;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSM_ERR_DIM = 2,         /* a dimension is <= 0 or the sizes overflow int64 */
+  SSM_ERR_UNSUPPORTED = 3, /* N not supported, unknown dtype, or a pointer not 16-byte aligned */
+  SSM_ERR_ALIAS = 4,       /* an output overlaps an input, another output or the workspace */
+  SSM_ERR_WORKSPACE = 5,   /* workspace smaller than ssm_scan_workspace_bytes() */
+  SSM_ERR_LAUNCH = 6       /* the HIP runtime rejected a launch */
+} ssm_status;
+
+/* Supported state sizes N. */
+#define SSM_MAX_N 16
+
+/*
+ * Bytes of device workspace that ssm_scan_fwd (bidir = 0) or
+ * ssm_scan_bidir_fwd (bidir = 1) needs for these sizes. Zero means the call
+ * may pass workspace = NULL. The workspace needs no initialisation and holds
+ * nothing of interest after the call. Returns 0 for invalid sizes too (the
+ * call itself then reports the error).
+ */
+size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int bidir);
+
+/*
+ * Forward selective scan (the recurrence above).
+ *   x, delta : (Bs, L, ED) of dtype        -- input sequence and step sizes
+ *   A        : (ED, N) float32             -- state matrix (diagonal per channel)
+ *   B, C     : (Bs, L, N) of dtype         -- input and output projections
+ *   D        : (ED) float32, or NULL (treated as zero)
+ *   y        : (Bs, L, ED) of dtype        -- output, written in full
+ *   h_last   : (Bs, ED, N) float32, or NULL -- state after the last step
+ * Returns SSM_OK once the kernels are enqueued, else the first error found.
+ */
+int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bidirectional selective scan (forward plus reverse-time scan plus D x).
+ * Arguments as ssm_scan_fwd, and
+ *   h_last  : (Bs, ED, N) float32 or NULL -- forward state after t = L-1
+ *   g_first : (Bs, ED, N) float32 or NULL -- reverse state after t = 0
+ */
+int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L,
+                       int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* ssm_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,135 @@
+"""Python binding of the MI355X selective-scan library (libssm_scan.so).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``csrc/ssm_scan.hip`` behind the C ABI declared in ``include/ssm_scan.h``.
+PyTorch supplies device memory and the stream. There is no fallback: if the
+library is not built, or the tensors are not on a GPU, the calls raise.
+"""
+import ctypes
+import os
+import subprocess
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+LIB_PATH = os.path.join(_HERE, "libssm_scan.so")
+SOURCES = [os.path.join(_HERE, "csrc", "ssm_scan.hip")]
+INCLUDE = os.path.join(_ROOT, "include")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_OK, SSM_ERR_NULL, SSM_ERR_DIM, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH = range(7)
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+    # no packed-FP32 instructions anywhere in the library
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+_lib = None
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
+
+
+def build(verbose=False):
+    """Compile libssm_scan.so for gfx950 with hipcc (works without a GPU)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc] + HIPCC_FLAGS + ["-I", INCLUDE] + SOURCES + ["-o", tmp]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout)
+    if verbose:
+        print(res.stdout)
+    os.replace(tmp, LIB_PATH)
+    global _lib
+    _lib = None
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssm_scan.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        L.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
+        L.ssm_scan_workspace_bytes.restype = sz
+        L.ssm_scan_fwd.argtypes = [vp] * 8 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_fwd.restype = ci
+        L.ssm_scan_bidir_fwd.argtypes = [vp] * 9 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_fwd.restype = ci
+        L.ssm_status_str.argtypes = [ci]
+        L.ssm_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().ssm_status_str(int(status)).decode()
+
+
+def ssm_scan_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32, bidir=False):
+    return int(lib().ssm_scan_workspace_bytes(Bs, L, ED, N, int(dtype), int(bool(bidir))))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError("x must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _prepare(x, delta, A, B, C, D, y, bidir, workspace):
+    import torch
+    if not x.is_cuda:
+        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
+    dt = _dtype_code(x)
+    Bs, L, ED = x.shape
+    N = A.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    need = ssm_scan_workspace_bytes(Bs, L, ED, N, dt, bidir)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return dt, (Bs, L, ED, N), y, workspace, ws_bytes
+
+
+def _stream(x, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None, stream=None):
+    """y = selective_scan(x, delta, A, B, C, D); optionally the final state into h_last."""
+    dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, False, workspace)
+    rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), _ptr(h_last),
+                            Bs, L, ED, N, dt, _ptr(workspace), ws_bytes, _stream(x, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_scan_fwd")
+    return y
+
+
+def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=None, workspace=None,
+                       stream=None):
+    """y = forward scan + reverse-time scan (shared weights, read in place) + D x."""
+    dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, True, workspace)
+    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+                                  _ptr(h_last), _ptr(g_first), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
+                                  _stream(x, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_scan_bidir_fwd")
+    return y

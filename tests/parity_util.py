@@ -1,0 +1,90 @@
+"""Helpers for GPU parity tests: run the HIP path through the binding, run
+the oracle on the same buffers, and compare under the stated tolerance
+
+    pass  iff  max_i ( |y_i - y_ref_i| - tol * (1 + |y_ref_i|) ) <= 0,
+
+tol = 1e-4 for float32 outputs and 2e-2 for bfloat16 outputs (float32 state
+and accumulation in both cases)."""
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(inp, dev):
+    import torch
+    out = {}
+    for k, v in inp.items():
+        if v.dtype == np.uint16:
+            out[k] = torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            out[k] = torch.from_numpy(v).to(dev)
+    return out
+
+
+def y_to_numpy(y):
+    import torch
+    if y.dtype == torch.bfloat16:
+        return y.float().cpu().numpy().astype(np.float64)
+    return y.double().cpu().numpy()
+
+
+def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False):
+    import torch
+    import state_space_model_selective_amd as ssm
+    dev = torch.device("cuda:0")
+    t = to_device(inp, dev)
+    Bs, L, ED = inp["x"].shape
+    N = inp["A"].shape[1]
+    h = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev) if want_h else None
+    g = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev) if want_g else None
+    D = None if D_none else t["D"]
+    if bidir:
+        y = ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, g_first=g,
+                                   stream=stream)
+    else:
+        y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, stream=stream)
+    torch.cuda.synchronize()
+    return (y_to_numpy(y), None if h is None else h.double().cpu().numpy(),
+            None if g is None else g.double().cpu().numpy())
+
+
+def excess(got, ref, tol):
+    return np.abs(got - ref) - tol * (1.0 + np.abs(ref))
+
+
+def assert_close(name, got, ref, tol, chunk_hint=None):
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s has non-finite values" % name
+    ex = excess(got, ref, tol)
+    i = np.unravel_index(np.argmax(ex), ex.shape)
+    worst = float(ex[i])
+    rel = float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+    log("  %s: max |d|/(1+|ref|) = %.3e (tol %.0e) at %s" % (name, rel, tol, tuple(int(v) for v in i)))
+    assert worst <= 0.0, "%s: tolerance exceeded by %.3e at index %s (got %r, ref %r)" % (
+        name, worst, tuple(int(v) for v in i), float(got[i]), float(ref[i]))
+    return rel
+
+
+def sample_channels(Bs, ED, count, seed=0):
+    """Channel ids b*ED + e: both ends, and a seeded spread in between."""
+    rng = np.random.default_rng(seed)
+    n = Bs * ED
+    pick = {0, n - 1, ED - 1, min(ED, n - 1), n // 2}
+    pick.update(int(v) for v in rng.integers(0, n, size=max(0, count - len(pick))))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def gather_channels(y, chans, ED):
+    """y (Bs, L, ED) -> (len(chans), L) in the oracle's channel-major order."""
+    b, e = np.divmod(chans, ED)
+    return y[b, :, e]

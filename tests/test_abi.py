@@ -1,0 +1,110 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import state_space_model_selective_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+# fake device addresses, 16-byte aligned and far apart; only used on paths that
+# must fail validation before anything touches them
+P = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"ssm_scan_fwd", "ssm_scan_bidir_fwd", "ssm_scan_workspace_bytes", "ssm_status_str"} <= set(names)
+    lib = ctypes.CDLL(ssm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(7):
+        assert ssm.status_str(s)
+    assert ssm.status_str(999) == "unknown status"
+
+
+def fwd(**kw):
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], Bs=2, L=64, ED=64, N=16,
+                dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args.update(kw)
+    return ssm.lib().ssm_scan_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["y"],
+                                  args["h"], args["Bs"], args["L"], args["ED"], args["N"], args["dtype"], args["ws"],
+                                  args["ws_bytes"], None)
+
+
+def bidir(**kw):
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], Bs=2, L=64, ED=64,
+                N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args.update(kw)
+    return ssm.lib().ssm_scan_bidir_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                                        args["y"], args["h"], args["g"], args["Bs"], args["L"], args["ED"],
+                                        args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "y"])
+def test_null_pointer(name):
+    assert fwd(**{name: None}) == ssm.SSM_ERR_NULL
+    assert bidir(**{name: None}) == ssm.SSM_ERR_NULL
+
+
+@pytest.mark.parametrize("dim", ["Bs", "L", "ED", "N"])
+@pytest.mark.parametrize("val", [0, -1])
+def test_bad_dimension(dim, val):
+    assert fwd(**{dim: val}) == ssm.SSM_ERR_DIM
+    assert bidir(**{dim: val}) == ssm.SSM_ERR_DIM
+
+
+def test_size_overflow():
+    assert fwd(Bs=1 << 40, L=1 << 20, ED=1 << 10) == ssm.SSM_ERR_DIM
+
+
+@pytest.mark.parametrize("N", [1, 8, 15, 17, 32])
+def test_unsupported_state_size(N):
+    assert fwd(N=N) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_unknown_dtype():
+    assert fwd(dtype=7) == ssm.SSM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "y", "h"])
+def test_misaligned_pointer(name):
+    base = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7])
+    assert fwd(**{name: base[name] + 4}) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_output_aliasing_an_input():
+    assert fwd(y=P[0]) == ssm.SSM_ERR_ALIAS            # y on top of x
+    assert fwd(y=P[1] + 4096) == ssm.SSM_ERR_ALIAS     # y inside delta
+    assert fwd(h=P[6] + 64) == ssm.SSM_ERR_ALIAS       # h_last inside y
+    assert bidir(g=P[7]) == ssm.SSM_ERR_ALIAS          # g_first on h_last
+
+
+def test_workspace_query_and_check():
+    assert ssm.ssm_scan_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32, False) == 0
+    assert ssm.ssm_scan_workspace_bytes(0, 64, 64, 16, ssm.SSM_F32, False) == 0
+    need = ssm.ssm_scan_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16, True)
+    if need:
+        assert bidir(dtype=ssm.SSM_BF16) == ssm.SSM_ERR_WORKSPACE
+        assert bidir(dtype=ssm.SSM_BF16, ws=P[9], ws_bytes=need - 1) == ssm.SSM_ERR_WORKSPACE
+        assert bidir(dtype=ssm.SSM_BF16, ws=P[6], ws_bytes=need) == ssm.SSM_ERR_ALIAS
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 16)
+    with pytest.raises(RuntimeError):
+        ssm.ssm_scan_fwd(x, x, torch.zeros(16, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))

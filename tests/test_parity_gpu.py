@@ -1,0 +1,79 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity_util import TOL, assert_close, gather_channels, log, run_gpu, sample_channels
+
+pytestmark = pytest.mark.gpu
+
+
+def check_full(Bs, L, ED, dtype="f32", bidir=False, seed=0, D_none=False):
+    log("case Bs=%d L=%d ED=%d dtype=%s bidir=%s seed=%d" % (Bs, L, ED, dtype, bidir, seed))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=seed)
+    y, h, g = run_gpu(inp, bidir=bidir, want_h=True, want_g=bidir, D_none=D_none)
+    ref_inp = dict(inp, D=None) if D_none else inp
+    y_ref, h_ref, g_ref = oracle.scan(**ref_inp, bidir=bidir, want_h_last=True, want_g_first=bidir)
+    assert_close("y", y, y_ref, TOL[dtype])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+    if bidir:
+        assert_close("g_first", g, g_ref, TOL["f32"])
+
+
+def test_page_shape_forward():
+    check_full(2, 64, 64)
+
+
+def test_page_shape_bidirectional():
+    check_full(2, 64, 64, bidir=True)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 63, 64, 65, 127, 1009])
+def test_sequence_lengths(L):
+    check_full(2, L, 128, seed=L)
+
+
+@pytest.mark.parametrize("L", [1, 5, 129, 1009])
+def test_sequence_lengths_bidirectional(L):
+    check_full(1, L, 64, bidir=True, seed=L)
+
+
+@pytest.mark.parametrize("ED", [16, 48, 64, 80, 192, 1040])
+def test_channel_counts(ED):
+    check_full(3, 200, ED, seed=ED)
+
+
+def test_single_batch_row_long():
+    check_full(1, 4099, 256, seed=5)
+
+
+def test_bf16_forward():
+    check_full(2, 300, 256, dtype="bf16", seed=6)
+
+
+def test_bf16_bidirectional():
+    check_full(2, 300, 128, dtype="bf16", bidir=True, seed=7)
+
+
+def test_without_D():
+    check_full(2, 100, 64, D_none=True, seed=8)
+    check_full(2, 100, 64, D_none=True, bidir=True, seed=9)
+
+
+def test_repeatable_bitwise():
+    inp = synth.make_inputs(2, 777, 192, 16, "f32", seed=10)
+    y1, h1, _ = run_gpu(inp, want_h=True)
+    y2, h2, _ = run_gpu(inp, want_h=True)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_on_a_side_stream():
+    import torch
+    inp = synth.make_inputs(2, 130, 64, 16, "f32", seed=11)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y, _, _ = run_gpu(inp, stream=s)
+    y_ref, _, _ = oracle.scan(**inp)
+    assert_close("y", y, y_ref, TOL["f32"])
