@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
@@ -66,19 +67,36 @@ struct Vec4<uint16_t> {
 };
 
 // ---------------------------------------------------------------------------
-// Cross-lane moves (DPP). quad_bcast<J>: every lane of a quad reads lane J of
-// that quad. row_ror<K>: lane i of a 16-lane row reads lane (i + K) mod 16.
-// Written as moves; the compiler folds them into the consuming VALU op as a
-// DPP source modifier where the encoding allows it.
+// Cross-lane operands (DPP). Lane q of a 16-lane row holds B_t[q] (or
+// C_t[q]); quad g of the row needs B_t[4g .. 4g+3]. quad_bcast<J> makes every
+// lane of a quad read lane J of that quad. As a plain move the compiler folds
+// it into the consuming multiply as a DPP source modifier (and inserts the
+// wait states DPP needs). It does not fold it into v_fmac, so the C
+// contraction issues v_fmac_f32_dpp itself; the leading s_nop 1 provides the
+// two wait states a DPP read needs after a VALU write of its source.
 // ---------------------------------------------------------------------------
 template <int J>
 __device__ __forceinline__ float quad_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, true));
 }
-template <int K>
-__device__ __forceinline__ float row_ror(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + K, 0xf, 0xf, true));
-}
+
+#define SSM_FMAC_QUAD(J)                                                                              \
+  template <>                                                                                         \
+  __device__ __forceinline__ float fmac_quad<J>(float acc, float src, float other) {                  \
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[" #J "," #J "," #J "," #J                    \
+        "] row_mask:0xf bank_mask:0xf bound_ctrl:1"                                                   \
+        : "+v"(acc)                                                                                   \
+        : "v"(src), "v"(other));                                                                      \
+    return acc;                                                                                       \
+  }
+// acc + (lane J of this lane's quad's src) * other
+template <int J>
+__device__ __forceinline__ float fmac_quad(float acc, float src, float other);
+SSM_FMAC_QUAD(0)
+SSM_FMAC_QUAD(1)
+SSM_FMAC_QUAD(2)
+SSM_FMAC_QUAD(3)
+#undef SSM_FMAC_QUAD
 
 // ---------------------------------------------------------------------------
 // Chunked selective-scan kernel.
@@ -90,22 +108,25 @@ __device__ __forceinline__ float row_ror(float v) {
 // Lanes of a wave: lane = 16 r + 4 g + c (r, g, c in 0..3) holds channel
 // 4 r + c and the four states n = 4 g .. 4 g + 3 of that channel. The lanes
 // of quad g of every row therefore need exactly B_t[4g .. 4g+3] and
-// C_t[4g .. 4g+3]: lane q of a row loads B_t[q] and a quad broadcast (DPP)
-// hands each lane the other three, without extra VALU work. y_t for a channel
-// is the sum over the four quads of a row (two DPP rotate-adds).
+// C_t[4g .. 4g+3]: lane q of a row reads B_t[q] and C_t[q], and quad
+// broadcasts (DPP) hand each lane the other three. Each lane writes its
+// partial sum over its four states to LDS; y_t for a channel is the sum of
+// the four quads' partials, formed when the output tile is stored.
 //
 // Per round:
 //   staging  global -> registers (prefetched one round ahead, 16-byte loads)
-//            -> LDS tile: (delta, delta*x), D*x, B, C (and, in the forward
-//            sweep of the bidirectional scan, the reverse sweep's partial y)
+//            -> LDS tile: delta, delta*x, B, C and D*x (in the forward sweep
+//            of the bidirectional scan: the reverse sweep's partial y instead)
 //   local    each wave runs its segment from a zero state, keeping a_t and
 //            b_t of all TS steps in registers; segment aggregate
-//            (prod a = exp2(A log2e * sum delta), h_end)
-//   fold     through LDS: the state entering segment s is the round's carry
-//            folded through the aggregates of segments 0..s-1
+//            (prod a = exp2(A log2e * sum delta), h_end) to LDS
+//   fold     the state entering segment s is the previous round's carry
+//            folded through the aggregates of segments 0..s-1; the last wave
+//            also folds its own aggregate and publishes the round's carry
 //   replay   h_t = a_t h_{t-1} + b_t from the true entering state, then the
-//            C contraction and the cross-quad sum into the LDS output tile
-//   store    the output tile, one round later, 16-byte stores
+//            C contraction over the lane's states into the LDS output tile
+//   store    one round later: sum of the four state quads + D x (or the
+//            reverse sweep's partial), 16-byte stores
 // With SEG == 1 the carry is known before the segment starts, so the local
 // pass is the final pass (no replay).
 //
@@ -113,6 +134,10 @@ __device__ __forceinline__ float row_ror(float v) {
 // tau reads time L-1-tau in place, no flipped copy), storing
 // sum_n C g + D x as float32 partials, then sweeps forward adding
 // sum_n C h to them.
+//
+// VEC: ED is a multiple of 4, so every 4-channel chunk is 16-byte (float32)
+// or 8-byte (bfloat16) aligned and either wholly inside or wholly outside
+// [0, ED); otherwise chunks are loaded and stored element by element.
 // ---------------------------------------------------------------------------
 template <typename T>
 struct ScanArgs {
@@ -133,34 +158,53 @@ struct ScanArgs {
   int remap;       // spread neighbouring channel groups over one XCD
 };
 
+// Input tile of one round (double-buffered).
 template <int RT>
 struct alignas(16) Tile {
-  float2 xd[RT][16];   // (delta, delta * x) per channel
-  float bq[RT][16];    // B_t[n]
-  float4 c4[RT][4];    // C_t[4g .. 4g+3]
-  float skip[RT][16];  // D * x
-  float yt[RT][16];    // sum_n C_t[n] h_t[n] per channel
-  float part[RT][16];  // bidir forward sweep: partial from the reverse sweep
+  float dt[RT][16];   // delta per channel
+  float dx[RT][16];   // delta * x per channel
+  float bq[RT][16];   // B_t[n]
+  float cq[RT][16];   // C_t[n]
+  float aux[RT][16];  // D x, or (forward sweep of bidir) the reverse sweep's partial
+};
+
+// Output tile of one round (single-buffered: written by the replay after the
+// round's mid barrier, read by the store at the start of the next round).
+template <int RT>
+struct alignas(16) OutTile {
+  float yq[4][RT + 1][16];  // per state quad g: sum over its 4 states of C h (rows padded)
+};
+
+// Segment aggregates and the carry between rounds.
+template <int SEG>
+struct alignas(16) FoldArea {
+  float4 A[SEG][64];   // prod of a over the segment, per lane's 4 states
+  float4 H[SEG][64];   // state at the segment's end, started from zero
+  float4 carry[2][64]; // state after the round, by round parity
 };
 
 // Staging of one round: each thread owns TPT fixed (row, chunk) tasks of the
 // x/delta tile (4 channels per chunk) or of the B/C tile (4 states per chunk),
 // loads them one round ahead into registers, writes them to the LDS tile, and
-// stores its chunk of the output tile one round later.
-template <typename T, int RT, int TPT>
+// stores its chunk of the output tile one round later. Offsets advance by one
+// round (RT steps, forward or backward in time) per call.
+template <typename T, int RT, int TPT, bool BIDIR, bool VEC>
 struct Stager {
   int row[TPT], chk[TPT];
-  bool is_xd[TPT];
+  bool is_xd[TPT], chunk_ok[TPT];
   float4 dval[TPT];              // D of the chunk's channels
   float4 ra[TPT], rb[TPT], rp[TPT];
-  int64_t e0, ED, L;
-  bool vec_ok, rev, add_part;
+  int64_t pre_off[TPT];          // element offset of this task's row in the next round to prefetch
+  int64_t out_off[TPT];          // element offset of this task's row in the next round to store
+  int64_t step_xd, step_bc;      // offset change per round
+  int64_t ce0;                   // first channel of the group
+  int64_t ED, L;
+  bool rev, add_part;
 
-  __device__ __forceinline__ void init(const ScanArgs<T>& p, int tid, int64_t e0_, int64_t ED_) {
-    e0 = e0_;
-    ED = ED_;
+  __device__ __forceinline__ void init(const ScanArgs<T>& p, int tid, int64_t b, int64_t e0) {
+    ED = p.ED;
     L = p.L;
-    vec_ok = (ED & 3) == 0;
+    ce0 = e0;
     rev = add_part = false;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
@@ -170,44 +214,52 @@ struct Stager {
       row[k] = u >> 2;
       chk[k] = u & 3;
       const int64_t ce = e0 + 4 * chk[k];
+      chunk_ok[k] = !is_xd[k] || ce < ED;
       const bool dd = is_xd[k] && p.D != nullptr;
       dval[k] = make_float4(dd && ce + 0 < ED ? p.D[ce + 0] : 0.f, dd && ce + 1 < ED ? p.D[ce + 1] : 0.f,
                             dd && ce + 2 < ED ? p.D[ce + 2] : 0.f, dd && ce + 3 < ED ? p.D[ce + 3] : 0.f);
     }
+    (void)b;
   }
 
-  __device__ __forceinline__ int64_t time_of(int64_t tau) const { return rev ? (L - 1 - tau) : tau; }
-
-  // global -> registers for round rr
-  __device__ __forceinline__ void prefetch(const ScanArgs<T>& p, int64_t b, int64_t rr) {
+  // start a sweep: round 0 of both prefetch and store
+  __device__ __forceinline__ void begin(int64_t b, bool rev_, bool add_part_) {
+    rev = rev_;
+    add_part = add_part_;
+    step_xd = (rev ? -RT : RT) * ED;
+    step_bc = (rev ? -RT : RT) * 16;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
-      const int64_t tau = rr * RT + row[k];
+      const int64_t t = rev ? (L - 1 - row[k]) : row[k];
+      pre_off[k] = is_xd[k] ? (b * L + t) * ED + ce0 + 4 * chk[k] : (b * L + t) * 16 + 4 * chk[k];
+      out_off[k] = pre_off[k];
+    }
+  }
+
+  // global -> registers for round rr
+  __device__ __forceinline__ void prefetch(const ScanArgs<T>& p, int64_t rr) {
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int64_t off = pre_off[k];
+      pre_off[k] += is_xd[k] ? step_xd : step_bc;
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a;
-      if (tau < L) {
-        const int64_t t = time_of(tau);
-        if (is_xd[k]) {
-          const int64_t ce = e0 + 4 * chk[k];
-          const int64_t off = (b * L + t) * ED + ce;
-          if (vec_ok) {
-            if (ce < ED) {
-              a = Vec4<T>::load(p.x + off);
-              bb = Vec4<T>::load(p.dl + off);
-              if (add_part) pp = *reinterpret_cast<const float4*>(p.part + off);
-            }
-          } else {
-            a = make_float4(ce + 0 < ED ? to_f32(p.x[off + 0]) : 0.f, ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
-                            ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
-            bb = make_float4(ce + 0 < ED ? to_f32(p.dl[off + 0]) : 0.f, ce + 1 < ED ? to_f32(p.dl[off + 1]) : 0.f,
-                             ce + 2 < ED ? to_f32(p.dl[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dl[off + 3]) : 0.f);
-            if (add_part)
-              pp = make_float4(ce + 0 < ED ? p.part[off + 0] : 0.f, ce + 1 < ED ? p.part[off + 1] : 0.f,
-                               ce + 2 < ED ? p.part[off + 2] : 0.f, ce + 3 < ED ? p.part[off + 3] : 0.f);
-          }
-        } else {
-          const int64_t off = (b * L + t) * 16 + 4 * chk[k];
+      if (rr * RT + row[k] < L && chunk_ok[k]) {
+        if (!is_xd[k]) {
           a = Vec4<T>::load(p.B + off);
           bb = Vec4<T>::load(p.C + off);
+        } else if (VEC) {
+          a = Vec4<T>::load(p.x + off);
+          bb = Vec4<T>::load(p.dl + off);
+          if (BIDIR && add_part) pp = *reinterpret_cast<const float4*>(p.part + off);
+        } else {
+          const int64_t ce = ce0 + 4 * chk[k];
+          a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
+                          ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
+          bb = make_float4(to_f32(p.dl[off]), ce + 1 < ED ? to_f32(p.dl[off + 1]) : 0.f,
+                           ce + 2 < ED ? to_f32(p.dl[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dl[off + 3]) : 0.f);
+          if (BIDIR && add_part)
+            pp = make_float4(p.part[off], ce + 1 < ED ? p.part[off + 1] : 0.f, ce + 2 < ED ? p.part[off + 2] : 0.f,
+                             ce + 3 < ED ? p.part[off + 3] : 0.f);
         }
       }
       ra[k] = a;
@@ -223,52 +275,59 @@ struct Stager {
       const int r = row[k], c4 = 4 * chk[k];
       if (is_xd[k]) {
         const float4 xv = ra[k], dv = rb[k];
-        *reinterpret_cast<float4*>(&tl.xd[r][c4]) = make_float4(dv.x, dv.x * xv.x, dv.y, dv.y * xv.y);
-        *reinterpret_cast<float4*>(&tl.xd[r][c4 + 2]) = make_float4(dv.z, dv.z * xv.z, dv.w, dv.w * xv.w);
-        *reinterpret_cast<float4*>(&tl.skip[r][c4]) =
-            make_float4(dval[k].x * xv.x, dval[k].y * xv.y, dval[k].z * xv.z, dval[k].w * xv.w);
-        if (add_part) *reinterpret_cast<float4*>(&tl.part[r][c4]) = rp[k];
+        *reinterpret_cast<float4*>(&tl.dt[r][c4]) = dv;
+        *reinterpret_cast<float4*>(&tl.dx[r][c4]) = make_float4(dv.x * xv.x, dv.y * xv.y, dv.z * xv.z, dv.w * xv.w);
+        *reinterpret_cast<float4*>(&tl.aux[r][c4]) =
+            (BIDIR && add_part) ? rp[k]
+                                : make_float4(dval[k].x * xv.x, dval[k].y * xv.y, dval[k].z * xv.z, dval[k].w * xv.w);
       } else {
         *reinterpret_cast<float4*>(&tl.bq[r][c4]) = ra[k];
-        tl.c4[r][chk[k]] = rb[k];
+        *reinterpret_cast<float4*>(&tl.cq[r][c4]) = rb[k];
       }
     }
   }
 
-  // LDS output tile of round rr -> global
-  __device__ __forceinline__ void store_out(const ScanArgs<T>& p, int64_t b, int64_t rr, const Tile<RT>& tl) const {
+  // output of round rr (whose input tile is tl) -> global
+  __device__ __forceinline__ void store_out(const ScanArgs<T>& p, int64_t rr, const Tile<RT>& tl,
+                                            const OutTile<RT>& ot) {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       if (!is_xd[k]) continue;
+      const int64_t off = out_off[k];
+      out_off[k] += step_xd;
       const int r = row[k], c4 = 4 * chk[k];
-      const int64_t tau = rr * RT + r;
-      const int64_t ce = e0 + c4;
-      if (tau >= L || ce >= ED) continue;
-      const int64_t off = (b * L + time_of(tau)) * ED + ce;
-      const float4 v = *reinterpret_cast<const float4*>(&tl.yt[r][c4]);
-      const float4 a = add_part ? *reinterpret_cast<const float4*>(&tl.part[r][c4])
-                                : *reinterpret_cast<const float4*>(&tl.skip[r][c4]);
-      const float4 o = make_float4(v.x + a.x, v.y + a.y, v.z + a.z, v.w + a.w);
-      if (vec_ok) {
-        if (rev) *reinterpret_cast<float4*>(p.part + off) = o;
+      if (rr * RT + r >= L || !chunk_ok[k]) continue;
+      const float4 v0 = *reinterpret_cast<const float4*>(&ot.yq[0][r][c4]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&ot.yq[1][r][c4]);
+      const float4 v2 = *reinterpret_cast<const float4*>(&ot.yq[2][r][c4]);
+      const float4 v3 = *reinterpret_cast<const float4*>(&ot.yq[3][r][c4]);
+      const float4 a = *reinterpret_cast<const float4*>(&tl.aux[r][c4]);
+      const float4 o = make_float4((v0.x + v1.x) + (v2.x + v3.x) + a.x, (v0.y + v1.y) + (v2.y + v3.y) + a.y,
+                                   (v0.z + v1.z) + (v2.z + v3.z) + a.z, (v0.w + v1.w) + (v2.w + v3.w) + a.w);
+      if (VEC) {
+        if (BIDIR && rev) *reinterpret_cast<float4*>(p.part + off) = o;
         else Vec4<T>::store(p.y + off, o);
-      } else if (rev) {
-        p.part[off] = o.x;
-        if (ce + 1 < ED) p.part[off + 1] = o.y;
-        if (ce + 2 < ED) p.part[off + 2] = o.z;
-        if (ce + 3 < ED) p.part[off + 3] = o.w;
       } else {
-        p.y[off] = from_f32<T>(o.x);
-        if (ce + 1 < ED) p.y[off + 1] = from_f32<T>(o.y);
-        if (ce + 2 < ED) p.y[off + 2] = from_f32<T>(o.z);
-        if (ce + 3 < ED) p.y[off + 3] = from_f32<T>(o.w);
+        const int64_t ce = ce0 + c4;
+        if (BIDIR && rev) {
+          p.part[off] = o.x;
+          if (ce + 1 < ED) p.part[off + 1] = o.y;
+          if (ce + 2 < ED) p.part[off + 2] = o.z;
+          if (ce + 3 < ED) p.part[off + 3] = o.w;
+        } else {
+          p.y[off] = from_f32<T>(o.x);
+          if (ce + 1 < ED) p.y[off + 1] = from_f32<T>(o.y);
+          if (ce + 2 < ED) p.y[off + 2] = from_f32<T>(o.z);
+          if (ce + 3 < ED) p.y[off + 3] = from_f32<T>(o.w);
+        }
       }
     }
   }
 };
 
-template <typename T, int SEG, int TS, bool BIDIR>
-__global__ __launch_bounds__(64 * SEG) void scan_chunked_kernel(const ScanArgs<T> p) {
+template <typename T, int SEG, int TS, bool BIDIR, bool VEC, int WPE = 3>
+__global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE))) void scan_chunked_kernel(
+    const ScanArgs<T> p) {
   constexpr int RT = SEG * TS;
   constexpr int NT = 64 * SEG;
   constexpr int TPT = (8 * RT) / NT;  // staging tasks per thread
@@ -276,7 +335,8 @@ __global__ __launch_bounds__(64 * SEG) void scan_chunked_kernel(const ScanArgs<T
   static_assert(TPT * NT == 8 * RT, "staging tasks must divide evenly");
 
   __shared__ Tile<RT> tile[2];
-  __shared__ float4 agg[SEG][64][2];
+  __shared__ OutTile<RT> out;
+  __shared__ FoldArea<SEG> fa;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,44 +360,44 @@ __global__ __launch_bounds__(64 * SEG) void scan_chunked_kernel(const ScanArgs<T
 #pragma unroll
   for (int j = 0; j < 4; ++j) A2[j] = p.A[ec * 16 + 4 * g + j] * kLog2e;
 
-  Stager<T, RT, TPT> st;
-  st.init(p, tid, e0, ED);
+  Stager<T, RT, TPT, BIDIR, VEC> st;
+  st.init(p, tid, b, e0);
 
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
     const bool rev = BIDIR && sweep == 0;
-    const bool add_part = BIDIR && sweep == 1;
+    st.begin(b, rev, BIDIR && sweep == 1);
     float carry[4] = {0.f, 0.f, 0.f, 0.f};
-    st.rev = rev;
-    st.add_part = add_part;
+    if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    st.prefetch(p, b, 0);
+    st.prefetch(p, 0);
     st.commit(tile[0]);
     __syncthreads();
 
     for (int64_t r = 0; r < rounds; ++r) {
       Tile<RT>& cur = tile[r & 1];
       Tile<RT>& nxt = tile[(r + 1) & 1];
-      if (r + 1 < rounds) st.prefetch(p, b, r + 1);
-      if (r >= 1) st.store_out(p, b, r - 1, nxt);
+      if (r + 1 < rounds) st.prefetch(p, r + 1);
+      // output of round r-1, whose input tile stays intact until this round's commit
+      if (r >= 1) st.store_out(p, r - 1, nxt, out);
 
       if constexpr (SEG == 1) {
+        // the output tile is single-buffered: the store above must finish
+        // reading it before this round writes it
+        __syncthreads();
         // the entering state is known: single pass
 #pragma unroll
         for (int i = 0; i < TS; ++i) {
-          const float2 xd = cur.xd[i][ch];
-          const float bq = cur.bq[i][q];
-          const float4 cv = cur.c4[i][g];
+          const float dt = cur.dt[i][ch], dx = cur.dx[i][ch];
+          const float bq = cur.bq[i][q], cq = cur.cq[i][q];
           const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            carry[j] = __builtin_fmaf(__builtin_amdgcn_exp2f(xd.x * A2[j]), carry[j], xd.y * bb[j]);
-          float yp = cv.x * carry[0];
-          yp = __builtin_fmaf(cv.y, carry[1], yp);
-          yp = __builtin_fmaf(cv.z, carry[2], yp);
-          yp = __builtin_fmaf(cv.w, carry[3], yp);
-          yp += row_ror<4>(yp);
-          yp += row_ror<8>(yp);
-          if (g == (i & 3)) cur.yt[i][ch] = yp;
+            carry[j] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * A2[j]), carry[j], dx * bb[j]);
+          float yp = quad_bcast<0>(cq) * carry[0];
+          yp = fmac_quad<1>(yp, cq, carry[1]);
+          yp = fmac_quad<2>(yp, cq, carry[2]);
+          yp = fmac_quad<3>(yp, cq, carry[3]);
+          out.yq[g][i][ch] = yp;
         }
       } else {
         // local pass from a zero state
@@ -347,61 +407,62 @@ __global__ __launch_bounds__(64 * SEG) void scan_chunked_kernel(const ScanArgs<T
 #pragma unroll
         for (int i = 0; i < TS; ++i) {
           const int row = wave * TS + i;
-          const float2 xd = cur.xd[row][ch];
+          const float dt = cur.dt[row][ch], dx = cur.dx[row][ch];
           const float bq = cur.bq[row][q];
-          sd += xd.x;
+          sd += dt;
           const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            av[i][j] = __builtin_amdgcn_exp2f(xd.x * A2[j]);
-            bv[i][j] = xd.y * bb[j];
+            av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
+            bv[i][j] = dx * bb[j];
             hl[j] = __builtin_fmaf(av[i][j], hl[j], bv[i][j]);
           }
         }
-        agg[wave][lane][0] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
-                                         __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
-        agg[wave][lane][1] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+        fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
+                                       __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
+        fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
         __syncthreads();
 
-        // fold the segment aggregates in order
-        float hin[4] = {carry[0], carry[1], carry[2], carry[3]};
-#pragma unroll
-        for (int k = 0; k < SEG; ++k) {
-          if (k == wave) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hin[j] = carry[j];
-          }
-          const float4 Ak = agg[k][lane][0], Hk = agg[k][lane][1];
-          carry[0] = __builtin_fmaf(Ak.x, carry[0], Hk.x);
-          carry[1] = __builtin_fmaf(Ak.y, carry[1], Hk.y);
-          carry[2] = __builtin_fmaf(Ak.z, carry[2], Hk.z);
-          carry[3] = __builtin_fmaf(Ak.w, carry[3], Hk.w);
+        // entering state: previous round's carry through segments 0 .. wave-1
+        // (wave is uniform, so the loop bound is scalar)
+        const float4 c0 = fa.carry[(r + 1) & 1][lane];
+        float hin[4] = {c0.x, c0.y, c0.z, c0.w};
+        for (int k = 0; k < wave; ++k) {
+          const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane];
+          hin[0] = __builtin_fmaf(Ak.x, hin[0], Hk.x);
+          hin[1] = __builtin_fmaf(Ak.y, hin[1], Hk.y);
+          hin[2] = __builtin_fmaf(Ak.z, hin[2], Hk.z);
+          hin[3] = __builtin_fmaf(Ak.w, hin[3], Hk.w);
         }
 
         // replay from the entering state
 #pragma unroll
         for (int i = 0; i < TS; ++i) {
           const int row = wave * TS + i;
-          const float4 cv = cur.c4[row][g];
+          const float cq = cur.cq[row][q];
 #pragma unroll
           for (int j = 0; j < 4; ++j) hin[j] = __builtin_fmaf(av[i][j], hin[j], bv[i][j]);
-          float yp = cv.x * hin[0];
-          yp = __builtin_fmaf(cv.y, hin[1], yp);
-          yp = __builtin_fmaf(cv.z, hin[2], yp);
-          yp = __builtin_fmaf(cv.w, hin[3], yp);
-          yp += row_ror<4>(yp);
-          yp += row_ror<8>(yp);
-          if (g == (i & 3)) cur.yt[row][ch] = yp;
+          float yp = quad_bcast<0>(cq) * hin[0];
+          yp = fmac_quad<1>(yp, cq, hin[1]);
+          yp = fmac_quad<2>(yp, cq, hin[2]);
+          yp = fmac_quad<3>(yp, cq, hin[3]);
+          out.yq[g][row][ch] = yp;
+        }
+        // the last segment's end state is the round's carry
+        if (wave == SEG - 1) {
+          fa.carry[r & 1][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) carry[j] = hin[j];
         }
       }
 
       if (r + 1 < rounds) st.commit(nxt);
       __syncthreads();
     }
-    st.store_out(p, b, rounds - 1, tile[(rounds - 1) & 1]);
+    st.store_out(p, rounds - 1, tile[(rounds - 1) & 1], out);
 
     float* h_out = rev ? p.g_first : p.h_last;
-    if (h_out && wave == 0 && ch_ok)
+    if (h_out && wave == SEG - 1 && ch_ok)
       *reinterpret_cast<float4*>(h_out + (b * ED + e) * 16 + 4 * g) = make_float4(carry[0], carry[1], carry[2], carry[3]);
     if (BIDIR) __syncthreads();
   }
@@ -486,6 +547,28 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
   return SSM_OK;
 }
 
+// Extra (dynamic) LDS per workgroup so that the workgroups spread evenly over
+// the compute units. The dispatcher fills a CU up to its resource limit before
+// using the next one, so 768 workgroups that fit 4 per CU would run on 192 of
+// 256 CUs. Padding each workgroup's LDS lowers the per-CU limit to
+// ceil(blocks / CUs) when that is below the natural limit.
+size_t spread_lds(int64_t nblk, size_t lds_static, int max_per_cu) {
+  int dev = 0, ncu = 0, lds_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) return 0;
+  if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+      lds_cu <= 0)
+    return 0;
+  const int64_t natural = std::min<int64_t>(max_per_cu, lds_cu / static_cast<int64_t>(lds_static));
+  const int64_t want = (nblk + ncu - 1) / ncu;
+  if (want >= natural || want <= 0) return 0;
+  // per-workgroup LDS in (lds_cu / (want + 1), lds_cu / want]
+  size_t total = static_cast<size_t>(lds_cu / (want + 1)) + 1024;
+  total = (total + 511) & ~static_cast<size_t>(511);
+  if (total > static_cast<size_t>(lds_cu / want) || total <= lds_static) return 0;
+  return total - lds_static;
+}
+
 template <typename T>
 int launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                 void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
@@ -510,10 +593,16 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.nblocks = static_cast<int>(nblk);
   a.remap = (nblk % 8 == 0) ? 1 : 0;
   constexpr int SEG = 4, TS = 8;
-  if (bidir)
-    hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, true>), dim3(nblk), dim3(64 * SEG), 0, stream, a);
-  else
-    hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, false>), dim3(nblk), dim3(64 * SEG), 0, stream, a);
+  const size_t lds = sizeof(Tile<SEG * TS>) * 2 + sizeof(OutTile<SEG * TS>) + sizeof(FoldArea<SEG>);
+  const size_t dyn = spread_lds(nblk, lds, 16 / SEG);
+  const bool vec = (ED % 4) == 0;
+  if (bidir) {
+    if (vec) hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, true, true>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
+    else hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, true, false>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, false, true>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
+    else hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, false, false>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
