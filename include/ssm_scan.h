@@ -73,10 +73,14 @@ typedef enum {
 
 /*
  * Bytes of device workspace that ssm_scan_fwd (bidir = 0) or
- * ssm_scan_bidir_fwd (bidir = 1) needs for these sizes. Zero means the call
- * may pass workspace = NULL. The workspace needs no initialisation and holds
- * nothing of interest after the call. Returns 0 for invalid sizes too (the
- * call itself then reports the error).
+ * ssm_scan_bidir_fwd (bidir = 1) needs for these sizes on the current
+ * device (the forward scan splits long sequences over more workgroups when
+ * the device has many compute units per channel group, and then needs room
+ * to pass states between them; the bidirectional bf16 scan keeps float32
+ * partial sums). Zero means the call may pass workspace = NULL. The
+ * workspace needs no initialisation and holds nothing of interest after the
+ * call. Returns 0 for invalid sizes too (the call itself then reports the
+ * error).
  */
 size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int bidir);
 

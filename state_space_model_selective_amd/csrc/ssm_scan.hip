@@ -139,6 +139,16 @@ SSM_FMAC_QUAD(3)
 // or 8-byte (bfloat16) aligned and either wholly inside or wholly outside
 // [0, ED); otherwise chunks are loaded and stored element by element.
 // ---------------------------------------------------------------------------
+// Cross-workgroup state of the split-sequence scan (device workspace). A
+// sequence too long for the available channel parallelism is cut into
+// chunks that run concurrently; chunk k hands its inclusive end state to
+// chunk k+1 through `state` and `flag`.
+struct SplitHeader {
+  unsigned ticket;  // dispatch order: chunk-major, so lower chunks start first
+  unsigned err;     // set if a wait gave up (never expected)
+  unsigned pad[62];
+};
+
 template <typename T>
 struct ScanArgs {
   const T* x;
@@ -156,6 +166,12 @@ struct ScanArgs {
   int ngroups;     // channel groups per batch row
   int nblocks;
   int remap;       // spread neighbouring channel groups over one XCD
+  // split sequence (nchunks > 1)
+  int nchunks;
+  int64_t chunk_len;    // multiple of the round length
+  SplitHeader* hdr;
+  int* flag;            // [bg * nchunks + k]
+  float* state;         // [bg * nchunks + k][16 channels][16 states]
 };
 
 // Input tile of one round (double-buffered).
@@ -165,7 +181,7 @@ struct alignas(16) Tile {
   float dx[RT][16];   // delta * x per channel
   float bq[RT][16];   // B_t[n]
   float cq[RT][16];   // C_t[n]
-  float aux[RT][16];  // D x, or (forward sweep of bidir) the reverse sweep's partial
+  float aux[RT][16];  // D x; the reverse sweep's partial (bidir forward sweep); y so far (correction pass)
 };
 
 // Output tile of one round (single-buffered: written by the replay after the
@@ -178,16 +194,20 @@ struct alignas(16) OutTile {
 // Segment aggregates and the carry between rounds.
 template <int SEG>
 struct alignas(16) FoldArea {
-  float4 A[SEG][64];   // prod of a over the segment, per lane's 4 states
-  float4 H[SEG][64];   // state at the segment's end, started from zero
-  float4 carry[2][64]; // state after the round, by round parity
+  float4 A[SEG][64];    // prod of a over the segment, per lane's 4 states
+  float4 H[SEG][64];    // state at the segment's end, started from zero
+  float4 carry[2][64];  // state after the round, by round parity
+  double sd[SEG][64];   // split sequence: sum of delta over each wave's segments
 };
+
+enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
 
 // Staging of one round: each thread owns TPT fixed (row, chunk) tasks of the
 // x/delta tile (4 channels per chunk) or of the B/C tile (4 states per chunk),
 // loads them one round ahead into registers, writes them to the LDS tile, and
 // stores its chunk of the output tile one round later. Offsets advance by one
-// round (RT steps, forward or backward in time) per call.
+// round (RT steps, forward or backward in time) per call. A pass covers the
+// Lk steps starting at time t0 (the whole sequence unless it is split).
 template <typename T, int RT, int TPT, bool BIDIR, bool VEC>
 struct Stager {
   int row[TPT], chk[TPT];
@@ -198,14 +218,12 @@ struct Stager {
   int64_t out_off[TPT];          // element offset of this task's row in the next round to store
   int64_t step_xd, step_bc;      // offset change per round
   int64_t ce0;                   // first channel of the group
-  int64_t ED, L;
+  int64_t ED, Lk;
   bool rev, add_part;
 
-  __device__ __forceinline__ void init(const ScanArgs<T>& p, int tid, int64_t b, int64_t e0) {
+  __device__ __forceinline__ void init(const ScanArgs<T>& p, int tid, int64_t e0) {
     ED = p.ED;
-    L = p.L;
     ce0 = e0;
-    rev = add_part = false;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       int u = tid + k * (8 * RT / TPT);
@@ -219,44 +237,51 @@ struct Stager {
       dval[k] = make_float4(dd && ce + 0 < ED ? p.D[ce + 0] : 0.f, dd && ce + 1 < ED ? p.D[ce + 1] : 0.f,
                             dd && ce + 2 < ED ? p.D[ce + 2] : 0.f, dd && ce + 3 < ED ? p.D[ce + 3] : 0.f);
     }
-    (void)b;
   }
 
-  // start a sweep: round 0 of both prefetch and store
-  __device__ __forceinline__ void begin(int64_t b, bool rev_, bool add_part_) {
+  // start a pass over times [t0, t0 + Lk) (reverse: t0 + Lk - 1 down to t0)
+  __device__ __forceinline__ void begin(int64_t b, int64_t L, int64_t t0, int64_t Lk_, bool rev_, bool add_part_) {
+    Lk = Lk_;
     rev = rev_;
     add_part = add_part_;
     step_xd = (rev ? -RT : RT) * ED;
     step_bc = (rev ? -RT : RT) * 16;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
-      const int64_t t = rev ? (L - 1 - row[k]) : row[k];
+      const int64_t t = rev ? (t0 + Lk - 1 - row[k]) : (t0 + row[k]);
       pre_off[k] = is_xd[k] ? (b * L + t) * ED + ce0 + 4 * chk[k] : (b * L + t) * 16 + 4 * chk[k];
       out_off[k] = pre_off[k];
     }
   }
 
-  // global -> registers for round rr
+  // global -> registers for round rr. STAGE_SCAN: x, delta, B, C (and the
+  // reverse sweep's partial); STAGE_CORRECT: delta, C and the current y.
+  template <int STAGE>
   __device__ __forceinline__ void prefetch(const ScanArgs<T>& p, int64_t rr) {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const int64_t off = pre_off[k];
       pre_off[k] += is_xd[k] ? step_xd : step_bc;
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a;
-      if (rr * RT + row[k] < L && chunk_ok[k]) {
+      if (rr * RT + row[k] < Lk && chunk_ok[k]) {
         if (!is_xd[k]) {
-          a = Vec4<T>::load(p.B + off);
+          if (STAGE == STAGE_SCAN) a = Vec4<T>::load(p.B + off);
           bb = Vec4<T>::load(p.C + off);
         } else if (VEC) {
-          a = Vec4<T>::load(p.x + off);
+          if (STAGE == STAGE_SCAN) a = Vec4<T>::load(p.x + off);
           bb = Vec4<T>::load(p.dl + off);
+          if (STAGE == STAGE_CORRECT) pp = Vec4<T>::load(p.y + off);
           if (BIDIR && add_part) pp = *reinterpret_cast<const float4*>(p.part + off);
         } else {
           const int64_t ce = ce0 + 4 * chk[k];
-          a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
-                          ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
+          if (STAGE == STAGE_SCAN)
+            a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
+                            ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
           bb = make_float4(to_f32(p.dl[off]), ce + 1 < ED ? to_f32(p.dl[off + 1]) : 0.f,
                            ce + 2 < ED ? to_f32(p.dl[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dl[off + 3]) : 0.f);
+          if (STAGE == STAGE_CORRECT)
+            pp = make_float4(to_f32(p.y[off]), ce + 1 < ED ? to_f32(p.y[off + 1]) : 0.f,
+                             ce + 2 < ED ? to_f32(p.y[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.y[off + 3]) : 0.f);
           if (BIDIR && add_part)
             pp = make_float4(p.part[off], ce + 1 < ED ? p.part[off + 1] : 0.f, ce + 2 < ED ? p.part[off + 2] : 0.f,
                              ce + 3 < ED ? p.part[off + 3] : 0.f);
@@ -269,6 +294,7 @@ struct Stager {
   }
 
   // registers -> LDS tile
+  template <int STAGE>
   __device__ __forceinline__ void commit(Tile<RT>& tl) const {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
@@ -276,12 +302,18 @@ struct Stager {
       if (is_xd[k]) {
         const float4 xv = ra[k], dv = rb[k];
         *reinterpret_cast<float4*>(&tl.dt[r][c4]) = dv;
-        *reinterpret_cast<float4*>(&tl.dx[r][c4]) = make_float4(dv.x * xv.x, dv.y * xv.y, dv.z * xv.z, dv.w * xv.w);
-        *reinterpret_cast<float4*>(&tl.aux[r][c4]) =
-            (BIDIR && add_part) ? rp[k]
-                                : make_float4(dval[k].x * xv.x, dval[k].y * xv.y, dval[k].z * xv.z, dval[k].w * xv.w);
+        if (STAGE == STAGE_CORRECT) {
+          *reinterpret_cast<float4*>(&tl.aux[r][c4]) = rp[k];
+        } else {
+          *reinterpret_cast<float4*>(&tl.dx[r][c4]) =
+              make_float4(dv.x * xv.x, dv.y * xv.y, dv.z * xv.z, dv.w * xv.w);
+          *reinterpret_cast<float4*>(&tl.aux[r][c4]) =
+              (BIDIR && add_part)
+                  ? rp[k]
+                  : make_float4(dval[k].x * xv.x, dval[k].y * xv.y, dval[k].z * xv.z, dval[k].w * xv.w);
+        }
       } else {
-        *reinterpret_cast<float4*>(&tl.bq[r][c4]) = ra[k];
+        if (STAGE == STAGE_SCAN) *reinterpret_cast<float4*>(&tl.bq[r][c4]) = ra[k];
         *reinterpret_cast<float4*>(&tl.cq[r][c4]) = rb[k];
       }
     }
@@ -296,7 +328,7 @@ struct Stager {
       const int64_t off = out_off[k];
       out_off[k] += step_xd;
       const int r = row[k], c4 = 4 * chk[k];
-      if (rr * RT + r >= L || !chunk_ok[k]) continue;
+      if (rr * RT + r >= Lk || !chunk_ok[k]) continue;
       const float4 v0 = *reinterpret_cast<const float4*>(&ot.yq[0][r][c4]);
       const float4 v1 = *reinterpret_cast<const float4*>(&ot.yq[1][r][c4]);
       const float4 v2 = *reinterpret_cast<const float4*>(&ot.yq[2][r][c4]);
@@ -325,7 +357,19 @@ struct Stager {
   }
 };
 
-template <typename T, int SEG, int TS, bool BIDIR, bool VEC, int WPE = 3>
+// Wait, bounded, until another workgroup sets *flag; called by one lane.
+__device__ __forceinline__ void wait_flag(int* flag, unsigned* err) {
+  for (unsigned it = 0;; ++it) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+    if (it >= (1u << 26)) {  // ~ seconds: give up rather than hang the device
+      atomicOr(err, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+template <typename T, int SEG, int TS, bool BIDIR, bool VEC, bool SPLIT, int WPE = 3>
 __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE))) void scan_chunked_kernel(
     const ScanArgs<T> p) {
   constexpr int RT = SEG * TS;
@@ -333,10 +377,13 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   constexpr int TPT = (8 * RT) / NT;  // staging tasks per thread
   static_assert(TS % 8 == 0, "TS must be a multiple of 8");
   static_assert(TPT * NT == 8 * RT, "staging tasks must divide evenly");
+  static_assert(!(SPLIT && BIDIR), "the split-sequence scan is forward only");
+  static_assert(!SPLIT || SEG > 1, "the split-sequence scan needs several segments");
 
   __shared__ Tile<RT> tile[2];
   __shared__ OutTile<RT> out;
   __shared__ FoldArea<SEG> fa;
+  __shared__ int s_ticket;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -344,13 +391,27 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int q = lane & 15;
   const int g = q >> 2;
   const int ch = ((lane >> 4) << 2) | (q & 3);
-
-  int blk = blockIdx.x;
-  if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
-  const int64_t b = blk / p.ngroups;
-  const int64_t e0 = static_cast<int64_t>(blk % p.ngroups) * 16;
   const int64_t L = p.L, ED = p.ED;
-  const int64_t rounds = (L + RT - 1) / RT;
+
+  // which (batch row, channel group) and which chunk of the sequence
+  int64_t bg, kchunk = 0, t0 = 0, Lk = L;
+  if constexpr (SPLIT) {
+    if (tid == 0) s_ticket = static_cast<int>(atomicAdd(&p.hdr->ticket, 1u));
+    __syncthreads();
+    const int64_t tk = s_ticket;
+    const int64_t nbg = p.nblocks / p.nchunks;
+    kchunk = tk / nbg;
+    bg = tk % nbg;
+    t0 = kchunk * p.chunk_len;
+    Lk = L - t0 < p.chunk_len ? L - t0 : p.chunk_len;
+  } else {
+    int blk = blockIdx.x;
+    if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
+    bg = blk;
+  }
+  const int64_t b = bg / p.ngroups;
+  const int64_t e0 = (bg % p.ngroups) * 16;
+  const int64_t rounds = (Lk + RT - 1) / RT;
 
   // this lane's channel and states
   const int64_t e = e0 + ch;
@@ -361,22 +422,25 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   for (int j = 0; j < 4; ++j) A2[j] = p.A[ec * 16 + 4 * g + j] * kLog2e;
 
   Stager<T, RT, TPT, BIDIR, VEC> st;
-  st.init(p, tid, b, e0);
+  st.init(p, tid, e0);
+  double sd_total = 0.0;  // split sequence: sum of delta over this wave's segments
+  float carry[4];         // state after the last completed round (valid in wave SEG-1)
 
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
     const bool rev = BIDIR && sweep == 0;
-    st.begin(b, rev, BIDIR && sweep == 1);
-    float carry[4] = {0.f, 0.f, 0.f, 0.f};
+    st.begin(b, L, t0, Lk, rev, BIDIR && sweep == 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) carry[j] = 0.f;
     if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    st.prefetch(p, 0);
-    st.commit(tile[0]);
+    st.template prefetch<STAGE_SCAN>(p, 0);
+    st.template commit<STAGE_SCAN>(tile[0]);
     __syncthreads();
 
     for (int64_t r = 0; r < rounds; ++r) {
       Tile<RT>& cur = tile[r & 1];
       Tile<RT>& nxt = tile[(r + 1) & 1];
-      if (r + 1 < rounds) st.prefetch(p, r + 1);
+      if (r + 1 < rounds) st.template prefetch<STAGE_SCAN>(p, r + 1);
       // output of round r-1, whose input tile stays intact until this round's commit
       if (r >= 1) st.store_out(p, r - 1, nxt, out);
 
@@ -418,6 +482,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
             hl[j] = __builtin_fmaf(av[i][j], hl[j], bv[i][j]);
           }
         }
+        if (SPLIT) sd_total += static_cast<double>(sd);
         fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
                                        __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
         fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
@@ -456,15 +521,109 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
         }
       }
 
-      if (r + 1 < rounds) st.commit(nxt);
+      if (r + 1 < rounds) st.template commit<STAGE_SCAN>(nxt);
       __syncthreads();
     }
     st.store_out(p, rounds - 1, tile[(rounds - 1) & 1], out);
 
-    float* h_out = rev ? p.g_first : p.h_last;
-    if (h_out && wave == SEG - 1 && ch_ok)
-      *reinterpret_cast<float4*>(h_out + (b * ED + e) * 16 + 4 * g) = make_float4(carry[0], carry[1], carry[2], carry[3]);
-    if (BIDIR) __syncthreads();
+    if constexpr (!SPLIT) {
+      float* h_out = rev ? p.g_first : p.h_last;
+      if (h_out && wave == SEG - 1 && ch_ok)
+        *reinterpret_cast<float4*>(h_out + (b * ED + e) * 16 + 4 * g) =
+            make_float4(carry[0], carry[1], carry[2], carry[3]);
+      if (BIDIR) __syncthreads();
+    }
+  }
+
+  if constexpr (SPLIT) {
+    // ---- hand the chunk's end state to the next chunk -------------------
+    // chunk aggregate: prod of a over the chunk = exp2(A log2e * sum delta),
+    // the sum taken in float64 over all waves' segments
+    fa.sd[wave][lane] = sd_total;
+    __syncthreads();
+    const int64_t slot = bg * p.nchunks + kchunk;
+    float hin[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave == SEG - 1) {
+      double sum = 0.0;
+#pragma unroll
+      for (int s = 0; s < SEG; ++s) sum += fa.sd[s][lane];
+      const float sdc = static_cast<float>(sum);
+      float incl[4] = {carry[0], carry[1], carry[2], carry[3]};
+      if (kchunk > 0) {
+        if (lane == 0) wait_flag(p.flag + slot - 1, &p.hdr->err);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const float4 v = *reinterpret_cast<const float4*>(p.state + (slot - 1) * 256 + ch * 16 + 4 * g);
+        hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) incl[j] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[j] * sdc), hin[j], carry[j]);
+      }
+      if (kchunk + 1 < p.nchunks) {
+        *reinterpret_cast<float4*>(p.state + slot * 256 + ch * 16 + 4 * g) =
+            make_float4(incl[0], incl[1], incl[2], incl[3]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) __hip_atomic_store(p.flag + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (p.h_last && ch_ok) {
+        *reinterpret_cast<float4*>(p.h_last + (b * ED + e) * 16 + 4 * g) =
+            make_float4(incl[0], incl[1], incl[2], incl[3]);
+      }
+      fa.carry[0][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
+    }
+    if (kchunk == 0) return;  // uniform across the workgroup
+    __syncthreads();
+    {
+      const float4 v = fa.carry[0][lane];
+      hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
+    }
+
+    // ---- correction: y_t += sum_n C_t[n] (prod_{s <= t} a_s[n]) h_in[n] ----
+    // over the chunk from its start, with prod a = exp2(A log2e * cumulative
+    // delta) (float64 running sum). Once every carried product is exactly zero
+    // it stays zero if delta >= 0 and A <= 0 (checked as we go), and the pass
+    // stops there: the remaining terms are exact zeros.
+    bool mono = A2[0] <= 0.f && A2[1] <= 0.f && A2[2] <= 0.f && A2[3] <= 0.f;
+    double base = 0.0;  // cumulative delta before the current round
+    st.begin(b, L, t0, Lk, false, false);
+    st.template prefetch<STAGE_CORRECT>(p, 0);
+    st.template commit<STAGE_CORRECT>(tile[0]);
+    __syncthreads();
+    for (int64_t r = 0; r < rounds; ++r) {
+      Tile<RT>& cur = tile[r & 1];
+      Tile<RT>& nxt = tile[(r + 1) & 1];
+      if (r + 1 < rounds) st.template prefetch<STAGE_CORRECT>(p, r + 1);
+      if (r >= 1) st.store_out(p, r - 1, nxt, out);
+      __syncthreads();  // the output tile is reused below
+      float pre = 0.f;  // delta of the round's rows before this wave's segment
+      for (int i = 0; i < wave * TS; ++i) pre += cur.dt[i][ch];
+      bool alive = false;
+#pragma unroll
+      for (int i = 0; i < TS; ++i) {
+        const int row = wave * TS + i;
+        const float dt = cur.dt[row][ch];
+        mono = mono && dt >= 0.f;
+        pre += dt;
+        const float cum = static_cast<float>(base + static_cast<double>(pre));
+        float w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_exp2f(A2[j] * cum) * hin[j];
+        alive = alive || w[0] != 0.f || w[1] != 0.f || w[2] != 0.f || w[3] != 0.f;
+        const float cq = cur.cq[row][q];
+        float yp = quad_bcast<0>(cq) * w[0];
+        yp = fmac_quad<1>(yp, cq, w[1]);
+        yp = fmac_quad<2>(yp, cq, w[2]);
+        yp = fmac_quad<3>(yp, cq, w[3]);
+        out.yq[g][row][ch] = yp;
+      }
+      float rest = 0.f;  // rows after this wave's segment
+      for (int i = (wave + 1) * TS; i < RT; ++i) rest += cur.dt[i][ch];
+      base += static_cast<double>(pre + rest);
+      if (r + 1 < rounds) st.template commit<STAGE_CORRECT>(nxt);
+      const int go_on = __syncthreads_or((alive || !mono) ? 1 : 0);
+      if (!go_on) {
+        st.store_out(p, r, cur, out);
+        return;
+      }
+    }
+    st.store_out(p, rounds - 1, tile[(rounds - 1) & 1], out);
   }
 }
 
@@ -505,12 +664,55 @@ int check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, Sizes* 
   return SSM_OK;
 }
 
+// Kernel configuration: SEG waves per workgroup, TS steps per wave per round.
+constexpr int kSEG = 4, kTS = 8, kRT = kSEG * kTS;
+
+int device_cus() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return ncu;
+}
+
+// How the forward scan splits a sequence across workgroups: when there are
+// fewer than two (batch row, 16-channel group) pairs per compute unit, cut
+// the sequence into chunks (each at least 16 rounds long) so that about three
+// workgroups per CU are in flight.
+struct SplitPlan {
+  int64_t nbg;        // (batch row, channel group) pairs
+  int64_t nchunks;    // 1: no split
+  int64_t chunk_len;
+  size_t flag_off, state_off, bytes;  // workspace layout
+};
+
+SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
+  SplitPlan sp{};
+  sp.nbg = Bs * ((ED + 15) / 16);
+  sp.nchunks = 1;
+  sp.chunk_len = L;
+  if (!bidir && ncu > 0 && sp.nbg < 2 * static_cast<int64_t>(ncu)) {
+    const int64_t want = (3 * static_cast<int64_t>(ncu) + sp.nbg - 1) / sp.nbg;
+    const int64_t k = std::min<int64_t>(want, L / (16 * kRT));
+    if (k >= 2) {
+      const int64_t len = ((L + k - 1) / k + kRT - 1) / kRT * kRT;
+      sp.chunk_len = len;
+      sp.nchunks = (L + len - 1) / len;
+    }
+  }
+  if (sp.nchunks > 1) {
+    sp.flag_off = sizeof(SplitHeader);
+    sp.state_off = (sp.flag_off + static_cast<size_t>(sp.nbg * sp.nchunks) * 4 + 255) & ~static_cast<size_t>(255);
+    sp.bytes = sp.state_off + static_cast<size_t>(sp.nbg * sp.nchunks) * 256 * 4;
+  }
+  return sp;
+}
+
 size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int bidir) {
   Sizes s;
   if (check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK) return 0;
   // the bidirectional bf16 scan keeps its reverse-time partial sums in float32
   if (bidir && dtype == SSM_BF16) return static_cast<size_t>(s.seq) * 4;
-  return 0;
+  return plan_split(Bs, L, ED, bidir, device_cus()).bytes;
 }
 
 Range rng(const void* p, int64_t bytes) {
@@ -569,12 +771,27 @@ size_t spread_lds(int64_t nblk, size_t lds_static, int max_per_cu) {
   return total - lds_static;
 }
 
+// Clears the split-sequence workspace header and flags (a kernel rather than
+// a memset, so the call stays safe to capture in a graph).
+__global__ void zero_words_kernel(unsigned* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+template <typename T, bool BIDIR, bool VEC, bool SPLIT>
+void launch_one(const ScanArgs<T>& a, int64_t nblk, size_t dyn, hipStream_t stream) {
+  hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT>), dim3(nblk), dim3(64 * kSEG), dyn, stream,
+                     a);
+}
+
 template <typename T>
 int launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                 void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
                 hipStream_t stream) {
   const int64_t ngroups = (ED + 15) / 16;
-  const int64_t nblk = Bs * ngroups;
+  const SplitPlan sp = plan_split(Bs, L, ED, bidir, device_cus());
+  const int64_t nblk = sp.nbg * sp.nchunks;
   if (nblk > INT32_MAX / 2) return SSM_ERR_DIM;
   ScanArgs<T> a;
   a.x = static_cast<const T*>(x);
@@ -592,16 +809,33 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.ngroups = static_cast<int>(ngroups);
   a.nblocks = static_cast<int>(nblk);
   a.remap = (nblk % 8 == 0) ? 1 : 0;
-  constexpr int SEG = 4, TS = 8;
-  const size_t lds = sizeof(Tile<SEG * TS>) * 2 + sizeof(OutTile<SEG * TS>) + sizeof(FoldArea<SEG>);
-  const size_t dyn = spread_lds(nblk, lds, 16 / SEG);
+  a.nchunks = static_cast<int>(sp.nchunks);
+  a.chunk_len = sp.chunk_len;
+  a.hdr = nullptr;
+  a.flag = nullptr;
+  a.state = nullptr;
+  const bool split = sp.nchunks > 1;
+  if (split) {
+    char* w = static_cast<char*>(ws);
+    a.hdr = reinterpret_cast<SplitHeader*>(w);
+    a.flag = reinterpret_cast<int*>(w + sp.flag_off);
+    a.state = reinterpret_cast<float*>(w + sp.state_off);
+    const int64_t words = static_cast<int64_t>(sp.state_off / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(std::min<int64_t>((words + 255) / 256, 1024))),
+                       dim3(256), 0, stream, reinterpret_cast<unsigned*>(w), words);
+  }
+  const size_t lds = sizeof(Tile<kRT>) * 2 + sizeof(OutTile<kRT>) + sizeof(FoldArea<kSEG>) + 16;
+  const size_t dyn = spread_lds(nblk, lds, 16 / kSEG);
   const bool vec = (ED % 4) == 0;
   if (bidir) {
-    if (vec) hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, true, true>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
-    else hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, true, false>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
+    if (vec) launch_one<T, true, true, false>(a, nblk, dyn, stream);
+    else launch_one<T, true, false, false>(a, nblk, dyn, stream);
+  } else if (split) {
+    if (vec) launch_one<T, false, true, true>(a, nblk, dyn, stream);
+    else launch_one<T, false, false, true>(a, nblk, dyn, stream);
   } else {
-    if (vec) hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, false, true>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
-    else hipLaunchKernelGGL((scan_chunked_kernel<T, SEG, TS, false, false>), dim3(nblk), dim3(64 * SEG), dyn, stream, a);
+    if (vec) launch_one<T, false, true, false>(a, nblk, dyn, stream);
+    else launch_one<T, false, false, false>(a, nblk, dyn, stream);
   }
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }

@@ -77,3 +77,40 @@ def test_on_a_side_stream():
         y, _, _ = run_gpu(inp, stream=s)
     y_ref, _, _ = oracle.scan(**inp)
     assert_close("y", y, y_ref, TOL["f32"])
+
+
+# ---- sequences split across workgroups (few channels, long L) ----------------
+# With fewer than two (batch row, 16-channel group) pairs per compute unit the
+# forward scan cuts the sequence into chunks that hand their end states on and
+# correct the start of their output. These shapes take that path.
+
+@pytest.mark.parametrize("Bs,L,ED,dtype", [(1, 3000, 64, "f32"), (1, 5000, 40, "f32"), (2, 4096, 32, "bf16"),
+                                           (1, 20000, 128, "f32")])
+def test_split_sequence(Bs, L, ED, dtype):
+    check_full(Bs, L, ED, dtype=dtype, seed=L + ED)
+
+
+def test_split_sequence_slow_decay_and_no_decay():
+    # tiny step sizes (the carried state decays over the whole chunk) and
+    # A = 0 for some states (no decay at all): the correction runs to the end
+    log("case split, slow decay")
+    inp = synth.make_inputs(1, 6000, 64, 16, "f32", seed=21)
+    inp["delta"] = (inp["delta"] * 1e-3).astype(np.float32)
+    inp["A"][:, :3] = 0.0
+    y, h, _ = run_gpu(inp, want_h=True)
+    y_ref, h_ref, _ = oracle.scan(**inp, want_h_last=True)
+    assert_close("y", y, y_ref, TOL["f32"])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+
+
+def test_split_sequence_negative_steps():
+    # raw step sizes may be negative (the pages pass randn): the early stop of
+    # the correction must not trigger then
+    log("case split, mixed-sign delta")
+    inp = synth.make_inputs(1, 4000, 64, 16, "f32", seed=22)
+    sign = np.where(synth.uniform(22, 9, inp["delta"].shape, 0, 1) < 0.1, -1.0, 1.0).astype(np.float32)
+    inp["delta"] = (inp["delta"] * sign).astype(np.float32)
+    y, h, _ = run_gpu(inp, want_h=True)
+    y_ref, h_ref, _ = oracle.scan(**inp, want_h_last=True)
+    assert_close("y", y, y_ref, TOL["f32"])
+    assert_close("h_last", h, h_ref, TOL["f32"])
