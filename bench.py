@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU-baseline leg")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the scan, run plain device copies of MIB MiB (a known-size reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and print their size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,6 +112,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_per_launch": n * 4, "launches": args.steps}))
+        return
 
     import state_space_model_selective_amd as ssm
     import synth
@@ -151,18 +164,19 @@ def main():
         step(sets[i % nsets])
     torch.cuda.synchronize()
 
-    # timed region: K steps, one launch sequence each, events around each step
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: K steps back to back, HIP events on the launch stream at
+    # its two ends; the per-launch kernel time is the region time over K
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(sets[i % nsets])
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     E = Bs * L * ED * N

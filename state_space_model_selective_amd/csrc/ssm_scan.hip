@@ -144,9 +144,8 @@ SSM_FMAC_QUAD(3)
 // chunks that run concurrently; chunk k hands its inclusive end state to
 // chunk k+1 through `state` and `flag`.
 struct SplitHeader {
-  unsigned ticket;  // dispatch order: chunk-major, so lower chunks start first
   unsigned err;     // set if a wait gave up (never expected)
-  unsigned pad[62];
+  unsigned pad[63];
 };
 
 template <typename T>
@@ -383,7 +382,6 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   __shared__ Tile<RT> tile[2];
   __shared__ OutTile<RT> out;
   __shared__ FoldArea<SEG> fa;
-  __shared__ int s_ticket;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -393,21 +391,20 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int ch = ((lane >> 4) << 2) | (q & 3);
   const int64_t L = p.L, ED = p.ED;
 
-  // which (batch row, channel group) and which chunk of the sequence
-  int64_t bg, kchunk = 0, t0 = 0, Lk = L;
+  // which (batch row, channel group) and, for a split sequence, which chunk.
+  // Consecutive logical blocks share an XCD (its L2 serves the cache lines
+  // that neighbouring channel groups share); the split sequence numbers its
+  // blocks chunk-major. Every block of a split launch is resident at once
+  // (the host bounds the grid), so a chunk can wait for its predecessor.
+  int blk = blockIdx.x;
+  if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
+  int64_t bg = blk, kchunk = 0, t0 = 0, Lk = L;
   if constexpr (SPLIT) {
-    if (tid == 0) s_ticket = static_cast<int>(atomicAdd(&p.hdr->ticket, 1u));
-    __syncthreads();
-    const int64_t tk = s_ticket;
     const int64_t nbg = p.nblocks / p.nchunks;
-    kchunk = tk / nbg;
-    bg = tk % nbg;
+    kchunk = blk / nbg;
+    bg = blk % nbg;
     t0 = kchunk * p.chunk_len;
     Lk = L - t0 < p.chunk_len ? L - t0 : p.chunk_len;
-  } else {
-    int blk = blockIdx.x;
-    if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
-    bg = blk;
   }
   const int64_t b = bg / p.ngroups;
   const int64_t e0 = (bg % p.ngroups) * 16;
@@ -674,10 +671,34 @@ int device_cus() {
   return ncu;
 }
 
+// Workgroups of the split-sequence kernel that fit on one CU at once (the
+// smallest over its instantiations), 0 if the runtime cannot tell.
+int split_blocks_per_cu() {
+  int best = 1 << 30;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<float, kSEG, kTS, false, true, true>,
+                                                   64 * kSEG, 0) != hipSuccess)
+    return 0;
+  best = std::min(best, n);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<float, kSEG, kTS, false, false, true>,
+                                                   64 * kSEG, 0) != hipSuccess)
+    return 0;
+  best = std::min(best, n);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<uint16_t, kSEG, kTS, false, true, true>,
+                                                   64 * kSEG, 0) != hipSuccess)
+    return 0;
+  best = std::min(best, n);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<uint16_t, kSEG, kTS, false, false, true>,
+                                                   64 * kSEG, 0) != hipSuccess)
+    return 0;
+  return std::min(best, n);
+}
+
 // How the forward scan splits a sequence across workgroups: when there are
 // fewer than two (batch row, 16-channel group) pairs per compute unit, cut
 // the sequence into chunks (each at least 16 rounds long) so that about three
-// workgroups per CU are in flight.
+// workgroups per CU are in flight, and never more than fit on the device at
+// once (a chunk waits for its predecessor, which must therefore be running).
 struct SplitPlan {
   int64_t nbg;        // (batch row, channel group) pairs
   int64_t nchunks;    // 1: no split
@@ -691,7 +712,8 @@ SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
   sp.nchunks = 1;
   sp.chunk_len = L;
   if (!bidir && ncu > 0 && sp.nbg < 2 * static_cast<int64_t>(ncu)) {
-    const int64_t want = (3 * static_cast<int64_t>(ncu) + sp.nbg - 1) / sp.nbg;
+    const int64_t per_cu = std::min<int64_t>(3, split_blocks_per_cu());  // workgroups resident per CU
+    const int64_t want = per_cu * static_cast<int64_t>(ncu) / sp.nbg;
     const int64_t k = std::min<int64_t>(want, L / (16 * kRT));
     if (k >= 2) {
       const int64_t len = ((L + k - 1) / k + kRT - 1) / kRT * kRT;
