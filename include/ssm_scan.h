@@ -12,8 +12,9 @@
  *   h_t[n]   = a_t[n] * h_{t-1}[n] + (delta[b,t,e] * x[b,t,e]) * B[b,t,n],   h_{-1} = 0
  *   y[b,t,e] = sum_n C[b,t,n] * h_t[n] + D[e] * x[b,t,e]
  *
- * delta is used as given (no softplus, bias or clamp) and the initial state is
- * zero; the pages pass neither.
+ * delta is used as given (no softplus, bias or clamp). The initial state is
+ * zero unless an h0 is passed: then h_{-1} = h0, which resumes a sequence
+ * from a carried state (pass the h_last of the previous piece).
  *
  * The bidirectional variant follows "Some questions of Bi-Mamba2 and Hydra"
  * (Hprairie/Bi-Mamba2 issue 1), the author's first reply: the sum of two SSMs
@@ -90,23 +91,25 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
  *   A        : (ED, N) float32             -- state matrix (diagonal per channel)
  *   B, C     : (Bs, L, N) of dtype         -- input and output projections
  *   D        : (ED) float32, or NULL (treated as zero)
+ *   h0       : (Bs, ED, N) float32, or NULL -- initial state h_{-1} (zero if NULL)
  *   y        : (Bs, L, ED) of dtype        -- output, written in full
  *   h_last   : (Bs, ED, N) float32, or NULL -- state after the last step
  * Returns SSM_OK once the kernels are enqueued, else the first error found.
  */
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED, int64_t N,
-                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+                 const float* D, const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED,
+                 int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bidirectional selective scan (forward plus reverse-time scan plus D x).
- * Arguments as ssm_scan_fwd, and
+ * Arguments as ssm_scan_fwd (h0 initialises the forward direction; the
+ * reverse direction starts from zero at t = L-1), and
  *   h_last  : (Bs, ED, N) float32 or NULL -- forward state after t = L-1
  *   g_first : (Bs, ED, N) float32 or NULL -- reverse state after t = 0
  */
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L,
-                       int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                       const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs,
+                       int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
 
 /* Static description of a status code (never NULL). */

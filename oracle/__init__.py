@@ -37,7 +37,7 @@ def lib():
             build()
         L = ctypes.CDLL(_SO)
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
-        L.oracle_scan.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+        L.oracle_scan.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                   i64, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         L.oracle_scan.restype = ctypes.c_int
         _lib = L
@@ -54,13 +54,14 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def scan(x, delta, A, B, C, D=None, *, bidir=False, chans=None, want_h_last=False,
+def scan(x, delta, A, B, C, D=None, *, h0=None, bidir=False, chans=None, want_h_last=False,
          want_g_first=False, nthreads=None):
     """Run the oracle.
 
     x, delta: (Bs, L, ED); B, C: (Bs, L, N) -- float32, or uint16 bf16 bit
     patterns (all four the same dtype). A: (ED, N) float32; D: (ED,) float32
-    or None. chans: optional int64 array of channel ids b*ED + e.
+    or None. h0: optional (Bs, ED, N) float32 initial forward state (zero if
+    None). chans: optional int64 array of channel ids b*ED + e.
 
     Returns (y, h_last, g_first): y is (Bs, L, ED) float64 when chans is None,
     else (len(chans), L) channel-major; h_last / g_first are (Bs, ED, N) or
@@ -72,6 +73,7 @@ def scan(x, delta, A, B, C, D=None, *, bidir=False, chans=None, want_h_last=Fals
     C = np.ascontiguousarray(C)
     A = np.ascontiguousarray(A, dtype=np.float32)
     D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
     if x.dtype == np.uint16:
         dtype = BF16
     elif x.dtype == np.float32:
@@ -85,6 +87,7 @@ def scan(x, delta, A, B, C, D=None, *, bidir=False, chans=None, want_h_last=Fals
     N = A.shape[1]
     assert delta.shape == x.shape and B.shape == (Bs, L, N) and C.shape == (Bs, L, N)
     assert A.shape == (ED, N) and (D is None or D.shape == (ED,))
+    assert h0 is None or h0.shape == (Bs, ED, N)
     if chans is not None:
         chans = np.ascontiguousarray(chans, dtype=np.int64)
         nch = chans.size
@@ -94,7 +97,7 @@ def scan(x, delta, A, B, C, D=None, *, bidir=False, chans=None, want_h_last=Fals
     h = np.empty((nch, N), dtype=np.float64) if want_h_last else None
     g = np.empty((nch, N), dtype=np.float64) if (want_g_first and bidir) else None
     rc = lib().oracle_scan(dtype, int(bool(bidir)), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                           _ptr(D), Bs, L, ED, N, _ptr(chans), nch, _ptr(y), _ptr(h), _ptr(g),
+                           _ptr(D), _ptr(h0), Bs, L, ED, N, _ptr(chans), nch, _ptr(y), _ptr(h), _ptr(g),
                            _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_scan failed with code %d" % rc)

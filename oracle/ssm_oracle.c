@@ -16,6 +16,10 @@
  *     a_t[n] = exp(delta[b,t,e] * A[e,n])
  *     h_t[n] = a_t[n] * h_{t-1}[n] + (delta[b,t,e] * x[b,t,e]) * B[b,t,n],  h_{-1} = 0
  *     y[b,t,e] = sum_n C[b,t,n] * h_t[n] + D[e] * x[b,t,e]
+ *   Initial state: h_{-1} = 0, or h0[b,e,n] when an initial state is given
+ *   (resuming a sequence from a carried state; the chunked forward of
+ *   "Some questions of Bi-Mamba2 and Hydra" returns per-direction final
+ *   states for exactly this use).
  *   Final state h_last[b,e,n] = h_{L-1}[n] (the forward scan's final state,
  *   as the Bi-Mamba2 forward returns per direction: "Some questions of
  *   Bi-Mamba2 and Hydra", the MambaChunkScanCombinedFn.forward listing).
@@ -51,6 +55,7 @@ typedef struct {
   int dtype, bidir;
   const void *x, *delta, *B, *C;
   const float *A, *D;
+  const float* h0; /* (Bs, ED, N) initial forward state, or NULL for zero */
   int64_t Bs, L, ED, N;
   const int64_t* chans; /* channel ids c = b*ED + e, or NULL for all */
   int64_t nchans;
@@ -67,7 +72,7 @@ static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
   const int64_t L = w->L, ED = w->ED, N = w->N;
   double* y = w->y + k * L;
 
-  for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+  for (int64_t n = 0; n < N; ++n) h[n] = w->h0 ? (double)w->h0[(b * ED + e) * N + n] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
     const int64_t ix = (b * L + t) * ED + e; /* x, delta index */
     const int64_t ib = (b * L + t) * N;      /* B, C row index */
@@ -127,7 +132,7 @@ static void* worker(void* p) {
  * -1 on bad arguments, -2 when memory for a worker could not be allocated.
  */
 int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const float* A, const void* B,
-                const void* C, const float* D, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                const void* C, const float* D, const float* h0, int64_t Bs, int64_t L, int64_t ED, int64_t N,
                 const int64_t* chans, int64_t nchans, double* y, double* h_last, double* g_first,
                 int nthreads) {
   if (!x || !delta || !A || !B || !C || !y) return -1;
@@ -141,7 +146,7 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
   if (nthreads > 256) nthreads = 256;
   if (nthreads > nchans) nthreads = (int)(nchans > 0 ? nchans : 1);
 
-  work_t base = {dtype, bidir, x, delta, B, C, A, D, Bs, L, ED, N, chans, nchans, y, h_last,
+  work_t base = {dtype, bidir, x, delta, B, C, A, D, h0, Bs, L, ED, N, chans, nchans, y, h_last,
                  bidir ? g_first : NULL, 0, 0};
   work_t* ws = (work_t*)malloc(sizeof(work_t) * (size_t)nthreads);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);

@@ -59,9 +59,9 @@ def lib():
         vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
         L.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_workspace_bytes.restype = sz
-        L.ssm_scan_fwd.argtypes = [vp] * 8 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_fwd.argtypes = [vp] * 9 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_fwd.restype = ci
-        L.ssm_scan_bidir_fwd.argtypes = [vp] * 9 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_fwd.argtypes = [vp] * 10 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
@@ -113,10 +113,11 @@ def _stream(x, stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None, stream=None):
-    """y = selective_scan(x, delta, A, B, C, D); optionally the final state into h_last."""
+def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None, stream=None, h0=None):
+    """y = selective_scan(x, delta, A, B, C, D) from initial state h0 (zero if None);
+    optionally the final state into h_last."""
     dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, False, workspace)
-    rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), _ptr(h_last),
+    rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_last),
                             Bs, L, ED, N, dt, _ptr(workspace), ws_bytes, _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_fwd")
@@ -124,10 +125,11 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None,
 
 
 def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=None, workspace=None,
-                       stream=None):
-    """y = forward scan + reverse-time scan (shared weights, read in place) + D x."""
+                       stream=None, h0=None):
+    """y = forward scan (from h0, zero if None) + reverse-time scan (shared
+    weights, read in place) + D x."""
     dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, True, workspace)
-    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
                                   _ptr(h_last), _ptr(g_first), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
                                   _stream(x, stream))
     if rc != SSM_OK:

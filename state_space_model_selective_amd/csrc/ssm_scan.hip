@@ -156,6 +156,7 @@ struct ScanArgs {
   const T* B;
   const T* C;
   const float* D;
+  const float* h0;  // initial forward state (Bs, ED, N) or nullptr for zero
   T* y;
   float* part;     // bidir: float32 partials of the reverse sweep (may alias y)
   float* h_last;   // forward final state or nullptr
@@ -426,9 +427,11 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
     const bool rev = BIDIR && sweep == 0;
     st.begin(b, L, t0, Lk, rev, BIDIR && sweep == 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) carry[j] = 0.f;
-    if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // entering state: h0 for the forward sweep's first chunk, else zero
+    float4 init = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.h0 && !rev && kchunk == 0 && ch_ok) init = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
+    carry[0] = init.x, carry[1] = init.y, carry[2] = init.z, carry[3] = init.w;
+    if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = init;
 
     st.template prefetch<STAGE_SCAN>(p, 0);
     st.template commit<STAGE_SCAN>(tile[0]);
@@ -743,19 +746,20 @@ Range rng(const void* p, int64_t bytes) {
 }
 
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-             const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
+             const float* h0, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
              int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s) {
   if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
   int rc = check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
-  const void* ptrs[] = {x, delta, A, B, C, D, y, h_last, g_first, ws};
+  const void* ptrs[] = {x, delta, A, B, C, D, h0, y, h_last, g_first, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSM_ERR_UNSUPPORTED;
   size_t need = workspace_bytes(Bs, L, ED, N, dtype, bidir);
   if (need > 0 && (!ws || ws_bytes < need)) return SSM_ERR_WORKSPACE;
 
   Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
-                rng(B, s->bc * s->elem), rng(C, s->bc * s->elem), rng(D, D ? ED * 4 : 0)};
+                rng(B, s->bc * s->elem), rng(C, s->bc * s->elem), rng(D, D ? ED * 4 : 0),
+                rng(h0, h0 ? s->state * 4 : 0)};
   Range out[4];
   int nout = 0;
   out[nout++] = rng(y, s->seq * s->elem);
@@ -809,7 +813,7 @@ void launch_one(const ScanArgs<T>& a, int64_t nblk, size_t dyn, hipStream_t stre
 
 template <typename T>
 int launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
+                const float* h0, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
                 hipStream_t stream) {
   const int64_t ngroups = (ED + 15) / 16;
   const SplitPlan sp = plan_split(Bs, L, ED, bidir, device_cus());
@@ -822,6 +826,7 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.B = static_cast<const T*>(B);
   a.C = static_cast<const T*>(C);
   a.D = D;
+  a.h0 = h0;
   a.y = static_cast<T*>(y);
   a.part = bidir ? (std::is_same<T, float>::value ? reinterpret_cast<float*>(y) : static_cast<float*>(ws)) : nullptr;
   a.h_last = h_last;
@@ -862,16 +867,17 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
-int run(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D, void* y,
+int run(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+        const float* h0, void* y,
         float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* ws,
         size_t ws_bytes, void* stream, int bidir) {
   Sizes s;
-  int rc = validate(x, delta, A, B, C, D, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
+  int rc = validate(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SSM_F32)
-    return launch_scan<float>(x, delta, A, B, C, D, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
-  return launch_scan<uint16_t>(x, delta, A, B, C, D, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+    return launch_scan<float>(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
 }
 
 }  // namespace
@@ -883,15 +889,15 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
 }
 
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
-  return run(x, delta, A, B, C, D, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 0);
+                 const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 0);
 }
 
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED,
-                       int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return run(x, delta, A, B, C, D, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
+                       const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L,
+                       int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
 }
 
 const char* ssm_status_str(int status) {

@@ -38,7 +38,7 @@ def y_to_numpy(y):
     return y.double().cpu().numpy()
 
 
-def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False):
+def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False, h0=None):
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -48,11 +48,12 @@ def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=Fa
     h = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev) if want_h else None
     g = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev) if want_g else None
     D = None if D_none else t["D"]
+    h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, dtype=np.float32)).to(dev)
     if bidir:
         y = ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, g_first=g,
-                                   stream=stream)
+                                   stream=stream, h0=h0t)
     else:
-        y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, stream=stream)
+        y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, stream=stream, h0=h0t)
     torch.cuda.synchronize()
     return (y_to_numpy(y), None if h is None else h.double().cpu().numpy(),
             None if g is None else g.double().cpu().numpy())

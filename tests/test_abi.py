@@ -37,20 +37,21 @@ def test_status_strings():
 
 
 def fwd(**kw):
-    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], Bs=2, L=64, ED=64, N=16,
-                dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], h0=P[10], Bs=2, L=64, ED=64,
+                N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
     args.update(kw)
-    return ssm.lib().ssm_scan_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["y"],
+    return ssm.lib().ssm_scan_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["h0"],
+                                  args["y"],
                                   args["h"], args["Bs"], args["L"], args["ED"], args["N"], args["dtype"], args["ws"],
                                   args["ws_bytes"], None)
 
 
 def bidir(**kw):
-    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], Bs=2, L=64, ED=64,
-                N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], h0=P[10], Bs=2,
+                L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
     args.update(kw)
     return ssm.lib().ssm_scan_bidir_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"],
-                                        args["y"], args["h"], args["g"], args["Bs"], args["L"], args["ED"],
+                                        args["h0"], args["y"], args["h"], args["g"], args["Bs"], args["L"], args["ED"],
                                         args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -80,9 +81,9 @@ def test_unknown_dtype():
     assert fwd(dtype=7) == ssm.SSM_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "y", "h"])
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "y", "h", "h0"])
 def test_misaligned_pointer(name):
-    base = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7])
+    base = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], h0=P[10])
     assert fwd(**{name: base[name] + 4}) == ssm.SSM_ERR_UNSUPPORTED
 
 
@@ -91,6 +92,7 @@ def test_output_aliasing_an_input():
     assert fwd(y=P[1] + 4096) == ssm.SSM_ERR_ALIAS     # y inside delta
     assert fwd(h=P[6] + 64) == ssm.SSM_ERR_ALIAS       # h_last inside y
     assert bidir(g=P[7]) == ssm.SSM_ERR_ALIAS          # g_first on h_last
+    assert fwd(h=P[10]) == ssm.SSM_ERR_ALIAS           # h_last on top of h0
 
 
 def test_workspace_query_and_check():

@@ -351,3 +351,34 @@ def test_oracle_rejects_bad_arguments():
     inp = small_inputs(1, 4, 2, 2)
     with pytest.raises(RuntimeError):
         oracle.scan(**inp, chans=np.array([5], np.int64))
+
+
+# --- initial state: resuming a split sequence ----------------------------------
+def test_initial_state_superposition_and_resume():
+    # the scan is affine in its initial state: starting [L1, L) from h0 adds
+    # sum_n C_t[n] (prod_{s<=t} a_s[n]) h0[n] to y and (prod a) h0 to h_L;
+    # with h0 = the carried state h_{L1-1} it resumes the full scan
+    inp = small_inputs(2, 70, 5, 16, seed=23)
+    L1 = 29
+    pre = {k: (np.ascontiguousarray(v[:, :L1]) if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    suf = {k: (np.ascontiguousarray(v[:, L1:]) if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    y_full, h_full, _ = oracle.scan(**inp, want_h_last=True)
+    _, h1, _ = oracle.scan(**pre, want_h_last=True)
+    h0 = h1.astype(np.float32)   # the initial-state input is float32
+    y2, h2, _ = oracle.scan(**suf, h0=h0, want_h_last=True)
+    y_ref, h_ref, _ = oracle.scan(**suf, want_h_last=True)
+    a, _ = discretise(suf["x"], suf["delta"], suf["A"], suf["B"])
+    P = np.cumprod(a, axis=0)                                   # (L2, Bs, ED, N)
+    Ct = suf["C"].astype(np.float64).transpose(1, 0, 2)[:, :, None, :]
+    corr = (P * h0.astype(np.float64)[None] * Ct).sum(-1).transpose(1, 0, 2)
+    assert rel_err(y2, y_ref + corr) < 1e-13
+    assert rel_err(h2, h_ref + P[-1] * h0) < 1e-13
+    # resuming from the (float32-rounded) carried state reproduces the full scan
+    assert rel_err(y2, y_full[:, L1:]) < 1e-6
+
+
+def test_zero_initial_state_is_no_initial_state():
+    inp = small_inputs(2, 31, 4, 16, seed=24)
+    y0, h0_, _ = oracle.scan(**inp, want_h_last=True)
+    yz, hz, _ = oracle.scan(**inp, h0=np.zeros((2, 4, 16), np.float32), want_h_last=True)
+    assert np.array_equal(y0, yz) and np.array_equal(h0_, hz)

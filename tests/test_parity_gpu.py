@@ -114,3 +114,32 @@ def test_split_sequence_negative_steps():
     y_ref, h_ref, _ = oracle.scan(**inp, want_h_last=True)
     assert_close("y", y, y_ref, TOL["f32"])
     assert_close("h_last", h, h_ref, TOL["f32"])
+
+
+# ---- initial state h0 (resuming a sequence) ---------------------------------------
+
+@pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(2, 300, 64, "f32", False), (1, 5000, 64, "f32", False),
+                                                 (2, 257, 48, "bf16", False), (2, 200, 64, "f32", True)])
+def test_initial_state(Bs, L, ED, dtype, bidir):
+    log("case h0 Bs=%d L=%d ED=%d %s bidir=%s" % (Bs, L, ED, dtype, bidir))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=L + 7)
+    h0 = (0.5 * synth.normal(31, 8, (Bs, ED, 16))).astype(np.float32)
+    y, h, _ = run_gpu(inp, bidir=bidir, want_h=True, h0=h0)
+    y_ref, h_ref, _ = oracle.scan(**inp, h0=h0, bidir=bidir, want_h_last=True)
+    assert_close("y", y, y_ref, TOL[dtype])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+
+
+def test_resume_in_two_pieces():
+    # scan [0, L1), then [L1, L) from the first piece's final state: the
+    # concatenation matches the oracle's scan of the whole sequence
+    log("case resume")
+    Bs, L, ED, L1 = 2, 3000, 64, 1111
+    inp = synth.make_inputs(Bs, L, ED, 16, "f32", seed=41)
+    cut = lambda a, b: {k: (np.ascontiguousarray(v[:, a:b]) if k in ("x", "delta", "B", "C") else v)
+                        for k, v in inp.items()}
+    y1, h1, _ = run_gpu(cut(0, L1), want_h=True)
+    y2, h2, _ = run_gpu(cut(L1, L), want_h=True, h0=h1.astype(np.float32))
+    y_ref, h_ref, _ = oracle.scan(**inp, want_h_last=True)
+    assert_close("y", np.concatenate([y1, y2], axis=1), y_ref, TOL["f32"])
+    assert_close("h_last", h2, h_ref, TOL["f32"])
