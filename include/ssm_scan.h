@@ -66,8 +66,28 @@ typedef enum {
   SSM_ERR_UNSUPPORTED = 3, /* N not supported, unknown dtype, or a pointer not 16-byte aligned */
   SSM_ERR_ALIAS = 4,       /* an output overlaps an input, another output or the workspace */
   SSM_ERR_WORKSPACE = 5,   /* workspace smaller than ssm_scan_workspace_bytes() */
-  SSM_ERR_LAUNCH = 6       /* the HIP runtime rejected a launch */
+  SSM_ERR_LAUNCH = 6,      /* the HIP runtime rejected a launch */
+  SSM_ERR_ARG = 7          /* an option is invalid (dt_min > dt_max, or a NaN bound) */
 } ssm_status;
+
+/*
+ * Optional step-size pre-processing and output gate, the options of the
+ * Bi-Mamba2 forward ("Some questions of Bi-Mamba2 and Hydra", the
+ * MambaChunkScanCombinedFn.forward listing: dt_bias, dt_softplus, dt_limit,
+ * z), with their usual meaning:
+ *   delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max)
+ *            softplus(v) = v for v > 20, else log(1 + exp(v))
+ *   y'     = y * z * sigmoid(z)      (after D x; both directions for bidir)
+ * delta' replaces delta everywhere in the recurrence. A NULL options pointer
+ * means none of them (raw delta, no clamp, no gate).
+ */
+typedef struct {
+  const float* dt_bias; /* (ED) float32 added to delta, or NULL */
+  int dt_softplus;      /* nonzero: apply softplus after the bias */
+  float dt_min;         /* clamp bounds applied last; -INFINITY / +INFINITY: none */
+  float dt_max;
+  const void* z;        /* (Bs, L, ED) of dtype, or NULL: no gate */
+} ssm_scan_options;
 
 /* Supported state sizes N. */
 #define SSM_MAX_N 16
@@ -92,12 +112,13 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
  *   B, C     : (Bs, L, N) of dtype         -- input and output projections
  *   D        : (ED) float32, or NULL (treated as zero)
  *   h0       : (Bs, ED, N) float32, or NULL -- initial state h_{-1} (zero if NULL)
+ *   opts     : pre-processing and gate (see ssm_scan_options), or NULL
  *   y        : (Bs, L, ED) of dtype        -- output, written in full
  *   h_last   : (Bs, ED, N) float32, or NULL -- state after the last step
  * Returns SSM_OK once the kernels are enqueued, else the first error found.
  */
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D, const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED,
+                 const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED,
                  int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -108,7 +129,7 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
  *   g_first : (Bs, ED, N) float32 or NULL -- reverse state after t = 0
  */
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs,
+                       const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, int64_t Bs,
                        int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
 

@@ -37,7 +37,9 @@ def lib():
             build()
         L = ctypes.CDLL(_SO)
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        dbl = ctypes.c_double
         L.oracle_scan.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, ctypes.c_int, dbl, dbl, vp,
                                   i64, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         L.oracle_scan.restype = ctypes.c_int
         _lib = L
@@ -54,14 +56,19 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def scan(x, delta, A, B, C, D=None, *, h0=None, bidir=False, chans=None, want_h_last=False,
+def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
+         dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, chans=None, want_h_last=False,
          want_g_first=False, nthreads=None):
     """Run the oracle.
 
     x, delta: (Bs, L, ED); B, C: (Bs, L, N) -- float32, or uint16 bf16 bit
     patterns (all four the same dtype). A: (ED, N) float32; D: (ED,) float32
     or None. h0: optional (Bs, ED, N) float32 initial forward state (zero if
-    None). chans: optional int64 array of channel ids b*ED + e.
+    None). dt_bias (ED,) float32, dt_softplus, dt_limit = (lo, hi): the step
+    size used is clamp(softplus?(delta + dt_bias), lo, hi) (no clamp by
+    default: raw step sizes may be negative). z: optional gate,
+    same shape and dtype as x; the output is multiplied by z * sigmoid(z).
+    chans: optional int64 array of channel ids b*ED + e.
 
     Returns (y, h_last, g_first): y is (Bs, L, ED) float64 when chans is None,
     else (len(chans), L) channel-major; h_last / g_first are (Bs, ED, N) or
@@ -74,6 +81,10 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, bidir=False, chans=None, want_h_
     A = np.ascontiguousarray(A, dtype=np.float32)
     D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    dt_bias = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float32)
+    z = None if z is None else np.ascontiguousarray(z)
+    if z is not None and (z.dtype != x.dtype or z.shape != x.shape):
+        raise TypeError("z must match x in shape and dtype")
     if x.dtype == np.uint16:
         dtype = BF16
     elif x.dtype == np.float32:
@@ -88,6 +99,7 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, bidir=False, chans=None, want_h_
     assert delta.shape == x.shape and B.shape == (Bs, L, N) and C.shape == (Bs, L, N)
     assert A.shape == (ED, N) and (D is None or D.shape == (ED,))
     assert h0 is None or h0.shape == (Bs, ED, N)
+    assert dt_bias is None or dt_bias.shape == (ED,)
     if chans is not None:
         chans = np.ascontiguousarray(chans, dtype=np.int64)
         nch = chans.size
@@ -97,7 +109,8 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, bidir=False, chans=None, want_h_
     h = np.empty((nch, N), dtype=np.float64) if want_h_last else None
     g = np.empty((nch, N), dtype=np.float64) if (want_g_first and bidir) else None
     rc = lib().oracle_scan(dtype, int(bool(bidir)), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                           _ptr(D), _ptr(h0), Bs, L, ED, N, _ptr(chans), nch, _ptr(y), _ptr(h), _ptr(g),
+                           _ptr(D), _ptr(h0), _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]),
+                           float(dt_limit[1]), _ptr(z), Bs, L, ED, N, _ptr(chans), nch, _ptr(y), _ptr(h), _ptr(g),
                            _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_scan failed with code %d" % rc)

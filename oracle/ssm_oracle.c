@@ -29,6 +29,15 @@
  *     y[b,t,e] = sum_n C[b,t,n] * (h_t[n] + g_t[n]) + D[e] * x[b,t,e]
  *   with the same a_t, inputs read in place (no shift, no flipped copy).
  *
+ * Optional step-size pre-processing and output gate, the options of the
+ * Bi-Mamba2 forward (same page, the MambaChunkScanCombinedFn.forward
+ * listing: dt_bias, dt_softplus, dt_limit, z), with their usual meaning:
+ *     delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max)
+ *     softplus(v) = v for v > 20, else log(1 + exp(v))
+ *     y' = y * z * sigmoid(z)            (z of the same shape as y)
+ * delta' replaces delta everywhere above; the gate multiplies the complete
+ * output (both directions and the D x term).
+ *
  * Every product of two fp32 (or bf16) inputs is exact in fp64; exp is the
  * host libm's. Threads split only the independent (b, e) channels; the
  * arithmetic of each channel runs in the order written above.
@@ -51,11 +60,18 @@ static double load(const void* p, int64_t i, int dtype) {
   return (double)((const float*)p)[i];
 }
 
-typedef struct {
+struct work;
+static double step_size(const struct work* w, int64_t ix, int64_t e);
+
+typedef struct work {
   int dtype, bidir;
   const void *x, *delta, *B, *C;
   const float *A, *D;
   const float* h0; /* (Bs, ED, N) initial forward state, or NULL for zero */
+  const float* dt_bias; /* (ED) or NULL */
+  int dt_softplus;
+  double dt_min, dt_max;
+  const void* z;   /* (Bs, L, ED) gate, same dtype as x, or NULL */
   int64_t Bs, L, ED, N;
   const int64_t* chans; /* channel ids c = b*ED + e, or NULL for all */
   int64_t nchans;
@@ -64,6 +80,16 @@ typedef struct {
   double* g_first;/* (nchans, N) or NULL: reverse state at t = 0 (bidir only) */
   int64_t k0, k1; /* this worker's range of k */
 } work_t;
+
+/* delta' for the element at index ix of channel e */
+static double step_size(const struct work* w, int64_t ix, int64_t e) {
+  double v = load(w->delta, ix, w->dtype);
+  if (w->dt_bias) v += (double)w->dt_bias[e];
+  if (w->dt_softplus) v = v > 20.0 ? v : log1p(exp(v));
+  if (v < w->dt_min) v = w->dt_min;
+  if (v > w->dt_max) v = w->dt_max;
+  return v;
+}
 
 /* One channel: the forward recurrence, then (bidir) the reverse one. */
 static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
@@ -76,7 +102,7 @@ static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
   for (int64_t t = 0; t < L; ++t) {
     const int64_t ix = (b * L + t) * ED + e; /* x, delta index */
     const int64_t ib = (b * L + t) * N;      /* B, C row index */
-    const double dt = load(w->delta, ix, w->dtype);
+    const double dt = step_size(w, ix, e);
     const double xv = load(w->x, ix, w->dtype);
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
@@ -94,7 +120,7 @@ static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
     for (int64_t t = L - 1; t >= 0; --t) {
       const int64_t ix = (b * L + t) * ED + e;
       const int64_t ib = (b * L + t) * N;
-      const double dt = load(w->delta, ix, w->dtype);
+      const double dt = step_size(w, ix, e);
       const double xv = load(w->x, ix, w->dtype);
       double acc = 0.0;
       for (int64_t n = 0; n < N; ++n) {
@@ -108,11 +134,16 @@ static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
       for (int64_t n = 0; n < N; ++n) w->g_first[k * N + n] = g[n];
   }
 
-  /* the skip term D x, added once */
+  /* the skip term D x, added once; then the gate */
   for (int64_t t = 0; t < L; ++t) {
-    const double xv = load(w->x, (b * L + t) * ED + e, w->dtype);
+    const int64_t ix = (b * L + t) * ED + e;
+    const double xv = load(w->x, ix, w->dtype);
     const double d = w->D ? (double)w->D[e] : 0.0;
     y[t] += d * xv;
+    if (w->z) {
+      const double zv = load(w->z, ix, w->dtype);
+      y[t] *= zv / (1.0 + exp(-zv));
+    }
   }
 }
 
@@ -132,7 +163,8 @@ static void* worker(void* p) {
  * -1 on bad arguments, -2 when memory for a worker could not be allocated.
  */
 int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const float* A, const void* B,
-                const void* C, const float* D, const float* h0, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                const void* C, const float* D, const float* h0, const float* dt_bias, int dt_softplus,
+                double dt_min, double dt_max, const void* z, int64_t Bs, int64_t L, int64_t ED, int64_t N,
                 const int64_t* chans, int64_t nchans, double* y, double* h_last, double* g_first,
                 int nthreads) {
   if (!x || !delta || !A || !B || !C || !y) return -1;
@@ -146,7 +178,8 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
   if (nthreads > 256) nthreads = 256;
   if (nthreads > nchans) nthreads = (int)(nchans > 0 ? nchans : 1);
 
-  work_t base = {dtype, bidir, x, delta, B, C, A, D, h0, Bs, L, ED, N, chans, nchans, y, h_last,
+  work_t base = {dtype, bidir, x, delta, B, C, A, D, h0, dt_bias, dt_softplus, dt_min, dt_max, z,
+                 Bs, L, ED, N, chans, nchans, y, h_last,
                  bidir ? g_first : NULL, 0, 0};
   work_t* ws = (work_t*)malloc(sizeof(work_t) * (size_t)nthreads);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);

@@ -16,7 +16,14 @@ SOURCES = [os.path.join(_HERE, "csrc", "ssm_scan.hip")]
 INCLUDE = os.path.join(_ROOT, "include")
 
 SSM_F32, SSM_BF16 = 0, 1
-SSM_OK, SSM_ERR_NULL, SSM_ERR_DIM, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH = range(7)
+(SSM_OK, SSM_ERR_NULL, SSM_ERR_DIM, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH,
+ SSM_ERR_ARG) = range(8)
+
+
+class SSMOptions(ctypes.Structure):
+    """ssm_scan_options: step-size pre-processing and output gate."""
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float), ("z", ctypes.c_void_p)]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
@@ -59,9 +66,9 @@ def lib():
         vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
         L.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_workspace_bytes.restype = sz
-        L.ssm_scan_fwd.argtypes = [vp] * 9 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_fwd.argtypes = [vp] * 10 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_fwd.restype = ci
-        L.ssm_scan_bidir_fwd.argtypes = [vp] * 10 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_fwd.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
@@ -106,6 +113,18 @@ def _prepare(x, delta, A, B, C, D, y, bidir, workspace):
     return dt, (Bs, L, ED, N), y, workspace, ws_bytes
 
 
+def _options(dt_bias, dt_softplus, dt_limit, z):
+    """An SSMOptions for ctypes.byref, or None when no option is set."""
+    if dt_bias is None and not dt_softplus and dt_limit is None and z is None:
+        return None
+    lo, hi = (-float("inf"), float("inf")) if dt_limit is None else dt_limit
+    return SSMOptions(_ptr(dt_bias), int(bool(dt_softplus)), float(lo), float(hi), _ptr(z))
+
+
+def _byref(o):
+    return None if o is None else ctypes.byref(o)
+
+
 def _stream(x, stream):
     import torch
     if stream is None:
@@ -113,11 +132,15 @@ def _stream(x, stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None, stream=None, h0=None):
+def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None, stream=None, h0=None,
+                 dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
     """y = selective_scan(x, delta, A, B, C, D) from initial state h0 (zero if None);
-    optionally the final state into h_last."""
+    optionally the final state into h_last. dt_bias / dt_softplus / dt_limit
+    pre-process delta, z gates the output (y * silu(z))."""
     dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, False, workspace)
-    rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_last),
+    opts = _options(dt_bias, dt_softplus, dt_limit, z)
+    rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
+                            _ptr(y), _ptr(h_last),
                             Bs, L, ED, N, dt, _ptr(workspace), ws_bytes, _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_fwd")
@@ -125,11 +148,13 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None,
 
 
 def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=None, workspace=None,
-                       stream=None, h0=None):
+                       stream=None, h0=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
     """y = forward scan (from h0, zero if None) + reverse-time scan (shared
-    weights, read in place) + D x."""
+    weights, read in place) + D x, with the same options as ssm_scan_fwd."""
     dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, True, workspace)
-    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+    opts = _options(dt_bias, dt_softplus, dt_limit, z)
+    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                                  _byref(opts), _ptr(y),
                                   _ptr(h_last), _ptr(g_first), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
                                   _stream(x, stream))
     if rc != SSM_OK:

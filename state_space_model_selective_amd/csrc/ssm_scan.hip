@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
@@ -157,6 +158,12 @@ struct ScanArgs {
   const T* C;
   const float* D;
   const float* h0;  // initial forward state (Bs, ED, N) or nullptr for zero
+  // step-size pre-processing: delta' = clamp(softplus?(delta + dt_bias), dt_min, dt_max)
+  const float* dt_bias;  // (ED) or nullptr
+  int dt_softplus;
+  int dt_pre;            // any pre-processing at all
+  float dt_min, dt_max;
+  const T* z;            // gate (Bs, L, ED): y *= z sigmoid(z); used when GATE
   T* y;
   float* part;     // bidir: float32 partials of the reverse sweep (may alias y)
   float* h_last;   // forward final state or nullptr
@@ -175,13 +182,14 @@ struct ScanArgs {
 };
 
 // Input tile of one round (double-buffered).
-template <int RT>
+template <int RT, bool GATE>
 struct alignas(16) Tile {
   float dt[RT][16];   // delta per channel
   float dx[RT][16];   // delta * x per channel
   float bq[RT][16];   // B_t[n]
   float cq[RT][16];   // C_t[n]
   float aux[RT][16];  // D x; the reverse sweep's partial (bidir forward sweep); y so far (correction pass)
+  float gate[GATE ? RT : 1][16];  // z sigmoid(z)
 };
 
 // Output tile of one round (single-buffered: written by the replay after the
@@ -202,18 +210,30 @@ struct alignas(16) FoldArea {
 
 enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
 
+// delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max); softplus(v)
+// = v above 20, else log(1 + e^v) (as log1p(e^v) for accuracy at small e^v).
+template <typename T>
+__device__ __forceinline__ float step_size(const ScanArgs<T>& p, float d, int64_t e) {
+  if (p.dt_bias) d += p.dt_bias[e];
+  if (p.dt_softplus) d = d > 20.f ? d : log1pf(__expf(d));
+  return fminf(fmaxf(d, p.dt_min), p.dt_max);
+}
+
+// z sigmoid(z)
+__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+
 // Staging of one round: each thread owns TPT fixed (row, chunk) tasks of the
 // x/delta tile (4 channels per chunk) or of the B/C tile (4 states per chunk),
 // loads them one round ahead into registers, writes them to the LDS tile, and
 // stores its chunk of the output tile one round later. Offsets advance by one
 // round (RT steps, forward or backward in time) per call. A pass covers the
 // Lk steps starting at time t0 (the whole sequence unless it is split).
-template <typename T, int RT, int TPT, bool BIDIR, bool VEC>
+template <typename T, int RT, int TPT, bool BIDIR, bool VEC, bool GATE>
 struct Stager {
   int row[TPT], chk[TPT];
-  bool is_xd[TPT], chunk_ok[TPT];
+  bool is_xd[TPT], chunk_ok[TPT], row_ok[TPT];
   float4 dval[TPT];              // D of the chunk's channels
-  float4 ra[TPT], rb[TPT], rp[TPT];
+  float4 ra[TPT], rb[TPT], rp[TPT], rz[TPT];
   int64_t pre_off[TPT];          // element offset of this task's row in the next round to prefetch
   int64_t out_off[TPT];          // element offset of this task's row in the next round to store
   int64_t step_xd, step_bc;      // offset change per round
@@ -262,8 +282,9 @@ struct Stager {
     for (int k = 0; k < TPT; ++k) {
       const int64_t off = pre_off[k];
       pre_off[k] += is_xd[k] ? step_xd : step_bc;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a;
-      if (rr * RT + row[k] < Lk && chunk_ok[k]) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a, zz = a;
+      row_ok[k] = rr * RT + row[k] < Lk;
+      if (row_ok[k] && chunk_ok[k]) {
         if (!is_xd[k]) {
           if (STAGE == STAGE_SCAN) a = Vec4<T>::load(p.B + off);
           bb = Vec4<T>::load(p.C + off);
@@ -272,6 +293,7 @@ struct Stager {
           bb = Vec4<T>::load(p.dl + off);
           if (STAGE == STAGE_CORRECT) pp = Vec4<T>::load(p.y + off);
           if (BIDIR && add_part) pp = *reinterpret_cast<const float4*>(p.part + off);
+          if (GATE) zz = Vec4<T>::load(p.z + off);
         } else {
           const int64_t ce = ce0 + 4 * chk[k];
           if (STAGE == STAGE_SCAN)
@@ -285,22 +307,38 @@ struct Stager {
           if (BIDIR && add_part)
             pp = make_float4(p.part[off], ce + 1 < ED ? p.part[off + 1] : 0.f, ce + 2 < ED ? p.part[off + 2] : 0.f,
                              ce + 3 < ED ? p.part[off + 3] : 0.f);
+          if (GATE)
+            zz = make_float4(to_f32(p.z[off]), ce + 1 < ED ? to_f32(p.z[off + 1]) : 0.f,
+                             ce + 2 < ED ? to_f32(p.z[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.z[off + 3]) : 0.f);
         }
       }
       ra[k] = a;
       rb[k] = bb;
       rp[k] = pp;
+      if (GATE) rz[k] = zz;
     }
   }
 
   // registers -> LDS tile
   template <int STAGE>
-  __device__ __forceinline__ void commit(Tile<RT>& tl) const {
+  __device__ __forceinline__ void commit(const ScanArgs<T>& p, Tile<RT, GATE>& tl) const {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const int r = row[k], c4 = 4 * chk[k];
       if (is_xd[k]) {
-        const float4 xv = ra[k], dv = rb[k];
+        const float4 xv = ra[k];
+        float4 dv = rb[k];
+        if (p.dt_pre) {
+          // padded rows and channels keep delta = 0 (a = 1, b = 0: no effect)
+          const bool ok = row_ok[k] && chunk_ok[k];
+          const int64_t ce = ce0 + c4;
+          dv.x = ok && ce + 0 < ED ? step_size(p, dv.x, ce + 0) : 0.f;
+          dv.y = ok && ce + 1 < ED ? step_size(p, dv.y, ce + 1) : 0.f;
+          dv.z = ok && ce + 2 < ED ? step_size(p, dv.z, ce + 2) : 0.f;
+          dv.w = ok && ce + 3 < ED ? step_size(p, dv.w, ce + 3) : 0.f;
+        }
+        if (GATE)
+          *reinterpret_cast<float4*>(&tl.gate[r][c4]) = make_float4(silu(rz[k].x), silu(rz[k].y), silu(rz[k].z), silu(rz[k].w));
         *reinterpret_cast<float4*>(&tl.dt[r][c4]) = dv;
         if (STAGE == STAGE_CORRECT) {
           *reinterpret_cast<float4*>(&tl.aux[r][c4]) = rp[k];
@@ -319,8 +357,12 @@ struct Stager {
     }
   }
 
-  // output of round rr (whose input tile is tl) -> global
-  __device__ __forceinline__ void store_out(const ScanArgs<T>& p, int64_t rr, const Tile<RT>& tl,
+  // output of round rr (whose input tile is tl) -> global:
+  //   scan pass:       (sum over the state quads + aux) * gate
+  //   reverse sweep:   sum + aux (float32 partial, no gate)
+  //   correction pass: aux + sum * gate
+  template <int STAGE>
+  __device__ __forceinline__ void store_out(const ScanArgs<T>& p, int64_t rr, const Tile<RT, GATE>& tl,
                                             const OutTile<RT>& ot) {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
@@ -334,8 +376,14 @@ struct Stager {
       const float4 v2 = *reinterpret_cast<const float4*>(&ot.yq[2][r][c4]);
       const float4 v3 = *reinterpret_cast<const float4*>(&ot.yq[3][r][c4]);
       const float4 a = *reinterpret_cast<const float4*>(&tl.aux[r][c4]);
-      const float4 o = make_float4((v0.x + v1.x) + (v2.x + v3.x) + a.x, (v0.y + v1.y) + (v2.y + v3.y) + a.y,
-                                   (v0.z + v1.z) + (v2.z + v3.z) + a.z, (v0.w + v1.w) + (v2.w + v3.w) + a.w);
+      float4 o = make_float4((v0.x + v1.x) + (v2.x + v3.x), (v0.y + v1.y) + (v2.y + v3.y),
+                             (v0.z + v1.z) + (v2.z + v3.z), (v0.w + v1.w) + (v2.w + v3.w));
+      if (STAGE == STAGE_SCAN) o = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+      if (GATE && !(BIDIR && rev)) {
+        const float4 gv = *reinterpret_cast<const float4*>(&tl.gate[r][c4]);
+        o = make_float4(o.x * gv.x, o.y * gv.y, o.z * gv.z, o.w * gv.w);
+      }
+      if (STAGE == STAGE_CORRECT) o = make_float4(a.x + o.x, a.y + o.y, a.z + o.z, a.w + o.w);
       if (VEC) {
         if (BIDIR && rev) *reinterpret_cast<float4*>(p.part + off) = o;
         else Vec4<T>::store(p.y + off, o);
@@ -369,7 +417,7 @@ __device__ __forceinline__ void wait_flag(int* flag, unsigned* err) {
   }
 }
 
-template <typename T, int SEG, int TS, bool BIDIR, bool VEC, bool SPLIT, int WPE = 3>
+template <typename T, int SEG, int TS, bool BIDIR, bool VEC, bool SPLIT, bool GATE, int WPE = 3>
 __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE))) void scan_chunked_kernel(
     const ScanArgs<T> p) {
   constexpr int RT = SEG * TS;
@@ -380,7 +428,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   static_assert(!(SPLIT && BIDIR), "the split-sequence scan is forward only");
   static_assert(!SPLIT || SEG > 1, "the split-sequence scan needs several segments");
 
-  __shared__ Tile<RT> tile[2];
+  __shared__ Tile<RT, GATE> tile[2];
   __shared__ OutTile<RT> out;
   __shared__ FoldArea<SEG> fa;
 
@@ -419,7 +467,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
   for (int j = 0; j < 4; ++j) A2[j] = p.A[ec * 16 + 4 * g + j] * kLog2e;
 
-  Stager<T, RT, TPT, BIDIR, VEC> st;
+  Stager<T, RT, TPT, BIDIR, VEC, GATE> st;
   st.init(p, tid, e0);
   double sd_total = 0.0;  // split sequence: sum of delta over this wave's segments
   float carry[4];         // state after the last completed round (valid in wave SEG-1)
@@ -434,15 +482,15 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
     if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = init;
 
     st.template prefetch<STAGE_SCAN>(p, 0);
-    st.template commit<STAGE_SCAN>(tile[0]);
+    st.template commit<STAGE_SCAN>(p, tile[0]);
     __syncthreads();
 
     for (int64_t r = 0; r < rounds; ++r) {
-      Tile<RT>& cur = tile[r & 1];
-      Tile<RT>& nxt = tile[(r + 1) & 1];
+      Tile<RT, GATE>& cur = tile[r & 1];
+      Tile<RT, GATE>& nxt = tile[(r + 1) & 1];
       if (r + 1 < rounds) st.template prefetch<STAGE_SCAN>(p, r + 1);
       // output of round r-1, whose input tile stays intact until this round's commit
-      if (r >= 1) st.store_out(p, r - 1, nxt, out);
+      if (r >= 1) st.template store_out<STAGE_SCAN>(p, r - 1, nxt, out);
 
       if constexpr (SEG == 1) {
         // the output tile is single-buffered: the store above must finish
@@ -521,10 +569,10 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
         }
       }
 
-      if (r + 1 < rounds) st.template commit<STAGE_SCAN>(nxt);
+      if (r + 1 < rounds) st.template commit<STAGE_SCAN>(p, nxt);
       __syncthreads();
     }
-    st.store_out(p, rounds - 1, tile[(rounds - 1) & 1], out);
+    st.template store_out<STAGE_SCAN>(p, rounds - 1, tile[(rounds - 1) & 1], out);
 
     if constexpr (!SPLIT) {
       float* h_out = rev ? p.g_first : p.h_last;
@@ -584,13 +632,13 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
     double base = 0.0;  // cumulative delta before the current round
     st.begin(b, L, t0, Lk, false, false);
     st.template prefetch<STAGE_CORRECT>(p, 0);
-    st.template commit<STAGE_CORRECT>(tile[0]);
+    st.template commit<STAGE_CORRECT>(p, tile[0]);
     __syncthreads();
     for (int64_t r = 0; r < rounds; ++r) {
-      Tile<RT>& cur = tile[r & 1];
-      Tile<RT>& nxt = tile[(r + 1) & 1];
+      Tile<RT, GATE>& cur = tile[r & 1];
+      Tile<RT, GATE>& nxt = tile[(r + 1) & 1];
       if (r + 1 < rounds) st.template prefetch<STAGE_CORRECT>(p, r + 1);
-      if (r >= 1) st.store_out(p, r - 1, nxt, out);
+      if (r >= 1) st.template store_out<STAGE_CORRECT>(p, r - 1, nxt, out);
       __syncthreads();  // the output tile is reused below
       float pre = 0.f;  // delta of the round's rows before this wave's segment
       for (int i = 0; i < wave * TS; ++i) pre += cur.dt[i][ch];
@@ -616,14 +664,14 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       float rest = 0.f;  // rows after this wave's segment
       for (int i = (wave + 1) * TS; i < RT; ++i) rest += cur.dt[i][ch];
       base += static_cast<double>(pre + rest);
-      if (r + 1 < rounds) st.template commit<STAGE_CORRECT>(nxt);
+      if (r + 1 < rounds) st.template commit<STAGE_CORRECT>(p, nxt);
       const int go_on = __syncthreads_or((alive || !mono) ? 1 : 0);
       if (!go_on) {
-        st.store_out(p, r, cur, out);
+        st.template store_out<STAGE_CORRECT>(p, r, cur, out);
         return;
       }
     }
-    st.store_out(p, rounds - 1, tile[(rounds - 1) & 1], out);
+    st.template store_out<STAGE_CORRECT>(p, rounds - 1, tile[(rounds - 1) & 1], out);
   }
 }
 
@@ -679,19 +727,19 @@ int device_cus() {
 int split_blocks_per_cu() {
   int best = 1 << 30;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<float, kSEG, kTS, false, true, true>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<float, kSEG, kTS, false, true, true, true>,
                                                    64 * kSEG, 0) != hipSuccess)
     return 0;
   best = std::min(best, n);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<float, kSEG, kTS, false, false, true>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<float, kSEG, kTS, false, false, true, true>,
                                                    64 * kSEG, 0) != hipSuccess)
     return 0;
   best = std::min(best, n);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<uint16_t, kSEG, kTS, false, true, true>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<uint16_t, kSEG, kTS, false, true, true, true>,
                                                    64 * kSEG, 0) != hipSuccess)
     return 0;
   best = std::min(best, n);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<uint16_t, kSEG, kTS, false, false, true>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_chunked_kernel<uint16_t, kSEG, kTS, false, false, true, true>,
                                                    64 * kSEG, 0) != hipSuccess)
     return 0;
   return std::min(best, n);
@@ -746,12 +794,15 @@ Range rng(const void* p, int64_t bytes) {
 }
 
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-             const float* h0, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
+             const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
              int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s) {
   if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
   int rc = check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
-  const void* ptrs[] = {x, delta, A, B, C, D, h0, y, h_last, g_first, ws};
+  const float* dt_bias = opts ? opts->dt_bias : nullptr;
+  const void* z = opts ? opts->z : nullptr;
+  if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
+  const void* ptrs[] = {x, delta, A, B, C, D, h0, dt_bias, z, y, h_last, g_first, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSM_ERR_UNSUPPORTED;
   size_t need = workspace_bytes(Bs, L, ED, N, dtype, bidir);
@@ -759,7 +810,8 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
 
   Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
                 rng(B, s->bc * s->elem), rng(C, s->bc * s->elem), rng(D, D ? ED * 4 : 0),
-                rng(h0, h0 ? s->state * 4 : 0)};
+                rng(h0, h0 ? s->state * 4 : 0), rng(dt_bias, dt_bias ? ED * 4 : 0),
+                rng(z, z ? s->seq * s->elem : 0)};
   Range out[4];
   int nout = 0;
   out[nout++] = rng(y, s->seq * s->elem);
@@ -807,13 +859,17 @@ __global__ void zero_words_kernel(unsigned* p, int64_t n) {
 
 template <typename T, bool BIDIR, bool VEC, bool SPLIT>
 void launch_one(const ScanArgs<T>& a, int64_t nblk, size_t dyn, hipStream_t stream) {
-  hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT>), dim3(nblk), dim3(64 * kSEG), dyn, stream,
-                     a);
+  if (a.z)
+    hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT, true>), dim3(nblk), dim3(64 * kSEG), dyn,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT, false>), dim3(nblk), dim3(64 * kSEG), dyn,
+                       stream, a);
 }
 
 template <typename T>
 int launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                const float* h0, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
+                const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
                 hipStream_t stream) {
   const int64_t ngroups = (ED + 15) / 16;
   const SplitPlan sp = plan_split(Bs, L, ED, bidir, device_cus());
@@ -827,6 +883,12 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.C = static_cast<const T*>(C);
   a.D = D;
   a.h0 = h0;
+  a.dt_bias = opts ? opts->dt_bias : nullptr;
+  a.dt_softplus = opts && opts->dt_softplus ? 1 : 0;
+  a.dt_min = opts ? opts->dt_min : -INFINITY;
+  a.dt_max = opts ? opts->dt_max : INFINITY;
+  a.dt_pre = (a.dt_bias || a.dt_softplus || a.dt_min > -INFINITY || a.dt_max < INFINITY) ? 1 : 0;
+  a.z = opts ? static_cast<const T*>(opts->z) : nullptr;
   a.y = static_cast<T*>(y);
   a.part = bidir ? (std::is_same<T, float>::value ? reinterpret_cast<float*>(y) : static_cast<float*>(ws)) : nullptr;
   a.h_last = h_last;
@@ -851,7 +913,7 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
     hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(std::min<int64_t>((words + 255) / 256, 1024))),
                        dim3(256), 0, stream, reinterpret_cast<unsigned*>(w), words);
   }
-  const size_t lds = sizeof(Tile<kRT>) * 2 + sizeof(OutTile<kRT>) + sizeof(FoldArea<kSEG>) + 16;
+  const size_t lds = sizeof(Tile<kRT, true>) * 2 + sizeof(OutTile<kRT>) + sizeof(FoldArea<kSEG>) + 16;
   const size_t dyn = spread_lds(nblk, lds, 16 / kSEG);
   const bool vec = (ED % 4) == 0;
   if (bidir) {
@@ -868,16 +930,16 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
 }
 
 int run(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-        const float* h0, void* y,
+        const float* h0, const ssm_scan_options* opts, void* y,
         float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* ws,
         size_t ws_bytes, void* stream, int bidir) {
   Sizes s;
-  int rc = validate(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
+  int rc = validate(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SSM_F32)
-    return launch_scan<float>(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
-  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+    return launch_scan<float>(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
 }
 
 }  // namespace
@@ -889,15 +951,16 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
 }
 
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
-                 void* workspace, size_t workspace_bytes, void* stream) {
-  return run(x, delta, A, B, C, D, h0, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 0);
+                 const float* h0, const ssm_scan_options* opts, void* y, float* h_last, int64_t Bs, int64_t L,
+                 int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 0);
 }
 
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L,
-                       int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return run(x, delta, A, B, C, D, h0, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
+                       const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
+                       float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
 }
 
 const char* ssm_status_str(int status) {
@@ -909,6 +972,7 @@ const char* ssm_status_str(int status) {
     case SSM_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case SSM_ERR_WORKSPACE: return "workspace missing or smaller than ssm_scan_workspace_bytes()";
     case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case SSM_ERR_ARG: return "an option is invalid (dt_min > dt_max, or a NaN bound)";
     default: return "unknown status";
   }
 }

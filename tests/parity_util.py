@@ -38,7 +38,7 @@ def y_to_numpy(y):
     return y.double().cpu().numpy()
 
 
-def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False, h0=None):
+def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False, h0=None, opts=None):
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -49,11 +49,18 @@ def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=Fa
     g = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev) if want_g else None
     D = None if D_none else t["D"]
     h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, dtype=np.float32)).to(dev)
+    kw = {}
+    if opts:
+        kw = dict(opts)
+        if kw.get("dt_bias") is not None:
+            kw["dt_bias"] = torch.from_numpy(np.ascontiguousarray(kw["dt_bias"], dtype=np.float32)).to(dev)
+        if kw.get("z") is not None:
+            kw["z"] = to_device({"z": kw["z"]}, dev)["z"]
     if bidir:
         y = ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, g_first=g,
-                                   stream=stream, h0=h0t)
+                                   stream=stream, h0=h0t, **kw)
     else:
-        y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, stream=stream, h0=h0t)
+        y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, stream=stream, h0=h0t, **kw)
     torch.cuda.synchronize()
     return (y_to_numpy(y), None if h is None else h.double().cpu().numpy(),
             None if g is None else g.double().cpu().numpy())

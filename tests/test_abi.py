@@ -31,27 +31,27 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert ssm.status_str(s)
     assert ssm.status_str(999) == "unknown status"
 
 
 def fwd(**kw):
-    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], h0=P[10], Bs=2, L=64, ED=64,
-                N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], h0=P[10], opts=None, Bs=2,
+                L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
     args.update(kw)
     return ssm.lib().ssm_scan_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["h0"],
-                                  args["y"],
+                                  args["opts"], args["y"],
                                   args["h"], args["Bs"], args["L"], args["ED"], args["N"], args["dtype"], args["ws"],
                                   args["ws_bytes"], None)
 
 
 def bidir(**kw):
-    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], h0=P[10], Bs=2,
-                L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], h0=P[10], opts=None,
+                Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
     args.update(kw)
     return ssm.lib().ssm_scan_bidir_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"],
-                                        args["h0"], args["y"], args["h"], args["g"], args["Bs"], args["L"], args["ED"],
+                                        args["h0"], args["opts"], args["y"], args["h"], args["g"], args["Bs"], args["L"], args["ED"],
                                         args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -110,3 +110,25 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 16)
     with pytest.raises(RuntimeError):
         ssm.ssm_scan_fwd(x, x, torch.zeros(16, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
+
+
+def opts(**kw):
+    o = ssm.SSMOptions(None, 0, -float("inf"), float("inf"), None)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return ctypes.byref(o), o
+
+
+def test_options_validation():
+    ref, _ = opts(dt_min=0.5, dt_max=0.1)
+    assert fwd(opts=ref) == ssm.SSM_ERR_ARG
+    ref, _ = opts(dt_min=float("nan"))
+    assert bidir(opts=ref) == ssm.SSM_ERR_ARG
+    ref, _ = opts(z=P[6])                               # gate on top of y
+    assert fwd(opts=ref) == ssm.SSM_ERR_ALIAS
+    ref, _ = opts(dt_bias=P[11] + 8)                    # misaligned bias
+    assert fwd(opts=ref) == ssm.SSM_ERR_UNSUPPORTED
+    ref, _ = opts(z=P[11] + 4)
+    assert fwd(opts=ref) == ssm.SSM_ERR_UNSUPPORTED
+    ref, _ = opts(dt_bias=P[7])                         # h_last on top of the bias
+    assert fwd(opts=ref) == ssm.SSM_ERR_ALIAS

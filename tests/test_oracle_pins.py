@@ -382,3 +382,68 @@ def test_zero_initial_state_is_no_initial_state():
     y0, h0_, _ = oracle.scan(**inp, want_h_last=True)
     yz, hz, _ = oracle.scan(**inp, h0=np.zeros((2, 4, 16), np.float32), want_h_last=True)
     assert np.array_equal(y0, yz) and np.array_equal(h0_, hz)
+
+
+# --- step-size pre-processing and the output gate -----------------------------
+def test_dt_bias_is_added_to_delta_exactly():
+    # delta and bias on a 2^-12 grid: delta + bias is exact in float32, so the
+    # biased scan must equal the scan of the pre-added step sizes bitwise
+    inp = small_inputs(2, 40, 6, 16, seed=25)
+    rng = np.random.default_rng(25)
+    inp["delta"] = (rng.integers(1, 200, inp["delta"].shape) / 4096.0).astype(np.float32)
+    bias = (rng.integers(-20, 40, (6,)) / 4096.0).astype(np.float32)
+    y1, h1, _ = oracle.scan(**inp, dt_bias=bias, want_h_last=True)
+    y2, h2, _ = oracle.scan(**dict(inp, delta=(inp["delta"] + bias).astype(np.float32)), want_h_last=True)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_softplus_step_sizes():
+    # softplus(v) = log(1 + e^v): against step sizes transformed with numpy
+    # (rounded to float32, hence the tolerance), and softplus(0) = ln 2
+    inp = small_inputs(2, 50, 5, 16, seed=26)
+    raw = synth.normal(26, 11, inp["delta"].shape) * 2.0 - 3.0
+    y1, _, _ = oracle.scan(**dict(inp, delta=raw.astype(np.float32)), dt_softplus=True)
+    sp = np.log1p(np.exp(raw.astype(np.float32).astype(np.float64))).astype(np.float32)
+    y2, _, _ = oracle.scan(**dict(inp, delta=sp))
+    assert rel_err(y1, y2) < 1e-6
+    zero = np.zeros_like(inp["delta"])
+    y3, _, _ = oracle.scan(**dict(inp, delta=zero), dt_softplus=True)
+    y4, _, _ = oracle.scan(**dict(inp, delta=np.full_like(zero, np.log(2.0))))
+    assert rel_err(y3, y4) < 1e-7
+    big = np.full_like(zero, 30.0)   # above the threshold softplus is the identity
+    y5, _, _ = oracle.scan(**dict(inp, delta=big), dt_softplus=True)
+    y6, _, _ = oracle.scan(**dict(inp, delta=big))
+    assert np.array_equal(y5, y6)
+
+
+def test_dt_limit_clamps():
+    inp = small_inputs(1, 60, 4, 16, seed=27)
+    lo, hi = 0.0078125, 0.046875   # float32-representable bounds
+    y1, _, _ = oracle.scan(**inp, dt_limit=(lo, hi))
+    y2, _, _ = oracle.scan(**dict(inp, delta=np.clip(inp["delta"], np.float32(lo), np.float32(hi))))
+    assert rel_err(y1, y2) < 1e-15
+
+
+def test_gate_special_values():
+    inp = small_inputs(2, 30, 4, 16, seed=28)
+    y, _, _ = oracle.scan(**inp)
+    zero = np.zeros_like(inp["x"])
+    yz, _, _ = oracle.scan(**inp, z=zero)                    # silu(0) = 0
+    assert not yz.any()
+    yb, _, _ = oracle.scan(**inp, z=np.full_like(zero, 50.0))  # sigmoid(50) = 1 in double
+    assert rel_err(yb, 50.0 * y) < 1e-15
+    yn, _, _ = oracle.scan(**inp, z=np.full_like(zero, -800.0))  # e^800 overflows: exact zero
+    assert not yn.any()
+    yo, _, _ = oracle.scan(**inp, z=np.ones_like(zero))       # silu(1) = 1 / (1 + 1/e)
+    assert rel_err(yo, y / (1.0 + np.exp(-1.0))) < 1e-15
+
+
+def test_gate_and_bias_apply_to_bidirectional_output():
+    inp = small_inputs(2, 33, 4, 16, seed=29)
+    z = synth.normal(29, 12, inp["x"].shape)
+    bias = synth.normal(29, 13, (4,)) * 0.01
+    yb, _, _ = oracle.scan(**inp, bidir=True, dt_bias=bias, dt_softplus=True, z=z)
+    sp = np.log1p(np.exp(inp["delta"].astype(np.float64) + bias.astype(np.float64)))
+    yu, _, _ = oracle.scan(**dict(inp, delta=sp.astype(np.float32)), bidir=True)
+    g = z.astype(np.float64) / (1.0 + np.exp(-z.astype(np.float64)))
+    assert rel_err(yb, yu * g) < 1e-6

@@ -143,3 +143,49 @@ def test_resume_in_two_pieces():
     y_ref, h_ref, _ = oracle.scan(**inp, want_h_last=True)
     assert_close("y", np.concatenate([y1, y2], axis=1), y_ref, TOL["f32"])
     assert_close("h_last", h2, h_ref, TOL["f32"])
+
+
+# ---- step-size pre-processing and output gate ------------------------------------
+
+def options_inputs(Bs, L, ED, dtype, seed):
+    """Raw step sizes around softplus^-1 of the usual range, a bias, a gate."""
+    inp = synth.make_inputs(Bs, L, ED, 16, "f32", seed=seed)
+    raw = (0.7 * synth.normal(seed, 21, (Bs, L, ED)) - 3.5).astype(np.float32)
+    z = synth.normal(seed, 22, (Bs, L, ED))
+    bias = (0.3 * synth.normal(seed, 23, (ED,))).astype(np.float32)
+    inp["delta"] = raw
+    if dtype == "bf16":
+        for k in ("x", "delta", "B", "C"):
+            inp[k] = synth.to_bf16(inp[k])
+        z = synth.to_bf16(z)
+    return inp, dict(dt_bias=bias, dt_softplus=True, dt_limit=(1e-3, 0.1), z=z)
+
+
+@pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(2, 300, 64, "f32", False), (2, 301, 40, "f32", False),
+                                                 (2, 257, 64, "bf16", False), (2, 200, 64, "f32", True),
+                                                 (1, 5000, 64, "f32", False), (1, 4500, 48, "bf16", False)])
+def test_preprocessing_and_gate(Bs, L, ED, dtype, bidir):
+    log("case options Bs=%d L=%d ED=%d %s bidir=%s" % (Bs, L, ED, dtype, bidir))
+    inp, opts = options_inputs(Bs, L, ED, dtype, seed=L + ED)
+    y, h, _ = run_gpu(inp, bidir=bidir, want_h=True, opts=opts)
+    y_ref, h_ref, _ = oracle.scan(**inp, bidir=bidir, want_h_last=True, **opts)
+    assert_close("y", y, y_ref, TOL[dtype])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+
+
+def test_options_each_alone():
+    inp, opts = options_inputs(2, 150, 32, "f32", seed=5)
+    positive = synth.make_inputs(2, 150, 32, 16, "f32", seed=5)["delta"]   # log-uniform steps
+    singles = {"dt_bias": dict(dt_bias=np.abs(opts["dt_bias"]) * 0.02),
+               "dt_softplus": dict(dt_softplus=True),
+               "dt_limit": dict(dt_limit=(0.01, 0.05)),
+               "z": dict(z=opts["z"])}
+    for key, one in singles.items():
+        log("case option %s alone" % key)
+        # raw steps only through softplus; otherwise positive steps (negative
+        # raw steps make the state grow without bound)
+        inp2 = inp if key == "dt_softplus" else dict(inp, delta=positive)
+        y, h, _ = run_gpu(inp2, want_h=True, opts=one)
+        y_ref, h_ref, _ = oracle.scan(**inp2, want_h_last=True, **one)
+        assert_close("y", y, y_ref, TOL["f32"])
+        assert_close("h_last", h, h_ref, TOL["f32"])
