@@ -282,8 +282,8 @@ struct Stager {
     for (int k = 0; k < TPT; ++k) {
       const int64_t off = pre_off[k];
       pre_off[k] += is_xd[k] ? step_xd : step_bc;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a, zz = a;
       row_ok[k] = rr * RT + row[k] < Lk;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a, zz = a;
       if (row_ok[k] && chunk_ok[k]) {
         if (!is_xd[k]) {
           if (STAGE == STAGE_SCAN) a = Vec4<T>::load(p.B + off);
@@ -514,20 +514,20 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       } else {
         // local pass from a zero state
         float av[TS][4], bv[TS][4];
-        float hl[4] = {0.f, 0.f, 0.f, 0.f};
-        float sd = 0.f;
+        float hl[4];
+        float sd;
 #pragma unroll
         for (int i = 0; i < TS; ++i) {
           const int row = wave * TS + i;
           const float dt = cur.dt[row][ch], dx = cur.dx[row][ch];
           const float bq = cur.bq[row][q];
-          sd += dt;
+          sd = i == 0 ? dt : sd + dt;
           const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
             bv[i][j] = dx * bb[j];
-            hl[j] = __builtin_fmaf(av[i][j], hl[j], bv[i][j]);
+            hl[j] = i == 0 ? bv[i][j] : __builtin_fmaf(av[i][j], hl[j], bv[i][j]);
           }
         }
         if (SPLIT) sd_total += static_cast<double>(sd);
