@@ -7,6 +7,8 @@ this package. The product path (the HIP library and its binding) never does.
   a_t[n] = exp(delta_t * A[e, n]);  h_t = a_t * h_{t-1} + (delta_t * x_t) * B_t[n]
   y_t = sum_n C_t[n] h_t[n] + D[e] x_t
 (plus the reverse-time scan for the bidirectional variant), in fp64.
+``scan_bwd`` is the adjoint of that recurrence: the gradients of sum(dy * y)
+with respect to x, delta, A, B, C, D and h0.
 """
 import ctypes
 import os
@@ -42,6 +44,8 @@ def lib():
                                   vp, ctypes.c_int, dbl, dbl, vp,
                                   i64, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         L.oracle_scan.restype = ctypes.c_int
+        L.oracle_scan_bwd.argtypes = [ctypes.c_int] + [vp] * 8 + [i64] * 4 + [vp] * 7 + [ctypes.c_int]
+        L.oracle_scan_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -121,3 +125,35 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
         if g is not None:
             g = g.reshape(Bs, ED, N)
     return y, h, g
+
+
+def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, nthreads=None):
+    """Gradients of L = sum(dy * y) for the forward scan (no options), in fp64.
+
+    Same input conventions as scan(); dy has y's shape and x's dtype.
+    Returns a dict with dx, ddelta (Bs, L, ED), dA (ED, N), dB, dC (Bs, L, N),
+    dD (ED,) and dh0 (Bs, ED, N) (zeros when h0 is None).
+    """
+    x = np.ascontiguousarray(x)
+    delta = np.ascontiguousarray(delta)
+    B = np.ascontiguousarray(B)
+    C = np.ascontiguousarray(C)
+    dy = np.ascontiguousarray(dy)
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    dtype = BF16 if x.dtype == np.uint16 else F32
+    for t in (delta, B, C, dy):
+        if t.dtype != x.dtype:
+            raise TypeError("x, delta, B, C, dy must share a dtype")
+    Bs, L, ED = x.shape
+    N = A.shape[1]
+    assert dy.shape == x.shape
+    out = dict(dx=np.empty((Bs, L, ED)), ddelta=np.empty((Bs, L, ED)), dA=np.empty((ED, N)),
+               dB=np.empty((Bs, L, N)), dC=np.empty((Bs, L, N)), dD=np.empty((ED,)), dh0=np.empty((Bs, ED, N)))
+    rc = lib().oracle_scan_bwd(dtype, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy),
+                               Bs, L, ED, N, _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                               _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_bwd failed with code %d" % rc)
+    return out

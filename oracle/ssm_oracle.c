@@ -38,6 +38,13 @@
  * delta' replaces delta everywhere above; the gate multiplies the complete
  * output (both directions and the D x term).
  *
+ * Backward pass (oracle_scan_bwd): the gradients of sum(dy * y) for the
+ * forward scan without options, the step the Bi-Mamba2 page's autograd
+ * function takes after the forward ("Some questions of Bi-Mamba2 and Hydra",
+ * the backward listing: dx, ddt, dA, dB, dC, dD from dout). The pages give
+ * no formula; it is the adjoint of the recurrence above, derived by the chain
+ * rule and written out where the function is defined.
+ *
  * Every product of two fp32 (or bf16) inputs is exact in fp64; exp is the
  * host libm's. Threads split only the independent (b, e) channels; the
  * arithmetic of each channel runs in the order written above.
@@ -202,6 +209,148 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
     pthread_join(th[i], &r);
     if (r) rc = -2;
   }
+  free(ws);
+  free(th);
+  return rc;
+}
+
+/*
+ * Backward pass of the forward scan (no options, no bidirectional variant):
+ * given dy = dL/dy, the gradients of L with respect to every input, by the
+ * adjoint of the recurrence above. With g_t[n] = dL/dh_t[n]:
+ *     g_t = dy_t C_t + a_{t+1} g_{t+1}          (g_L = 0; reverse time)
+ *     dC[b,t,n] = sum_e dy_t h_t[n]             dD[e] = sum_{b,t} dy_t x_t
+ *     dx_t = sum_n g_t[n] delta_t B_t[n] + dy_t D[e]
+ *     ddelta_t = sum_n g_t[n] (x_t B_t[n] + A[e,n] a_t[n] h_{t-1}[n])
+ *     dB[b,t,n] = sum_e g_t[n] delta_t x_t
+ *     dA[e,n] = sum_{b,t} g_t[n] a_t[n] h_{t-1}[n] delta_t
+ *     dh0 = a_0 g_0 (h_{-1} = h0)
+ * Work is split over batch rows (dB, dC of a row come from one thread);
+ * dA and dD are summed over rows in row order afterwards. Outputs are fp64:
+ * dx, ddelta (Bs, L, ED); dA (ED, N); dB, dC (Bs, L, N); dD (ED);
+ * dh0 (Bs, ED, N) or NULL.
+ */
+typedef struct {
+  int dtype;
+  const void *x, *delta, *B, *C, *dy;
+  const float *A, *D, *h0;
+  int64_t Bs, L, ED, N;
+  double *dx, *ddelta, *dB, *dC, *dh0;
+  double *dA_part, *dD_part; /* per row: (Bs, ED, N), (Bs, ED) */
+  int64_t b0, b1;
+} bwd_t;
+
+static void* bwd_worker(void* p) {
+  bwd_t* w = (bwd_t*)p;
+  const int64_t L = w->L, ED = w->ED, N = w->N;
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(L + 1) * N); /* h_{t-1} at row t */
+  double* g = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !g) {
+    free(hs);
+    free(g);
+    return (void*)1;
+  }
+  for (int64_t b = w->b0; b < w->b1; ++b) {
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t t = 0; t < L; ++t) w->dB[(b * L + t) * N + n] = 0.0, w->dC[(b * L + t) * N + n] = 0.0;
+    }
+    for (int64_t e = 0; e < ED; ++e) {
+      /* forward, keeping every state */
+      for (int64_t n = 0; n < N; ++n) hs[n] = w->h0 ? (double)w->h0[(b * ED + e) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t ix = (b * L + t) * ED + e, ib = (b * L + t) * N;
+        const double dt = load(w->delta, ix, w->dtype), xv = load(w->x, ix, w->dtype);
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = exp(dt * (double)w->A[e * N + n]);
+          hs[(t + 1) * N + n] = a * hs[t * N + n] + (dt * xv) * load(w->B, ib + n, w->dtype);
+        }
+      }
+      /* reverse: the adjoint state and every gradient term */
+      for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+      double dD = 0.0;
+      double* dA = w->dA_part + (b * ED + e) * N;
+      for (int64_t n = 0; n < N; ++n) dA[n] = 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t ix = (b * L + t) * ED + e, ib = (b * L + t) * N;
+        const double dt = load(w->delta, ix, w->dtype), xv = load(w->x, ix, w->dtype);
+        const double dyv = load(w->dy, ix, w->dtype);
+        double dxv = w->D ? dyv * (double)w->D[e] : 0.0, ddv = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double An = (double)w->A[e * N + n];
+          const double Bv = load(w->B, ib + n, w->dtype), Cv = load(w->C, ib + n, w->dtype);
+          /* g_t = dy_t C_t + a_{t+1} g_{t+1}: g[n] holds a_{t+1} g_{t+1} here */
+          g[n] += dyv * Cv;
+          const double a = exp(dt * An);
+          const double hprev = hs[t * N + n];
+          w->dC[ib + n] += dyv * hs[(t + 1) * N + n];
+          w->dB[ib + n] += g[n] * dt * xv;
+          dxv += g[n] * dt * Bv;
+          ddv += g[n] * (xv * Bv + An * a * hprev);
+          dA[n] += g[n] * a * hprev * dt;
+          g[n] *= a; /* a_t g_t, the carry into step t-1 */
+        }
+        dD += dyv * xv;
+        w->dx[ix] = dxv;
+        w->ddelta[ix] = ddv;
+      }
+      if (w->dh0)
+        for (int64_t n = 0; n < N; ++n) w->dh0[(b * ED + e) * N + n] = g[n];
+      w->dD_part[b * ED + e] = dD;
+    }
+  }
+  free(hs);
+  free(g);
+  return NULL;
+}
+
+int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D, const float* h0, const void* dy, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                    double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dh0,
+                    int nthreads) {
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC || !dD) return -1;
+  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > Bs) nthreads = (int)Bs;
+  if (nthreads > 256) nthreads = 256;
+  double* dA_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED * N));
+  double* dD_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED));
+  bwd_t* ws = (bwd_t*)malloc(sizeof(bwd_t) * (size_t)nthreads);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  int rc = 0;
+  if (!dA_part || !dD_part || !ws || !th) {
+    rc = -2;
+  } else {
+    int64_t per = (Bs + nthreads - 1) / nthreads;
+    for (int i = 0; i < nthreads; ++i) {
+      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, Bs, L, ED, N, dx, ddelta, dB, dC,
+                      h0 ? dh0 : NULL, dA_part, dD_part, 0, 0};
+      ws[i].b0 = per * i < Bs ? per * i : Bs;
+      ws[i].b1 = per * (i + 1) < Bs ? per * (i + 1) : Bs;
+    }
+    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, bwd_worker, &ws[i]);
+    if (bwd_worker(&ws[0])) rc = -2;
+    for (int i = 1; i < nthreads; ++i) {
+      void* r = NULL;
+      pthread_join(th[i], &r);
+      if (r) rc = -2;
+    }
+    /* sums over batch rows, in row order */
+    for (int64_t i = 0; rc == 0 && i < ED * N; ++i) {
+      double s = 0.0;
+      for (int64_t b = 0; b < Bs; ++b) s += dA_part[b * ED * N + i];
+      dA[i] = s;
+    }
+    for (int64_t e = 0; rc == 0 && e < ED; ++e) {
+      double s = 0.0;
+      for (int64_t b = 0; b < Bs; ++b) s += dD_part[b * ED + e];
+      dD[e] = s;
+    }
+    if (h0 == NULL && dh0 != NULL)
+      for (int64_t i = 0; i < Bs * ED * N; ++i) dh0[i] = 0.0;
+  }
+  free(dA_part);
+  free(dD_part);
   free(ws);
   free(th);
   return rc;

@@ -14,6 +14,7 @@ normal; step size Delta log-uniform on [1e-3, 1e-1]; A[e, n] = -(n + 1)):
   C     (Bs, L, N)   N(0, 1)                   stream 4
   D     (ED,)        N(0, 1)                   stream 5
   A     (ED, N)      -(n + 1), exact
+  dy    (Bs, L, ED)  N(0, 1)                   stream 6 (output gradient, backward pass)
 
 For bf16 workloads x, delta, B and C are rounded to bfloat16 (round to nearest
 even) and handed over as uint16 bit patterns; A and D stay float32.
@@ -29,7 +30,7 @@ _SRC = os.path.join(_HERE, "synth.c")
 _SO = os.path.join(_HERE, "libssm_synth.so")
 _lib = None
 
-STREAM_X, STREAM_DELTA, STREAM_B, STREAM_C, STREAM_D = 1, 2, 3, 4, 5
+STREAM_X, STREAM_DELTA, STREAM_B, STREAM_C, STREAM_D, STREAM_DY = 1, 2, 3, 4, 5, 6
 DELTA_LO, DELTA_HI = 1e-3, 1e-1
 
 # The five workloads of the selective-scan study, named by what they are.
@@ -134,3 +135,9 @@ def make_inputs(Bs, L, ED, N, dtype="f32", seed=0, nthreads=None):
 def workload_inputs(name, seed=0, nthreads=None):
     w = WORKLOADS[name]
     return make_inputs(w["Bs"], w["L"], w["ED"], w["N"], w["dtype"], seed, nthreads)
+
+
+def make_output_grad(Bs, L, ED, dtype="f32", seed=0, nthreads=None):
+    """Gradient dL/dy for the backward pass, N(0, 1), of the workload's dtype."""
+    dy = normal(seed, STREAM_DY, (Bs, L, ED), nthreads)
+    return to_bf16(dy) if dtype == "bf16" else dy
