@@ -132,7 +132,8 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, nthreads=None):
 
     Same input conventions as scan(); dy has y's shape and x's dtype.
     Returns a dict with dx, ddelta (Bs, L, ED), dA (ED, N), dB, dC (Bs, L, N),
-    dD (ED,) and dh0 (Bs, ED, N) (zeros when h0 is None).
+    dD (ED,) and dh0 (Bs, ED, N) (the same with or without h0: y is affine in
+    the initial state).
     """
     x = np.ascontiguousarray(x)
     delta = np.ascontiguousarray(delta)

@@ -228,7 +228,8 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
  * Work is split over batch rows (dB, dC of a row come from one thread);
  * dA and dD are summed over rows in row order afterwards. Outputs are fp64:
  * dx, ddelta (Bs, L, ED); dA (ED, N); dB, dC (Bs, L, N); dD (ED);
- * dh0 (Bs, ED, N) or NULL.
+ * dh0 (Bs, ED, N) or NULL. y is affine in h0, so dh0 does not depend on h0
+ * and is returned for h0 = NULL (the zero initial state) as well.
  */
 typedef struct {
   int dtype;
@@ -324,7 +325,7 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
     int64_t per = (Bs + nthreads - 1) / nthreads;
     for (int i = 0; i < nthreads; ++i) {
       ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, Bs, L, ED, N, dx, ddelta, dB, dC,
-                      h0 ? dh0 : NULL, dA_part, dD_part, 0, 0};
+                      dh0, dA_part, dD_part, 0, 0};
       ws[i].b0 = per * i < Bs ? per * i : Bs;
       ws[i].b1 = per * (i + 1) < Bs ? per * (i + 1) : Bs;
     }
@@ -346,8 +347,6 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
       for (int64_t b = 0; b < Bs; ++b) s += dD_part[b * ED + e];
       dD[e] = s;
     }
-    if (h0 == NULL && dh0 != NULL)
-      for (int64_t i = 0; i < Bs * ED * N; ++i) dh0[i] = 0.0;
   }
   free(dA_part);
   free(dD_part);
