@@ -133,6 +133,43 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
                        int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * Backward pass of the forward scan: the gradients of L = sum(dy * y) for
+ * y = ssm_scan_fwd(x, delta, A, B, C, D, h0, opts = NULL). This is the step
+ * that follows the forward in the autograd function of "Some questions of
+ * Bi-Mamba2 and Hydra" (the backward listing, which returns dx, ddt, dA, dB,
+ * dC and dD from dout); the pages give no formula, so the gradients are the
+ * adjoint of the recurrence above. With g_t[n] = dL/dh_t[n] (reverse time,
+ * g_{L-1} = dy_{L-1} C_{L-1}):
+ *   g_t      = dy_t C_t + a_{t+1} g_{t+1}
+ *   dx_t     = delta_t sum_n g_t B_t + D dy_t
+ *   ddelta_t = x_t sum_n g_t B_t + sum_n A[e,n] g_t a_t h_{t-1}
+ *   dB_t[n]  = sum_e g_t delta_t x_t,      dC_t[n] = sum_e dy_t h_t
+ *   dA[e,n]  = sum_{b,t} delta_t g_t a_t h_{t-1},   dD[e] = sum_{b,t} dy_t x_t
+ *   dh0      = a_0 g_0
+ * Step-size options and the gate are not covered (the forward must have run
+ * without them); neither is the bidirectional scan.
+ *   x, delta, A, B, C, D, h0 : as ssm_scan_fwd (D and h0 may be NULL)
+ *   dy      : (Bs, L, ED) of dtype         -- dL/dy
+ *   dx, ddelta : (Bs, L, ED) of dtype      -- written in full
+ *   dA      : (ED, N) float32              -- written in full
+ *   dB, dC  : (Bs, L, N) of dtype          -- written in full
+ *   dD      : (ED) float32, or NULL (not computed)
+ *   dh0     : (Bs, ED, N) float32, or NULL (not computed)
+ *   workspace : at least ssm_scan_bwd_workspace_bytes() bytes (required; it
+ *     holds the state at every 32-step boundary and float32 partial sums of
+ *     dB, dC, dA and dD), no initialisation needed.
+ * Sums over channels (dB, dC) and over batch rows and time (dA, dD) are
+ * taken in a fixed order, so repeated calls give identical bits.
+ * Conventions, alignment and error codes as ssm_scan_fwd.
+ */
+size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype);
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                 float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

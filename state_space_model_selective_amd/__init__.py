@@ -1,7 +1,8 @@
 """Python binding of the MI355X selective-scan library (libssm_scan.so).
 
 Argument marshalling only: every step of the scan runs in the HIP kernels of
-``csrc/ssm_scan.hip`` behind the C ABI declared in ``include/ssm_scan.h``.
+``csrc/ssm_scan.hip`` (forward) and ``csrc/ssm_scan_bwd.hip`` (backward)
+behind the C ABI declared in ``include/ssm_scan.h``.
 PyTorch supplies device memory and the stream. There is no fallback: if the
 library is not built, or the tensors are not on a GPU, the calls raise.
 """
@@ -12,7 +13,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libssm_scan.so")
-SOURCES = [os.path.join(_HERE, "csrc", "ssm_scan.hip")]
+SOURCES = [os.path.join(_HERE, "csrc", "ssm_scan.hip"), os.path.join(_HERE, "csrc", "ssm_scan_bwd.hip")]
 INCLUDE = os.path.join(_ROOT, "include")
 
 SSM_F32, SSM_BF16 = 0, 1
@@ -70,6 +71,10 @@ def lib():
         L.ssm_scan_fwd.restype = ci
         L.ssm_scan_bidir_fwd.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
+        L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+        L.ssm_scan_bwd_workspace_bytes.restype = sz
+        L.ssm_scan_bwd.argtypes = [vp] * 15 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -160,3 +165,44 @@ def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=N
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_bidir_fwd")
     return y
+
+
+def ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32):
+    return int(lib().ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, int(dtype)))
+
+
+def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
+                 stream=None):
+    """Gradients of sum(dy * y) for y = ssm_scan_fwd(x, delta, A, B, C, D, h0=h0).
+
+    Returns a dict with dx, ddelta (like x), dA (like A), dB, dC (like B),
+    dD (ED,) float32 if want_dD, dh0 (Bs, ED, N) float32 if want_dh0. Tensors
+    given in ``out`` (same keys) are written instead of new ones.
+    """
+    import torch
+    if not x.is_cuda:
+        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
+    dt = _dtype_code(x)
+    Bs, L, ED = x.shape
+    N = A.shape[1]
+    o = dict(out or {})
+    o.setdefault("dx", torch.empty_like(x))
+    o.setdefault("ddelta", torch.empty_like(x))
+    o.setdefault("dA", torch.empty((ED, N), dtype=torch.float32, device=x.device))
+    o.setdefault("dB", torch.empty_like(B))
+    o.setdefault("dC", torch.empty_like(C))
+    if want_dD:
+        o.setdefault("dD", torch.empty((ED,), dtype=torch.float32, device=x.device))
+    if want_dh0:
+        o.setdefault("dh0", torch.empty((Bs, ED, N), dtype=torch.float32, device=x.device))
+    need = ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, dt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy),
+                            _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
+                            _ptr(o.get("dD")), _ptr(o.get("dh0")), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
+                            _stream(x, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_scan_bwd")
+    return o

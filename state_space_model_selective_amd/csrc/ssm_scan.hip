@@ -18,86 +18,10 @@
 #include <type_traits>
 
 #include "ssm_scan.h"
+#include "scan_common.h"
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-// ---------------------------------------------------------------------------
-// element access: float32 or bfloat16 (uint16 bit pattern)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-
-template <typename T>
-__device__ __forceinline__ T from_f32(float v);
-template <>
-__device__ __forceinline__ float from_f32<float>(float v) { return v; }
-template <>
-__device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
-  // round to nearest even; NaN stays NaN
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
-// ---------------------------------------------------------------------------
-// 4-wide element access (16-byte float32 / 8-byte bfloat16 vectors)
-// ---------------------------------------------------------------------------
-template <typename T>
-struct Vec4;
-template <>
-struct Vec4<float> {
-  static __device__ __forceinline__ float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
-  static __device__ __forceinline__ void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
-};
-template <>
-struct Vec4<uint16_t> {
-  static __device__ __forceinline__ float4 load(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-  }
-  static __device__ __forceinline__ void store(uint16_t* p, float4 v) {
-    uint2 u;
-    u.x = static_cast<uint32_t>(from_f32<uint16_t>(v.x)) | (static_cast<uint32_t>(from_f32<uint16_t>(v.y)) << 16);
-    u.y = static_cast<uint32_t>(from_f32<uint16_t>(v.z)) | (static_cast<uint32_t>(from_f32<uint16_t>(v.w)) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Cross-lane operands (DPP). Lane q of a 16-lane row holds B_t[q] (or
-// C_t[q]); quad g of the row needs B_t[4g .. 4g+3]. quad_bcast<J> makes every
-// lane of a quad read lane J of that quad. As a plain move the compiler folds
-// it into the consuming multiply as a DPP source modifier (and inserts the
-// wait states DPP needs). It does not fold it into v_fmac, so the C
-// contraction issues v_fmac_f32_dpp itself; the leading s_nop 1 provides the
-// two wait states a DPP read needs after a VALU write of its source.
-// ---------------------------------------------------------------------------
-template <int J>
-__device__ __forceinline__ float quad_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, true));
-}
-
-#define SSM_FMAC_QUAD(J)                                                                              \
-  template <>                                                                                         \
-  __device__ __forceinline__ float fmac_quad<J>(float acc, float src, float other) {                  \
-    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[" #J "," #J "," #J "," #J                    \
-        "] row_mask:0xf bank_mask:0xf bound_ctrl:1"                                                   \
-        : "+v"(acc)                                                                                   \
-        : "v"(src), "v"(other));                                                                      \
-    return acc;                                                                                       \
-  }
-// acc + (lane J of this lane's quad's src) * other
-template <int J>
-__device__ __forceinline__ float fmac_quad(float acc, float src, float other);
-SSM_FMAC_QUAD(0)
-SSM_FMAC_QUAD(1)
-SSM_FMAC_QUAD(2)
-SSM_FMAC_QUAD(3)
-#undef SSM_FMAC_QUAD
 
 // ---------------------------------------------------------------------------
 // Chunked selective-scan kernel.
@@ -678,21 +602,6 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 // ---------------------------------------------------------------------------
 // host-side validation
 // ---------------------------------------------------------------------------
-struct Range {
-  uintptr_t lo, hi;  // [lo, hi)
-};
-
-bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
-
-bool mul_ok(int64_t a, int64_t b, int64_t* out) {
-  if (a <= 0 || b <= 0) return false;
-  if (a > INT64_MAX / b) return false;
-  *out = a * b;
-  return true;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 struct Sizes {
   int64_t seq;     // Bs * L * ED
   int64_t bc;      // Bs * L * N
@@ -714,13 +623,6 @@ int check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, Sizes* 
 
 // Kernel configuration: SEG waves per workgroup, TS steps per wave per round.
 constexpr int kSEG = 4, kTS = 8, kRT = kSEG * kTS;
-
-int device_cus() {
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return ncu;
-}
 
 // Workgroups of the split-sequence kernel that fit on one CU at once (the
 // smallest over its instantiations), 0 if the runtime cannot tell.
@@ -788,11 +690,6 @@ size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, 
   return plan_split(Bs, L, ED, bidir, device_cus()).bytes;
 }
 
-Range rng(const void* p, int64_t bytes) {
-  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
-}
-
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
              const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
              int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s) {
@@ -825,36 +722,6 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
       if (overlap(out[i], out[j])) return SSM_ERR_ALIAS;
   }
   return SSM_OK;
-}
-
-// Extra (dynamic) LDS per workgroup so that the workgroups spread evenly over
-// the compute units. The dispatcher fills a CU up to its resource limit before
-// using the next one, so 768 workgroups that fit 4 per CU would run on 192 of
-// 256 CUs. Padding each workgroup's LDS lowers the per-CU limit to
-// ceil(blocks / CUs) when that is below the natural limit.
-size_t spread_lds(int64_t nblk, size_t lds_static, int max_per_cu) {
-  int dev = 0, ncu = 0, lds_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) return 0;
-  if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
-      lds_cu <= 0)
-    return 0;
-  const int64_t natural = std::min<int64_t>(max_per_cu, lds_cu / static_cast<int64_t>(lds_static));
-  const int64_t want = (nblk + ncu - 1) / ncu;
-  if (want >= natural || want <= 0) return 0;
-  // per-workgroup LDS in (lds_cu / (want + 1), lds_cu / want]
-  size_t total = static_cast<size_t>(lds_cu / (want + 1)) + 1024;
-  total = (total + 511) & ~static_cast<size_t>(511);
-  if (total > static_cast<size_t>(lds_cu / want) || total <= lds_static) return 0;
-  return total - lds_static;
-}
-
-// Clears the split-sequence workspace header and flags (a kernel rather than
-// a memset, so the call stays safe to capture in a graph).
-__global__ void zero_words_kernel(unsigned* p, int64_t n) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = 0u;
 }
 
 template <typename T, bool BIDIR, bool VEC, bool SPLIT>

@@ -1,0 +1,657 @@
+// Backward pass of the selective scan for MI355X (gfx950).
+//
+// Given dy = dL/dy for the forward scan
+//   a_t = exp(delta_t A[e,n]),  h_t = a_t h_{t-1} + (delta_t x_t) B_t[n],
+//   y_t = sum_n C_t[n] h_t[n] + D[e] x_t,          h_{-1} = h0 (or zero),
+// it returns every input's gradient. This is the step after the forward in
+// the autograd function of "Some questions of Bi-Mamba2 and Hydra" (the
+// backward listing: dx, ddt, dA, dB, dC, dD from dout); the pages give no
+// formula, so the kernel computes the adjoint of the recurrence. With
+// g_t = dL/dh_t and k_t = a_t g_t (the part of g_t that reaches step t-1):
+//   g_t = dy_t C_t + k_{t+1},          k_L = 0
+//   dx_t     = delta_t sum_n g_t B_t + D dy_t
+//   ddelta_t = x_t sum_n g_t B_t + sum_n A g_t a_t h_{t-1}
+//   dB_t[n]  = sum_e g_t delta_t x_t      dC_t[n] = sum_e dy_t h_t
+//   dA[e,n]  = sum_{b,t} delta_t g_t a_t h_{t-1}
+//   dD[e]    = sum_{b,t} dy_t x_t          dh0 = k_0
+//
+// Work: one workgroup per (batch row, 16 consecutive channels), the lane
+// layout of the forward kernel (lane = 16 r + 4 g + c holds channel 4 r + c
+// and states 4 g .. 4 g + 3), SEG waves, each owning TS consecutive steps of
+// a round of RT = SEG * TS steps.
+//   sweep 1 (increasing rounds): the forward scan's round aggregates only
+//     (no per-step replay, no output); the state entering each round is
+//     written to a workspace checkpoint.
+//   sweep 2 (decreasing rounds): per round, the forward states are rebuilt
+//     from the checkpoint (local pass, fold, replay that keeps h_{t-1} of
+//     every step in registers), then the adjoint runs backward in time the
+//     same way (local pass from a zero carry, fold over the later segments
+//     and the next round's carry, replay) and every gradient term of the step
+//     is formed in the replay. Sums over the lane's 4 states and over the 4
+//     state quads of a channel go through DPP; sums over the 16 channels of
+//     dB and dC go through DPP (over the quad) and LDS (over the 4 lane rows)
+//     into per-workgroup partials that a second kernel adds up in a fixed
+//     order (no atomics: the result is deterministic).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "scan_common.h"
+#include "ssm_scan.h"
+
+namespace {
+
+constexpr int kBSEG = 4, kBTS = 8, kBRT = kBSEG * kBTS;
+
+template <typename T>
+struct BwdArgs {
+  const T* x;
+  const T* dl;
+  const float* A;
+  const T* B;
+  const T* C;
+  const float* D;    // or nullptr
+  const float* h0;   // or nullptr
+  const T* dy;
+  T* dx;
+  T* ddl;
+  float* dh0;        // or nullptr
+  float* ckpt;       // [Bs][rounds][EDp][16]: state entering each round (round 0 unused)
+  float* pB;         // [ngroups][Bs][L][16]: dB partial of each channel group
+  float* pC;         // same for dC
+  float* pA;         // [Bs][EDp][16]: dA partial of each batch row
+  float* pD;         // [Bs][EDp]: dD partial of each batch row
+  int64_t Bs, L, ED, EDp, rounds;
+  int ngroups;
+  int nblocks;
+  int remap;
+};
+
+template <int RT>
+struct alignas(16) BwdTile {
+  float dt[RT][16];  // delta per channel
+  float xv[RT][16];  // x per channel
+  float dy[RT][16];  // dL/dy per channel
+  float2 bc[RT][16]; // (B_t[q], C_t[q])
+};
+
+template <int RT>
+struct alignas(16) ColSums {
+  float v[RT][4][2][16];  // [step][lane row r][dB, dC][state]: sums over the row's 4 channels
+};
+
+template <int SEG>
+struct alignas(16) BwdFold {
+  float4 A[SEG][64];   // prod of a over each segment
+  float4 H[SEG][64];   // forward: segment end state from zero
+  float4 K[SEG][64];   // adjoint: k at the segment start from a zero carry
+  float4 kc[2][64];    // adjoint carry between rounds, by round parity
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;  // row_ror:4
+constexpr int kRowRor8 = 0x128;  // row_ror:8
+
+// sum over the 4 lanes of a quad (every lane gets the sum)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  return v + dpp<kQuadXor2>(v);
+}
+// sum over the lanes 4 apart in a row (the 4 state quads of a channel)
+__device__ __forceinline__ float bank_sum(float v) {
+  v += dpp<kRowRor4>(v);
+  return v + dpp<kRowRor8>(v);
+}
+
+// Staging: one task per thread. Threads 0 .. 4 RT - 1 own a (row, 4-channel
+// chunk) of x / delta / dy, the others a (row, 4-state chunk) of B / C.
+template <typename T, int RT, bool VEC>
+struct BwdStager {
+  int row, chk;
+  bool is_xd, chunk_ok, row_ok;
+  float4 ra, rb, rc;
+  int64_t b, e0, ED, L;
+
+  __device__ __forceinline__ void init(int tid, int64_t b_, int64_t e0_, int64_t ED_, int64_t L_) {
+    int u = tid;
+    is_xd = u < 4 * RT;
+    if (!is_xd) u -= 4 * RT;
+    row = u >> 2;
+    chk = u & 3;
+    b = b_, e0 = e0_, ED = ED_, L = L_;
+    chunk_ok = !is_xd || e0 + 4 * chk < ED;
+  }
+
+  // global -> registers for round rr; WITH_ADJ also loads dy and C
+  template <bool WITH_ADJ>
+  __device__ __forceinline__ void prefetch(const BwdArgs<T>& p, int64_t rr) {
+    const int64_t t = rr * RT + row;
+    row_ok = t < L;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, cc = a;
+    if (row_ok && chunk_ok) {
+      if (!is_xd) {
+        const int64_t off = (b * L + t) * 16 + 4 * chk;
+        a = Vec4<T>::load(p.B + off);
+        if (WITH_ADJ) bb = Vec4<T>::load(p.C + off);
+      } else {
+        const int64_t ce = e0 + 4 * chk;
+        const int64_t off = (b * L + t) * ED + ce;
+        if (VEC) {
+          a = Vec4<T>::load(p.x + off);
+          bb = Vec4<T>::load(p.dl + off);
+          if (WITH_ADJ) cc = Vec4<T>::load(p.dy + off);
+        } else {
+          a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
+                          ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
+          bb = make_float4(to_f32(p.dl[off]), ce + 1 < ED ? to_f32(p.dl[off + 1]) : 0.f,
+                           ce + 2 < ED ? to_f32(p.dl[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dl[off + 3]) : 0.f);
+          if (WITH_ADJ)
+            cc = make_float4(to_f32(p.dy[off]), ce + 1 < ED ? to_f32(p.dy[off + 1]) : 0.f,
+                             ce + 2 < ED ? to_f32(p.dy[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dy[off + 3]) : 0.f);
+        }
+      }
+    }
+    ra = a, rb = bb, rc = cc;
+  }
+
+  // registers -> LDS tile (padded rows and channels are zero: delta = 0
+  // gives a = 1 and b = 0, dy = 0 gives no adjoint input)
+  template <bool WITH_ADJ>
+  __device__ __forceinline__ void commit(BwdTile<RT>& tl) const {
+    const int c4 = 4 * chk;
+    if (is_xd) {
+      *reinterpret_cast<float4*>(&tl.xv[row][c4]) = ra;
+      *reinterpret_cast<float4*>(&tl.dt[row][c4]) = rb;
+      if (WITH_ADJ) *reinterpret_cast<float4*>(&tl.dy[row][c4]) = rc;
+    } else {
+      *reinterpret_cast<float4*>(&tl.bc[row][c4]) = make_float4(ra.x, rb.x, ra.y, rb.y);
+      *reinterpret_cast<float4*>(&tl.bc[row][c4 + 2]) = make_float4(ra.z, rb.z, ra.w, rb.w);
+    }
+  }
+};
+
+// dB / dC partials of round rr (their column sums are in cs) -> workspace
+template <typename T, int RT>
+__device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums<RT>& cs, int tid, int64_t b,
+                                              int64_t grp, int64_t rr) {
+  const int tt = tid >> 3, qq = (tid >> 2) & 1, n4 = 4 * (tid & 3);
+  const int64_t t = rr * RT + tt;
+  if (t >= p.L) return;
+  float4 s = *reinterpret_cast<const float4*>(&cs.v[tt][0][qq][n4]);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float4 v = *reinterpret_cast<const float4*>(&cs.v[tt][r][qq][n4]);
+    s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+  }
+  float* dst = qq ? p.pC : p.pB;
+  *reinterpret_cast<float4*>(dst + ((grp * p.Bs + b) * p.L + t) * 16 + n4) = s;
+}
+
+template <typename T, int SEG, int TS, bool VEC>
+__global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
+    const BwdArgs<T> p) {
+  constexpr int RT = SEG * TS;
+  static_assert(SEG * 64 == 8 * RT, "one staging task per thread");
+
+  __shared__ BwdTile<RT> tile[2];
+  __shared__ ColSums<RT> cs;
+  __shared__ BwdFold<SEG> fa;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 15;
+  const int g = q >> 2;
+  const int c = q & 3;
+  const int lrow = lane >> 4;
+  const int ch = (lrow << 2) | c;
+  const int64_t L = p.L, ED = p.ED;
+
+  int blk = blockIdx.x;
+  if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
+  const int64_t b = blk / p.ngroups;
+  const int64_t grp = blk % p.ngroups;
+  const int64_t e0 = grp * 16;
+  const int64_t R = p.rounds;
+
+  const int64_t e = e0 + ch;
+  const bool ch_ok = e < ED;
+  const int64_t ec = ch_ok ? e : ED - 1;
+  float A2[4], Ar[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    Ar[j] = p.A[ec * 16 + 4 * g + j];
+    A2[j] = Ar[j] * kLog2e;
+  }
+  const float Dv = (p.D && ch_ok) ? p.D[e] : 0.f;
+
+  BwdStager<T, RT, VEC> st;
+  st.init(tid, b, e0, ED, L);
+  // checkpoint of round rr for this lane's 4 states
+  auto ck = [&](int64_t rr) { return p.ckpt + ((b * R + rr) * p.EDp + e) * 16 + 4 * g; };
+
+  // ---- sweep 1: forward round aggregates -> checkpoints --------------------
+  if (R > 1) {
+    float hc[4] = {0.f, 0.f, 0.f, 0.f};  // state entering the round (wave SEG-1)
+    if (p.h0 && ch_ok) {
+      const float4 v = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
+      hc[0] = v.x, hc[1] = v.y, hc[2] = v.z, hc[3] = v.w;
+    }
+    st.template prefetch<false>(p, 0);
+    st.template commit<false>(tile[0]);
+    __syncthreads();
+    for (int64_t r = 0; r + 1 < R; ++r) {
+      BwdTile<RT>& cur = tile[r & 1];
+      BwdTile<RT>& nxt = tile[(r + 1) & 1];
+      if (r + 2 < R) st.template prefetch<false>(p, r + 1);
+      float hl[4], sd;
+#pragma unroll
+      for (int i = 0; i < TS; ++i) {
+        const int row = wave * TS + i;
+        const float dt = cur.dt[row][ch], dxv = dt * cur.xv[row][ch];
+        const float bq = cur.bc[row][q].x;
+        sd = i == 0 ? dt : sd + dt;
+        const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float bv = dxv * bb[j];
+          hl[j] = i == 0 ? bv : __builtin_fmaf(__builtin_amdgcn_exp2f(dt * A2[j]), hl[j], bv);
+        }
+      }
+      fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
+                                     __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
+      fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+      __syncthreads();
+      if (wave == SEG - 1) {
+        for (int k = 0; k < SEG; ++k) {
+          const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane];
+          hc[0] = __builtin_fmaf(Ak.x, hc[0], Hk.x);
+          hc[1] = __builtin_fmaf(Ak.y, hc[1], Hk.y);
+          hc[2] = __builtin_fmaf(Ak.z, hc[2], Hk.z);
+          hc[3] = __builtin_fmaf(Ak.w, hc[3], Hk.w);
+        }
+        *reinterpret_cast<float4*>(ck(r + 1)) = make_float4(hc[0], hc[1], hc[2], hc[3]);
+      }
+      if (r + 2 < R) st.template commit<false>(nxt);
+      __syncthreads();
+    }
+  }
+
+  // ---- sweep 2: rounds in decreasing order --------------------------------
+  float dA[4] = {0.f, 0.f, 0.f, 0.f};
+  float dDacc = 0.f;
+  float kcar[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint carry out of round 0 (wave 0)
+  if (wave == 0) fa.kc[R & 1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+  st.template prefetch<true>(p, R - 1);
+  st.template commit<true>(tile[(R - 1) & 1]);
+  __syncthreads();
+  for (int64_t r = R - 1; r >= 0; --r) {
+    BwdTile<RT>& cur = tile[r & 1];
+    BwdTile<RT>& nxt = tile[(r + 1) & 1];  // round r-1 has the other parity
+    if (r >= 1) st.template prefetch<true>(p, r - 1);
+    if (r + 1 < R) store_colsums(p, cs, tid, b, grp, r + 1);
+
+    // forward local pass from a zero state
+    float av[TS][4], hv[TS][4];  // a_t; b_t, then h_{t-1}
+    float hl[4], sd;
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+      const int row = wave * TS + i;
+      const float dt = cur.dt[row][ch], dxv = dt * cur.xv[row][ch];
+      const float bq = cur.bc[row][q].x;
+      sd = i == 0 ? dt : sd + dt;
+      const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
+        hv[i][j] = dxv * bb[j];
+        hl[j] = i == 0 ? hv[i][j] : __builtin_fmaf(av[i][j], hl[j], hv[i][j]);
+      }
+    }
+    const float4 Aseg = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
+                                    __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
+    fa.A[wave][lane] = Aseg;
+    fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+    __syncthreads();
+
+    // state entering the segment: the round's checkpoint through segments 0 .. wave-1
+    float hin[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r > 0) {
+      const float4 v = *reinterpret_cast<const float4*>(ck(r));
+      hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
+    } else if (p.h0 && ch_ok) {
+      const float4 v = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
+      hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
+    }
+    for (int k = 0; k < wave; ++k) {
+      const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane];
+      hin[0] = __builtin_fmaf(Ak.x, hin[0], Hk.x);
+      hin[1] = __builtin_fmaf(Ak.y, hin[1], Hk.y);
+      hin[2] = __builtin_fmaf(Ak.z, hin[2], Hk.z);
+      hin[3] = __builtin_fmaf(Ak.w, hin[3], Hk.w);
+    }
+    // forward replay: hv[i] <- h_{t-1} of step i; hin ends as the segment's last state
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float hp = hin[j];
+        hin[j] = __builtin_fmaf(av[i][j], hin[j], hv[i][j]);
+        hv[i][j] = hp;
+      }
+    }
+
+    // adjoint local pass from a zero carry: k at the segment start
+    float kl[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = TS - 1; i >= 0; --i) {
+      const int row = wave * TS + i;
+      const float dyv = cur.dy[row][ch];
+      const float cq = cur.bc[row][q].y;
+      float gg[4];
+      gg[0] = fmac_quad<0>(kl[0], cq, dyv);
+      gg[1] = fmac_quad<1>(kl[1], cq, dyv);
+      gg[2] = fmac_quad<2>(kl[2], cq, dyv);
+      gg[3] = fmac_quad<3>(kl[3], cq, dyv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kl[j] = av[i][j] * gg[j];
+    }
+    fa.K[wave][lane] = make_float4(kl[0], kl[1], kl[2], kl[3]);
+    __syncthreads();
+
+    // adjoint carry entering the segment's end: the next round's carry through
+    // segments SEG-1 .. wave+1
+    const float4 k0 = fa.kc[(r + 1) & 1][lane];
+    float kin[4] = {k0.x, k0.y, k0.z, k0.w};
+    for (int k = SEG - 1; k > wave; --k) {
+      const float4 Ak = fa.A[k][lane], Kk = fa.K[k][lane];
+      kin[0] = __builtin_fmaf(Ak.x, kin[0], Kk.x);
+      kin[1] = __builtin_fmaf(Ak.y, kin[1], Kk.y);
+      kin[2] = __builtin_fmaf(Ak.z, kin[2], Kk.z);
+      kin[3] = __builtin_fmaf(Ak.w, kin[3], Kk.w);
+    }
+
+    // adjoint replay and the gradient terms of every step
+    float hnext[4] = {hin[0], hin[1], hin[2], hin[3]};  // h_t of the step being processed
+#pragma unroll
+    for (int i = TS - 1; i >= 0; --i) {
+      const int row = wave * TS + i;
+      const int64_t t = r * RT + row;
+      const float dt = cur.dt[row][ch], xv = cur.xv[row][ch], dyv = cur.dy[row][ch];
+      const float dxv = dt * xv;
+      const float2 bcv = cur.bc[row][q];
+      const float bq = bcv.x, cq = bcv.y;
+      float gg[4];
+      gg[0] = fmac_quad<0>(kin[0], cq, dyv);
+      gg[1] = fmac_quad<1>(kin[1], cq, dyv);
+      gg[2] = fmac_quad<2>(kin[2], cq, dyv);
+      gg[3] = fmac_quad<3>(kin[3], cq, dyv);
+      // sum_n g B (this lane's 4 states)
+      float s1 = quad_bcast<0>(bq) * gg[0];
+      s1 = fmac_quad<1>(s1, bq, gg[1]);
+      s1 = fmac_quad<2>(s1, bq, gg[2]);
+      s1 = fmac_quad<3>(s1, bq, gg[3]);
+      float s2 = 0.f, pb[4], pc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float qv = gg[j] * av[i][j] * hv[i][j];  // g a h_{t-1}
+        s2 = __builtin_fmaf(Ar[j], qv, s2);
+        dA[j] = __builtin_fmaf(dt, qv, dA[j]);
+        pb[j] = dxv * gg[j];
+        pc[j] = dyv * hnext[j];
+        kin[j] = av[i][j] * gg[j];
+        hnext[j] = hv[i][j];
+      }
+      dDacc = __builtin_fmaf(dyv, xv, dDacc);
+      s1 = bank_sum(s1);
+      s2 = bank_sum(s2);
+      if (g == 0 && ch_ok && t < L) {
+        const int64_t off = (b * L + t) * ED + e;
+        p.dx[off] = from_f32<T>(__builtin_fmaf(dt, s1, Dv * dyv));
+        p.ddl[off] = from_f32<T>(__builtin_fmaf(xv, s1, s2));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pb[j] = quad_sum(pb[j]);
+        pc[j] = quad_sum(pc[j]);
+      }
+      if (c == 0) {
+        *reinterpret_cast<float4*>(&cs.v[row][lrow][0][4 * g]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
+        *reinterpret_cast<float4*>(&cs.v[row][lrow][1][4 * g]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
+      }
+    }
+    if (wave == 0) {
+      fa.kc[r & 1][lane] = make_float4(kin[0], kin[1], kin[2], kin[3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kcar[j] = kin[j];
+    }
+    if (r >= 1) st.template commit<true>(nxt);
+    __syncthreads();
+  }
+  store_colsums(p, cs, tid, b, grp, 0);
+
+  // ---- per-workgroup results ----------------------------------------------
+  if (p.dh0 && wave == 0 && ch_ok)
+    *reinterpret_cast<float4*>(p.dh0 + (b * ED + e) * 16 + 4 * g) = make_float4(kcar[0], kcar[1], kcar[2], kcar[3]);
+  // dA and dD: sums over the waves' segments, then one partial per batch row
+  fa.A[wave][lane] = make_float4(dA[0], dA[1], dA[2], dA[3]);
+  fa.H[wave][lane] = make_float4(dDacc, 0.f, 0.f, 0.f);
+  __syncthreads();
+  if (wave == 0) {
+    float4 s = fa.A[0][lane];
+    float sdd = fa.H[0][lane].x;
+    for (int k = 1; k < SEG; ++k) {
+      const float4 v = fa.A[k][lane];
+      s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+      sdd += fa.H[k][lane].x;
+    }
+    *reinterpret_cast<float4*>(p.pA + (b * p.EDp + e) * 16 + 4 * g) = s;
+    if (g == 0) p.pD[b * p.EDp + e] = sdd;
+  }
+}
+
+// dB, dC: sum of the channel groups' partials, in group order.
+template <typename T>
+__global__ void bwd_reduce_bc_kernel(const float* __restrict__ pB, const float* __restrict__ pC, T* dB, T* dC,
+                                     int64_t n4, int ngroups) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;  // float4 index
+  if (i >= 2 * n4) return;
+  const bool isC = i >= n4;
+  const int64_t k = isC ? i - n4 : i;
+  const float* src = isC ? pC : pB;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const float4 v = reinterpret_cast<const float4*>(src)[gi * n4 + k];
+    s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+  }
+  Vec4<T>::store((isC ? dC : dB) + 4 * k, s);
+}
+
+// dA, dD: sum of the batch rows' partials, in row order.
+__global__ void bwd_reduce_ad_kernel(const float* __restrict__ pA, const float* __restrict__ pD, float* dA,
+                                     float* dD, int64_t Bs, int64_t ED, int64_t EDp) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i < ED * 16) {
+    const int64_t e = i >> 4, n = i & 15;
+    float s = 0.f;
+    for (int64_t b = 0; b < Bs; ++b) s += pA[(b * EDp + e) * 16 + n];
+    dA[i] = s;
+  } else if (dD && i < ED * 17) {
+    const int64_t e = i - ED * 16;
+    float s = 0.f;
+    for (int64_t b = 0; b < Bs; ++b) s += pD[b * EDp + e];
+    dD[e] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct BwdLayout {
+  int64_t rounds, ngroups, EDp;
+  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, bytes;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo) {
+  lo->rounds = (L + kBRT - 1) / kBRT;
+  lo->ngroups = (ED + 15) / 16;
+  lo->EDp = lo->ngroups * 16;
+  // every count below is checked against overflow of size_t arithmetic
+  const double total = 4.0 * (static_cast<double>(Bs) * lo->rounds * lo->EDp * 16 +
+                              2.0 * lo->ngroups * Bs * L * 16 + Bs * lo->EDp * 17) + 5 * 256.0;
+  if (total > 9.0e18) return false;
+  size_t off = 0;
+  lo->ckpt_off = off;
+  off = align256(off + static_cast<size_t>(Bs * lo->rounds * lo->EDp * 16) * 4);
+  lo->pB_off = off;
+  off = align256(off + static_cast<size_t>(lo->ngroups * Bs * L * 16) * 4);
+  lo->pC_off = off;
+  off = align256(off + static_cast<size_t>(lo->ngroups * Bs * L * 16) * 4);
+  lo->pA_off = off;
+  off = align256(off + static_cast<size_t>(Bs * lo->EDp * 16) * 4);
+  lo->pD_off = off;
+  off = align256(off + static_cast<size_t>(Bs * lo->EDp) * 4);
+  lo->bytes = off;
+  return true;
+}
+
+struct BwdSizes {
+  int64_t seq, bc, state, elem;
+};
+
+int bwd_check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, BwdSizes* s) {
+  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return SSM_ERR_DIM;
+  int64_t t;
+  if (!mul_ok(Bs, L, &t) || !mul_ok(t, ED, &s->seq) || !mul_ok(t, N, &s->bc)) return SSM_ERR_DIM;
+  if (!mul_ok(Bs, ED, &t) || !mul_ok(t, N, &s->state)) return SSM_ERR_DIM;
+  if (s->seq > INT64_MAX / 8 || s->state > INT64_MAX / 8 || s->bc > INT64_MAX / 8 / ((ED + 15) / 16 + 1))
+    return SSM_ERR_DIM;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (N != 16) return SSM_ERR_UNSUPPORTED;
+  s->elem = dtype == SSM_F32 ? 4 : 2;
+  return SSM_OK;
+}
+
+size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
+  BwdSizes s;
+  BwdLayout lo;
+  if (bwd_check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || !bwd_layout(Bs, L, ED, &lo)) return 0;
+  return lo.bytes;
+}
+
+int bwd_validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const float* h0, const void* dy, const void* dx, const void* ddelta, const float* dA, const void* dB,
+                 const void* dC, const float* dD, const float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                 int dtype, const void* ws, size_t ws_bytes, BwdSizes* s) {
+  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return SSM_ERR_NULL;
+  int rc = bwd_check_sizes(Bs, L, ED, N, dtype, s);
+  if (rc != SSM_OK) return rc;
+  const void* ptrs[] = {x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, ws};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
+  BwdLayout lo;
+  if (!bwd_layout(Bs, L, ED, &lo)) return SSM_ERR_DIM;
+  if (!ws || ws_bytes < lo.bytes) return SSM_ERR_WORKSPACE;
+  const Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
+                      rng(B, s->bc * s->elem),  rng(C, s->bc * s->elem),      rng(D, D ? ED * 4 : 0),
+                      rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem)};
+  const Range out[] = {rng(dx, s->seq * s->elem), rng(ddelta, s->seq * s->elem), rng(dA, ED * N * 4),
+                       rng(dB, s->bc * s->elem),  rng(dC, s->bc * s->elem),      rng(dD, dD ? ED * 4 : 0),
+                       rng(dh0, dh0 ? s->state * 4 : 0), rng(ws, static_cast<int64_t>(lo.bytes))};
+  constexpr int nout = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < nout; ++i) {
+    if (out[i].hi == out[i].lo) continue;
+    for (const Range& r : in)
+      if (r.hi > r.lo && overlap(out[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (out[j].hi > out[j].lo && overlap(out[i], out[j])) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
+template <typename T>
+int launch_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+               const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+               float* dh0, int64_t Bs, int64_t L, int64_t ED, void* ws, hipStream_t stream) {
+  BwdLayout lo;
+  bwd_layout(Bs, L, ED, &lo);
+  const int64_t nblk = Bs * lo.ngroups;
+  if (nblk > INT32_MAX / 2) return SSM_ERR_DIM;
+  char* w = static_cast<char*>(ws);
+  BwdArgs<T> a;
+  a.x = static_cast<const T*>(x);
+  a.dl = static_cast<const T*>(delta);
+  a.A = A;
+  a.B = static_cast<const T*>(B);
+  a.C = static_cast<const T*>(C);
+  a.D = D;
+  a.h0 = h0;
+  a.dy = static_cast<const T*>(dy);
+  a.dx = static_cast<T*>(dx);
+  a.ddl = static_cast<T*>(ddelta);
+  a.dh0 = dh0;
+  a.ckpt = reinterpret_cast<float*>(w + lo.ckpt_off);
+  a.pB = reinterpret_cast<float*>(w + lo.pB_off);
+  a.pC = reinterpret_cast<float*>(w + lo.pC_off);
+  a.pA = reinterpret_cast<float*>(w + lo.pA_off);
+  a.pD = reinterpret_cast<float*>(w + lo.pD_off);
+  a.Bs = Bs;
+  a.L = L;
+  a.ED = ED;
+  a.EDp = lo.EDp;
+  a.rounds = lo.rounds;
+  a.ngroups = static_cast<int>(lo.ngroups);
+  a.nblocks = static_cast<int>(nblk);
+  a.remap = (nblk % 8 == 0) ? 1 : 0;
+
+  const size_t lds = sizeof(BwdTile<kBRT>) * 2 + sizeof(ColSums<kBRT>) + sizeof(BwdFold<kBSEG>) + 16;
+  const size_t dyn = spread_lds(nblk, lds, 16 / kBSEG);
+  if (ED % 4 == 0)
+    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, false>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
+
+  const int64_t n4 = Bs * L * 4;  // float4s per dB (or dC)
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3(static_cast<unsigned>((2 * n4 + 255) / 256)), dim3(256), 0,
+                     stream, a.pB, a.pC, static_cast<T*>(dB), static_cast<T*>(dC), n4, a.ngroups);
+  if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
+  hipLaunchKernelGGL(bwd_reduce_ad_kernel, dim3(static_cast<unsigned>((ED * 17 + 255) / 256)), dim3(256), 0, stream,
+                     a.pA, a.pD, dA, dD, Bs, ED, lo.EDp);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
+  return bwd_workspace_bytes(Bs, L, ED, N, dtype);
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                 float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  BwdSizes s;
+  const int rc = bwd_validate(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype,
+                              workspace, workspace_bytes, &s);
+  if (rc != SSM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == SSM_F32)
+    return launch_bwd<float>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace, st);
+  return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace,
+                              st);
+}
+
+}  // extern "C"

@@ -96,3 +96,34 @@ def gather_channels(y, chans, ED):
     """y (Bs, L, ED) -> (len(chans), L) in the oracle's channel-major order."""
     b, e = np.divmod(chans, ED)
     return y[b, :, e]
+
+
+def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None):
+    """ssm_scan_bwd on the GPU; every gradient as a float64 numpy array."""
+    import torch
+    import state_space_model_selective_amd as ssm
+    dev = torch.device("cuda:0")
+    t = to_device(dict(inp, dy=dy), dev)
+    h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, dtype=np.float32)).to(dev)
+    # outputs start as NaN so that an element the kernels never write shows
+    out = {}
+    for k, ref in (("dx", t["x"]), ("ddelta", t["x"]), ("dA", t["A"]), ("dB", t["B"]), ("dC", t["B"])):
+        out[k] = torch.full_like(ref, float("nan"))
+    Bs, L, ED = inp["x"].shape
+    N = inp["A"].shape[1]
+    if want_dD:
+        out["dD"] = torch.full((ED,), float("nan"), dtype=torch.float32, device=dev)
+    if want_dh0:
+        out["dh0"] = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev)
+    res = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
+                           h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream)
+    torch.cuda.synchronize()
+    return {k: y_to_numpy(v) for k, v in res.items()}
+
+
+def assert_grads_close(got, ref, dtype):
+    """Every gradient the GPU returned against the oracle's. dx, ddelta, dB
+    and dC carry the inputs' dtype; dA, dD and dh0 are float32."""
+    for k, v in got.items():
+        tol = TOL[dtype] if k in ("dx", "ddelta", "dB", "dC") else TOL["f32"]
+        assert_close(k, v, ref[k], tol)

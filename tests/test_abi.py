@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
 
 # fake device addresses, 16-byte aligned and far apart; only used on paths that
 # must fail validation before anything touches them
-P = [0x10000000 * (i + 1) for i in range(12)]
+P = [0x10000000 * (i + 1) for i in range(20)]
 
 
 def declared_functions():
@@ -132,3 +132,48 @@ def test_options_validation():
     assert fwd(opts=ref) == ssm.SSM_ERR_UNSUPPORTED
     ref, _ = opts(dt_bias=P[7])                         # h_last on top of the bias
     assert fwd(opts=ref) == ssm.SSM_ERR_ALIAS
+
+
+BWD_PTRS = ["x", "delta", "A", "B", "C", "D", "h0", "dy", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0", "ws"]
+
+
+def bwd(**kw):
+    args = {n: P[i] for i, n in enumerate(BWD_PTRS)}
+    args.update(Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32)
+    args["ws_bytes"] = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32)
+    args.update(kw)
+    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_PTRS[:15]], args["Bs"], args["L"], args["ED"], args["N"],
+                                  args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bwd_workspace_size():
+    need = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32)
+    # checkpoints (2 rows x 2 rounds x 64 channels x 16 states), dB and dC
+    # partials (4 groups x 2 x 64 x 16 each), dA and dD partials, all float32
+    assert need >= 4 * (2 * 2 * 64 * 16 + 2 * 4 * 2 * 64 * 16 + 2 * 64 * 17)
+    assert ssm.ssm_scan_bwd_workspace_bytes(0, 64, 64, 16, ssm.SSM_F32) == 0
+    assert ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 8, ssm.SSM_F32) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "dy", "dx", "ddelta", "dA", "dB", "dC"])
+def test_bwd_null_pointer(name):
+    assert bwd(**{name: None}) == ssm.SSM_ERR_NULL
+
+
+def test_bwd_optional_pointers_may_be_null():
+    # D, h0, dD, dh0 are optional: with them NULL the call gets past the NULL
+    # check and fails only on the fake (misaligned) workspace below
+    assert bwd(D=None, h0=None, dD=None, dh0=None, ws=P[15] + 4) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_bwd_validation():
+    assert bwd(L=0) == ssm.SSM_ERR_DIM
+    assert bwd(N=8) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(dtype=3) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(dB=P[11] + 4) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(ws=None) == ssm.SSM_ERR_WORKSPACE
+    assert bwd(ws_bytes=1024) == ssm.SSM_ERR_WORKSPACE
+    assert bwd(dx=P[0]) == ssm.SSM_ERR_ALIAS              # dx on top of x
+    assert bwd(ddelta=P[8] + 256) == ssm.SSM_ERR_ALIAS    # ddelta inside dx
+    assert bwd(dh0=P[6]) == ssm.SSM_ERR_ALIAS             # dh0 on top of h0
+    assert bwd(ws=P[7]) == ssm.SSM_ERR_ALIAS              # workspace on top of dy

@@ -1,0 +1,70 @@
+"""GPU parity of the backward pass (ssm_scan_bwd) against the oracle's
+adjoint (oracle.scan_bwd) on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity_util import assert_grads_close, log, run_gpu_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+def check(Bs, L, ED, dtype="f32", seed=0, h0=False, D_none=False, want_dD=True):
+    log("bwd case Bs=%d L=%d ED=%d dtype=%s seed=%d h0=%s D_none=%s" % (Bs, L, ED, dtype, seed, h0, D_none))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=seed)
+    dy = synth.make_output_grad(Bs, L, ED, dtype, seed=seed)
+    h = synth.normal(seed, 79, (Bs, ED, 16)) if h0 else None
+    got = run_gpu_bwd(inp, dy, h0=h, D_none=D_none, want_dD=want_dD, want_dh0=True)
+    ref_inp = dict(inp, D=None) if D_none else inp
+    ref = oracle.scan_bwd(**ref_inp, dy=dy, h0=h)
+    assert_grads_close(got, ref, dtype)
+    return got
+
+
+def test_page_shape():
+    check(2, 64, 64)
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 64, 65, 200, 1009])
+def test_sequence_lengths(L):
+    check(2, L, 64, seed=L)
+
+
+@pytest.mark.parametrize("ED", [16, 20, 48, 100, 130])
+def test_channel_counts(ED):
+    check(2, 77, ED, seed=ED)
+
+
+def test_bf16():
+    check(2, 300, 96, dtype="bf16", seed=5)
+
+
+def test_initial_state():
+    check(2, 150, 64, seed=6, h0=True)
+
+
+def test_no_D():
+    check(2, 70, 32, seed=7, D_none=True)
+
+
+def test_no_dD():
+    check(2, 70, 32, seed=8, want_dD=False)
+
+
+def test_many_batch_rows():
+    check(9, 40, 48, seed=9)
+
+
+def test_repeatable_bits():
+    inp = synth.make_inputs(3, 257, 80, 16, "f32", seed=10)
+    dy = synth.make_output_grad(3, 257, 80, "f32", seed=10)
+    a = run_gpu_bwd(inp, dy, want_dh0=True)
+    b = run_gpu_bwd(inp, dy, want_dh0=True)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_training_shape_full():
+    # the forward training shape (Bs 8, L 1024, ED 1536, N 16), every gradient compared in full
+    check(8, 1024, 1536, seed=11, h0=True)
