@@ -225,37 +225,45 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
  *     dB[b,t,n] = sum_e g_t[n] delta_t x_t
  *     dA[e,n] = sum_{b,t} g_t[n] a_t[n] h_{t-1}[n] delta_t
  *     dh0 = a_0 g_0 (h_{-1} = h0)
- * Work is split over batch rows (dB, dC of a row come from one thread);
- * dA and dD are summed over rows in row order afterwards. Outputs are fp64:
+ * Rows are done one after the other; the channels of a row are cut into
+ * fixed blocks of 64 that threads share. dB and dC of a row are the sums of
+ * the blocks' partial sums in block order, and dA and dD the sums of the
+ * rows' in row order, so the result does not depend on the thread count. Outputs are fp64:
  * dx, ddelta (Bs, L, ED); dA (ED, N); dB, dC (Bs, L, N); dD (ED);
  * dh0 (Bs, ED, N) or NULL. y is affine in h0, so dh0 does not depend on h0
  * and is returned for h0 = NULL (the zero initial state) as well.
  */
+enum { BWD_BLOCK = 64 }; /* channels per work item */
+
 typedef struct {
   int dtype;
   const void *x, *delta, *B, *C, *dy;
   const float *A, *D, *h0;
   int64_t Bs, L, ED, N;
-  double *dx, *ddelta, *dB, *dC, *dh0;
+  double *dx, *ddelta, *dh0;
   double *dA_part, *dD_part; /* per row: (Bs, ED, N), (Bs, ED) */
-  int64_t b0, b1;
+  double *partB, *partC;     /* per channel block of the current row: (nblk, L, N) */
+  int64_t b, blk0, blk1;     /* row, channel blocks [blk0, blk1) */
+  int fail;
 } bwd_t;
 
 static void* bwd_worker(void* p) {
   bwd_t* w = (bwd_t*)p;
-  const int64_t L = w->L, ED = w->ED, N = w->N;
+  const int64_t L = w->L, ED = w->ED, N = w->N, b = w->b;
   double* hs = (double*)malloc(sizeof(double) * (size_t)(L + 1) * N); /* h_{t-1} at row t */
   double* g = (double*)malloc(sizeof(double) * (size_t)N);
   if (!hs || !g) {
     free(hs);
     free(g);
-    return (void*)1;
+    w->fail = 1;
+    return NULL;
   }
-  for (int64_t b = w->b0; b < w->b1; ++b) {
-    for (int64_t n = 0; n < N; ++n) {
-      for (int64_t t = 0; t < L; ++t) w->dB[(b * L + t) * N + n] = 0.0, w->dC[(b * L + t) * N + n] = 0.0;
-    }
-    for (int64_t e = 0; e < ED; ++e) {
+  for (int64_t blk = w->blk0; blk < w->blk1; ++blk) {
+    double* pB = w->partB + blk * L * N;
+    double* pC = w->partC + blk * L * N;
+    for (int64_t i = 0; i < L * N; ++i) pB[i] = 0.0, pC[i] = 0.0;
+    const int64_t e1 = (blk + 1) * BWD_BLOCK < ED ? (blk + 1) * BWD_BLOCK : ED;
+    for (int64_t e = blk * BWD_BLOCK; e < e1; ++e) {
       /* forward, keeping every state */
       for (int64_t n = 0; n < N; ++n) hs[n] = w->h0 ? (double)w->h0[(b * ED + e) * N + n] : 0.0;
       for (int64_t t = 0; t < L; ++t) {
@@ -283,8 +291,8 @@ static void* bwd_worker(void* p) {
           g[n] += dyv * Cv;
           const double a = exp(dt * An);
           const double hprev = hs[t * N + n];
-          w->dC[ib + n] += dyv * hs[(t + 1) * N + n];
-          w->dB[ib + n] += g[n] * dt * xv;
+          pC[t * N + n] += dyv * hs[(t + 1) * N + n];
+          pB[t * N + n] += g[n] * dt * xv;
           dxv += g[n] * dt * Bv;
           ddv += g[n] * (xv * Bv + An * a * hprev);
           dA[n] += g[n] * a * hprev * dt;
@@ -311,45 +319,55 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC || !dD) return -1;
   if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const int64_t nblk = (ED + BWD_BLOCK - 1) / BWD_BLOCK;
   if (nthreads < 1) nthreads = 1;
-  if (nthreads > Bs) nthreads = (int)Bs;
+  if (nthreads > nblk) nthreads = (int)nblk;
   if (nthreads > 256) nthreads = 256;
   double* dA_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED * N));
   double* dD_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED));
+  double* partB = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N));
+  double* partC = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N));
   bwd_t* ws = (bwd_t*)malloc(sizeof(bwd_t) * (size_t)nthreads);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
   int rc = 0;
-  if (!dA_part || !dD_part || !ws || !th) {
-    rc = -2;
-  } else {
-    int64_t per = (Bs + nthreads - 1) / nthreads;
+  if (!dA_part || !dD_part || !partB || !partC || !ws || !th) rc = -2;
+  /* one batch row at a time; its channel blocks are split over the threads,
+     and dB, dC of the row are the sums of the blocks' partials in block order */
+  for (int64_t b = 0; rc == 0 && b < Bs; ++b) {
+    const int64_t per = (nblk + nthreads - 1) / nthreads;
     for (int i = 0; i < nthreads; ++i) {
-      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, Bs, L, ED, N, dx, ddelta, dB, dC,
-                      dh0, dA_part, dD_part, 0, 0};
-      ws[i].b0 = per * i < Bs ? per * i : Bs;
-      ws[i].b1 = per * (i + 1) < Bs ? per * (i + 1) : Bs;
+      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, Bs, L, ED, N, dx, ddelta,
+                      dh0, dA_part, dD_part, partB, partC, b, 0, 0, 0};
+      ws[i].blk0 = per * i < nblk ? per * i : nblk;
+      ws[i].blk1 = per * (i + 1) < nblk ? per * (i + 1) : nblk;
     }
     for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, bwd_worker, &ws[i]);
-    if (bwd_worker(&ws[0])) rc = -2;
-    for (int i = 1; i < nthreads; ++i) {
-      void* r = NULL;
-      pthread_join(th[i], &r);
-      if (r) rc = -2;
+    bwd_worker(&ws[0]);
+    for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i)
+      if (ws[i].fail) rc = -2;
+    for (int64_t i = 0; rc == 0 && i < L * N; ++i) {
+      double sb = 0.0, sc = 0.0;
+      for (int64_t k = 0; k < nblk; ++k) sb += partB[k * L * N + i], sc += partC[k * L * N + i];
+      dB[b * L * N + i] = sb;
+      dC[b * L * N + i] = sc;
     }
-    /* sums over batch rows, in row order */
-    for (int64_t i = 0; rc == 0 && i < ED * N; ++i) {
-      double s = 0.0;
-      for (int64_t b = 0; b < Bs; ++b) s += dA_part[b * ED * N + i];
-      dA[i] = s;
-    }
-    for (int64_t e = 0; rc == 0 && e < ED; ++e) {
-      double s = 0.0;
-      for (int64_t b = 0; b < Bs; ++b) s += dD_part[b * ED + e];
-      dD[e] = s;
-    }
+  }
+  /* sums over batch rows, in row order */
+  for (int64_t i = 0; rc == 0 && i < ED * N; ++i) {
+    double s = 0.0;
+    for (int64_t b = 0; b < Bs; ++b) s += dA_part[b * ED * N + i];
+    dA[i] = s;
+  }
+  for (int64_t e = 0; rc == 0 && e < ED; ++e) {
+    double s = 0.0;
+    for (int64_t b = 0; b < Bs; ++b) s += dD_part[b * ED + e];
+    dD[e] = s;
   }
   free(dA_part);
   free(dD_part);
+  free(partB);
+  free(partC);
   free(ws);
   free(th);
   return rc;

@@ -75,8 +75,10 @@ def test_backward_matches_finite_differences(name):
         assert abs(got - want) <= 1e-5 * (1.0 + abs(want)), (name, idx, got, want)
 
 
-def test_homogeneity_identities():
-    Bs, L, ED, N = 3, 40, 5, 6
+@pytest.mark.parametrize("ED", [5, 150])
+def test_homogeneity_identities(ED):
+    # ED = 150 spans three of the oracle's 64-channel work blocks
+    Bs, L, N = 3, 40, 6
     inp, dy, _ = inputs(Bs, L, ED, N, seed=4)
     dy64 = dy.astype(np.float64)
     x64 = inp["x"].astype(np.float64)
