@@ -2,7 +2,8 @@
 
 One step = one full pass of the scan (discretise, scan over L, C-contraction,
 D skip term, final state) over one batch of synthetic input already resident in
-device memory. Three input sets are rotated so that consecutive steps do not
+device memory; for a backward workload, one full backward pass (every
+gradient). Three input sets are rotated so that consecutive steps do not
 re-read a working set left in the 256 MB last-level cache.
 
 Prints ONE JSON line. `value` is scan elements (Bs*L*ED*N) per second;
@@ -32,11 +33,18 @@ VALU_SLOTS_PER_S = CUS * SIMDS * LANES * CLOCK_GHZ * 1e9
 # FMA, the C FMA (4 full-rate slots) + one v_exp_f32 (half rate on gfx950: 2)
 SLOTS_PER_ELEMENT = 6.0
 SLOTS_PER_ELEMENT_BIDIR = 8.0
+# backward: rebuild the state (delta*A, exp, (delta x)*B, state FMA: 5) and
+# the adjoint with its terms (g FMA, k = a g, dC and dB products, sum g B,
+# q = g a h_{t-1} (2), sum A q, dA += delta q: 9)
+SLOTS_PER_ELEMENT_BWD = 14.0
 
 
 def alg_bytes(w):
     s = 4 if w["dtype"] == "f32" else 2
     Bs, L, ED, N = w["Bs"], w["L"], w["ED"], w["N"]
+    if w.get("bwd"):
+        # read x, delta, dy, B, C, A, D; write dx, ddelta, dB, dC, dA, dD
+        return Bs * L * ED * 5 * s + 4 * Bs * L * N * s + 2 * (4 * ED * N + 4 * ED)
     b = Bs * L * ED * (2 * s + s) + 2 * Bs * L * N * s + 4 * ED * N + 4 * ED
     if w.get("h_last"):
         b += 4 * Bs * ED * N
@@ -92,6 +100,34 @@ def cpu_baseline(inp, w, budget_s=20.0):
                 sample=sample + " (fp64 sequential recurrence, %.2f s)" % dt), y_ref, chans
 
 
+def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
+    """The oracle's backward pass on the first batch rows of the workload (as
+    many as fit the time budget, at least one)."""
+    import numpy as np
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    Bs = w["Bs"]
+
+    def rows(k):
+        sub = {n: (v[:k] if v.ndim == 3 else v) for n, v in inp.items()}
+        return sub, dy[:k]
+
+    sub, dys = rows(1)
+    t0 = time.perf_counter()
+    ref = oracle.scan_bwd(**sub, dy=dys, nthreads=threads)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    k = int(min(Bs, max(1, budget_s / dt)))
+    if k > 1:
+        sub, dys = rows(k)
+        t0 = time.perf_counter()
+        ref = oracle.scan_bwd(**sub, dy=dys, nthreads=threads)
+        dt = time.perf_counter() - t0
+    E = k * w["L"] * w["ED"] * w["N"]
+    sample = ("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))
+    return dict(value=E / dt, unit="scan elements/s", cores=threads, kind="oracle",
+                sample=sample + " (fp64 forward states + adjoint, %.2f s)" % dt), ref, k
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,22 +174,35 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     nsets = 3
+    bwd = bool(w.get("bwd"))
+    dcode = ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16
     host_sets, sets = [], []
     for i in range(nsets):
         inp = synth.make_inputs(Bs, L, ED, N, w["dtype"], seed=i)
-        host_sets.append(inp if i == 0 else None)
         t = {k: to_dev(v) for k, v in inp.items()}
-        t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
-        t["h"] = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev) if w["h_last"] else None
-        need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16,
-                                            w["bidir"])
+        if bwd:
+            dy = synth.make_output_grad(Bs, L, ED, w["dtype"], seed=i)
+            t["dy"] = to_dev(dy)
+            host_sets.append((inp, dy) if i == 0 else None)
+            t["out"] = {"dx": torch.empty_like(t["x"]), "ddelta": torch.empty_like(t["x"]),
+                        "dA": torch.empty_like(t["A"]), "dB": torch.empty_like(t["B"]),
+                        "dC": torch.empty_like(t["C"]), "dD": torch.empty_like(t["D"])}
+            need = ssm.ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, dcode)
+        else:
+            host_sets.append(inp if i == 0 else None)
+            t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
+            t["h"] = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev) if w["h_last"] else None
+            need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, dcode, w["bidir"])
         t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         sets.append(t)
 
     stream = torch.cuda.current_stream(dev)
 
     def step(t):
-        if w["bidir"]:
+        if bwd:
+            ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
+                             workspace=t["ws"], stream=stream)
+        elif w["bidir"]:
             ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], h_last=t["h"],
                                    workspace=t["ws"], stream=stream)
         else:
@@ -185,7 +234,7 @@ def main():
     kernel_elem_rate = E / avg_launch_s
     # bidirectional: the exp and the two multiplies are shared by both
     # directions; algorithmic cost 2 mul + exp + 2 x (state FMA + C FMA) = 8
-    slots = SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT
+    slots = SLOTS_PER_ELEMENT_BWD if bwd else (SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT)
     achieved_slots = kernel_elem_rate * slots
     src_hash = kernel_source_hash()
     traffic = load_traffic(args.workload, src_hash)
@@ -193,7 +242,19 @@ def main():
     # parity check of step 0's input set against the oracle (also the CPU baseline)
     cpu = None
     parity = None
-    if not args.no_cpu:
+    if not args.no_cpu and bwd:
+        inp0, dy0 = host_sets[0]
+        cpu, ref, k = cpu_baseline_bwd(inp0, dy0, w)
+        step(sets[0])
+        torch.cuda.synchronize()
+        tol = 1e-4 if w["dtype"] == "f32" else 2e-2
+        rel = 0.0
+        for name in ("dx", "ddelta", "dB", "dC"):
+            got = sets[0]["out"][name][:k].float().cpu().numpy().astype(np.float64)
+            rel = max(rel, float(np.max(np.abs(got - ref[name]) / (1 + np.abs(ref[name])))))
+        parity = dict(max_rel_err=rel, tol=tol, passed=bool(rel <= tol),
+                      checked="dx, ddelta, dB, dC of the sampled batch rows")
+    elif not args.no_cpu:
         cpu, y_ref, chans = cpu_baseline(host_sets[0], w)
         step(sets[0])
         torch.cuda.synchronize()
@@ -220,9 +281,9 @@ def main():
         "vs_baseline": None,
         "dtype": w["dtype"],
         "data": "synthetic (seeded counter-based generator; x,B,C,D ~ N(0,1), delta log-uniform [1e-3,1e-1], "
-                "A[e,n] = -(n+1)); 3 input sets rotated",
+                "A[e,n] = -(n+1)" + ("; dy ~ N(0,1)" if bwd else "") + "); 3 input sets rotated",
         "config": {"workload": args.workload, "Bs": Bs, "L": L, "ED": ED, "N": N, "bidir": w["bidir"],
-                   "h_last": w["h_last"], "parallelism": "single GPU"},
+                   "h_last": w["h_last"], "backward": bwd, "parallelism": "single GPU"},
         "roofline": {
             "bound": "alu",
             "achieved": achieved_slots / 1e12,
@@ -231,6 +292,8 @@ def main():
             "frac": achieved_slots / VALU_SLOTS_PER_S,
             "traffic": traffic,
             "kernel_avg_us": avg_launch_s * 1e6,
+            "timed": ("whole backward step: the scan kernel and the two small kernels that add up the "
+                      "dB/dC and dA/dD partial sums") if bwd else "the scan kernel (one launch per step)",
             "slots_per_element": slots,
         },
         "hbm": {

@@ -62,8 +62,8 @@ struct BwdArgs {
   float* ckpt;       // [Bs][rounds][EDp][16]: state entering each round (round 0 unused)
   float* pB;         // [ngroups][Bs][L][16]: dB partial of each channel group
   float* pC;         // same for dC
-  float* pA;         // [Bs][EDp][16]: dA partial of each batch row
-  float* pD;         // [Bs][EDp]: dD partial of each batch row
+  double* pA;        // [Bs][EDp][16]: dA partial of each batch row
+  double* pD;        // [Bs][EDp]: dD partial of each batch row
   int64_t Bs, L, ED, EDp, rounds;
   int ngroups;
   int nblocks;
@@ -91,24 +91,59 @@ struct alignas(16) BwdFold {
   float4 kc[2][64];    // adjoint carry between rounds, by round parity
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kRowRor4 = 0x124;  // row_ror:4
-constexpr int kRowRor8 = 0x128;  // row_ror:8
+// The reductions below issue their DPP adds themselves: written as a DPP move
+// plus an add, the compiler keeps the move separate when the add is fused
+// with a product or sunk into a branch. A DPP read of a VGPR needs two wait
+// states after a VALU write of it; each block opens with s_nop 1 for the
+// values written before it, and its own writes are read at least two
+// instructions later.
 
-// sum over the 4 lanes of a quad (every lane gets the sum)
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<kQuadXor1>(v);
-  return v + dpp<kQuadXor2>(v);
+// v[i] <- sum of v[i] over the 4 lanes of the quad (lanes c = 0..3: the 4
+// channels of a quad that hold the same states)
+__device__ __forceinline__ void quad_sum8(float (&v)[8]) {
+  asm("s_nop 1\n\t"
+#define SSM_QA(I, P) "v_add_f32_dpp %" #I ", %" #I ", %" #I " quad_perm:" P " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      SSM_QA(0, "[1,0,3,2]") SSM_QA(1, "[1,0,3,2]") SSM_QA(2, "[1,0,3,2]") SSM_QA(3, "[1,0,3,2]")
+      SSM_QA(4, "[1,0,3,2]") SSM_QA(5, "[1,0,3,2]") SSM_QA(6, "[1,0,3,2]") SSM_QA(7, "[1,0,3,2]")
+      SSM_QA(0, "[2,3,0,1]") SSM_QA(1, "[2,3,0,1]") SSM_QA(2, "[2,3,0,1]") SSM_QA(3, "[2,3,0,1]")
+      SSM_QA(4, "[2,3,0,1]") SSM_QA(5, "[2,3,0,1]") SSM_QA(6, "[2,3,0,1]") SSM_QA(7, "[2,3,0,1]")
+#undef SSM_QA
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
 }
-// sum over the lanes 4 apart in a row (the 4 state quads of a channel)
-__device__ __forceinline__ float bank_sum(float v) {
-  v += dpp<kRowRor4>(v);
-  return v + dpp<kRowRor8>(v);
+
+// a, b <- sums over the lanes 4 apart in a row (the 4 state quads of a channel)
+__device__ __forceinline__ void bank_sum2(float& a, float& b) {
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 0\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(a), "+v"(b));
+}
+
+// g[j] <- g[j] + C_t[4 g + j] dy for j = 0..3 (C_t[q] in lane q of the row)
+__device__ __forceinline__ void add_c_dy(float (&gv)[4], float cq, float dyv) {
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %4, %5 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %1, %4, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %2, %4, %5 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %3, %4, %5 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(gv[0]), "+v"(gv[1]), "+v"(gv[2]), "+v"(gv[3])
+      : "v"(cq), "v"(dyv));
+}
+
+// sum_j B_t[4 g + j] g[j]
+__device__ __forceinline__ float dot_b(float bq, const float (&gv)[4]) {
+  float s;
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %1, %2 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %1, %3 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %1, %4 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %1, %5 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(s)
+      : "v"(bq), "v"(gv[0]), "v"(gv[1]), "v"(gv[2]), "v"(gv[3]));
+  return s;
 }
 
 // Staging: one task per thread. Threads 0 .. 4 RT - 1 own a (row, 4-channel
@@ -286,8 +321,8 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 
   // ---- sweep 2: rounds in decreasing order --------------------------------
-  float dA[4] = {0.f, 0.f, 0.f, 0.f};
-  float dDacc = 0.f;
+  double dA[4] = {0.0, 0.0, 0.0, 0.0};  // float32 within a round, float64 across rounds
+  double dDacc = 0.0;
   float kcar[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint carry out of round 0 (wave 0)
   if (wave == 0) fa.kc[R & 1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
   st.template prefetch<true>(p, R - 1);
@@ -356,13 +391,9 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
       const int row = wave * TS + i;
       const float dyv = cur.dy[row][ch];
       const float cq = cur.bc[row][q].y;
-      float gg[4];
-      gg[0] = fmac_quad<0>(kl[0], cq, dyv);
-      gg[1] = fmac_quad<1>(kl[1], cq, dyv);
-      gg[2] = fmac_quad<2>(kl[2], cq, dyv);
-      gg[3] = fmac_quad<3>(kl[3], cq, dyv);
+      add_c_dy(kl, cq, dyv);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kl[j] = av[i][j] * gg[j];
+      for (int j = 0; j < 4; ++j) kl[j] *= av[i][j];
     }
     fa.K[wave][lane] = make_float4(kl[0], kl[1], kl[2], kl[3]);
     __syncthreads();
@@ -380,54 +411,47 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 
     // adjoint replay and the gradient terms of every step
+    const int64_t tseg = r * RT + wave * TS;  // time of the segment's first step (uniform)
+    T* const dxp = p.dx + (b * L + tseg) * ED + e;
+    T* const ddp = p.ddl + (b * L + tseg) * ED + e;
+    const bool writer = g == 0 && ch_ok;      // one lane per channel stores dx, ddelta
+    float dAr[4] = {0.f, 0.f, 0.f, 0.f}, dDr = 0.f;
     float hnext[4] = {hin[0], hin[1], hin[2], hin[3]};  // h_t of the step being processed
 #pragma unroll
     for (int i = TS - 1; i >= 0; --i) {
       const int row = wave * TS + i;
-      const int64_t t = r * RT + row;
       const float dt = cur.dt[row][ch], xv = cur.xv[row][ch], dyv = cur.dy[row][ch];
       const float dxv = dt * xv;
       const float2 bcv = cur.bc[row][q];
-      const float bq = bcv.x, cq = bcv.y;
-      float gg[4];
-      gg[0] = fmac_quad<0>(kin[0], cq, dyv);
-      gg[1] = fmac_quad<1>(kin[1], cq, dyv);
-      gg[2] = fmac_quad<2>(kin[2], cq, dyv);
-      gg[3] = fmac_quad<3>(kin[3], cq, dyv);
-      // sum_n g B (this lane's 4 states)
-      float s1 = quad_bcast<0>(bq) * gg[0];
-      s1 = fmac_quad<1>(s1, bq, gg[1]);
-      s1 = fmac_quad<2>(s1, bq, gg[2]);
-      s1 = fmac_quad<3>(s1, bq, gg[3]);
-      float s2 = 0.f, pb[4], pc[4];
+      add_c_dy(kin, bcv.y, dyv);                  // kin <- g_t
+      const float s1 = dot_b(bcv.x, kin);         // sum_n g B (this lane's 4 states)
+      float s2 = 0.f, pv[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float qv = gg[j] * av[i][j] * hv[i][j];  // g a h_{t-1}
+        pv[j] = dxv * kin[j];                     // dB term
+        pv[4 + j] = dyv * hnext[j];               // dC term
+        kin[j] *= av[i][j];                       // k_t = a_t g_t
+        const float qv = kin[j] * hv[i][j];       // g a h_{t-1}
         s2 = __builtin_fmaf(Ar[j], qv, s2);
-        dA[j] = __builtin_fmaf(dt, qv, dA[j]);
-        pb[j] = dxv * gg[j];
-        pc[j] = dyv * hnext[j];
-        kin[j] = av[i][j] * gg[j];
+        dAr[j] = __builtin_fmaf(dt, qv, dAr[j]);
         hnext[j] = hv[i][j];
       }
-      dDacc = __builtin_fmaf(dyv, xv, dDacc);
-      s1 = bank_sum(s1);
-      s2 = bank_sum(s2);
-      if (g == 0 && ch_ok && t < L) {
-        const int64_t off = (b * L + t) * ED + e;
-        p.dx[off] = from_f32<T>(__builtin_fmaf(dt, s1, Dv * dyv));
-        p.ddl[off] = from_f32<T>(__builtin_fmaf(xv, s1, s2));
+      dDr = __builtin_fmaf(dyv, xv, dDr);
+      float s1r = s1;
+      bank_sum2(s1r, s2);
+      if (writer && tseg + i < L) {
+        dxp[i * ED] = from_f32<T>(__builtin_fmaf(dt, s1r, Dv * dyv));
+        ddp[i * ED] = from_f32<T>(__builtin_fmaf(xv, s1r, s2));
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pb[j] = quad_sum(pb[j]);
-        pc[j] = quad_sum(pc[j]);
-      }
+      quad_sum8(pv);
       if (c == 0) {
-        *reinterpret_cast<float4*>(&cs.v[row][lrow][0][4 * g]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
-        *reinterpret_cast<float4*>(&cs.v[row][lrow][1][4 * g]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
+        *reinterpret_cast<float4*>(&cs.v[row][lrow][0][4 * g]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        *reinterpret_cast<float4*>(&cs.v[row][lrow][1][4 * g]) = make_float4(pv[4], pv[5], pv[6], pv[7]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dA[j] += static_cast<double>(dAr[j]);
+    dDacc += static_cast<double>(dDr);
     if (wave == 0) {
       fa.kc[r & 1][lane] = make_float4(kin[0], kin[1], kin[2], kin[3]);
 #pragma unroll
@@ -442,19 +466,20 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   if (p.dh0 && wave == 0 && ch_ok)
     *reinterpret_cast<float4*>(p.dh0 + (b * ED + e) * 16 + 4 * g) = make_float4(kcar[0], kcar[1], kcar[2], kcar[3]);
   // dA and dD: sums over the waves' segments, then one partial per batch row
-  fa.A[wave][lane] = make_float4(dA[0], dA[1], dA[2], dA[3]);
-  fa.H[wave][lane] = make_float4(dDacc, 0.f, 0.f, 0.f);
+  double* red = reinterpret_cast<double*>(&fa);  // [SEG][5][64]; the fold area is free now
+  static_assert(sizeof(BwdFold<SEG>) >= sizeof(double) * SEG * 5 * 64, "reduction area");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[(wave * 5 + j) * 64 + lane] = dA[j];
+  red[(wave * 5 + 4) * 64 + lane] = dDacc;
   __syncthreads();
   if (wave == 0) {
-    float4 s = fa.A[0][lane];
-    float sdd = fa.H[0][lane].x;
-    for (int k = 1; k < SEG; ++k) {
-      const float4 v = fa.A[k][lane];
-      s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
-      sdd += fa.H[k][lane].x;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      double s = red[j * 64 + lane];
+      for (int k = 1; k < SEG; ++k) s += red[(k * 5 + j) * 64 + lane];
+      if (j < 4) p.pA[(b * p.EDp + e) * 16 + 4 * g + j] = s;
+      else if (g == 0) p.pD[b * p.EDp + e] = s;
     }
-    *reinterpret_cast<float4*>(p.pA + (b * p.EDp + e) * 16 + 4 * g) = s;
-    if (g == 0) p.pD[b * p.EDp + e] = sdd;
   }
 }
 
@@ -476,19 +501,19 @@ __global__ void bwd_reduce_bc_kernel(const float* __restrict__ pB, const float* 
 }
 
 // dA, dD: sum of the batch rows' partials, in row order.
-__global__ void bwd_reduce_ad_kernel(const float* __restrict__ pA, const float* __restrict__ pD, float* dA,
+__global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double* __restrict__ pD, float* dA,
                                      float* dD, int64_t Bs, int64_t ED, int64_t EDp) {
   const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (i < ED * 16) {
     const int64_t e = i >> 4, n = i & 15;
-    float s = 0.f;
+    double s = 0.0;
     for (int64_t b = 0; b < Bs; ++b) s += pA[(b * EDp + e) * 16 + n];
-    dA[i] = s;
+    dA[i] = static_cast<float>(s);
   } else if (dD && i < ED * 17) {
     const int64_t e = i - ED * 16;
-    float s = 0.f;
+    double s = 0.0;
     for (int64_t b = 0; b < Bs; ++b) s += pD[b * EDp + e];
-    dD[e] = s;
+    dD[e] = static_cast<float>(s);
   }
 }
 
@@ -508,7 +533,7 @@ bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo) {
   lo->EDp = lo->ngroups * 16;
   // every count below is checked against overflow of size_t arithmetic
   const double total = 4.0 * (static_cast<double>(Bs) * lo->rounds * lo->EDp * 16 +
-                              2.0 * lo->ngroups * Bs * L * 16 + Bs * lo->EDp * 17) + 5 * 256.0;
+                              2.0 * lo->ngroups * Bs * L * 16 + 2.0 * Bs * lo->EDp * 17) + 5 * 256.0;
   if (total > 9.0e18) return false;
   size_t off = 0;
   lo->ckpt_off = off;
@@ -518,9 +543,9 @@ bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo) {
   lo->pC_off = off;
   off = align256(off + static_cast<size_t>(lo->ngroups * Bs * L * 16) * 4);
   lo->pA_off = off;
-  off = align256(off + static_cast<size_t>(Bs * lo->EDp * 16) * 4);
+  off = align256(off + static_cast<size_t>(Bs * lo->EDp * 16) * 8);
   lo->pD_off = off;
-  off = align256(off + static_cast<size_t>(Bs * lo->EDp) * 4);
+  off = align256(off + static_cast<size_t>(Bs * lo->EDp) * 8);
   lo->bytes = off;
   return true;
 }
@@ -603,8 +628,8 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.ckpt = reinterpret_cast<float*>(w + lo.ckpt_off);
   a.pB = reinterpret_cast<float*>(w + lo.pB_off);
   a.pC = reinterpret_cast<float*>(w + lo.pC_off);
-  a.pA = reinterpret_cast<float*>(w + lo.pA_off);
-  a.pD = reinterpret_cast<float*>(w + lo.pD_off);
+  a.pA = reinterpret_cast<double*>(w + lo.pA_off);
+  a.pD = reinterpret_cast<double*>(w + lo.pD_off);
   a.Bs = Bs;
   a.L = L;
   a.ED = ED;

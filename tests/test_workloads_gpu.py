@@ -52,3 +52,22 @@ def test_fp32_long_sequence_131072():
 
 def test_bidirectional_8x4096x1536():
     run_workload("bidir_f32_Bs8_L4096_ED1536_N16", 256)
+
+
+def run_bwd_workload(name):
+    from parity_util import assert_grads_close, run_gpu_bwd
+    w = synth.WORKLOADS[name]
+    log("backward workload %s" % name)
+    inp = synth.workload_inputs(name, seed=0)
+    dy = synth.make_output_grad(w["Bs"], w["L"], w["ED"], w["dtype"], seed=0)
+    got = run_gpu_bwd(inp, dy, want_dh0=True)
+    ref = oracle.scan_bwd(**inp, dy=dy)
+    assert_grads_close(got, ref, w["dtype"])
+
+
+def test_backward_fp32_8x1024x1536():
+    run_bwd_workload("bwd_f32_Bs8_L1024_ED1536_N16")
+
+
+def test_backward_bf16_4x8192x5120():
+    run_bwd_workload("bwd_bf16_Bs4_L8192_ED5120_N16")
