@@ -483,21 +483,40 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
-// dB, dC: sum of the channel groups' partials, in group order.
+// dB, dC: sum of the channel groups' partials. A workgroup covers 64 float4
+// positions; its 4 waves each add up one quarter of the groups in group
+// order, and the quarters are added in order (a fixed order: deterministic).
 template <typename T>
-__global__ void bwd_reduce_bc_kernel(const float* __restrict__ pB, const float* __restrict__ pC, T* dB, T* dC,
-                                     int64_t n4, int ngroups) {
-  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;  // float4 index
-  if (i >= 2 * n4) return;
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ pB,
+                                                            const float* __restrict__ pC, T* dB, T* dC, int64_t n4,
+                                                            int ngroups) {
+  __shared__ float4 part[4][64];
+  const int lane = threadIdx.x & 63, quarter = threadIdx.x >> 6;
+  const int64_t i = blockIdx.x * static_cast<int64_t>(64) + lane;  // float4 index over dB then dC
+  const bool ok = i < 2 * n4;
   const bool isC = i >= n4;
   const int64_t k = isC ? i - n4 : i;
-  const float* src = isC ? pC : pB;
+  const float4* src = reinterpret_cast<const float4*>(isC ? pC : pB) + k;
+  const int per = (ngroups + 3) / 4;
+  const int g0 = quarter * per, g1 = min(ngroups, g0 + per);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int gi = 0; gi < ngroups; ++gi) {
-    const float4 v = reinterpret_cast<const float4*>(src)[gi * n4 + k];
-    s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+  if (ok) {
+#pragma unroll 8
+    for (int gi = g0; gi < g1; ++gi) {
+      const float4 v = src[gi * n4];
+      s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+    }
   }
-  Vec4<T>::store((isC ? dC : dB) + 4 * k, s);
+  part[quarter][lane] = s;
+  __syncthreads();
+  if (quarter == 0 && ok) {
+#pragma unroll
+    for (int h = 1; h < 4; ++h) {
+      const float4 v = part[h][lane];
+      s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+    }
+    Vec4<T>::store((isC ? dC : dB) + 4 * k, s);
+  }
 }
 
 // dA, dD: sum of the batch rows' partials, in row order.
@@ -648,7 +667,8 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
 
   const int64_t n4 = Bs * L * 4;  // float4s per dB (or dC)
-  hipLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3(static_cast<unsigned>((2 * n4 + 255) / 256)), dim3(256), 0,
+  if ((2 * n4 + 63) / 64 > INT32_MAX) return SSM_ERR_DIM;
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3(static_cast<unsigned>((2 * n4 + 63) / 64)), dim3(256), 0,
                      stream, a.pB, a.pC, static_cast<T*>(dB), static_cast<T*>(dC), n4, a.ngroups);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_reduce_ad_kernel, dim3(static_cast<unsigned>((ED * 17 + 255) / 256)), dim3(256), 0, stream,
