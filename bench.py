@@ -52,10 +52,11 @@ def alg_bytes(w):
 
 
 def kernel_source_hash():
+    """sha256[:16] over every file of the HIP sources folder (sorted by name)."""
     h = hashlib.sha256()
-    import state_space_model_selective_amd as ssm
-    for p in ssm.SOURCES:
-        with open(p, "rb") as f:
+    src = os.path.join(ROOT, "state_space_model_selective_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        with open(os.path.join(src, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
