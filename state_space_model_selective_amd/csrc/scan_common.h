@@ -62,32 +62,30 @@ struct Vec4<uint16_t> {
 // C_t[q]); quad g of the row needs B_t[4g .. 4g+3]. quad_bcast<J> makes every
 // lane of a quad read lane J of that quad. As a plain move the compiler folds
 // it into the consuming multiply as a DPP source modifier (and inserts the
-// wait states DPP needs). It does not fold it into v_fmac, so the C
-// contraction issues v_fmac_f32_dpp itself; the leading s_nop 1 provides the
-// two wait states a DPP read needs after a VALU write of its source.
+// wait states DPP needs). It does not fold it into v_fmac, so dot products
+// with the quad's values issue v_fmac_f32_dpp themselves (dot_quad).
 // ---------------------------------------------------------------------------
 template <int J>
 __device__ __forceinline__ float quad_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), J * 0x55, 0xf, 0xf, true));
 }
 
-#define SSM_FMAC_QUAD(J)                                                                              \
-  template <>                                                                                         \
-  __device__ __forceinline__ float fmac_quad<J>(float acc, float src, float other) {                  \
-    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 quad_perm:[" #J "," #J "," #J "," #J                    \
-        "] row_mask:0xf bank_mask:0xf bound_ctrl:1"                                                   \
-        : "+v"(acc)                                                                                   \
-        : "v"(src), "v"(other));                                                                      \
-    return acc;                                                                                       \
-  }
-// acc + (lane J of this lane's quad's src) * other
-template <int J>
-__device__ __forceinline__ float fmac_quad(float acc, float src, float other);
-SSM_FMAC_QUAD(0)
-SSM_FMAC_QUAD(1)
-SSM_FMAC_QUAD(2)
-SSM_FMAC_QUAD(3)
-#undef SSM_FMAC_QUAD
+// sum_j (lane j of this lane's quad's src) * h[j]: a dot product of the
+// quad's 4 values of src (B_t or C_t of the lane's 4 states) with h, as one
+// DPP multiply and three DPP fmacs behind a single s_nop 1 (a DPP read of a
+// VGPR needs two wait states after a VALU write of it; src is not written
+// inside the block, and the accumulator is not a DPP operand).
+__device__ __forceinline__ float dot_quad(float src, const float (&h)[4]) {
+  float s;
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %1, %2 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %1, %3 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %1, %4 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %1, %5 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(s)
+      : "v"(src), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]));
+  return s;
+}
 
 // ---------------------------------------------------------------------------
 // host-side helpers

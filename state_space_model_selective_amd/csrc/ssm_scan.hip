@@ -429,10 +429,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             carry[j] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * A2[j]), carry[j], dx * bb[j]);
-          float yp = quad_bcast<0>(cq) * carry[0];
-          yp = fmac_quad<1>(yp, cq, carry[1]);
-          yp = fmac_quad<2>(yp, cq, carry[2]);
-          yp = fmac_quad<3>(yp, cq, carry[3]);
+          const float yp = dot_quad(cq, carry);
           out.yq[g][i][ch] = yp;
         }
       } else {
@@ -479,10 +476,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
           const float cq = cur.cq[row][q];
 #pragma unroll
           for (int j = 0; j < 4; ++j) hin[j] = __builtin_fmaf(av[i][j], hin[j], bv[i][j]);
-          float yp = quad_bcast<0>(cq) * hin[0];
-          yp = fmac_quad<1>(yp, cq, hin[1]);
-          yp = fmac_quad<2>(yp, cq, hin[2]);
-          yp = fmac_quad<3>(yp, cq, hin[3]);
+          const float yp = dot_quad(cq, hin);
           out.yq[g][row][ch] = yp;
         }
         // the last segment's end state is the round's carry
@@ -579,10 +573,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_exp2f(A2[j] * cum) * hin[j];
         alive = alive || w[0] != 0.f || w[1] != 0.f || w[2] != 0.f || w[3] != 0.f;
         const float cq = cur.cq[row][q];
-        float yp = quad_bcast<0>(cq) * w[0];
-        yp = fmac_quad<1>(yp, cq, w[1]);
-        yp = fmac_quad<2>(yp, cq, w[2]);
-        yp = fmac_quad<3>(yp, cq, w[3]);
+        const float yp = dot_quad(cq, w);
         out.yq[g][row][ch] = yp;
       }
       float rest = 0.f;  // rows after this wave's segment

@@ -133,19 +133,6 @@ __device__ __forceinline__ void add_c_dy(float (&gv)[4], float cq, float dyv) {
       : "v"(cq), "v"(dyv));
 }
 
-// sum_j B_t[4 g + j] g[j]
-__device__ __forceinline__ float dot_b(float bq, const float (&gv)[4]) {
-  float s;
-  asm("s_nop 1\n\t"
-      "v_mul_f32_dpp %0, %1, %2 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_fmac_f32_dpp %0, %1, %3 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_fmac_f32_dpp %0, %1, %4 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_fmac_f32_dpp %0, %1, %5 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf bound_ctrl:1"
-      : "=&v"(s)
-      : "v"(bq), "v"(gv[0]), "v"(gv[1]), "v"(gv[2]), "v"(gv[3]));
-  return s;
-}
-
 // Staging: one task per thread. Threads 0 .. 4 RT - 1 own a (row, 4-channel
 // chunk) of x / delta / dy, the others a (row, 4-state chunk) of B / C.
 template <typename T, int RT, bool VEC>
@@ -424,7 +411,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
       const float dxv = dt * xv;
       const float2 bcv = cur.bc[row][q];
       add_c_dy(kin, bcv.y, dyv);                  // kin <- g_t
-      const float s1 = dot_b(bcv.x, kin);         // sum_n g B (this lane's 4 states)
+      const float s1 = dot_quad(bcv.x, kin);         // sum_n g B (this lane's 4 states)
       float s2 = 0.f, pv[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
