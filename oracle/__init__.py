@@ -8,7 +8,9 @@ this package. The product path (the HIP library and its binding) never does.
   y_t = sum_n C_t[n] h_t[n] + D[e] x_t
 (plus the reverse-time scan for the bidirectional variant), in fp64.
 ``scan_bwd`` is the adjoint of that recurrence: the gradients of sum(dy * y)
-with respect to x, delta, A, B, C, D and h0.
+with respect to x, delta, A, B, C, D and h0. ``ssd`` is the multi-head
+(Mamba-2 / SSD) form: one scalar decay per head, B and C shared by a group of
+heads, a (headdim x state) matrix state per head.
 """
 import ctypes
 import os
@@ -46,6 +48,8 @@ def lib():
         L.oracle_scan.restype = ctypes.c_int
         L.oracle_scan_bwd.argtypes = [ctypes.c_int] + [vp] * 8 + [i64] * 4 + [vp] * 7 + [ctypes.c_int]
         L.oracle_scan_bwd.restype = ctypes.c_int
+        L.oracle_ssd.argtypes = [ctypes.c_int, ctypes.c_int] + [vp] * 7 + [i64] * 6 + [vp] * 3 + [ctypes.c_int]
+        L.oracle_ssd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -158,3 +162,35 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, nthreads=None):
     if rc != 0:
         raise RuntimeError("oracle_scan_bwd failed with code %d" % rc)
     return out
+
+
+def ssd(x, dt, A, B, C, D=None, *, h0=None, bidir=False, want_h_last=False, want_g_first=False, nthreads=None):
+    """Multi-head selective scan in fp64.
+
+    x (Bs, L, H, P), dt (Bs, L, H), A (H,), B and C (Bs, L, G, N), D (H,) or
+    None, h0 (Bs, H, P, N) or None; float32 arrays, or uint16 bfloat16 bit
+    patterns for x, dt, B, C. Returns (y (Bs, L, H, P), h_last, g_first) with
+    the states (Bs, H, P, N) when requested, else None.
+    """
+    x = np.ascontiguousarray(x)
+    dt = np.ascontiguousarray(dt)
+    B = np.ascontiguousarray(B)
+    C = np.ascontiguousarray(C)
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    dtype = BF16 if x.dtype == np.uint16 else F32
+    for t in (dt, B, C):
+        if t.dtype != x.dtype:
+            raise TypeError("x, dt, B, C must share a dtype")
+    Bs, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (Bs, L, H) and B.shape == C.shape == (Bs, L, G, N) and A.shape == (H,)
+    y = np.empty((Bs, L, H, P))
+    hl = np.empty((Bs, H, P, N)) if want_h_last else None
+    gf = np.empty((Bs, H, P, N)) if (want_g_first and bidir) else None
+    rc = lib().oracle_ssd(dtype, int(bool(bidir)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                          Bs, L, H, P, G, N, _ptr(y), _ptr(hl), _ptr(gf), _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_ssd failed with code %d" % rc)
+    return y, hl, gf

@@ -372,3 +372,107 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
   free(th);
   return rc;
 }
+
+/*
+ * Multi-head (Mamba-2 / SSD) selective scan, the layout of the chunked scan
+ * the Bi-Mamba2 page calls ("Some questions of Bi-Mamba2 and Hydra", the
+ * MambaChunkScanCombinedFn listings): x (Bs, L, H, P), dt (Bs, L, H), a scalar
+ * A per head, B and C (Bs, L, G, N) shared by the H / G heads of a group,
+ * D (H). For batch row b, head h (group g = h / (H / G)), head channel p and
+ * state n the recurrence is the one above with one decay per head:
+ *   a_t = exp(dt[b,t,h] A[h])
+ *   S_t[p][n] = a_t S_{t-1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],  S_{-1} = h0 (or 0)
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p][n] + D[h] x[b,t,h,p]
+ * bidir adds the reverse-time scan with the same a_t (no shift, D x once):
+ *   R_t = a_t R_{t+1} + (dt x)_t B_t,  R_L = 0,   y += sum_n C_t R_t.
+ * The chunk length of the pages' kernels does not change the result; this
+ * definition has none. Outputs fp64: y (Bs, L, H, P); h_last and g_first
+ * (Bs, H, P, N) or NULL. Threads split the independent (b, h) pairs.
+ */
+typedef struct {
+  int dtype, bidir;
+  const void *x, *dt, *B, *C;
+  const float *A, *D, *h0;
+  int64_t Bs, L, H, P, G, N;
+  double *y, *h_last, *g_first;
+  int64_t k0, k1; /* (b, h) pairs [k0, k1) */
+  int fail;
+} ssd_t;
+
+static void* ssd_worker(void* arg) {
+  ssd_t* w = (ssd_t*)arg;
+  const int64_t L = w->L, H = w->H, P = w->P, G = w->G, N = w->N;
+  double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));
+  if (!S) {
+    w->fail = 1;
+    return NULL;
+  }
+  for (int64_t k = w->k0; k < w->k1; ++k) {
+    const int64_t b = k / H, h = k % H, g = h / (H / G);
+    const double Ah = (double)w->A[h];
+    const double Dh = w->D ? (double)w->D[h] : 0.0;
+    for (int dir = 0; dir < (w->bidir ? 2 : 1); ++dir) {
+      for (int64_t i = 0; i < P * N; ++i)
+        S[i] = (dir == 0 && w->h0) ? (double)w->h0[(b * H + h) * P * N + i] : 0.0;
+      for (int64_t s = 0; s < L; ++s) {
+        const int64_t t = dir == 0 ? s : L - 1 - s;
+        const double dtv = load(w->dt, (b * L + t) * H + h, w->dtype);
+        const double a = exp(dtv * Ah);
+        const int64_t ib = ((b * L + t) * G + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+          const int64_t ix = ((b * L + t) * H + h) * P + p;
+          const double xv = load(w->x, ix, w->dtype);
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            S[p * N + n] = a * S[p * N + n] + (dtv * xv) * load(w->B, ib + n, w->dtype);
+            acc += load(w->C, ib + n, w->dtype) * S[p * N + n];
+          }
+          if (dir == 0)
+            w->y[ix] = acc + Dh * xv;
+          else
+            w->y[ix] += acc;
+        }
+      }
+      double* out = dir == 0 ? w->h_last : w->g_first;
+      if (out)
+        for (int64_t i = 0; i < P * N; ++i) out[(b * H + h) * P * N + i] = S[i];
+    }
+  }
+  free(S);
+  return NULL;
+}
+
+int oracle_ssd(int dtype, int bidir, const void* x, const void* dt, const float* A, const void* B, const void* C,
+               const float* D, const float* h0, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+               double* y, double* h_last, double* g_first, int nthreads) {
+  if (!x || !dt || !A || !B || !C || !y) return -1;
+  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  const int64_t K = Bs * H;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > K) nthreads = (int)K;
+  if (nthreads > 256) nthreads = 256;
+  ssd_t* ws = (ssd_t*)malloc(sizeof(ssd_t) * (size_t)nthreads);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!ws || !th) {
+    free(ws);
+    free(th);
+    return -2;
+  }
+  const int64_t per = (K + nthreads - 1) / nthreads;
+  for (int i = 0; i < nthreads; ++i) {
+    ws[i] = (ssd_t){dtype, bidir, x, dt, B, C, A, D, h0, Bs, L, H, P, G, N, y, h_last, bidir ? g_first : NULL,
+                    0, 0, 0};
+    ws[i].k0 = per * i < K ? per * i : K;
+    ws[i].k1 = per * (i + 1) < K ? per * (i + 1) : K;
+  }
+  for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, ssd_worker, &ws[i]);
+  ssd_worker(&ws[0]);
+  for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
+  int rc = 0;
+  for (int i = 0; i < nthreads; ++i)
+    if (ws[i].fail) rc = -2;
+  free(ws);
+  free(th);
+  return rc;
+}

@@ -16,6 +16,11 @@ normal; step size Delta log-uniform on [1e-3, 1e-1]; A[e, n] = -(n + 1)):
   A     (ED, N)      -(n + 1), exact
   dy    (Bs, L, ED)  N(0, 1)                   stream 6 (output gradient, backward pass)
 
+Multi-head (SSD) inputs, ``make_ssd_inputs``: x (Bs, L, H, P) N(0, 1) stream 11;
+dt (Bs, L, H) log-uniform on [1e-3, 1e-1] stream 12; A (H) = -U(1, 16)
+stream 13 (one decay rate per head); B, C (Bs, L, G, N) N(0, 1) streams 14,
+15; D (H) N(0, 1) stream 16.
+
 For bf16 workloads x, delta, B and C are rounded to bfloat16 (round to nearest
 even) and handed over as uint16 bit patterns; A and D stay float32.
 """
@@ -146,3 +151,21 @@ def make_output_grad(Bs, L, ED, dtype="f32", seed=0, nthreads=None):
     """Gradient dL/dy for the backward pass, N(0, 1), of the workload's dtype."""
     dy = normal(seed, STREAM_DY, (Bs, L, ED), nthreads)
     return to_bf16(dy) if dtype == "bf16" else dy
+
+
+STREAM_SSD_X, STREAM_SSD_DT, STREAM_SSD_A, STREAM_SSD_B, STREAM_SSD_C, STREAM_SSD_D = 11, 12, 13, 14, 15, 16
+
+
+def make_ssd_inputs(Bs, L, H, P, G, N, dtype="f32", seed=0, nthreads=None):
+    """Multi-head scan inputs as numpy arrays (bf16 tensors as uint16 bit patterns)."""
+    x = normal(seed, STREAM_SSD_X, (Bs, L, H, P), nthreads)
+    dt = loguniform(seed, STREAM_SSD_DT, (Bs, L, H), DELTA_LO, DELTA_HI, nthreads)
+    A = -uniform(seed, STREAM_SSD_A, (H,), 1.0, 16.0, nthreads)
+    B = normal(seed, STREAM_SSD_B, (Bs, L, G, N), nthreads)
+    C = normal(seed, STREAM_SSD_C, (Bs, L, G, N), nthreads)
+    D = normal(seed, STREAM_SSD_D, (H,), nthreads)
+    if dtype == "bf16":
+        x, dt, B, C = to_bf16(x), to_bf16(dt), to_bf16(B), to_bf16(C)
+    elif dtype != "f32":
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D)
