@@ -170,6 +170,33 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * Multi-head (Mamba-2 / SSD) selective scan, in the layout of the chunked
+ * scan of "Some questions of Bi-Mamba2 and Hydra" (the
+ * MambaChunkScanCombinedFn listings: x (batch, seqlen, nheads, headdim), dt
+ * (batch, seqlen, nheads), one A per head, B and C per group of heads). For
+ * batch row b, head h (group g = h / (H / G)), head channel p and state n:
+ *
+ *   a_t       = exp(dt[b,t,h] A[h])
+ *   S_t[p][n] = a_t S_{t-1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],   S_{-1} = h0 (or 0)
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p][n] + D[h] x[b,t,h,p]
+ *
+ * (the recurrence of ssm_scan_fwd with one decay per head and a shared B, C
+ * per group). dt is used as given.
+ *   x      : (Bs, L, H, P) of dtype      dt : (Bs, L, H) of dtype
+ *   A      : (H) float32                 B, C : (Bs, L, G, N) of dtype
+ *   D      : (H) float32, or NULL        h0 : (Bs, H, P, N) float32, or NULL
+ *   y      : (Bs, L, H, P) of dtype, written in full
+ *   h_last : (Bs, H, P, N) float32, or NULL -- S after the last step
+ * Supported: P = 64, N = 64 or 128, H a multiple of G. Arithmetic is
+ * float32 throughout (bfloat16 inputs are widened; y is rounded to nearest
+ * even). No workspace. Conventions, alignment and error codes as
+ * ssm_scan_fwd (SSM_ERR_DIM also when H is not a multiple of G).
+ */
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G,
+                int64_t N, int dtype, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

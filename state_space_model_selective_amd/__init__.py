@@ -1,8 +1,9 @@
 """Python binding of the MI355X selective-scan library (libssm_scan.so).
 
 Argument marshalling only: every step of the scan runs in the HIP kernels of
-``csrc/ssm_scan.hip`` (forward) and ``csrc/ssm_scan_bwd.hip`` (backward)
-behind the C ABI declared in ``include/ssm_scan.h``.
+``csrc/ssm_scan.hip`` (forward), ``csrc/ssm_scan_bwd.hip`` (backward) and
+``csrc/ssm_ssd.hip`` (multi-head scan) behind the C ABI declared in
+``include/ssm_scan.h``.
 PyTorch supplies device memory and the stream. There is no fallback: if the
 library is not built, or the tensors are not on a GPU, the calls raise.
 """
@@ -13,7 +14,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libssm_scan.so")
-SOURCES = [os.path.join(_HERE, "csrc", "ssm_scan.hip"), os.path.join(_HERE, "csrc", "ssm_scan_bwd.hip")]
+SOURCES = [os.path.join(_HERE, "csrc", n) for n in ("ssm_scan.hip", "ssm_scan_bwd.hip", "ssm_ssd.hip")]
 INCLUDE = os.path.join(_ROOT, "include")
 
 SSM_F32, SSM_BF16 = 0, 1
@@ -75,6 +76,8 @@ def lib():
         L.ssm_scan_bwd_workspace_bytes.restype = sz
         L.ssm_scan_bwd.argtypes = [vp] * 15 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bwd.restype = ci
+        L.ssm_ssd_fwd.argtypes = [vp] * 9 + [i64] * 6 + [ci, vp]
+        L.ssm_ssd_fwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -206,3 +209,22 @@ def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_bwd")
     return o
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=None):
+    """Multi-head selective scan: x (Bs, L, H, P), dt (Bs, L, H), A (H,),
+    B and C (Bs, L, G, N), D (H,) or None, h0 (Bs, H, P, N) or None.
+    Returns y (Bs, L, H, P); the final state goes to h_last if given."""
+    import torch
+    if not x.is_cuda:
+        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
+    dtc = _dtype_code(x)
+    Bs, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_last),
+                           Bs, L, H, P, G, N, dtc, _stream(x, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_ssd_fwd")
+    return y

@@ -1,0 +1,329 @@
+// Multi-head (Mamba-2 / SSD) selective scan for MI355X (gfx950).
+//
+// For batch row b, head h (group g = h / (H / G)), head channel p and state n:
+//   a_t = exp(dt[b,t,h] A[h])
+//   S_t[p][n] = a_t S_{t-1}[p][n] + dt[b,t,h] x[b,t,h,p] B[b,t,g,n],   S_{-1} = h0 (or 0)
+//   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p][n] + D[h] x[b,t,h,p]
+// the layout of the chunked scan in "Some questions of Bi-Mamba2 and Hydra"
+// (the MambaChunkScanCombinedFn listings: x (batch, seqlen, nheads, headdim),
+// dt (batch, seqlen, nheads), one A per head, B and C per group).
+//
+// With one decay per head the scan over a chunk of Q steps is a few dense
+// products (the chunked form of the scan): with cs_t = A sum_{r<=t} dt_r
+// inside the chunk and S_in the state entering it,
+//   Y   = M X + diag(e^{cs}) C S_in^T,     M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s  (s <= t)
+//   S_out = e^{cs_end} S_in + sum_s X_s^T (e^{cs_end - cs_s} dt_s) B_s
+// which the matrix cores compute (v_mfma_f32_16x16x4f32: float32 operands and
+// accumulation, so bf16 inputs are widened and nothing is rounded below
+// float32). One workgroup of 4 waves owns one (batch row, head), keeps the
+// head's 64 x N state on chip for the whole sequence (registers for the
+// update, an LDS copy for the output product) and walks the chunks in order;
+// the next chunk's inputs are loaded into registers while the current one is
+// computed (double-buffered LDS tiles).
+//
+// Matrix-core operand layout (16 x 16 x 4, one wave): lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; result register r of lane l is
+// D[4 (l / 16) + r][l % 16].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "scan_common.h"
+#include "ssm_scan.h"
+
+namespace {
+
+constexpr int kQ = 32;       // chunk length
+constexpr int kP = 64;       // head channels (headdim)
+constexpr int kWaves = 4;
+
+template <typename T>
+struct SsdArgs {
+  const T* x;
+  const T* dt;
+  const float* A;
+  const T* B;
+  const T* C;
+  const float* D;
+  const float* h0;
+  T* y;
+  float* h_last;
+  int64_t L, H, G;
+};
+
+template <int N>
+struct alignas(16) SsdSmem {
+  float X[2][kQ][kP + 16];   // x chunk, row padded so that 4 consecutive rows hit different banks
+  float Bm[2][kQ][N + 4];    // B chunk
+  float Cm[2][kQ][N + 4];    // C chunk
+  float S[kP][N + 4];        // state entering the chunk (operand of C S^T)
+  float M[kQ][kQ + 4];       // masked, decayed C B^T
+  float dt[2][kQ];
+  float cs[kQ];              // A * inclusive cumulative dt within the chunk
+  float ecs[kQ];             // e^{cs_t}
+  float w[kQ];               // e^{cs_end - cs_s} dt_s
+  float cs_end;
+};
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Loads of one chunk into registers (4 elements per task) and their commit to
+// LDS. Rows at or past L are zero (dt = 0: a = 1 and no input).
+template <typename T, int N>
+struct SsdStager {
+  static constexpr int kXT = kQ * kP / 4 / (64 * kWaves);  // x tasks per thread
+  static constexpr int kBT = kQ * N / 4 / (64 * kWaves);   // B (and C) tasks per thread
+  float4 rx[kXT], rb[kBT], rc[kBT];
+  float rdt;
+
+  __device__ __forceinline__ void load(const SsdArgs<T>& p, int tid, int64_t b, int64_t h, int64_t g, int64_t t0) {
+#pragma unroll
+    for (int k = 0; k < kXT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
+      const int64_t t = t0 + row;
+      rx[k] = t < p.L ? Vec4<T>::load(p.x + ((b * p.L + t) * p.H + h) * kP + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kBT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
+      const int64_t t = t0 + row;
+      const int64_t off = ((b * p.L + t) * p.G + g) * N + c4;
+      rb[k] = t < p.L ? Vec4<T>::load(p.B + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      rc[k] = t < p.L ? Vec4<T>::load(p.C + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    rdt = 0.f;
+    if (tid < kQ && t0 + tid < p.L) rdt = to_f32(p.dt[(b * p.L + t0 + tid) * p.H + h]);
+  }
+
+  __device__ __forceinline__ void commit(SsdSmem<N>& sm, int buf, int tid) const {
+#pragma unroll
+    for (int k = 0; k < kXT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
+      *reinterpret_cast<float4*>(&sm.X[buf][row][c4]) = rx[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kBT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
+      *reinterpret_cast<float4*>(&sm.Bm[buf][row][c4]) = rb[k];
+      *reinterpret_cast<float4*>(&sm.Cm[buf][row][c4]) = rc[k];
+    }
+    if (tid < kQ) sm.dt[buf][tid] = rdt;
+  }
+};
+
+template <typename T, int N>
+__global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p) {
+  static_assert(kQ == 32 && kP == 64 && kWaves == 4, "work split below assumes these sizes");
+  static_assert(N % 32 == 0, "each wave owns N / 32 ... state column blocks");
+  constexpr int NB = N / 16 / kWaves;  // state column blocks per wave (2 for N = 128)
+
+  __shared__ SsdSmem<N> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lk = lane >> 4;  // operand row / column and k index
+  const int64_t b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int64_t g = h / (p.H / p.G);
+  const float Ah = p.A[h];
+  const float Dh = p.D ? p.D[h] : 0.f;
+  const int64_t nchunks = (p.L + kQ - 1) / kQ;
+
+  // the wave's share of the state: all 4 row blocks (p) x NB column blocks (n)
+  f4 st[4][NB];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int nb = wave * NB + j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * pb + 4 * lk + r, nn = 16 * nb + li;
+        st[pb][j][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
+        sm.S[pp][nn] = st[pb][j][r];
+      }
+    }
+
+  SsdStager<T, N> stg;
+  stg.load(p, tid, b, h, g, 0);
+  stg.commit(sm, 0, tid);
+  __syncthreads();
+
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int cur = c & 1;
+    const int64_t t0 = c * kQ;
+    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ);
+
+    // decay of the chunk: cs_t, e^{cs_t}, the state-update weights
+    if (wave == 0 && lane < kQ) {
+      float s = 0.f, tot = 0.f;
+      for (int r = 0; r < kQ; ++r) {
+        const float v = sm.dt[cur][r];
+        tot += v;
+        if (r <= lane) s += v;
+      }
+      const float cst = Ah * s, cse = Ah * tot;
+      sm.cs[lane] = cst;
+      sm.ecs[lane] = __expf(cst);
+      sm.w[lane] = __expf(cse - cst) * sm.dt[cur][lane];
+      if (lane == 0) sm.cs_end = cse;
+    }
+    __syncthreads();
+
+    // C B^T on the causal blocks (t-block, s-block) = (0,0), (1,0), (1,1),
+    // masked and decayed into M
+    if (wave < 3) {
+      const int tb = wave == 0 ? 0 : 1, sb = wave == 2 ? 1 : 0;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int n0 = 0; n0 < N; n0 += 4)
+        acc = mfma4(sm.Cm[cur][16 * tb + li][n0 + lk], sm.Bm[cur][16 * sb + li][n0 + lk], acc);
+      const int s = 16 * sb + li;
+      const float css = sm.cs[s], dts = sm.dt[cur][s];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * lk + r;
+        sm.M[t][s] = s <= t ? acc[r] * __expf(sm.cs[t] - css) * dts : 0.f;
+      }
+    }
+
+    // inter-chunk output diag(e^{cs}) C S_in^T for head-channel block `wave`
+    f4 y[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int n0 = 0; n0 < N; n0 += 4)
+        acc = mfma4(sm.Cm[cur][16 * tb + li][n0 + lk], sm.S[16 * wave + li][n0 + lk], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= sm.ecs[16 * tb + 4 * lk + r];
+      y[tb] = acc;
+    }
+    __syncthreads();  // M complete
+
+    // intra-chunk output M X (causal: s-blocks up to the t-block)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+      for (int s0 = 0; s0 < 16 * (tb + 1); s0 += 4)
+        y[tb] = mfma4(sm.M[16 * tb + li][s0 + lk], sm.X[cur][s0 + lk][16 * wave + li], y[tb]);
+    }
+    // y + D x -> global
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * lk + r, pp = 16 * wave + li;
+        if (t0 + t < p.L)
+          p.y[((b * p.L + t0 + t) * p.H + h) * kP + pp] = from_f32<T>(y[tb][r] + Dh * sm.X[cur][t][pp]);
+      }
+
+    // state update S = e^{cs_end} S + (X w)^T B for the wave's blocks
+    const float dec = __expf(sm.cs_end);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        f4 acc = st[pb][j] * dec;
+#pragma unroll
+        for (int s0 = 0; s0 < kQ; s0 += 4)
+          acc = mfma4(sm.X[cur][s0 + lk][16 * pb + li] * sm.w[s0 + lk], sm.Bm[cur][s0 + lk][16 * (wave * NB + j) + li],
+                      acc);
+        st[pb][j] = acc;
+      }
+    __syncthreads();  // every read of S_in and of this chunk's tiles is done
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.S[16 * pb + 4 * lk + r][16 * (wave * NB + j) + li] = st[pb][j][r];
+    if (c + 1 < nchunks) stg.commit(sm, cur ^ 1, tid);
+    __syncthreads();
+  }
+
+  if (p.h_last) {
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pp = 16 * pb + 4 * lk + r, nn = 16 * (wave * NB + j) + li;
+          p.h_last[((b * p.H + h) * kP + pp) * N + nn] = st[pb][j][r];
+        }
+  }
+}
+
+int ssd_validate(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                 const float* h0, const void* y, const float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t P,
+                 int64_t G, int64_t N, int dtype) {
+  if (!x || !dt || !A || !B || !C || !y) return SSM_ERR_NULL;
+  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0) return SSM_ERR_DIM;
+  int64_t t, rows, seq, bc, state, hd;
+  if (!mul_ok(Bs, L, &rows) || !mul_ok(rows, H, &hd) || !mul_ok(hd, P, &seq) || !mul_ok(rows, G, &t) ||
+      !mul_ok(t, N, &bc) || !mul_ok(Bs, H, &t) || !mul_ok(t, P, &t) || !mul_ok(t, N, &state))
+    return SSM_ERR_DIM;
+  if (seq > INT64_MAX / 8 || bc > INT64_MAX / 8 || state > INT64_MAX / 8) return SSM_ERR_DIM;
+  if (H % G != 0) return SSM_ERR_DIM;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (P != kP || (N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
+  if (Bs * H > INT32_MAX) return SSM_ERR_DIM;
+  const void* ptrs[] = {x, dt, A, B, C, D, h0, y, h_last};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = dtype == SSM_F32 ? 4 : 2;
+  const Range in[] = {rng(x, seq * es), rng(dt, hd * es), rng(A, H * 4), rng(B, bc * es), rng(C, bc * es),
+                      rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0)};
+  const Range out[] = {rng(y, seq * es), rng(h_last, h_last ? state * 4 : 0)};
+  for (int i = 0; i < 2; ++i) {
+    if (out[i].hi == out[i].lo) continue;
+    for (const Range& r : in)
+      if (r.hi > r.lo && overlap(out[i], r)) return SSM_ERR_ALIAS;
+  }
+  if (out[1].hi > out[1].lo && overlap(out[0], out[1])) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+template <typename T>
+int launch_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+               const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t G, int64_t N,
+               hipStream_t stream) {
+  SsdArgs<T> a;
+  a.x = static_cast<const T*>(x);
+  a.dt = static_cast<const T*>(dt);
+  a.A = A;
+  a.B = static_cast<const T*>(B);
+  a.C = static_cast<const T*>(C);
+  a.D = D;
+  a.h0 = h0;
+  a.y = static_cast<T*>(y);
+  a.h_last = h_last;
+  a.L = L;
+  a.H = H;
+  a.G = G;
+  const dim3 grid(static_cast<unsigned>(Bs * H)), block(64 * kWaves);
+  if (N == 128)
+    hipLaunchKernelGGL((ssd_fwd_kernel<T, 128>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((ssd_fwd_kernel<T, 64>), grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                           const float* D, const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H,
+                           int64_t P, int64_t G, int64_t N, int dtype, void* stream) {
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, y, h_last, Bs, L, H, P, G, N, dtype);
+  if (rc != SSM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == SSM_F32) return launch_ssd<float>(x, dt, A, B, C, D, h0, y, h_last, Bs, L, H, G, N, st);
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, y, h_last, Bs, L, H, G, N, st);
+}

@@ -52,6 +52,15 @@ WORKLOADS = {
                                           bwd=True),
 }
 
+# Multi-head (SSD) workloads: batch 32, seqlen 400, 8 heads is the shape the
+# Bi-Mamba2 page prints for its chunked scan; headdim 64, state 128 and one
+# group are the usual Mamba-2 layer settings. The second is a longer,
+# wider layer.
+SSD_WORKLOADS = {
+    "ssd_f32_Bs32_L400_H8_P64_N128": dict(Bs=32, L=400, H=8, P=64, G=1, N=128, dtype="f32"),
+    "ssd_bf16_Bs8_L4096_H32_P64_N128": dict(Bs=8, L=4096, H=32, P=64, G=1, N=128, dtype="bf16"),
+}
+
 
 def build():
     """Compile the generator library (gcc, no GPU needed)."""

@@ -127,3 +127,20 @@ def assert_grads_close(got, ref, dtype):
     for k, v in got.items():
         tol = TOL[dtype] if k in ("dx", "ddelta", "dB", "dC") else TOL["f32"]
         assert_close(k, v, ref[k], tol)
+
+
+def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None):
+    """ssm_ssd_fwd on the GPU: (y, h_last) as float64 numpy arrays."""
+    import torch
+    import state_space_model_selective_amd as ssm
+    dev = torch.device("cuda:0")
+    t = to_device(inp, dev)
+    Bs, L, H, P = inp["x"].shape
+    N = inp["B"].shape[3]
+    h = torch.full((Bs, H, P, N), float("nan"), dtype=torch.float32, device=dev) if want_h else None
+    h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, dtype=np.float32)).to(dev)
+    y = torch.full_like(t["x"], float("nan"))
+    ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], None if D_none else t["D"], y=y, h_last=h, h0=h0t,
+                    stream=stream)
+    torch.cuda.synchronize()
+    return y_to_numpy(y), (None if h is None else h.double().cpu().numpy())

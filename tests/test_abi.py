@@ -177,3 +177,31 @@ def test_bwd_validation():
     assert bwd(ddelta=P[8] + 256) == ssm.SSM_ERR_ALIAS    # ddelta inside dx
     assert bwd(dh0=P[6]) == ssm.SSM_ERR_ALIAS             # dh0 on top of h0
     assert bwd(ws=P[7]) == ssm.SSM_ERR_ALIAS              # workspace on top of dy
+
+
+SSD_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "y", "h"]
+
+
+def ssd(**kw):
+    args = {n: P[i] for i, n in enumerate(SSD_PTRS)}
+    args.update(Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_F32)
+    args.update(kw)
+    return ssm.lib().ssm_ssd_fwd(*[args[n] for n in SSD_PTRS], args["Bs"], args["L"], args["H"], args["P"],
+                                 args["G"], args["N"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
+def test_ssd_null_pointer(name):
+    assert ssd(**{name: None}) == ssm.SSM_ERR_NULL
+
+
+def test_ssd_validation():
+    assert ssd(L=0) == ssm.SSM_ERR_DIM
+    assert ssd(H=3, G=2) == ssm.SSM_ERR_DIM          # heads not a multiple of groups
+    assert ssd(P=32) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(N=16) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(dtype=5) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(dt=P[1] + 8) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(y=P[0] + 64) == ssm.SSM_ERR_ALIAS     # y inside x
+    assert ssd(h=P[7]) == ssm.SSM_ERR_ALIAS          # h_last on top of y
+    assert ssd(h=P[6]) == ssm.SSM_ERR_ALIAS          # h_last on top of h0

@@ -1,0 +1,68 @@
+"""GPU parity of the multi-head (SSD) scan (ssm_ssd_fwd) against the oracle
+(oracle.ssd) on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity_util import TOL, assert_close, log, run_gpu_ssd
+
+pytestmark = pytest.mark.gpu
+
+
+def check(Bs, L, H, G, N, dtype="f32", seed=0, h0=False, D_none=False):
+    log("ssd case Bs=%d L=%d H=%d G=%d N=%d dtype=%s seed=%d h0=%s D_none=%s" % (Bs, L, H, G, N, dtype, seed, h0,
+                                                                               D_none))
+    inp = synth.make_ssd_inputs(Bs, L, H, 64, G, N, dtype, seed=seed)
+    h = synth.normal(seed, 93, (Bs, H, 64, N)) if h0 else None
+    y, hl = run_gpu_ssd(inp, h0=h, want_h=True, D_none=D_none)
+    y_ref, h_ref, _ = oracle.ssd(**(dict(inp, D=None) if D_none else inp), h0=h, want_h_last=True)
+    assert_close("y", y, y_ref, TOL[dtype])
+    assert_close("h_last", hl, h_ref, TOL["f32"])
+
+
+def test_small():
+    check(2, 64, 4, 1, 64)
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 100, 400])
+def test_sequence_lengths(L):
+    check(2, L, 2, 1, 128, seed=L)
+
+
+def test_state_128_and_groups():
+    check(2, 150, 8, 2, 128, seed=3)
+
+
+def test_groups_64():
+    check(3, 70, 6, 3, 64, seed=4)
+
+
+def test_bf16():
+    check(2, 200, 4, 1, 128, dtype="bf16", seed=5)
+
+
+def test_initial_state():
+    check(2, 90, 4, 2, 128, seed=6, h0=True)
+
+
+def test_no_D():
+    check(1, 50, 2, 1, 64, seed=7, D_none=True)
+
+
+def test_repeatable_bits():
+    inp = synth.make_ssd_inputs(2, 77, 4, 64, 1, 128, seed=8)
+    a, ha = run_gpu_ssd(inp, want_h=True)
+    b, hb = run_gpu_ssd(inp, want_h=True)
+    assert np.array_equal(a, b) and np.array_equal(ha, hb)
+
+
+@pytest.mark.parametrize("name", ["ssd_f32_Bs32_L400_H8_P64_N128", "ssd_bf16_Bs8_L4096_H32_P64_N128"])
+def test_workloads(name):
+    w = synth.SSD_WORKLOADS[name]
+    log("ssd workload %s" % name)
+    inp = synth.make_ssd_inputs(w["Bs"], w["L"], w["H"], w["P"], w["G"], w["N"], w["dtype"], seed=0)
+    y, hl = run_gpu_ssd(inp, want_h=True)
+    y_ref, h_ref, _ = oracle.ssd(**inp, want_h_last=True)
+    assert_close("y", y, y_ref, TOL[w["dtype"]])
+    assert_close("h_last", hl, h_ref, TOL["f32"])
