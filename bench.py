@@ -129,6 +129,132 @@ def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
                 sample=sample + " (fp64 forward states + adjoint, %.2f s)" % dt), ref, k
 
 
+# dense fp32 matrix-core peak of the MI355X (the multi-head scan's products run there)
+MFMA_F32_PEAK_TFLOPS = 157.3
+SSD_CHUNK = 32  # chunk length of the multi-head kernel
+
+
+def ssd_flops(w):
+    """Products of the chunked multi-head scan per launch: per (batch row,
+    head) and chunk of Q steps, the causal C B^T (Q (Q+1)/2 N multiply-adds),
+    its product with x (Q (Q+1)/2 P), C S^T (Q N P) and the state update
+    (Q N P); 2 flops per multiply-add."""
+    Q, P, N = SSD_CHUNK, w["P"], w["N"]
+    chunks = (w["L"] + Q - 1) // Q
+    per_chunk = 2 * (Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P)
+    return w["Bs"] * w["H"] * chunks * per_chunk
+
+
+def bench_ssd(args, name):
+    import numpy as np
+    import torch
+    import state_space_model_selective_amd as ssm
+    import synth
+    w = dict(synth.SSD_WORKLOADS[name])
+    Bs, L, H, P, G, N = w["Bs"], w["L"], w["H"], w["P"], w["G"], w["N"]
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    nsets = 3
+    sets, host0 = [], None
+    for i in range(nsets):
+        inp = synth.make_ssd_inputs(Bs, L, H, P, G, N, w["dtype"], seed=i)
+        if i == 0:
+            host0 = inp
+        t = {k: to_dev(v) for k, v in inp.items()}
+        t["y"] = torch.empty_like(t["x"])
+        sets.append(t)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], stream=stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % nsets])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    E = Bs * L * H * P * N
+    flops = ssd_flops(w)
+    s = 4 if w["dtype"] == "f32" else 2
+    alg_bytes = 2 * Bs * L * H * P * s + Bs * L * H * s + 2 * Bs * L * G * N * s + 8 * H
+
+    cpu = parity = None
+    if not args.no_cpu:
+        import oracle
+        threads = min(16, os.cpu_count() or 1)
+
+        def rows(k):
+            return {n: (v[:k] if v.ndim >= 3 else v) for n, v in host0.items()}
+        t1 = time.perf_counter()
+        oracle.ssd(**rows(1), nthreads=threads)
+        dt1 = max(time.perf_counter() - t1, 1e-6)
+        k = int(min(Bs, max(1, 20.0 / dt1)))
+        t1 = time.perf_counter()
+        y_ref, _, _ = oracle.ssd(**rows(k), nthreads=threads)
+        dtk = time.perf_counter() - t1
+        cpu = dict(value=k * L * H * P * N / dtk, unit="scan elements/s", cores=threads, kind="oracle",
+                   sample=(("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))) +
+                   " (fp64 sequential recurrence, %.2f s)" % dtk)
+        step(sets[0])
+        torch.cuda.synchronize()
+        got = sets[0]["y"][:k].float().cpu().numpy().astype(np.float64)
+        tol = 1e-4 if w["dtype"] == "f32" else 2e-2
+        rel = float(np.max(np.abs(got - y_ref) / (1 + np.abs(y_ref))))
+        parity = dict(max_rel_err=rel, tol=tol, passed=bool(rel <= tol))
+
+    out = {
+        "metric": "multi-head scan elements (Bs·L·H·P·N)/s",
+        "value": E / (wall / args.steps),
+        "unit": "scan elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded counter-based generator; x,B,C,D ~ N(0,1), dt log-uniform [1e-3,1e-1], "
+                "A[h] = -U(1,16)); 3 input sets rotated",
+        "config": {"workload": name, "Bs": Bs, "L": L, "H": H, "P": P, "G": G, "N": N,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": flops / avg / 1e12,
+            "peak": MFMA_F32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops / avg / 1e12 / MFMA_F32_PEAK_TFLOPS,
+            "traffic": load_traffic(name, kernel_source_hash()),
+            "kernel_avg_us": avg * 1e6,
+            "flops_per_launch": flops,
+            "timed": "the multi-head scan kernel (one launch per step); products in float32 on the matrix cores",
+        },
+        "hbm": {
+            "alg_bytes_per_launch": alg_bytes,
+            "achieved_GBps": alg_bytes / avg / 1e9,
+            "peak_GBps": HBM_PEAK_GBPS,
+            "frac": alg_bytes / avg / 1e9 / HBM_PEAK_GBPS,
+        },
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +289,10 @@ def main():
     import state_space_model_selective_amd as ssm
     import synth
     from synth import WORKLOADS
+
+    if args.workload in synth.SSD_WORKLOADS:
+        bench_ssd(args, args.workload)
+        return
 
     w = dict(WORKLOADS[args.workload])
     Bs, L, ED, N = w["Bs"], w["L"], w["ED"], w["N"]

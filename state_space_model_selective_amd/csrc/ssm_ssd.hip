@@ -15,7 +15,7 @@
 //   S_out = e^{cs_end} S_in + sum_s X_s^T (e^{cs_end - cs_s} dt_s) B_s
 // which the matrix cores compute (v_mfma_f32_16x16x4f32: float32 operands and
 // accumulation, so bf16 inputs are widened and nothing is rounded below
-// float32). One workgroup of 4 waves owns one (batch row, head), keeps the
+// float32). One workgroup of 8 waves owns one (batch row, head), keeps the
 // head's 64 x N state on chip for the whole sequence (registers for the
 // update, an LDS copy for the output product) and walks the chunks in order;
 // the next chunk's inputs are loaded into registers while the current one is
@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kQ = 32;       // chunk length
 constexpr int kP = 64;       // head channels (headdim)
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 
 template <typename T>
 struct SsdArgs {
@@ -59,7 +59,7 @@ struct alignas(16) SsdSmem {
   float Bm[2][kQ][N + 4];    // B chunk
   float Cm[2][kQ][N + 4];    // C chunk
   float S[kP][N + 4];        // state entering the chunk (operand of C S^T)
-  float M[kQ][kQ + 4];       // masked, decayed C B^T
+  float M[2][kQ][kQ + 4];    // masked, decayed C B^T: two halves of the sum over n
   float dt[2][kQ];
   float cs[kQ];              // A * inclusive cumulative dt within the chunk
   float ecs[kQ];             // e^{cs_t}
@@ -119,9 +119,10 @@ struct SsdStager {
 
 template <typename T, int N>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p) {
-  static_assert(kQ == 32 && kP == 64 && kWaves == 4, "work split below assumes these sizes");
-  static_assert(N % 32 == 0, "each wave owns N / 32 ... state column blocks");
-  constexpr int NB = N / 16 / kWaves;  // state column blocks per wave (2 for N = 128)
+  static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
+  static_assert(N == 64 || N == 128, "state sizes");
+  constexpr int NB = N / 16;          // state column blocks
+  constexpr int PBW = 4 * NB / 8;     // state row blocks per wave (its column block is wave % NB)
 
   __shared__ SsdSmem<N> sm;
 
@@ -135,19 +136,22 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const float Dh = p.D ? p.D[h] : 0.f;
   const int64_t nchunks = (p.L + kQ - 1) / kQ;
 
-  // the wave's share of the state: all 4 row blocks (p) x NB column blocks (n)
-  f4 st[4][NB];
+  // output block of this wave: t-block ytb (16 steps) x head-channel block ypb
+  const int ytb = wave >> 2, ypb = wave & 3;
+  // state blocks of this wave: rows 16 (spb + k), k < PBW, column block snb
+  const int snb = wave % NB, spb = (wave / NB) * PBW;
+  // C B^T task: causal block (0,0), (1,0) or (1,1), half of the sum over n
+  const int mblk = wave >> 1, mhalf = wave & 1;
+  const int mtb = mblk == 0 ? 0 : 1, msb = mblk == 2 ? 1 : 0;
+
+  f4 st[PBW];
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb)
+  for (int k = 0; k < PBW; ++k)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int nb = wave * NB + j;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * pb + 4 * lk + r, nn = 16 * nb + li;
-        st[pb][j][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
-        sm.S[pp][nn] = st[pb][j][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
+      st[k][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
+      sm.S[pp][nn] = st[k][r];
     }
 
   SsdStager<T, N> stg;
@@ -163,10 +167,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     // decay of the chunk: cs_t, e^{cs_t}, the state-update weights
     if (wave == 0 && lane < kQ) {
       float s = 0.f, tot = 0.f;
+#pragma unroll
       for (int r = 0; r < kQ; ++r) {
         const float v = sm.dt[cur][r];
         tot += v;
-        if (r <= lane) s += v;
+        s += r <= lane ? v : 0.f;
       }
       const float cst = Ah * s, cse = Ah * tot;
       sm.cs[lane] = cst;
@@ -176,88 +181,78 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     }
     __syncthreads();
 
-    // C B^T on the causal blocks (t-block, s-block) = (0,0), (1,0), (1,1),
-    // masked and decayed into M
-    if (wave < 3) {
-      const int tb = wave == 0 ? 0 : 1, sb = wave == 2 ? 1 : 0;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int n0 = 0; n0 < N; n0 += 4)
-        acc = mfma4(sm.Cm[cur][16 * tb + li][n0 + lk], sm.Bm[cur][16 * sb + li][n0 + lk], acc);
-      const int s = 16 * sb + li;
+    // C B^T on the causal blocks, each half of the sum over n by one wave,
+    // masked and decayed into M[half]
+    if (wave < 6) {
+      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+      const int n1 = mhalf * (N / 2);
+#pragma unroll
+      for (int n0 = 0; n0 < N / 2; n0 += 8) {
+        a0 = mfma4(sm.Cm[cur][16 * mtb + li][n1 + n0 + lk], sm.Bm[cur][16 * msb + li][n1 + n0 + lk], a0);
+        a1 = mfma4(sm.Cm[cur][16 * mtb + li][n1 + n0 + 4 + lk], sm.Bm[cur][16 * msb + li][n1 + n0 + 4 + lk], a1);
+      }
+      const int s = 16 * msb + li;
       const float css = sm.cs[s], dts = sm.dt[cur][s];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tb + 4 * lk + r;
-        sm.M[t][s] = s <= t ? acc[r] * __expf(sm.cs[t] - css) * dts : 0.f;
+        const int t = 16 * mtb + 4 * lk + r;
+        sm.M[mhalf][t][s] = s <= t ? (a0[r] + a1[r]) * __expf(sm.cs[t] - css) * dts : 0.f;
       }
     }
 
-    // inter-chunk output diag(e^{cs}) C S_in^T for head-channel block `wave`
-    f4 y[2];
+    // inter-chunk output diag(e^{cs}) C S_in^T for the wave's output block
+    f4 y;
+    {
+      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int n0 = 0; n0 < N; n0 += 4)
-        acc = mfma4(sm.Cm[cur][16 * tb + li][n0 + lk], sm.S[16 * wave + li][n0 + lk], acc);
+      for (int n0 = 0; n0 < N; n0 += 8) {
+        a0 = mfma4(sm.Cm[cur][16 * ytb + li][n0 + lk], sm.S[16 * ypb + li][n0 + lk], a0);
+        a1 = mfma4(sm.Cm[cur][16 * ytb + li][n0 + 4 + lk], sm.S[16 * ypb + li][n0 + 4 + lk], a1);
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= sm.ecs[16 * tb + 4 * lk + r];
-      y[tb] = acc;
+      for (int r = 0; r < 4; ++r) y[r] = (a0[r] + a1[r]) * sm.ecs[16 * ytb + 4 * lk + r];
     }
     __syncthreads();  // M complete
 
     // intra-chunk output M X (causal: s-blocks up to the t-block)
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-      for (int s0 = 0; s0 < 16 * (tb + 1); s0 += 4)
-        y[tb] = mfma4(sm.M[16 * tb + li][s0 + lk], sm.X[cur][s0 + lk][16 * wave + li], y[tb]);
-    }
+    for (int s0 = 0; s0 < 16 * (ytb + 1); s0 += 4)
+      y = mfma4(sm.M[0][16 * ytb + li][s0 + lk] + sm.M[1][16 * ytb + li][s0 + lk],
+                sm.X[cur][s0 + lk][16 * ypb + li], y);
     // y + D x -> global
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tb + 4 * lk + r, pp = 16 * wave + li;
-        if (t0 + t < p.L)
-          p.y[((b * p.L + t0 + t) * p.H + h) * kP + pp] = from_f32<T>(y[tb][r] + Dh * sm.X[cur][t][pp]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ytb + 4 * lk + r, pp = 16 * ypb + li;
+      if (t0 + t < p.L) p.y[((b * p.L + t0 + t) * p.H + h) * kP + pp] = from_f32<T>(y[r] + Dh * sm.X[cur][t][pp]);
+    }
 
     // state update S = e^{cs_end} S + (X w)^T B for the wave's blocks
     const float dec = __expf(sm.cs_end);
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int k = 0; k < PBW; ++k) st[k] *= dec;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        f4 acc = st[pb][j] * dec;
+    for (int s0 = 0; s0 < kQ; s0 += 4) {
+      const float bo = sm.Bm[cur][s0 + lk][16 * snb + li];
+      const float wv = sm.w[s0 + lk];
 #pragma unroll
-        for (int s0 = 0; s0 < kQ; s0 += 4)
-          acc = mfma4(sm.X[cur][s0 + lk][16 * pb + li] * sm.w[s0 + lk], sm.Bm[cur][s0 + lk][16 * (wave * NB + j) + li],
-                      acc);
-        st[pb][j] = acc;
-      }
+      for (int k = 0; k < PBW; ++k) st[k] = mfma4(sm.X[cur][s0 + lk][16 * (spb + k) + li] * wv, bo, st[k]);
+    }
     __syncthreads();  // every read of S_in and of this chunk's tiles is done
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int k = 0; k < PBW; ++k)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.S[16 * pb + 4 * lk + r][16 * (wave * NB + j) + li] = st[pb][j][r];
+      for (int r = 0; r < 4; ++r) sm.S[16 * (spb + k) + 4 * lk + r][16 * snb + li] = st[k][r];
     if (c + 1 < nchunks) stg.commit(sm, cur ^ 1, tid);
     __syncthreads();
   }
 
   if (p.h_last) {
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int k = 0; k < PBW; ++k)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pp = 16 * pb + 4 * lk + r, nn = 16 * (wave * NB + j) + li;
-          p.h_last[((b * p.H + h) * kP + pp) * N + nn] = st[pb][j][r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
+        p.h_last[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
+      }
   }
 }
 
