@@ -33,22 +33,32 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// 4-wide element access (16-byte float32 / 8-byte bfloat16 vectors)
+// 4-wide element access (16-byte float32 / 8-byte bfloat16 vectors).
+// Prefetches keep the loaded bits (Raw) and widen them only when they are
+// used: a conversion right after the load would make the wave wait for the
+// load there, and the prefetch would no longer overlap the computation.
 // ---------------------------------------------------------------------------
 template <typename T>
 struct Vec4;
 template <>
 struct Vec4<float> {
+  using Raw = float4;
+  static __device__ __forceinline__ Raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  static __device__ __forceinline__ float4 widen(Raw r) { return r; }
   static __device__ __forceinline__ float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
   static __device__ __forceinline__ void store(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 };
 template <>
 struct Vec4<uint16_t> {
-  static __device__ __forceinline__ float4 load(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
+  using Raw = uint2;
+  static __device__ __forceinline__ Raw zero() { return make_uint2(0u, 0u); }
+  static __device__ __forceinline__ Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  static __device__ __forceinline__ float4 widen(Raw u) {
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
   }
+  static __device__ __forceinline__ float4 load(const uint16_t* p) { return widen(load_raw(p)); }
   static __device__ __forceinline__ void store(uint16_t* p, float4 v) {
     uint2 u;
     u.x = static_cast<uint32_t>(from_f32<uint16_t>(v.x)) | (static_cast<uint32_t>(from_f32<uint16_t>(v.y)) << 16);

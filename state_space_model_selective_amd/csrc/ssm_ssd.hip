@@ -60,6 +60,7 @@ struct alignas(16) SsdSmem {
   float Cm[2][kQ][N + 4];    // C chunk
   float S[kP][N + 4];        // state entering the chunk (operand of C S^T)
   float M[2][kQ][kQ + 4];    // masked, decayed C B^T: two halves of the sum over n
+  float Y[kQ][kP + 4];       // output of the chunk before D x
   float dt[2][kQ];
   float cs[kQ];              // A * inclusive cumulative dt within the chunk
   float ecs[kQ];             // e^{cs_t}
@@ -73,47 +74,55 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Loads of one chunk into registers (4 elements per task) and their commit to
-// LDS. Rows at or past L are zero (dt = 0: a = 1 and no input).
+// Loads of one chunk into registers (4 elements per task, raw bits) and their
+// commit to LDS (widened there). Rows at or past L are zero (dt = 0: a = 1 and
+// no input); their loads read the last row instead (always in bounds, no
+// branch around the load), and the commit drops them.
 template <typename T, int N>
 struct SsdStager {
+  using V = Vec4<T>;
   static constexpr int kXT = kQ * kP / 4 / (64 * kWaves);  // x tasks per thread
   static constexpr int kBT = kQ * N / 4 / (64 * kWaves);   // B (and C) tasks per thread
-  float4 rx[kXT], rb[kBT], rc[kBT];
-  float rdt;
+  typename V::Raw rx[kXT], rb[kBT], rc[kBT];
+  T rdt;
+  bool vx[kXT], vb[kBT], vdt;
 
   __device__ __forceinline__ void load(const SsdArgs<T>& p, int tid, int64_t b, int64_t h, int64_t g, int64_t t0) {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
       const int64_t t = t0 + row;
-      rx[k] = t < p.L ? Vec4<T>::load(p.x + ((b * p.L + t) * p.H + h) * kP + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vx[k] = t < p.L;
+      rx[k] = V::load_raw(p.x + ((b * p.L + (vx[k] ? t : p.L - 1)) * p.H + h) * kP + c4);
     }
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
       const int64_t t = t0 + row;
-      const int64_t off = ((b * p.L + t) * p.G + g) * N + c4;
-      rb[k] = t < p.L ? Vec4<T>::load(p.B + off) : make_float4(0.f, 0.f, 0.f, 0.f);
-      rc[k] = t < p.L ? Vec4<T>::load(p.C + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vb[k] = t < p.L;
+      const int64_t off = ((b * p.L + (vb[k] ? t : p.L - 1)) * p.G + g) * N + c4;
+      rb[k] = V::load_raw(p.B + off);
+      rc[k] = V::load_raw(p.C + off);
     }
-    rdt = 0.f;
-    if (tid < kQ && t0 + tid < p.L) rdt = to_f32(p.dt[(b * p.L + t0 + tid) * p.H + h]);
+    const int64_t td = t0 + (tid & (kQ - 1));
+    vdt = tid < kQ && td < p.L;
+    rdt = p.dt[(b * p.L + (td < p.L ? td : p.L - 1)) * p.H + h];
   }
 
   __device__ __forceinline__ void commit(SsdSmem<N>& sm, int buf, int tid) const {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
-      *reinterpret_cast<float4*>(&sm.X[buf][row][c4]) = rx[k];
+      *reinterpret_cast<float4*>(&sm.X[buf][row][c4]) = vx[k] ? V::widen(rx[k]) : z;
     }
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
-      *reinterpret_cast<float4*>(&sm.Bm[buf][row][c4]) = rb[k];
-      *reinterpret_cast<float4*>(&sm.Cm[buf][row][c4]) = rc[k];
+      *reinterpret_cast<float4*>(&sm.Bm[buf][row][c4]) = vb[k] ? V::widen(rb[k]) : z;
+      *reinterpret_cast<float4*>(&sm.Cm[buf][row][c4]) = vb[k] ? V::widen(rc[k]) : z;
     }
-    if (tid < kQ) sm.dt[buf][tid] = rdt;
+    if (tid < kQ) sm.dt[buf][tid] = vdt ? to_f32(rdt) : 0.f;
   }
 };
 
@@ -184,12 +193,21 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     // C B^T on the causal blocks, each half of the sum over n by one wave,
     // masked and decayed into M[half]
     if (wave < 6) {
-      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+      // operands first (all LDS reads in flight together), then the products
+      constexpr int K = N / 8;
+      float ca[K], cb[K];
       const int n1 = mhalf * (N / 2);
 #pragma unroll
-      for (int n0 = 0; n0 < N / 2; n0 += 8) {
-        a0 = mfma4(sm.Cm[cur][16 * mtb + li][n1 + n0 + lk], sm.Bm[cur][16 * msb + li][n1 + n0 + lk], a0);
-        a1 = mfma4(sm.Cm[cur][16 * mtb + li][n1 + n0 + 4 + lk], sm.Bm[cur][16 * msb + li][n1 + n0 + 4 + lk], a1);
+      for (int j = 0; j < K; ++j) {
+        ca[j] = sm.Cm[cur][16 * mtb + li][n1 + 4 * j + lk];
+        cb[j] = sm.Bm[cur][16 * msb + li][n1 + 4 * j + lk];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+      for (int j = 0; j < K; j += 2) {
+        a0 = mfma4(ca[j], cb[j], a0);
+        a1 = mfma4(ca[j + 1], cb[j + 1], a1);
       }
       const int s = 16 * msb + li;
       const float css = sm.cs[s], dts = sm.dt[cur][s];
@@ -203,45 +221,85 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     // inter-chunk output diag(e^{cs}) C S_in^T for the wave's output block
     f4 y;
     {
+      constexpr int K = N / 4;
+      float ca[K], sb[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        ca[j] = sm.Cm[cur][16 * ytb + li][4 * j + lk];
+        sb[j] = sm.S[16 * ypb + li][4 * j + lk];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-      for (int n0 = 0; n0 < N; n0 += 8) {
-        a0 = mfma4(sm.Cm[cur][16 * ytb + li][n0 + lk], sm.S[16 * ypb + li][n0 + lk], a0);
-        a1 = mfma4(sm.Cm[cur][16 * ytb + li][n0 + 4 + lk], sm.S[16 * ypb + li][n0 + 4 + lk], a1);
+      for (int j = 0; j < K; j += 2) {
+        a0 = mfma4(ca[j], sb[j], a0);
+        a1 = mfma4(ca[j + 1], sb[j + 1], a1);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[r] = (a0[r] + a1[r]) * sm.ecs[16 * ytb + 4 * lk + r];
     }
     __syncthreads();  // M complete
 
-    // intra-chunk output M X (causal: s-blocks up to the t-block)
-    for (int s0 = 0; s0 < 16 * (ytb + 1); s0 += 4)
-      y = mfma4(sm.M[0][16 * ytb + li][s0 + lk] + sm.M[1][16 * ytb + li][s0 + lk],
-                sm.X[cur][s0 + lk][16 * ypb + li], y);
-    // y + D x -> global
+    // intra-chunk output M X (causal: s-blocks up to the t-block); the
+    // t-block 0 waves use the first half of the operands only
+    {
+      float ma[8], xb[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * ytb + 4 * lk + r, pp = 16 * ypb + li;
-      if (t0 + t < p.L) p.y[((b * p.L + t0 + t) * p.H + h) * kP + pp] = from_f32<T>(y[r] + Dh * sm.X[cur][t][pp]);
+      for (int j = 0; j < 8; ++j) {
+        const int s0 = 4 * j;
+        ma[j] = sm.M[0][16 * ytb + li][s0 + lk] + sm.M[1][16 * ytb + li][s0 + lk];
+        xb[j] = sm.X[cur][s0 + lk][16 * ypb + li];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y = mfma4(ma[j], xb[j], y);
+      if (ytb == 1) {
+#pragma unroll
+        for (int j = 4; j < 8; ++j) y = mfma4(ma[j], xb[j], y);
+      }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.Y[16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
 
     // state update S = e^{cs_end} S + (X w)^T B for the wave's blocks
     const float dec = __expf(sm.cs_end);
 #pragma unroll
     for (int k = 0; k < PBW; ++k) st[k] *= dec;
+    {
+      float bo[kQ / 4], xa[kQ / 4][PBW];
 #pragma unroll
-    for (int s0 = 0; s0 < kQ; s0 += 4) {
-      const float bo = sm.Bm[cur][s0 + lk][16 * snb + li];
-      const float wv = sm.w[s0 + lk];
+      for (int j = 0; j < kQ / 4; ++j) {
+        const int s0 = 4 * j;
+        bo[j] = sm.Bm[cur][s0 + lk][16 * snb + li];
+        const float wv = sm.w[s0 + lk];
 #pragma unroll
-      for (int k = 0; k < PBW; ++k) st[k] = mfma4(sm.X[cur][s0 + lk][16 * (spb + k) + li] * wv, bo, st[k]);
+        for (int k = 0; k < PBW; ++k) xa[j][k] = sm.X[cur][s0 + lk][16 * (spb + k) + li] * wv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kQ / 4; ++j)
+#pragma unroll
+        for (int k = 0; k < PBW; ++k) st[k] = mfma4(xa[j][k], bo[j], st[k]);
     }
-    __syncthreads();  // every read of S_in and of this chunk's tiles is done
+    __syncthreads();  // every read of S_in and of this chunk's tiles is done; Y complete
 #pragma unroll
     for (int k = 0; k < PBW; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.S[16 * (spb + k) + 4 * lk + r][16 * snb + li] = st[k][r];
+    // the next chunk's tiles (waits for its loads), then this chunk's output:
+    // the store is the last memory operation of the chunk, so no later wait
+    // for the loads has to wait for it as well
     if (c + 1 < nchunks) stg.commit(sm, cur ^ 1, tid);
+    {
+      // y + D x -> global, 4 consecutive head channels per thread
+      const int t = tid >> 4, c4 = (tid & 15) * 4;
+      if (t0 + t < p.L) {
+        const float4 yv = *reinterpret_cast<const float4*>(&sm.Y[t][c4]);
+        const float4 xv = *reinterpret_cast<const float4*>(&sm.X[cur][t][c4]);
+        Vec4<T>::store(p.y + ((b * p.L + t0 + t) * p.H + h) * kP + c4,
+                       make_float4(yv.x + Dh * xv.x, yv.y + Dh * xv.y, yv.z + Dh * xv.z, yv.w + Dh * xv.w));
+      }
+    }
     __syncthreads();
   }
 
