@@ -157,6 +157,12 @@ struct Stager {
   int row[TPT], chk[TPT];
   bool is_xd[TPT], chunk_ok[TPT], row_ok[TPT];
   float4 dval[TPT];              // D of the chunk's channels
+  // prefetched data: loaded bits (VEC; widened at commit, so that the wave
+  // does not wait for the loads at the prefetch), or widened values (element
+  // by element loads of a ragged channel count)
+  typename Vec4<T>::Raw qa[VEC ? TPT : 1], qb[VEC ? TPT : 1], qy[VEC ? TPT : 1], qz[VEC ? TPT : 1];
+  float4 qp[VEC ? TPT : 1];      // the reverse sweep's float32 partial
+  bool ld_ok[TPT];
   float4 ra[TPT], rb[TPT], rp[TPT], rz[TPT];
   int64_t pre_off[TPT];          // element offset of this task's row in the next round to prefetch
   int64_t out_off[TPT];          // element offset of this task's row in the next round to store
@@ -207,17 +213,27 @@ struct Stager {
       const int64_t off = pre_off[k];
       pre_off[k] += is_xd[k] ? step_xd : step_bc;
       row_ok[k] = rr * RT + row[k] < Lk;
+      ld_ok[k] = row_ok[k] && chunk_ok[k];
+      if constexpr (VEC) {
+        // rows past the end read element 0 instead (in bounds); commit drops them
+        const int64_t lo = ld_ok[k] ? off : 0;
+        if (!is_xd[k]) {
+          if (STAGE == STAGE_SCAN) qa[k] = Vec4<T>::load_raw(p.B + lo);
+          qb[k] = Vec4<T>::load_raw(p.C + lo);
+        } else {
+          if (STAGE == STAGE_SCAN) qa[k] = Vec4<T>::load_raw(p.x + lo);
+          qb[k] = Vec4<T>::load_raw(p.dl + lo);
+          if (STAGE == STAGE_CORRECT) qy[k] = Vec4<T>::load_raw(p.y + lo);
+          if (BIDIR && add_part) qp[k] = *reinterpret_cast<const float4*>(p.part + lo);
+          if (GATE) qz[k] = Vec4<T>::load_raw(p.z + lo);
+        }
+        continue;
+      }
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, pp = a, zz = a;
       if (row_ok[k] && chunk_ok[k]) {
         if (!is_xd[k]) {
           if (STAGE == STAGE_SCAN) a = Vec4<T>::load(p.B + off);
           bb = Vec4<T>::load(p.C + off);
-        } else if (VEC) {
-          if (STAGE == STAGE_SCAN) a = Vec4<T>::load(p.x + off);
-          bb = Vec4<T>::load(p.dl + off);
-          if (STAGE == STAGE_CORRECT) pp = Vec4<T>::load(p.y + off);
-          if (BIDIR && add_part) pp = *reinterpret_cast<const float4*>(p.part + off);
-          if (GATE) zz = Vec4<T>::load(p.z + off);
         } else {
           const int64_t ce = ce0 + 4 * chk[k];
           if (STAGE == STAGE_SCAN)
@@ -243,6 +259,29 @@ struct Stager {
     }
   }
 
+  // prefetched values of task k (zero for rows past the end)
+  __device__ __forceinline__ float4 val_a(int k) const {
+    if constexpr (VEC) return ld_ok[k] ? Vec4<T>::widen(qa[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    return ra[k];
+  }
+  __device__ __forceinline__ float4 val_b(int k) const {
+    if constexpr (VEC) return ld_ok[k] ? Vec4<T>::widen(qb[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    return rb[k];
+  }
+  template <int STAGE>
+  __device__ __forceinline__ float4 val_p(int k) const {
+    if constexpr (VEC) {
+      const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (STAGE == STAGE_CORRECT) return ld_ok[k] ? Vec4<T>::widen(qy[k]) : z4;
+      return ld_ok[k] ? qp[k] : z4;
+    }
+    return rp[k];
+  }
+  __device__ __forceinline__ float4 val_z(int k) const {
+    if constexpr (VEC) return ld_ok[k] ? Vec4<T>::widen(qz[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    return rz[k];
+  }
+
   // registers -> LDS tile
   template <int STAGE>
   __device__ __forceinline__ void commit(const ScanArgs<T>& p, Tile<RT, GATE>& tl) const {
@@ -250,8 +289,8 @@ struct Stager {
     for (int k = 0; k < TPT; ++k) {
       const int r = row[k], c4 = 4 * chk[k];
       if (is_xd[k]) {
-        const float4 xv = ra[k];
-        float4 dv = rb[k];
+        const float4 xv = val_a(k);
+        float4 dv = val_b(k);
         if (p.dt_pre) {
           // padded rows and channels keep delta = 0 (a = 1, b = 0: no effect)
           const bool ok = row_ok[k] && chunk_ok[k];
@@ -261,22 +300,24 @@ struct Stager {
           dv.z = ok && ce + 2 < ED ? step_size(p, dv.z, ce + 2) : 0.f;
           dv.w = ok && ce + 3 < ED ? step_size(p, dv.w, ce + 3) : 0.f;
         }
-        if (GATE)
-          *reinterpret_cast<float4*>(&tl.gate[r][c4]) = make_float4(silu(rz[k].x), silu(rz[k].y), silu(rz[k].z), silu(rz[k].w));
+        if (GATE) {
+          const float4 zv = val_z(k);
+          *reinterpret_cast<float4*>(&tl.gate[r][c4]) = make_float4(silu(zv.x), silu(zv.y), silu(zv.z), silu(zv.w));
+        }
         *reinterpret_cast<float4*>(&tl.dt[r][c4]) = dv;
         if (STAGE == STAGE_CORRECT) {
-          *reinterpret_cast<float4*>(&tl.aux[r][c4]) = rp[k];
+          *reinterpret_cast<float4*>(&tl.aux[r][c4]) = val_p<STAGE>(k);
         } else {
           *reinterpret_cast<float4*>(&tl.dx[r][c4]) =
               make_float4(dv.x * xv.x, dv.y * xv.y, dv.z * xv.z, dv.w * xv.w);
           *reinterpret_cast<float4*>(&tl.aux[r][c4]) =
               (BIDIR && add_part)
-                  ? rp[k]
+                  ? val_p<STAGE>(k)
                   : make_float4(dval[k].x * xv.x, dval[k].y * xv.y, dval[k].z * xv.z, dval[k].w * xv.w);
         }
       } else {
-        if (STAGE == STAGE_SCAN) *reinterpret_cast<float4*>(&tl.bq[r][c4]) = ra[k];
-        *reinterpret_cast<float4*>(&tl.cq[r][c4]) = rb[k];
+        if (STAGE == STAGE_SCAN) *reinterpret_cast<float4*>(&tl.bq[r][c4]) = val_a(k);
+        *reinterpret_cast<float4*>(&tl.cq[r][c4]) = val_b(k);
       }
     }
   }
