@@ -51,11 +51,27 @@ def alg_bytes(w):
     return b
 
 
-def kernel_source_hash():
-    """sha256[:16] over every file of the HIP sources folder (sorted by name)."""
+KERNEL_SOURCES = {
+    "fwd": ("scan_common.h", "ssm_scan.hip"),
+    "bwd": ("scan_common.h", "ssm_scan_bwd.hip"),
+    "ssd": ("scan_common.h", "ssm_ssd.hip"),
+}
+
+
+def kernel_family(workload):
+    if workload.startswith("bwd"):
+        return "bwd"
+    if workload.startswith("ssd"):
+        return "ssd"
+    return "fwd"
+
+
+def kernel_source_hash(workload):
+    """sha256[:16] over the HIP source files that the workload's kernels are
+    built from (in the order listed in KERNEL_SOURCES)."""
     h = hashlib.sha256()
     src = os.path.join(ROOT, "state_space_model_selective_amd", "csrc")
-    for name in sorted(os.listdir(src)):
+    for name in KERNEL_SOURCES[kernel_family(workload)]:
         with open(os.path.join(src, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -237,7 +253,7 @@ def bench_ssd(args, name):
             "peak": MFMA_F32_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops / avg / 1e12 / MFMA_F32_PEAK_TFLOPS,
-            "traffic": load_traffic(name, kernel_source_hash()),
+            "traffic": load_traffic(name, kernel_source_hash(name)),
             "kernel_avg_us": avg * 1e6,
             "flops_per_launch": flops,
             "timed": "the multi-head scan kernel (one launch per step); products in float32 on the matrix cores",
@@ -248,7 +264,7 @@ def bench_ssd(args, name):
             "peak_GBps": HBM_PEAK_GBPS,
             "frac": alg_bytes / avg / 1e9 / HBM_PEAK_GBPS,
         },
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(name),
         "parity": parity,
         "cpu_baseline": cpu,
     }
@@ -367,7 +383,7 @@ def main():
     # directions; algorithmic cost 2 mul + exp + 2 x (state FMA + C FMA) = 8
     slots = SLOTS_PER_ELEMENT_BWD if bwd else (SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT)
     achieved_slots = kernel_elem_rate * slots
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(args.workload)
     traffic = load_traffic(args.workload, src_hash)
 
     # parity check of step 0's input set against the oracle (also the CPU baseline)
