@@ -42,14 +42,22 @@ namespace {
 //   staging  global -> registers (prefetched one round ahead, 16-byte loads)
 //            -> LDS tile: delta, delta*x, B, C and D*x (in the forward sweep
 //            of the bidirectional scan: the reverse sweep's partial y instead)
-//   local    each wave runs its segment from a zero state, keeping a_t and
-//            b_t of all TS steps in registers; segment aggregate
-//            (prod a = exp2(A log2e * sum delta), h_end) to LDS
-//   fold     the state entering segment s is the previous round's carry
-//            folded through the aggregates of segments 0..s-1; the last wave
-//            also folds its own aggregate and publishes the round's carry
+//   segment  the waves' segments rotate with the round (wave w takes
+//            segment (w + round) mod SEG), so that every wave does the same
+//            work over SEG rounds
+//   first    the wave of segment 0 knows its entering state (the previous
+//            round's carry): one pass, h_t = a_t h_{t-1} + b_t and the C
+//            contraction (into the LDS output tile after the round's mid
+//            barrier, since the store of the previous round reads that tile
+//            before it); its end state goes to LDS
+//   local    the other waves run their segments from a zero state, keeping
+//            a_t and b_t of all TS steps in registers; segments 1 .. SEG-2
+//            also publish their aggregate (prod a = exp2(A log2e * sum
+//            delta), h_end) to LDS
+//   fold     the state entering segment s > 0 is segment 0's end state
+//            folded through the aggregates of segments 1 .. s-1
 //   replay   h_t = a_t h_{t-1} + b_t from the true entering state, then the
-//            C contraction over the lane's states into the LDS output tile
+//            C contraction; the last segment's end state is the round's carry
 //   store    one round later: sum of the four state quads + D x (or the
 //            reverse sweep's partial), 16-byte stores
 // With SEG == 1 the carry is known before the segment starts, so the local
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   Stager<T, RT, TPT, BIDIR, VEC, GATE> st;
   st.init(p, tid, e0);
   double sd_total = 0.0;  // split sequence: sum of delta over this wave's segments
-  float carry[4];         // state after the last completed round (valid in wave SEG-1)
+  float carry[4];         // state after the last completed round (valid in wave SEG-1 after the sweep)
 
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
     const bool rev = BIDIR && sweep == 0;
@@ -474,57 +482,96 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
           out.yq[g][i][ch] = yp;
         }
       } else {
-        // local pass from a zero state
+        // This wave's segment of the round. The roles rotate with the round,
+        // so that over SEG rounds every wave (and SIMD) does the same work.
+        const int seg = (wave + static_cast<int>(r)) & (SEG - 1);
         float av[TS][4], bv[TS][4];
-        float hl[4];
-        float sd;
+        float ys[TS];
+        if (seg == 0) {
+          // the entering state is the previous round's carry: a single pass,
+          // whose end state is the exact state entering segment 1
+          const float4 c0 = fa.carry[(r + 1) & 1][lane];
+          float h[4] = {c0.x, c0.y, c0.z, c0.w};
+          float sd = 0.f;
 #pragma unroll
-        for (int i = 0; i < TS; ++i) {
-          const int row = wave * TS + i;
-          const float dt = cur.dt[row][ch], dx = cur.dx[row][ch];
-          const float bq = cur.bq[row][q];
-          sd = i == 0 ? dt : sd + dt;
-          const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
+          for (int i = 0; i < TS; ++i) {
+            const float dt = cur.dt[i][ch], dx = cur.dx[i][ch];
+            const float bq = cur.bq[i][q], cq = cur.cq[i][q];
+            if (SPLIT) sd += dt;
+            const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
-            bv[i][j] = dx * bb[j];
-            hl[j] = i == 0 ? bv[i][j] : __builtin_fmaf(av[i][j], hl[j], bv[i][j]);
+            for (int j = 0; j < 4; ++j) {
+              // (kept in av / bv like the other segments' values, so that
+              // both paths leave them in the same registers)
+              av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
+              bv[i][j] = dx * bb[j];
+              h[j] = __builtin_fmaf(av[i][j], h[j], bv[i][j]);
+            }
+            // the output tile may still be read by this round's store of the
+            // previous round: the contraction goes to the tile after the barrier
+            ys[i] = dot_quad(cq, h);
+          }
+          if (SPLIT) sd_total += static_cast<double>(sd);
+          fa.H[0][lane] = make_float4(h[0], h[1], h[2], h[3]);
+        } else {
+          // local pass from a zero state: a_t and b_t of every step
+          float sd = 0.f;
+#pragma unroll
+          for (int i = 0; i < TS; ++i) {
+            const int row = seg * TS + i;
+            const float dt = cur.dt[row][ch], dx = cur.dx[row][ch];
+            const float bq = cur.bq[row][q];
+            sd += dt;
+            const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
+              bv[i][j] = dx * bb[j];
+            }
+          }
+          if (SPLIT) sd_total += static_cast<double>(sd);
+          if (seg < SEG - 1) {
+            // aggregate for the later segments (the last one needs none):
+            // prod a = exp2(A log2e * sum delta) and the end state from zero
+            float hl[4] = {bv[0][0], bv[0][1], bv[0][2], bv[0][3]};
+#pragma unroll
+            for (int i = 1; i < TS; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) hl[j] = __builtin_fmaf(av[i][j], hl[j], bv[i][j]);
+            fa.A[seg][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
+                                          __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
+            fa.H[seg][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
           }
         }
-        if (SPLIT) sd_total += static_cast<double>(sd);
-        fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
-                                       __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
-        fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
         __syncthreads();
 
-        // entering state: previous round's carry through segments 0 .. wave-1
-        // (wave is uniform, so the loop bound is scalar)
-        const float4 c0 = fa.carry[(r + 1) & 1][lane];
-        float hin[4] = {c0.x, c0.y, c0.z, c0.w};
-        for (int k = 0; k < wave; ++k) {
-          const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane];
-          hin[0] = __builtin_fmaf(Ak.x, hin[0], Hk.x);
-          hin[1] = __builtin_fmaf(Ak.y, hin[1], Hk.y);
-          hin[2] = __builtin_fmaf(Ak.z, hin[2], Hk.z);
-          hin[3] = __builtin_fmaf(Ak.w, hin[3], Hk.w);
-        }
-
-        // replay from the entering state
+        if (seg == 0) {
 #pragma unroll
-        for (int i = 0; i < TS; ++i) {
-          const int row = wave * TS + i;
-          const float cq = cur.cq[row][q];
+          for (int i = 0; i < TS; ++i) out.yq[g][i][ch] = ys[i];
+        } else {
+          // entering state: segment 0's end state through segments 1 .. seg-1
+          // (seg is uniform, so the loop bound is scalar)
+          const float4 c0 = fa.H[0][lane];
+          float hin[4] = {c0.x, c0.y, c0.z, c0.w};
+#pragma unroll 1
+          for (int k = 1; k < seg; ++k) {
+            const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane];
+            hin[0] = __builtin_fmaf(Ak.x, hin[0], Hk.x);
+            hin[1] = __builtin_fmaf(Ak.y, hin[1], Hk.y);
+            hin[2] = __builtin_fmaf(Ak.z, hin[2], Hk.z);
+            hin[3] = __builtin_fmaf(Ak.w, hin[3], Hk.w);
+          }
+          // replay from the entering state
 #pragma unroll
-          for (int j = 0; j < 4; ++j) hin[j] = __builtin_fmaf(av[i][j], hin[j], bv[i][j]);
-          const float yp = dot_quad(cq, hin);
-          out.yq[g][row][ch] = yp;
-        }
-        // the last segment's end state is the round's carry
-        if (wave == SEG - 1) {
-          fa.carry[r & 1][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
+          for (int i = 0; i < TS; ++i) {
+            const int row = seg * TS + i;
+            const float cq = cur.cq[row][q];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) carry[j] = hin[j];
+            for (int j = 0; j < 4; ++j) hin[j] = __builtin_fmaf(av[i][j], hin[j], bv[i][j]);
+            out.yq[g][row][ch] = dot_quad(cq, hin);
+          }
+          // the last segment's end state is the round's carry
+          if (seg == SEG - 1) fa.carry[r & 1][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
         }
       }
 
@@ -532,6 +579,11 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       __syncthreads();
     }
     st.template store_out<STAGE_SCAN>(p, rounds - 1, tile[(rounds - 1) & 1], out);
+    if (SEG > 1 && wave == SEG - 1) {
+      // the last round's carry (published before the round's closing barrier)
+      const float4 c = fa.carry[(rounds - 1) & 1][lane];
+      carry[0] = c.x, carry[1] = c.y, carry[2] = c.z, carry[3] = c.w;
+    }
 
     if constexpr (!SPLIT) {
       float* h_out = rev ? p.g_first : p.h_last;
