@@ -46,10 +46,10 @@ namespace {
 //            segment (w + round) mod SEG), so that every wave does the same
 //            work over SEG rounds
 //   first    the wave of segment 0 knows its entering state (the previous
-//            round's carry): one pass, h_t = a_t h_{t-1} + b_t and the C
-//            contraction (into the LDS output tile after the round's mid
-//            barrier, since the store of the previous round reads that tile
-//            before it); its end state goes to LDS
+//            round's carry): one pass, h_t = a_t h_{t-1} + b_t, keeping the
+//            states; its end state goes to LDS. Its C contraction runs after
+//            the round's mid barrier (the store of the previous round reads
+//            the output tile before it)
 //   local    the other waves run their segments from a zero state, keeping
 //            a_t and b_t of all TS steps in registers; segments 1 .. SEG-2
 //            also publish their aggregate (prod a = exp2(A log2e * sum
@@ -486,7 +486,6 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
         // so that over SEG rounds every wave (and SIMD) does the same work.
         const int seg = (wave + static_cast<int>(r)) & (SEG - 1);
         float av[TS][4], bv[TS][4];
-        float ys[TS];
         if (seg == 0) {
           // the entering state is the previous round's carry: a single pass,
           // whose end state is the exact state entering segment 1
@@ -496,20 +495,19 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
           for (int i = 0; i < TS; ++i) {
             const float dt = cur.dt[i][ch], dx = cur.dx[i][ch];
-            const float bq = cur.bq[i][q], cq = cur.cq[i][q];
+            const float bq = cur.bq[i][q];
             if (SPLIT) sd += dt;
             const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              // (kept in av / bv like the other segments' values, so that
-              // both paths leave them in the same registers)
+              // (a_t and b_t go to av / bv like the other segments' values, so
+              // that both paths leave them in the same registers; once used,
+              // av keeps the state h_t for the contraction after the barrier)
               av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
               bv[i][j] = dx * bb[j];
               h[j] = __builtin_fmaf(av[i][j], h[j], bv[i][j]);
+              av[i][j] = h[j];
             }
-            // the output tile may still be read by this round's store of the
-            // previous round: the contraction goes to the tile after the barrier
-            ys[i] = dot_quad(cq, h);
           }
           if (SPLIT) sd_total += static_cast<double>(sd);
           fa.H[0][lane] = make_float4(h[0], h[1], h[2], h[3]);
@@ -546,8 +544,11 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
         __syncthreads();
 
         if (seg == 0) {
+          // the C contraction of segment 0's states; the output tile may be
+          // read by this round's store of the previous round until the barrier.
+          // (Doing it here also balances the two phases' work over the waves.)
 #pragma unroll
-          for (int i = 0; i < TS; ++i) out.yq[g][i][ch] = ys[i];
+          for (int i = 0; i < TS; ++i) out.yq[g][i][ch] = dot_quad(cur.cq[i][q], av[i]);
         } else {
           // entering state: segment 0's end state through segments 1 .. seg-1
           // (seg is uniform, so the loop bound is scalar)
