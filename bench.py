@@ -146,7 +146,8 @@ def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
 
 
 # dense fp32 matrix-core peak of the MI355X (the multi-head scan's products run there)
-MFMA_F32_PEAK_TFLOPS = 157.3
+MFMA_F32_PEAK_TFLOPS = 157.3   # dense float32 matrix instructions
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix instructions
 SSD_CHUNK = 32  # chunk length of the multi-head kernel
 
 
@@ -231,6 +232,27 @@ def bench_ssd(args, name):
         rel = float(np.max(np.abs(got - y_ref) / (1 + np.abs(y_ref))))
         parity = dict(max_rel_err=rel, tol=tol, passed=bool(rel <= tol))
 
+    # float32 inputs run on the float32 matrix instructions, bf16 inputs on the
+    # bf16 ones; the roofline is the resource whose time bound is the larger
+    bf16 = w["dtype"] == "bf16"
+    peak_mfma = MFMA_BF16_PEAK_TFLOPS if bf16 else MFMA_F32_PEAK_TFLOPS
+    mfma = {"achieved_TFLOPs": flops / avg / 1e12, "peak_TFLOPs": peak_mfma,
+            "frac": flops / avg / 1e12 / peak_mfma, "flops_per_launch": flops,
+            "instruction": "v_mfma_f32_16x16x32_bf16" if bf16 else "v_mfma_f32_16x16x4f32"}
+    hbm = {"alg_bytes_per_launch": alg_bytes, "achieved_GBps": alg_bytes / avg / 1e9, "peak_GBps": HBM_PEAK_GBPS,
+           "frac": alg_bytes / avg / 1e9 / HBM_PEAK_GBPS}
+    timed = ("the multi-head scan kernel (one launch per step); products on the " +
+             ("bf16 matrix instructions (float32 operands split into two bf16 parts)" if bf16
+              else "float32 matrix instructions"))
+    if flops / (peak_mfma * 1e12) >= alg_bytes / (HBM_PEAK_GBPS * 1e9):
+        roofline = {"bound": "mfma", "achieved": mfma["achieved_TFLOPs"], "peak": peak_mfma, "unit": "TFLOP/s",
+                    "frac": mfma["frac"]}
+    else:
+        roofline = {"bound": "hbm", "achieved": hbm["achieved_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": hbm["frac"]}
+    roofline.update({"traffic": load_traffic(name, kernel_source_hash(name)), "kernel_avg_us": avg * 1e6,
+                     "timed": timed})
+
     out = {
         "metric": "multi-head scan elements (Bs·L·H·P·N)/s",
         "value": E / (wall / args.steps),
@@ -247,23 +269,9 @@ def bench_ssd(args, name):
                 "A[h] = -U(1,16)); 3 input sets rotated",
         "config": {"workload": name, "Bs": Bs, "L": L, "H": H, "P": P, "G": G, "N": N,
                    "parallelism": "single GPU"},
-        "roofline": {
-            "bound": "mfma",
-            "achieved": flops / avg / 1e12,
-            "peak": MFMA_F32_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": flops / avg / 1e12 / MFMA_F32_PEAK_TFLOPS,
-            "traffic": load_traffic(name, kernel_source_hash(name)),
-            "kernel_avg_us": avg * 1e6,
-            "flops_per_launch": flops,
-            "timed": "the multi-head scan kernel (one launch per step); products in float32 on the matrix cores",
-        },
-        "hbm": {
-            "alg_bytes_per_launch": alg_bytes,
-            "achieved_GBps": alg_bytes / avg / 1e9,
-            "peak_GBps": HBM_PEAK_GBPS,
-            "frac": alg_bytes / avg / 1e9 / HBM_PEAK_GBPS,
-        },
+        "roofline": roofline,
+        "mfma": mfma,
+        "hbm": hbm,
         "kernel_source_sha256_16": kernel_source_hash(name),
         "parity": parity,
         "cpu_baseline": cpu,

@@ -29,6 +29,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "scan_common.h"
 #include "ssm_scan.h"
@@ -314,6 +315,315 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   }
 }
 
+// ---------------------------------------------------------------------------
+// bfloat16 inputs. The products take bf16 operands on the bf16 matrix
+// instruction, v_mfma_f32_16x16x32_bf16 (float32 accumulation; 16 times the
+// float32 instruction's rate). C, B and x are bf16 already and enter exactly.
+// The float32 operands -- the decayed, masked C B^T, the state (kept float32
+// in registers; its LDS copy is the operand) and the decay-weighted B of the
+// state update -- are split into a high and a low bf16 part, v = hi + lo with
+// hi = bf16(v) and lo = bf16(v - hi) (round to nearest even), and each product
+// takes both parts: the operand error is then below 2^-17 |v|, so the state
+// and the output keep float32-level accuracy.
+//
+// Operand layout (16 x 16 x 32, one wave): lane l supplies the 8 consecutive
+// k = 8 (l / 16) .. 8 (l / 16) + 7 of row l % 16 of A and of column l % 16 of
+// B, i.e. one 16-byte read of a k-contiguous LDS row; result register r of
+// lane l is D[4 (l / 16) + r][l % 16]. Products over the state index n read
+// n-contiguous tiles (C[t][n], B[s][n], S[p][n]); products over the chunk's
+// steps read s-contiguous ones (M[t][s], x transposed to Xt[p][s]).
+//
+// Per chunk, two barriers:
+//   phase 1  store y of the previous chunk; C B^T on the three causal 16 x 16
+//            blocks (waves 0..2) -> masked, decayed M (bf16 pair); every wave: its
+//            16 x 16 block of diag(e^{cs}) C S_in^T and the state update of
+//            its state blocks, S = e^{cs_end} S + X^T (w B)
+//   phase 2  M X added to the output block, + D x -> Y (float32, by chunk
+//            parity); bf16 pair copy of the new state; the next chunk's tiles
+//            (prefetched into registers during phase 1) and its decays
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f4 mfma_bf16(uint4 a, uint4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+// v = hi + lo, hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  const __bf16 h = static_cast<__bf16>(v);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = bf16_bits(v - static_cast<float>(h));
+}
+__device__ __forceinline__ void split_pack_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = pack_bf16(a - static_cast<float>(h[0]), b - static_cast<float>(h[1]));
+}
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int N>
+struct alignas(16) SsdSmemBf {
+  static constexpr int NP = N + 8;   // row pitch (elements) of the n-contiguous tiles
+  static constexpr int TP = kQ + 8;  // row pitch of the s-contiguous tiles
+  uint16_t C[2][kQ][NP];   // C chunk [t][n]
+  uint16_t B[2][kQ][NP];   // B chunk [s][n]
+  uint16_t Xt[2][kP][TP];  // x chunk, transposed [p][s]
+  uint16_t S[2][kP][NP];   // state entering the chunk [p][n]: high, low bf16 part
+  uint16_t M[2][kQ][TP];   // masked, decayed C B^T [t][s]: high, low part
+  float Y[2][kQ][kP + 4];  // y of a chunk (with D x), by chunk parity
+  float dt[2][kQ];
+  float cs[2][kQ];         // A * inclusive cumulative dt within the chunk
+  float ecs[2][kQ];        // e^{cs_t}
+  float w[2][kQ];          // e^{cs_end - cs_s} dt_s
+  float cs_end[2];
+};
+
+template <int N>
+struct SsdStagerBf {
+  static constexpr int kXT = kQ * kP / 4 / (64 * kWaves);  // x tasks per thread
+  static constexpr int kBT = kQ * N / 4 / (64 * kWaves);   // B (and C) tasks per thread
+  uint2 rx[kXT], rb[kBT], rc[kBT];
+  uint16_t rdt;
+  bool vx[kXT], vb[kBT], vdt;
+
+  __device__ __forceinline__ void load(const SsdArgs<uint16_t>& p, int tid, int64_t b, int64_t h, int64_t g,
+                                       int64_t t0) {
+#pragma unroll
+    for (int k = 0; k < kXT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
+      const int64_t t = t0 + row;
+      vx[k] = t < p.L;
+      rx[k] = *reinterpret_cast<const uint2*>(p.x + ((b * p.L + (vx[k] ? t : p.L - 1)) * p.H + h) * kP + c4);
+    }
+#pragma unroll
+    for (int k = 0; k < kBT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
+      const int64_t t = t0 + row;
+      vb[k] = t < p.L;
+      const int64_t off = ((b * p.L + (vb[k] ? t : p.L - 1)) * p.G + g) * N + c4;
+      rb[k] = *reinterpret_cast<const uint2*>(p.B + off);
+      rc[k] = *reinterpret_cast<const uint2*>(p.C + off);
+    }
+    const int64_t td = t0 + (tid & (kQ - 1));
+    vdt = tid < kQ && td < p.L;
+    rdt = p.dt[(b * p.L + (td < p.L ? td : p.L - 1)) * p.H + h];
+  }
+
+  // rows at or past L are zero (dt = 0: a = 1 and no input)
+  __device__ __forceinline__ void commit(SsdSmemBf<N>& sm, int buf, int tid) const {
+#pragma unroll
+    for (int k = 0; k < kXT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
+      const uint2 v = vx[k] ? rx[k] : make_uint2(0u, 0u);
+      sm.Xt[buf][c4 + 0][row] = static_cast<uint16_t>(v.x);
+      sm.Xt[buf][c4 + 1][row] = static_cast<uint16_t>(v.x >> 16);
+      sm.Xt[buf][c4 + 2][row] = static_cast<uint16_t>(v.y);
+      sm.Xt[buf][c4 + 3][row] = static_cast<uint16_t>(v.y >> 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kBT; ++k) {
+      const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
+      *reinterpret_cast<uint2*>(&sm.B[buf][row][c4]) = vb[k] ? rb[k] : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(&sm.C[buf][row][c4]) = vb[k] ? rc[k] : make_uint2(0u, 0u);
+    }
+    if (tid < kQ) sm.dt[buf][tid] = vdt ? to_f32(rdt) : 0.f;
+  }
+};
+
+// cs, e^{cs}, w and cs_end of the chunk in buffer buf (one wave, from the dt
+// that this same wave committed)
+template <int N>
+__device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah, int lane) {
+  if (lane < kQ) {
+    float s = 0.f, tot = 0.f;
+#pragma unroll
+    for (int r = 0; r < kQ; ++r) {
+      const float v = sm.dt[buf][r];
+      tot += v;
+      s += r <= lane ? v : 0.f;
+    }
+    const float cst = Ah * s, cse = Ah * tot;
+    sm.cs[buf][lane] = cst;
+    sm.ecs[buf][lane] = __expf(cst);
+    sm.w[buf][lane] = __expf(cse - cst) * sm.dt[buf][lane];
+    if (lane == 0) sm.cs_end[buf] = cse;
+  }
+}
+
+// y rows t0 .. t0 + kQ - 1 (those before L) -> global, 4 head channels per thread
+__device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const float (&Y)[kQ][kP + 4], int tid,
+                                             int64_t b, int64_t h, int64_t t0) {
+  const int t = tid >> 4, c4 = (tid & 15) * 4;
+  if (t0 + t < p.L) {
+    const float4 v = *reinterpret_cast<const float4*>(&Y[t][c4]);
+    *reinterpret_cast<uint2*>(p.y + ((b * p.L + t0 + t) * p.H + h) * kP + c4) =
+        make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+  }
+}
+
+template <int N>
+__global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs<uint16_t> p) {
+  static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
+  static_assert(N == 64 || N == 128, "state sizes");
+  constexpr int NB = N / 16;       // state column blocks
+  constexpr int PBW = 4 * NB / 8;  // state row blocks per wave (its column block is wave % NB)
+  constexpr int KN = N / 32;       // products over n: instructions per 16 x 16 block
+
+  __shared__ SsdSmemBf<N> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int64_t b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int64_t g = h / (p.H / p.G);
+  const float Ah = p.A[h];
+  const float Dh = p.D ? p.D[h] : 0.f;
+  const int64_t nchunks = (p.L + kQ - 1) / kQ;
+
+  const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
+  const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
+  const int mtb = wave == 0 ? 0 : 1, msb = wave == 2 ? 1 : 0;  // causal C B^T block of waves 0..2
+
+  f4 st[PBW];
+#pragma unroll
+  for (int k = 0; k < PBW; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
+      st[k][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
+      split_bf16(st[k][r], sm.S[0][pp][nn], sm.S[1][pp][nn]);
+    }
+  // the block t < 16, s >= 16 of M stays zero (future steps)
+  for (int i = tid; i < 2 * kQ * SsdSmemBf<N>::TP; i += 64 * kWaves) (&sm.M[0][0][0])[i] = 0;
+
+  SsdStagerBf<N> stg;
+  stg.load(p, tid, b, h, g, 0);
+  stg.commit(sm, 0, tid);
+  if (wave == 0) chunk_decay(sm, 0, Ah, lane);
+  __syncthreads();
+
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int cur = c & 1, nxt = cur ^ 1;
+    const int64_t t0 = c * kQ;
+    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ);
+
+    // ---- phase 1 ----
+    if (c > 0) store_y_bf16(p, sm.Y[nxt], tid, b, h, t0 - kQ);
+
+    if (wave < 3) {
+      // causal block of C B^T, masked and decayed: M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t
+      uint4 ca[KN], cb[KN];
+#pragma unroll
+      for (int j = 0; j < KN; ++j) {
+        ca[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * mtb + li][32 * j + 8 * lk]);
+        cb[j] = *reinterpret_cast<const uint4*>(&sm.B[cur][16 * msb + li][32 * j + 8 * lk]);
+      }
+      f4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KN; ++j) a = mfma_bf16(ca[j], cb[j], a);
+      const int s = 16 * msb + li;
+      const float css = sm.cs[cur][s], dts = sm.dt[cur][s];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mtb + 4 * lk + r;
+        split_bf16(s <= t ? a[r] * __expf(sm.cs[cur][t] - css) * dts : 0.f, sm.M[0][t][s], sm.M[1][t][s]);
+      }
+    }
+
+    // inter-chunk output of the wave's block: diag(e^{cs}) C S_in^T
+    f4 y;
+    {
+      uint4 ca[KN], sh[KN], sl[KN];
+#pragma unroll
+      for (int j = 0; j < KN; ++j) {
+        ca[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * ytb + li][32 * j + 8 * lk]);
+        sh[j] = *reinterpret_cast<const uint4*>(&sm.S[0][16 * ypb + li][32 * j + 8 * lk]);
+        sl[j] = *reinterpret_cast<const uint4*>(&sm.S[1][16 * ypb + li][32 * j + 8 * lk]);
+      }
+      f4 a = {0.f, 0.f, 0.f, 0.f}, a2 = a;
+#pragma unroll
+      for (int j = 0; j < KN; ++j) {
+        a = mfma_bf16(ca[j], sh[j], a);
+        a2 = mfma_bf16(ca[j], sl[j], a2);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = (a[r] + a2[r]) * sm.ecs[cur][16 * ytb + 4 * lk + r];
+    }
+
+    // state update of the wave's blocks: S = e^{cs_end} S + X^T (w B)
+    {
+      const float dec = __expf(sm.cs_end[cur]);
+#pragma unroll
+      for (int k = 0; k < PBW; ++k) st[k] *= dec;
+      // operand B: w_s B[s][n] for s = 8 lk .. 8 lk + 7, n = 16 snb + li
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s0 = 8 * lk + 2 * i;
+        const float b0 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0][16 * snb + li]) << 16);
+        const float b1 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0 + 1][16 * snb + li]) << 16);
+        split_pack_bf16(b0 * sm.w[cur][s0], b1 * sm.w[cur][s0 + 1], bh[i], bl[i]);
+      }
+      const uint4 boh = make_uint4(bh[0], bh[1], bh[2], bh[3]), bol = make_uint4(bl[0], bl[1], bl[2], bl[3]);
+#pragma unroll
+      for (int k = 0; k < PBW; ++k) {
+        const uint4 xa = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * (spb + k) + li][8 * lk]);
+        st[k] = mfma_bf16(xa, boh, st[k]);
+        st[k] = mfma_bf16(xa, bol, st[k]);
+      }
+    }
+    __syncthreads();  // M complete; every read of S_in done
+
+    // ---- phase 2 ----
+    {
+      // intra-chunk output M X (M is zero above the diagonal), then + D x
+      const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[0][16 * ytb + li][8 * lk]);
+      const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[1][16 * ytb + li][8 * lk]);
+      const uint4 xb = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * ypb + li][8 * lk]);
+      y = mfma_bf16(mh, xb, y);
+      y = mfma_bf16(ml, xb, y);
+      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * ypb + li][16 * ytb + 4 * lk]);
+      y[0] += Dh * bf_lo(xv.x);
+      y[1] += Dh * bf_hi(xv.x);
+      y[2] += Dh * bf_lo(xv.y);
+      y[3] += Dh * bf_hi(xv.y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.Y[cur][16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
+    }
+#pragma unroll
+    for (int k = 0; k < PBW; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
+        split_bf16(st[k][r], sm.S[0][pp][nn], sm.S[1][pp][nn]);
+      }
+    if (c + 1 < nchunks) {
+      stg.commit(sm, nxt, tid);
+      if (wave == 0) chunk_decay(sm, nxt, Ah, lane);
+    }
+    __syncthreads();
+  }
+  store_y_bf16(p, sm.Y[(nchunks - 1) & 1], tid, b, h, (nchunks - 1) * kQ);
+
+  if (p.h_last) {
+#pragma unroll
+    for (int k = 0; k < PBW; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
+        p.h_last[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
+      }
+  }
+}
+
 int ssd_validate(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const void* y, const float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t P,
                  int64_t G, int64_t N, int dtype) {
@@ -362,10 +672,17 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   a.H = H;
   a.G = G;
   const dim3 grid(static_cast<unsigned>(Bs * H)), block(64 * kWaves);
-  if (N == 128)
-    hipLaunchKernelGGL((ssd_fwd_kernel<T, 128>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((ssd_fwd_kernel<T, 64>), grid, block, 0, stream, a);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (N == 128)
+      hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64>), grid, block, 0, stream, a);
+  } else {
+    if (N == 128)
+      hipLaunchKernelGGL((ssd_fwd_kernel<T, 128>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((ssd_fwd_kernel<T, 64>), grid, block, 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 

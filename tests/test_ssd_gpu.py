@@ -25,33 +25,44 @@ def test_small():
     check(2, 64, 4, 1, 64)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 100, 400])
-def test_sequence_lengths(L):
-    check(2, L, 2, 1, 128, seed=L)
+def test_sequence_lengths(L, dtype):
+    check(2, L, 2, 1, 128, dtype=dtype, seed=L)
 
 
-def test_state_128_and_groups():
-    check(2, 150, 8, 2, 128, seed=3)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_128_and_groups(dtype):
+    check(2, 150, 8, 2, 128, dtype=dtype, seed=3)
 
 
-def test_groups_64():
-    check(3, 70, 6, 3, 64, seed=4)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_groups_64(dtype):
+    check(3, 70, 6, 3, 64, dtype=dtype, seed=4)
 
 
 def test_bf16():
     check(2, 200, 4, 1, 128, dtype="bf16", seed=5)
 
 
-def test_initial_state():
-    check(2, 90, 4, 2, 128, seed=6, h0=True)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_initial_state(dtype):
+    check(2, 90, 4, 2, 128, dtype=dtype, seed=6, h0=True)
 
 
-def test_no_D():
-    check(1, 50, 2, 1, 64, seed=7, D_none=True)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_D(dtype):
+    check(1, 50, 2, 1, 64, dtype=dtype, seed=7, D_none=True)
 
 
-def test_repeatable_bits():
-    inp = synth.make_ssd_inputs(2, 77, 4, 64, 1, 128, seed=8)
+def test_bf16_long_state_accuracy():
+    # 128 chunks: the bf16 operand splitting keeps the carried state at float32 accuracy
+    check(1, 4096, 2, 1, 128, dtype="bf16", seed=9, h0=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_repeatable_bits(dtype):
+    inp = synth.make_ssd_inputs(2, 77, 4, 64, 1, 128, dtype, seed=8)
     a, ha = run_gpu_ssd(inp, want_h=True)
     b, hb = run_gpu_ssd(inp, want_h=True)
     assert np.array_equal(a, b) and np.array_equal(ha, hb)
