@@ -334,13 +334,17 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 // steps read s-contiguous ones (M[t][s], x transposed to Xt[p][s]).
 //
 // Per chunk, two barriers:
-//   phase 1  store y of the previous chunk; C B^T on the three causal 16 x 16
-//            blocks (waves 0..2) -> masked, decayed M (bf16 pair); every wave: its
-//            16 x 16 block of diag(e^{cs}) C S_in^T and the state update of
-//            its state blocks, S = e^{cs_end} S + X^T (w B)
+//   phase 1  store y of the previous chunk; the three causal 16 x 16 blocks
+//            of C B^T (waves 0..2, computed as B C^T so that a lane holds 4
+//            consecutive s of one t) -> masked, decayed M (bf16 pair); every
+//            wave: its 16 x 16 block of diag(e^{cs}) C S_in^T and the update
+//            of its state blocks, S^T = e^{cs_end} S^T + (w B)^T X (so that a
+//            lane holds 4 consecutive n of one p)
 //   phase 2  M X added to the output block, + D x -> Y (float32, by chunk
-//            parity); bf16 pair copy of the new state; the next chunk's tiles
-//            (prefetched into registers during phase 1) and its decays
+//            parity); bf16 pair copy of the new state (8-byte stores); the
+//            next chunk's tiles (prefetched into registers during phase 1);
+//            its decays by the last wave, a prefix sum over the lanes (DPP)
+//            of the step sizes that wave loaded
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -411,10 +415,14 @@ struct SsdStagerBf {
       rb[k] = *reinterpret_cast<const uint2*>(p.B + off);
       rc[k] = *reinterpret_cast<const uint2*>(p.C + off);
     }
+    // step sizes: lanes 0 .. kQ-1 of the last wave
     const int64_t td = t0 + (tid & (kQ - 1));
-    vdt = tid < kQ && td < p.L;
+    vdt = (tid >> 6) == kWaves - 1 && (tid & 63) < kQ && td < p.L;
     rdt = p.dt[(b * p.L + (td < p.L ? td : p.L - 1)) * p.H + h];
   }
+
+  // step size of this lane's row (zero past L or outside the dt task)
+  __device__ __forceinline__ float dt_value() const { return vdt ? to_f32(rdt) : 0.f; }
 
   // rows at or past L are zero (dt = 0: a = 1 and no input)
   __device__ __forceinline__ void commit(SsdSmemBf<N>& sm, int buf, int tid) const {
@@ -433,26 +441,36 @@ struct SsdStagerBf {
       *reinterpret_cast<uint2*>(&sm.B[buf][row][c4]) = vb[k] ? rb[k] : make_uint2(0u, 0u);
       *reinterpret_cast<uint2*>(&sm.C[buf][row][c4]) = vb[k] ? rc[k] : make_uint2(0u, 0u);
     }
-    if (tid < kQ) sm.dt[buf][tid] = vdt ? to_f32(rdt) : 0.f;
+    if ((tid >> 6) == kWaves - 1 && (tid & 63) < kQ) sm.dt[buf][tid & 63] = dt_value();
   }
 };
 
-// cs, e^{cs}, w and cs_end of the chunk in buffer buf (one wave, from the dt
-// that this same wave committed)
+// v summed over lanes 0 .. lane of each half wave (lanes 0..31 and 32..63):
+// row shifts within the 16-lane rows, then row 1 (3) adds lane 15 (47)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_shifted(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float lane_prefix_sum32(float v) {
+  v += dpp_shifted<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_shifted<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_shifted<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_shifted<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_shifted<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  return v;
+}
+
+// cs, e^{cs}, w and cs_end of the chunk in buffer buf, by the wave whose lanes
+// 0 .. kQ-1 hold the chunk's step sizes (zero past L)
 template <int N>
-__device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah, int lane) {
+__device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah, int lane, float dtv) {
+  const float incl = lane_prefix_sum32(dtv);
+  const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), kQ - 1));
   if (lane < kQ) {
-    float s = 0.f, tot = 0.f;
-#pragma unroll
-    for (int r = 0; r < kQ; ++r) {
-      const float v = sm.dt[buf][r];
-      tot += v;
-      s += r <= lane ? v : 0.f;
-    }
-    const float cst = Ah * s, cse = Ah * tot;
+    const float cst = Ah * incl, cse = Ah * tot;
     sm.cs[buf][lane] = cst;
     sm.ecs[buf][lane] = __expf(cst);
-    sm.w[buf][lane] = __expf(cse - cst) * sm.dt[buf][lane];
+    sm.w[buf][lane] = __expf(cse - cst) * dtv;
     if (lane == 0) sm.cs_end[buf] = cse;
   }
 }
@@ -466,6 +484,16 @@ __device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const f
     *reinterpret_cast<uint2*>(p.y + ((b * p.L + t0 + t) * p.H + h) * kP + c4) =
         make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
   }
+}
+
+// S[p][n0 .. n0+3] (high and low bf16 parts) from 4 float32 values
+template <int N>
+__device__ __forceinline__ void store_state_bf16(SsdSmemBf<N>& sm, int pp, int n0, f4 v) {
+  uint32_t h01, l01, h23, l23;
+  split_pack_bf16(v[0], v[1], h01, l01);
+  split_pack_bf16(v[2], v[3], h23, l23);
+  *reinterpret_cast<uint2*>(&sm.S[0][pp][n0]) = make_uint2(h01, h23);
+  *reinterpret_cast<uint2*>(&sm.S[1][pp][n0]) = make_uint2(l01, l23);
 }
 
 template <int N>
@@ -492,22 +520,22 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
   const int mtb = wave == 0 ? 0 : 1, msb = wave == 2 ? 1 : 0;  // causal C B^T block of waves 0..2
 
+  // st[k][r] = S[p][n], p = 16 (spb + k) + li, n = 16 snb + 4 lk + r
   f4 st[PBW];
 #pragma unroll
-  for (int k = 0; k < PBW; ++k)
+  for (int k = 0; k < PBW; ++k) {
+    const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-      st[k][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
-      split_bf16(st[k][r], sm.S[0][pp][nn], sm.S[1][pp][nn]);
-    }
+    for (int r = 0; r < 4; ++r) st[k][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + n0 + r] : 0.f;
+    store_state_bf16(sm, pp, n0, st[k]);
+  }
   // the block t < 16, s >= 16 of M stays zero (future steps)
   for (int i = tid; i < 2 * kQ * SsdSmemBf<N>::TP; i += 64 * kWaves) (&sm.M[0][0][0])[i] = 0;
 
   SsdStagerBf<N> stg;
   stg.load(p, tid, b, h, g, 0);
   stg.commit(sm, 0, tid);
-  if (wave == 0) chunk_decay(sm, 0, Ah, lane);
+  if (wave == kWaves - 1) chunk_decay(sm, 0, Ah, lane, stg.dt_value());
   __syncthreads();
 
   for (int64_t c = 0; c < nchunks; ++c) {
@@ -519,23 +547,30 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
     if (c > 0) store_y_bf16(p, sm.Y[nxt], tid, b, h, t0 - kQ);
 
     if (wave < 3) {
-      // causal block of C B^T, masked and decayed: M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t
-      uint4 ca[KN], cb[KN];
+      // causal block of C B^T, masked and decayed: M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t,
+      // as the block of B C^T: register r of the lane is s = 16 msb + 4 lk + r, t = 16 mtb + li
+      uint4 bb[KN], cc[KN];
 #pragma unroll
       for (int j = 0; j < KN; ++j) {
-        ca[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * mtb + li][32 * j + 8 * lk]);
-        cb[j] = *reinterpret_cast<const uint4*>(&sm.B[cur][16 * msb + li][32 * j + 8 * lk]);
+        bb[j] = *reinterpret_cast<const uint4*>(&sm.B[cur][16 * msb + li][32 * j + 8 * lk]);
+        cc[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * mtb + li][32 * j + 8 * lk]);
       }
       f4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < KN; ++j) a = mfma_bf16(ca[j], cb[j], a);
-      const int s = 16 * msb + li;
-      const float css = sm.cs[cur][s], dts = sm.dt[cur][s];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mtb + 4 * lk + r;
-        split_bf16(s <= t ? a[r] * __expf(sm.cs[cur][t] - css) * dts : 0.f, sm.M[0][t][s], sm.M[1][t][s]);
-      }
+      for (int j = 0; j < KN; ++j) a = mfma_bf16(bb[j], cc[j], a);
+      const int t = 16 * mtb + li, s0 = 16 * msb + 4 * lk;
+      const float cst = sm.cs[cur][t];
+      const float4 css = *reinterpret_cast<const float4*>(&sm.cs[cur][s0]);
+      const float4 dts = *reinterpret_cast<const float4*>(&sm.dt[cur][s0]);
+      const float m0 = s0 + 0 <= t ? a[0] * __expf(cst - css.x) * dts.x : 0.f;
+      const float m1 = s0 + 1 <= t ? a[1] * __expf(cst - css.y) * dts.y : 0.f;
+      const float m2 = s0 + 2 <= t ? a[2] * __expf(cst - css.z) * dts.z : 0.f;
+      const float m3 = s0 + 3 <= t ? a[3] * __expf(cst - css.w) * dts.w : 0.f;
+      uint32_t h01, l01, h23, l23;
+      split_pack_bf16(m0, m1, h01, l01);
+      split_pack_bf16(m2, m3, h23, l23);
+      *reinterpret_cast<uint2*>(&sm.M[0][t][s0]) = make_uint2(h01, h23);
+      *reinterpret_cast<uint2*>(&sm.M[1][t][s0]) = make_uint2(l01, l23);
     }
 
     // inter-chunk output of the wave's block: diag(e^{cs}) C S_in^T
@@ -558,12 +593,12 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
       for (int r = 0; r < 4; ++r) y[r] = (a[r] + a2[r]) * sm.ecs[cur][16 * ytb + 4 * lk + r];
     }
 
-    // state update of the wave's blocks: S = e^{cs_end} S + X^T (w B)
+    // state update of the wave's blocks: S^T = e^{cs_end} S^T + (w B)^T X
     {
       const float dec = __expf(sm.cs_end[cur]);
 #pragma unroll
       for (int k = 0; k < PBW; ++k) st[k] *= dec;
-      // operand B: w_s B[s][n] for s = 8 lk .. 8 lk + 7, n = 16 snb + li
+      // operand A: (w B)^T[n][s] = w_s B[s][n] for n = 16 snb + li, s = 8 lk .. 8 lk + 7
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -576,8 +611,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
 #pragma unroll
       for (int k = 0; k < PBW; ++k) {
         const uint4 xa = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * (spb + k) + li][8 * lk]);
-        st[k] = mfma_bf16(xa, boh, st[k]);
-        st[k] = mfma_bf16(xa, bol, st[k]);
+        st[k] = mfma_bf16(boh, xa, st[k]);
+        st[k] = mfma_bf16(bol, xa, st[k]);
       }
     }
     __syncthreads();  // M complete; every read of S_in done
@@ -599,15 +634,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
       for (int r = 0; r < 4; ++r) sm.Y[cur][16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
     }
 #pragma unroll
-    for (int k = 0; k < PBW; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-        split_bf16(st[k][r], sm.S[0][pp][nn], sm.S[1][pp][nn]);
-      }
+    for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
     if (c + 1 < nchunks) {
       stg.commit(sm, nxt, tid);
-      if (wave == 0) chunk_decay(sm, nxt, Ah, lane);
+      if (wave == kWaves - 1) chunk_decay(sm, nxt, Ah, lane, stg.dt_value());
     }
     __syncthreads();
   }
@@ -616,11 +646,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   if (p.h_last) {
 #pragma unroll
     for (int k = 0; k < PBW; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-        p.h_last[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
-      }
+      *reinterpret_cast<float4*>(p.h_last + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+          make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
   }
 }
 
