@@ -374,9 +374,15 @@ __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 
 
 template <int N>
 struct alignas(16) SsdSmemBf {
-  static constexpr int NP = N + 8;   // row pitch (elements) of the n-contiguous tiles
-  static constexpr int TP = kQ + 8;  // row pitch of the s-contiguous tiles
-  uint16_t C[2][kQ][NP];   // C chunk [t][n]
+  // Row pitches (elements). With lanes on rows and 16-byte column blocks, a
+  // 16-byte read is free of bank conflicts when the pitch in bytes is 32 mod
+  // 64, an 8-byte access when it is 16 mod 64 (measured on gfx950): C is
+  // only read 16 bytes at a time; B, the state copy and x also take 8-byte
+  // stores or reads.
+  static constexpr int NPC = N + 16;  // C
+  static constexpr int NP = N + 8;    // B and the state copy
+  static constexpr int TP = kQ + 8;   // the s-contiguous tiles
+  uint16_t C[2][kQ][NPC];  // C chunk [t][n]
   uint16_t B[2][kQ][NP];   // B chunk [s][n]
   uint16_t Xt[2][kP][TP];  // x chunk, transposed [p][s]
   uint16_t S[2][kP][NP];   // state entering the chunk [p][n]: high, low bf16 part
@@ -401,7 +407,9 @@ struct SsdStagerBf {
                                        int64_t t0) {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
-      const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
+      // rows along the lanes, so that the transposed stores of the commit
+      // fall on distinct banks
+      const int u = tid + k * 64 * kWaves, row = u % kQ, c4 = (u / kQ) * 4;
       const int64_t t = t0 + row;
       vx[k] = t < p.L;
       rx[k] = *reinterpret_cast<const uint2*>(p.x + ((b * p.L + (vx[k] ? t : p.L - 1)) * p.H + h) * kP + c4);
@@ -428,7 +436,7 @@ struct SsdStagerBf {
   __device__ __forceinline__ void commit(SsdSmemBf<N>& sm, int buf, int tid) const {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
-      const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
+      const int u = tid + k * 64 * kWaves, row = u % kQ, c4 = (u / kQ) * 4;
       const uint2 v = vx[k] ? rx[k] : make_uint2(0u, 0u);
       sm.Xt[buf][c4 + 0][row] = static_cast<uint16_t>(v.x);
       sm.Xt[buf][c4 + 1][row] = static_cast<uint16_t>(v.x >> 16);
@@ -598,11 +606,15 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
       const float dec = __expf(sm.cs_end[cur]);
 #pragma unroll
       for (int k = 0; k < PBW; ++k) st[k] *= dec;
-      // operand A: (w B)^T[n][s] = w_s B[s][n] for n = 16 snb + li, s = 8 lk .. 8 lk + 7
+      // operand A: (w B)^T[n][s] = w_s B[s][n] for n = 16 snb + li. The sum
+      // over s does not depend on which k slot holds which s as long as both
+      // operands agree: the lane's 8 slots hold s = 4 lk .. 4 lk + 3 and
+      // 16 + 4 lk .. 16 + 4 lk + 3, so that the lanes' column reads of B fall
+      // on rows 4 apart (distinct LDS banks).
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s0 = 8 * lk + 2 * i;
+        const int s0 = (i < 2 ? 0 : 16) + 4 * lk + 2 * (i & 1);
         const float b0 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0][16 * snb + li]) << 16);
         const float b1 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0 + 1][16 * snb + li]) << 16);
         split_pack_bf16(b0 * sm.w[cur][s0], b1 * sm.w[cur][s0 + 1], bh[i], bl[i]);
@@ -610,7 +622,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
       const uint4 boh = make_uint4(bh[0], bh[1], bh[2], bh[3]), bol = make_uint4(bl[0], bl[1], bl[2], bl[3]);
 #pragma unroll
       for (int k = 0; k < PBW; ++k) {
-        const uint4 xa = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * (spb + k) + li][8 * lk]);
+        // operand B: X[s][p] = Xt[p][s], p = 16 (spb + k) + li, the same s slots
+        const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][4 * lk]);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][16 + 4 * lk]);
+        const uint4 xa = make_uint4(x0.x, x0.y, x1.x, x1.y);
         st[k] = mfma_bf16(boh, xa, st[k]);
         st[k] = mfma_bf16(bol, xa, st[k]);
       }
