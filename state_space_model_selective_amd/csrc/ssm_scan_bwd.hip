@@ -27,8 +27,10 @@
 //     every step in registers), then the adjoint runs backward in time the
 //     same way (local pass from a zero carry, fold over the later segments
 //     and the next round's carry, replay) and every gradient term of the step
-//     is formed in the replay. Sums over the lane's 4 states and over the 4
-//     state quads of a channel go through DPP; sums over the 16 channels of
+//     is formed in the replay (dx and ddelta go to the round's LDS tile
+//     and out one round later, 4 channels per store). Sums over the lane's
+//     4 states and over the 4 state quads of a channel go through DPP; sums
+//     over the 16 channels of
 //     dB and dC go through DPP (over the quad) and LDS (over the 4 lane rows)
 //     into per-workgroup partials that a second kernel adds up in a fixed
 //     order (no atomics: the result is deterministic).
@@ -184,6 +186,29 @@ struct BwdStager {
     ra = a, rb = bb, rc = cc;
   }
 
+  // dx and ddelta of round rr (written into the x and dy slots of its tile by
+  // the adjoint replay) -> global
+  __device__ __forceinline__ void store_grads(const BwdArgs<T>& p, const BwdTile<RT>& tl, int64_t rr) const {
+    const int64_t t = rr * RT + row;
+    if (!is_xd || t >= L || !chunk_ok) return;
+    const int c4 = 4 * chk;
+    const float4 gx = *reinterpret_cast<const float4*>(&tl.xv[row][c4]);
+    const float4 gd = *reinterpret_cast<const float4*>(&tl.dy[row][c4]);
+    const int64_t ce = e0 + c4, off = (b * L + t) * ED + ce;
+    if (VEC) {
+      Vec4<T>::store(p.dx + off, gx);
+      Vec4<T>::store(p.ddl + off, gd);
+    } else {
+      const float vx[4] = {gx.x, gx.y, gx.z, gx.w}, vd[4] = {gd.x, gd.y, gd.z, gd.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (ce + k < ED) {
+          p.dx[off + k] = from_f32<T>(vx[k]);
+          p.ddl[off + k] = from_f32<T>(vd[k]);
+        }
+    }
+  }
+
   // registers -> LDS tile (padded rows and channels are zero: delta = 0
   // gives a = 1 and b = 0, dy = 0 gives no adjoint input)
   template <bool WITH_ADJ>
@@ -319,7 +344,10 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     BwdTile<RT>& cur = tile[r & 1];
     BwdTile<RT>& nxt = tile[(r + 1) & 1];  // round r-1 has the other parity
     if (r >= 1) st.template prefetch<true>(p, r - 1);
-    if (r + 1 < R) store_colsums(p, cs, tid, b, grp, r + 1);
+    if (r + 1 < R) {
+      store_colsums(p, cs, tid, b, grp, r + 1);
+      st.store_grads(p, nxt, r + 1);  // dx, ddelta of round r+1 (tile of the same parity)
+    }
 
     // forward local pass from a zero state
     float av[TS][4], hv[TS][4];  // a_t; b_t, then h_{t-1}
@@ -398,10 +426,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 
     // adjoint replay and the gradient terms of every step
-    const int64_t tseg = r * RT + wave * TS;  // time of the segment's first step (uniform)
-    T* const dxp = p.dx + (b * L + tseg) * ED + e;
-    T* const ddp = p.ddl + (b * L + tseg) * ED + e;
-    const bool writer = g == 0 && ch_ok;      // one lane per channel stores dx, ddelta
+    const bool writer = g == 0;  // one lane per channel writes dx, ddelta to the tile
     float dAr[4] = {0.f, 0.f, 0.f, 0.f}, dDr = 0.f;
     float hnext[4] = {hin[0], hin[1], hin[2], hin[3]};  // h_t of the step being processed
 #pragma unroll
@@ -426,9 +451,12 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
       dDr = __builtin_fmaf(dyv, xv, dDr);
       float s1r = s1;
       bank_sum2(s1r, s2);
-      if (writer && tseg + i < L) {
-        dxp[i * ED] = from_f32<T>(__builtin_fmaf(dt, s1r, Dv * dyv));
-        ddp[i * ED] = from_f32<T>(__builtin_fmaf(xv, s1r, s2));
+      if (writer) {
+        // dx and ddelta of the step replace x and dy in the round's tile (this
+        // step has read them; no later step reads this row); the staging
+        // threads store them one round later, 4 channels per 16-byte store
+        cur.xv[row][ch] = __builtin_fmaf(dt, s1r, Dv * dyv);
+        cur.dy[row][ch] = __builtin_fmaf(xv, s1r, s2);
       }
       quad_sum8(pv);
       if (c == 0) {
@@ -448,6 +476,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     __syncthreads();
   }
   store_colsums(p, cs, tid, b, grp, 0);
+  st.store_grads(p, tile[0], 0);
 
   // ---- per-workgroup results ----------------------------------------------
   if (p.dh0 && wave == 0 && ch_ok)
