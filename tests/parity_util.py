@@ -24,6 +24,8 @@ def to_device(inp, dev):
     import torch
     out = {}
     for k, v in inp.items():
+        if not v.flags.writeable:
+            v = v.copy()  # torch wants writable host memory
         if v.dtype == np.uint16:
             out[k] = torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
         else:
@@ -144,3 +146,30 @@ def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None):
                     stream=stream)
     torch.cuda.synchronize()
     return y_to_numpy(y), (None if h is None else h.double().cpu().numpy())
+
+
+def degenerate_inputs(case, Bs=2, L=200, ED=64, seed=13):
+    """The scan's special cases: no decay (A = 0: a prefix sum), full decay
+    (a underflows to 0: the state restarts every step), steps of zero (a = 1,
+    no input), growth (A > 0), no input (x = 0), and all of them mixed."""
+    inp = synth.make_inputs(Bs, L, ED, 16, "f32", seed=seed)
+    A = inp["A"].copy()
+    if case == "no_decay":
+        A[:] = 0.0
+    elif case == "full_decay":
+        A[:] = -1.0e4
+    elif case == "growth":
+        A[:] = 0.5
+    elif case == "zero_steps":
+        inp["delta"] = inp["delta"].copy()
+        inp["delta"][:, ::2, :] = 0.0
+    elif case == "zero_input":
+        inp["x"] = np.zeros_like(inp["x"])
+    elif case == "mixed":
+        A[:, 0:4] = 0.0
+        A[:, 4:8] = -1.0e4
+        A[:, 8:10] = 0.25
+        inp["delta"] = inp["delta"].copy()
+        inp["delta"][:, 5::7, :] = 0.0
+    inp["A"] = A
+    return inp

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from parity_util import assert_grads_close, log, run_gpu_bwd
+from parity_util import assert_grads_close, degenerate_inputs, log, run_gpu_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,16 @@ def test_channel_counts(ED):
 
 def test_bf16():
     check(2, 300, 96, dtype="bf16", seed=5)
+
+
+@pytest.mark.parametrize("case", ["no_decay", "full_decay", "growth", "zero_steps", "zero_input", "mixed"])
+def test_degenerate_inputs(case):
+    log("bwd degenerate case %s" % case)
+    inp = degenerate_inputs(case, L=150, ED=48)
+    dy = synth.make_output_grad(2, 150, 48, "f32", seed=14)
+    got = run_gpu_bwd(inp, dy, want_dD=True, want_dh0=True)
+    ref = oracle.scan_bwd(**inp, dy=dy)
+    assert_grads_close(got, ref, "f32")
 
 
 def test_initial_state():

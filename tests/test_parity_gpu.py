@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from parity_util import TOL, assert_close, gather_channels, log, run_gpu, sample_channels
+from parity_util import TOL, assert_close, degenerate_inputs, gather_channels, log, run_gpu, sample_channels
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,33 @@ def test_sequence_lengths_bidirectional(L):
 @pytest.mark.parametrize("ED", [16, 48, 64, 80, 192, 1040])
 def test_channel_counts(ED):
     check_full(3, 200, ED, seed=ED)
+
+
+@pytest.mark.parametrize("ED,dtype,bidir", [(1, "f32", False), (3, "f32", False), (37, "f32", False),
+                                             (150, "f32", False), (37, "bf16", False), (150, "bf16", False),
+                                             (37, "f32", True), (150, "bf16", True)])
+def test_channel_counts_not_multiple_of_4(ED, dtype, bidir):
+    # element-by-element loads and stores of the channel chunks (no 16-byte vectors)
+    check_full(2, 133, ED, dtype=dtype, bidir=bidir, seed=ED + 1)
+
+
+def test_split_sequence_channels_not_multiple_of_4():
+    check_full(1, 3000, 37, seed=11)
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("case", ["no_decay", "full_decay", "growth", "zero_steps", "zero_input", "mixed"])
+def test_degenerate_inputs(case, bidir):
+    log("degenerate case %s bidir=%s" % (case, bidir))
+    inp = degenerate_inputs(case)
+    y, h, g = run_gpu(inp, bidir=bidir, want_h=True, want_g=bidir)
+    y_ref, h_ref, g_ref = oracle.scan(**inp, bidir=bidir, want_h_last=True, want_g_first=bidir)
+    assert_close("y", y, y_ref, TOL["f32"])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+    if bidir:
+        assert_close("g_first", g, g_ref, TOL["f32"])
+    if case == "zero_input":
+        assert np.all(y == 0.0) and np.all(h == 0.0)
 
 
 def test_single_batch_row_long():
