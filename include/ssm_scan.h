@@ -188,9 +188,13 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
  *   D      : (H) float32, or NULL        h0 : (Bs, H, P, N) float32, or NULL
  *   y      : (Bs, L, H, P) of dtype, written in full
  *   h_last : (Bs, H, P, N) float32, or NULL -- S after the last step
- * Supported: P = 64, N = 64 or 128, H a multiple of G. Arithmetic is
- * float32 throughout (bfloat16 inputs are widened; y is rounded to nearest
- * even). No workspace. Conventions, alignment and error codes as
+ * Supported: P = 64, N = 64 or 128, H a multiple of G. The state and every
+ * accumulation are float32. With float32 inputs the chunk products take
+ * float32 operands; with bfloat16 inputs they run on the bf16 matrix
+ * instructions, with x, B and C as given and each float32 operand (the
+ * decayed C B^T, the state, the decay-weighted B) split into a high and a
+ * low bf16 part, so every product is within 2^-17 of its float32 value; y is
+ * rounded to nearest even. No workspace. Conventions, alignment and error codes as
  * ssm_scan_fwd (SSM_ERR_DIM also when H is not a multiple of G).
  */
 int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
