@@ -155,11 +155,13 @@ def ssd_flops(w):
     """Products of the chunked multi-head scan per launch: per (batch row,
     head) and chunk of Q steps, the causal C B^T (Q (Q+1)/2 N multiply-adds),
     its product with x (Q (Q+1)/2 P), C S^T (Q N P) and the state update
-    (Q N P); 2 flops per multiply-add."""
+    (Q N P); 2 flops per multiply-add; twice that for the bidirectional scan
+    (one sweep per direction)."""
     Q, P, N = SSD_CHUNK, w["P"], w["N"]
     chunks = (w["L"] + Q - 1) // Q
     per_chunk = 2 * (Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P)
-    return w["Bs"] * w["H"] * chunks * per_chunk
+    sweeps = 2 if w.get("bidir") else 1
+    return sweeps * w["Bs"] * w["H"] * chunks * per_chunk
 
 
 def bench_ssd(args, name):
@@ -176,6 +178,7 @@ def bench_ssd(args, name):
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    bidir = bool(w.get("bidir"))
     nsets = 3
     sets, host0 = [], None
     for i in range(nsets):
@@ -186,9 +189,18 @@ def bench_ssd(args, name):
         t["y"] = torch.empty_like(t["x"])
         sets.append(t)
     stream = torch.cuda.current_stream(dev)
+    ws = None
+    if bidir:
+        dcode = ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16
+        need = ssm.ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dcode)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
 
     def step(t):
-        ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], stream=stream)
+        if bidir:
+            ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], workspace=ws,
+                                  stream=stream)
+        else:
+            ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], stream=stream)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -216,11 +228,11 @@ def bench_ssd(args, name):
         def rows(k):
             return {n: (v[:k] if v.ndim >= 3 else v) for n, v in host0.items()}
         t1 = time.perf_counter()
-        oracle.ssd(**rows(1), nthreads=threads)
+        oracle.ssd(**rows(1), bidir=bidir, nthreads=threads)
         dt1 = max(time.perf_counter() - t1, 1e-6)
         k = int(min(Bs, max(1, 20.0 / dt1)))
         t1 = time.perf_counter()
-        y_ref, _, _ = oracle.ssd(**rows(k), nthreads=threads)
+        y_ref, _, _ = oracle.ssd(**rows(k), bidir=bidir, nthreads=threads)
         dtk = time.perf_counter() - t1
         cpu = dict(value=k * L * H * P * N / dtk, unit="scan elements/s", cores=threads, kind="oracle",
                    sample=(("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))) +
@@ -241,7 +253,8 @@ def bench_ssd(args, name):
             "instruction": "v_mfma_f32_16x16x32_bf16" if bf16 else "v_mfma_f32_16x16x4f32"}
     hbm = {"alg_bytes_per_launch": alg_bytes, "achieved_GBps": alg_bytes / avg / 1e9, "peak_GBps": HBM_PEAK_GBPS,
            "frac": alg_bytes / avg / 1e9 / HBM_PEAK_GBPS}
-    timed = ("the multi-head scan kernel (one launch per step); products on the " +
+    timed = (("the bidirectional multi-head scan kernel (one launch per step, both sweeps)" if bidir
+              else "the multi-head scan kernel (one launch per step)") + "; products on the " +
              ("bf16 matrix instructions (float32 operands split into two bf16 parts)" if bf16
               else "float32 matrix instructions"))
     if flops / (peak_mfma * 1e12) >= alg_bytes / (HBM_PEAK_GBPS * 1e9):
@@ -267,7 +280,7 @@ def bench_ssd(args, name):
         "dtype": w["dtype"],
         "data": "synthetic (seeded counter-based generator; x,B,C,D ~ N(0,1), dt log-uniform [1e-3,1e-1], "
                 "A[h] = -U(1,16)); 3 input sets rotated",
-        "config": {"workload": name, "Bs": Bs, "L": L, "H": H, "P": P, "G": G, "N": N,
+        "config": {"workload": name, "Bs": Bs, "L": L, "H": H, "P": P, "G": G, "N": N, "bidir": bidir,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "mfma": mfma,

@@ -201,6 +201,32 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
                 const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G,
                 int64_t N, int dtype, void* stream);
 
+/*
+ * Bidirectional multi-head scan (Bi-Mamba2 on the multi-head form): the
+ * forward scan of ssm_ssd_fwd (with D x and h0) plus the same scan run in
+ * decreasing time from a zero state over the same inputs, read in place (no
+ * flipped copy), the two outputs added -- the bidirectional combination of
+ * "Some questions of Bi-Mamba2 and Hydra" (the author's first reply: two SSMs
+ * with shared weights, the reverse one on the flipped sequence, plus D x):
+ *
+ *   g_t[p][n] = a_t g_{t+1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],   g_L = 0
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] (S_t[p][n] + g_t[p][n]) + D[h] x[b,t,h,p]
+ *
+ * Arguments as ssm_ssd_fwd, and
+ *   g_first   : (Bs, H, P, N) float32, or NULL -- g after t = 0
+ *   workspace : device memory of ssm_ssd_bidir_workspace_bytes(...) bytes for
+ *               bfloat16 (the reverse direction's float32 partial of y; it
+ *               may not overlap an argument); not used for float32 (the
+ *               partial goes through y). Owned by the caller.
+ * SSM_ERR_WORKSPACE if a bfloat16 call has no or too small a workspace.
+ * Otherwise conventions, numerics and error codes as ssm_ssd_fwd.
+ */
+size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype);
+int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                      const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs,
+                      int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

@@ -78,6 +78,10 @@ def lib():
         L.ssm_scan_bwd.restype = ci
         L.ssm_ssd_fwd.argtypes = [vp] * 9 + [i64] * 6 + [ci, vp]
         L.ssm_ssd_fwd.restype = ci
+        L.ssm_ssd_bidir_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+        L.ssm_ssd_bidir_workspace_bytes.restype = sz
+        L.ssm_ssd_bidir_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp, sz, vp]
+        L.ssm_ssd_bidir_fwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -227,4 +231,35 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=Non
                            Bs, L, H, P, G, N, dtc, _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")
+    return y
+
+
+def ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtype=SSM_F32):
+    """Workspace bytes of ssm_ssd_bidir_fwd (SSM_F32: none, SSM_BF16: the
+    reverse sweep's float32 partial output)."""
+    return lib().ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtype)
+
+
+def ssm_ssd_bidir_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, g_first=None, h0=None, workspace=None,
+                      stream=None):
+    """Bidirectional multi-head scan: ssm_ssd_fwd plus the same scan in
+    decreasing time from a zero state (no D). Returns y; the final states go
+    to h_last (forward) and g_first (reverse) if given."""
+    import torch
+    if not x.is_cuda:
+        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
+    dtc = _dtype_code(x)
+    Bs, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    need = lib().ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtc)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().ssm_ssd_bidir_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+                                 _ptr(h_last), _ptr(g_first), Bs, L, H, P, G, N, dtc, _ptr(workspace), wsb,
+                                 _stream(x, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_ssd_bidir_fwd")
     return y

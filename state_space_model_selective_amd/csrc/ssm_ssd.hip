@@ -54,8 +54,16 @@ struct SsdArgs {
   const float* h0;
   T* y;
   float* h_last;
+  // bidirectional scan: float32 partial of the reverse direction, (Bs, L, H,
+  // P) (may alias y for float32), and the reverse direction's final state
+  float* part;
+  float* g_first;
   int64_t L, H, G;
 };
+
+// Time of step tau of a sweep: the forward sweep runs t = tau, the reverse
+// sweep of the bidirectional scan t = L - 1 - tau (inputs read in place).
+__device__ __forceinline__ int64_t sweep_time(int64_t tau, int64_t L, bool rev) { return rev ? L - 1 - tau : tau; }
 
 template <int N>
 struct alignas(16) SsdSmem {
@@ -91,26 +99,29 @@ struct SsdStager {
   T rdt;
   bool vx[kXT], vb[kBT], vdt;
 
-  __device__ __forceinline__ void load(const SsdArgs<T>& p, int tid, int64_t b, int64_t h, int64_t g, int64_t t0) {
+  // rows tau0 .. tau0 + kQ - 1 of the sweep (rev: time L - 1 - tau)
+  __device__ __forceinline__ void load(const SsdArgs<T>& p, int tid, int64_t b, int64_t h, int64_t g, int64_t tau0,
+                                       bool rev) {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (kP / 4), c4 = (u % (kP / 4)) * 4;
-      const int64_t t = t0 + row;
-      vx[k] = t < p.L;
-      rx[k] = V::load_raw(p.x + ((b * p.L + (vx[k] ? t : p.L - 1)) * p.H + h) * kP + c4);
+      const int64_t tau = tau0 + row;
+      vx[k] = tau < p.L;
+      const int64_t t = sweep_time(vx[k] ? tau : p.L - 1, p.L, rev);
+      rx[k] = V::load_raw(p.x + ((b * p.L + t) * p.H + h) * kP + c4);
     }
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
-      const int64_t t = t0 + row;
-      vb[k] = t < p.L;
-      const int64_t off = ((b * p.L + (vb[k] ? t : p.L - 1)) * p.G + g) * N + c4;
+      const int64_t tau = tau0 + row;
+      vb[k] = tau < p.L;
+      const int64_t off = ((b * p.L + sweep_time(vb[k] ? tau : p.L - 1, p.L, rev)) * p.G + g) * N + c4;
       rb[k] = V::load_raw(p.B + off);
       rc[k] = V::load_raw(p.C + off);
     }
-    const int64_t td = t0 + (tid & (kQ - 1));
+    const int64_t td = tau0 + (tid & (kQ - 1));
     vdt = tid < kQ && td < p.L;
-    rdt = p.dt[(b * p.L + (td < p.L ? td : p.L - 1)) * p.H + h];
+    rdt = p.dt[(b * p.L + sweep_time(td < p.L ? td : p.L - 1, p.L, rev)) * p.H + h];
   }
 
   __device__ __forceinline__ void commit(SsdSmem<N>& sm, int buf, int tid) const {
@@ -130,7 +141,7 @@ struct SsdStager {
   }
 };
 
-template <typename T, int N>
+template <typename T, int N, bool BIDIR>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p) {
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
@@ -157,25 +168,34 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const int mblk = wave >> 1, mhalf = wave & 1;
   const int mtb = mblk == 0 ? 0 : 1, msb = mblk == 2 ? 1 : 0;
 
+  // BIDIR: a reverse sweep (zero initial state, no D x) storing a float32
+  // partial, then the forward sweep adding it
+  for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
+  const bool rev = BIDIR && sweep == 0;
   f4 st[PBW];
 #pragma unroll
   for (int k = 0; k < PBW; ++k)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-      st[k][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
+      st[k][r] = p.h0 && !rev ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
       sm.S[pp][nn] = st[k][r];
     }
 
   SsdStager<T, N> stg;
-  stg.load(p, tid, b, h, g, 0);
+  stg.load(p, tid, b, h, g, 0, rev);
   stg.commit(sm, 0, tid);
   __syncthreads();
 
   for (int64_t c = 0; c < nchunks; ++c) {
     const int cur = c & 1;
-    const int64_t t0 = c * kQ;
-    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ);
+    const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
+    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ, rev);
+    // forward sweep of the bidirectional scan: the reverse partial of this
+    // chunk's output rows, for the store at the chunk's end
+    float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (BIDIR && !rev && t0 + (tid >> 4) < p.L)
+      pv = *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + (tid >> 4)) * p.H + h) * kP + (tid & 15) * 4);
 
     // decay of the chunk: cs_t, e^{cs_t}, the state-update weights
     if (wave == 0 && lane < kQ) {
@@ -295,27 +315,35 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     // for the loads has to wait for it as well
     if (c + 1 < nchunks) stg.commit(sm, cur ^ 1, tid);
     {
-      // y + D x -> global, 4 consecutive head channels per thread
+      // 4 consecutive head channels per thread: y + D x (+ the reverse
+      // partial) -> y, or the reverse sweep's partial -> part
       const int t = tid >> 4, c4 = (tid & 15) * 4;
       if (t0 + t < p.L) {
         const float4 yv = *reinterpret_cast<const float4*>(&sm.Y[t][c4]);
-        const float4 xv = *reinterpret_cast<const float4*>(&sm.X[cur][t][c4]);
-        Vec4<T>::store(p.y + ((b * p.L + t0 + t) * p.H + h) * kP + c4,
-                       make_float4(yv.x + Dh * xv.x, yv.y + Dh * xv.y, yv.z + Dh * xv.z, yv.w + Dh * xv.w));
+        const int64_t row = (b * p.L + sweep_time(t0 + t, p.L, rev)) * p.H + h;
+        if (rev) {
+          *reinterpret_cast<float4*>(p.part + row * kP + c4) = yv;
+        } else {
+          const float4 xv = *reinterpret_cast<const float4*>(&sm.X[cur][t][c4]);
+          Vec4<T>::store(p.y + row * kP + c4, make_float4(yv.x + Dh * xv.x + pv.x, yv.y + Dh * xv.y + pv.y,
+                                                          yv.z + Dh * xv.z + pv.z, yv.w + Dh * xv.w + pv.w));
+        }
       }
     }
     __syncthreads();
   }
 
-  if (p.h_last) {
+  float* const fin = rev ? p.g_first : p.h_last;
+  if (fin) {
 #pragma unroll
     for (int k = 0; k < PBW; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-        p.h_last[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
+        fin[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
       }
   }
+  }  // sweep
 }
 
 // ---------------------------------------------------------------------------
@@ -406,30 +434,32 @@ struct SsdStagerBf {
   uint16_t rdt;
   bool vx[kXT], vb[kBT], vdt;
 
+  // rows tau0 .. tau0 + kQ - 1 of the sweep (rev: time L - 1 - tau)
   __device__ __forceinline__ void load(const SsdArgs<uint16_t>& p, int tid, int64_t b, int64_t h, int64_t g,
-                                       int64_t t0) {
+                                       int64_t tau0, bool rev) {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
       // rows along the lanes, so that the transposed stores of the commit
       // fall on distinct banks
       const int u = tid + k * 64 * kWaves, row = u % kQ, c4 = (u / kQ) * 4;
-      const int64_t t = t0 + row;
-      vx[k] = t < p.L;
-      rx[k] = *reinterpret_cast<const uint2*>(p.x + ((b * p.L + (vx[k] ? t : p.L - 1)) * p.H + h) * kP + c4);
+      const int64_t tau = tau0 + row;
+      vx[k] = tau < p.L;
+      const int64_t t = sweep_time(vx[k] ? tau : p.L - 1, p.L, rev);
+      rx[k] = *reinterpret_cast<const uint2*>(p.x + ((b * p.L + t) * p.H + h) * kP + c4);
     }
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
-      const int64_t t = t0 + row;
-      vb[k] = t < p.L;
-      const int64_t off = ((b * p.L + (vb[k] ? t : p.L - 1)) * p.G + g) * N + c4;
+      const int64_t tau = tau0 + row;
+      vb[k] = tau < p.L;
+      const int64_t off = ((b * p.L + sweep_time(vb[k] ? tau : p.L - 1, p.L, rev)) * p.G + g) * N + c4;
       rb[k] = *reinterpret_cast<const uint2*>(p.B + off);
       rc[k] = *reinterpret_cast<const uint2*>(p.C + off);
     }
     // step sizes: lanes 0 .. kQ-1 of the last wave
-    const int64_t td = t0 + (tid & (kQ - 1));
+    const int64_t td = tau0 + (tid & (kQ - 1));
     vdt = (tid >> 6) == kWaves - 1 && (tid & 63) < kQ && td < p.L;
-    rdt = p.dt[(b * p.L + (td < p.L ? td : p.L - 1)) * p.H + h];
+    rdt = p.dt[(b * p.L + sweep_time(td < p.L ? td : p.L - 1, p.L, rev)) * p.H + h];
   }
 
   // step size of this lane's row (zero past L or outside the dt task)
@@ -486,15 +516,29 @@ __device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah,
   }
 }
 
-// y rows t0 .. t0 + kQ - 1 (those before L) -> global, 4 head channels per thread
+// rows t0 .. t0 + kQ - 1 of the sweep (those before L), 4 head channels per
+// thread: y (+ the reverse partial pv) -> y, or, in the reverse sweep, the
+// float32 partial -> part
 __device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const float (&Y)[kQ][kP + 4], int tid,
-                                             int64_t b, int64_t h, int64_t t0) {
+                                             int64_t b, int64_t h, int64_t t0, bool rev, float4 pv) {
   const int t = tid >> 4, c4 = (tid & 15) * 4;
   if (t0 + t < p.L) {
     const float4 v = *reinterpret_cast<const float4*>(&Y[t][c4]);
-    *reinterpret_cast<uint2*>(p.y + ((b * p.L + t0 + t) * p.H + h) * kP + c4) =
-        make_uint2(pack_bf16(v.x, v.y), pack_bf16(v.z, v.w));
+    const int64_t row = (b * p.L + sweep_time(t0 + t, p.L, rev)) * p.H + h;
+    if (rev)
+      *reinterpret_cast<float4*>(p.part + row * kP + c4) = v;
+    else
+      *reinterpret_cast<uint2*>(p.y + row * kP + c4) =
+          make_uint2(pack_bf16(v.x + pv.x, v.y + pv.y), pack_bf16(v.z + pv.z, v.w + pv.w));
   }
+}
+
+// the reverse partial of sweep rows t0 .. t0 + kQ - 1 for this thread's store
+__device__ __forceinline__ float4 load_partial(const SsdArgs<uint16_t>& p, int tid, int64_t b, int64_t h,
+                                               int64_t t0) {
+  const int t = tid >> 4, c4 = (tid & 15) * 4;
+  if (t0 + t >= p.L) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + t) * p.H + h) * kP + c4);
 }
 
 // S[p][n0 .. n0+3] (high and low bf16 parts) from 4 float32 values
@@ -507,7 +551,7 @@ __device__ __forceinline__ void store_state_bf16(SsdSmemBf<N>& sm, int pp, int n
   *reinterpret_cast<uint2*>(&sm.S[1][pp][n0]) = make_uint2(l01, l23);
 }
 
-template <int N>
+template <int N, bool BIDIR>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs<uint16_t> p) {
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
@@ -524,12 +568,21 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   const int64_t b = blockIdx.x / p.H, h = blockIdx.x % p.H;
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
-  const float Dh = p.D ? p.D[h] : 0.f;
+  const float Dfwd = p.D ? p.D[h] : 0.f;
   const int64_t nchunks = (p.L + kQ - 1) / kQ;
 
   const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
   const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
   const int mtb = wave == 0 ? 0 : 1, msb = wave == 2 ? 1 : 0;  // causal C B^T block of waves 0..2
+
+  // the block t < 16, s >= 16 of M stays zero (future steps)
+  for (int i = tid; i < 2 * kQ * SsdSmemBf<N>::TP; i += 64 * kWaves) (&sm.M[0][0][0])[i] = 0;
+
+  // BIDIR: a reverse sweep (zero initial state, no D x) storing a float32
+  // partial, then the forward sweep adding it
+  for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
+  const bool rev = BIDIR && sweep == 0;
+  const float Dh = rev ? 0.f : Dfwd;
 
   // st[k][r] = S[p][n], p = 16 (spb + k) + li, n = 16 snb + 4 lk + r
   f4 st[PBW];
@@ -537,25 +590,31 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   for (int k = 0; k < PBW; ++k) {
     const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[k][r] = p.h0 ? p.h0[((b * p.H + h) * kP + pp) * N + n0 + r] : 0.f;
+    for (int r = 0; r < 4; ++r) st[k][r] = p.h0 && !rev ? p.h0[((b * p.H + h) * kP + pp) * N + n0 + r] : 0.f;
     store_state_bf16(sm, pp, n0, st[k]);
   }
-  // the block t < 16, s >= 16 of M stays zero (future steps)
-  for (int i = tid; i < 2 * kQ * SsdSmemBf<N>::TP; i += 64 * kWaves) (&sm.M[0][0][0])[i] = 0;
 
   SsdStagerBf<N> stg;
-  stg.load(p, tid, b, h, g, 0);
+  stg.load(p, tid, b, h, g, 0, rev);
   stg.commit(sm, 0, tid);
   if (wave == kWaves - 1) chunk_decay(sm, 0, Ah, lane, stg.dt_value());
+  // forward sweep of the bidirectional scan: the reverse partial of the chunk
+  // whose output is stored next, one chunk ahead of its store
+  float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pv_prev = pv;
+  if (BIDIR && !rev) pv = load_partial(p, tid, b, h, 0);
   __syncthreads();
 
   for (int64_t c = 0; c < nchunks; ++c) {
     const int cur = c & 1, nxt = cur ^ 1;
-    const int64_t t0 = c * kQ;
-    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ);
+    const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
+    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ, rev);
 
     // ---- phase 1 ----
-    if (c > 0) store_y_bf16(p, sm.Y[nxt], tid, b, h, t0 - kQ);
+    if (c > 0) store_y_bf16(p, sm.Y[nxt], tid, b, h, t0 - kQ, rev, pv_prev);
+    if (BIDIR && !rev) {
+      pv_prev = pv;
+      if (c + 1 < nchunks) pv = load_partial(p, tid, b, h, t0 + kQ);
+    }
 
     if (wave < 3) {
       // causal block of C B^T, masked and decayed: M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t,
@@ -659,19 +718,22 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
     }
     __syncthreads();
   }
-  store_y_bf16(p, sm.Y[(nchunks - 1) & 1], tid, b, h, (nchunks - 1) * kQ);
+  store_y_bf16(p, sm.Y[(nchunks - 1) & 1], tid, b, h, (nchunks - 1) * kQ, rev, pv_prev);
 
-  if (p.h_last) {
+  float* const fin = rev ? p.g_first : p.h_last;
+  if (fin) {
 #pragma unroll
     for (int k = 0; k < PBW; ++k)
-      *reinterpret_cast<float4*>(p.h_last + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+      *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
           make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
   }
+  if (BIDIR && rev) __syncthreads();  // the forward sweep reuses the LDS tiles
+  }  // sweep
 }
 
 int ssd_validate(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const void* y, const float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t P,
-                 int64_t G, int64_t N, int dtype) {
+                 const float* h0, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L,
+                 int64_t H, int64_t P, int64_t G, int64_t N, int dtype) {
   if (!x || !dt || !A || !B || !C || !y) return SSM_ERR_NULL;
   if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0) return SSM_ERR_DIM;
   int64_t t, rows, seq, bc, state, hd;
@@ -683,26 +745,37 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (P != kP || (N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
   if (Bs * H > INT32_MAX) return SSM_ERR_DIM;
-  const void* ptrs[] = {x, dt, A, B, C, D, h0, y, h_last};
+  const void* ptrs[] = {x, dt, A, B, C, D, h0, y, h_last, g_first};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   const int64_t es = dtype == SSM_F32 ? 4 : 2;
   const Range in[] = {rng(x, seq * es), rng(dt, hd * es), rng(A, H * 4), rng(B, bc * es), rng(C, bc * es),
                       rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0)};
-  const Range out[] = {rng(y, seq * es), rng(h_last, h_last ? state * 4 : 0)};
-  for (int i = 0; i < 2; ++i) {
+  const Range out[] = {rng(y, seq * es), rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0)};
+  for (int i = 0; i < 3; ++i) {
     if (out[i].hi == out[i].lo) continue;
     for (const Range& r : in)
       if (r.hi > r.lo && overlap(out[i], r)) return SSM_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (out[j].hi > out[j].lo && overlap(out[i], out[j])) return SSM_ERR_ALIAS;
   }
-  if (out[1].hi > out[1].lo && overlap(out[0], out[1])) return SSM_ERR_ALIAS;
   return SSM_OK;
+}
+
+// float32 partial of the bidirectional scan's reverse sweep: into y for
+// float32 (read back and overwritten by the same thread), into the workspace
+// for bf16
+size_t ssd_bidir_ws_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
+  if (dtype != SSM_BF16) return 0;
+  int64_t n;
+  if (!mul_ok(Bs, L, &n) || !mul_ok(n, H, &n) || !mul_ok(n, P, &n) || n > INT64_MAX / 8) return 0;
+  return (static_cast<size_t>(n) * 4 + 255) & ~static_cast<size_t>(255);
 }
 
 template <typename T>
 int launch_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-               const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t G, int64_t N,
-               hipStream_t stream) {
+               const float* h0, void* y, float* h_last, float* g_first, float* part, bool bidir, int64_t Bs,
+               int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream) {
   SsdArgs<T> a;
   a.x = static_cast<const T*>(x);
   a.dt = static_cast<const T*>(dt);
@@ -713,20 +786,28 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   a.h0 = h0;
   a.y = static_cast<T*>(y);
   a.h_last = h_last;
+  a.part = part;
+  a.g_first = g_first;
   a.L = L;
   a.H = H;
   a.G = G;
   const dim3 grid(static_cast<unsigned>(Bs * H)), block(64 * kWaves);
   if constexpr (std::is_same<T, uint16_t>::value) {
-    if (N == 128)
-      hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64>), grid, block, 0, stream, a);
+    if (N == 128) {
+      if (bidir) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+    } else {
+      if (bidir) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    }
   } else {
-    if (N == 128)
-      hipLaunchKernelGGL((ssd_fwd_kernel<T, 128>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((ssd_fwd_kernel<T, 64>), grid, block, 0, stream, a);
+    if (N == 128) {
+      if (bidir) hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, false>), grid, block, 0, stream, a);
+    } else {
+      if (bidir) hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, false>), grid, block, 0, stream, a);
+    }
   }
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
@@ -736,9 +817,39 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
 extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                            const float* D, const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H,
                            int64_t P, int64_t G, int64_t N, int dtype, void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, y, h_last, Bs, L, H, P, G, N, dtype);
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == SSM_F32) return launch_ssd<float>(x, dt, A, B, C, D, h0, y, h_last, Bs, L, H, G, N, st);
-  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, y, h_last, Bs, L, H, G, N, st);
+  if (dtype == SSM_F32)
+    return launch_ssd<float>(x, dt, A, B, C, D, h0, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
+}
+
+extern "C" size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
+  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0) return 0;
+  return ssd_bidir_ws_bytes(Bs, L, H, P, dtype);
+}
+
+extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                                 const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs,
+                                 int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
+  if (rc != SSM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == SSM_F32)
+    return launch_ssd<float>(x, dt, A, B, C, D, h0, y, h_last, g_first, static_cast<float*>(y), true, Bs, L, H, G,
+                             N, st);
+  const size_t need = ssd_bidir_ws_bytes(Bs, L, H, P, dtype);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SSM_ERR_WORKSPACE;
+  // the workspace may not overlap any argument
+  int64_t seq = Bs * L * H * P, hd = Bs * L * H, bc = Bs * L * G * N, state = Bs * H * P * N;
+  const Range ws = rng(workspace, static_cast<int64_t>(need));
+  const Range args[] = {rng(x, seq * 2), rng(dt, hd * 2), rng(A, H * 4), rng(B, bc * 2), rng(C, bc * 2),
+                        rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(y, seq * 2),
+                        rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0)};
+  for (const Range& r : args)
+    if (r.hi > r.lo && overlap(ws, r)) return SSM_ERR_ALIAS;
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, y, h_last, g_first, static_cast<float*>(workspace), true, Bs, L,
+                              H, G, N, st);
 }

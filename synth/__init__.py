@@ -59,6 +59,7 @@ WORKLOADS = {
 SSD_WORKLOADS = {
     "ssd_f32_Bs32_L400_H8_P64_N128": dict(Bs=32, L=400, H=8, P=64, G=1, N=128, dtype="f32"),
     "ssd_bf16_Bs8_L4096_H32_P64_N128": dict(Bs=8, L=4096, H=32, P=64, G=1, N=128, dtype="bf16"),
+    "ssd_bidir_bf16_Bs8_L4096_H32_P64_N128": dict(Bs=8, L=4096, H=32, P=64, G=1, N=128, dtype="bf16", bidir=True),
 }
 
 

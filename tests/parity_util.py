@@ -131,8 +131,9 @@ def assert_grads_close(got, ref, dtype):
         assert_close(k, v, ref[k], tol)
 
 
-def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None):
-    """ssm_ssd_fwd on the GPU: (y, h_last) as float64 numpy arrays."""
+def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=False, want_g=False):
+    """ssm_ssd_fwd (or ssm_ssd_bidir_fwd) on the GPU: (y, h_last) as float64
+    numpy arrays, and g_first as a third value for the bidirectional scan."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -140,12 +141,20 @@ def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None):
     Bs, L, H, P = inp["x"].shape
     N = inp["B"].shape[3]
     h = torch.full((Bs, H, P, N), float("nan"), dtype=torch.float32, device=dev) if want_h else None
+    gf = torch.full((Bs, H, P, N), float("nan"), dtype=torch.float32, device=dev) if want_g else None
     h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, dtype=np.float32)).to(dev)
     y = torch.full_like(t["x"], float("nan"))
-    ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], None if D_none else t["D"], y=y, h_last=h, h0=h0t,
-                    stream=stream)
+    D = None if D_none else t["D"]
+    if bidir:
+        ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, g_first=gf, h0=h0t,
+                              stream=stream)
+    else:
+        ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, h0=h0t, stream=stream)
     torch.cuda.synchronize()
-    return y_to_numpy(y), (None if h is None else h.double().cpu().numpy())
+    out = (y_to_numpy(y), (None if h is None else h.double().cpu().numpy()))
+    if bidir:
+        out = out + ((None if gf is None else gf.double().cpu().numpy()),)
+    return out
 
 
 def degenerate_inputs(case, Bs=2, L=200, ED=64, seed=13):

@@ -205,3 +205,42 @@ def test_ssd_validation():
     assert ssd(y=P[0] + 64) == ssm.SSM_ERR_ALIAS     # y inside x
     assert ssd(h=P[7]) == ssm.SSM_ERR_ALIAS          # h_last on top of y
     assert ssd(h=P[6]) == ssm.SSM_ERR_ALIAS          # h_last on top of h0
+
+
+SSD_BI_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "y", "h", "g"]
+
+
+def ssd_bidir(**kw):
+    args = {n: P[i] for i, n in enumerate(SSD_BI_PTRS)}
+    args.update(Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16, ws=P[12])
+    args["ws_bytes"] = ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16)
+    args.update(kw)
+    return ssm.lib().ssm_ssd_bidir_fwd(*[args[n] for n in SSD_BI_PTRS], args["Bs"], args["L"], args["H"], args["P"],
+                                       args["G"], args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+def test_ssd_bidir_workspace_size():
+    # the reverse sweep's float32 partial output, one value per element of y
+    assert ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16) >= 4 * 2 * 64 * 4 * 64
+    assert ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_F32) == 0
+    assert ssm.ssm_ssd_bidir_workspace_bytes(0, 64, 4, 64, ssm.SSM_BF16) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
+def test_ssd_bidir_null_pointer(name):
+    assert ssd_bidir(**{name: None}) == ssm.SSM_ERR_NULL
+
+
+def test_ssd_bidir_validation():
+    need = ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16)
+    assert ssd_bidir(L=0) == ssm.SSM_ERR_DIM
+    assert ssd_bidir(N=96) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd_bidir(ws=None) == ssm.SSM_ERR_WORKSPACE
+    assert ssd_bidir(ws_bytes=need - 1) == ssm.SSM_ERR_WORKSPACE
+    assert ssd_bidir(ws=P[12] + 4) == ssm.SSM_ERR_WORKSPACE       # misaligned workspace
+    assert ssd_bidir(g=P[8]) == ssm.SSM_ERR_ALIAS                  # g_first on top of h_last
+    assert ssd_bidir(g=P[7] + 64) == ssm.SSM_ERR_ALIAS             # g_first inside y
+    assert ssd_bidir(ws=P[7]) == ssm.SSM_ERR_ALIAS                 # workspace on top of y
+    assert ssd_bidir(ws=P[0]) == ssm.SSM_ERR_ALIAS                 # workspace on top of x
+    # float32 needs no workspace: the reverse partial is kept in y itself
+    assert ssd_bidir(dtype=ssm.SSM_F32, ws=None, ws_bytes=0, N=96) == ssm.SSM_ERR_UNSUPPORTED

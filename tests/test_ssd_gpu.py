@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from parity_util import TOL, assert_close, log, run_gpu_ssd
+from parity_util import TOL, assert_close, log, run_gpu_ssd, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -68,12 +68,62 @@ def test_repeatable_bits(dtype):
     assert np.array_equal(a, b) and np.array_equal(ha, hb)
 
 
-@pytest.mark.parametrize("name", ["ssd_f32_Bs32_L400_H8_P64_N128", "ssd_bf16_Bs8_L4096_H32_P64_N128"])
+@pytest.mark.parametrize("name", sorted(synth.SSD_WORKLOADS))
 def test_workloads(name):
     w = synth.SSD_WORKLOADS[name]
+    bidir = w.get("bidir", False)
     log("ssd workload %s" % name)
     inp = synth.make_ssd_inputs(w["Bs"], w["L"], w["H"], w["P"], w["G"], w["N"], w["dtype"], seed=0)
-    y, hl = run_gpu_ssd(inp, want_h=True)
-    y_ref, h_ref, _ = oracle.ssd(**inp, want_h_last=True)
-    assert_close("y", y, y_ref, TOL[w["dtype"]])
+    out = run_gpu_ssd(inp, want_h=True, want_g=bidir, bidir=bidir)
+    ref = oracle.ssd(**inp, bidir=bidir, want_h_last=True, want_g_first=bidir)
+    assert_close("y", out[0], ref[0], TOL[w["dtype"]])
+    assert_close("h_last", out[1], ref[1], TOL["f32"])
+    if bidir:
+        assert_close("g_first", out[2], ref[2], TOL["f32"])
+
+
+def check_bidir(Bs, L, H, G, N, dtype="f32", seed=0, h0=False, D_none=False):
+    log("ssd bidir case Bs=%d L=%d H=%d G=%d N=%d dtype=%s seed=%d h0=%s D_none=%s" % (Bs, L, H, G, N, dtype, seed,
+                                                                                     h0, D_none))
+    inp = synth.make_ssd_inputs(Bs, L, H, 64, G, N, dtype, seed=seed)
+    h = synth.normal(seed, 94, (Bs, H, 64, N)) if h0 else None
+    y, hl, gf = run_gpu_ssd(inp, h0=h, want_h=True, want_g=True, D_none=D_none, bidir=True)
+    ref_inp = dict(inp, D=None) if D_none else inp
+    y_ref, h_ref, g_ref = oracle.ssd(**ref_inp, h0=h, bidir=True, want_h_last=True, want_g_first=True)
+    assert_close("y", y, y_ref, TOL[dtype])
     assert_close("h_last", hl, h_ref, TOL["f32"])
+    assert_close("g_first", gf, g_ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1, 31, 32, 33, 100, 400])
+def test_bidirectional_sequence_lengths(L, dtype):
+    check_bidir(2, L, 2, 1, 128, dtype=dtype, seed=L + 50)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bidirectional_groups_and_state_64(dtype):
+    check_bidir(3, 70, 6, 3, 64, dtype=dtype, seed=51)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bidirectional_initial_state_and_no_D(dtype):
+    check_bidir(2, 90, 4, 2, 128, dtype=dtype, seed=52, h0=True, D_none=True)
+
+
+def test_bidirectional_long_bf16():
+    check_bidir(1, 4096, 2, 1, 128, dtype="bf16", seed=53, h0=True)
+
+
+def test_bidirectional_workspace_checks():
+    import torch
+    import state_space_model_selective_amd as ssm
+    inp = synth.make_ssd_inputs(1, 40, 2, 64, 1, 64, "bf16", seed=54)
+    t = to_device(inp, torch.device("cuda:0"))
+    need = ssm.ssm_ssd_bidir_workspace_bytes(1, 40, 2, 64, ssm.SSM_BF16)
+    assert need >= 1 * 40 * 2 * 64 * 4
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], workspace=small)
+    assert e.value.status == ssm.SSM_ERR_WORKSPACE
+
