@@ -727,7 +727,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
       *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
           make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
   }
-  if (BIDIR && rev) __syncthreads();  // the forward sweep reuses the LDS tiles
+  // the forward sweep reuses the LDS tiles and reads the partial just stored
+  if (BIDIR && rev) __syncthreads();
   }  // sweep
 }
 
@@ -763,8 +764,9 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
 }
 
 // float32 partial of the bidirectional scan's reverse sweep: into y for
-// float32 (read back and overwritten by the same thread), into the workspace
-// for bf16
+// float32, into the workspace for bf16. Another wave of the same workgroup
+// reads each value in the forward sweep; the workgroup barrier that ends the
+// reverse sweep orders the stores before those loads.
 size_t ssd_bidir_ws_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
   if (dtype != SSM_BF16) return 0;
   int64_t n;
