@@ -48,7 +48,8 @@ def lib():
         L.oracle_scan.restype = ctypes.c_int
         L.oracle_scan_bwd.argtypes = [ctypes.c_int] + [vp] * 8 + [i64] * 4 + [vp] * 7 + [ctypes.c_int]
         L.oracle_scan_bwd.restype = ctypes.c_int
-        L.oracle_ssd.argtypes = [ctypes.c_int, ctypes.c_int] + [vp] * 7 + [i64] * 6 + [vp] * 3 + [ctypes.c_int]
+        L.oracle_ssd.argtypes = ([ctypes.c_int, ctypes.c_int] + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
+                                 ctypes.c_double, vp] + [i64] * 6 + [vp] * 3 + [ctypes.c_int])
         L.oracle_ssd.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -164,14 +165,22 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, nthreads=None):
     return out
 
 
-def ssd(x, dt, A, B, C, D=None, *, h0=None, bidir=False, want_h_last=False, want_g_first=False, nthreads=None):
+def ssd(x, dt, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
+        dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, want_h_last=False, want_g_first=False,
+        nthreads=None):
     """Multi-head selective scan in fp64.
 
     x (Bs, L, H, P), dt (Bs, L, H), A (H,), B and C (Bs, L, G, N), D (H,) or
     None, h0 (Bs, H, P, N) or None; float32 arrays, or uint16 bfloat16 bit
-    patterns for x, dt, B, C. Returns (y (Bs, L, H, P), h_last, g_first) with
-    the states (Bs, H, P, N) when requested, else None.
+    patterns for x, dt, B, C. dt_bias (H,) float32, dt_softplus, dt_limit and
+    the gate z (x's shape and dtype) as in scan(), per head. Returns
+    (y (Bs, L, H, P), h_last, g_first) with the states (Bs, H, P, N) when
+    requested, else None.
     """
+    dt_bias = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float32)
+    z = None if z is None else np.ascontiguousarray(z)
+    if z is not None and (z.dtype != np.asarray(x).dtype or z.shape != np.shape(x)):
+        raise TypeError("z must match x in shape and dtype")
     x = np.ascontiguousarray(x)
     dt = np.ascontiguousarray(dt)
     B = np.ascontiguousarray(B)
@@ -186,10 +195,12 @@ def ssd(x, dt, A, B, C, D=None, *, h0=None, bidir=False, want_h_last=False, want
     Bs, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     assert dt.shape == (Bs, L, H) and B.shape == C.shape == (Bs, L, G, N) and A.shape == (H,)
+    assert dt_bias is None or dt_bias.shape == (H,)
     y = np.empty((Bs, L, H, P))
     hl = np.empty((Bs, H, P, N)) if want_h_last else None
     gf = np.empty((Bs, H, P, N)) if (want_g_first and bidir) else None
     rc = lib().oracle_ssd(dtype, int(bool(bidir)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                          _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]), _ptr(z),
                           Bs, L, H, P, G, N, _ptr(y), _ptr(hl), _ptr(gf), _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_ssd failed with code %d" % rc)

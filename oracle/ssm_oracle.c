@@ -88,14 +88,19 @@ typedef struct work {
   int64_t k0, k1; /* this worker's range of k */
 } work_t;
 
+/* clamp(softplus?(v + bias), dt_min, dt_max); bias is dt_bias[e] or 0 */
+static double step_map(double v, double bias, int softplus, double dt_min, double dt_max) {
+  v += bias;
+  if (softplus) v = v > 20.0 ? v : log1p(exp(v));
+  if (v < dt_min) v = dt_min;
+  if (v > dt_max) v = dt_max;
+  return v;
+}
+
 /* delta' for the element at index ix of channel e */
 static double step_size(const struct work* w, int64_t ix, int64_t e) {
-  double v = load(w->delta, ix, w->dtype);
-  if (w->dt_bias) v += (double)w->dt_bias[e];
-  if (w->dt_softplus) v = v > 20.0 ? v : log1p(exp(v));
-  if (v < w->dt_min) v = w->dt_min;
-  if (v > w->dt_max) v = w->dt_max;
-  return v;
+  return step_map(load(w->delta, ix, w->dtype), w->dt_bias ? (double)w->dt_bias[e] : 0.0, w->dt_softplus,
+                  w->dt_min, w->dt_max);
 }
 
 /* One channel: the forward recurrence, then (bidir) the reverse one. */
@@ -385,6 +390,11 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
  *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p][n] + D[h] x[b,t,h,p]
  * bidir adds the reverse-time scan with the same a_t (no shift, D x once):
  *   R_t = a_t R_{t+1} + (dt x)_t B_t,  R_L = 0,   y += sum_n C_t R_t.
+ * The same options as the per-channel form, with the head in place of the
+ * channel (the forward listing of the Bi-Mamba2 page passes dt_bias per head
+ * and z of x's shape to this scan):
+ *   dt' = clamp(softplus?(dt[b,t,h] + dt_bias[h]), dt_min, dt_max) replaces dt,
+ *   y'[b,t,h,p] = y[b,t,h,p] z sigmoid(z), z = z[b,t,h,p] (the complete output).
  * The chunk length of the pages' kernels does not change the result; this
  * definition has none. Outputs fp64: y (Bs, L, H, P); h_last and g_first
  * (Bs, H, P, N) or NULL. Threads split the independent (b, h) pairs.
@@ -393,6 +403,10 @@ typedef struct {
   int dtype, bidir;
   const void *x, *dt, *B, *C;
   const float *A, *D, *h0;
+  const float* dt_bias; /* (H) or NULL */
+  int dt_softplus;
+  double dt_min, dt_max;
+  const void* z; /* (Bs, L, H, P) gate, x's dtype, or NULL */
   int64_t Bs, L, H, P, G, N;
   double *y, *h_last, *g_first;
   int64_t k0, k1; /* (b, h) pairs [k0, k1) */
@@ -416,7 +430,8 @@ static void* ssd_worker(void* arg) {
         S[i] = (dir == 0 && w->h0) ? (double)w->h0[(b * H + h) * P * N + i] : 0.0;
       for (int64_t s = 0; s < L; ++s) {
         const int64_t t = dir == 0 ? s : L - 1 - s;
-        const double dtv = load(w->dt, (b * L + t) * H + h, w->dtype);
+        const double dtv = step_map(load(w->dt, (b * L + t) * H + h, w->dtype),
+                                    w->dt_bias ? (double)w->dt_bias[h] : 0.0, w->dt_softplus, w->dt_min, w->dt_max);
         const double a = exp(dtv * Ah);
         const int64_t ib = ((b * L + t) * G + g) * N;
         for (int64_t p = 0; p < P; ++p) {
@@ -437,14 +452,23 @@ static void* ssd_worker(void* arg) {
       if (out)
         for (int64_t i = 0; i < P * N; ++i) out[(b * H + h) * P * N + i] = S[i];
     }
+    /* the gate multiplies the complete output of the head */
+    if (w->z)
+      for (int64_t t = 0; t < L; ++t)
+        for (int64_t p = 0; p < P; ++p) {
+          const int64_t ix = ((b * L + t) * H + h) * P + p;
+          const double zv = load(w->z, ix, w->dtype);
+          w->y[ix] *= zv / (1.0 + exp(-zv));
+        }
   }
   free(S);
   return NULL;
 }
 
 int oracle_ssd(int dtype, int bidir, const void* x, const void* dt, const float* A, const void* B, const void* C,
-               const float* D, const float* h0, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
-               double* y, double* h_last, double* g_first, int nthreads) {
+               const float* D, const float* h0, const float* dt_bias, int dt_softplus, double dt_min, double dt_max,
+               const void* z, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, double* y,
+               double* h_last, double* g_first, int nthreads) {
   if (!x || !dt || !A || !B || !C || !y) return -1;
   if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
@@ -461,8 +485,8 @@ int oracle_ssd(int dtype, int bidir, const void* x, const void* dt, const float*
   }
   const int64_t per = (K + nthreads - 1) / nthreads;
   for (int i = 0; i < nthreads; ++i) {
-    ws[i] = (ssd_t){dtype, bidir, x, dt, B, C, A, D, h0, Bs, L, H, P, G, N, y, h_last, bidir ? g_first : NULL,
-                    0, 0, 0};
+    ws[i] = (ssd_t){dtype, bidir, x, dt, B, C, A, D, h0, dt_bias, dt_softplus, dt_min, dt_max, z,
+                    Bs, L, H, P, G, N, y, h_last, bidir ? g_first : NULL, 0, 0, 0};
     ws[i].k0 = per * i < K ? per * i : K;
     ws[i].k1 = per * (i + 1) < K ? per * (i + 1) : K;
   }

@@ -42,6 +42,43 @@ def test_equals_per_channel_scan_group_by_group(G):
         np.testing.assert_array_equal(hl[:, heads].reshape(Bs, ED, N), h1)
 
 
+@pytest.mark.parametrize("G,bidir", [(1, False), (2, False), (2, True)])
+def test_options_equal_per_channel_options(G, bidir):
+    # dt_bias per head, softplus, a clamp that binds at both ends, and the
+    # gate, against the per-channel oracle's (separately pinned) options on
+    # the expanded inputs
+    Bs, L, H, P, N = 2, 29, 4, 3, 5
+    inp = synth.make_ssd_inputs(Bs, L, H, P, G, N, seed=11)
+    inp["dt"] = synth.normal(11, 95, (Bs, L, H))           # raw, both signs
+    dt_bias = synth.normal(11, 96, (H,))
+    z = synth.normal(11, 97, (Bs, L, H, P))
+    h0 = synth.normal(11, 98, (Bs, H, P, N))
+    opts = dict(dt_bias=dt_bias, dt_softplus=True, dt_limit=(0.05, 1.2), z=z)
+    y, hl, gf = oracle.ssd(**inp, h0=h0, bidir=bidir, want_h_last=True, want_g_first=bidir, **opts)
+    y0, _, _ = oracle.ssd(**inp, h0=h0, bidir=bidir)
+    assert rel(y, y0) > 1e-2                                # the options change the result
+    hpg = H // G
+    for g in range(G):
+        heads = list(range(g * hpg, (g + 1) * hpg))
+        ED = hpg * P
+        x = np.ascontiguousarray(inp["x"][:, :, heads, :].reshape(Bs, L, ED))
+        delta = np.ascontiguousarray(np.repeat(inp["dt"][:, :, heads], P, axis=2))
+        A = np.ascontiguousarray(np.repeat(inp["A"][heads], P)[:, None] * np.ones((1, N), np.float32))
+        D = np.ascontiguousarray(np.repeat(inp["D"][heads], P))
+        B = np.ascontiguousarray(inp["B"][:, :, g, :])
+        C = np.ascontiguousarray(inp["C"][:, :, g, :])
+        h0e = np.ascontiguousarray(h0[:, heads].reshape(Bs, ED, N))
+        ze = np.ascontiguousarray(z[:, :, heads, :].reshape(Bs, L, ED))
+        be = np.ascontiguousarray(np.repeat(dt_bias[heads], P))
+        y1, h1, g1 = oracle.scan(x, delta, A, B, C, D, h0=h0e, dt_bias=be, dt_softplus=True, dt_limit=(0.05, 1.2),
+                                 z=ze, bidir=bidir, want_h_last=True, want_g_first=bidir)
+        # the bidirectional sums add the D x term in another order
+        assert rel(y[:, :, heads, :].reshape(Bs, L, ED), y1) < 1e-13
+        assert rel(hl[:, heads].reshape(Bs, ED, N), h1) == 0.0
+        if bidir:
+            assert rel(gf[:, heads].reshape(Bs, ED, N), g1) == 0.0
+
+
 def test_closed_matrix_form():
     # y_t = sum_{s <= t} (C_t . B_s) exp(A sum_{r=s+1}^{t} dt_r) dt_s x_s + D x_t
     #       + sum_n C_t[n] exp(A sum_{r<=t} dt_r) h0[n]
