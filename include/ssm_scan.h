@@ -182,10 +182,16 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
  *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p][n] + D[h] x[b,t,h,p]
  *
  * (the recurrence of ssm_scan_fwd with one decay per head and a shared B, C
- * per group). dt is used as given.
+ * per group).
  *   x      : (Bs, L, H, P) of dtype      dt : (Bs, L, H) of dtype
  *   A      : (H) float32                 B, C : (Bs, L, G, N) of dtype
  *   D      : (H) float32, or NULL        h0 : (Bs, H, P, N) float32, or NULL
+ *   opts   : the options of ssm_scan_options, per head: dt_bias is (H)
+ *            float32 (dt' = clamp(softplus?(dt + dt_bias[h]), dt_min,
+ *            dt_max) replaces dt) and the gate z is (Bs, L, H, P) of dtype
+ *            (y' = y z sigmoid(z), after D x); NULL: dt as given, no gate
+ *            (the chunked-scan forward listing of that page passes dt_bias,
+ *            dt_softplus, dt_limit and z to this scan)
  *   y      : (Bs, L, H, P) of dtype, written in full
  *   h_last : (Bs, H, P, N) float32, or NULL -- S after the last step
  * Supported: P = 64, N = 64 or 128, H a multiple of G. The state and every
@@ -198,8 +204,8 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
  * ssm_scan_fwd (SSM_ERR_DIM also when H is not a multiple of G).
  */
 int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-                const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G,
-                int64_t N, int dtype, void* stream);
+                const float* h0, const ssm_scan_options* opts, void* y, float* h_last, int64_t Bs, int64_t L,
+                int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* stream);
 
 /*
  * Bidirectional multi-head scan (Bi-Mamba2 on the multi-head form): the
@@ -212,7 +218,8 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
  *   g_t[p][n] = a_t g_{t+1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],   g_L = 0
  *   y[b,t,h,p] = sum_n C[b,t,g,n] (S_t[p][n] + g_t[p][n]) + D[h] x[b,t,h,p]
  *
- * Arguments as ssm_ssd_fwd, and
+ * with dt' in place of dt in both directions and the gate applied to the
+ * complete sum when opts sets them. Arguments as ssm_ssd_fwd, and
  *   g_first   : (Bs, H, P, N) float32, or NULL -- g after t = 0
  *   workspace : device memory of ssm_ssd_bidir_workspace_bytes(...) bytes for
  *               bfloat16 (the reverse direction's float32 partial of y; it
@@ -223,9 +230,9 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
  */
 size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype);
 int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                      const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs,
-                      int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
+                      float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);

@@ -76,11 +76,11 @@ def lib():
         L.ssm_scan_bwd_workspace_bytes.restype = sz
         L.ssm_scan_bwd.argtypes = [vp] * 15 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bwd.restype = ci
-        L.ssm_ssd_fwd.argtypes = [vp] * 9 + [i64] * 6 + [ci, vp]
+        L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp]
         L.ssm_ssd_fwd.restype = ci
         L.ssm_ssd_bidir_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
         L.ssm_ssd_bidir_workspace_bytes.restype = sz
-        L.ssm_ssd_bidir_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp, sz, vp]
+        L.ssm_ssd_bidir_fwd.argtypes = [vp] * 11 + [i64] * 6 + [ci, vp, sz, vp]
         L.ssm_ssd_bidir_fwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
@@ -215,10 +215,13 @@ def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False
     return o
 
 
-def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=None):
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=None, dt_bias=None,
+                dt_softplus=False, dt_limit=None, z=None):
     """Multi-head selective scan: x (Bs, L, H, P), dt (Bs, L, H), A (H,),
     B and C (Bs, L, G, N), D (H,) or None, h0 (Bs, H, P, N) or None.
-    Returns y (Bs, L, H, P); the final state goes to h_last if given."""
+    dt_bias (H,) / dt_softplus / dt_limit pre-process dt, z (like x) gates
+    the output. Returns y (Bs, L, H, P); the final state goes to h_last if
+    given."""
     import torch
     if not x.is_cuda:
         raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
@@ -227,8 +230,9 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=Non
     G, N = B.shape[2], B.shape[3]
     if y is None:
         y = torch.empty_like(x)
-    rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_last),
-                           Bs, L, H, P, G, N, dtc, _stream(x, stream))
+    opts = _options(dt_bias, dt_softplus, dt_limit, z)
+    rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts), _ptr(y),
+                           _ptr(h_last), Bs, L, H, P, G, N, dtc, _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")
     return y
@@ -241,10 +245,11 @@ def ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtype=SSM_F32):
 
 
 def ssm_ssd_bidir_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, g_first=None, h0=None, workspace=None,
-                      stream=None):
+                      stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
     """Bidirectional multi-head scan: ssm_ssd_fwd plus the same scan in
-    decreasing time from a zero state (no D). Returns y; the final states go
-    to h_last (forward) and g_first (reverse) if given."""
+    decreasing time from a zero state (no D), with the options of
+    ssm_ssd_fwd (the gate applies to the sum). Returns y; the final states
+    go to h_last (forward) and g_first (reverse) if given."""
     import torch
     if not x.is_cuda:
         raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
@@ -257,8 +262,9 @@ def ssm_ssd_bidir_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, g_first=None,
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib().ssm_ssd_bidir_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
-                                 _ptr(h_last), _ptr(g_first), Bs, L, H, P, G, N, dtc, _ptr(workspace), wsb,
+    opts = _options(dt_bias, dt_softplus, dt_limit, z)
+    rc = lib().ssm_ssd_bidir_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
+                                 _ptr(y), _ptr(h_last), _ptr(g_first), Bs, L, H, P, G, N, dtc, _ptr(workspace), wsb,
                                  _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_bidir_fwd")

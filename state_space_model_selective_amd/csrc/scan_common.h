@@ -68,6 +68,21 @@ struct Vec4<uint16_t> {
 };
 
 // ---------------------------------------------------------------------------
+// Options of the Bi-Mamba2 forward ("Some questions of Bi-Mamba2 and Hydra",
+// the MambaChunkScanCombinedFn.forward listing): the step size used is
+// clamp(softplus?(d + bias), lo, hi), softplus(v) = v above 20, else
+// log(1 + e^v) (as log1p(e^v) for accuracy at small e^v); the output gate is
+// y z sigmoid(z). bias points at the channel's (or head's) bias, or is null.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float map_step(float d, const float* bias, int softplus, float lo, float hi) {
+  if (bias) d += *bias;
+  if (softplus) d = d > 20.f ? d : log1pf(__expf(d));
+  return fminf(fmaxf(d, lo), hi);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
 // Cross-lane operands (DPP). Lane q of a 16-lane row holds B_t[q] (or
 // C_t[q]); quad g of the row needs B_t[4g .. 4g+3]. quad_bcast<J> makes every
 // lane of a quad read lane J of that quad. As a plain move the compiler folds

@@ -142,17 +142,11 @@ struct alignas(16) FoldArea {
 
 enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
 
-// delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max); softplus(v)
-// = v above 20, else log(1 + e^v) (as log1p(e^v) for accuracy at small e^v).
+// delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max)
 template <typename T>
 __device__ __forceinline__ float step_size(const ScanArgs<T>& p, float d, int64_t e) {
-  if (p.dt_bias) d += p.dt_bias[e];
-  if (p.dt_softplus) d = d > 20.f ? d : log1pf(__expf(d));
-  return fminf(fmaxf(d, p.dt_min), p.dt_max);
+  return map_step(d, p.dt_bias ? p.dt_bias + e : nullptr, p.dt_softplus, p.dt_min, p.dt_max);
 }
-
-// z sigmoid(z)
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
 
 // Staging of one round: each thread owns TPT fixed (row, chunk) tasks of the
 // x/delta tile (4 channels per chunk) or of the B/C tile (4 states per chunk),

@@ -58,8 +58,35 @@ struct SsdArgs {
   // P) (may alias y for float32), and the reverse direction's final state
   float* part;
   float* g_first;
+  // options: dt' = clamp(softplus?(dt + dt_bias[h]), dt_min, dt_max) when
+  // dt_pre; the output (after D x and, bidirectional, both directions) times
+  // z sigmoid(z) when z is set
+  const float* dt_bias;
+  int dt_softplus;
+  int dt_pre;
+  float dt_min, dt_max;
+  const T* z;
   int64_t L, H, G;
 };
+
+// step size of the head whose bias (or null) is given, after the options
+template <typename T>
+__device__ __forceinline__ float ssd_step(const SsdArgs<T>& p, float d, const float* bias) {
+  return p.dt_pre ? map_step(d, bias, p.dt_softplus, p.dt_min, p.dt_max) : d;
+}
+
+// gate of 4 consecutive head channels of the row at time t (zero-filled bits
+// past L are never used)
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::Raw load_gate(const SsdArgs<T>& p, int tid, int64_t b, int64_t h,
+                                                           int64_t t) {
+  if (t + (tid >> 4) >= p.L) return Vec4<T>::zero();
+  return Vec4<T>::load_raw(p.z + ((b * p.L + t + (tid >> 4)) * p.H + h) * kP + (tid & 15) * 4);
+}
+
+__device__ __forceinline__ float4 gated(float4 v, float4 z) {
+  return make_float4(v.x * silu(z.x), v.y * silu(z.y), v.z * silu(z.z), v.w * silu(z.w));
+}
 
 // Time of step tau of a sweep: the forward sweep runs t = tau, the reverse
 // sweep of the bidirectional scan t = L - 1 - tau (inputs read in place).
@@ -141,7 +168,7 @@ struct SsdStager {
   }
 };
 
-template <typename T, int N, bool BIDIR>
+template <typename T, int N, bool BIDIR, bool GATE>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p) {
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
@@ -158,6 +185,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.f;
+  const float* const bias = p.dt_bias ? p.dt_bias + h : nullptr;
   const int64_t nchunks = (p.L + kQ - 1) / kQ;
 
   // output block of this wave: t-block ytb (16 steps) x head-channel block ypb
@@ -190,15 +218,12 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   for (int64_t c = 0; c < nchunks; ++c) {
     const int cur = c & 1;
     const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
-    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ, rev);
-    // forward sweep of the bidirectional scan: the reverse partial of this
-    // chunk's output rows, for the store at the chunk's end
-    float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (BIDIR && !rev && t0 + (tid >> 4) < p.L)
-      pv = *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + (tid >> 4)) * p.H + h) * kP + (tid & 15) * 4);
-
-    // decay of the chunk: cs_t, e^{cs_t}, the state-update weights
+    // decay of the chunk: cs_t, e^{cs_t}, the state-update weights (ahead of
+    // the next chunk's loads, whose registers are live from there on)
     if (wave == 0 && lane < kQ) {
+      // the step sizes after the options, in place (rows past L keep 0; the
+      // wave's LDS accesses stay in order, so the reads below see them)
+      if (p.dt_pre && t0 + lane < p.L) sm.dt[cur][lane] = ssd_step(p, sm.dt[cur][lane], bias);
       float s = 0.f, tot = 0.f;
 #pragma unroll
       for (int r = 0; r < kQ; ++r) {
@@ -212,6 +237,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
       sm.w[lane] = __expf(cse - cst) * sm.dt[cur][lane];
       if (lane == 0) sm.cs_end = cse;
     }
+    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ, rev);
+    // forward sweep of the bidirectional scan: the reverse partial of this
+    // chunk's output rows, for the store at the chunk's end
+    float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (BIDIR && !rev && t0 + (tid >> 4) < p.L)
+      pv = *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + (tid >> 4)) * p.H + h) * kP + (tid & 15) * 4);
+    // the gate of the same rows (forward sweep only: the partial is ungated)
+    typename Vec4<T>::Raw zr = Vec4<T>::zero();
+    if (GATE && !rev) zr = load_gate(p, tid, b, h, t0);
+
     __syncthreads();
 
     // C B^T on the causal blocks, each half of the sum over n by one wave,
@@ -325,8 +360,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
           *reinterpret_cast<float4*>(p.part + row * kP + c4) = yv;
         } else {
           const float4 xv = *reinterpret_cast<const float4*>(&sm.X[cur][t][c4]);
-          Vec4<T>::store(p.y + row * kP + c4, make_float4(yv.x + Dh * xv.x + pv.x, yv.y + Dh * xv.y + pv.y,
-                                                          yv.z + Dh * xv.z + pv.z, yv.w + Dh * xv.w + pv.w));
+          float4 o = make_float4(yv.x + Dh * xv.x + pv.x, yv.y + Dh * xv.y + pv.y, yv.z + Dh * xv.z + pv.z,
+                                 yv.w + Dh * xv.w + pv.w);
+          if (GATE) o = gated(o, Vec4<T>::widen(zr));
+          Vec4<T>::store(p.y + row * kP + c4, o);
         }
       }
     }
@@ -463,10 +500,14 @@ struct SsdStagerBf {
   }
 
   // step size of this lane's row (zero past L or outside the dt task)
-  __device__ __forceinline__ float dt_value() const { return vdt ? to_f32(rdt) : 0.f; }
+  // (rows past L keep dt = 0 whatever the options would make of it)
+  __device__ __forceinline__ float dt_value(const SsdArgs<uint16_t>& p, const float* bias) const {
+    return vdt ? ssd_step(p, to_f32(rdt), bias) : 0.f;
+  }
 
   // rows at or past L are zero (dt = 0: a = 1 and no input)
-  __device__ __forceinline__ void commit(SsdSmemBf<N>& sm, int buf, int tid) const {
+  __device__ __forceinline__ void commit(const SsdArgs<uint16_t>& p, const float* bias, SsdSmemBf<N>& sm, int buf,
+                                         int tid) const {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
       const int u = tid + k * 64 * kWaves, row = u % kQ, c4 = (u / kQ) * 4;
@@ -482,7 +523,7 @@ struct SsdStagerBf {
       *reinterpret_cast<uint2*>(&sm.B[buf][row][c4]) = vb[k] ? rb[k] : make_uint2(0u, 0u);
       *reinterpret_cast<uint2*>(&sm.C[buf][row][c4]) = vb[k] ? rc[k] : make_uint2(0u, 0u);
     }
-    if ((tid >> 6) == kWaves - 1 && (tid & 63) < kQ) sm.dt[buf][tid & 63] = dt_value();
+    if ((tid >> 6) == kWaves - 1 && (tid & 63) < kQ) sm.dt[buf][tid & 63] = dt_value(p, bias);
   }
 };
 
@@ -517,19 +558,22 @@ __device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah,
 }
 
 // rows t0 .. t0 + kQ - 1 of the sweep (those before L), 4 head channels per
-// thread: y (+ the reverse partial pv) -> y, or, in the reverse sweep, the
-// float32 partial -> part
+// thread: y (+ the reverse partial pv), times the gate -> y, or, in the
+// reverse sweep, the float32 partial -> part
+template <bool GATE>
 __device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const float (&Y)[kQ][kP + 4], int tid,
-                                             int64_t b, int64_t h, int64_t t0, bool rev, float4 pv) {
+                                             int64_t b, int64_t h, int64_t t0, bool rev, float4 pv, uint2 zr) {
   const int t = tid >> 4, c4 = (tid & 15) * 4;
   if (t0 + t < p.L) {
     const float4 v = *reinterpret_cast<const float4*>(&Y[t][c4]);
     const int64_t row = (b * p.L + sweep_time(t0 + t, p.L, rev)) * p.H + h;
     if (rev)
       *reinterpret_cast<float4*>(p.part + row * kP + c4) = v;
-    else
-      *reinterpret_cast<uint2*>(p.y + row * kP + c4) =
-          make_uint2(pack_bf16(v.x + pv.x, v.y + pv.y), pack_bf16(v.z + pv.z, v.w + pv.w));
+    else {
+      float4 o = make_float4(v.x + pv.x, v.y + pv.y, v.z + pv.z, v.w + pv.w);
+      if (GATE) o = gated(o, Vec4<uint16_t>::widen(zr));
+      *reinterpret_cast<uint2*>(p.y + row * kP + c4) = make_uint2(pack_bf16(o.x, o.y), pack_bf16(o.z, o.w));
+    }
   }
 }
 
@@ -551,7 +595,7 @@ __device__ __forceinline__ void store_state_bf16(SsdSmemBf<N>& sm, int pp, int n
   *reinterpret_cast<uint2*>(&sm.S[1][pp][n0]) = make_uint2(l01, l23);
 }
 
-template <int N, bool BIDIR>
+template <int N, bool BIDIR, bool GATE>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs<uint16_t> p) {
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
@@ -569,6 +613,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
   const float Dfwd = p.D ? p.D[h] : 0.f;
+  const float* const bias = p.dt_bias ? p.dt_bias + h : nullptr;
   const int64_t nchunks = (p.L + kQ - 1) / kQ;
 
   const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
@@ -594,26 +639,38 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
     store_state_bf16(sm, pp, n0, st[k]);
   }
 
-  SsdStagerBf<N> stg;
-  stg.load(p, tid, b, h, g, 0, rev);
-  stg.commit(sm, 0, tid);
-  if (wave == kWaves - 1) chunk_decay(sm, 0, Ah, lane, stg.dt_value());
+  // two stagers: while chunk c is computed, chunk c + 1 waits in one of them
+  // (loaded during chunk c - 1, committed at the end of chunk c) and chunk
+  // c + 2 is loaded into the other
+  SsdStagerBf<N> stg0, stg1;
+  stg0.load(p, tid, b, h, g, 0, rev);
+  stg0.commit(p, bias, sm, 0, tid);
+  if (wave == kWaves - 1) chunk_decay(sm, 0, Ah, lane, stg0.dt_value(p, bias));
+  if (nchunks > 1) stg1.load(p, tid, b, h, g, kQ, rev);
   // forward sweep of the bidirectional scan: the reverse partial of the chunk
   // whose output is stored next, one chunk ahead of its store
   float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pv_prev = pv;
   if (BIDIR && !rev) pv = load_partial(p, tid, b, h, 0);
+  // the gate of those rows, the same way (forward sweep only)
+  uint2 zr = make_uint2(0u, 0u), zr_prev = zr;
+  if (GATE && !rev) zr = load_gate(p, tid, b, h, 0);
   __syncthreads();
 
-  for (int64_t c = 0; c < nchunks; ++c) {
+  // one chunk: ld receives chunk c + 2, cm holds chunk c + 1
+  auto chunk = [&](const int64_t c, SsdStagerBf<N>& ld, const SsdStagerBf<N>& cm) {
     const int cur = c & 1, nxt = cur ^ 1;
     const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
-    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ, rev);
+    if (c + 2 < nchunks) ld.load(p, tid, b, h, g, t0 + 2 * kQ, rev);
 
     // ---- phase 1 ----
-    if (c > 0) store_y_bf16(p, sm.Y[nxt], tid, b, h, t0 - kQ, rev, pv_prev);
+    if (c > 0) store_y_bf16<GATE>(p, sm.Y[nxt], tid, b, h, t0 - kQ, rev, pv_prev, zr_prev);
     if (BIDIR && !rev) {
       pv_prev = pv;
       if (c + 1 < nchunks) pv = load_partial(p, tid, b, h, t0 + kQ);
+    }
+    if (GATE && !rev) {
+      zr_prev = zr;
+      if (c + 1 < nchunks) zr = load_gate(p, tid, b, h, t0 + kQ);
     }
 
     if (wave < 3) {
@@ -713,12 +770,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
 #pragma unroll
     for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
     if (c + 1 < nchunks) {
-      stg.commit(sm, nxt, tid);
-      if (wave == kWaves - 1) chunk_decay(sm, nxt, Ah, lane, stg.dt_value());
+      cm.commit(p, bias, sm, nxt, tid);
+      if (wave == kWaves - 1) chunk_decay(sm, nxt, Ah, lane, cm.dt_value(p, bias));
     }
     __syncthreads();
+  };
+  for (int64_t c = 0; c < nchunks; c += 2) {
+    chunk(c, stg0, stg1);
+    if (c + 1 < nchunks) chunk(c + 1, stg1, stg0);
   }
-  store_y_bf16(p, sm.Y[(nchunks - 1) & 1], tid, b, h, (nchunks - 1) * kQ, rev, pv_prev);
+  store_y_bf16<GATE>(p, sm.Y[(nchunks - 1) & 1], tid, b, h, (nchunks - 1) * kQ, rev, pv_prev, zr_prev);
 
   float* const fin = rev ? p.g_first : p.h_last;
   if (fin) {
@@ -733,8 +794,9 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
 }
 
 int ssd_validate(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L,
-                 int64_t H, int64_t P, int64_t G, int64_t N, int dtype) {
+                 const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last,
+                 const float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                 int dtype) {
   if (!x || !dt || !A || !B || !C || !y) return SSM_ERR_NULL;
   if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0) return SSM_ERR_DIM;
   int64_t t, rows, seq, bc, state, hd;
@@ -746,12 +808,16 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (P != kP || (N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
   if (Bs * H > INT32_MAX) return SSM_ERR_DIM;
-  const void* ptrs[] = {x, dt, A, B, C, D, h0, y, h_last, g_first};
+  const float* dt_bias = opts ? opts->dt_bias : nullptr;
+  const void* z = opts ? opts->z : nullptr;
+  if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
+  const void* ptrs[] = {x, dt, A, B, C, D, h0, dt_bias, z, y, h_last, g_first};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   const int64_t es = dtype == SSM_F32 ? 4 : 2;
   const Range in[] = {rng(x, seq * es), rng(dt, hd * es), rng(A, H * 4), rng(B, bc * es), rng(C, bc * es),
-                      rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0)};
+                      rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(dt_bias, dt_bias ? H * 4 : 0),
+                      rng(z, z ? seq * es : 0)};
   const Range out[] = {rng(y, seq * es), rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0)};
   for (int i = 0; i < 3; ++i) {
     if (out[i].hi == out[i].lo) continue;
@@ -774,10 +840,21 @@ size_t ssd_bidir_ws_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype
   return (static_cast<size_t>(n) * 4 + 255) & ~static_cast<size_t>(255);
 }
 
+template <typename T, bool BIDIR, bool GATE>
+void launch_ssd_kernel(const SsdArgs<T>& a, int64_t N, dim3 grid, dim3 block, hipStream_t stream) {
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (N == 128) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, BIDIR, GATE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, BIDIR, GATE>), grid, block, 0, stream, a);
+  } else {
+    if (N == 128) hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, BIDIR, GATE>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, BIDIR, GATE>), grid, block, 0, stream, a);
+  }
+}
+
 template <typename T>
 int launch_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-               const float* h0, void* y, float* h_last, float* g_first, float* part, bool bidir, int64_t Bs,
-               int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream) {
+               const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, float* part,
+               bool bidir, int64_t Bs, int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream) {
   SsdArgs<T> a;
   a.x = static_cast<const T*>(x);
   a.dt = static_cast<const T*>(dt);
@@ -790,26 +867,22 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   a.h_last = h_last;
   a.part = part;
   a.g_first = g_first;
+  a.dt_bias = opts ? opts->dt_bias : nullptr;
+  a.dt_softplus = opts && opts->dt_softplus ? 1 : 0;
+  a.dt_min = opts ? opts->dt_min : -INFINITY;
+  a.dt_max = opts ? opts->dt_max : INFINITY;
+  a.dt_pre = (a.dt_bias || a.dt_softplus || a.dt_min > -INFINITY || a.dt_max < INFINITY) ? 1 : 0;
+  a.z = opts ? static_cast<const T*>(opts->z) : nullptr;
   a.L = L;
   a.H = H;
   a.G = G;
   const dim3 grid(static_cast<unsigned>(Bs * H)), block(64 * kWaves);
-  if constexpr (std::is_same<T, uint16_t>::value) {
-    if (N == 128) {
-      if (bidir) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
-    } else {
-      if (bidir) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
-    }
+  if (bidir) {
+    if (a.z) launch_ssd_kernel<T, true, true>(a, N, grid, block, stream);
+    else launch_ssd_kernel<T, true, false>(a, N, grid, block, stream);
   } else {
-    if (N == 128) {
-      if (bidir) hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, false>), grid, block, 0, stream, a);
-    } else {
-      if (bidir) hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, false>), grid, block, 0, stream, a);
-    }
+    if (a.z) launch_ssd_kernel<T, false, true>(a, N, grid, block, stream);
+    else launch_ssd_kernel<T, false, false>(a, N, grid, block, stream);
   }
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
@@ -817,14 +890,15 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
 }  // namespace
 
 extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                           const float* D, const float* h0, void* y, float* h_last, int64_t Bs, int64_t L, int64_t H,
-                           int64_t P, int64_t G, int64_t N, int dtype, void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
+                           const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
+                           int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                           void* stream) {
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SSM_F32)
-    return launch_ssd<float>(x, dt, A, B, C, D, h0, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
-  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
+    return launch_ssd<float>(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
 }
 
 extern "C" size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
@@ -833,25 +907,29 @@ extern "C" size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H
 }
 
 extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                                 const float* D, const float* h0, void* y, float* h_last, float* g_first, int64_t Bs,
-                                 int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
+                                 const float* D, const float* h0, const ssm_scan_options* opts, void* y,
+                                 float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P,
+                                 int64_t G, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SSM_F32)
-    return launch_ssd<float>(x, dt, A, B, C, D, h0, y, h_last, g_first, static_cast<float*>(y), true, Bs, L, H, G,
-                             N, st);
+    return launch_ssd<float>(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, static_cast<float*>(y), true, Bs, L, H,
+                             G, N, st);
   const size_t need = ssd_bidir_ws_bytes(Bs, L, H, P, dtype);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SSM_ERR_WORKSPACE;
   // the workspace may not overlap any argument
   int64_t seq = Bs * L * H * P, hd = Bs * L * H, bc = Bs * L * G * N, state = Bs * H * P * N;
   const Range ws = rng(workspace, static_cast<int64_t>(need));
+  const float* dt_bias = opts ? opts->dt_bias : nullptr;
+  const void* z = opts ? opts->z : nullptr;
   const Range args[] = {rng(x, seq * 2), rng(dt, hd * 2), rng(A, H * 4), rng(B, bc * 2), rng(C, bc * 2),
                         rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(y, seq * 2),
-                        rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0)};
+                        rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0),
+                        rng(dt_bias, dt_bias ? H * 4 : 0), rng(z, z ? seq * 2 : 0)};
   for (const Range& r : args)
     if (r.hi > r.lo && overlap(ws, r)) return SSM_ERR_ALIAS;
-  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, y, h_last, g_first, static_cast<float*>(workspace), true, Bs, L,
-                              H, G, N, st);
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, static_cast<float*>(workspace), true,
+                              Bs, L, H, G, N, st);
 }

@@ -131,9 +131,10 @@ def assert_grads_close(got, ref, dtype):
         assert_close(k, v, ref[k], tol)
 
 
-def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=False, want_g=False):
+def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=False, want_g=False, opts=None):
     """ssm_ssd_fwd (or ssm_ssd_bidir_fwd) on the GPU: (y, h_last) as float64
-    numpy arrays, and g_first as a third value for the bidirectional scan."""
+    numpy arrays, and g_first as a third value for the bidirectional scan.
+    opts: dt_bias / dt_softplus / dt_limit / z as numpy values or None."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -145,11 +146,18 @@ def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=Fal
     h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, dtype=np.float32)).to(dev)
     y = torch.full_like(t["x"], float("nan"))
     D = None if D_none else t["D"]
+    kw = {}
+    if opts:
+        kw = dict(opts)
+        if kw.get("dt_bias") is not None:
+            kw["dt_bias"] = torch.from_numpy(np.ascontiguousarray(kw["dt_bias"], dtype=np.float32)).to(dev)
+        if kw.get("z") is not None:
+            kw["z"] = to_device({"z": kw["z"]}, dev)["z"]
     if bidir:
         ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, g_first=gf, h0=h0t,
-                              stream=stream)
+                              stream=stream, **kw)
     else:
-        ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, h0=h0t, stream=stream)
+        ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, h0=h0t, stream=stream, **kw)
     torch.cuda.synchronize()
     out = (y_to_numpy(y), (None if h is None else h.double().cpu().numpy()))
     if bidir:

@@ -12,8 +12,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
 
 # fake device addresses, 16-byte aligned and far apart; only used on paths that
-# must fail validation before anything touches them
+# must fail validation before anything touches them. Where a GPU is present a
+# validation gap would launch a kernel on them, so these host-only checks are
+# skipped there (the GPU tests load and call the same library).
 P = [0x10000000 * (i + 1) for i in range(20)]
+
+pytestmark = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                                reason="calls the library with fake device addresses: host-only")
 
 
 def declared_functions():
@@ -179,12 +184,15 @@ def test_bwd_validation():
     assert bwd(ws=P[7]) == ssm.SSM_ERR_ALIAS              # workspace on top of dy
 
 
-SSD_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "y", "h"]
+SSD_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "opts", "y", "h"]
+
+
+SP = {n: P[i] for i, n in enumerate(SSD_PTRS)}  # the default pointer of each argument
 
 
 def ssd(**kw):
-    args = {n: P[i] for i, n in enumerate(SSD_PTRS)}
-    args.update(Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_F32)
+    args = dict(SP)
+    args.update(opts=None, Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_F32)
     args.update(kw)
     return ssm.lib().ssm_ssd_fwd(*[args[n] for n in SSD_PTRS], args["Bs"], args["L"], args["H"], args["P"],
                                  args["G"], args["N"], args["dtype"], None)
@@ -201,18 +209,21 @@ def test_ssd_validation():
     assert ssd(P=32) == ssm.SSM_ERR_UNSUPPORTED
     assert ssd(N=16) == ssm.SSM_ERR_UNSUPPORTED
     assert ssd(dtype=5) == ssm.SSM_ERR_UNSUPPORTED
-    assert ssd(dt=P[1] + 8) == ssm.SSM_ERR_UNSUPPORTED
-    assert ssd(y=P[0] + 64) == ssm.SSM_ERR_ALIAS     # y inside x
-    assert ssd(h=P[7]) == ssm.SSM_ERR_ALIAS          # h_last on top of y
-    assert ssd(h=P[6]) == ssm.SSM_ERR_ALIAS          # h_last on top of h0
+    assert ssd(dt=SP["dt"] + 8) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(y=SP["x"] + 64) == ssm.SSM_ERR_ALIAS   # y inside x
+    assert ssd(h=SP["y"]) == ssm.SSM_ERR_ALIAS        # h_last on top of y
+    assert ssd(h=SP["h0"]) == ssm.SSM_ERR_ALIAS       # h_last on top of h0
 
 
-SSD_BI_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "y", "h", "g"]
+SSD_BI_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "opts", "y", "h", "g"]
+
+
+BP = dict({n: P[i] for i, n in enumerate(SSD_BI_PTRS)}, ws=P[12])  # default pointers
 
 
 def ssd_bidir(**kw):
-    args = {n: P[i] for i, n in enumerate(SSD_BI_PTRS)}
-    args.update(Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16, ws=P[12])
+    args = dict(BP)
+    args.update(opts=None, Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16)
     args["ws_bytes"] = ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16)
     args.update(kw)
     return ssm.lib().ssm_ssd_bidir_fwd(*[args[n] for n in SSD_BI_PTRS], args["Bs"], args["L"], args["H"], args["P"],
@@ -237,10 +248,31 @@ def test_ssd_bidir_validation():
     assert ssd_bidir(N=96) == ssm.SSM_ERR_UNSUPPORTED
     assert ssd_bidir(ws=None) == ssm.SSM_ERR_WORKSPACE
     assert ssd_bidir(ws_bytes=need - 1) == ssm.SSM_ERR_WORKSPACE
-    assert ssd_bidir(ws=P[12] + 4) == ssm.SSM_ERR_WORKSPACE       # misaligned workspace
-    assert ssd_bidir(g=P[8]) == ssm.SSM_ERR_ALIAS                  # g_first on top of h_last
-    assert ssd_bidir(g=P[7] + 64) == ssm.SSM_ERR_ALIAS             # g_first inside y
-    assert ssd_bidir(ws=P[7]) == ssm.SSM_ERR_ALIAS                 # workspace on top of y
-    assert ssd_bidir(ws=P[0]) == ssm.SSM_ERR_ALIAS                 # workspace on top of x
+    assert ssd_bidir(ws=BP["ws"] + 4) == ssm.SSM_ERR_WORKSPACE     # misaligned workspace
+    assert ssd_bidir(g=BP["h"]) == ssm.SSM_ERR_ALIAS               # g_first on top of h_last
+    assert ssd_bidir(g=BP["y"] + 64) == ssm.SSM_ERR_ALIAS          # g_first inside y
+    assert ssd_bidir(ws=BP["y"]) == ssm.SSM_ERR_ALIAS              # workspace on top of y
+    assert ssd_bidir(ws=BP["x"]) == ssm.SSM_ERR_ALIAS              # workspace on top of x
     # float32 needs no workspace: the reverse partial is kept in y itself
     assert ssd_bidir(dtype=ssm.SSM_F32, ws=None, ws_bytes=0, N=96) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_ssd_options_validation():
+    ref, _ = opts(dt_min=0.5, dt_max=0.1)
+    assert ssd(opts=ref) == ssm.SSM_ERR_ARG
+    ref, _ = opts(dt_max=float("nan"))
+    assert ssd_bidir(opts=ref) == ssm.SSM_ERR_ARG
+    ref, _ = opts(z=SP["y"])                            # gate on top of y
+    assert ssd(opts=ref) == ssm.SSM_ERR_ALIAS
+    ref, _ = opts(dt_bias=SP["h"])                      # h_last on top of the bias
+    assert ssd(opts=ref) == ssm.SSM_ERR_ALIAS
+    ref, _ = opts(z=P[13] + 8)                          # misaligned gate
+    assert ssd(opts=ref) == ssm.SSM_ERR_UNSUPPORTED
+    ref, _ = opts(dt_bias=P[13] + 4)                    # misaligned bias
+    assert ssd_bidir(opts=ref) == ssm.SSM_ERR_UNSUPPORTED
+    ref, _ = opts(z=BP["ws"])                           # gate inside the bidirectional workspace
+    assert ssd_bidir(opts=ref) == ssm.SSM_ERR_ALIAS
+    # valid options get past validation to the (missing) workspace check
+    ref, _ = opts(dt_bias=P[13], dt_softplus=1, dt_min=0.0, dt_max=1.0, z=P[14])
+    assert ssd_bidir(opts=ref, ws=None) == ssm.SSM_ERR_WORKSPACE
+

@@ -127,3 +127,58 @@ def test_bidirectional_workspace_checks():
         ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], workspace=small)
     assert e.value.status == ssm.SSM_ERR_WORKSPACE
 
+
+def check_options(Bs, L, H, G, N, dtype, seed, bidir=False, bias=True, softplus=True, limit=(0.02, 0.3),
+                  gate=True, h0=False):
+    log("ssd options case Bs=%d L=%d H=%d G=%d N=%d dtype=%s seed=%d bidir=%s bias=%s softplus=%s limit=%s "
+        "gate=%s h0=%s" % (Bs, L, H, G, N, dtype, seed, bidir, bias, softplus, limit, gate, h0))
+    inp = synth.make_ssd_inputs(Bs, L, H, 64, G, N, dtype, seed=seed)
+    opts = {}
+    if bias:
+        nb = synth.normal(seed, 99, (H,))
+        if softplus or (limit is not None and limit[0] > 0):
+            # mostly negative: dt + bias < 0 for many steps, which softplus or the clamp maps back
+            opts["dt_bias"] = (nb * 0.5 - 1.5).astype(np.float32)
+        else:
+            # the bias alone must keep the step positive (a negative step grows the state
+            # without bound: the overflow regime outside the contract)
+            opts["dt_bias"] = (np.abs(nb) * 0.05).astype(np.float32)
+    if softplus:
+        opts["dt_softplus"] = True
+    if limit is not None:
+        opts["dt_limit"] = limit
+    if gate:
+        z = synth.normal(seed, 100, (Bs, L, H, 64))
+        opts["z"] = synth.to_bf16(z) if dtype == "bf16" else z
+    h = synth.normal(seed, 101, (Bs, H, 64, N)) if h0 else None
+    out = run_gpu_ssd(inp, h0=h, want_h=True, want_g=bidir, bidir=bidir, opts=opts)
+    ref = oracle.ssd(**inp, h0=h, bidir=bidir, want_h_last=True, want_g_first=bidir, **opts)
+    assert_close("y", out[0], ref[0], TOL[dtype])
+    assert_close("h_last", out[1], ref[1], TOL["f32"])
+    if bidir:
+        assert_close("g_first", out[2], ref[2], TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1, 33, 200])
+def test_options_all(L, dtype):
+    check_options(2, L, 4, 2, 128, dtype, seed=60 + L)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_options_bidirectional(dtype):
+    check_options(2, 150, 4, 1, 128, dtype, seed=61, bidir=True, h0=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_options_state_64_bidirectional_ragged(dtype):
+    check_options(1, 77, 2, 1, 64, dtype, seed=62, bidir=True)
+
+
+@pytest.mark.parametrize("which", ["bias", "softplus", "limit", "gate"])
+def test_options_one_at_a_time(which):
+    # each option alone (the others off), bf16 and f32 alternating
+    kw = dict(bias=which == "bias", softplus=which == "softplus", limit=(0.02, 0.3) if which == "limit" else None,
+              gate=which == "gate")
+    check_options(2, 70, 4, 1, 128, "bf16" if which in ("bias", "gate") else "f32", seed=63, **kw)
+
