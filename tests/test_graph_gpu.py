@@ -1,0 +1,106 @@
+"""The entry points under HIP graph capture (torch.cuda.graph): each call is
+captured once and replayed several times, with the outputs overwritten and
+other eager work and synchronisations between the replays; every replay must
+reproduce the eager result bit for bit. The captured calls include the
+kernel that clears the split-sequence workspace (no memset node), the
+backward's reduction kernels and the bidirectional calls' workspaces."""
+import numpy as np
+import pytest
+
+import synth
+from parity_util import log, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def replay_check(name, fn, outs, reps=4):
+    import torch
+    log("graph case %s" % name)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up off the default stream, as capture wants
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    fn()  # the eager result
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    for r in ref:
+        assert bool(torch.isfinite(r.float()).all()), "eager result of %s is not finite" % name
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        for o in outs:
+            o.fill_(float("nan"))
+        noise = torch.randn(1 << 20, device=outs[0].device)
+        float(noise.abs().sum())  # eager work and a synchronisation between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, r), "%s: replay %d differs from the eager result in output %d" % (name, i, k)
+
+
+def test_forward_split_sequence_graph():
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 1, 8192, 64, 16
+    need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32, False)
+    assert need > 0, "this shape should take the split-sequence path"
+    dev = torch.device("cuda:0")
+    t = to_device(synth.make_inputs(Bs, L, ED, N, "f32", seed=70), dev)
+    y = torch.empty_like(t["x"])
+    h = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    replay_check("forward, split sequence", lambda: ssm.ssm_scan_fwd(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=y, h_last=h, workspace=ws), [y, h])
+
+
+def test_bidirectional_bf16_graph():
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 2, 600, 128, 16
+    need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_BF16, True)
+    dev = torch.device("cuda:0")
+    t = to_device(synth.make_inputs(Bs, L, ED, N, "bf16", seed=71), dev)
+    y = torch.empty_like(t["x"])
+    gf = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    replay_check("bidirectional bf16", lambda: ssm.ssm_scan_bidir_fwd(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=y, g_first=gf, workspace=ws if need else None),
+        [y, gf])
+
+
+def test_backward_graph():
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 2, 300, 64, 16
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(Bs, L, ED, N, "f32", seed=72)
+    t = to_device(dict(inp, dy=synth.make_output_grad(Bs, L, ED, "f32", seed=72)), dev)
+    out = {"dx": torch.empty_like(t["x"]), "ddelta": torch.empty_like(t["x"]), "dA": torch.empty_like(t["A"]),
+           "dB": torch.empty_like(t["B"]), "dC": torch.empty_like(t["B"]),
+           "dD": torch.empty((ED,), dtype=torch.float32, device=dev)}
+    need = ssm.ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    replay_check("backward", lambda: ssm.ssm_scan_bwd(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=out, workspace=ws),
+        [out[k] for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")])
+
+
+def test_multi_head_bidirectional_options_graph():
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, H, P, G, N = 1, 200, 4, 64, 1, 128
+    dev = torch.device("cuda:0")
+    t = to_device(synth.make_ssd_inputs(Bs, L, H, P, G, N, "bf16", seed=73), dev)
+    z = to_device({"z": synth.to_bf16(synth.normal(73, 100, (Bs, L, H, P)))}, dev)["z"]
+    bias = torch.from_numpy(np.ascontiguousarray(synth.normal(73, 99, (H,)) * 0.5 - 1.0, dtype=np.float32)).to(dev)
+    y = torch.empty_like(t["x"])
+    h = torch.empty((Bs, H, P, N), dtype=torch.float32, device=dev)
+    need = ssm.ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, ssm.SSM_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    replay_check("multi-head bidirectional bf16 with options", lambda: ssm.ssm_ssd_bidir_fwd(
+        t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=y, h_last=h, workspace=ws, dt_bias=bias,
+        dt_softplus=True, dt_limit=(0.01, 0.5), z=z), [y, h])
