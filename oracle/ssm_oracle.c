@@ -180,7 +180,9 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
                 const int64_t* chans, int64_t nchans, double* y, double* h_last, double* g_first,
                 int nthreads) {
   if (!x || !delta || !A || !B || !C || !y) return -1;
-  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return -1;
+  /* empty batches, sequences or channel sets are allowed: over zero steps the
+     state stays where it entered (h0, or zero) */
+  if (Bs < 0 || L < 0 || ED < 0 || N <= 0) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
   if (!chans) nchans = Bs * ED;
   if (nchans < 0) return -1;
@@ -322,16 +324,17 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
                     double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dh0,
                     int nthreads) {
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC || !dD) return -1;
-  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return -1;
+  if (Bs < 0 || L < 0 || ED < 0 || N <= 0) return -1; /* empty sizes allowed */
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
   const int64_t nblk = (ED + BWD_BLOCK - 1) / BWD_BLOCK;
-  if (nthreads < 1) nthreads = 1;
   if (nthreads > nblk) nthreads = (int)nblk;
   if (nthreads > 256) nthreads = 256;
-  double* dA_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED * N));
-  double* dD_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED));
-  double* partB = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N));
-  double* partC = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N));
+  if (nthreads < 1) nthreads = 1;
+  /* (one element more than needed, so that empty sizes still get a buffer) */
+  double* dA_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED * N + 1));
+  double* dD_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED + 1));
+  double* partB = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N + 1));
+  double* partC = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N + 1));
   bwd_t* ws = (bwd_t*)malloc(sizeof(bwd_t) * (size_t)nthreads);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
   int rc = 0;
@@ -470,12 +473,13 @@ int oracle_ssd(int dtype, int bidir, const void* x, const void* dt, const float*
                const void* z, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, double* y,
                double* h_last, double* g_first, int nthreads) {
   if (!x || !dt || !A || !B || !C || !y) return -1;
-  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
+  /* empty batches or sequences are allowed (over zero steps the state stays h0) */
+  if (Bs < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
   const int64_t K = Bs * H;
-  if (nthreads < 1) nthreads = 1;
   if (nthreads > K) nthreads = (int)K;
   if (nthreads > 256) nthreads = 256;
+  if (nthreads < 1) nthreads = 1;
   ssd_t* ws = (ssd_t*)malloc(sizeof(ssd_t) * (size_t)nthreads);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
   if (!ws || !th) {

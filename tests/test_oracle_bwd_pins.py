@@ -189,3 +189,20 @@ def test_backward_threads_agree():
     g4 = oracle.scan_bwd(**inp, dy=dy, nthreads=4)
     for k in g1:
         np.testing.assert_array_equal(g1[k], g4[k], err_msg=k)
+
+
+def test_backward_of_empty_inputs():
+    # an empty sequence has no output, so every gradient is zero (dh0 too:
+    # the loss does not depend on the state); with no channels, dB and dC
+    # (sums over the channels) are zero
+    inp = synth.make_inputs(2, 0, 6, 16, seed=31)
+    h0 = synth.normal(31, 9, (2, 6, 16))
+    g = oracle.scan_bwd(**inp, dy=np.zeros((2, 0, 6), np.float32), h0=h0)
+    assert g["dx"].shape == (2, 0, 6) and g["dB"].shape == (2, 0, 16)
+    for k in ("dA", "dD", "dh0"):
+        assert np.array_equal(g[k], np.zeros_like(g[k])), k
+    inp = synth.make_inputs(2, 7, 0, 16, seed=32)
+    g = oracle.scan_bwd(**inp, dy=np.zeros((2, 7, 0), np.float32))
+    assert g["dA"].shape == (0, 16) and g["dD"].shape == (0,)
+    for k in ("dB", "dC"):
+        assert g[k].shape == (2, 7, 16) and np.array_equal(g[k], np.zeros((2, 7, 16))), k

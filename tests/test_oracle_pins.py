@@ -384,6 +384,29 @@ def test_zero_initial_state_is_no_initial_state():
     assert np.array_equal(y0, yz) and np.array_equal(h0_, hz)
 
 
+def test_empty_sequence_keeps_the_entering_state():
+    # zero steps: no output, the forward state stays h0 (or zero) and the
+    # reverse state g_L = 0; a sequence cut at L1 = 0 resumes exactly
+    inp = small_inputs(2, 37, 5, 16, seed=25)
+    empty = {k: (np.ascontiguousarray(v[:, :0]) if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    h0 = (0.5 * synth.normal(25, 9, (2, 5, 16))).astype(np.float32)
+    y, h, g = oracle.scan(**empty, h0=h0, bidir=True, want_h_last=True, want_g_first=True)
+    assert y.shape == (2, 0, 5)
+    assert np.array_equal(h, h0.astype(np.float64)) and np.array_equal(g, np.zeros((2, 5, 16)))
+    _, hz, _ = oracle.scan(**empty, want_h_last=True)
+    assert np.array_equal(hz, np.zeros((2, 5, 16)))
+    y_full, h_full, _ = oracle.scan(**inp, h0=h0, want_h_last=True)
+    y2, h2, _ = oracle.scan(**inp, h0=h.astype(np.float32), want_h_last=True)
+    assert np.array_equal(y2, y_full) and np.array_equal(h2, h_full)
+
+
+def test_empty_batch_or_channels_give_empty_outputs():
+    for Bs, ED in ((0, 5), (2, 0)):
+        inp = small_inputs(Bs, 9, ED, 16, seed=26) if Bs * ED else synth.make_inputs(Bs, 9, ED, 16, seed=26)
+        y, h, g = oracle.scan(**inp, bidir=True, want_h_last=True, want_g_first=True)
+        assert y.shape == (Bs, 9, ED) and h.shape == (Bs, ED, 16) and g.shape == (Bs, ED, 16)
+
+
 # --- step-size pre-processing and the output gate -----------------------------
 def test_dt_bias_is_added_to_delta_exactly():
     # delta and bias on a 2^-12 grid: delta + bias is exact in float32, so the

@@ -148,6 +148,17 @@ def test_bf16_widens_exactly_and_threads_agree():
     np.testing.assert_array_equal(y16, y32)
 
 
+def test_empty_sequence_keeps_the_entering_state():
+    Bs, H, P, G, N = 2, 4, 3, 2, 5
+    inp = synth.make_ssd_inputs(Bs, 0, H, P, G, N, seed=8)
+    h0 = synth.normal(8, 9, (Bs, H, P, N))
+    y, hl, gf = oracle.ssd(**inp, h0=h0, bidir=True, want_h_last=True, want_g_first=True)
+    assert y.shape == (Bs, 0, H, P)
+    assert np.array_equal(hl, h0.astype(np.float64)) and np.array_equal(gf, np.zeros((Bs, H, P, N)))
+    y0, _, _ = oracle.ssd(**synth.make_ssd_inputs(0, 6, H, P, G, N, seed=8))
+    assert y0.shape == (0, 6, H, P)
+
+
 def test_rejects_bad_arguments():
     inp = synth.make_ssd_inputs(1, 4, 3, 2, 1, 2, seed=7)
     with pytest.raises(RuntimeError):
