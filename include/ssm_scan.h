@@ -43,6 +43,13 @@
  *    caller's next synchronisation on that stream.
  *  - Numerics: inputs whose state overflows float32 (a > 1, i.e. delta*A > 0
  *    over long spans) propagate inf/NaN; no error code is returned for them.
+ *  - Empty inputs: the batch size, the sequence length and the channel count
+ *    (Bs, L, ED; Bs and L of the multi-head scan) may be zero, and a buffer
+ *    with no elements may then be NULL. Nothing is scanned; over zero time
+ *    steps the forward state stays where it entered, so h_last = h0 (zero
+ *    without h0) and g_first = 0, and every gradient of the backward pass
+ *    is zero (dA, dD, dh0; dB and dC when there are time steps but no
+ *    channels). No workspace is needed.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -62,7 +69,8 @@ typedef enum {
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL = 1,        /* a required pointer is NULL */
-  SSM_ERR_DIM = 2,         /* a dimension is <= 0 or the sizes overflow int64 */
+  SSM_ERR_DIM = 2,         /* a dimension is negative (or zero where it must be positive: N, and H,
+                              P, G of the multi-head scan) or the sizes overflow int64 */
   SSM_ERR_UNSUPPORTED = 3, /* N not supported, unknown dtype, or a pointer not 16-byte aligned */
   SSM_ERR_ALIAS = 4,       /* an output overlaps an input, another output or the workspace */
   SSM_ERR_WORKSPACE = 5,   /* workspace smaller than ssm_scan_workspace_bytes() */

@@ -128,6 +128,15 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// a * b for sizes that may be zero (empty tensors); false if either is
+// negative or the product overflows
+bool mul_nn(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a > 0 && b > 0 && a > INT64_MAX / b) return false;
+  *out = a * b;
+  return true;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 Range rng(const void* p, int64_t bytes) {
@@ -170,6 +179,25 @@ __global__ void zero_words_kernel(unsigned* p, int64_t n) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[i] = 0u;
+}
+
+// dst[i] = src ? src[i] : 0 for n 4-byte words (the outputs of an empty
+// sequence: final states equal to the initial ones, zero gradients)
+__global__ void fill_words_kernel(unsigned* dst, const unsigned* src, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    dst[i] = src ? src[i] : 0u;
+}
+
+// Enqueues fill_words_kernel over `bytes` bytes (a multiple of 4) when dst is
+// set and bytes > 0; false if the launch failed.
+bool fill_async(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  if (!dst || bytes <= 0) return true;
+  const int64_t n = bytes / 4;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(fill_words_kernel, dim3(grid), dim3(256), 0, stream, static_cast<unsigned*>(dst),
+                     static_cast<const unsigned*>(src), n);
+  return hipGetLastError() == hipSuccess;
 }
 
 }  // namespace

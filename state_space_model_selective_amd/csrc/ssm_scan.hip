@@ -688,11 +688,12 @@ struct Sizes {
   int64_t elem;    // bytes per x/delta/B/C/y element
 };
 
+// Bs, L and ED may be zero (empty tensors); N must be 16.
 int check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, Sizes* s) {
-  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return SSM_ERR_DIM;
+  if (Bs < 0 || L < 0 || ED < 0 || N <= 0) return SSM_ERR_DIM;
   int64_t t;
-  if (!mul_ok(Bs, L, &t) || !mul_ok(t, ED, &s->seq) || !mul_ok(t, N, &s->bc)) return SSM_ERR_DIM;
-  if (!mul_ok(Bs, ED, &t) || !mul_ok(t, N, &s->state)) return SSM_ERR_DIM;
+  if (!mul_nn(Bs, L, &t) || !mul_nn(t, ED, &s->seq) || !mul_nn(t, N, &s->bc)) return SSM_ERR_DIM;
+  if (!mul_nn(Bs, ED, &t) || !mul_nn(t, N, &s->state)) return SSM_ERR_DIM;
   if (s->seq > INT64_MAX / 8 || s->state > INT64_MAX / 8) return SSM_ERR_DIM;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (N != 16) return SSM_ERR_UNSUPPORTED;
@@ -763,7 +764,7 @@ SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
 
 size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int bidir) {
   Sizes s;
-  if (check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK) return 0;
+  if (check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || s.seq == 0) return 0;
   // the bidirectional bf16 scan keeps its reverse-time partial sums in float32
   if (bidir && dtype == SSM_BF16) return static_cast<size_t>(s.seq) * 4;
   return plan_split(Bs, L, ED, bidir, device_cus()).bytes;
@@ -772,9 +773,10 @@ size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, 
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
              const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
              int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s) {
-  if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
   int rc = check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
+  // a buffer with no elements may be NULL
+  if ((s->seq > 0 && (!x || !delta || !y)) || (s->bc > 0 && (!B || !C)) || (ED > 0 && !A)) return SSM_ERR_NULL;
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
   const void* z = opts ? opts->z : nullptr;
   if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
@@ -795,10 +797,11 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
   if (g_first) out[nout++] = rng(g_first, s->state * 4);
   if (need > 0) out[nout++] = rng(ws, static_cast<int64_t>(need));
   for (int i = 0; i < nout; ++i) {
+    if (out[i].hi == out[i].lo) continue;
     for (const Range& r : in)
       if (r.hi > r.lo && overlap(out[i], r)) return SSM_ERR_ALIAS;
     for (int j = i + 1; j < nout; ++j)
-      if (overlap(out[i], out[j])) return SSM_ERR_ALIAS;
+      if (out[j].hi > out[j].lo && overlap(out[i], out[j])) return SSM_ERR_ALIAS;
   }
   return SSM_OK;
 }
@@ -883,6 +886,13 @@ int run(const void* x, const void* delta, const float* A, const void* B, const v
   int rc = validate(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.seq == 0) {
+    // nothing to scan. Over an empty sequence the forward state stays where it
+    // entered (h_last = h0, or zero) and the reverse state is zero.
+    const bool ok = fill_async(h_last, h0, s.state * 4, st) && fill_async(bidir ? g_first : nullptr, nullptr,
+                                                                          s.state * 4, st);
+    return ok ? SSM_OK : SSM_ERR_LAUNCH;
+  }
   if (dtype == SSM_F32)
     return launch_scan<float>(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
   return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
@@ -913,7 +923,7 @@ const char* ssm_status_str(int status) {
   switch (status) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "a required pointer is NULL";
-    case SSM_ERR_DIM: return "a dimension is not positive or the sizes overflow";
+    case SSM_ERR_DIM: return "a dimension is negative (or not positive where it must be) or the sizes overflow";
     case SSM_ERR_UNSUPPORTED: return "unsupported N or dtype, or a pointer not aligned to 16 bytes";
     case SSM_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case SSM_ERR_WORKSPACE: return "workspace missing or smaller than ssm_scan_workspace_bytes()";

@@ -589,11 +589,12 @@ struct BwdSizes {
   int64_t seq, bc, state, elem;
 };
 
+// Bs, L and ED may be zero (empty tensors); N must be 16.
 int bwd_check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, BwdSizes* s) {
-  if (Bs <= 0 || L <= 0 || ED <= 0 || N <= 0) return SSM_ERR_DIM;
+  if (Bs < 0 || L < 0 || ED < 0 || N <= 0) return SSM_ERR_DIM;
   int64_t t;
-  if (!mul_ok(Bs, L, &t) || !mul_ok(t, ED, &s->seq) || !mul_ok(t, N, &s->bc)) return SSM_ERR_DIM;
-  if (!mul_ok(Bs, ED, &t) || !mul_ok(t, N, &s->state)) return SSM_ERR_DIM;
+  if (!mul_nn(Bs, L, &t) || !mul_nn(t, ED, &s->seq) || !mul_nn(t, N, &s->bc)) return SSM_ERR_DIM;
+  if (!mul_nn(Bs, ED, &t) || !mul_nn(t, N, &s->state)) return SSM_ERR_DIM;
   if (s->seq > INT64_MAX / 8 || s->state > INT64_MAX / 8 || s->bc > INT64_MAX / 8 / ((ED + 15) / 16 + 1))
     return SSM_ERR_DIM;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
@@ -605,7 +606,7 @@ int bwd_check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, Bwd
 size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
   BwdSizes s;
   BwdLayout lo;
-  if (bwd_check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || !bwd_layout(Bs, L, ED, &lo)) return 0;
+  if (bwd_check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || s.seq == 0 || !bwd_layout(Bs, L, ED, &lo)) return 0;
   return lo.bytes;
 }
 
@@ -613,15 +614,19 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
                  const float* h0, const void* dy, const void* dx, const void* ddelta, const float* dA, const void* dB,
                  const void* dC, const float* dD, const float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N,
                  int dtype, const void* ws, size_t ws_bytes, BwdSizes* s) {
-  if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return SSM_ERR_NULL;
   int rc = bwd_check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
+  // a buffer with no elements may be NULL
+  if ((s->seq > 0 && (!x || !delta || !dy || !dx || !ddelta)) || (s->bc > 0 && (!B || !C || !dB || !dC)) ||
+      (ED > 0 && (!A || !dA)))
+    return SSM_ERR_NULL;
   const void* ptrs[] = {x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, ws};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   BwdLayout lo;
   if (!bwd_layout(Bs, L, ED, &lo)) return SSM_ERR_DIM;
-  if (!ws || ws_bytes < lo.bytes) return SSM_ERR_WORKSPACE;
+  if (s->seq == 0) lo.bytes = 0;  // nothing is scanned: no workspace
+  if (lo.bytes > 0 && (!ws || ws_bytes < lo.bytes)) return SSM_ERR_WORKSPACE;
   const Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
                       rng(B, s->bc * s->elem),  rng(C, s->bc * s->elem),      rng(D, D ? ED * 4 : 0),
                       rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem)};
@@ -709,6 +714,14 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                               workspace, workspace_bytes, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.seq == 0) {
+    // an empty output: every gradient is zero (dB and dC too when there are
+    // time steps but no channels)
+    const bool ok = fill_async(dA, nullptr, ED * N * 4, st) && fill_async(dD, nullptr, ED * 4, st) &&
+                    fill_async(dh0, nullptr, s.state * 4, st) && fill_async(dB, nullptr, s.bc * s.elem, st) &&
+                    fill_async(dC, nullptr, s.bc * s.elem, st);
+    return ok ? SSM_OK : SSM_ERR_LAUNCH;
+  }
   if (dtype == SSM_F32)
     return launch_bwd<float>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace, st);
   return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace,

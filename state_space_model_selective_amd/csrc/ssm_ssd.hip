@@ -797,12 +797,14 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
                  const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last,
                  const float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
                  int dtype) {
-  if (!x || !dt || !A || !B || !C || !y) return SSM_ERR_NULL;
-  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0) return SSM_ERR_DIM;
+  // Bs and L may be zero (empty tensors); H, P, G and N are positive
+  if (Bs < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0) return SSM_ERR_DIM;
   int64_t t, rows, seq, bc, state, hd;
-  if (!mul_ok(Bs, L, &rows) || !mul_ok(rows, H, &hd) || !mul_ok(hd, P, &seq) || !mul_ok(rows, G, &t) ||
-      !mul_ok(t, N, &bc) || !mul_ok(Bs, H, &t) || !mul_ok(t, P, &t) || !mul_ok(t, N, &state))
+  if (!mul_nn(Bs, L, &rows) || !mul_nn(rows, H, &hd) || !mul_nn(hd, P, &seq) || !mul_nn(rows, G, &t) ||
+      !mul_nn(t, N, &bc) || !mul_nn(Bs, H, &t) || !mul_nn(t, P, &t) || !mul_nn(t, N, &state))
     return SSM_ERR_DIM;
+  // a buffer with no elements may be NULL
+  if (!A || (seq > 0 && (!x || !dt || !y || !B || !C))) return SSM_ERR_NULL;
   if (seq > INT64_MAX / 8 || bc > INT64_MAX / 8 || state > INT64_MAX / 8) return SSM_ERR_DIM;
   if (H % G != 0) return SSM_ERR_DIM;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
@@ -887,6 +889,14 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
+// An empty batch or sequence: nothing to scan. Over zero steps the forward
+// state stays where it entered (h_last = h0, or zero); the reverse state is
+// zero.
+int ssd_empty(const float* h0, float* h_last, float* g_first, int64_t state, hipStream_t stream) {
+  const bool ok = fill_async(h_last, h0, state * 4, stream) && fill_async(g_first, nullptr, state * 4, stream);
+  return ok ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
@@ -896,6 +906,7 @@ extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const 
   const int rc = ssd_validate(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (Bs == 0 || L == 0) return ssd_empty(h0, h_last, nullptr, Bs * H * P * N, st);
   if (dtype == SSM_F32)
     return launch_ssd<float>(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
   return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
@@ -914,6 +925,7 @@ extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, 
   const int rc = ssd_validate(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (Bs == 0 || L == 0) return ssd_empty(h0, h_last, g_first, Bs * H * P * N, st);
   if (dtype == SSM_F32)
     return launch_ssd<float>(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, static_cast<float*>(y), true, Bs, L, H,
                              G, N, st);

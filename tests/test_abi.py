@@ -66,11 +66,33 @@ def test_null_pointer(name):
     assert bidir(**{name: None}) == ssm.SSM_ERR_NULL
 
 
-@pytest.mark.parametrize("dim", ["Bs", "L", "ED", "N"])
-@pytest.mark.parametrize("val", [0, -1])
+@pytest.mark.parametrize("dim,val", [("Bs", -1), ("L", -1), ("ED", -1), ("N", 0), ("N", -1)])
 def test_bad_dimension(dim, val):
     assert fwd(**{dim: val}) == ssm.SSM_ERR_DIM
     assert bidir(**{dim: val}) == ssm.SSM_ERR_DIM
+
+
+# Empty inputs are valid. The calls below have nothing to write (no final
+# state requested, or no channels), so they return before any HIP call, and
+# every buffer without elements may be NULL. (Empty calls that do write --
+# h_last = h0, zero gradients -- are GPU tests.)
+E_NULL = dict(x=None, delta=None, B=None, C=None, D=None, y=None, h=None, h0=None)
+
+
+# (with ED = 0, B and C -- (Bs, L, N) -- still have elements and stay given)
+@pytest.mark.parametrize("sizes", [dict(Bs=0), dict(ED=0, A=None, B=P[3], C=P[4]), dict(Bs=0, L=0, ED=0, A=None)])
+def test_empty_inputs_are_valid(sizes):
+    assert fwd(**dict(E_NULL, **sizes)) == ssm.SSM_OK
+    assert bidir(**dict(E_NULL, g=None, **sizes)) == ssm.SSM_OK
+    for bi in (0, 1):
+        assert ssm.ssm_scan_workspace_bytes(sizes.get("Bs", 2), sizes.get("L", 64), sizes.get("ED", 64), 16,
+                                            ssm.SSM_BF16, bi) == 0
+
+
+def test_empty_sequence_without_states_is_valid():
+    # L = 0 with A given: no output, nothing requested
+    assert fwd(**dict(E_NULL, L=0)) == ssm.SSM_OK
+    assert bidir(**dict(E_NULL, L=0, g=None)) == ssm.SSM_OK
 
 
 def test_size_overflow():
@@ -171,8 +193,16 @@ def test_bwd_optional_pointers_may_be_null():
     assert bwd(D=None, h0=None, dD=None, dh0=None, ws=P[15] + 4) == ssm.SSM_ERR_UNSUPPORTED
 
 
+def test_bwd_empty_inputs_are_valid():
+    # no batch rows and no channels: no gradient has an element
+    none = {n: None for n in BWD_PTRS}
+    assert bwd(**dict(none, Bs=0, ED=0, ws_bytes=0)) == ssm.SSM_OK
+    assert ssm.ssm_scan_bwd_workspace_bytes(2, 0, 64, 16, ssm.SSM_F32) == 0
+    assert ssm.ssm_scan_bwd_workspace_bytes(2, 64, 0, 16, ssm.SSM_BF16) == 0
+
+
 def test_bwd_validation():
-    assert bwd(L=0) == ssm.SSM_ERR_DIM
+    assert bwd(L=-1) == ssm.SSM_ERR_DIM
     assert bwd(N=8) == ssm.SSM_ERR_UNSUPPORTED
     assert bwd(dtype=3) == ssm.SSM_ERR_UNSUPPORTED
     assert bwd(dB=P[11] + 4) == ssm.SSM_ERR_UNSUPPORTED
@@ -203,8 +233,17 @@ def test_ssd_null_pointer(name):
     assert ssd(**{name: None}) == ssm.SSM_ERR_NULL
 
 
+def test_ssd_empty_inputs_are_valid():
+    none = dict(x=None, dt=None, B=None, C=None, D=None, h0=None, y=None, h=None)
+    assert ssd(**dict(none, L=0)) == ssm.SSM_OK
+    assert ssd(**dict(none, Bs=0)) == ssm.SSM_OK
+    assert ssd(**dict(none, L=0, A=None)) == ssm.SSM_ERR_NULL   # A (H) is never empty
+    assert ssd_bidir(**dict(none, g=None, ws=None, ws_bytes=0, L=0)) == ssm.SSM_OK
+
+
 def test_ssd_validation():
-    assert ssd(L=0) == ssm.SSM_ERR_DIM
+    assert ssd(L=-1) == ssm.SSM_ERR_DIM
+    assert ssd(H=0) == ssm.SSM_ERR_DIM
     assert ssd(H=3, G=2) == ssm.SSM_ERR_DIM          # heads not a multiple of groups
     assert ssd(P=32) == ssm.SSM_ERR_UNSUPPORTED
     assert ssd(N=16) == ssm.SSM_ERR_UNSUPPORTED
@@ -244,7 +283,7 @@ def test_ssd_bidir_null_pointer(name):
 
 def test_ssd_bidir_validation():
     need = ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16)
-    assert ssd_bidir(L=0) == ssm.SSM_ERR_DIM
+    assert ssd_bidir(L=-1) == ssm.SSM_ERR_DIM
     assert ssd_bidir(N=96) == ssm.SSM_ERR_UNSUPPORTED
     assert ssd_bidir(ws=None) == ssm.SSM_ERR_WORKSPACE
     assert ssd_bidir(ws_bytes=need - 1) == ssm.SSM_ERR_WORKSPACE

@@ -78,3 +78,17 @@ def test_repeatable_bits():
 def test_training_shape_full():
     # the forward training shape (Bs 8, L 1024, ED 1536, N 16), every gradient compared in full
     check(8, 1024, 1536, seed=11, h0=True)
+
+
+@pytest.mark.parametrize("Bs,L,ED", [(2, 0, 48), (0, 17, 48), (2, 17, 0)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_of_empty_inputs(Bs, L, ED, dtype):
+    """An empty output has zero gradients everywhere (dA, dD, dh0; dB and dC
+    when there are steps but no channels), as the oracle gives."""
+    log("backward empty case Bs=%d L=%d ED=%d dtype=%s" % (Bs, L, ED, dtype))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=42)
+    dy = synth.make_output_grad(Bs, L, ED, dtype, seed=42)
+    h0 = synth.normal(42, 9, (Bs, ED, 16))
+    got = run_gpu_bwd(inp, dy, h0=h0, want_dh0=True)
+    ref = oracle.scan_bwd(**inp, dy=dy, h0=h0)
+    assert_grads_close(got, ref, dtype)

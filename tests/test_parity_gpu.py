@@ -216,3 +216,25 @@ def test_options_each_alone():
         y_ref, h_ref, _ = oracle.scan(**inp2, want_h_last=True, **one)
         assert_close("y", y, y_ref, TOL["f32"])
         assert_close("h_last", h, h_ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("Bs,L,ED", [(2, 0, 48), (0, 17, 48), (2, 17, 0), (3, 0, 21)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_inputs(Bs, L, ED, dtype):
+    """Zero batch rows, steps or channels: nothing is scanned; over an empty
+    sequence the forward state stays h0 (zero without it) and the reverse
+    state is zero, as the oracle gives."""
+    log("empty case Bs=%d L=%d ED=%d dtype=%s" % (Bs, L, ED, dtype))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=41)
+    h0 = (0.5 * synth.normal(41, 9, (Bs, ED, 16))).astype(np.float32)
+    for with_h0 in (False, True):
+        h0v = h0 if with_h0 else None
+        y, h, _ = run_gpu(inp, want_h=True, h0=h0v)
+        y_ref, h_ref, _ = oracle.scan(**inp, h0=h0v, want_h_last=True)
+        assert_close("y", y, y_ref, TOL[dtype])
+        assert_close("h_last", h, h_ref, TOL["f32"])
+        y, h, g = run_gpu(inp, bidir=True, want_h=True, want_g=True, h0=h0v)
+        y_ref, h_ref, g_ref = oracle.scan(**inp, h0=h0v, bidir=True, want_h_last=True, want_g_first=True)
+        assert_close("y bidir", y, y_ref, TOL[dtype])
+        assert_close("h_last bidir", h, h_ref, TOL["f32"])
+        assert_close("g_first", g, g_ref, TOL["f32"])

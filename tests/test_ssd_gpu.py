@@ -182,3 +182,22 @@ def test_options_one_at_a_time(which):
               gate=which == "gate")
     check_options(2, 70, 4, 1, 128, "bf16" if which in ("bias", "gate") else "f32", seed=63, **kw)
 
+
+@pytest.mark.parametrize("Bs,L", [(2, 0), (0, 40)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_inputs(Bs, L, dtype):
+    """No batch rows or no steps: nothing is scanned; the forward state stays
+    h0 and the reverse state is zero, as the oracle gives."""
+    log("ssd empty case Bs=%d L=%d dtype=%s" % (Bs, L, dtype))
+    H, P, G, N = 4, 64, 1, 64
+    inp = synth.make_ssd_inputs(Bs, L, H, P, G, N, dtype, seed=43)
+    h0 = (0.5 * synth.normal(43, 9, (Bs, H, P, N))).astype(np.float32)
+    y, h = run_gpu_ssd(inp, h0=h0, want_h=True)
+    y_ref, h_ref, _ = oracle.ssd(**inp, h0=h0, want_h_last=True)
+    assert_close("y", y, y_ref, TOL[dtype])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+    y, h, g = run_gpu_ssd(inp, h0=h0, want_h=True, bidir=True, want_g=True)
+    y_ref, h_ref, g_ref = oracle.ssd(**inp, h0=h0, bidir=True, want_h_last=True, want_g_first=True)
+    assert_close("y bidir", y, y_ref, TOL[dtype])
+    assert_close("h_last bidir", h, h_ref, TOL["f32"])
+    assert_close("g_first", g, g_ref, TOL["f32"])
