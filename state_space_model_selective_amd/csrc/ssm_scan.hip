@@ -105,6 +105,7 @@ struct ScanArgs {
   int ngroups;     // channel groups per batch row
   int nblocks;
   int remap;       // spread neighbouring channel groups over one XCD
+  int rot_ncu;     // compute units, when every workgroup is resident at once; else 0 (no priority rotation)
   // split sequence (nchunks > 1)
   int nchunks;
   int64_t chunk_len;    // multiple of the round length
@@ -455,6 +456,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
     for (int64_t r = 0; r < rounds; ++r) {
       Tile<RT, GATE>& cur = tile[r & 1];
       Tile<RT, GATE>& nxt = tile[(r + 1) & 1];
+      rotate_priority(r, p.rot_ncu);
       if (r + 1 < rounds) st.template prefetch<STAGE_SCAN>(p, r + 1);
       // output of round r-1, whose input tile stays intact until this round's commit
       if (r >= 1) st.template store_out<STAGE_SCAN>(p, r - 1, nxt, out);
@@ -847,6 +849,7 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.ngroups = static_cast<int>(ngroups);
   a.nblocks = static_cast<int>(nblk);
   a.remap = (nblk % 8 == 0) ? 1 : 0;
+  a.rot_ncu = rotation_cus(nblk);
   a.nchunks = static_cast<int>(sp.nchunks);
   a.chunk_len = sp.chunk_len;
   a.hdr = nullptr;

@@ -70,6 +70,7 @@ struct BwdArgs {
   int ngroups;
   int nblocks;
   int remap;
+  int rot_ncu;  // compute units, when every workgroup is resident at once; else 0 (no priority rotation)
 };
 
 template <int RT>
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     st.template commit<false>(tile[0]);
     __syncthreads();
     for (int64_t r = 0; r + 1 < R; ++r) {
+      rotate_priority(r, p.rot_ncu);
       BwdTile<RT>& cur = tile[r & 1];
       BwdTile<RT>& nxt = tile[(r + 1) & 1];
       if (r + 2 < R) st.template prefetch<false>(p, r + 1);
@@ -341,6 +343,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   st.template commit<true>(tile[(R - 1) & 1]);
   __syncthreads();
   for (int64_t r = R - 1; r >= 0; --r) {
+    rotate_priority(r, p.rot_ncu);
     BwdTile<RT>& cur = tile[r & 1];
     BwdTile<RT>& nxt = tile[(r + 1) & 1];  // round r-1 has the other parity
     if (r >= 1) st.template prefetch<true>(p, r - 1);
@@ -678,6 +681,7 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.ngroups = static_cast<int>(lo.ngroups);
   a.nblocks = static_cast<int>(nblk);
   a.remap = (nblk % 8 == 0) ? 1 : 0;
+  a.rot_ncu = rotation_cus(nblk);
 
   const size_t lds = sizeof(BwdTile<kBRT>) * 2 + sizeof(ColSums<kBRT>) + sizeof(BwdFold<kBSEG>) + 16;
   const size_t dyn = spread_lds(nblk, lds, 16 / kBSEG);
