@@ -132,14 +132,30 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     return y, h, g
 
 
-def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, nthreads=None):
+def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, bidir=False, nthreads=None):
     """Gradients of L = sum(dy * y) for the forward scan (no options), in fp64.
 
     Same input conventions as scan(); dy has y's shape and x's dtype.
     Returns a dict with dx, ddelta (Bs, L, ED), dA (ED, N), dB, dC (Bs, L, N),
     dD (ED,) and dh0 (Bs, ED, N) (the same with or without h0: y is affine in
     the initial state).
+
+    bidir: the gradients of the bidirectional scan, whose output is the
+    forward scan (with D x and h0) plus the reverse-time scan, i.e. the
+    forward scan of the time-flipped inputs from a zero state without D,
+    flipped back ("Some questions of Bi-Mamba2 and Hydra", the author's first
+    reply). Its gradient is the sum of the two scans' gradients, the reverse
+    one taken on flipped copies and flipped back; D and h0 enter the forward
+    scan only.
     """
+    if bidir:
+        fwd = scan_bwd(x, delta, A, B, C, D, dy, h0=h0, nthreads=nthreads)
+        flip = lambda a: np.ascontiguousarray(np.asarray(a)[:, ::-1])
+        rev = scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), None, flip(dy), nthreads=nthreads)
+        for k in ("dx", "ddelta", "dB", "dC"):
+            fwd[k] = fwd[k] + rev[k][:, ::-1]
+        fwd["dA"] = fwd["dA"] + rev["dA"]
+        return fwd
     x = np.ascontiguousarray(x)
     delta = np.ascontiguousarray(delta)
     B = np.ascontiguousarray(B)

@@ -206,3 +206,52 @@ def test_backward_of_empty_inputs():
     assert g["dA"].shape == (0, 16) and g["dD"].shape == (0,)
     for k in ("dB", "dC"):
         assert g[k].shape == (2, 7, 16) and np.array_equal(g[k], np.zeros((2, 7, 16))), k
+
+
+def bidir_loss(inp, dy, h0=None):
+    y, _, _ = oracle.scan(**inp, h0=h0, bidir=True)
+    return float(np.sum(dy.astype(np.float64) * y))
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "h0"])
+def test_bidirectional_backward_matches_finite_differences(name):
+    # central differences of the (pinned) bidirectional forward oracle
+    Bs, L, ED, N = 2, 11, 3, 4
+    inp, dy, h0 = inputs(Bs, L, ED, N, seed=4, h0=True)
+    g = oracle.scan_bwd(**inp, dy=dy, h0=h0, bidir=True)[GRAD_OF[name]]
+    shape = h0.shape if name == "h0" else inp[name].shape
+    rng = np.random.default_rng(6)
+    src = h0 if name == "h0" else inp[name]
+    for _ in range(10):
+        idx = tuple(int(rng.integers(0, s)) for s in shape)
+        v = float(src[idx])
+        st = 2.0 ** -11 * max(1.0, abs(v))  # (two directions: more curvature than the forward scan)
+        up, dn = np.float32(v + st), np.float32(v - st)
+        vals = []
+        for w in (up, dn):
+            arr = src.copy()
+            arr[idx] = w
+            vals.append(bidir_loss(inp, dy, arr) if name == "h0" else bidir_loss(dict(inp, **{name: arr}), dy, h0))
+        want = (vals[0] - vals[1]) / (float(up) - float(dn))
+        assert abs(g[idx] - want) <= 1e-5 * (1.0 + abs(want)), (name, idx, g[idx], want)
+
+
+def test_bidirectional_backward_identities():
+    # y is linear in x (h0 = 0): <dx, x> = <dy, y>; y - D x is linear in C:
+    # <dC, C> = <dy, y - D x>; the time flip of every input and of dy maps the
+    # bidirectional scan to itself up to which direction carries h0, so with
+    # h0 = 0 the gradients flip with the inputs
+    inp, dy, _ = inputs(2, 23, 5, 16, seed=8)
+    g = oracle.scan_bwd(**inp, dy=dy, bidir=True)
+    y, _, _ = oracle.scan(**inp, bidir=True)
+    d64 = dy.astype(np.float64)
+    assert abs(np.sum(g["dx"] * inp["x"]) - np.sum(d64 * y)) <= 1e-9 * np.sum(np.abs(d64 * y))
+    dx_ = inp["D"].astype(np.float64)[None, None, :] * inp["x"]
+    assert abs(np.sum(g["dC"] * inp["C"]) - np.sum(d64 * (y - dx_))) <= 1e-9 * np.sum(np.abs(d64 * y))
+    flip = lambda a: np.ascontiguousarray(a[:, ::-1])
+    fl = {k: (flip(v) if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    gf = oracle.scan_bwd(**fl, dy=flip(dy), bidir=True)
+    for k in ("dx", "ddelta", "dB", "dC"):
+        assert np.allclose(gf[k][:, ::-1], g[k], rtol=1e-10, atol=1e-12), k
+    for k in ("dA", "dD"):
+        assert np.allclose(gf[k], g[k], rtol=1e-10, atol=1e-12), k
