@@ -156,7 +156,7 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
  *   dA[e,n]  = sum_{b,t} delta_t g_t a_t h_{t-1},   dD[e] = sum_{b,t} dy_t x_t
  *   dh0      = a_0 g_0
  * Step-size options and the gate are not covered (the forward must have run
- * without them); neither is the bidirectional scan.
+ * without them); the bidirectional scan has ssm_scan_bidir_bwd below.
  *   x, delta, A, B, C, D, h0 : as ssm_scan_fwd (D and h0 may be NULL)
  *   dy      : (Bs, L, ED) of dtype         -- dL/dy
  *   dx, ddelta : (Bs, L, ED) of dtype      -- written in full
@@ -177,6 +177,30 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
                  float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of the bidirectional scan: the gradients of L = sum(dy * y)
+ * for y = ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, opts = NULL), the sum
+ * of the forward scan (with D x and h0) and the reverse-time scan (from a
+ * zero state, shared weights) of "Some questions of Bi-Mamba2 and Hydra" (the
+ * author's first reply). Its gradient is the sum of the two scans' gradients:
+ * the reverse scan's adjoint runs in increasing time, g'_t = dy_t C_t +
+ * a_{t-1} g'_{t-1}, with the terms of ssm_scan_bwd at the same (b, t, e); D
+ * and h0 enter the forward scan only. The inputs are read in place (no
+ * flipped copy): two passes of the backward kernels, the second mapping
+ * every step t to time L-1-t and adding its dx and ddelta to the first's
+ * (kept in float32 in the workspace for bfloat16 outputs, so that they are
+ * rounded once); dB, dC and dA sum both passes' partials in a fixed order.
+ * Arguments, outputs and conventions as ssm_scan_bwd; the workspace is
+ * ssm_scan_bidir_bwd_workspace_bytes() bytes (both passes' partial sums and,
+ * for bfloat16, two float32 values per element of x).
+ */
+size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype);
+
+int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB,
+                       void* dC, float* dD, float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Multi-head (Mamba-2 / SSD) selective scan, in the layout of the chunked

@@ -71,6 +71,14 @@ struct BwdArgs {
   int nblocks;
   int remap;
   int rot_ncu;  // compute units, when every workgroup is resident at once; else 0 (no priority rotation)
+  // bidirectional backward: the first (forward-time) launch may write dx and
+  // ddelta as float32 partials (part_dx, part_dd) instead of the outputs; the
+  // second (reverse-time, REV) launch adds float32 partials (acc_dx, acc_dd:
+  // those, or the float32 outputs themselves) before its one rounding
+  float* part_dx;
+  float* part_dd;
+  const float* acc_dx;
+  const float* acc_dd;
 };
 
 template <int RT>
@@ -138,7 +146,10 @@ __device__ __forceinline__ void add_c_dy(float (&gv)[4], float cq, float dyv) {
 
 // Staging: one task per thread. Threads 0 .. 4 RT - 1 own a (row, 4-channel
 // chunk) of x / delta / dy, the others a (row, 4-state chunk) of B / C.
-template <typename T, int RT, bool VEC>
+// REV: the reverse-time scan of the bidirectional form. Virtual step t of the
+// sweeps is time L - 1 - t: every load and store maps the time, nothing else
+// changes (the inputs are read in place, no flipped copy).
+template <typename T, int RT, bool VEC, bool REV>
 struct BwdStager {
   int row, chk;
   bool is_xd, chunk_ok, row_ok;
@@ -158,8 +169,9 @@ struct BwdStager {
   // global -> registers for round rr; WITH_ADJ also loads dy and C
   template <bool WITH_ADJ>
   __device__ __forceinline__ void prefetch(const BwdArgs<T>& p, int64_t rr) {
-    const int64_t t = rr * RT + row;
-    row_ok = t < L;
+    const int64_t tv = rr * RT + row;
+    row_ok = tv < L;
+    const int64_t t = REV ? L - 1 - tv : tv;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, cc = a;
     if (row_ok && chunk_ok) {
       if (!is_xd) {
@@ -190,22 +202,43 @@ struct BwdStager {
   // dx and ddelta of round rr (written into the x and dy slots of its tile by
   // the adjoint replay) -> global
   __device__ __forceinline__ void store_grads(const BwdArgs<T>& p, const BwdTile<RT>& tl, int64_t rr) const {
-    const int64_t t = rr * RT + row;
-    if (!is_xd || t >= L || !chunk_ok) return;
+    const int64_t tv = rr * RT + row;
+    if (!is_xd || tv >= L || !chunk_ok) return;
+    const int64_t t = REV ? L - 1 - tv : tv;
     const int c4 = 4 * chk;
-    const float4 gx = *reinterpret_cast<const float4*>(&tl.xv[row][c4]);
-    const float4 gd = *reinterpret_cast<const float4*>(&tl.dy[row][c4]);
+    float4 gx = *reinterpret_cast<const float4*>(&tl.xv[row][c4]);
+    float4 gd = *reinterpret_cast<const float4*>(&tl.dy[row][c4]);
     const int64_t ce = e0 + c4, off = (b * L + t) * ED + ce;
     if (VEC) {
-      Vec4<T>::store(p.dx + off, gx);
-      Vec4<T>::store(p.ddl + off, gd);
+      if (REV && p.acc_dx) {
+        const float4 ax = *reinterpret_cast<const float4*>(p.acc_dx + off);
+        const float4 ad = *reinterpret_cast<const float4*>(p.acc_dd + off);
+        gx = make_float4(gx.x + ax.x, gx.y + ax.y, gx.z + ax.z, gx.w + ax.w);
+        gd = make_float4(gd.x + ad.x, gd.y + ad.y, gd.z + ad.z, gd.w + ad.w);
+      }
+      if (p.part_dx) {
+        *reinterpret_cast<float4*>(p.part_dx + off) = gx;
+        *reinterpret_cast<float4*>(p.part_dd + off) = gd;
+      } else {
+        Vec4<T>::store(p.dx + off, gx);
+        Vec4<T>::store(p.ddl + off, gd);
+      }
     } else {
-      const float vx[4] = {gx.x, gx.y, gx.z, gx.w}, vd[4] = {gd.x, gd.y, gd.z, gd.w};
+      float vx[4] = {gx.x, gx.y, gx.z, gx.w}, vd[4] = {gd.x, gd.y, gd.z, gd.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (ce + k < ED) {
-          p.dx[off + k] = from_f32<T>(vx[k]);
-          p.ddl[off + k] = from_f32<T>(vd[k]);
+          if (REV && p.acc_dx) {
+            vx[k] += p.acc_dx[off + k];
+            vd[k] += p.acc_dd[off + k];
+          }
+          if (p.part_dx) {
+            p.part_dx[off + k] = vx[k];
+            p.part_dd[off + k] = vd[k];
+          } else {
+            p.dx[off + k] = from_f32<T>(vx[k]);
+            p.ddl[off + k] = from_f32<T>(vd[k]);
+          }
         }
     }
   }
@@ -227,12 +260,13 @@ struct BwdStager {
 };
 
 // dB / dC partials of round rr (their column sums are in cs) -> workspace
-template <typename T, int RT>
+template <typename T, int RT, bool REV>
 __device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums<RT>& cs, int tid, int64_t b,
                                               int64_t grp, int64_t rr) {
   const int tt = tid >> 3, qq = (tid >> 2) & 1, n4 = 4 * (tid & 3);
-  const int64_t t = rr * RT + tt;
-  if (t >= p.L) return;
+  const int64_t tv = rr * RT + tt;
+  if (tv >= p.L) return;
+  const int64_t t = REV ? p.L - 1 - tv : tv;
   float4 s = *reinterpret_cast<const float4*>(&cs.v[tt][0][qq][n4]);
 #pragma unroll
   for (int r = 1; r < 4; ++r) {
@@ -243,7 +277,7 @@ __device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums
   *reinterpret_cast<float4*>(dst + ((grp * p.Bs + b) * p.L + t) * 16 + n4) = s;
 }
 
-template <typename T, int SEG, int TS, bool VEC>
+template <typename T, int SEG, int TS, bool VEC, bool REV>
 __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
     const BwdArgs<T> p) {
   constexpr int RT = SEG * TS;
@@ -281,7 +315,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   const float Dv = (p.D && ch_ok) ? p.D[e] : 0.f;
 
-  BwdStager<T, RT, VEC> st;
+  BwdStager<T, RT, VEC, REV> st;
   st.init(tid, b, e0, ED, L);
   // checkpoint of round rr for this lane's 4 states
   auto ck = [&](int64_t rr) { return p.ckpt + ((b * R + rr) * p.EDp + e) * 16 + 4 * g; };
@@ -348,7 +382,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     BwdTile<RT>& nxt = tile[(r + 1) & 1];  // round r-1 has the other parity
     if (r >= 1) st.template prefetch<true>(p, r - 1);
     if (r + 1 < R) {
-      store_colsums(p, cs, tid, b, grp, r + 1);
+      store_colsums<T, RT, REV>(p, cs, tid, b, grp, r + 1);
       st.store_grads(p, nxt, r + 1);  // dx, ddelta of round r+1 (tile of the same parity)
     }
 
@@ -478,7 +512,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     if (r >= 1) st.template commit<true>(nxt);
     __syncthreads();
   }
-  store_colsums(p, cs, tid, b, grp, 0);
+  store_colsums<T, RT, REV>(p, cs, tid, b, grp, 0);
   st.store_grads(p, tile[0], 0);
 
   // ---- per-workgroup results ----------------------------------------------
@@ -538,19 +572,21 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   }
 }
 
-// dA, dD: sum of the batch rows' partials, in row order.
+// dA, dD: sum of the batch rows' partials, in row order (the bidirectional
+// backward has 2 Bs rows of dA partials: the forward-time scan's, then the
+// reverse-time scan's; dD comes from the forward-time scan alone).
 __global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double* __restrict__ pD, float* dA,
-                                     float* dD, int64_t Bs, int64_t ED, int64_t EDp) {
+                                     float* dD, int64_t rowsA, int64_t rowsD, int64_t ED, int64_t EDp) {
   const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (i < ED * 16) {
     const int64_t e = i >> 4, n = i & 15;
     double s = 0.0;
-    for (int64_t b = 0; b < Bs; ++b) s += pA[(b * EDp + e) * 16 + n];
+    for (int64_t b = 0; b < rowsA; ++b) s += pA[(b * EDp + e) * 16 + n];
     dA[i] = static_cast<float>(s);
   } else if (dD && i < ED * 17) {
     const int64_t e = i - ED * 16;
     double s = 0.0;
-    for (int64_t b = 0; b < Bs; ++b) s += pD[b * EDp + e];
+    for (int64_t b = 0; b < rowsD; ++b) s += pD[b * EDp + e];
     dD[e] = static_cast<float>(s);
   }
 }
@@ -560,30 +596,39 @@ __global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double
 // ---------------------------------------------------------------------------
 struct BwdLayout {
   int64_t rounds, ngroups, EDp;
-  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, bytes;
+  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, part_off, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo) {
+// Workspace: round checkpoints, the dB / dC partials of every channel group,
+// the dA / dD partials of every batch row; the bidirectional backward keeps
+// both directions' partials (dirs = 2) and, for bf16 outputs, the forward-time
+// scan's dx and ddelta as float32 (part_f32).
+bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo, bool bidir = false, bool part_f32 = false) {
+  const int64_t dirs = bidir ? 2 : 1;
   lo->rounds = (L + kBRT - 1) / kBRT;
   lo->ngroups = (ED + 15) / 16;
   lo->EDp = lo->ngroups * 16;
   // every count below is checked against overflow of size_t arithmetic
   const double total = 4.0 * (static_cast<double>(Bs) * lo->rounds * lo->EDp * 16 +
-                              2.0 * lo->ngroups * Bs * L * 16 + 2.0 * Bs * lo->EDp * 17) + 5 * 256.0;
+                              2.0 * dirs * lo->ngroups * Bs * L * 16 + 2.0 * dirs * Bs * lo->EDp * 17 +
+                              (part_f32 ? 2.0 * Bs * L * ED : 0.0)) +
+                       6 * 256.0;
   if (total > 9.0e18) return false;
   size_t off = 0;
   lo->ckpt_off = off;
   off = align256(off + static_cast<size_t>(Bs * lo->rounds * lo->EDp * 16) * 4);
   lo->pB_off = off;
-  off = align256(off + static_cast<size_t>(lo->ngroups * Bs * L * 16) * 4);
+  off = align256(off + static_cast<size_t>(dirs * lo->ngroups * Bs * L * 16) * 4);
   lo->pC_off = off;
-  off = align256(off + static_cast<size_t>(lo->ngroups * Bs * L * 16) * 4);
+  off = align256(off + static_cast<size_t>(dirs * lo->ngroups * Bs * L * 16) * 4);
   lo->pA_off = off;
-  off = align256(off + static_cast<size_t>(Bs * lo->EDp * 16) * 8);
+  off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp * 16) * 8);
   lo->pD_off = off;
-  off = align256(off + static_cast<size_t>(Bs * lo->EDp) * 8);
+  off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp) * 8);
+  lo->part_off = off;
+  if (part_f32) off = align256(off + static_cast<size_t>(2 * Bs * L * ED) * 4);
   lo->bytes = off;
   return true;
 }
@@ -606,17 +651,19 @@ int bwd_check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, Bwd
   return SSM_OK;
 }
 
-size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
+size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, bool bidir) {
   BwdSizes s;
   BwdLayout lo;
-  if (bwd_check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || s.seq == 0 || !bwd_layout(Bs, L, ED, &lo)) return 0;
+  if (bwd_check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || s.seq == 0 ||
+      !bwd_layout(Bs, L, ED, &lo, bidir, bidir && dtype == SSM_BF16))
+    return 0;
   return lo.bytes;
 }
 
 int bwd_validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const void* dy, const void* dx, const void* ddelta, const float* dA, const void* dB,
                  const void* dC, const float* dD, const float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N,
-                 int dtype, const void* ws, size_t ws_bytes, BwdSizes* s) {
+                 int dtype, const void* ws, size_t ws_bytes, bool bidir, BwdSizes* s) {
   int rc = bwd_check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
   // a buffer with no elements may be NULL
@@ -627,7 +674,7 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   BwdLayout lo;
-  if (!bwd_layout(Bs, L, ED, &lo)) return SSM_ERR_DIM;
+  if (!bwd_layout(Bs, L, ED, &lo, bidir, bidir && dtype == SSM_BF16)) return SSM_ERR_DIM;
   if (s->seq == 0) lo.bytes = 0;  // nothing is scanned: no workspace
   if (lo.bytes > 0 && (!ws || ws_bytes < lo.bytes)) return SSM_ERR_WORKSPACE;
   const Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
@@ -647,12 +694,21 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
   return SSM_OK;
 }
 
+template <typename T, bool REV>
+void launch_bwd_kernel(const BwdArgs<T>& a, int64_t nblk, size_t dyn, bool vec, hipStream_t stream) {
+  if (vec)
+    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true, REV>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, false, REV>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+}
+
 template <typename T>
 int launch_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-               float* dh0, int64_t Bs, int64_t L, int64_t ED, void* ws, hipStream_t stream) {
+               float* dh0, int64_t Bs, int64_t L, int64_t ED, void* ws, bool bidir, hipStream_t stream) {
+  const bool part_f32 = bidir && !std::is_same<T, float>::value;
   BwdLayout lo;
-  bwd_layout(Bs, L, ED, &lo);
+  bwd_layout(Bs, L, ED, &lo, bidir, part_f32);
   const int64_t nblk = Bs * lo.ngroups;
   if (nblk > INT32_MAX / 2) return SSM_ERR_DIM;
   char* w = static_cast<char*>(ws);
@@ -682,40 +738,55 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.nblocks = static_cast<int>(nblk);
   a.remap = (nblk % 8 == 0) ? 1 : 0;
   a.rot_ncu = rotation_cus(nblk);
+  float* part = reinterpret_cast<float*>(w + lo.part_off);
+  a.part_dx = part_f32 ? part : nullptr;
+  a.part_dd = part_f32 ? part + Bs * L * ED : nullptr;
+  a.acc_dx = nullptr;
+  a.acc_dd = nullptr;
 
   const size_t lds = sizeof(BwdTile<kBRT>) * 2 + sizeof(ColSums<kBRT>) + sizeof(BwdFold<kBSEG>) + 16;
   const size_t dyn = spread_lds(nblk, lds, 16 / kBSEG);
-  if (ED % 4 == 0)
-    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
-  else
-    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, false>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  const bool vec = ED % 4 == 0;
+  launch_bwd_kernel<T, false>(a, nblk, dyn, vec, stream);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
+  if (bidir) {
+    // the reverse-time scan: zero state at t = L-1, no D, its own halves of
+    // the partials, dx and ddelta added to the forward-time scan's (in order
+    // on the stream) and rounded once
+    BwdArgs<T> r = a;
+    r.D = nullptr;
+    r.h0 = nullptr;
+    r.dh0 = nullptr;
+    r.pB = a.pB + lo.ngroups * Bs * L * 16;
+    r.pC = a.pC + lo.ngroups * Bs * L * 16;
+    r.pA = a.pA + Bs * lo.EDp * 16;
+    r.pD = a.pD + Bs * lo.EDp;
+    r.part_dx = nullptr;
+    r.part_dd = nullptr;
+    r.acc_dx = part_f32 ? a.part_dx : static_cast<const float*>(dx);
+    r.acc_dd = part_f32 ? a.part_dd : static_cast<const float*>(ddelta);
+    launch_bwd_kernel<T, true>(r, nblk, dyn, vec, stream);
+    if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
+  }
 
   const int64_t n4 = Bs * L * 4;  // float4s per dB (or dC)
   if ((2 * n4 + 63) / 64 > INT32_MAX) return SSM_ERR_DIM;
   hipLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3(static_cast<unsigned>((2 * n4 + 63) / 64)), dim3(256), 0,
-                     stream, a.pB, a.pC, static_cast<T*>(dB), static_cast<T*>(dC), n4, a.ngroups);
+                     stream, a.pB, a.pC, static_cast<T*>(dB), static_cast<T*>(dC), n4,
+                     static_cast<int>(bidir ? 2 * lo.ngroups : lo.ngroups));
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_reduce_ad_kernel, dim3(static_cast<unsigned>((ED * 17 + 255) / 256)), dim3(256), 0, stream,
-                     a.pA, a.pD, dA, dD, Bs, ED, lo.EDp);
+                     a.pA, a.pD, dA, dD, bidir ? 2 * Bs : Bs, Bs, ED, lo.EDp);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
-  return bwd_workspace_bytes(Bs, L, ED, N, dtype);
-}
-
-int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-                 float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+int run_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+            const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+            float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+            size_t workspace_bytes, void* stream, bool bidir) {
   BwdSizes s;
   const int rc = bwd_validate(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype,
-                              workspace, workspace_bytes, &s);
+                              workspace, workspace_bytes, bidir, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.seq == 0) {
@@ -727,9 +798,38 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
     return ok ? SSM_OK : SSM_ERR_LAUNCH;
   }
   if (dtype == SSM_F32)
-    return launch_bwd<float>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace, st);
+    return launch_bwd<float>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace,
+                             bidir, st);
   return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace,
-                              st);
+                              bidir, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
+  return bwd_workspace_bytes(Bs, L, ED, N, dtype, false);
+}
+
+size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
+  return bwd_workspace_bytes(Bs, L, ED, N, dtype, true);
+}
+
+int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                 float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return run_bwd(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype, workspace,
+                 workspace_bytes, stream, false);
+}
+
+int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB,
+                       void* dC, float* dD, float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype, workspace,
+                 workspace_bytes, stream, true);
 }
 
 }  // extern "C"

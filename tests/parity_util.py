@@ -103,8 +103,9 @@ def gather_channels(y, chans, ED):
     return y[b, :, e]
 
 
-def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None):
-    """ssm_scan_bwd on the GPU; every gradient as a float64 numpy array."""
+def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None, bidir=False):
+    """ssm_scan_bwd (bidir: ssm_scan_bidir_bwd) on the GPU; every gradient as
+    a float64 numpy array."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -120,8 +121,9 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
         out["dD"] = torch.full((ED,), float("nan"), dtype=torch.float32, device=dev)
     if want_dh0:
         out["dh0"] = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev)
-    res = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
-                           h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream)
+    fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
+    res = fn(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
+             h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream)
     torch.cuda.synchronize()
     return {k: y_to_numpy(v) for k, v in res.items()}
 

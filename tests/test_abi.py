@@ -315,3 +315,37 @@ def test_ssd_options_validation():
     ref, _ = opts(dt_bias=P[13], dt_softplus=1, dt_min=0.0, dt_max=1.0, z=P[14])
     assert ssd_bidir(opts=ref, ws=None) == ssm.SSM_ERR_WORKSPACE
 
+
+def bidir_bwd(**kw):
+    args = {n: P[i] for i, n in enumerate(BWD_PTRS)}
+    args.update(Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_BF16)
+    args["ws_bytes"] = ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
+    args.update(kw)
+    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BWD_PTRS[:15]], args["Bs"], args["L"], args["ED"],
+                                        args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bidir_bwd_workspace_size():
+    plain = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
+    both = ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
+    # both directions' dB / dC partials (4 groups x 2 x 64 x 16 each, twice)
+    # and the forward direction's float32 dx and ddelta
+    assert both >= plain + 4 * (2 * 4 * 2 * 64 * 16 + 2 * 2 * 64 * 64)
+    assert ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32) < both
+    assert ssm.ssm_scan_bidir_bwd_workspace_bytes(0, 64, 64, 16, ssm.SSM_BF16) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "dy", "dx", "ddelta", "dA", "dB", "dC"])
+def test_bidir_bwd_null_pointer(name):
+    assert bidir_bwd(**{name: None}) == ssm.SSM_ERR_NULL
+
+
+def test_bidir_bwd_validation():
+    plain = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
+    assert bidir_bwd(L=-1) == ssm.SSM_ERR_DIM
+    assert bidir_bwd(N=8) == ssm.SSM_ERR_UNSUPPORTED
+    assert bidir_bwd(ws=None) == ssm.SSM_ERR_WORKSPACE
+    assert bidir_bwd(ws_bytes=plain) == ssm.SSM_ERR_WORKSPACE   # the one-direction size is too small
+    assert bidir_bwd(dx=P[0]) == ssm.SSM_ERR_ALIAS
+    none = {n: None for n in BWD_PTRS}
+    assert bidir_bwd(**dict(none, Bs=0, ED=0, ws_bytes=0)) == ssm.SSM_OK

@@ -1,5 +1,6 @@
-"""GPU parity of the backward pass (ssm_scan_bwd) against the oracle's
-adjoint (oracle.scan_bwd) on the same seeded inputs."""
+"""GPU parity of the backward passes (ssm_scan_bwd, ssm_scan_bidir_bwd)
+against the oracle's adjoint (oracle.scan_bwd, bidir=False / True) on the
+same seeded inputs."""
 import numpy as np
 import pytest
 
@@ -10,14 +11,15 @@ from parity_util import assert_grads_close, degenerate_inputs, log, run_gpu_bwd
 pytestmark = pytest.mark.gpu
 
 
-def check(Bs, L, ED, dtype="f32", seed=0, h0=False, D_none=False, want_dD=True):
-    log("bwd case Bs=%d L=%d ED=%d dtype=%s seed=%d h0=%s D_none=%s" % (Bs, L, ED, dtype, seed, h0, D_none))
+def check(Bs, L, ED, dtype="f32", seed=0, h0=False, D_none=False, want_dD=True, bidir=False):
+    log("bwd case Bs=%d L=%d ED=%d dtype=%s seed=%d h0=%s D_none=%s bidir=%s" % (Bs, L, ED, dtype, seed, h0, D_none,
+                                                                               bidir))
     inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=seed)
     dy = synth.make_output_grad(Bs, L, ED, dtype, seed=seed)
     h = synth.normal(seed, 79, (Bs, ED, 16)) if h0 else None
-    got = run_gpu_bwd(inp, dy, h0=h, D_none=D_none, want_dD=want_dD, want_dh0=True)
+    got = run_gpu_bwd(inp, dy, h0=h, D_none=D_none, want_dD=want_dD, want_dh0=True, bidir=bidir)
     ref_inp = dict(inp, D=None) if D_none else inp
-    ref = oracle.scan_bwd(**ref_inp, dy=dy, h0=h)
+    ref = oracle.scan_bwd(**ref_inp, dy=dy, h0=h, bidir=bidir)
     assert_grads_close(got, ref, dtype)
     return got
 
@@ -92,3 +94,53 @@ def test_backward_of_empty_inputs(Bs, L, ED, dtype):
     got = run_gpu_bwd(inp, dy, h0=h0, want_dh0=True)
     ref = oracle.scan_bwd(**inp, dy=dy, h0=h0)
     assert_grads_close(got, ref, dtype)
+
+
+# ---- bidirectional backward -------------------------------------------------
+def test_bidir_page_shape():
+    check(2, 64, 64, bidir=True)
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 33, 200, 1009])
+def test_bidir_sequence_lengths(L):
+    check(2, L, 64, seed=L + 100, bidir=True)
+
+
+@pytest.mark.parametrize("ED", [20, 130])
+def test_bidir_channel_counts(ED):
+    check(2, 77, ED, seed=ED + 100, bidir=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bidir_initial_state_and_no_D(dtype):
+    check(2, 150, 64, dtype=dtype, seed=106, h0=True, bidir=True)
+    check(2, 70, 32, dtype=dtype, seed=107, D_none=True, bidir=True)
+
+
+def test_bidir_bf16():
+    check(2, 300, 96, dtype="bf16", seed=105, bidir=True)
+
+
+@pytest.mark.parametrize("case", ["no_decay", "full_decay", "growth", "mixed"])
+def test_bidir_degenerate_inputs(case):
+    log("bidir bwd degenerate case %s" % case)
+    inp = degenerate_inputs(case, L=150, ED=48)
+    dy = synth.make_output_grad(2, 150, 48, "f32", seed=15)
+    got = run_gpu_bwd(inp, dy, want_dD=True, want_dh0=True, bidir=True)
+    ref = oracle.scan_bwd(**inp, dy=dy, bidir=True)
+    assert_grads_close(got, ref, "f32")
+
+
+def test_bidir_repeatable_bits():
+    inp = synth.make_inputs(3, 257, 80, 16, "bf16", seed=110)
+    dy = synth.make_output_grad(3, 257, 80, "bf16", seed=110)
+    a = run_gpu_bwd(inp, dy, want_dh0=True, bidir=True)
+    b = run_gpu_bwd(inp, dy, want_dh0=True, bidir=True)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_bidir_training_shape_full():
+    # the bidirectional training shape of the forward (Bs 8, L 4096, ED 1536)
+    # at a quarter of the length, every gradient compared in full
+    check(8, 1024, 1536, seed=111, h0=True, bidir=True)
