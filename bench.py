@@ -37,6 +37,9 @@ SLOTS_PER_ELEMENT_BIDIR = 8.0
 # the adjoint with its terms (g FMA, k = a g, dC and dB products, sum g B,
 # q = g a h_{t-1} (2), sum A q, dA += delta q: 9)
 SLOTS_PER_ELEMENT_BWD = 14.0
+# bidirectional backward: both directions' 14, less the discretisation they
+# share (delta*A, exp, (delta x)*B: 4)
+SLOTS_PER_ELEMENT_BIDIR_BWD = 24.0
 
 
 def alg_bytes(w):
@@ -138,15 +141,16 @@ def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
         sub = {n: (v[:k] if v.ndim == 3 else v) for n, v in inp.items()}
         return sub, dy[:k]
 
+    bidir = bool(w["bidir"])
     sub, dys = rows(1)
     t0 = time.perf_counter()
-    ref = oracle.scan_bwd(**sub, dy=dys, nthreads=threads)
+    ref = oracle.scan_bwd(**sub, dy=dys, bidir=bidir, nthreads=threads)
     dt = max(time.perf_counter() - t0, 1e-6)
     k = int(min(Bs, max(1, budget_s / dt)))
     if k > 1:
         sub, dys = rows(k)
         t0 = time.perf_counter()
-        ref = oracle.scan_bwd(**sub, dy=dys, nthreads=threads)
+        ref = oracle.scan_bwd(**sub, dy=dys, bidir=bidir, nthreads=threads)
         dt = time.perf_counter() - t0
     E = k * w["L"] * w["ED"] * w["N"]
     sample = ("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))
@@ -364,7 +368,8 @@ def main():
             t["out"] = {"dx": torch.empty_like(t["x"]), "ddelta": torch.empty_like(t["x"]),
                         "dA": torch.empty_like(t["A"]), "dB": torch.empty_like(t["B"]),
                         "dC": torch.empty_like(t["C"]), "dD": torch.empty_like(t["D"])}
-            need = ssm.ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, dcode)
+            need = (ssm.ssm_scan_bidir_bwd_workspace_bytes if w["bidir"] else ssm.ssm_scan_bwd_workspace_bytes)(
+                Bs, L, ED, N, dcode)
         else:
             host_sets.append(inp if i == 0 else None)
             t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
@@ -377,7 +382,8 @@ def main():
 
     def step(t):
         if bwd:
-            ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
+            (ssm.ssm_scan_bidir_bwd if w["bidir"] else ssm.ssm_scan_bwd)(
+                             t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
                              workspace=t["ws"], stream=stream)
         elif w["bidir"]:
             ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], h_last=t["h"],
@@ -411,7 +417,10 @@ def main():
     kernel_elem_rate = E / avg_launch_s
     # bidirectional: the exp and the two multiplies are shared by both
     # directions; algorithmic cost 2 mul + exp + 2 x (state FMA + C FMA) = 8
-    slots = SLOTS_PER_ELEMENT_BWD if bwd else (SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT)
+    if bwd:
+        slots = SLOTS_PER_ELEMENT_BIDIR_BWD if w["bidir"] else SLOTS_PER_ELEMENT_BWD
+    else:
+        slots = SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT
     achieved_slots = kernel_elem_rate * slots
     src_hash = kernel_source_hash(args.workload)
     traffic = load_traffic(args.workload, src_hash)
@@ -469,8 +478,9 @@ def main():
             "frac": achieved_slots / VALU_SLOTS_PER_S,
             "traffic": traffic,
             "kernel_avg_us": avg_launch_s * 1e6,
-            "timed": ("whole backward step: the scan kernel and the two small kernels that add up the "
-                      "dB/dC and dA/dD partial sums") if bwd else "the scan kernel (one launch per step)",
+            "timed": (("whole backward step: the scan kernel (once per direction) and the two small kernels "
+                       "that add up the dB/dC and dA/dD partial sums") if bwd else
+                      "the scan kernel (one launch per step)"),
             "slots_per_element": slots,
         },
         "hbm": {

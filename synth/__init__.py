@@ -50,6 +50,9 @@ WORKLOADS = {
                                          bwd=True),
     "bwd_bf16_Bs4_L8192_ED5120_N16": dict(Bs=4, L=8192, ED=5120, N=16, dtype="bf16", bidir=False, h_last=False,
                                           bwd=True),
+    # backward pass of the bidirectional scan at its forward shape
+    "bwd_bidir_f32_Bs8_L4096_ED1536_N16": dict(Bs=8, L=4096, ED=1536, N=16, dtype="f32", bidir=True,
+                                               h_last=False, bwd=True),
 }
 
 # Multi-head (SSD) workloads: batch 32, seqlen 400, 8 heads is the shape the

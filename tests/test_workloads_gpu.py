@@ -60,8 +60,8 @@ def run_bwd_workload(name):
     log("backward workload %s" % name)
     inp = synth.workload_inputs(name, seed=0)
     dy = synth.make_output_grad(w["Bs"], w["L"], w["ED"], w["dtype"], seed=0)
-    got = run_gpu_bwd(inp, dy, want_dh0=True)
-    ref = oracle.scan_bwd(**inp, dy=dy)
+    got = run_gpu_bwd(inp, dy, want_dh0=True, bidir=w["bidir"])
+    ref = oracle.scan_bwd(**inp, dy=dy, bidir=w["bidir"])
     assert_grads_close(got, ref, w["dtype"])
 
 
@@ -71,3 +71,7 @@ def test_backward_fp32_8x1024x1536():
 
 def test_backward_bf16_4x8192x5120():
     run_bwd_workload("bwd_bf16_Bs4_L8192_ED5120_N16")
+
+
+def test_backward_bidirectional_8x4096x1536():
+    run_bwd_workload("bwd_bidir_f32_Bs8_L4096_ED1536_N16")
