@@ -104,3 +104,22 @@ def test_multi_head_bidirectional_options_graph():
     replay_check("multi-head bidirectional bf16 with options", lambda: ssm.ssm_ssd_bidir_fwd(
         t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=y, h_last=h, workspace=ws, dt_bias=bias,
         dt_softplus=True, dt_limit=(0.01, 0.5), z=z), [y, h])
+
+
+def test_bidirectional_backward_bf16_graph():
+    # two backward launches (the second adding to the first's float32 dx and
+    # ddelta in the workspace) and the reductions over both directions
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 2, 300, 64, 16
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(Bs, L, ED, N, "bf16", seed=74)
+    t = to_device(dict(inp, dy=synth.make_output_grad(Bs, L, ED, "bf16", seed=74)), dev)
+    out = {"dx": torch.empty_like(t["x"]), "ddelta": torch.empty_like(t["x"]), "dA": torch.empty_like(t["A"]),
+           "dB": torch.empty_like(t["B"]), "dC": torch.empty_like(t["B"]),
+           "dD": torch.empty((ED,), dtype=torch.float32, device=dev)}
+    need = ssm.ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, ssm.SSM_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    replay_check("bidirectional backward bf16", lambda: ssm.ssm_scan_bidir_bwd(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=out, workspace=ws),
+        [out[k] for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")])
