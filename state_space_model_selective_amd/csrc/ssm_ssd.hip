@@ -67,7 +67,19 @@ struct SsdArgs {
   float dt_min, dt_max;
   const T* z;
   int64_t L, H, G;
+  int nblocks;  // workgroups of the launch
 };
+
+// Workgroups are dealt to the 8 XCDs in turn (block i to XCD i mod 8). The
+// (batch row, head) of block i is taken so that each XCD gets consecutive
+// pairs, i.e. the heads of the same batch rows, which share B and C: those
+// then come from the XCD's own L2 instead of every XCD fetching every row's.
+// (Identity when the block count is not a multiple of 8.)
+__device__ __forceinline__ int64_t xcd_local_block(int nblocks) {
+  const int64_t blk = blockIdx.x;
+  if (nblocks % 8 != 0) return blk;
+  return (blk & 7) * (nblocks >> 3) + (blk >> 3);
+}
 
 // step size of the head whose bias (or null) is given, after the options
 template <typename T>
@@ -181,7 +193,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lk = lane >> 4;  // operand row / column and k index
-  const int64_t b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int64_t bh = xcd_local_block(p.nblocks);
+  const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.f;
@@ -609,7 +622,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lk = lane >> 4;
-  const int64_t b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int64_t bh = xcd_local_block(p.nblocks);
+  const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
   const float Dfwd = p.D ? p.D[h] : 0.f;
@@ -878,6 +892,7 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   a.L = L;
   a.H = H;
   a.G = G;
+  a.nblocks = static_cast<int>(Bs * H);
   const dim3 grid(static_cast<unsigned>(Bs * H)), block(64 * kWaves);
   if (bidir) {
     if (a.z) launch_ssd_kernel<T, true, true>(a, N, grid, block, stream);
