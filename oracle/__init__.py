@@ -46,7 +46,8 @@ def lib():
                                   vp, ctypes.c_int, dbl, dbl, vp,
                                   i64, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         L.oracle_scan.restype = ctypes.c_int
-        L.oracle_scan_bwd.argtypes = [ctypes.c_int] + [vp] * 8 + [i64] * 4 + [vp] * 7 + [ctypes.c_int]
+        L.oracle_scan_bwd.argtypes = ([ctypes.c_int] + [vp] * 8 + [ctypes.c_int, ctypes.c_double, ctypes.c_double] +
+                                      [vp] * 2 + [i64] * 4 + [vp] * 8 + [ctypes.c_int])
         L.oracle_scan_bwd.restype = ctypes.c_int
         L.oracle_ssd.argtypes = ([ctypes.c_int, ctypes.c_int] + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
                                  ctypes.c_double, vp] + [i64] * 6 + [vp] * 3 + [ctypes.c_int])
@@ -132,13 +133,21 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     return y, h, g
 
 
-def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, bidir=False, nthreads=None):
-    """Gradients of L = sum(dy * y) for the forward scan (no options), in fp64.
+def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, dt_bias=None, dt_softplus=False,
+             dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, nthreads=None):
+    """Gradients of L = sum(dy * y) for the forward scan, in fp64.
 
-    Same input conventions as scan(); dy has y's shape and x's dtype.
-    Returns a dict with dx, ddelta (Bs, L, ED), dA (ED, N), dB, dC (Bs, L, N),
+    Same input conventions as scan() (including the options dt_bias,
+    dt_softplus, dt_limit and the gate z); dy has y's shape and x's dtype.
+    Returns a dict with dx, ddelta (Bs, L, ED; ddelta is the gradient of the
+    raw step size, through the step-size map), dA (ED, N), dB, dC (Bs, L, N),
     dD (ED,) and dh0 (Bs, ED, N) (the same with or without h0: y is affine in
-    the initial state).
+    the initial state), and ddt_bias (ED,) when dt_bias is given, dz (like x)
+    when z is given.
+
+    With a gate, y' = y z sigmoid(z): the scan itself sees the output
+    gradient dy z sigmoid(z), and dz = dy y (d/dz of z sigmoid(z)) with y the
+    whole ungated output (both directions and D x), taken from scan().
 
     bidir: the gradients of the bidirectional scan, whose output is the
     forward scan (with D x and h0) plus the reverse-time scan, i.e. the
@@ -146,15 +155,21 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, bidir=False, nthrea
     flipped back ("Some questions of Bi-Mamba2 and Hydra", the author's first
     reply). Its gradient is the sum of the two scans' gradients, the reverse
     one taken on flipped copies and flipped back; D and h0 enter the forward
-    scan only.
+    scan only; the step-size map and the gate's factor apply to both.
     """
+    opts = dict(dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit)
     if bidir:
-        fwd = scan_bwd(x, delta, A, B, C, D, dy, h0=h0, nthreads=nthreads)
+        fwd = scan_bwd(x, delta, A, B, C, D, dy, h0=h0, z=z, nthreads=nthreads, **opts)
         flip = lambda a: np.ascontiguousarray(np.asarray(a)[:, ::-1])
-        rev = scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), None, flip(dy), nthreads=nthreads)
+        rev = scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), None, flip(dy),
+                       z=None if z is None else flip(z), nthreads=nthreads, **opts)
         for k in ("dx", "ddelta", "dB", "dC"):
             fwd[k] = fwd[k] + rev[k][:, ::-1]
         fwd["dA"] = fwd["dA"] + rev["dA"]
+        if dt_bias is not None:
+            fwd["ddt_bias"] = fwd["ddt_bias"] + rev["ddt_bias"]
+        if z is not None:
+            fwd["dz"] = _gate_grad(x, delta, A, B, C, D, dy, h0, z, True, nthreads, opts)
         return fwd
     x = np.ascontiguousarray(x)
     delta = np.ascontiguousarray(delta)
@@ -164,21 +179,47 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, bidir=False, nthrea
     A = np.ascontiguousarray(A, dtype=np.float32)
     D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    dtb = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float32)
+    zc = None if z is None else np.ascontiguousarray(z)
     dtype = BF16 if x.dtype == np.uint16 else F32
-    for t in (delta, B, C, dy):
+    for t in (delta, B, C, dy) + (() if zc is None else (zc,)):
         if t.dtype != x.dtype:
-            raise TypeError("x, delta, B, C, dy must share a dtype")
+            raise TypeError("x, delta, B, C, dy (and z) must share a dtype")
     Bs, L, ED = x.shape
     N = A.shape[1]
-    assert dy.shape == x.shape
+    assert dy.shape == x.shape and (zc is None or zc.shape == x.shape)
+    assert dtb is None or dtb.shape == (ED,)
     out = dict(dx=np.empty((Bs, L, ED)), ddelta=np.empty((Bs, L, ED)), dA=np.empty((ED, N)),
                dB=np.empty((Bs, L, N)), dC=np.empty((Bs, L, N)), dD=np.empty((ED,)), dh0=np.empty((Bs, ED, N)))
-    rc = lib().oracle_scan_bwd(dtype, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy),
+    dbias = np.empty((ED,)) if dtb is not None else None
+    rc = lib().oracle_scan_bwd(dtype, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dtb),
+                               int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]), _ptr(zc), _ptr(dy),
                                Bs, L, ED, N, _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
-                               _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _threads(nthreads))
+                               _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(dbias), _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_scan_bwd failed with code %d" % rc)
+    if dbias is not None:
+        out["ddt_bias"] = dbias
+    if zc is not None:
+        out["dz"] = _gate_grad(x, delta, A, B, C, D, dy, h0, zc, False, nthreads, opts)
     return out
+
+
+def _gate_grad(x, delta, A, B, C, D, dy, h0, z, bidir, nthreads, opts):
+    """dz = dy y d(z sigmoid(z))/dz for y' = y z sigmoid(z), with y the
+    ungated output of the scan (forward or bidirectional, with the options)."""
+    y, _, _ = scan(x, delta, A, B, C, D, h0=h0, bidir=bidir, nthreads=nthreads, **opts)
+    zf = _widen(z)
+    sg = 1.0 / (1.0 + np.exp(-zf))
+    return _widen(dy) * y * (sg * (1.0 + zf * (1.0 - sg)))
+
+
+def _widen(a):
+    """float32 or bf16 (uint16 bits) -> float64"""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def ssd(x, dt, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,

@@ -97,6 +97,20 @@ static double step_map(double v, double bias, int softplus, double dt_min, doubl
   return v;
 }
 
+/* d delta' / d delta of step_map at v (the derivative of the clamp is taken
+   as 0 at and beyond its bounds, 1 inside; softplus' = sigmoid below 20, 1
+   above, matching the map) */
+static double step_map_deriv(double v, double bias, int softplus, double dt_min, double dt_max) {
+  v += bias;
+  double u = v, d = 1.0;
+  if (softplus && v <= 20.0) {
+    u = log1p(exp(v));
+    d = 1.0 / (1.0 + exp(-v));
+  }
+  if (u <= dt_min || u >= dt_max) d = 0.0;
+  return d;
+}
+
 /* delta' for the element at index ix of channel e */
 static double step_size(const struct work* w, int64_t ix, int64_t e) {
   return step_map(load(w->delta, ix, w->dtype), w->dt_bias ? (double)w->dt_bias[e] : 0.0, w->dt_softplus,
@@ -222,9 +236,14 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
 }
 
 /*
- * Backward pass of the forward scan (no options, no bidirectional variant):
- * given dy = dL/dy, the gradients of L with respect to every input, by the
- * adjoint of the recurrence above. With g_t[n] = dL/dh_t[n]:
+ * Backward pass of the forward scan (the bidirectional variant is composed
+ * from it in oracle/__init__.py): given dy = dL/dy, the gradients of L with
+ * respect to every input, by the adjoint of the recurrence above, where
+ * delta_t stands for the mapped step size delta' of the options and dy_t for
+ * the scan's own output gradient, dy z sigmoid(z) under a gate (the gate's
+ * dz needs the whole output and is formed by the Python wrapper). The raw
+ * step size gets ddelta times d delta'/d delta (step_map_deriv), and
+ * ddt_bias[e] is the sum over (b, t) of that. With g_t[n] = dL/dh_t[n]:
  *     g_t = dy_t C_t + a_{t+1} g_{t+1}          (g_L = 0; reverse time)
  *     dC[b,t,n] = sum_e dy_t h_t[n]             dD[e] = sum_{b,t} dy_t x_t
  *     dx_t = sum_n g_t[n] delta_t B_t[n] + dy_t D[e]
@@ -237,7 +256,7 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
  * the blocks' partial sums in block order, and dA and dD the sums of the
  * rows' in row order, so the result does not depend on the thread count. Outputs are fp64:
  * dx, ddelta (Bs, L, ED); dA (ED, N); dB, dC (Bs, L, N); dD (ED);
- * dh0 (Bs, ED, N) or NULL. y is affine in h0, so dh0 does not depend on h0
+ * dh0 (Bs, ED, N) or NULL; ddt_bias (ED) or NULL. y is affine in h0, so dh0 does not depend on h0
  * and is returned for h0 = NULL (the zero initial state) as well.
  */
 enum { BWD_BLOCK = 64 }; /* channels per work item */
@@ -246,9 +265,13 @@ typedef struct {
   int dtype;
   const void *x, *delta, *B, *C, *dy;
   const float *A, *D, *h0;
+  const float* dt_bias; /* (ED) or NULL */
+  int dt_softplus;
+  double dt_min, dt_max;
+  const void* z;        /* gate (Bs, L, ED) or NULL: dy is taken as dy z sigmoid(z) */
   int64_t Bs, L, ED, N;
   double *dx, *ddelta, *dh0;
-  double *dA_part, *dD_part; /* per row: (Bs, ED, N), (Bs, ED) */
+  double *dA_part, *dD_part, *dbias_part; /* per row: (Bs, ED, N), (Bs, ED), (Bs, ED) */
   double *partB, *partC;     /* per channel block of the current row: (nblk, L, N) */
   int64_t b, blk0, blk1;     /* row, channel blocks [blk0, blk1) */
   int fail;
@@ -271,11 +294,13 @@ static void* bwd_worker(void* p) {
     for (int64_t i = 0; i < L * N; ++i) pB[i] = 0.0, pC[i] = 0.0;
     const int64_t e1 = (blk + 1) * BWD_BLOCK < ED ? (blk + 1) * BWD_BLOCK : ED;
     for (int64_t e = blk * BWD_BLOCK; e < e1; ++e) {
+      const double bias = w->dt_bias ? (double)w->dt_bias[e] : 0.0;
       /* forward, keeping every state */
       for (int64_t n = 0; n < N; ++n) hs[n] = w->h0 ? (double)w->h0[(b * ED + e) * N + n] : 0.0;
       for (int64_t t = 0; t < L; ++t) {
         const int64_t ix = (b * L + t) * ED + e, ib = (b * L + t) * N;
-        const double dt = load(w->delta, ix, w->dtype), xv = load(w->x, ix, w->dtype);
+        const double dt = step_map(load(w->delta, ix, w->dtype), bias, w->dt_softplus, w->dt_min, w->dt_max);
+        const double xv = load(w->x, ix, w->dtype);
         for (int64_t n = 0; n < N; ++n) {
           const double a = exp(dt * (double)w->A[e * N + n]);
           hs[(t + 1) * N + n] = a * hs[t * N + n] + (dt * xv) * load(w->B, ib + n, w->dtype);
@@ -286,10 +311,17 @@ static void* bwd_worker(void* p) {
       double dD = 0.0;
       double* dA = w->dA_part + (b * ED + e) * N;
       for (int64_t n = 0; n < N; ++n) dA[n] = 0.0;
+      double dbias = 0.0;
       for (int64_t t = L - 1; t >= 0; --t) {
         const int64_t ix = (b * L + t) * ED + e, ib = (b * L + t) * N;
-        const double dt = load(w->delta, ix, w->dtype), xv = load(w->x, ix, w->dtype);
-        const double dyv = load(w->dy, ix, w->dtype);
+        const double raw = load(w->delta, ix, w->dtype);
+        const double dt = step_map(raw, bias, w->dt_softplus, w->dt_min, w->dt_max);
+        const double xv = load(w->x, ix, w->dtype);
+        double dyv = load(w->dy, ix, w->dtype);
+        if (w->z) { /* the scan's output is gated: its own output gradient is dy z sigmoid(z) */
+          const double zv = load(w->z, ix, w->dtype);
+          dyv *= zv / (1.0 + exp(-zv));
+        }
         double dxv = w->D ? dyv * (double)w->D[e] : 0.0, ddv = 0.0;
         for (int64_t n = 0; n < N; ++n) {
           const double An = (double)w->A[e * N + n];
@@ -307,11 +339,15 @@ static void* bwd_worker(void* p) {
         }
         dD += dyv * xv;
         w->dx[ix] = dxv;
-        w->ddelta[ix] = ddv;
+        /* through the step-size map: d/d(raw delta) = d/d(delta') * delta'(raw) */
+        const double ddr = ddv * step_map_deriv(raw, bias, w->dt_softplus, w->dt_min, w->dt_max);
+        w->ddelta[ix] = ddr;
+        dbias += ddr;
       }
       if (w->dh0)
         for (int64_t n = 0; n < N; ++n) w->dh0[(b * ED + e) * N + n] = g[n];
       w->dD_part[b * ED + e] = dD;
+      w->dbias_part[b * ED + e] = dbias;
     }
   }
   free(hs);
@@ -320,9 +356,10 @@ static void* bwd_worker(void* p) {
 }
 
 int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A, const void* B, const void* C,
-                    const float* D, const float* h0, const void* dy, int64_t Bs, int64_t L, int64_t ED, int64_t N,
+                    const float* D, const float* h0, const float* dt_bias, int dt_softplus, double dt_min,
+                    double dt_max, const void* z, const void* dy, int64_t Bs, int64_t L, int64_t ED, int64_t N,
                     double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dh0,
-                    int nthreads) {
+                    double* ddt_bias, int nthreads) {
   if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC || !dD) return -1;
   if (Bs < 0 || L < 0 || ED < 0 || N <= 0) return -1; /* empty sizes allowed */
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
@@ -333,19 +370,20 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
   /* (one element more than needed, so that empty sizes still get a buffer) */
   double* dA_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED * N + 1));
   double* dD_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED + 1));
+  double* dbias_part = (double*)malloc(sizeof(double) * (size_t)(Bs * ED + 1));
   double* partB = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N + 1));
   double* partC = (double*)malloc(sizeof(double) * (size_t)(nblk * L * N + 1));
   bwd_t* ws = (bwd_t*)malloc(sizeof(bwd_t) * (size_t)nthreads);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
   int rc = 0;
-  if (!dA_part || !dD_part || !partB || !partC || !ws || !th) rc = -2;
+  if (!dA_part || !dD_part || !dbias_part || !partB || !partC || !ws || !th) rc = -2;
   /* one batch row at a time; its channel blocks are split over the threads,
      and dB, dC of the row are the sums of the blocks' partials in block order */
   for (int64_t b = 0; rc == 0 && b < Bs; ++b) {
     const int64_t per = (nblk + nthreads - 1) / nthreads;
     for (int i = 0; i < nthreads; ++i) {
-      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, Bs, L, ED, N, dx, ddelta,
-                      dh0, dA_part, dD_part, partB, partC, b, 0, 0, 0};
+      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, dt_bias, dt_softplus, dt_min, dt_max, z,
+                      Bs, L, ED, N, dx, ddelta, dh0, dA_part, dD_part, dbias_part, partB, partC, b, 0, 0, 0};
       ws[i].blk0 = per * i < nblk ? per * i : nblk;
       ws[i].blk1 = per * (i + 1) < nblk ? per * (i + 1) : nblk;
     }
@@ -372,8 +410,14 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
     for (int64_t b = 0; b < Bs; ++b) s += dD_part[b * ED + e];
     dD[e] = s;
   }
+  for (int64_t e = 0; rc == 0 && ddt_bias && e < ED; ++e) {
+    double s = 0.0;
+    for (int64_t b = 0; b < Bs; ++b) s += dbias_part[b * ED + e];
+    ddt_bias[e] = s;
+  }
   free(dA_part);
   free(dD_part);
+  free(dbias_part);
   free(partB);
   free(partC);
   free(ws);

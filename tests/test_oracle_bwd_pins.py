@@ -255,3 +255,87 @@ def test_bidirectional_backward_identities():
         assert np.allclose(gf[k][:, ::-1], g[k], rtol=1e-10, atol=1e-12), k
     for k in ("dA", "dD"):
         assert np.allclose(gf[k], g[k], rtol=1e-10, atol=1e-12), k
+
+
+# ---- the backward through the step-size options and the gate ---------------
+OPT_GRAD = dict(GRAD_OF, dt_bias="ddt_bias", z="dz")
+
+
+def options_case(Bs, L, ED, N, seed):
+    inp, dy, h0 = inputs(Bs, L, ED, N, seed=seed, h0=True)
+    inp["delta"] = synth.uniform(seed, 80, (Bs, L, ED), -3.0, 1.0)   # raw step sizes (softplus makes them > 0)
+    opts = dict(dt_bias=(0.5 * synth.normal(seed, 81, (ED,)) - 0.5).astype(np.float32), dt_softplus=True,
+                dt_limit=(0.08, 0.6), z=synth.normal(seed, 82, (Bs, L, ED)))
+    return inp, dy, h0, opts
+
+
+def options_loss(inp, dy, h0, opts, bidir):
+    y, _, _ = oracle.scan(**inp, h0=h0, bidir=bidir, **opts)
+    return float(np.sum(dy.astype(np.float64) * y))
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "D", "h0", "dt_bias", "z"])
+def test_options_backward_matches_finite_differences(name, bidir):
+    # central differences of the (pinned) forward oracle with bias, softplus,
+    # a clamp that binds on some steps, and the gate
+    Bs, L, ED, N = 2, 11, 3, 4
+    inp, dy, h0, opts = options_case(Bs, L, ED, N, seed=5)
+    g = oracle.scan_bwd(**inp, dy=dy, h0=h0, bidir=bidir, **opts)[OPT_GRAD[name]]
+    src = h0 if name == "h0" else (opts[name] if name in ("dt_bias", "z") else inp[name])
+    rng = np.random.default_rng(7)
+    lo, hi = opts["dt_limit"]
+    checked = 0
+    for _ in range(14):
+        idx = tuple(int(rng.integers(0, s)) for s in src.shape)
+        v = float(src[idx])
+        st = 2.0 ** -11 * max(1.0, abs(v))
+        if name in ("delta", "dt_bias"):
+            # skip points whose mapped step size lies within a few steps of a
+            # clamp bound (the map has a kink there)
+            e = idx[-1]
+            raw = inp["delta"][..., e] + opts["dt_bias"][e]
+            u = np.where(raw > 20, raw, np.log1p(np.exp(raw.astype(np.float64))))
+            near = np.abs(u - lo) < 8 * st if name == "dt_bias" else abs(u[idx[:-1]] - lo) < 8 * st
+            near = np.any(near) or np.any(np.abs(u - hi) < 8 * st) if name == "dt_bias" else \
+                near or abs(u[idx[:-1]] - hi) < 8 * st
+            if near:
+                continue
+        up, dn = np.float32(v + st), np.float32(v - st)
+        vals = []
+        for w in (up, dn):
+            arr = src.copy()
+            arr[idx] = w
+            if name == "h0":
+                vals.append(options_loss(inp, dy, arr, opts, bidir))
+            elif name in ("dt_bias", "z"):
+                vals.append(options_loss(inp, dy, h0, dict(opts, **{name: arr}), bidir))
+            else:
+                vals.append(options_loss(dict(inp, **{name: arr}), dy, h0, opts, bidir))
+        want = (vals[0] - vals[1]) / (float(up) - float(dn))
+        assert abs(g[idx] - want) <= 1e-5 * (1.0 + abs(want)), (name, bidir, idx, g[idx], want)
+        checked += 1
+    assert checked >= 5
+
+
+def test_options_backward_clamped_steps_have_no_gradient():
+    # a step size held at a clamp bound does not move with its raw value
+    inp, dy, h0, opts = options_case(2, 40, 5, 16, seed=9)
+    g = oracle.scan_bwd(**inp, dy=dy, h0=h0, **opts)
+    raw = inp["delta"].astype(np.float64) + opts["dt_bias"][None, None, :]
+    u = np.log1p(np.exp(raw))
+    clamped = (u <= opts["dt_limit"][0]) | (u >= opts["dt_limit"][1])
+    assert clamped.any() and (~clamped).any()
+    assert np.all(g["ddelta"][clamped] == 0.0)
+    assert np.all(g["ddelta"][~clamped] != 0.0)
+    # ddt_bias is the sum of the raw step sizes' gradients over batch rows and time
+    np.testing.assert_allclose(g["ddt_bias"], g["ddelta"].sum(axis=(0, 1)), rtol=1e-12, atol=1e-14)
+
+
+def test_no_options_equals_plain_backward():
+    inp, dy, h0 = inputs(2, 30, 4, 16, seed=10, h0=True)
+    a = oracle.scan_bwd(**inp, dy=dy, h0=h0)
+    b = oracle.scan_bwd(**inp, dy=dy, h0=h0, dt_bias=np.zeros(4, np.float32))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    np.testing.assert_allclose(b["ddt_bias"], a["ddelta"].sum(axis=(0, 1)), rtol=1e-12, atol=1e-14)
