@@ -155,15 +155,26 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
  *   dB_t[n]  = sum_e g_t delta_t x_t,      dC_t[n] = sum_e dy_t h_t
  *   dA[e,n]  = sum_{b,t} delta_t g_t a_t h_{t-1},   dD[e] = sum_{b,t} dy_t x_t
  *   dh0      = a_0 g_0
- * Step-size options and the gate are not covered (the forward must have run
- * without them); the bidirectional scan has ssm_scan_bidir_bwd below.
+ * The bidirectional scan has ssm_scan_bidir_bwd below.
+ * Step-size options (opts: dt_bias, dt_softplus, dt_min, dt_max, as given
+ * to the forward): the recurrence above runs with delta' = clamp(softplus?(
+ * delta + dt_bias), dt_min, dt_max) in place of delta, ddelta is the
+ * gradient of the raw delta, ddelta' d delta'/d delta, where the derivative
+ * is sigmoid(delta + dt_bias) (1 without softplus) and 0 where the clamp
+ * holds delta' at a bound (taken as 0 at the bound itself), and ddt_bias[e]
+ * is the sum of ddelta over rows and time. The output gate is not covered:
+ * opts->z must be NULL (SSM_ERR_UNSUPPORTED otherwise); gate the output
+ * gradient outside the call.
  *   x, delta, A, B, C, D, h0 : as ssm_scan_fwd (D and h0 may be NULL)
+ *   opts    : step-size options of the forward, or NULL
  *   dy      : (Bs, L, ED) of dtype         -- dL/dy
  *   dx, ddelta : (Bs, L, ED) of dtype      -- written in full
  *   dA      : (ED, N) float32              -- written in full
  *   dB, dC  : (Bs, L, N) of dtype          -- written in full
  *   dD      : (ED) float32, or NULL (not computed)
  *   dh0     : (Bs, ED, N) float32, or NULL (not computed)
+ *   ddt_bias : (ED) float32, or NULL (not computed; with no option it is
+ *              the sum of ddelta over rows and time)
  *   workspace : at least ssm_scan_bwd_workspace_bytes() bytes (required; it
  *     holds the state at every 32-step boundary and float32 partial sums of
  *     dB, dC, dA and dD), no initialisation needed.
@@ -174,13 +185,13 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
 size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype);
 
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-                 float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream);
+                 const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
+                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
+                 int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward pass of the bidirectional scan: the gradients of L = sum(dy * y)
- * for y = ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, opts = NULL), the sum
+ * for y = ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, opts), the sum
  * of the forward scan (with D x and h0) and the reverse-time scan (from a
  * zero state, shared weights) of "Some questions of Bi-Mamba2 and Hydra" (the
  * author's first reply). Its gradient is the sum of the two scans' gradients:
@@ -198,9 +209,10 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
 size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype);
 
 int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB,
-                       void* dC, float* dD, float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       const float* D, const float* h0, const ssm_scan_options* opts, const void* dy, void* dx,
+                       void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias,
+                       int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * Multi-head (Mamba-2 / SSD) selective scan, in the layout of the chunked

@@ -57,6 +57,12 @@ struct BwdArgs {
   const T* C;
   const float* D;    // or nullptr
   const float* h0;   // or nullptr
+  // step-size options of the forward: delta' = clamp(softplus?(delta + dt_bias), dt_min, dt_max)
+  const float* dt_bias;  // (ED) or nullptr
+  int dt_softplus;
+  int dt_pre;            // any option at all
+  float dt_min, dt_max;
+  double* pDB;       // [Bs][EDp]: ddt_bias partial of each batch row, or nullptr
   const T* dy;
   T* dx;
   T* ddl;
@@ -149,12 +155,14 @@ __device__ __forceinline__ void add_c_dy(float (&gv)[4], float cq, float dyv) {
 // REV: the reverse-time scan of the bidirectional form. Virtual step t of the
 // sweeps is time L - 1 - t: every load and store maps the time, nothing else
 // changes (the inputs are read in place, no flipped copy).
-template <typename T, int RT, bool VEC, bool REV>
+// OPTS: the forward ran with step-size options (delta' = the map of delta).
+template <typename T, int RT, bool VEC, bool REV, bool OPTS>
 struct BwdStager {
   int row, chk;
   bool is_xd, chunk_ok, row_ok;
   float4 ra, rb, rc;
   int64_t b, e0, ED, L;
+  float4 dbacc = make_float4(0.f, 0.f, 0.f, 0.f);  // this task's raw step-size gradients, summed over its rounds
 
   __device__ __forceinline__ void init(int tid, int64_t b_, int64_t e0_, int64_t ED_, int64_t L_) {
     int u = tid;
@@ -201,13 +209,27 @@ struct BwdStager {
 
   // dx and ddelta of round rr (written into the x and dy slots of its tile by
   // the adjoint replay) -> global
-  __device__ __forceinline__ void store_grads(const BwdArgs<T>& p, const BwdTile<RT>& tl, int64_t rr) const {
+  // d delta'/d delta from delta' itself: 0 where the clamp holds it at a bound,
+  // else the softplus derivative sigmoid(v) = 1 - exp(-softplus(v)) (or 1)
+  __device__ __forceinline__ float map_deriv(const BwdArgs<T>& p, float m) const {
+    if (m <= p.dt_min || m >= p.dt_max) return 0.f;
+    return p.dt_softplus ? -expm1f(-m) : 1.f;
+  }
+
+  __device__ __forceinline__ void store_grads(const BwdArgs<T>& p, const BwdTile<RT>& tl, int64_t rr) {
     const int64_t tv = rr * RT + row;
     if (!is_xd || tv >= L || !chunk_ok) return;
     const int64_t t = REV ? L - 1 - tv : tv;
     const int c4 = 4 * chk;
     float4 gx = *reinterpret_cast<const float4*>(&tl.xv[row][c4]);
     float4 gd = *reinterpret_cast<const float4*>(&tl.dy[row][c4]);
+    if constexpr (OPTS) {
+      // through the step-size map to the raw step size; ddt_bias sums it
+      const float4 m = *reinterpret_cast<const float4*>(&tl.dt[row][c4]);
+      gd = make_float4(gd.x * map_deriv(p, m.x), gd.y * map_deriv(p, m.y), gd.z * map_deriv(p, m.z),
+                       gd.w * map_deriv(p, m.w));
+      dbacc = make_float4(dbacc.x + gd.x, dbacc.y + gd.y, dbacc.z + gd.z, dbacc.w + gd.w);
+    }
     const int64_t ce = e0 + c4, off = (b * L + t) * ED + ce;
     if (VEC) {
       if (REV && p.acc_dx) {
@@ -244,13 +266,24 @@ struct BwdStager {
   }
 
   // registers -> LDS tile (padded rows and channels are zero: delta = 0
-  // gives a = 1 and b = 0, dy = 0 gives no adjoint input)
+  // gives a = 1 and b = 0, dy = 0 gives no adjoint input). The tile holds
+  // the step size after the options, delta'.
   template <bool WITH_ADJ>
-  __device__ __forceinline__ void commit(BwdTile<RT>& tl) const {
+  __device__ __forceinline__ void commit(const BwdArgs<T>& p, BwdTile<RT>& tl) const {
     const int c4 = 4 * chk;
     if (is_xd) {
       *reinterpret_cast<float4*>(&tl.xv[row][c4]) = ra;
-      *reinterpret_cast<float4*>(&tl.dt[row][c4]) = rb;
+      float4 dv = rb;
+      if constexpr (OPTS) {
+        const bool ok = row_ok && chunk_ok;
+        const int64_t ce = e0 + c4;
+        const float* bias = p.dt_bias;
+        dv.x = ok && ce + 0 < ED ? map_step(dv.x, bias ? bias + ce + 0 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.y = ok && ce + 1 < ED ? map_step(dv.y, bias ? bias + ce + 1 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.z = ok && ce + 2 < ED ? map_step(dv.z, bias ? bias + ce + 2 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.w = ok && ce + 3 < ED ? map_step(dv.w, bias ? bias + ce + 3 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+      }
+      *reinterpret_cast<float4*>(&tl.dt[row][c4]) = dv;
       if (WITH_ADJ) *reinterpret_cast<float4*>(&tl.dy[row][c4]) = rc;
     } else {
       *reinterpret_cast<float4*>(&tl.bc[row][c4]) = make_float4(ra.x, rb.x, ra.y, rb.y);
@@ -277,7 +310,7 @@ __device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums
   *reinterpret_cast<float4*>(dst + ((grp * p.Bs + b) * p.L + t) * 16 + n4) = s;
 }
 
-template <typename T, int SEG, int TS, bool VEC, bool REV>
+template <typename T, int SEG, int TS, bool VEC, bool REV, bool OPTS>
 __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(
     const BwdArgs<T> p) {
   constexpr int RT = SEG * TS;
@@ -315,7 +348,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   const float Dv = (p.D && ch_ok) ? p.D[e] : 0.f;
 
-  BwdStager<T, RT, VEC, REV> st;
+  BwdStager<T, RT, VEC, REV, OPTS> st;
   st.init(tid, b, e0, ED, L);
   // checkpoint of round rr for this lane's 4 states
   auto ck = [&](int64_t rr) { return p.ckpt + ((b * R + rr) * p.EDp + e) * 16 + 4 * g; };
@@ -328,7 +361,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
       hc[0] = v.x, hc[1] = v.y, hc[2] = v.z, hc[3] = v.w;
     }
     st.template prefetch<false>(p, 0);
-    st.template commit<false>(tile[0]);
+    st.template commit<false>(p, tile[0]);
     __syncthreads();
     for (int64_t r = 0; r + 1 < R; ++r) {
       rotate_priority(r, p.rot_ncu);
@@ -363,7 +396,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
         }
         *reinterpret_cast<float4*>(ck(r + 1)) = make_float4(hc[0], hc[1], hc[2], hc[3]);
       }
-      if (r + 2 < R) st.template commit<false>(nxt);
+      if (r + 2 < R) st.template commit<false>(p, nxt);
       __syncthreads();
     }
   }
@@ -374,7 +407,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   float kcar[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint carry out of round 0 (wave 0)
   if (wave == 0) fa.kc[R & 1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
   st.template prefetch<true>(p, R - 1);
-  st.template commit<true>(tile[(R - 1) & 1]);
+  st.template commit<true>(p, tile[(R - 1) & 1]);
   __syncthreads();
   for (int64_t r = R - 1; r >= 0; --r) {
     rotate_priority(r, p.rot_ncu);
@@ -509,7 +542,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int j = 0; j < 4; ++j) kcar[j] = kin[j];
     }
-    if (r >= 1) st.template commit<true>(nxt);
+    if (r >= 1) st.template commit<true>(p, nxt);
     __syncthreads();
   }
   store_colsums<T, RT, REV>(p, cs, tid, b, grp, 0);
@@ -532,6 +565,24 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int k = 1; k < SEG; ++k) s += red[(k * 5 + j) * 64 + lane];
       if (j < 4) p.pA[(b * p.EDp + e) * 16 + 4 * g + j] = s;
       else if (g == 0) p.pD[b * p.EDp + e] = s;
+    }
+  }
+  // ddt_bias: the step-size tasks' sums, added over the round's rows in row
+  // order (the column-sum tile is free since the barrier above)
+  if (OPTS && p.pDB) {
+    double* dbs = reinterpret_cast<double*>(&cs);  // [RT rows][16 channels]
+    static_assert(sizeof(ColSums<RT>) >= sizeof(double) * RT * 16, "reduction area");
+    if (st.is_xd) {
+      dbs[st.row * 16 + 4 * st.chk + 0] = st.dbacc.x;
+      dbs[st.row * 16 + 4 * st.chk + 1] = st.dbacc.y;
+      dbs[st.row * 16 + 4 * st.chk + 2] = st.dbacc.z;
+      dbs[st.row * 16 + 4 * st.chk + 3] = st.dbacc.w;
+    }
+    __syncthreads();
+    if (tid < 16) {
+      double s = 0.0;
+      for (int r = 0; r < RT; ++r) s += dbs[r * 16 + tid];
+      p.pDB[b * p.EDp + e0 + tid] = s;
     }
   }
 }
@@ -575,8 +626,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
 // dA, dD: sum of the batch rows' partials, in row order (the bidirectional
 // backward has 2 Bs rows of dA partials: the forward-time scan's, then the
 // reverse-time scan's; dD comes from the forward-time scan alone).
-__global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double* __restrict__ pD, float* dA,
-                                     float* dD, int64_t rowsA, int64_t rowsD, int64_t ED, int64_t EDp) {
+__global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double* __restrict__ pD,
+                                     const double* __restrict__ pDB, float* dA, float* dD, float* ddt_bias,
+                                     int64_t rowsA, int64_t rowsD, int64_t ED, int64_t EDp) {
   const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (i < ED * 16) {
     const int64_t e = i >> 4, n = i & 15;
@@ -588,6 +640,12 @@ __global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double
     double s = 0.0;
     for (int64_t b = 0; b < rowsD; ++b) s += pD[b * EDp + e];
     dD[e] = static_cast<float>(s);
+  } else if (ddt_bias && i >= ED * 17 && i < ED * 18) {
+    // ddt_bias: the sum of the rows' partials (both directions for the bidirectional scan)
+    const int64_t e = i - ED * 17;
+    double s = 0.0;
+    for (int64_t b = 0; b < rowsA; ++b) s += pDB[b * EDp + e];
+    ddt_bias[e] = static_cast<float>(s);
   }
 }
 
@@ -596,7 +654,7 @@ __global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double
 // ---------------------------------------------------------------------------
 struct BwdLayout {
   int64_t rounds, ngroups, EDp;
-  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, part_off, bytes;
+  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, pDB_off, part_off, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -612,7 +670,7 @@ bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo, bool bidir = f
   lo->EDp = lo->ngroups * 16;
   // every count below is checked against overflow of size_t arithmetic
   const double total = 4.0 * (static_cast<double>(Bs) * lo->rounds * lo->EDp * 16 +
-                              2.0 * dirs * lo->ngroups * Bs * L * 16 + 2.0 * dirs * Bs * lo->EDp * 17 +
+                              2.0 * dirs * lo->ngroups * Bs * L * 16 + 2.0 * dirs * Bs * lo->EDp * 18 +
                               (part_f32 ? 2.0 * Bs * L * ED : 0.0)) +
                        6 * 256.0;
   if (total > 9.0e18) return false;
@@ -626,6 +684,8 @@ bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo, bool bidir = f
   lo->pA_off = off;
   off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp * 16) * 8);
   lo->pD_off = off;
+  off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp) * 8);
+  lo->pDB_off = off;
   off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp) * 8);
   lo->part_off = off;
   if (part_f32) off = align256(off + static_cast<size_t>(2 * Bs * L * ED) * 4);
@@ -661,16 +721,20 @@ size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dty
 }
 
 int bwd_validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const void* dy, const void* dx, const void* ddelta, const float* dA, const void* dB,
-                 const void* dC, const float* dD, const float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N,
-                 int dtype, const void* ws, size_t ws_bytes, bool bidir, BwdSizes* s) {
+                 const float* h0, const ssm_scan_options* opts, const void* dy, const void* dx, const void* ddelta,
+                 const float* dA, const void* dB, const void* dC, const float* dD, const float* dh0,
+                 const float* ddt_bias, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, const void* ws,
+                 size_t ws_bytes, bool bidir, BwdSizes* s) {
   int rc = bwd_check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
+  if (opts && opts->z) return SSM_ERR_UNSUPPORTED;                   // the gate's backward is not provided
+  if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
+  const float* dt_bias = opts ? opts->dt_bias : nullptr;
   // a buffer with no elements may be NULL
   if ((s->seq > 0 && (!x || !delta || !dy || !dx || !ddelta)) || (s->bc > 0 && (!B || !C || !dB || !dC)) ||
       (ED > 0 && (!A || !dA)))
     return SSM_ERR_NULL;
-  const void* ptrs[] = {x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, ws};
+  const void* ptrs[] = {x, delta, A, B, C, D, h0, dt_bias, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, ws};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   BwdLayout lo;
@@ -679,10 +743,11 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
   if (lo.bytes > 0 && (!ws || ws_bytes < lo.bytes)) return SSM_ERR_WORKSPACE;
   const Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
                       rng(B, s->bc * s->elem),  rng(C, s->bc * s->elem),      rng(D, D ? ED * 4 : 0),
-                      rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem)};
+                      rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem), rng(dt_bias, dt_bias ? ED * 4 : 0)};
   const Range out[] = {rng(dx, s->seq * s->elem), rng(ddelta, s->seq * s->elem), rng(dA, ED * N * 4),
                        rng(dB, s->bc * s->elem),  rng(dC, s->bc * s->elem),      rng(dD, dD ? ED * 4 : 0),
-                       rng(dh0, dh0 ? s->state * 4 : 0), rng(ws, static_cast<int64_t>(lo.bytes))};
+                       rng(dh0, dh0 ? s->state * 4 : 0), rng(ddt_bias, ddt_bias ? ED * 4 : 0),
+                       rng(ws, static_cast<int64_t>(lo.bytes))};
   constexpr int nout = sizeof(out) / sizeof(out[0]);
   for (int i = 0; i < nout; ++i) {
     if (out[i].hi == out[i].lo) continue;
@@ -696,16 +761,24 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
 
 template <typename T, bool REV>
 void launch_bwd_kernel(const BwdArgs<T>& a, int64_t nblk, size_t dyn, bool vec, hipStream_t stream) {
-  if (vec)
-    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true, REV>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
-  else
-    hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, false, REV>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  if (a.dt_pre) {
+    if (vec)
+      hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true, REV, true>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+    else
+      hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, false, REV, true>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true, REV, false>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+    else
+      hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, false, REV, false>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
+  }
 }
 
 template <typename T>
 int launch_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-               const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-               float* dh0, int64_t Bs, int64_t L, int64_t ED, void* ws, bool bidir, hipStream_t stream) {
+               const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
+               void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
+               void* ws, bool bidir, hipStream_t stream) {
   const bool part_f32 = bidir && !std::is_same<T, float>::value;
   BwdLayout lo;
   bwd_layout(Bs, L, ED, &lo, bidir, part_f32);
@@ -720,6 +793,14 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.C = static_cast<const T*>(C);
   a.D = D;
   a.h0 = h0;
+  a.dt_bias = opts ? opts->dt_bias : nullptr;
+  a.dt_softplus = opts && opts->dt_softplus ? 1 : 0;
+  a.dt_min = opts ? opts->dt_min : -INFINITY;
+  a.dt_max = opts ? opts->dt_max : INFINITY;
+  // (a requested ddt_bias takes the options path: with no option the map is
+  // the identity and ddt_bias is the sum of ddelta)
+  a.dt_pre = (a.dt_bias || a.dt_softplus || a.dt_min > -INFINITY || a.dt_max < INFINITY || ddt_bias) ? 1 : 0;
+  a.pDB = ddt_bias ? reinterpret_cast<double*>(w + lo.pDB_off) : nullptr;
   a.dy = static_cast<const T*>(dy);
   a.dx = static_cast<T*>(dx);
   a.ddl = static_cast<T*>(ddelta);
@@ -761,6 +842,7 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
     r.pC = a.pC + lo.ngroups * Bs * L * 16;
     r.pA = a.pA + Bs * lo.EDp * 16;
     r.pD = a.pD + Bs * lo.EDp;
+    r.pDB = a.pDB ? a.pDB + Bs * lo.EDp : nullptr;
     r.part_dx = nullptr;
     r.part_dd = nullptr;
     r.acc_dx = part_f32 ? a.part_dx : static_cast<const float*>(dx);
@@ -775,18 +857,18 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
                      stream, a.pB, a.pC, static_cast<T*>(dB), static_cast<T*>(dC), n4,
                      static_cast<int>(bidir ? 2 * lo.ngroups : lo.ngroups));
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
-  hipLaunchKernelGGL(bwd_reduce_ad_kernel, dim3(static_cast<unsigned>((ED * 17 + 255) / 256)), dim3(256), 0, stream,
-                     a.pA, a.pD, dA, dD, bidir ? 2 * Bs : Bs, Bs, ED, lo.EDp);
+  hipLaunchKernelGGL(bwd_reduce_ad_kernel, dim3(static_cast<unsigned>((ED * 18 + 255) / 256)), dim3(256), 0, stream,
+                     a.pA, a.pD, a.pDB, dA, dD, ddt_bias, bidir ? 2 * Bs : Bs, Bs, ED, lo.EDp);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
 int run_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-            const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-            float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-            size_t workspace_bytes, void* stream, bool bidir) {
+            const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
+            void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
+            int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool bidir) {
   BwdSizes s;
-  const int rc = bwd_validate(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype,
-                              workspace, workspace_bytes, bidir, &s);
+  const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
+                              ED, N, dtype, workspace, workspace_bytes, bidir, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.seq == 0) {
@@ -794,14 +876,14 @@ int run_bwd(const void* x, const void* delta, const float* A, const void* B, con
     // time steps but no channels)
     const bool ok = fill_async(dA, nullptr, ED * N * 4, st) && fill_async(dD, nullptr, ED * 4, st) &&
                     fill_async(dh0, nullptr, s.state * 4, st) && fill_async(dB, nullptr, s.bc * s.elem, st) &&
-                    fill_async(dC, nullptr, s.bc * s.elem, st);
+                    fill_async(dC, nullptr, s.bc * s.elem, st) && fill_async(ddt_bias, nullptr, ED * 4, st);
     return ok ? SSM_OK : SSM_ERR_LAUNCH;
   }
   if (dtype == SSM_F32)
-    return launch_bwd<float>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace,
-                             bidir, st);
-  return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, workspace,
-                              bidir, st);
+    return launch_bwd<float>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
+                             ED, workspace, bidir, st);
+  return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
+                              ED, workspace, bidir, st);
 }
 
 }  // namespace
@@ -817,19 +899,20 @@ size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int
 }
 
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
-                 float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
-  return run_bwd(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype, workspace,
-                 workspace_bytes, stream, false);
+                 const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
+                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
+                 int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L, ED, N, dtype,
+                 workspace, workspace_bytes, stream, false);
 }
 
 int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, const void* dy, void* dx, void* ddelta, float* dA, void* dB,
-                       void* dC, float* dD, float* dh0, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(x, delta, A, B, C, D, h0, dy, dx, ddelta, dA, dB, dC, dD, dh0, Bs, L, ED, N, dtype, workspace,
-                 workspace_bytes, stream, true);
+                       const float* D, const float* h0, const ssm_scan_options* opts, const void* dy, void* dx,
+                       void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias,
+                       int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L, ED, N, dtype,
+                 workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -103,9 +103,11 @@ def gather_channels(y, chans, ED):
     return y[b, :, e]
 
 
-def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None, bidir=False):
+def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None, bidir=False,
+                dt_bias=None, dt_softplus=False, dt_limit=None):
     """ssm_scan_bwd (bidir: ssm_scan_bidir_bwd) on the GPU; every gradient as
-    a float64 numpy array."""
+    a float64 numpy array. dt_bias (numpy, float32) / dt_softplus / dt_limit
+    are the step-size options; with dt_bias the result holds ddt_bias."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -121,9 +123,14 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
         out["dD"] = torch.full((ED,), float("nan"), dtype=torch.float32, device=dev)
     if want_dh0:
         out["dh0"] = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev)
+    bias = None
+    if dt_bias is not None:
+        bias = torch.from_numpy(np.ascontiguousarray(dt_bias, dtype=np.float32)).to(dev)
+        out["ddt_bias"] = torch.full((ED,), float("nan"), dtype=torch.float32, device=dev)
     fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
     res = fn(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
-             h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream)
+             h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream, dt_bias=bias,
+             dt_softplus=dt_softplus, dt_limit=dt_limit)
     torch.cuda.synchronize()
     return {k: y_to_numpy(v) for k, v in res.items()}
 
@@ -195,3 +202,17 @@ def degenerate_inputs(case, Bs=2, L=200, ED=64, seed=13):
         inp["delta"][:, 5::7, :] = 0.0
     inp["A"] = A
     return inp
+
+
+def options_inputs(Bs, L, ED, dtype, seed):
+    """Raw step sizes around softplus^-1 of the usual range, a bias, a gate."""
+    inp = synth.make_inputs(Bs, L, ED, 16, "f32", seed=seed)
+    raw = (0.7 * synth.normal(seed, 21, (Bs, L, ED)) - 3.5).astype(np.float32)
+    z = synth.normal(seed, 22, (Bs, L, ED))
+    bias = (0.3 * synth.normal(seed, 23, (ED,))).astype(np.float32)
+    inp["delta"] = raw
+    if dtype == "bf16":
+        for k in ("x", "delta", "B", "C"):
+            inp[k] = synth.to_bf16(inp[k])
+        z = synth.to_bf16(z)
+    return inp, dict(dt_bias=bias, dt_softplus=True, dt_limit=(1e-3, 0.1), z=z)

@@ -161,15 +161,16 @@ def test_options_validation():
     assert fwd(opts=ref) == ssm.SSM_ERR_ALIAS
 
 
-BWD_PTRS = ["x", "delta", "A", "B", "C", "D", "h0", "dy", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0", "ws"]
+BWD_PTRS = ["x", "delta", "A", "B", "C", "D", "h0", "opts", "dy", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0",
+            "ddt_bias", "ws"]
 
 
 def bwd(**kw):
     args = {n: P[i] for i, n in enumerate(BWD_PTRS)}
-    args.update(Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32)
+    args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32)  # (opts is read on the host)
     args["ws_bytes"] = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32)
     args.update(kw)
-    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_PTRS[:15]], args["Bs"], args["L"], args["ED"], args["N"],
+    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_PTRS[:17]], args["Bs"], args["L"], args["ED"], args["N"],
                                   args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -190,7 +191,7 @@ def test_bwd_null_pointer(name):
 def test_bwd_optional_pointers_may_be_null():
     # D, h0, dD, dh0 are optional: with them NULL the call gets past the NULL
     # check and fails only on the fake (misaligned) workspace below
-    assert bwd(D=None, h0=None, dD=None, dh0=None, ws=P[15] + 4) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(D=None, h0=None, dD=None, dh0=None, ws=P[17] + 4) == ssm.SSM_ERR_UNSUPPORTED
 
 
 def test_bwd_empty_inputs_are_valid():
@@ -205,13 +206,13 @@ def test_bwd_validation():
     assert bwd(L=-1) == ssm.SSM_ERR_DIM
     assert bwd(N=8) == ssm.SSM_ERR_UNSUPPORTED
     assert bwd(dtype=3) == ssm.SSM_ERR_UNSUPPORTED
-    assert bwd(dB=P[11] + 4) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(dB=P[12] + 4) == ssm.SSM_ERR_UNSUPPORTED
     assert bwd(ws=None) == ssm.SSM_ERR_WORKSPACE
     assert bwd(ws_bytes=1024) == ssm.SSM_ERR_WORKSPACE
     assert bwd(dx=P[0]) == ssm.SSM_ERR_ALIAS              # dx on top of x
-    assert bwd(ddelta=P[8] + 256) == ssm.SSM_ERR_ALIAS    # ddelta inside dx
+    assert bwd(ddelta=P[9] + 256) == ssm.SSM_ERR_ALIAS    # ddelta inside dx
     assert bwd(dh0=P[6]) == ssm.SSM_ERR_ALIAS             # dh0 on top of h0
-    assert bwd(ws=P[7]) == ssm.SSM_ERR_ALIAS              # workspace on top of dy
+    assert bwd(ws=P[8]) == ssm.SSM_ERR_ALIAS              # workspace on top of dy
 
 
 SSD_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "opts", "y", "h"]
@@ -318,10 +319,10 @@ def test_ssd_options_validation():
 
 def bidir_bwd(**kw):
     args = {n: P[i] for i, n in enumerate(BWD_PTRS)}
-    args.update(Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_BF16)
+    args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_BF16)
     args["ws_bytes"] = ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
     args.update(kw)
-    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BWD_PTRS[:15]], args["Bs"], args["L"], args["ED"],
+    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BWD_PTRS[:17]], args["Bs"], args["L"], args["ED"],
                                         args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -349,3 +350,16 @@ def test_bidir_bwd_validation():
     assert bidir_bwd(dx=P[0]) == ssm.SSM_ERR_ALIAS
     none = {n: None for n in BWD_PTRS}
     assert bidir_bwd(**dict(none, Bs=0, ED=0, ws_bytes=0)) == ssm.SSM_OK
+
+
+def test_bwd_options_validation():
+    gated = ssm.SSMOptions(None, 1, -float("inf"), float("inf"), P[18])
+    assert bwd(opts=ctypes.byref(gated)) == ssm.SSM_ERR_UNSUPPORTED          # no backward through the gate
+    assert bidir_bwd(opts=ctypes.byref(gated)) == ssm.SSM_ERR_UNSUPPORTED
+    inverted = ssm.SSMOptions(None, 0, 0.5, 0.1, None)
+    assert bwd(opts=ctypes.byref(inverted)) == ssm.SSM_ERR_ARG
+    nan = ssm.SSMOptions(None, 0, float("nan"), 1.0, None)
+    assert bidir_bwd(opts=ctypes.byref(nan)) == ssm.SSM_ERR_ARG
+    misaligned = ssm.SSMOptions(P[19] + 4, 1, 0.0, 1.0, None)
+    assert bwd(opts=ctypes.byref(misaligned)) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(ddt_bias=P[0]) == ssm.SSM_ERR_ALIAS                           # ddt_bias on top of x

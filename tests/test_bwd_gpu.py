@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from parity_util import assert_grads_close, degenerate_inputs, log, run_gpu_bwd
+from parity_util import assert_grads_close, degenerate_inputs, log, options_inputs, run_gpu_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +144,75 @@ def test_bidir_training_shape_full():
     # the bidirectional training shape of the forward (Bs 8, L 4096, ED 1536)
     # at a quarter of the length, every gradient compared in full
     check(8, 1024, 1536, seed=111, h0=True, bidir=True)
+
+
+# ---- backward through the step-size options (bias, softplus, clamp) ---------
+def keep_clear_of_bounds(inp, opts):
+    """The clamp's derivative jumps at its bounds; a step mapped to within
+    rounding of one could be taken on different sides by the float32 kernel
+    and the fp64 oracle. Steps that land within 1e-5 (relative) of a bound --
+    the same mapping written in numpy -- are scaled by 1 - 2^-6 until none
+    does; the inputs are otherwise unchanged."""
+    bf16 = inp["delta"].dtype == np.uint16
+    raw = synth.from_bf16(inp["delta"]) if bf16 else inp["delta"].astype(np.float32)
+    for _ in range(8):
+        v = raw.astype(np.float64)
+        if opts.get("dt_bias") is not None:
+            v = v + opts["dt_bias"].astype(np.float32).astype(np.float64)
+        if opts.get("dt_softplus"):
+            v = np.logaddexp(0.0, v)
+        bad = np.zeros(v.shape, dtype=bool)
+        for bound in opts.get("dt_limit", ()):
+            if np.isfinite(bound):
+                bad |= np.abs(v - bound) <= 1e-5 * abs(bound)
+        if not bad.any():
+            return dict(inp, delta=synth.to_bf16(raw) if bf16 else raw)
+        raw = raw.copy()
+        raw[bad] *= np.float32(1 - 2.0 ** -6)
+        if bf16:
+            raw = synth.from_bf16(synth.to_bf16(raw))
+    raise AssertionError("steps stay on a clamp bound")
+
+
+def check_options(Bs, L, ED, dtype, seed, opts, bidir=False, h0=False, inp=None):
+    log("bwd options case Bs=%d L=%d ED=%d dtype=%s seed=%d bidir=%s options=%s" % (
+        Bs, L, ED, dtype, seed, bidir, sorted(opts)))
+    if inp is None:
+        inp, _ = options_inputs(Bs, L, ED, dtype, seed)
+    inp = keep_clear_of_bounds(inp, opts)
+    dy = synth.make_output_grad(Bs, L, ED, dtype, seed=seed)
+    h = synth.normal(seed, 79, (Bs, ED, 16)) if h0 else None
+    got = run_gpu_bwd(inp, dy, h0=h, want_dh0=True, bidir=bidir, **opts)
+    ref = oracle.scan_bwd(**inp, dy=dy, h0=h, bidir=bidir, **opts)
+    assert ("ddt_bias" in got) == (opts.get("dt_bias") is not None)
+    assert_grads_close(got, ref, dtype)
+
+
+@pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(2, 300, 64, "f32", False), (2, 301, 40, "f32", False),
+                                                 (2, 257, 64, "bf16", False), (2, 200, 64, "f32", True),
+                                                 (2, 150, 48, "bf16", True), (1, 2100, 32, "f32", False)])
+def test_step_size_options(Bs, L, ED, dtype, bidir):
+    _, opts = options_inputs(Bs, L, ED, dtype, seed=L + ED)
+    opts.pop("z")
+    check_options(Bs, L, ED, dtype, L + ED, opts, bidir=bidir, h0=True)
+
+
+def test_step_size_options_each_alone():
+    inp, opts = options_inputs(2, 150, 32, "f32", seed=5)
+    positive = synth.make_inputs(2, 150, 32, 16, "f32", seed=5)["delta"]   # log-uniform steps
+    singles = {"dt_bias": dict(dt_bias=np.abs(opts["dt_bias"]) * 0.02),
+               "dt_softplus": dict(dt_softplus=True),
+               "dt_limit": dict(dt_limit=(0.01, 0.05)),
+               "dt_min": dict(dt_limit=(0.02, float("inf"))),
+               "bias_and_limit": dict(dt_bias=np.abs(opts["dt_bias"]) * 0.02, dt_limit=(0.01, 0.05))}
+    for key, one in singles.items():
+        # raw steps only through softplus; otherwise positive steps
+        inp2 = inp if key == "dt_softplus" else dict(inp, delta=positive)
+        check_options(2, 150, 32, "f32", 5, one, inp=inp2)
+
+
+def test_step_size_options_training_shape():
+    # (Bs 8, L 1024, ED 1536) with bias, softplus and clamp
+    _, opts = options_inputs(8, 1024, 1536, "bf16", seed=12)
+    opts.pop("z")
+    check_options(8, 1024, 1536, "bf16", 12, opts)

@@ -5,7 +5,8 @@ import pytest
 
 import oracle
 import synth
-from parity_util import TOL, assert_close, degenerate_inputs, gather_channels, log, run_gpu, sample_channels
+from parity_util import (TOL, assert_close, degenerate_inputs, gather_channels, log, options_inputs, run_gpu,
+                         sample_channels)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,20 +174,6 @@ def test_resume_in_two_pieces():
 
 
 # ---- step-size pre-processing and output gate ------------------------------------
-
-def options_inputs(Bs, L, ED, dtype, seed):
-    """Raw step sizes around softplus^-1 of the usual range, a bias, a gate."""
-    inp = synth.make_inputs(Bs, L, ED, 16, "f32", seed=seed)
-    raw = (0.7 * synth.normal(seed, 21, (Bs, L, ED)) - 3.5).astype(np.float32)
-    z = synth.normal(seed, 22, (Bs, L, ED))
-    bias = (0.3 * synth.normal(seed, 23, (ED,))).astype(np.float32)
-    inp["delta"] = raw
-    if dtype == "bf16":
-        for k in ("x", "delta", "B", "C"):
-            inp[k] = synth.to_bf16(inp[k])
-        z = synth.to_bf16(z)
-    return inp, dict(dt_bias=bias, dt_softplus=True, dt_limit=(1e-3, 0.1), z=z)
-
 
 @pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(2, 300, 64, "f32", False), (2, 301, 40, "f32", False),
                                                  (2, 257, 64, "bf16", False), (2, 200, 64, "f32", True),
