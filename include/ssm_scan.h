@@ -162,9 +162,11 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
  * gradient of the raw delta, ddelta' d delta'/d delta, where the derivative
  * is sigmoid(delta + dt_bias) (1 without softplus) and 0 where the clamp
  * holds delta' at a bound (taken as 0 at the bound itself), and ddt_bias[e]
- * is the sum of ddelta over rows and time. The output gate is not covered:
- * opts->z must be NULL (SSM_ERR_UNSUPPORTED otherwise); gate the output
- * gradient outside the call.
+ * is the sum of ddelta over rows and time. With the output gate (opts->z
+ * set), y = y' z sigmoid(z) for the ungated output y': dz = dy y' silu'(z)
+ * is written to dz, and the other gradients are those of y' for the output
+ * gradient dy z sigmoid(z). The call recomputes y' with the forward scan
+ * (into dz), forms both with an elementwise kernel, then runs the backward.
  *   x, delta, A, B, C, D, h0 : as ssm_scan_fwd (D and h0 may be NULL)
  *   opts    : step-size options of the forward, or NULL
  *   dy      : (Bs, L, ED) of dtype         -- dL/dy
@@ -175,19 +177,23 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
  *   dh0     : (Bs, ED, N) float32, or NULL (not computed)
  *   ddt_bias : (ED) float32, or NULL (not computed; with no option it is
  *              the sum of ddelta over rows and time)
- *   workspace : at least ssm_scan_bwd_workspace_bytes() bytes (required; it
- *     holds the state at every 32-step boundary and float32 partial sums of
- *     dB, dC, dA and dD), no initialisation needed.
+ *   dz      : (Bs, L, ED) of dtype -- the gate's gradient, required with
+ *             opts->z, ignored (may be NULL) without it
+ *   workspace : at least ssm_scan_bwd_workspace_bytes(..., gate) bytes,
+ *     gate = 1 when opts->z is set (required; it holds the state at every
+ *     32-step boundary and float32 partial sums of dB, dC, dA and dD; with
+ *     the gate also dy z sigmoid(z), one float32 value per element of x),
+ *     no initialisation needed.
  * Sums over channels (dB, dC) and over batch rows and time (dA, dD) are
  * taken in a fixed order, so repeated calls give identical bits.
  * Conventions, alignment and error codes as ssm_scan_fwd.
  */
-size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype);
+size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int gate);
 
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
-                 int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+                 int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward pass of the bidirectional scan: the gradients of L = sum(dy * y)
@@ -203,15 +209,16 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
  * (kept in float32 in the workspace for bfloat16 outputs, so that they are
  * rounded once); dB, dC and dA sum both passes' partials in a fixed order.
  * Arguments, outputs and conventions as ssm_scan_bwd; the workspace is
- * ssm_scan_bidir_bwd_workspace_bytes() bytes (both passes' partial sums and,
- * for bfloat16, two float32 values per element of x).
+ * ssm_scan_bidir_bwd_workspace_bytes(..., gate) bytes (both passes' partial
+ * sums and, for bfloat16, two float32 values per element of x; with the gate
+ * also dy z sigmoid(z)).
  */
-size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype);
+size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int gate);
 
 int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                        const float* D, const float* h0, const ssm_scan_options* opts, const void* dy, void* dx,
                        void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias,
-                       int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                       void* dz, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /*

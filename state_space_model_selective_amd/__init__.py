@@ -72,13 +72,13 @@ def lib():
         L.ssm_scan_fwd.restype = ci
         L.ssm_scan_bidir_fwd.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
-        L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+        L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_bwd_workspace_bytes.restype = sz
-        L.ssm_scan_bwd.argtypes = [vp] * 17 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bwd.restype = ci
-        L.ssm_scan_bidir_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+        L.ssm_scan_bidir_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_bidir_bwd_workspace_bytes.restype = sz
-        L.ssm_scan_bidir_bwd.argtypes = [vp] * 17 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_bwd.argtypes = [vp] * 18 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_bwd.restype = ci
         L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp]
         L.ssm_ssd_fwd.restype = ci
@@ -178,16 +178,16 @@ def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=N
     return y
 
 
-def ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32):
-    return int(lib().ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, int(dtype)))
+def ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32, gate=False):
+    return int(lib().ssm_scan_bwd_workspace_bytes(Bs, L, ED, N, int(dtype), int(bool(gate))))
 
 
-def ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32):
-    return int(lib().ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, int(dtype)))
+def ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32, gate=False):
+    return int(lib().ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, int(dtype), int(bool(gate))))
 
 
 def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias, dt_softplus,
-         dt_limit, want_ddt_bias):
+         dt_limit, want_ddt_bias, z):
     import torch
     if not x.is_cuda:
         raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
@@ -206,15 +206,19 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
         o.setdefault("dh0", torch.empty((Bs, ED, N), dtype=torch.float32, device=x.device))
     if want_ddt_bias or dt_bias is not None:
         o.setdefault("ddt_bias", torch.empty((ED,), dtype=torch.float32, device=x.device))
-    opts = _options(dt_bias, dt_softplus, dt_limit, None)
-    need = (ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm_scan_bwd_workspace_bytes)(Bs, L, ED, N, dt)
+    if z is not None:
+        o.setdefault("dz", torch.empty_like(x))
+    opts = _options(dt_bias, dt_softplus, dt_limit, z)
+    need = (ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm_scan_bwd_workspace_bytes)(Bs, L, ED, N, dt,
+                                                                                            z is not None)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn, name = (lib().ssm_scan_bidir_bwd, "ssm_scan_bidir_bwd") if bidir else (lib().ssm_scan_bwd, "ssm_scan_bwd")
     rc = fn(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts), _ptr(dy),
             _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
-            _ptr(o.get("dD")), _ptr(o.get("dh0")), _ptr(o.get("ddt_bias")), Bs, L, ED, N, dt, _ptr(workspace),
+            _ptr(o.get("dD")), _ptr(o.get("dh0")), _ptr(o.get("ddt_bias")), _ptr(o.get("dz")), Bs, L, ED, N, dt,
+            _ptr(workspace),
             ws_bytes, _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, name)
@@ -222,26 +226,26 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
 
 
 def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
-                 stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False):
+                 stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None):
     """Gradients of sum(dy * y) for y = ssm_scan_fwd(x, delta, A, B, C, D, h0=h0,
-    dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit) (no gate).
+    dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit, z=z).
 
     Returns a dict with dx, ddelta (like x; the raw delta's gradient), dA
     (like A), dB, dC (like B), dD (ED,) float32 if want_dD, dh0 (Bs, ED, N)
     float32 if want_dh0, ddt_bias (ED,) float32 if dt_bias is given or
-    want_ddt_bias. Tensors given in ``out`` (same keys) are written instead
-    of new ones.
+    want_ddt_bias, dz (like x) if z is given. Tensors given in ``out`` (same
+    keys) are written instead of new ones.
     """
     return _bwd(False, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias,
-                dt_softplus, dt_limit, want_ddt_bias)
+                dt_softplus, dt_limit, want_ddt_bias, z)
 
 
 def ssm_scan_bidir_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
-                       stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False):
+                       stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None):
     """Gradients of sum(dy * y) for y = ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0=h0,
-    <step-size options>), with the outputs of ssm_scan_bwd."""
+    <step-size options>, z=z), with the outputs of ssm_scan_bwd."""
     return _bwd(True, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias,
-                dt_softplus, dt_limit, want_ddt_bias)
+                dt_softplus, dt_limit, want_ddt_bias, z)
 
 
 def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=None, dt_bias=None,

@@ -64,6 +64,7 @@ struct BwdArgs {
   float dt_min, dt_max;
   double* pDB;       // [Bs][EDp]: ddt_bias partial of each batch row, or nullptr
   const T* dy;
+  const float* dyf;  // float32 output gradient read instead of dy (behind the gate; OPTS kernels only), or nullptr
   T* dx;
   T* ddl;
   float* dh0;        // or nullptr
@@ -155,7 +156,8 @@ __device__ __forceinline__ void add_c_dy(float (&gv)[4], float cq, float dyv) {
 // REV: the reverse-time scan of the bidirectional form. Virtual step t of the
 // sweeps is time L - 1 - t: every load and store maps the time, nothing else
 // changes (the inputs are read in place, no flipped copy).
-// OPTS: the forward ran with step-size options (delta' = the map of delta).
+// OPTS: the forward ran with step-size options (delta' = the map of delta);
+// these kernels also take the output gradient in float32 (dyf) when it is set.
 template <typename T, int RT, bool VEC, bool REV, bool OPTS>
 struct BwdStager {
   int row, chk;
@@ -192,13 +194,16 @@ struct BwdStager {
         if (VEC) {
           a = Vec4<T>::load(p.x + off);
           bb = Vec4<T>::load(p.dl + off);
-          if (WITH_ADJ) cc = Vec4<T>::load(p.dy + off);
+          if (WITH_ADJ) cc = (OPTS && p.dyf) ? Vec4<float>::load(p.dyf + off) : Vec4<T>::load(p.dy + off);
         } else {
           a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
                           ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
           bb = make_float4(to_f32(p.dl[off]), ce + 1 < ED ? to_f32(p.dl[off + 1]) : 0.f,
                            ce + 2 < ED ? to_f32(p.dl[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dl[off + 3]) : 0.f);
-          if (WITH_ADJ)
+          if (WITH_ADJ && OPTS && p.dyf)
+            cc = make_float4(p.dyf[off], ce + 1 < ED ? p.dyf[off + 1] : 0.f, ce + 2 < ED ? p.dyf[off + 2] : 0.f,
+                             ce + 3 < ED ? p.dyf[off + 3] : 0.f);
+          else if (WITH_ADJ)
             cc = make_float4(to_f32(p.dy[off]), ce + 1 < ED ? to_f32(p.dy[off + 1]) : 0.f,
                              ce + 2 < ED ? to_f32(p.dy[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dy[off + 3]) : 0.f);
         }
@@ -649,6 +654,23 @@ __global__ void bwd_reduce_ad_kernel(const double* __restrict__ pA, const double
   }
 }
 
+// The output gate: y = y' silu(z), y' the ungated output (held in dz on
+// entry, recomputed by the forward scan). dz = dy y' silu'(z) with
+// silu'(z) = s (1 + z (1 - s)), s = sigmoid(z), written over y'; the scan's
+// own output gradient is dy silu(z) (dyg, kept in float32: it is summed
+// over many steps and channels, where a rounding to bf16 would add up).
+template <typename T>
+__global__ void gate_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ z, T* dz, float* __restrict__ dyg,
+                                int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float zv = to_f32(z[i]), g = to_f32(dy[i]), yp = to_f32(dz[i]);
+    const float sg = 1.f / (1.f + __expf(-zv));
+    dz[i] = from_f32<T>(g * yp * sg * (1.f + zv * (1.f - sg)));
+    dyg[i] = g * zv * sg;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -711,43 +733,58 @@ int bwd_check_sizes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, Bwd
   return SSM_OK;
 }
 
-size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, bool bidir) {
+// With the gate the workspace also holds dy silu(z) (float32, one value per
+// element of x) after the backward's own area; the forward scan that
+// recomputes the ungated output runs first and borrows the start of it.
+// *gate_off: where dy silu(z) starts.
+size_t gated_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, bool bidir, const BwdSizes& s,
+                   size_t bwd_bytes, size_t* gate_off) {
+  const size_t fwd = ssm_scan_workspace_bytes(Bs, L, ED, N, dtype, bidir ? 1 : 0);
+  *gate_off = align256(std::max(bwd_bytes, fwd));
+  return *gate_off + align256(static_cast<size_t>(s.seq * 4));
+}
+
+size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, bool bidir, bool gate) {
   BwdSizes s;
   BwdLayout lo;
   if (bwd_check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || s.seq == 0 ||
       !bwd_layout(Bs, L, ED, &lo, bidir, bidir && dtype == SSM_BF16))
     return 0;
-  return lo.bytes;
+  size_t off;
+  return gate ? gated_bytes(Bs, L, ED, N, dtype, bidir, s, lo.bytes, &off) : lo.bytes;
 }
 
 int bwd_validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const ssm_scan_options* opts, const void* dy, const void* dx, const void* ddelta,
                  const float* dA, const void* dB, const void* dC, const float* dD, const float* dh0,
-                 const float* ddt_bias, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, const void* ws,
-                 size_t ws_bytes, bool bidir, BwdSizes* s) {
+                 const float* ddt_bias, const void* dz, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                 const void* ws, size_t ws_bytes, bool bidir, BwdSizes* s, size_t* gate_off) {
   int rc = bwd_check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
-  if (opts && opts->z) return SSM_ERR_UNSUPPORTED;                   // the gate's backward is not provided
   if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
+  const void* z = opts ? opts->z : nullptr;
+  if (!z) dz = nullptr;  // dz is written only with the gate
   // a buffer with no elements may be NULL
-  if ((s->seq > 0 && (!x || !delta || !dy || !dx || !ddelta)) || (s->bc > 0 && (!B || !C || !dB || !dC)) ||
-      (ED > 0 && (!A || !dA)))
+  if ((s->seq > 0 && (!x || !delta || !dy || !dx || !ddelta || (z && !dz))) ||
+      (s->bc > 0 && (!B || !C || !dB || !dC)) || (ED > 0 && (!A || !dA)))
     return SSM_ERR_NULL;
-  const void* ptrs[] = {x, delta, A, B, C, D, h0, dt_bias, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, ws};
+  const void* ptrs[] = {x, delta, A, B, C, D, h0, dt_bias, z, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, ws};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   BwdLayout lo;
   if (!bwd_layout(Bs, L, ED, &lo, bidir, bidir && dtype == SSM_BF16)) return SSM_ERR_DIM;
   if (s->seq == 0) lo.bytes = 0;  // nothing is scanned: no workspace
+  else if (z) lo.bytes = gated_bytes(Bs, L, ED, N, dtype, bidir, *s, lo.bytes, gate_off);
   if (lo.bytes > 0 && (!ws || ws_bytes < lo.bytes)) return SSM_ERR_WORKSPACE;
   const Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
                       rng(B, s->bc * s->elem),  rng(C, s->bc * s->elem),      rng(D, D ? ED * 4 : 0),
-                      rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem), rng(dt_bias, dt_bias ? ED * 4 : 0)};
+                      rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem), rng(dt_bias, dt_bias ? ED * 4 : 0),
+                      rng(z, z ? s->seq * s->elem : 0)};
   const Range out[] = {rng(dx, s->seq * s->elem), rng(ddelta, s->seq * s->elem), rng(dA, ED * N * 4),
                        rng(dB, s->bc * s->elem),  rng(dC, s->bc * s->elem),      rng(dD, dD ? ED * 4 : 0),
                        rng(dh0, dh0 ? s->state * 4 : 0), rng(ddt_bias, ddt_bias ? ED * 4 : 0),
-                       rng(ws, static_cast<int64_t>(lo.bytes))};
+                       rng(dz, dz ? s->seq * s->elem : 0), rng(ws, static_cast<int64_t>(lo.bytes))};
   constexpr int nout = sizeof(out) / sizeof(out[0]);
   for (int i = 0; i < nout; ++i) {
     if (out[i].hi == out[i].lo) continue;
@@ -778,7 +815,7 @@ template <typename T>
 int launch_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
                void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
-               void* ws, bool bidir, hipStream_t stream) {
+               void* ws, bool bidir, const float* dyf, hipStream_t stream) {
   const bool part_f32 = bidir && !std::is_same<T, float>::value;
   BwdLayout lo;
   bwd_layout(Bs, L, ED, &lo, bidir, part_f32);
@@ -799,7 +836,9 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.dt_max = opts ? opts->dt_max : INFINITY;
   // (a requested ddt_bias takes the options path: with no option the map is
   // the identity and ddt_bias is the sum of ddelta)
-  a.dt_pre = (a.dt_bias || a.dt_softplus || a.dt_min > -INFINITY || a.dt_max < INFINITY || ddt_bias) ? 1 : 0;
+  // the gated output gradient (dyf) is read by the options kernels too
+  a.dt_pre = (a.dt_bias || a.dt_softplus || a.dt_min > -INFINITY || a.dt_max < INFINITY || ddt_bias || dyf) ? 1 : 0;
+  a.dyf = dyf;
   a.pDB = ddt_bias ? reinterpret_cast<double*>(w + lo.pDB_off) : nullptr;
   a.dy = static_cast<const T*>(dy);
   a.dx = static_cast<T*>(dx);
@@ -864,13 +903,38 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
 
 int run_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
             const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-            void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
-            int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool bidir) {
+            void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+            int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool bidir) {
   BwdSizes s;
-  const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
-                              ED, N, dtype, workspace, workspace_bytes, bidir, &s);
+  size_t gate_off = 0;
+  const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, Bs,
+                              L, ED, N, dtype, workspace, workspace_bytes, bidir, &s, &gate_off);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  ssm_scan_options ungated{};
+  const float* dyf = nullptr;
+  if (opts && opts->z && s.seq > 0) {
+    // the gate: recompute the ungated output y' into dz, form dz and
+    // dy silu(z), then the backward of y' with that output gradient
+    ungated = *opts;
+    ungated.z = nullptr;
+    const int frc = bidir ? ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, &ungated, dz, nullptr, nullptr, Bs, L, ED,
+                                               N, dtype, workspace, gate_off, stream)
+                          : ssm_scan_fwd(x, delta, A, B, C, D, h0, &ungated, dz, nullptr, Bs, L, ED, N, dtype,
+                                         workspace, gate_off, stream);
+    if (frc != SSM_OK) return frc;
+    float* dyg = reinterpret_cast<float*>(static_cast<char*>(workspace) + gate_off);
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((s.seq + 255) / 256, 8192));
+    if (dtype == SSM_F32)
+      hipLaunchKernelGGL(gate_bwd_kernel<float>, dim3(grid), dim3(256), 0, st, static_cast<const float*>(dy),
+                         static_cast<const float*>(opts->z), static_cast<float*>(dz), dyg, s.seq);
+    else
+      hipLaunchKernelGGL(gate_bwd_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(dy),
+                         static_cast<const uint16_t*>(opts->z), static_cast<uint16_t*>(dz), dyg, s.seq);
+    if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
+    dyf = dyg;
+    opts = &ungated;
+  }
   if (s.seq == 0) {
     // an empty output: every gradient is zero (dB and dC too when there are
     // time steps but no channels)
@@ -881,38 +945,38 @@ int run_bwd(const void* x, const void* delta, const float* A, const void* B, con
   }
   if (dtype == SSM_F32)
     return launch_bwd<float>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
-                             ED, workspace, bidir, st);
+                             ED, workspace, bidir, dyf, st);
   return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
-                              ED, workspace, bidir, st);
+                              ED, workspace, bidir, dyf, st);
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
-  return bwd_workspace_bytes(Bs, L, ED, N, dtype, false);
+size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int gate) {
+  return bwd_workspace_bytes(Bs, L, ED, N, dtype, false, gate != 0);
 }
 
-size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype) {
-  return bwd_workspace_bytes(Bs, L, ED, N, dtype, true);
+size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int gate) {
+  return bwd_workspace_bytes(Bs, L, ED, N, dtype, true, gate != 0);
 }
 
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
-                 int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L, ED, N, dtype,
-                 workspace, workspace_bytes, stream, false);
+                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+                 int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, Bs, L, ED, N,
+                 dtype, workspace, workspace_bytes, stream, false);
 }
 
 int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                        const float* D, const float* h0, const ssm_scan_options* opts, const void* dy, void* dx,
                        void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias,
-                       int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                       void* dz, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L, ED, N, dtype,
-                 workspace, workspace_bytes, stream, true);
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, Bs, L, ED, N,
+                 dtype, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -104,10 +104,11 @@ def gather_channels(y, chans, ED):
 
 
 def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None, bidir=False,
-                dt_bias=None, dt_softplus=False, dt_limit=None):
+                dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
     """ssm_scan_bwd (bidir: ssm_scan_bidir_bwd) on the GPU; every gradient as
     a float64 numpy array. dt_bias (numpy, float32) / dt_softplus / dt_limit
-    are the step-size options; with dt_bias the result holds ddt_bias."""
+    are the step-size options; with dt_bias the result holds ddt_bias; z (like
+    x) is the output gate, and the result then holds dz."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -127,19 +128,23 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
     if dt_bias is not None:
         bias = torch.from_numpy(np.ascontiguousarray(dt_bias, dtype=np.float32)).to(dev)
         out["ddt_bias"] = torch.full((ED,), float("nan"), dtype=torch.float32, device=dev)
+    zt = None
+    if z is not None:
+        zt = to_device(dict(z=z), dev)["z"]
+        out["dz"] = torch.full_like(t["x"], float("nan"))
     fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
     res = fn(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
              h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream, dt_bias=bias,
-             dt_softplus=dt_softplus, dt_limit=dt_limit)
+             dt_softplus=dt_softplus, dt_limit=dt_limit, z=zt)
     torch.cuda.synchronize()
     return {k: y_to_numpy(v) for k, v in res.items()}
 
 
 def assert_grads_close(got, ref, dtype):
-    """Every gradient the GPU returned against the oracle's. dx, ddelta, dB
-    and dC carry the inputs' dtype; dA, dD and dh0 are float32."""
+    """Every gradient the GPU returned against the oracle's. dx, ddelta, dB,
+    dC and dz carry the inputs' dtype; dA, dD, dh0 and ddt_bias are float32."""
     for k, v in got.items():
-        tol = TOL[dtype] if k in ("dx", "ddelta", "dB", "dC") else TOL["f32"]
+        tol = TOL[dtype] if k in ("dx", "ddelta", "dB", "dC", "dz") else TOL["f32"]
         assert_close(k, v, ref[k], tol)
 
 

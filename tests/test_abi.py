@@ -162,7 +162,7 @@ def test_options_validation():
 
 
 BWD_PTRS = ["x", "delta", "A", "B", "C", "D", "h0", "opts", "dy", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0",
-            "ddt_bias", "ws"]
+            "ddt_bias", "dz", "ws"]
 
 
 def bwd(**kw):
@@ -170,7 +170,7 @@ def bwd(**kw):
     args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32)  # (opts is read on the host)
     args["ws_bytes"] = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32)
     args.update(kw)
-    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_PTRS[:17]], args["Bs"], args["L"], args["ED"], args["N"],
+    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_PTRS[:18]], args["Bs"], args["L"], args["ED"], args["N"],
                                   args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -191,7 +191,7 @@ def test_bwd_null_pointer(name):
 def test_bwd_optional_pointers_may_be_null():
     # D, h0, dD, dh0 are optional: with them NULL the call gets past the NULL
     # check and fails only on the fake (misaligned) workspace below
-    assert bwd(D=None, h0=None, dD=None, dh0=None, ws=P[17] + 4) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(D=None, h0=None, dD=None, dh0=None, ws=P[18] + 4) == ssm.SSM_ERR_UNSUPPORTED
 
 
 def test_bwd_empty_inputs_are_valid():
@@ -322,7 +322,7 @@ def bidir_bwd(**kw):
     args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_BF16)
     args["ws_bytes"] = ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
     args.update(kw)
-    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BWD_PTRS[:17]], args["Bs"], args["L"], args["ED"],
+    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BWD_PTRS[:18]], args["Bs"], args["L"], args["ED"],
                                         args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -353,9 +353,14 @@ def test_bidir_bwd_validation():
 
 
 def test_bwd_options_validation():
-    gated = ssm.SSMOptions(None, 1, -float("inf"), float("inf"), P[18])
-    assert bwd(opts=ctypes.byref(gated)) == ssm.SSM_ERR_UNSUPPORTED          # no backward through the gate
-    assert bidir_bwd(opts=ctypes.byref(gated)) == ssm.SSM_ERR_UNSUPPORTED
+    gated = ssm.SSMOptions(None, 1, -float("inf"), float("inf"), P[19])
+    assert bwd(opts=ctypes.byref(gated), dz=None) == ssm.SSM_ERR_NULL            # the gate needs dz
+    assert bidir_bwd(opts=ctypes.byref(gated), dz=None) == ssm.SSM_ERR_NULL
+    assert bwd(opts=ctypes.byref(gated)) == ssm.SSM_ERR_WORKSPACE                # and the larger workspace
+    assert bidir_bwd(opts=ctypes.byref(gated)) == ssm.SSM_ERR_WORKSPACE
+    need = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32, gate=True)
+    assert bwd(opts=ctypes.byref(gated), ws_bytes=need, dz=P[0]) == ssm.SSM_ERR_ALIAS   # dz on top of x
+    assert bwd(opts=ctypes.byref(gated), ws_bytes=need, dz=P[17] + 4) == ssm.SSM_ERR_UNSUPPORTED
     inverted = ssm.SSMOptions(None, 0, 0.5, 0.1, None)
     assert bwd(opts=ctypes.byref(inverted)) == ssm.SSM_ERR_ARG
     nan = ssm.SSMOptions(None, 0, float("nan"), 1.0, None)
@@ -363,3 +368,15 @@ def test_bwd_options_validation():
     misaligned = ssm.SSMOptions(P[19] + 4, 1, 0.0, 1.0, None)
     assert bwd(opts=ctypes.byref(misaligned)) == ssm.SSM_ERR_UNSUPPORTED
     assert bwd(ddt_bias=P[0]) == ssm.SSM_ERR_ALIAS                           # ddt_bias on top of x
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("dtype", [ssm.SSM_F32, ssm.SSM_BF16])
+def test_gated_backward_workspace(bidir, dtype):
+    """With the gate the workspace also holds dy silu(z): one float32 value
+    per element of x, after the backward's own area."""
+    q = ssm.ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm.ssm_scan_bwd_workspace_bytes
+    plain, gated = q(2, 300, 64, 16, dtype), q(2, 300, 64, 16, dtype, gate=True)
+    assert gated >= plain + 2 * 300 * 64 * 4
+    assert gated < plain + 2 * 300 * 64 * 4 + 1024
+    assert q(0, 300, 64, 16, dtype, gate=True) == 0

@@ -185,6 +185,7 @@ def check_options(Bs, L, ED, dtype, seed, opts, bidir=False, h0=False, inp=None)
     got = run_gpu_bwd(inp, dy, h0=h, want_dh0=True, bidir=bidir, **opts)
     ref = oracle.scan_bwd(**inp, dy=dy, h0=h, bidir=bidir, **opts)
     assert ("ddt_bias" in got) == (opts.get("dt_bias") is not None)
+    assert ("dz" in got) == (opts.get("z") is not None)
     assert_grads_close(got, ref, dtype)
 
 
@@ -216,3 +217,27 @@ def test_step_size_options_training_shape():
     _, opts = options_inputs(8, 1024, 1536, "bf16", seed=12)
     opts.pop("z")
     check_options(8, 1024, 1536, "bf16", 12, opts)
+
+
+# ---- backward through the output gate ---------------------------------------
+@pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(2, 300, 64, "f32", False), (2, 257, 40, "bf16", False),
+                                                 (2, 200, 64, "f32", True), (2, 150, 48, "bf16", True)])
+def test_gate_with_step_size_options(Bs, L, ED, dtype, bidir):
+    _, opts = options_inputs(Bs, L, ED, dtype, seed=L + ED + 7)
+    check_options(Bs, L, ED, dtype, L + ED + 7, opts, bidir=bidir, h0=True)
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_gate_alone(bidir):
+    # positive log-uniform steps, no other option; z ~ N(0, 1) and a few
+    # large |z| where the gate saturates (silu(z) ~ z, or ~ 0)
+    inp = synth.make_inputs(2, 150, 32, 16, "f32", seed=31)
+    z = synth.normal(31, 22, (2, 150, 32))
+    z[:, ::17, :] *= 30.0
+    check_options(2, 150, 32, "f32", 31, dict(z=z), bidir=bidir, inp=inp)
+
+
+def test_gate_training_shape():
+    # (Bs 8, L 1024, ED 1536), bf16, with every option
+    _, opts = options_inputs(8, 1024, 1536, "bf16", seed=13)
+    check_options(8, 1024, 1536, "bf16", 13, opts)
