@@ -74,9 +74,28 @@ struct Vec4<uint16_t> {
 // log(1 + e^v) (as log1p(e^v) for accuracy at small e^v); the output gate is
 // y z sigmoid(z). bias points at the channel's (or head's) bias, or is null.
 // ---------------------------------------------------------------------------
+// log(1 + u) for u >= 0 from the hardware logarithm, accurate to a few ulp:
+// with w = 1 + u rounded, log(w) u / (w - 1) cancels the rounding of w
+// (D. Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991, section 4.1); u itself when w rounds to 1.
+__device__ __forceinline__ float log1p_pos(float u) {
+  const float w = 1.f + u;
+  return w == 1.f ? u : __logf(w) * (u / (w - 1.f));
+}
+
+// e^x - 1 from the hardware exponential and logarithm (W. Kahan's method:
+// with v = e^x rounded, (v - 1) x / log(v) cancels the rounding of v); x
+// itself when v rounds to 1, -1 when v rounds to 0.
+__device__ __forceinline__ float expm1_fast(float x) {
+  const float v = __expf(x);
+  if (v == 1.f) return x;
+  const float vm = v - 1.f;
+  return vm == -1.f ? -1.f : vm * (x / __logf(v));
+}
+
 __device__ __forceinline__ float map_step(float d, const float* bias, int softplus, float lo, float hi) {
   if (bias) d += *bias;
-  if (softplus) d = d > 20.f ? d : log1pf(__expf(d));
+  if (softplus) d = d > 20.f ? d : log1p_pos(__expf(d));
   return fminf(fmaxf(d, lo), hi);
 }
 

@@ -163,6 +163,7 @@ struct BwdStager {
   int row, chk;
   bool is_xd, chunk_ok, row_ok;
   float4 ra, rb, rc;
+  float4 bias4;  // OPTS: dt_bias of the task's channels
   int64_t b, e0, ED, L;
   float4 dbacc = make_float4(0.f, 0.f, 0.f, 0.f);  // this task's raw step-size gradients, summed over its rounds
 
@@ -216,9 +217,19 @@ struct BwdStager {
   // the adjoint replay) -> global
   // d delta'/d delta from delta' itself: 0 where the clamp holds it at a bound,
   // else the softplus derivative sigmoid(v) = 1 - exp(-softplus(v)) (or 1)
+  // OPTS: the biases of the thread's 4 channels, loaded once (the channels
+  // of a staging task do not change between rounds)
+  __device__ __forceinline__ void load_bias(const BwdArgs<T>& p) {
+    bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!OPTS || !p.dt_bias || !is_xd || !chunk_ok) return;
+    const int64_t ce = e0 + 4 * chk;
+    bias4 = make_float4(p.dt_bias[ce], ce + 1 < ED ? p.dt_bias[ce + 1] : 0.f, ce + 2 < ED ? p.dt_bias[ce + 2] : 0.f,
+                        ce + 3 < ED ? p.dt_bias[ce + 3] : 0.f);
+  }
+
   __device__ __forceinline__ float map_deriv(const BwdArgs<T>& p, float m) const {
     if (m <= p.dt_min || m >= p.dt_max) return 0.f;
-    return p.dt_softplus ? -expm1f(-m) : 1.f;
+    return p.dt_softplus ? -expm1_fast(-m) : 1.f;
   }
 
   __device__ __forceinline__ void store_grads(const BwdArgs<T>& p, const BwdTile<RT>& tl, int64_t rr) {
@@ -280,13 +291,13 @@ struct BwdStager {
       *reinterpret_cast<float4*>(&tl.xv[row][c4]) = ra;
       float4 dv = rb;
       if constexpr (OPTS) {
+        // (the chunk's biases are in registers: bias4, zero without a bias)
         const bool ok = row_ok && chunk_ok;
         const int64_t ce = e0 + c4;
-        const float* bias = p.dt_bias;
-        dv.x = ok && ce + 0 < ED ? map_step(dv.x, bias ? bias + ce + 0 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
-        dv.y = ok && ce + 1 < ED ? map_step(dv.y, bias ? bias + ce + 1 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
-        dv.z = ok && ce + 2 < ED ? map_step(dv.z, bias ? bias + ce + 2 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
-        dv.w = ok && ce + 3 < ED ? map_step(dv.w, bias ? bias + ce + 3 : nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.x = ok && ce + 0 < ED ? map_step(dv.x + bias4.x, nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.y = ok && ce + 1 < ED ? map_step(dv.y + bias4.y, nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.z = ok && ce + 2 < ED ? map_step(dv.z + bias4.z, nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
+        dv.w = ok && ce + 3 < ED ? map_step(dv.w + bias4.w, nullptr, p.dt_softplus, p.dt_min, p.dt_max) : 0.f;
       }
       *reinterpret_cast<float4*>(&tl.dt[row][c4]) = dv;
       if (WITH_ADJ) *reinterpret_cast<float4*>(&tl.dy[row][c4]) = rc;
@@ -355,6 +366,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
 
   BwdStager<T, RT, VEC, REV, OPTS> st;
   st.init(tid, b, e0, ED, L);
+  st.load_bias(p);
   // checkpoint of round rr for this lane's 4 states
   auto ck = [&](int64_t rr) { return p.ckpt + ((b * R + rr) * p.EDp + e) * 16 + 4 * g; };
 
