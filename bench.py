@@ -7,9 +7,15 @@ gradient). Three input sets are rotated so that consecutive steps do not
 re-read a working set left in the 256 MB last-level cache.
 
 Prints ONE JSON line. `value` is scan elements (Bs*L*ED*N) per second;
-`roofline` describes the dominant kernel (its per-launch time is measured with
-HIP events on the stream it is launched on); `cpu_baseline` is the fp64 oracle
-on the host cores over the same workload.
+`roofline` describes the dominant kernel against the HBM peak (algorithmic
+bytes per launch over its per-launch time, measured with HIP events on the
+stream it is launched on); `valu` puts the same time against the vector-ALU
+issue peak; `cpu_baseline` is the fp64 oracle on the host cores over the same
+workload.
+
+`--micro valu` instead measures the vector ALU's issue rates (float32 FMA,
+v_exp_f32, and the two mixed 4:1) with the probe kernels of
+csrc/valu_probe.hip; the ALU cost model below rests on those rates.
 """
 import argparse
 import hashlib
@@ -21,7 +27,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-DEFAULT_WORKLOAD = "fwd_f32_Bs8_L1024_ED1536_N16"
+# the largest single-GPU configuration: the long-sequence float32 scan (Bs 1,
+# L 2^17, ED 2048, N 16), which splits the sequence across workgroups
+DEFAULT_WORKLOAD = "fwd_f32_Bs1_L131072_ED2048_N16"
 METRIC = "scan elements (Bs·L·ED·N)/s and achieved HBM GB/s vs MI355X peak"
 
 # MI355X published figures
@@ -29,10 +37,16 @@ HBM_PEAK_GBPS = 8000.0
 CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
 # fp32 VALU issue slots per second (one non-packed lane-op per lane per clock)
 VALU_SLOTS_PER_S = CUS * SIMDS * LANES * CLOCK_GHZ * 1e9
+# issue slots one v_exp_f32 takes, in float32 FMA slots: the ratio of the two
+# issue rates that `bench.py --micro valu` measures (FMA 34.2 T, exp 17.9 T
+# lane-ops/s on the MI355X: 1.91; rounded to 2)
+EXP_SLOTS = 2.0
 # algorithmic VALU cost of one scan element: delta*A, (delta x)*B, the state
-# FMA, the C FMA (4 full-rate slots) + one v_exp_f32 (half rate on gfx950: 2)
-SLOTS_PER_ELEMENT = 6.0
-SLOTS_PER_ELEMENT_BIDIR = 8.0
+# FMA, the C FMA (4 full-rate slots) + one v_exp_f32
+SLOTS_PER_ELEMENT = 4.0 + EXP_SLOTS
+# bidirectional: the exp and the two multiplies are shared by both
+# directions; 2 mul + exp + 2 x (state FMA + C FMA)
+SLOTS_PER_ELEMENT_BIDIR = 6.0 + EXP_SLOTS
 # backward: rebuild the state (delta*A, exp, (delta x)*B, state FMA: 5) and
 # the adjoint with its terms (g FMA, k = a g, dC and dB products, sum g B,
 # q = g a h_{t-1} (2), sum A q, dA += delta q: 9)
@@ -96,10 +110,31 @@ def load_traffic(workload, src_hash):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_cpus():
+    """CPUs this process may run on (the host's core count as the scheduler
+    offers it), and the host's total."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return avail, os.cpu_count() or avail
+
+
+def oracle_threads():
+    """Threads the oracle baseline runs on: every CPU offered, at most 16 (a
+    GPU machine shares its host between 8 GPUs: 16 CPUs per GPU)."""
+    return min(16, host_cpus()[0])
+
+
+def cpu_fields(threads):
+    avail, total = host_cpus()
+    return dict(cores=threads, threads=threads, host_cpus_available=avail, host_cpus_total=total)
+
+
 def cpu_baseline(inp, w, budget_s=20.0):
     import numpy as np
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     Bs, ED = w["Bs"], w["ED"]
     E_per_channel = w["L"] * w["N"] * (2 if w["bidir"] else 1)
     # time a small sample first, then size the measured sample to the budget
@@ -125,7 +160,7 @@ def cpu_baseline(inp, w, budget_s=20.0):
     sample = ("all %d channels" % n_eff) if chans is None else ("%d of %d channels, every time step" % (n_eff, Bs * ED))
     if reps > 1:
         sample += ", %d runs" % reps
-    return dict(value=rate, unit="scan elements/s", cores=threads, kind="oracle",
+    return dict(value=rate, unit="scan elements/s", **cpu_fields(threads), kind="oracle",
                 sample=sample + " (fp64 sequential recurrence, %.2f s)" % dt), y_ref, chans
 
 
@@ -134,7 +169,7 @@ def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
     many as fit the time budget, at least one)."""
     import numpy as np
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     Bs = w["Bs"]
 
     def rows(k):
@@ -154,7 +189,7 @@ def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
         dt = time.perf_counter() - t0
     E = k * w["L"] * w["ED"] * w["N"]
     sample = ("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))
-    return dict(value=E / dt, unit="scan elements/s", cores=threads, kind="oracle",
+    return dict(value=E / dt, unit="scan elements/s", **cpu_fields(threads), kind="oracle",
                 sample=sample + " (fp64 forward states + adjoint, %.2f s)" % dt), ref, k
 
 
@@ -236,7 +271,7 @@ def bench_ssd(args, name):
     cpu = parity = None
     if not args.no_cpu:
         import oracle
-        threads = min(16, os.cpu_count() or 1)
+        threads = oracle_threads()
 
         def rows(k):
             return {n: (v[:k] if v.ndim >= 3 else v) for n, v in host0.items()}
@@ -247,7 +282,7 @@ def bench_ssd(args, name):
         t1 = time.perf_counter()
         y_ref, _, _ = oracle.ssd(**rows(k), bidir=bidir, nthreads=threads)
         dtk = time.perf_counter() - t1
-        cpu = dict(value=k * L * H * P * N / dtk, unit="scan elements/s", cores=threads, kind="oracle",
+        cpu = dict(value=k * L * H * P * N / dtk, unit="scan elements/s", **cpu_fields(threads), kind="oracle",
                    sample=(("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))) +
                    " (fp64 sequential recurrence, %.2f s)" % dtk)
         step(sets[0])
@@ -305,6 +340,57 @@ def bench_ssd(args, name):
     print(json.dumps(out))
 
 
+def micro_valu(args):
+    """Issue rates of the vector ALU: launches of 256-thread workgroups (one
+    wave per SIMD each), 1, 2, 4 or 8 workgroups per compute unit, each thread
+    running 8 independent chains; the rate is lane-operations per second of
+    the kernel time (HIP events around `steps` launches on one stream)."""
+    import ctypes
+    import torch
+    import state_space_model_selective_amd as ssm
+    P = ssm.probe_lib()
+    dev = torch.device("cuda:0")
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(8 * ncu * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kinds = ((0, "fma", 4096), (1, "exp", 2048), (2, "exp_plus_4_fma", 1024), (3, "fma_dpp_operand", 4096))
+    res = {}
+    for wps in (1, 2, 4, 8):
+        blocks = wps * ncu
+        for kind, name, iters in kinds:
+            nf, ne = ctypes.c_int(), ctypes.c_int()
+            P.ssm_probe_valu_ops_per_iter(kind, ctypes.byref(nf), ctypes.byref(ne))
+            it = max(1, iters * 2 // wps) if wps < 8 else iters
+            for _ in range(max(1, args.warmup)):
+                assert P.ssm_probe_valu_launch(kind, blocks, it, out.data_ptr(), stream.cuda_stream) == 0
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                assert P.ssm_probe_valu_launch(kind, blocks, it, out.data_ptr(), stream.cuda_stream) == 0
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            t = ev0.elapsed_time(ev1) / 1e3 / args.steps
+            lanes = blocks * 256 * it
+            res["%s_waves_per_simd_%d" % (name, wps)] = {
+                "kernel_avg_us": t * 1e6, "iters": it, "fma_lane_ops_per_s": lanes * nf.value / t,
+                "exp_lane_ops_per_s": lanes * ne.value / t}
+    fma = res["fma_waves_per_simd_8"]["fma_lane_ops_per_s"]
+    ex = res["exp_waves_per_simd_8"]["exp_lane_ops_per_s"]
+    mixed = res["exp_plus_4_fma_waves_per_simd_8"]["exp_lane_ops_per_s"]
+    print(json.dumps({
+        "micro": "valu",
+        "compute_units": ncu,
+        "rates": res,
+        "fma_lane_ops_per_s": fma,
+        "exp_lane_ops_per_s": ex,
+        "fma_frac_of_157_3_tflops": 2 * fma / 157.3e12,
+        "exp_slots_alone": fma / ex,
+        "exp_slots_mixed_with_4_fma": fma / mixed - 4.0,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +398,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU-baseline leg")
+    ap.add_argument("--micro", choices=["valu"], default=None,
+                    help="instead of the scan, measure the vector ALU issue rates (float32 FMA, v_exp_f32, mixed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the scan, run plain device copies of MIB MiB (a known-size reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and print their size")
@@ -325,6 +413,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.micro == "valu":
+        micro_valu(args)
+        return
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -471,23 +563,28 @@ def main():
         "config": {"workload": args.workload, "Bs": Bs, "L": L, "ED": ED, "N": N, "bidir": w["bidir"],
                    "h_last": w["h_last"], "backward": bwd, "parallelism": "single GPU"},
         "roofline": {
-            "bound": "alu",
-            "achieved": achieved_slots / 1e12,
-            "peak": VALU_SLOTS_PER_S / 1e12,
-            "unit": "T VALU-slot/s",
-            "frac": achieved_slots / VALU_SLOTS_PER_S,
+            "bound": "hbm",
+            "achieved": bytes_alg / avg_launch_s / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": bytes_alg / avg_launch_s / 1e9 / HBM_PEAK_GBPS,
             "traffic": traffic,
+            "alg_bytes_per_launch": bytes_alg,
             "kernel_avg_us": avg_launch_s * 1e6,
             "timed": (("whole backward step: the scan kernel (once per direction) and the two small kernels "
                        "that add up the dB/dC and dA/dD partial sums") if bwd else
                       "the scan kernel (one launch per step)"),
-            "slots_per_element": slots,
         },
-        "hbm": {
-            "alg_bytes_per_launch": bytes_alg,
-            "achieved_GBps": bytes_alg / avg_launch_s / 1e9,
-            "peak_GBps": HBM_PEAK_GBPS,
-            "frac": bytes_alg / avg_launch_s / 1e9 / HBM_PEAK_GBPS,
+        # the same kernel time against the vector ALU, the resource that
+        # actually bounds the scan (one exp per element; see --micro valu)
+        "valu": {
+            "achieved": achieved_slots / 1e12,
+            "peak": VALU_SLOTS_PER_S / 1e12,
+            "unit": "T VALU-slot/s",
+            "frac": achieved_slots / VALU_SLOTS_PER_S,
+            "slots_per_element": slots,
+            "exp_slots": EXP_SLOTS,
+            "peak_from": "256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, non-packed float32",
         },
         "kernel_source_sha256_16": src_hash,
         "parity": parity,

@@ -15,6 +15,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libssm_scan.so")
 SOURCES = [os.path.join(_HERE, "csrc", n) for n in ("ssm_scan.hip", "ssm_scan_bwd.hip", "ssm_ssd.hip")]
+# issue-rate probe of the vector ALU (measurement only; used by the benchmark's --micro mode)
+PROBE_LIB_PATH = os.path.join(_HERE, "libssm_valu_probe.so")
+PROBE_SOURCES = [os.path.join(_HERE, "csrc", "valu_probe.hip")]
 INCLUDE = os.path.join(_ROOT, "include")
 
 SSM_F32, SSM_BF16 = 0, 1
@@ -35,6 +38,7 @@ HIPCC_FLAGS = [
 ]
 
 _lib = None
+_probe = None
 
 
 class SSMError(RuntimeError):
@@ -43,19 +47,26 @@ class SSMError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
 
 
-def build(verbose=False):
-    """Compile libssm_scan.so for gfx950 with hipcc (works without a GPU)."""
+def _hipcc(sources, out, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc] + HIPCC_FLAGS + ["-I", INCLUDE] + SOURCES + ["-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc] + HIPCC_FLAGS + ["-I", INCLUDE] + sources + ["-o", tmp]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout)
     if verbose:
         print(res.stdout)
-    os.replace(tmp, LIB_PATH)
-    global _lib
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    """Compile libssm_scan.so (and the ALU issue-rate probe) for gfx950 with
+    hipcc (works without a GPU)."""
+    _hipcc(SOURCES, LIB_PATH, verbose)
+    _hipcc(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
+    global _lib, _probe
     _lib = None
+    _probe = None
 
 
 def lib():
@@ -92,6 +103,23 @@ def lib():
     return _lib
 
 
+def probe_lib():
+    """The ALU issue-rate probe library (measurement only)."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError("libssm_valu_probe.so is not built (run __graft_entry__.build())")
+        P = ctypes.CDLL(PROBE_LIB_PATH)
+        P.ssm_probe_valu_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        P.ssm_probe_valu_launch.restype = ctypes.c_int
+        P.ssm_probe_valu_ops_per_iter.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                                  ctypes.POINTER(ctypes.c_int)]
+        P.ssm_probe_valu_ops_per_iter.restype = ctypes.c_int
+        _probe = P
+    return _probe
+
+
 def status_str(status):
     return lib().ssm_status_str(int(status)).decode()
 
@@ -113,20 +141,110 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _prepare(x, delta, A, B, C, D, y, bidir, workspace):
+class _Args:
+    """Checks every tensor of one call against x (dtype, shape, contiguity,
+    device) before any pointer is taken: the C ABI sees only addresses and
+    sizes, so a tensor of the wrong dtype, shape or layout would be misread
+    there. The GPU check comes last (check_gpu), so that each rejection also
+    shows on CPU tensors."""
+
+    def __init__(self, where, x, ndim):
+        import torch
+        self.where = where
+        if not isinstance(x, torch.Tensor):
+            raise TypeError("%s: x must be a torch.Tensor, got %s" % (where, type(x).__name__))
+        if x.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("%s: x must be float32 or bfloat16, got %s" % (where, x.dtype))
+        if x.dim() != ndim:
+            raise ValueError("%s: x must have %d dimensions, got shape %s" % (where, ndim, tuple(x.shape)))
+        self.x = x
+        self.dtype = x.dtype
+        self.device = x.device
+        self.check("x", x, tuple(x.shape))
+
+    def check(self, name, t, shape, dtype=None, required=False):
+        """t may be None unless required; dtype None means x's dtype."""
+        import torch
+        if t is None:
+            if required:
+                raise ValueError("%s: %s is required" % (self.where, name))
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: %s must be a torch.Tensor, got %s" % (self.where, name, type(t).__name__))
+        want = self.dtype if dtype is None else dtype
+        if t.dtype != want:
+            raise TypeError("%s: %s must be %s, got %s" % (self.where, name, want, t.dtype))
+        if t.device != self.device:
+            raise ValueError("%s: %s is on %s, x on %s" % (self.where, name, t.device, self.device))
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s: %s must have shape %s, got %s" % (self.where, name, tuple(shape), tuple(t.shape)))
+        if not t.is_contiguous():
+            raise ValueError("%s: %s must be contiguous (dense row-major)" % (self.where, name))
+
+    def matrix(self, name, t, rows):
+        """A 2-D float32 tensor with `rows` rows; returns its column count."""
+        import torch
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError("%s: %s must be a 2-D tensor" % (self.where, name))
+        self.check(name, t, (rows, t.shape[1]), torch.float32, required=True)
+        return int(t.shape[1])
+
+    def workspace(self, t):
+        import torch
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: workspace must be a torch.Tensor" % self.where)
+        if t.device != self.device:
+            raise ValueError("%s: workspace is on %s, x on %s" % (self.where, t.device, self.device))
+        if not t.is_contiguous():
+            raise ValueError("%s: workspace must be contiguous" % self.where)
+
+    def limit(self, dt_limit):
+        if dt_limit is None:
+            return
+        if len(dt_limit) != 2:
+            raise ValueError("%s: dt_limit must be a pair (lo, hi)" % self.where)
+
+    def check_gpu(self):
+        if not self.x.is_cuda:
+            raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % self.x.device)
+
+
+def _scan_args(where, x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace, outs):
+    """Validates the per-channel scan's arguments; returns (checker, dims).
+    outs: (name, tensor, kind[, required]) with kind 'seq' (like x), 'bc'
+    (like B), 'state' (Bs, ED, N) float32, 'ed' (ED,) float32, 'a' (ED, N)
+    float32."""
     import torch
-    if not x.is_cuda:
-        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
-    dt = _dtype_code(x)
-    Bs, L, ED = x.shape
-    N = A.shape[1]
-    if y is None:
-        y = torch.empty_like(x)
-    need = ssm_scan_workspace_bytes(Bs, L, ED, N, dt, bidir)
+    a = _Args(where, x, 3)
+    Bs, L, ED = (int(v) for v in x.shape)
+    N = a.matrix("A", A, ED)
+    f32 = torch.float32
+    a.check("delta", delta, (Bs, L, ED), required=True)
+    a.check("B", B, (Bs, L, N), required=True)
+    a.check("C", C, (Bs, L, N), required=True)
+    a.check("D", D, (ED,), f32)
+    a.check("h0", h0, (Bs, ED, N), f32)
+    a.check("dt_bias", dt_bias, (ED,), f32)
+    a.check("z", z, (Bs, L, ED))
+    a.limit(dt_limit)
+    shapes = {"seq": ((Bs, L, ED), None), "bc": ((Bs, L, N), None), "state": ((Bs, ED, N), f32),
+              "ed": ((ED,), f32), "a": ((ED, N), f32)}
+    for name, t, kind, *req in outs:
+        shp, dt = shapes[kind]
+        a.check(name, t, shp, dt, required=bool(req and req[0]))
+    a.workspace(workspace)
+    a.check_gpu()
+    return a, (Bs, L, ED, N)
+
+
+def _workspace(workspace, need, device):
+    import torch
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return dt, (Bs, L, ED, N), y, workspace, ws_bytes
+    return workspace, ws_bytes
 
 
 def _options(dt_bias, dt_softplus, dt_limit, z):
@@ -153,7 +271,13 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None,
     """y = selective_scan(x, delta, A, B, C, D) from initial state h0 (zero if None);
     optionally the final state into h_last. dt_bias / dt_softplus / dt_limit
     pre-process delta, z gates the output (y * silu(z))."""
-    dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, False, workspace)
+    _, (Bs, L, ED, N) = _scan_args("ssm_scan_fwd", x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
+                                   [("y", y, "seq"), ("h_last", h_last, "state")])
+    dt = _dtype_code(x)
+    if y is None:
+        import torch
+        y = torch.empty_like(x)
+    workspace, ws_bytes = _workspace(workspace, ssm_scan_workspace_bytes(Bs, L, ED, N, dt, False), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
     rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
                             _ptr(y), _ptr(h_last),
@@ -167,7 +291,14 @@ def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=N
                        stream=None, h0=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
     """y = forward scan (from h0, zero if None) + reverse-time scan (shared
     weights, read in place) + D x, with the same options as ssm_scan_fwd."""
-    dt, (Bs, L, ED, N), y, workspace, ws_bytes = _prepare(x, delta, A, B, C, D, y, True, workspace)
+    _, (Bs, L, ED, N) = _scan_args("ssm_scan_bidir_fwd", x, delta, A, B, C, D, h0, dt_bias, dt_limit, z,
+                                   workspace, [("y", y, "seq"), ("h_last", h_last, "state"),
+                                               ("g_first", g_first, "state")])
+    dt = _dtype_code(x)
+    if y is None:
+        import torch
+        y = torch.empty_like(x)
+    workspace, ws_bytes = _workspace(workspace, ssm_scan_workspace_bytes(Bs, L, ED, N, dt, True), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
     rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
                                   _byref(opts), _ptr(y),
@@ -189,12 +320,16 @@ def ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32, gate=False):
 def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias, dt_softplus,
          dt_limit, want_ddt_bias, z):
     import torch
-    if not x.is_cuda:
-        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
-    dt = _dtype_code(x)
-    Bs, L, ED = x.shape
-    N = A.shape[1]
+    where = "ssm_scan_bidir_bwd" if bidir else "ssm_scan_bwd"
     o = dict(out or {})
+    known = {"dx": "seq", "ddelta": "seq", "dA": "a", "dB": "bc", "dC": "bc", "dD": "ed", "dh0": "state",
+             "ddt_bias": "ed", "dz": "seq"}
+    for k in o:
+        if k not in known:
+            raise ValueError("%s: unknown output %r" % (where, k))
+    a, (Bs, L, ED, N) = _scan_args(where, x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
+                                   [("dy", dy, "seq", True)] + [(k, v, known[k]) for k, v in o.items()])
+    dt = _dtype_code(x)
     o.setdefault("dx", torch.empty_like(x))
     o.setdefault("ddelta", torch.empty_like(x))
     o.setdefault("dA", torch.empty((ED, N), dtype=torch.float32, device=x.device))
@@ -211,17 +346,15 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
     need = (ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm_scan_bwd_workspace_bytes)(Bs, L, ED, N, dt,
                                                                                             z is not None)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    fn, name = (lib().ssm_scan_bidir_bwd, "ssm_scan_bidir_bwd") if bidir else (lib().ssm_scan_bwd, "ssm_scan_bwd")
+    workspace, ws_bytes = _workspace(workspace, need, x.device)
+    fn = lib().ssm_scan_bidir_bwd if bidir else lib().ssm_scan_bwd
     rc = fn(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts), _ptr(dy),
             _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
             _ptr(o.get("dD")), _ptr(o.get("dh0")), _ptr(o.get("ddt_bias")), _ptr(o.get("dz")), Bs, L, ED, N, dt,
             _ptr(workspace),
             ws_bytes, _stream(x, stream))
     if rc != SSM_OK:
-        raise SSMError(rc, name)
+        raise SSMError(rc, where)
     return o
 
 
@@ -248,6 +381,34 @@ def ssm_scan_bidir_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0
                 dt_softplus, dt_limit, want_ddt_bias, z)
 
 
+def _ssd_args(where, x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace, outs):
+    """Validates the multi-head scan's arguments; returns (Bs, L, H, P, G, N)."""
+    import torch
+    a = _Args(where, x, 4)
+    Bs, L, H, P = (int(v) for v in x.shape)
+    f32 = torch.float32
+    if not isinstance(B, torch.Tensor) or B.dim() != 4:
+        raise ValueError("%s: B must be a 4-D tensor (Bs, L, G, N)" % where)
+    G, N = int(B.shape[2]), int(B.shape[3])
+    a.check("dt", dt, (Bs, L, H), required=True)
+    a.check("A", A, (H,), f32, required=True)
+    a.check("B", B, (Bs, L, G, N), required=True)
+    a.check("C", C, (Bs, L, G, N), required=True)
+    a.check("D", D, (H,), f32)
+    a.check("h0", h0, (Bs, H, P, N), f32)
+    a.check("dt_bias", dt_bias, (H,), f32)
+    a.check("z", z, (Bs, L, H, P))
+    a.limit(dt_limit)
+    for name, t, kind in outs:
+        if kind == "seq":
+            a.check(name, t, (Bs, L, H, P))
+        else:
+            a.check(name, t, (Bs, H, P, N), f32)
+    a.workspace(workspace)
+    a.check_gpu()
+    return Bs, L, H, P, G, N
+
+
 def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=None, dt_bias=None,
                 dt_softplus=False, dt_limit=None, z=None):
     """Multi-head selective scan: x (Bs, L, H, P), dt (Bs, L, H), A (H,),
@@ -256,11 +417,9 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=Non
     the output. Returns y (Bs, L, H, P); the final state goes to h_last if
     given."""
     import torch
-    if not x.is_cuda:
-        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
+    Bs, L, H, P, G, N = _ssd_args("ssm_ssd_fwd", x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, None,
+                                  [("y", y, "seq"), ("h_last", h_last, "state")])
     dtc = _dtype_code(x)
-    Bs, L, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     if y is None:
         y = torch.empty_like(x)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
@@ -284,17 +443,12 @@ def ssm_ssd_bidir_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, g_first=None,
     ssm_ssd_fwd (the gate applies to the sum). Returns y; the final states
     go to h_last (forward) and g_first (reverse) if given."""
     import torch
-    if not x.is_cuda:
-        raise RuntimeError("the selective scan runs on the GPU only; x is on %s" % x.device)
+    Bs, L, H, P, G, N = _ssd_args("ssm_ssd_bidir_fwd", x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
+                                  [("y", y, "seq"), ("h_last", h_last, "state"), ("g_first", g_first, "state")])
     dtc = _dtype_code(x)
-    Bs, L, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     if y is None:
         y = torch.empty_like(x)
-    need = lib().ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtc)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    workspace, wsb = _workspace(workspace, lib().ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtc), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
     rc = lib().ssm_ssd_bidir_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
                                  _ptr(y), _ptr(h_last), _ptr(g_first), Bs, L, H, P, G, N, dtc, _ptr(workspace), wsb,
