@@ -75,7 +75,8 @@ typedef enum {
   SSM_ERR_ALIAS = 4,       /* an output overlaps an input, another output or the workspace */
   SSM_ERR_WORKSPACE = 5,   /* workspace smaller than ssm_scan_workspace_bytes() */
   SSM_ERR_LAUNCH = 6,      /* the HIP runtime rejected a launch */
-  SSM_ERR_ARG = 7          /* an option is invalid (dt_min > dt_max, or a NaN bound) */
+  SSM_ERR_ARG = 7,         /* an option is invalid (dt_min > dt_max, or a NaN bound) */
+  SSM_ERR_HANDOFF = 8      /* ssm_scan_fwd_status only: a split-sequence hand-off wait gave up */
 } ssm_status;
 
 /*
@@ -115,6 +116,14 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
 
 /*
  * Forward selective scan (the recurrence above).
+ * Long sequences with little channel parallelism are split into chunks that
+ * run concurrently and hand their end states on through the workspace; each
+ * chunk takes its place in the sequence from an atomic ticket, so a chunk's
+ * predecessor has always started (no assumption on which workgroups are
+ * resident, and other work may share the device). A hand-off wait is
+ * bounded (about seven seconds); if it ever gives up, the chunk's outputs,
+ * every later chunk's and h_last become NaN, and ssm_scan_fwd_status()
+ * reports SSM_ERR_HANDOFF.
  *   x, delta : (Bs, L, ED) of dtype        -- input sequence and step sizes
  *   A        : (ED, N) float32             -- state matrix (diagonal per channel)
  *   B, C     : (Bs, L, N) of dtype         -- input and output projections
@@ -128,6 +137,17 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                  const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last, int64_t Bs, int64_t L, int64_t ED,
                  int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Outcome of the split-sequence hand-off of the last ssm_scan_fwd call made
+ * with this workspace and these sizes: synchronises `stream`, then returns
+ * SSM_ERR_HANDOFF if a wait gave up (that call's affected outputs are NaN),
+ * SSM_OK otherwise (also when these sizes do not split the sequence, or the
+ * input is empty). Size errors as ssm_scan_fwd; SSM_ERR_NULL or
+ * SSM_ERR_WORKSPACE if a split call's workspace is missing or too small.
+ */
+int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t Bs, int64_t L, int64_t ED,
+                        int64_t N, int dtype, void* stream);
 
 /*
  * Bidirectional selective scan (forward plus reverse-time scan plus D x).

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(_ROOT, "include")
 
 SSM_F32, SSM_BF16 = 0, 1
 (SSM_OK, SSM_ERR_NULL, SSM_ERR_DIM, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH,
- SSM_ERR_ARG) = range(8)
+ SSM_ERR_ARG, SSM_ERR_HANDOFF) = range(9)
 
 
 class SSMOptions(ctypes.Structure):
@@ -83,6 +83,8 @@ def lib():
         L.ssm_scan_fwd.restype = ci
         L.ssm_scan_bidir_fwd.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
+        L.ssm_scan_fwd_status.argtypes = [vp, sz] + [i64] * 4 + [ci, vp]
+        L.ssm_scan_fwd_status.restype = ci
         L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_bwd_workspace_bytes.restype = sz
         L.ssm_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [ci, vp, sz, vp]
@@ -285,6 +287,23 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None,
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_fwd")
     return y
+
+
+def ssm_scan_fwd_status(x, A, workspace, stream=None):
+    """Outcome of the split-sequence hand-off of the last ssm_scan_fwd call on
+    tensors shaped like x and A with this workspace: synchronises the stream,
+    returns SSM_OK or SSM_ERR_HANDOFF (a hand-off wait gave up; that call's
+    affected outputs are NaN); raises SSMError for argument errors."""
+    a = _Args("ssm_scan_fwd_status", x, 3)
+    Bs, L, ED = (int(v) for v in x.shape)
+    N = a.matrix("A", A, ED)
+    a.workspace(workspace)
+    a.check_gpu()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ssm_scan_fwd_status(_ptr(workspace), ws_bytes, Bs, L, ED, N, _dtype_code(x), _stream(x, stream))
+    if rc not in (SSM_OK, SSM_ERR_HANDOFF):
+        raise SSMError(rc, "ssm_scan_fwd_status")
+    return rc
 
 
 def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=None, workspace=None,

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -76,9 +77,25 @@ namespace {
 // sequence too long for the available channel parallelism is cut into
 // chunks that run concurrently; chunk k hands its inclusive end state to
 // chunk k+1 through `state` and `flag`.
+//
+// Protocol. Each workgroup first takes a ticket (an atomic counter in this
+// header, cleared before the launch) and works on the chunk the ticket
+// names: tickets are numbered chunk-major (every chunk 0 of every channel
+// group, then every chunk 1, ...), so the predecessor of a chunk holds a
+// smaller ticket and has therefore already started, whichever workgroups the
+// hardware happens to dispatch first and whatever else runs on the device.
+// A started chunk finishes its main pass without waiting on anything, then
+// (chunk k > 0) waits for flag[k-1], reads state[k-1] (acquire), publishes
+// its own inclusive state and raises flag[k] (release); a chunk's wait
+// therefore only depends on earlier tickets, and every wait ends. The wait
+// is still bounded (a few seconds): if it ever gives up, `err` is set and
+// the chunk takes NaN as its entering state, so that its outputs, its
+// published state and every later chunk's become NaN rather than silently
+// wrong; ssm_scan_fwd_status() reports the error word to the host.
 struct SplitHeader {
-  unsigned err;     // set if a wait gave up (never expected)
-  unsigned pad[63];
+  unsigned err;     // nonzero: a wait gave up (never expected)
+  unsigned ticket;  // next chunk ticket, in dispatch order
+  unsigned pad[62];
 };
 
 template <typename T>
@@ -109,6 +126,7 @@ struct ScanArgs {
   // split sequence (nchunks > 1)
   int nchunks;
   int64_t chunk_len;    // multiple of the round length
+  unsigned spin_limit;  // iterations of a hand-off wait before it gives up
   SplitHeader* hdr;
   int* flag;            // [bg * nchunks + k]
   float* state;         // [bg * nchunks + k][16 channels][16 states]
@@ -374,15 +392,27 @@ struct Stager {
 };
 
 // Wait, bounded, until another workgroup sets *flag; called by one lane.
-__device__ __forceinline__ void wait_flag(int* flag, unsigned* err) {
+// Returns false (and sets *err) if the wait gave up.
+__device__ __forceinline__ bool wait_flag(int* flag, unsigned* err, unsigned spin_limit) {
   for (unsigned it = 0;; ++it) {
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-    if (it >= (1u << 26)) {  // ~ seconds: give up rather than hang the device
-      atomicOr(err, 1u);
-      return;
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
+    if (it >= spin_limit) {  // ~ seconds at the default limit: give up rather than hang the device
+      __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
     }
     __builtin_amdgcn_s_sleep(4);
   }
+}
+
+// The chunk (chunk index, channel-group index) that split-sequence ticket tk
+// names: chunk-major, and within a chunk, when the group count is a multiple
+// of 8, the groups in the order that puts neighbouring groups (which share
+// 128-byte lines of x, delta and y) on the same XCD when tickets follow the
+// round-robin dispatch over the 8 XCDs (a bijection on the groups only then).
+__device__ __forceinline__ void split_chunk_of_ticket(int tk, int nbg, int64_t* kchunk, int64_t* bg) {
+  *kchunk = tk / nbg;
+  const int u = tk % nbg;
+  *bg = (nbg & 7) == 0 ? (u & 7) * (nbg >> 3) + (u >> 3) : u;
 }
 
 template <typename T, int SEG, int TS, bool BIDIR, bool VEC, bool SPLIT, bool GATE, int WPE = 3>
@@ -410,18 +440,23 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   // which (batch row, channel group) and, for a split sequence, which chunk.
   // Consecutive logical blocks share an XCD (its L2 serves the cache lines
-  // that neighbouring channel groups share); the split sequence numbers its
-  // blocks chunk-major. Every block of a split launch is resident at once
-  // (the host bounds the grid), so a chunk can wait for its predecessor.
-  int blk = blockIdx.x;
-  if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
-  int64_t bg = blk, kchunk = 0, t0 = 0, Lk = L;
+  // that neighbouring channel groups share). A split sequence takes its chunk
+  // from a ticket (see SplitHeader): a chunk's predecessor holds an earlier
+  // ticket, so it has started and its state will be published.
+  int64_t bg, kchunk = 0, t0 = 0, Lk = L;
   if constexpr (SPLIT) {
-    const int64_t nbg = p.nblocks / p.nchunks;
-    kchunk = blk / nbg;
-    bg = blk % nbg;
+    __shared__ int s_ticket;
+    if (tid == 0) s_ticket = static_cast<int>(__hip_atomic_fetch_add(&p.hdr->ticket, 1u, __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    const int nbg = p.nblocks / p.nchunks;
+    split_chunk_of_ticket(s_ticket, nbg, &kchunk, &bg);
     t0 = kchunk * p.chunk_len;
     Lk = L - t0 < p.chunk_len ? L - t0 : p.chunk_len;
+  } else {
+    int blk = blockIdx.x;
+    if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
+    bg = blk;
   }
   const int64_t b = bg / p.ngroups;
   const int64_t e0 = (bg % p.ngroups) * 16;
@@ -606,10 +641,13 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       const float sdc = static_cast<float>(sum);
       float incl[4] = {carry[0], carry[1], carry[2], carry[3]};
       if (kchunk > 0) {
-        if (lane == 0) wait_flag(p.flag + slot - 1, &p.hdr->err);
+        int ok = 1;
+        if (lane == 0) ok = wait_flag(p.flag + slot - 1, &p.hdr->err, p.spin_limit) ? 1 : 0;
+        ok = __builtin_amdgcn_readfirstlane(ok);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const float4 v = *reinterpret_cast<const float4*>(p.state + (slot - 1) * 256 + ch * 16 + 4 * g);
         hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
+        if (!ok) hin[0] = hin[1] = hin[2] = hin[3] = __builtin_nanf("");  // a wait that gave up poisons the chunk
 #pragma unroll
         for (int j = 0; j < 4; ++j) incl[j] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[j] * sdc), hin[j], carry[j]);
       }
@@ -741,6 +779,19 @@ struct SplitPlan {
   size_t flag_off, state_off, bytes;  // workspace layout
 };
 
+// Iterations of a hand-off wait before it gives up (s_sleep 4 each: about
+// 7 s at 2^26). SSM_SPLIT_SPIN_LIMIT in the environment overrides it, so
+// that a test can force the give-up path from the host.
+unsigned split_spin_limit() {
+  const char* e = std::getenv("SSM_SPLIT_SPIN_LIMIT");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    if (end && *end == '\0') return static_cast<unsigned>(std::min<unsigned long>(v, 1ul << 26));
+  }
+  return 1u << 26;
+}
+
 SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
   SplitPlan sp{};
   sp.nbg = Bs * ((ED + 15) / 16);
@@ -852,6 +903,7 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.rot_ncu = rotation_cus(nblk);
   a.nchunks = static_cast<int>(sp.nchunks);
   a.chunk_len = sp.chunk_len;
+  a.spin_limit = split_spin_limit();
   a.hdr = nullptr;
   a.flag = nullptr;
   a.state = nullptr;
@@ -922,6 +974,23 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
   return run(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
 }
 
+int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t Bs, int64_t L, int64_t ED,
+                        int64_t N, int dtype, void* stream) {
+  Sizes s;
+  int rc = check_sizes(Bs, L, ED, N, dtype, &s);
+  if (rc != SSM_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return SSM_ERR_LAUNCH;
+  if (s.seq == 0) return SSM_OK;
+  const SplitPlan sp = plan_split(Bs, L, ED, 0, device_cus());
+  if (sp.nchunks <= 1) return SSM_OK;  // no hand-off in this call
+  if (!workspace) return SSM_ERR_NULL;
+  if (workspace_bytes < sp.bytes) return SSM_ERR_WORKSPACE;
+  unsigned err = 0;
+  if (hipMemcpy(&err, workspace, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return SSM_ERR_LAUNCH;
+  return err ? SSM_ERR_HANDOFF : SSM_OK;
+}
+
 const char* ssm_status_str(int status) {
   switch (status) {
     case SSM_OK: return "ok";
@@ -932,6 +1001,7 @@ const char* ssm_status_str(int status) {
     case SSM_ERR_WORKSPACE: return "workspace missing or smaller than ssm_scan_workspace_bytes()";
     case SSM_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SSM_ERR_ARG: return "an option is invalid (dt_min > dt_max, or a NaN bound)";
+    case SSM_ERR_HANDOFF: return "a split-sequence hand-off wait gave up; the affected outputs are NaN";
     default: return "unknown status";
   }
 }

@@ -36,8 +36,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(8):
-        assert ssm.status_str(s)
+    for s in range(9):
+        assert ssm.status_str(s) != "unknown status"
     assert ssm.status_str(999) == "unknown status"
 
 

@@ -144,6 +144,46 @@ def test_split_sequence_negative_steps():
     assert_close("h_last", h, h_ref, TOL["f32"])
 
 
+def test_split_sequence_status_and_forced_give_up(monkeypatch):
+    # The status query reports a clean hand-off for a normal call. Then the
+    # hand-off wait's spin limit is forced to zero from the host
+    # (SSM_SPLIT_SPIN_LIMIT), so a wait gives up unless its predecessor has
+    # already published: every give-up must show as SSM_ERR_HANDOFF and as
+    # NaN outputs, and a call without one must still match the oracle. The
+    # kernel itself never hangs or faults either way.
+    import torch
+    import state_space_model_selective_amd as ssm
+    from parity_util import to_device, y_to_numpy
+    Bs, L, ED, N = 1, 20000, 128, 16
+    need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32)
+    assert need > 0, "this shape is expected to split the sequence"
+    inp = synth.make_inputs(Bs, L, ED, N, "f32", seed=23)
+    y_ref, h_ref, _ = oracle.scan(**inp, want_h_last=True)
+    dev = torch.device("cuda:0")
+    t = to_device(inp, dev)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    for spin in (None, "0", "0", "0"):
+        if spin is None:
+            monkeypatch.delenv("SSM_SPLIT_SPIN_LIMIT", raising=False)
+        else:
+            monkeypatch.setenv("SSM_SPLIT_SPIN_LIMIT", spin)
+        log("case split status, spin limit %s" % spin)
+        h = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev)
+        y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], h_last=h, workspace=ws)
+        rc = ssm.ssm_scan_fwd_status(t["x"], t["A"], ws)
+        yn, hn = y_to_numpy(y), h.double().cpu().numpy()
+        log("  status %d, NaN in y: %s" % (rc, bool(np.isnan(yn).any())))
+        if spin is None:
+            assert rc == ssm.SSM_OK
+        if rc == ssm.SSM_OK:
+            assert_close("y", yn, y_ref, TOL["f32"])
+            assert_close("h_last", hn, h_ref, TOL["f32"])
+        else:
+            assert rc == ssm.SSM_ERR_HANDOFF
+            assert np.isnan(yn).any() and np.isnan(hn).any()
+    monkeypatch.delenv("SSM_SPLIT_SPIN_LIMIT", raising=False)
+
+
 # ---- initial state h0 (resuming a sequence) ---------------------------------------
 
 @pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(2, 300, 64, "f32", False), (1, 5000, 64, "f32", False),
