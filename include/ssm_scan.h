@@ -139,12 +139,32 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
                  int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward selective scan that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Arguments, results
+ * and errors as ssm_scan_fwd. The split-sequence hand-off buffer is the
+ * library's own device array of SSM_NOALLOC_SCRATCH_BYTES per device (held
+ * until the process ends; its address is resolved on the first call on each
+ * device, with that device current); sizes whose split plan would need more
+ * (ssm_scan_workspace_bytes(..., bidir = 0) larger than that, which no
+ * device of up to 340 compute units reaches) return SSM_ERR_WORKSPACE. The
+ * function calls no allocator. Every call on one device shares that array:
+ * calls that overlap in time on one device (two streams, two threads) race
+ * and give wrong results; calls in order on one stream are safe.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES (1u << 20)
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
+                         int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* stream);
+
+/*
  * Outcome of the split-sequence hand-off of the last ssm_scan_fwd call made
- * with this workspace and these sizes: synchronises `stream`, then returns
- * SSM_ERR_HANDOFF if a wait gave up (that call's affected outputs are NaN),
- * SSM_OK otherwise (also when these sizes do not split the sequence, or the
- * input is empty). Size errors as ssm_scan_fwd; SSM_ERR_NULL or
- * SSM_ERR_WORKSPACE if a split call's workspace is missing or too small.
+ * with this workspace and these sizes (workspace NULL: the last
+ * ssm_scan_fwd_noalloc call on the current device): synchronises `stream`,
+ * then returns SSM_ERR_HANDOFF if a wait gave up (that call's affected
+ * outputs are NaN), SSM_OK otherwise (also when these sizes do not split the
+ * sequence, or the input is empty). Size errors as ssm_scan_fwd;
+ * SSM_ERR_WORKSPACE if the workspace is too small for a split call.
  */
 int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t Bs, int64_t L, int64_t ED,
                         int64_t N, int dtype, void* stream);

@@ -21,6 +21,8 @@ PROBE_SOURCES = [os.path.join(_HERE, "csrc", "valu_probe.hip")]
 INCLUDE = os.path.join(_ROOT, "include")
 
 SSM_F32, SSM_BF16 = 0, 1
+# bytes of the device buffer that ssm_scan_fwd_noalloc uses in place of a workspace
+SSM_NOALLOC_SCRATCH_BYTES = 1 << 20
 (SSM_OK, SSM_ERR_NULL, SSM_ERR_DIM, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE, SSM_ERR_LAUNCH,
  SSM_ERR_ARG, SSM_ERR_HANDOFF) = range(9)
 
@@ -85,6 +87,8 @@ def lib():
         L.ssm_scan_bidir_fwd.restype = ci
         L.ssm_scan_fwd_status.argtypes = [vp, sz] + [i64] * 4 + [ci, vp]
         L.ssm_scan_fwd_status.restype = ci
+        L.ssm_scan_fwd_noalloc.argtypes = [vp] * 10 + [i64] * 4 + [ci, vp]
+        L.ssm_scan_fwd_noalloc.restype = ci
         L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_bwd_workspace_bytes.restype = sz
         L.ssm_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [ci, vp, sz, vp]
@@ -289,9 +293,31 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None,
     return y
 
 
+def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, y=None, h_last=None, stream=None, h0=None, dt_bias=None,
+                         dt_softplus=False, dt_limit=None, z=None):
+    """ssm_scan_fwd without a workspace: the library's own device buffer holds
+    the split-sequence hand-off (calls that overlap in time on one device
+    race). y must be given by callers that cannot allocate."""
+    _scan_args("ssm_scan_fwd_noalloc", x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, None,
+               [("y", y, "seq"), ("h_last", h_last, "state")])
+    Bs, L, ED = (int(v) for v in x.shape)
+    N = int(A.shape[1])
+    dt = _dtype_code(x)
+    if y is None:
+        import torch
+        y = torch.empty_like(x)
+    opts = _options(dt_bias, dt_softplus, dt_limit, z)
+    rc = lib().ssm_scan_fwd_noalloc(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                                    _byref(opts), _ptr(y), _ptr(h_last), Bs, L, ED, N, dt, _stream(x, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_scan_fwd_noalloc")
+    return y
+
+
 def ssm_scan_fwd_status(x, A, workspace, stream=None):
     """Outcome of the split-sequence hand-off of the last ssm_scan_fwd call on
-    tensors shaped like x and A with this workspace: synchronises the stream,
+    tensors shaped like x and A with this workspace (None: the last
+    ssm_scan_fwd_noalloc call on this device): synchronises the stream,
     returns SSM_OK or SSM_ERR_HANDOFF (a hand-off wait gave up; that call's
     affected outputs are NaN); raises SSMError for argument errors."""
     a = _Args("ssm_scan_fwd_status", x, 3)

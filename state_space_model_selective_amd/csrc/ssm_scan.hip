@@ -14,8 +14,10 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "ssm_scan.h"
@@ -955,6 +957,44 @@ int run(const void* x, const void* delta, const float* A, const void* B, const v
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// The split-sequence hand-off buffer of ssm_scan_fwd_noalloc: a file-scope
+// device array, one copy per device, held until the process ends. A split
+// plan needs a 256-byte header, one flag word and one 16 x 16 float32 state
+// per chunk (at most three chunks per compute unit): 1 MiB covers every plan
+// on a device of up to 340 compute units.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once resolved
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, resolved once per
+// device with that device current. (In host code the name `scratch` is a
+// host-side stand-in, not a device address: only this pointer may reach a
+// kernel or a copy.)
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSM_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return SSM_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSM_ERR_LAUNCH;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SSM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int bidir) {
@@ -974,6 +1014,22 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
   return run(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
 }
 
+int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
+                         int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* stream) {
+  Sizes s;
+  const int rc = check_sizes(Bs, L, ED, N, dtype, &s);
+  if (rc != SSM_OK) return rc;
+  const size_t need = s.seq == 0 ? 0 : workspace_bytes(Bs, L, ED, N, dtype, 0);
+  if (need > SSM_NOALLOC_SCRATCH_BYTES) return SSM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int r2 = scratch_on_current_device(&ws);
+    if (r2 != SSM_OK) return r2;
+  }
+  return run(x, delta, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, ws, need, stream, 0);
+}
+
 int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t Bs, int64_t L, int64_t ED,
                         int64_t N, int dtype, void* stream) {
   Sizes s;
@@ -984,7 +1040,14 @@ int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t B
   if (s.seq == 0) return SSM_OK;
   const SplitPlan sp = plan_split(Bs, L, ED, 0, device_cus());
   if (sp.nchunks <= 1) return SSM_OK;  // no hand-off in this call
-  if (!workspace) return SSM_ERR_NULL;
+  if (!workspace) {
+    // the internal buffer of ssm_scan_fwd_noalloc on the current device
+    void* p = nullptr;
+    const int r2 = scratch_on_current_device(&p);
+    if (r2 != SSM_OK) return r2;
+    workspace = p;
+    workspace_bytes = SSM_NOALLOC_SCRATCH_BYTES;
+  }
   if (workspace_bytes < sp.bytes) return SSM_ERR_WORKSPACE;
   unsigned err = 0;
   if (hipMemcpy(&err, workspace, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return SSM_ERR_LAUNCH;
