@@ -42,14 +42,14 @@ def lib():
         L = ctypes.CDLL(_SO)
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         dbl = ctypes.c_double
-        L.oracle_scan.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
+        L.oracle_scan.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, ctypes.c_int, dbl, dbl, vp,
                                   i64, i64, i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         L.oracle_scan.restype = ctypes.c_int
-        L.oracle_scan_bwd.argtypes = ([ctypes.c_int] + [vp] * 8 + [ctypes.c_int, ctypes.c_double, ctypes.c_double] +
+        L.oracle_scan_bwd.argtypes = ([ctypes.c_int] + [vp] * 9 + [ctypes.c_int, ctypes.c_double, ctypes.c_double] +
                                       [vp] * 2 + [i64] * 4 + [vp] * 8 + [ctypes.c_int])
         L.oracle_scan_bwd.restype = ctypes.c_int
-        L.oracle_ssd.argtypes = ([ctypes.c_int, ctypes.c_int] + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
+        L.oracle_ssd.argtypes = ([ctypes.c_int, ctypes.c_int] + [vp] * 9 + [ctypes.c_int, ctypes.c_double,
                                  ctypes.c_double, vp] + [i64] * 6 + [vp] * 3 + [ctypes.c_int])
         L.oracle_ssd.restype = ctypes.c_int
         _lib = L
@@ -66,7 +66,7 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
+def scan(x, delta, A, B, C, D=None, *, h0=None, g0=None, dt_bias=None, dt_softplus=False,
          dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, chans=None, want_h_last=False,
          want_g_first=False, nthreads=None):
     """Run the oracle.
@@ -91,6 +91,7 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     A = np.ascontiguousarray(A, dtype=np.float32)
     D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    g0 = None if g0 is None else np.ascontiguousarray(g0, dtype=np.float32)
     dt_bias = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float32)
     z = None if z is None else np.ascontiguousarray(z)
     if z is not None and (z.dtype != x.dtype or z.shape != x.shape):
@@ -109,6 +110,7 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     assert delta.shape == x.shape and B.shape == (Bs, L, N) and C.shape == (Bs, L, N)
     assert A.shape == (ED, N) and (D is None or D.shape == (ED,))
     assert h0 is None or h0.shape == (Bs, ED, N)
+    assert g0 is None or g0.shape == (Bs, ED, N)
     assert dt_bias is None or dt_bias.shape == (ED,)
     if chans is not None:
         chans = np.ascontiguousarray(chans, dtype=np.int64)
@@ -119,7 +121,7 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     h = np.empty((nch, N), dtype=np.float64) if want_h_last else None
     g = np.empty((nch, N), dtype=np.float64) if (want_g_first and bidir) else None
     rc = lib().oracle_scan(dtype, int(bool(bidir)), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                           _ptr(D), _ptr(h0), _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]),
+                           _ptr(D), _ptr(h0), _ptr(g0), _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]),
                            float(dt_limit[1]), _ptr(z), Bs, L, ED, N, _ptr(chans), nch, _ptr(y), _ptr(h), _ptr(g),
                            _threads(nthreads))
     if rc != 0:
@@ -133,8 +135,8 @@ def scan(x, delta, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     return y, h, g
 
 
-def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, dt_bias=None, dt_softplus=False,
-             dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, nthreads=None):
+def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, g0=None, dh_last=None, dg_first=None, dt_bias=None,
+             dt_softplus=False, dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, nthreads=None):
     """Gradients of L = sum(dy * y) for the forward scan, in fp64.
 
     Same input conventions as scan() (including the options dt_bias,
@@ -149,28 +151,38 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, dt_bias=None, dt_so
     gradient dy z sigmoid(z), and dz = dy y (d/dz of z sigmoid(z)) with y the
     whole ungated output (both directions and D x), taken from scan().
 
+    dh_last: optional (Bs, ED, N) gradient of the loss with respect to the
+    final state h_last (the Bi-Mamba2 backward's dfinal_states): the loss is
+    then sum(dy * y) + sum(dh_last * h_last).
+
     bidir: the gradients of the bidirectional scan, whose output is the
     forward scan (with D x and h0) plus the reverse-time scan, i.e. the
-    forward scan of the time-flipped inputs from a zero state without D,
+    forward scan of the time-flipped inputs from g0 (zero if None) without D,
     flipped back ("Some questions of Bi-Mamba2 and Hydra", the author's first
     reply). Its gradient is the sum of the two scans' gradients, the reverse
     one taken on flipped copies and flipped back; D and h0 enter the forward
-    scan only; the step-size map and the gate's factor apply to both.
+    scan only, g0 the reverse one; the step-size map and the gate's factor
+    apply to both. dg_first (the gradient of the reverse final state g_first)
+    enters the reverse scan's adjoint as dh_last enters the forward one, and
+    the result holds dg0 (the gradient of g0) beside dh0.
     """
     opts = dict(dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit)
     if bidir:
-        fwd = scan_bwd(x, delta, A, B, C, D, dy, h0=h0, z=z, nthreads=nthreads, **opts)
+        fwd = scan_bwd(x, delta, A, B, C, D, dy, h0=h0, dh_last=dh_last, z=z, nthreads=nthreads, **opts)
         flip = lambda a: np.ascontiguousarray(np.asarray(a)[:, ::-1])
-        rev = scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), None, flip(dy),
+        rev = scan_bwd(flip(x), flip(delta), A, flip(B), flip(C), None, flip(dy), h0=g0, dh_last=dg_first,
                        z=None if z is None else flip(z), nthreads=nthreads, **opts)
         for k in ("dx", "ddelta", "dB", "dC"):
             fwd[k] = fwd[k] + rev[k][:, ::-1]
         fwd["dA"] = fwd["dA"] + rev["dA"]
+        fwd["dg0"] = rev["dh0"]
         if dt_bias is not None:
             fwd["ddt_bias"] = fwd["ddt_bias"] + rev["ddt_bias"]
         if z is not None:
-            fwd["dz"] = _gate_grad(x, delta, A, B, C, D, dy, h0, z, True, nthreads, opts)
+            fwd["dz"] = _gate_grad(x, delta, A, B, C, D, dy, h0, z, True, nthreads, opts, g0=g0)
         return fwd
+    if g0 is not None or dg_first is not None:
+        raise ValueError("g0 and dg_first belong to the bidirectional scan")
     x = np.ascontiguousarray(x)
     delta = np.ascontiguousarray(delta)
     B = np.ascontiguousarray(B)
@@ -179,6 +191,7 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, dt_bias=None, dt_so
     A = np.ascontiguousarray(A, dtype=np.float32)
     D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    dhl = None if dh_last is None else np.ascontiguousarray(dh_last, dtype=np.float32)
     dtb = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float32)
     zc = None if z is None else np.ascontiguousarray(z)
     dtype = BF16 if x.dtype == np.uint16 else F32
@@ -189,10 +202,12 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, dt_bias=None, dt_so
     N = A.shape[1]
     assert dy.shape == x.shape and (zc is None or zc.shape == x.shape)
     assert dtb is None or dtb.shape == (ED,)
+    assert dhl is None or dhl.shape == (Bs, ED, N)
     out = dict(dx=np.empty((Bs, L, ED)), ddelta=np.empty((Bs, L, ED)), dA=np.empty((ED, N)),
                dB=np.empty((Bs, L, N)), dC=np.empty((Bs, L, N)), dD=np.empty((ED,)), dh0=np.empty((Bs, ED, N)))
     dbias = np.empty((ED,)) if dtb is not None else None
-    rc = lib().oracle_scan_bwd(dtype, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dtb),
+    rc = lib().oracle_scan_bwd(dtype, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dhl),
+                               _ptr(dtb),
                                int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]), _ptr(zc), _ptr(dy),
                                Bs, L, ED, N, _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
                                _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(dbias), _threads(nthreads))
@@ -205,10 +220,10 @@ def scan_bwd(x, delta, A, B, C, D=None, dy=None, *, h0=None, dt_bias=None, dt_so
     return out
 
 
-def _gate_grad(x, delta, A, B, C, D, dy, h0, z, bidir, nthreads, opts):
+def _gate_grad(x, delta, A, B, C, D, dy, h0, z, bidir, nthreads, opts, g0=None):
     """dz = dy y d(z sigmoid(z))/dz for y' = y z sigmoid(z), with y the
     ungated output of the scan (forward or bidirectional, with the options)."""
-    y, _, _ = scan(x, delta, A, B, C, D, h0=h0, bidir=bidir, nthreads=nthreads, **opts)
+    y, _, _ = scan(x, delta, A, B, C, D, h0=h0, g0=g0, bidir=bidir, nthreads=nthreads, **opts)
     zf = _widen(z)
     sg = 1.0 / (1.0 + np.exp(-zf))
     return _widen(dy) * y * (sg * (1.0 + zf * (1.0 - sg)))
@@ -222,13 +237,14 @@ def _widen(a):
     return a.astype(np.float64)
 
 
-def ssd(x, dt, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
+def ssd(x, dt, A, B, C, D=None, *, h0=None, g0=None, dt_bias=None, dt_softplus=False,
         dt_limit=(-float("inf"), float("inf")), z=None, bidir=False, want_h_last=False, want_g_first=False,
         nthreads=None):
     """Multi-head selective scan in fp64.
 
     x (Bs, L, H, P), dt (Bs, L, H), A (H,), B and C (Bs, L, G, N), D (H,) or
-    None, h0 (Bs, H, P, N) or None; float32 arrays, or uint16 bfloat16 bit
+    None, h0 (Bs, H, P, N) or None, g0 (Bs, H, P, N) or None (the reverse
+    state entering at the last step, bidir only); float32 arrays, or uint16 bfloat16 bit
     patterns for x, dt, B, C. dt_bias (H,) float32, dt_softplus, dt_limit and
     the gate z (x's shape and dtype) as in scan(), per head. Returns
     (y (Bs, L, H, P), h_last, g_first) with the states (Bs, H, P, N) when
@@ -245,6 +261,7 @@ def ssd(x, dt, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     A = np.ascontiguousarray(A, dtype=np.float32)
     D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
     h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float32)
+    g0 = None if g0 is None else np.ascontiguousarray(g0, dtype=np.float32)
     dtype = BF16 if x.dtype == np.uint16 else F32
     for t in (dt, B, C):
         if t.dtype != x.dtype:
@@ -256,7 +273,9 @@ def ssd(x, dt, A, B, C, D=None, *, h0=None, dt_bias=None, dt_softplus=False,
     y = np.empty((Bs, L, H, P))
     hl = np.empty((Bs, H, P, N)) if want_h_last else None
     gf = np.empty((Bs, H, P, N)) if (want_g_first and bidir) else None
+    assert g0 is None or g0.shape == (Bs, H, P, N)
     rc = lib().oracle_ssd(dtype, int(bool(bidir)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                          _ptr(g0),
                           _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]), _ptr(z),
                           Bs, L, H, P, G, N, _ptr(y), _ptr(hl), _ptr(gf), _threads(nthreads))
     if rc != 0:

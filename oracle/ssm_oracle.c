@@ -28,6 +28,10 @@
  *     g_t[n] = a_t[n] * g_{t+1}[n] + (delta x)[t] * B[b,t,n],  g_L = 0
  *     y[b,t,e] = sum_n C[b,t,n] * (h_t[n] + g_t[n]) + D[e] * x[b,t,e]
  *   with the same a_t, inputs read in place (no shift, no flipped copy).
+ *   The reverse state may also enter from a carried state, g_L = g0[b,e,n]
+ *   (the reverse direction's counterpart of h0: the Bi-Mamba2 forward
+ *   returns a final state per direction, final_states_f and final_states_b,
+ *   and a sequence cut in two resumes each direction from the other piece's).
  *
  * Optional step-size pre-processing and output gate, the options of the
  * Bi-Mamba2 forward (same page, the MambaChunkScanCombinedFn.forward
@@ -75,6 +79,7 @@ typedef struct work {
   const void *x, *delta, *B, *C;
   const float *A, *D;
   const float* h0; /* (Bs, ED, N) initial forward state, or NULL for zero */
+  const float* g0; /* (Bs, ED, N) reverse state entering at t = L-1 (bidir), or NULL for zero */
   const float* dt_bias; /* (ED) or NULL */
   int dt_softplus;
   double dt_min, dt_max;
@@ -142,7 +147,7 @@ static void scan_channel(const work_t* w, int64_t k, double* h, double* g) {
     for (int64_t n = 0; n < N; ++n) w->h_last[k * N + n] = h[n];
 
   if (w->bidir) {
-    for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+    for (int64_t n = 0; n < N; ++n) g[n] = w->g0 ? (double)w->g0[(b * ED + e) * N + n] : 0.0;
     for (int64_t t = L - 1; t >= 0; --t) {
       const int64_t ix = (b * L + t) * ED + e;
       const int64_t ib = (b * L + t) * N;
@@ -189,7 +194,7 @@ static void* worker(void* p) {
  * -1 on bad arguments, -2 when memory for a worker could not be allocated.
  */
 int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const float* A, const void* B,
-                const void* C, const float* D, const float* h0, const float* dt_bias, int dt_softplus,
+                const void* C, const float* D, const float* h0, const float* g0, const float* dt_bias, int dt_softplus,
                 double dt_min, double dt_max, const void* z, int64_t Bs, int64_t L, int64_t ED, int64_t N,
                 const int64_t* chans, int64_t nchans, double* y, double* h_last, double* g_first,
                 int nthreads) {
@@ -206,7 +211,7 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
   if (nthreads > 256) nthreads = 256;
   if (nthreads > nchans) nthreads = (int)(nchans > 0 ? nchans : 1);
 
-  work_t base = {dtype, bidir, x, delta, B, C, A, D, h0, dt_bias, dt_softplus, dt_min, dt_max, z,
+  work_t base = {dtype, bidir, x, delta, B, C, A, D, h0, bidir ? g0 : NULL, dt_bias, dt_softplus, dt_min, dt_max, z,
                  Bs, L, ED, N, chans, nchans, y, h_last,
                  bidir ? g_first : NULL, 0, 0};
   work_t* ws = (work_t*)malloc(sizeof(work_t) * (size_t)nthreads);
@@ -244,7 +249,7 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
  * dz needs the whole output and is formed by the Python wrapper). The raw
  * step size gets ddelta times d delta'/d delta (step_map_deriv), and
  * ddt_bias[e] is the sum over (b, t) of that. With g_t[n] = dL/dh_t[n]:
- *     g_t = dy_t C_t + a_{t+1} g_{t+1}          (g_L = 0; reverse time)
+ *     g_t = dy_t C_t + a_{t+1} g_{t+1}          (reverse time; a_L g_L = dh_last)
  *     dC[b,t,n] = sum_e dy_t h_t[n]             dD[e] = sum_{b,t} dy_t x_t
  *     dx_t = sum_n g_t[n] delta_t B_t[n] + dy_t D[e]
  *     ddelta_t = sum_n g_t[n] (x_t B_t[n] + A[e,n] a_t[n] h_{t-1}[n])
@@ -258,6 +263,10 @@ int oracle_scan(int dtype, int bidir, const void* x, const void* delta, const fl
  * dx, ddelta (Bs, L, ED); dA (ED, N); dB, dC (Bs, L, N); dD (ED);
  * dh0 (Bs, ED, N) or NULL; ddt_bias (ED) or NULL. y is affine in h0, so dh0 does not depend on h0
  * and is returned for h0 = NULL (the zero initial state) as well.
+ * dh_last (Bs, ED, N), or NULL for zero, is the gradient of the loss with
+ * respect to the final state h_{L-1} (the backward listing of the Bi-Mamba2
+ * page takes it as dfinal_states): the loss is sum(dy * y) + sum(dh_last *
+ * h_{L-1}), so the adjoint enters the last step with g_{L-1} = dy C + dh_last.
  */
 enum { BWD_BLOCK = 64 }; /* channels per work item */
 
@@ -265,6 +274,7 @@ typedef struct {
   int dtype;
   const void *x, *delta, *B, *C, *dy;
   const float *A, *D, *h0;
+  const float* dh_last; /* (Bs, ED, N) gradient of the final state, or NULL */
   const float* dt_bias; /* (ED) or NULL */
   int dt_softplus;
   double dt_min, dt_max;
@@ -306,8 +316,10 @@ static void* bwd_worker(void* p) {
           hs[(t + 1) * N + n] = a * hs[t * N + n] + (dt * xv) * load(w->B, ib + n, w->dtype);
         }
       }
-      /* reverse: the adjoint state and every gradient term */
-      for (int64_t n = 0; n < N; ++n) g[n] = 0.0;
+      /* reverse: the adjoint state and every gradient term; g holds a_{t+1}
+         g_{t+1} at the top of step t, which at t = L-1 is the final state's
+         own gradient */
+      for (int64_t n = 0; n < N; ++n) g[n] = w->dh_last ? (double)w->dh_last[(b * ED + e) * N + n] : 0.0;
       double dD = 0.0;
       double* dA = w->dA_part + (b * ED + e) * N;
       for (int64_t n = 0; n < N; ++n) dA[n] = 0.0;
@@ -356,7 +368,8 @@ static void* bwd_worker(void* p) {
 }
 
 int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A, const void* B, const void* C,
-                    const float* D, const float* h0, const float* dt_bias, int dt_softplus, double dt_min,
+                    const float* D, const float* h0, const float* dh_last, const float* dt_bias, int dt_softplus,
+                    double dt_min,
                     double dt_max, const void* z, const void* dy, int64_t Bs, int64_t L, int64_t ED, int64_t N,
                     double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dh0,
                     double* ddt_bias, int nthreads) {
@@ -382,7 +395,7 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
   for (int64_t b = 0; rc == 0 && b < Bs; ++b) {
     const int64_t per = (nblk + nthreads - 1) / nthreads;
     for (int i = 0; i < nthreads; ++i) {
-      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, dt_bias, dt_softplus, dt_min, dt_max, z,
+      ws[i] = (bwd_t){dtype, x, delta, B, C, dy, A, D, h0, dh_last, dt_bias, dt_softplus, dt_min, dt_max, z,
                       Bs, L, ED, N, dx, ddelta, dh0, dA_part, dD_part, dbias_part, partB, partC, b, 0, 0, 0};
       ws[i].blk0 = per * i < nblk ? per * i : nblk;
       ws[i].blk1 = per * (i + 1) < nblk ? per * (i + 1) : nblk;
@@ -436,7 +449,7 @@ int oracle_scan_bwd(int dtype, const void* x, const void* delta, const float* A,
  *   S_t[p][n] = a_t S_{t-1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],  S_{-1} = h0 (or 0)
  *   y[b,t,h,p] = sum_n C[b,t,g,n] S_t[p][n] + D[h] x[b,t,h,p]
  * bidir adds the reverse-time scan with the same a_t (no shift, D x once):
- *   R_t = a_t R_{t+1} + (dt x)_t B_t,  R_L = 0,   y += sum_n C_t R_t.
+ *   R_t = a_t R_{t+1} + (dt x)_t B_t,  R_L = g0 (or 0),   y += sum_n C_t R_t.
  * The same options as the per-channel form, with the head in place of the
  * channel (the forward listing of the Bi-Mamba2 page passes dt_bias per head
  * and z of x's shape to this scan):
@@ -450,6 +463,7 @@ typedef struct {
   int dtype, bidir;
   const void *x, *dt, *B, *C;
   const float *A, *D, *h0;
+  const float* g0;      /* (Bs, H, P, N) reverse state entering at t = L-1, or NULL */
   const float* dt_bias; /* (H) or NULL */
   int dt_softplus;
   double dt_min, dt_max;
@@ -473,8 +487,8 @@ static void* ssd_worker(void* arg) {
     const double Ah = (double)w->A[h];
     const double Dh = w->D ? (double)w->D[h] : 0.0;
     for (int dir = 0; dir < (w->bidir ? 2 : 1); ++dir) {
-      for (int64_t i = 0; i < P * N; ++i)
-        S[i] = (dir == 0 && w->h0) ? (double)w->h0[(b * H + h) * P * N + i] : 0.0;
+      const float* init = dir == 0 ? w->h0 : w->g0;
+      for (int64_t i = 0; i < P * N; ++i) S[i] = init ? (double)init[(b * H + h) * P * N + i] : 0.0;
       for (int64_t s = 0; s < L; ++s) {
         const int64_t t = dir == 0 ? s : L - 1 - s;
         const double dtv = step_map(load(w->dt, (b * L + t) * H + h, w->dtype),
@@ -513,7 +527,7 @@ static void* ssd_worker(void* arg) {
 }
 
 int oracle_ssd(int dtype, int bidir, const void* x, const void* dt, const float* A, const void* B, const void* C,
-               const float* D, const float* h0, const float* dt_bias, int dt_softplus, double dt_min, double dt_max,
+               const float* D, const float* h0, const float* g0, const float* dt_bias, int dt_softplus, double dt_min, double dt_max,
                const void* z, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, double* y,
                double* h_last, double* g_first, int nthreads) {
   if (!x || !dt || !A || !B || !C || !y) return -1;
@@ -533,7 +547,7 @@ int oracle_ssd(int dtype, int bidir, const void* x, const void* dt, const float*
   }
   const int64_t per = (K + nthreads - 1) / nthreads;
   for (int i = 0; i < nthreads; ++i) {
-    ws[i] = (ssd_t){dtype, bidir, x, dt, B, C, A, D, h0, dt_bias, dt_softplus, dt_min, dt_max, z,
+    ws[i] = (ssd_t){dtype, bidir, x, dt, B, C, A, D, h0, bidir ? g0 : NULL, dt_bias, dt_softplus, dt_min, dt_max, z,
                     Bs, L, H, P, G, N, y, h_last, bidir ? g_first : NULL, 0, 0, 0};
     ws[i].k0 = per * i < K ? per * i : K;
     ws[i].k1 = per * (i + 1) < K ? per * (i + 1) : K;
