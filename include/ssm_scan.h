@@ -22,7 +22,7 @@
  * decreasing time, plus D x once, with the inputs read in place (no flipped
  * copy) and no shift:
  *
- *   g_t[n]   = a_t[n] * g_{t+1}[n] + (delta x)[b,t,e] * B[b,t,n],   g_L = 0
+ *   g_t[n]   = a_t[n] * g_{t+1}[n] + (delta x)[b,t,e] * B[b,t,n],   g_L = 0 (or g0)
  *   y[b,t,e] = sum_n C[b,t,n] * (h_t[n] + g_t[n]) + D[e] * x[b,t,e]
  *
  * Conventions shared by every entry point:
@@ -46,10 +46,10 @@
  *  - Empty inputs: the batch size, the sequence length and the channel count
  *    (Bs, L, ED; Bs and L of the multi-head scan) may be zero, and a buffer
  *    with no elements may then be NULL. Nothing is scanned; over zero time
- *    steps the forward state stays where it entered, so h_last = h0 (zero
- *    without h0) and g_first = 0, and every gradient of the backward pass
- *    is zero (dA, dD, dh0; dB and dC when there are time steps but no
- *    channels). No workspace is needed.
+ *    steps each state stays where it entered, so h_last = h0 and g_first =
+ *    g0 (zero without them), and every gradient of the backward pass is zero
+ *    (dA, dD; dB and dC when there are time steps but no channels) except
+ *    dh0 = dh_last and dg0 = dg_first. No workspace is needed.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -171,15 +171,22 @@ int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t B
 
 /*
  * Bidirectional selective scan (forward plus reverse-time scan plus D x).
- * Arguments as ssm_scan_fwd (h0 initialises the forward direction; the
- * reverse direction starts from zero at t = L-1), and
+ * Arguments as ssm_scan_fwd (h0 initialises the forward direction), and
+ *   g0      : (Bs, ED, N) float32 or NULL -- reverse state entering at
+ *             t = L-1, i.e. g_L = g0 (zero if NULL). The Bi-Mamba2 forward
+ *             returns a final state per direction ("Some questions of
+ *             Bi-Mamba2 and Hydra", final_states_f and final_states_b in the
+ *             MambaChunkScanCombinedFn.forward listing); a sequence cut in
+ *             pieces resumes the forward direction of a piece from the
+ *             previous piece's h_last and the reverse direction from the
+ *             next piece's g_first.
  *   h_last  : (Bs, ED, N) float32 or NULL -- forward state after t = L-1
  *   g_first : (Bs, ED, N) float32 or NULL -- reverse state after t = 0
  */
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, int64_t Bs,
-                       int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
+                       float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward pass of the forward scan: the gradients of L = sum(dy * y) for
@@ -195,6 +202,12 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
  *   dB_t[n]  = sum_e g_t delta_t x_t,      dC_t[n] = sum_e dy_t h_t
  *   dA[e,n]  = sum_{b,t} delta_t g_t a_t h_{t-1},   dD[e] = sum_{b,t} dy_t x_t
  *   dh0      = a_0 g_0
+ * dh_last (the gradient of the final state h_last, the dfinal_states
+ * argument of that page's backward listing) enters the adjoint at the last
+ * step, g_{L-1} = dy_{L-1} C_{L-1} + dh_last: the loss is then
+ * sum(dy * y) + sum(dh_last * h_last), so that a sequence cut in pieces
+ * (h0 / h_last) is trained piece by piece, the later piece's dh0 being the
+ * earlier piece's dh_last.
  * The bidirectional scan has ssm_scan_bidir_bwd below.
  * Step-size options (opts: dt_bias, dt_softplus, dt_min, dt_max, as given
  * to the forward): the recurrence above runs with delta' = clamp(softplus?(
@@ -210,6 +223,7 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
  *   x, delta, A, B, C, D, h0 : as ssm_scan_fwd (D and h0 may be NULL)
  *   opts    : step-size options of the forward, or NULL
  *   dy      : (Bs, L, ED) of dtype         -- dL/dy
+ *   dh_last : (Bs, ED, N) float32, or NULL -- dL/dh_last (zero if NULL)
  *   dx, ddelta : (Bs, L, ED) of dtype      -- written in full
  *   dA      : (ED, N) float32              -- written in full
  *   dB, dC  : (Bs, L, N) of dtype          -- written in full
@@ -231,15 +245,17 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
 size_t ssm_scan_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int gate);
 
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
-                 int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+                 const float* h0, const ssm_scan_options* opts, const void* dy, const float* dh_last, void* dx,
+                 void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz,
+                 int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /*
  * Backward pass of the bidirectional scan: the gradients of L = sum(dy * y)
- * for y = ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, opts), the sum
- * of the forward scan (with D x and h0) and the reverse-time scan (from a
- * zero state, shared weights) of "Some questions of Bi-Mamba2 and Hydra" (the
+ * (plus sum(dh_last * h_last) + sum(dg_first * g_first)) for y =
+ * ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, g0, opts), the sum of the
+ * forward scan (with D x and h0) and the reverse-time scan (from g0, shared
+ * weights) of "Some questions of Bi-Mamba2 and Hydra" (the
  * author's first reply). Its gradient is the sum of the two scans' gradients:
  * the reverse scan's adjoint runs in increasing time, g'_t = dy_t C_t +
  * a_{t-1} g'_{t-1}, with the terms of ssm_scan_bwd at the same (b, t, e); D
@@ -248,6 +264,10 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
  * every step t to time L-1-t and adding its dx and ddelta to the first's
  * (kept in float32 in the workspace for bfloat16 outputs, so that they are
  * rounded once); dB, dC and dA sum both passes' partials in a fixed order.
+ * The reverse scan starts from g0 (the forward's reverse initial state; zero
+ * if NULL), its adjoint enters from dg_first (the gradient of g_first; zero
+ * if NULL), and the gradient of g0 is written to dg0 (if not NULL); h0,
+ * dh_last and dh0 belong to the forward-time scan as in ssm_scan_bwd.
  * Arguments, outputs and conventions as ssm_scan_bwd; the workspace is
  * ssm_scan_bidir_bwd_workspace_bytes(..., gate) bytes (both passes' partial
  * sums and, for bfloat16, two float32 values per element of x; with the gate
@@ -256,10 +276,10 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
 size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int gate);
 
 int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, const ssm_scan_options* opts, const void* dy, void* dx,
-                       void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias,
-                       void* dz, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, const void* dy,
+                       const float* dh_last, const float* dg_first, void* dx, void* ddelta, float* dA, void* dB,
+                       void* dC, float* dD, float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+                       int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Multi-head (Mamba-2 / SSD) selective scan, in the layout of the chunked
@@ -301,16 +321,19 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
 /*
  * Bidirectional multi-head scan (Bi-Mamba2 on the multi-head form): the
  * forward scan of ssm_ssd_fwd (with D x and h0) plus the same scan run in
- * decreasing time from a zero state over the same inputs, read in place (no
+ * decreasing time from g0 (zero if NULL) over the same inputs, read in place (no
  * flipped copy), the two outputs added -- the bidirectional combination of
  * "Some questions of Bi-Mamba2 and Hydra" (the author's first reply: two SSMs
  * with shared weights, the reverse one on the flipped sequence, plus D x):
  *
- *   g_t[p][n] = a_t g_{t+1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],   g_L = 0
+ *   g_t[p][n] = a_t g_{t+1}[p][n] + (dt[b,t,h] x[b,t,h,p]) B[b,t,g,n],   g_L = g0 (or 0)
  *   y[b,t,h,p] = sum_n C[b,t,g,n] (S_t[p][n] + g_t[p][n]) + D[h] x[b,t,h,p]
  *
  * with dt' in place of dt in both directions and the gate applied to the
  * complete sum when opts sets them. Arguments as ssm_ssd_fwd, and
+ *   g0        : (Bs, H, P, N) float32, or NULL -- the reverse state entering
+ *               at t = L-1 (zero if NULL; resumes the reverse direction from
+ *               the next piece's g_first, as h0 resumes the forward one)
  *   g_first   : (Bs, H, P, N) float32, or NULL -- g after t = 0
  *   workspace : device memory of ssm_ssd_bidir_workspace_bytes(...) bytes for
  *               bfloat16 (the reverse direction's float32 partial of y; it
@@ -321,8 +344,8 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
  */
 size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype);
 int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                      const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
-                      float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                      const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
+                      float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */

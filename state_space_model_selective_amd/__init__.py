@@ -83,7 +83,7 @@ def lib():
         L.ssm_scan_workspace_bytes.restype = sz
         L.ssm_scan_fwd.argtypes = [vp] * 10 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_fwd.restype = ci
-        L.ssm_scan_bidir_fwd.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_fwd.argtypes = [vp] * 12 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
         L.ssm_scan_fwd_status.argtypes = [vp, sz] + [i64] * 4 + [ci, vp]
         L.ssm_scan_fwd_status.restype = ci
@@ -91,17 +91,17 @@ def lib():
         L.ssm_scan_fwd_noalloc.restype = ci
         L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_bwd_workspace_bytes.restype = sz
-        L.ssm_scan_bwd.argtypes = [vp] * 18 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bwd.argtypes = [vp] * 19 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bwd.restype = ci
         L.ssm_scan_bidir_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
         L.ssm_scan_bidir_bwd_workspace_bytes.restype = sz
-        L.ssm_scan_bidir_bwd.argtypes = [vp] * 18 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_bwd.argtypes = [vp] * 22 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_bwd.restype = ci
         L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp]
         L.ssm_ssd_fwd.restype = ci
         L.ssm_ssd_bidir_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
         L.ssm_ssd_bidir_workspace_bytes.restype = sz
-        L.ssm_ssd_bidir_fwd.argtypes = [vp] * 11 + [i64] * 6 + [ci, vp, sz, vp]
+        L.ssm_ssd_bidir_fwd.argtypes = [vp] * 12 + [i64] * 6 + [ci, vp, sz, vp]
         L.ssm_ssd_bidir_fwd.restype = ci
         L.ssm_status_str.argtypes = [ci]
         L.ssm_status_str.restype = ctypes.c_char_p
@@ -333,11 +333,12 @@ def ssm_scan_fwd_status(x, A, workspace, stream=None):
 
 
 def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=None, workspace=None,
-                       stream=None, h0=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
-    """y = forward scan (from h0, zero if None) + reverse-time scan (shared
-    weights, read in place) + D x, with the same options as ssm_scan_fwd."""
+                       stream=None, h0=None, g0=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
+    """y = forward scan (from h0, zero if None) + reverse-time scan (from g0
+    at the last step, zero if None; shared weights, read in place) + D x,
+    with the same options as ssm_scan_fwd."""
     _, (Bs, L, ED, N) = _scan_args("ssm_scan_bidir_fwd", x, delta, A, B, C, D, h0, dt_bias, dt_limit, z,
-                                   workspace, [("y", y, "seq"), ("h_last", h_last, "state"),
+                                   workspace, [("g0", g0, "state"), ("y", y, "seq"), ("h_last", h_last, "state"),
                                                ("g_first", g_first, "state")])
     dt = _dtype_code(x)
     if y is None:
@@ -345,7 +346,7 @@ def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=N
         y = torch.empty_like(x)
     workspace, ws_bytes = _workspace(workspace, ssm_scan_workspace_bytes(Bs, L, ED, N, dt, True), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
-    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0),
                                   _byref(opts), _ptr(y),
                                   _ptr(h_last), _ptr(g_first), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
                                   _stream(x, stream))
@@ -363,17 +364,22 @@ def ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32, gate=False):
 
 
 def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias, dt_softplus,
-         dt_limit, want_ddt_bias, z):
+         dt_limit, want_ddt_bias, z, dh_last=None, g0=None, dg_first=None, want_dg0=False):
     import torch
     where = "ssm_scan_bidir_bwd" if bidir else "ssm_scan_bwd"
     o = dict(out or {})
     known = {"dx": "seq", "ddelta": "seq", "dA": "a", "dB": "bc", "dC": "bc", "dD": "ed", "dh0": "state",
              "ddt_bias": "ed", "dz": "seq"}
+    if bidir:
+        known["dg0"] = "state"
     for k in o:
         if k not in known:
             raise ValueError("%s: unknown output %r" % (where, k))
     a, (Bs, L, ED, N) = _scan_args(where, x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
-                                   [("dy", dy, "seq", True)] + [(k, v, known[k]) for k, v in o.items()])
+                                   [("dy", dy, "seq", True), ("dh_last", dh_last, "state"), ("g0", g0, "state"),
+                                    ("dg_first", dg_first, "state")] + [(k, v, known[k]) for k, v in o.items()])
+    if not bidir and (g0 is not None or dg_first is not None):
+        raise ValueError("%s: g0 and dg_first belong to the bidirectional scan" % where)
     dt = _dtype_code(x)
     o.setdefault("dx", torch.empty_like(x))
     o.setdefault("ddelta", torch.empty_like(x))
@@ -384,6 +390,8 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
         o.setdefault("dD", torch.empty((ED,), dtype=torch.float32, device=x.device))
     if want_dh0:
         o.setdefault("dh0", torch.empty((Bs, ED, N), dtype=torch.float32, device=x.device))
+    if bidir and want_dg0:
+        o.setdefault("dg0", torch.empty((Bs, ED, N), dtype=torch.float32, device=x.device))
     if want_ddt_bias or dt_bias is not None:
         o.setdefault("ddt_bias", torch.empty((ED,), dtype=torch.float32, device=x.device))
     if z is not None:
@@ -392,21 +400,29 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
     need = (ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm_scan_bwd_workspace_bytes)(Bs, L, ED, N, dt,
                                                                                             z is not None)
     workspace, ws_bytes = _workspace(workspace, need, x.device)
-    fn = lib().ssm_scan_bidir_bwd if bidir else lib().ssm_scan_bwd
-    rc = fn(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts), _ptr(dy),
-            _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
-            _ptr(o.get("dD")), _ptr(o.get("dh0")), _ptr(o.get("ddt_bias")), _ptr(o.get("dz")), Bs, L, ED, N, dt,
-            _ptr(workspace),
-            ws_bytes, _stream(x, stream))
+    grads = (_ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o.get("dD")),
+             _ptr(o.get("dh0")))
+    tail = (_ptr(o.get("ddt_bias")), _ptr(o.get("dz")), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
+            _stream(x, stream))
+    if bidir:
+        rc = lib().ssm_scan_bidir_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0),
+                                      _byref(opts), _ptr(dy), _ptr(dh_last), _ptr(dg_first), *grads,
+                                      _ptr(o.get("dg0")), *tail)
+    else:
+        rc = lib().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
+                                _ptr(dy), _ptr(dh_last), *grads, *tail)
     if rc != SSM_OK:
         raise SSMError(rc, where)
     return o
 
 
 def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
-                 stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None):
-    """Gradients of sum(dy * y) for y = ssm_scan_fwd(x, delta, A, B, C, D, h0=h0,
-    dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit, z=z).
+                 stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None,
+                 dh_last=None):
+    """Gradients of sum(dy * y) (+ sum(dh_last * h_last) when dh_last, the
+    final state's gradient, is given) for y = ssm_scan_fwd(x, delta, A, B,
+    C, D, h0=h0, dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit,
+    z=z).
 
     Returns a dict with dx, ddelta (like x; the raw delta's gradient), dA
     (like A), dB, dC (like B), dD (ED,) float32 if want_dD, dh0 (Bs, ED, N)
@@ -415,15 +431,20 @@ def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False
     keys) are written instead of new ones.
     """
     return _bwd(False, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias,
-                dt_softplus, dt_limit, want_ddt_bias, z)
+                dt_softplus, dt_limit, want_ddt_bias, z, dh_last=dh_last)
 
 
 def ssm_scan_bidir_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
-                       stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None):
-    """Gradients of sum(dy * y) for y = ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0=h0,
-    <step-size options>, z=z), with the outputs of ssm_scan_bwd."""
+                       stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None,
+                       g0=None, dh_last=None, dg_first=None, want_dg0=False):
+    """Gradients of sum(dy * y) (+ sum(dh_last * h_last) + sum(dg_first *
+    g_first) for the final states' gradients when given) for y =
+    ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0=h0, g0=g0, <step-size
+    options>, z=z), with the outputs of ssm_scan_bwd and dg0 (the gradient of
+    g0) if want_dg0."""
     return _bwd(True, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias,
-                dt_softplus, dt_limit, want_ddt_bias, z)
+                dt_softplus, dt_limit, want_ddt_bias, z, dh_last=dh_last, g0=g0, dg_first=dg_first,
+                want_dg0=want_dg0)
 
 
 def _ssd_args(where, x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace, outs):
@@ -482,20 +503,22 @@ def ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtype=SSM_F32):
 
 
 def ssm_ssd_bidir_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, g_first=None, h0=None, workspace=None,
-                      stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
+                      stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None, g0=None):
     """Bidirectional multi-head scan: ssm_ssd_fwd plus the same scan in
-    decreasing time from a zero state (no D), with the options of
+    decreasing time from g0 (zero if None; no D), with the options of
     ssm_ssd_fwd (the gate applies to the sum). Returns y; the final states
     go to h_last (forward) and g_first (reverse) if given."""
     import torch
     Bs, L, H, P, G, N = _ssd_args("ssm_ssd_bidir_fwd", x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
-                                  [("y", y, "seq"), ("h_last", h_last, "state"), ("g_first", g_first, "state")])
+                                  [("g0", g0, "state"), ("y", y, "seq"), ("h_last", h_last, "state"),
+                                   ("g_first", g_first, "state")])
     dtc = _dtype_code(x)
     if y is None:
         y = torch.empty_like(x)
     workspace, wsb = _workspace(workspace, lib().ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtc), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
-    rc = lib().ssm_ssd_bidir_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
+    rc = lib().ssm_ssd_bidir_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0),
+                                 _byref(opts),
                                  _ptr(y), _ptr(h_last), _ptr(g_first), Bs, L, H, P, G, N, dtc, _ptr(workspace), wsb,
                                  _stream(x, stream))
     if rc != SSM_OK:

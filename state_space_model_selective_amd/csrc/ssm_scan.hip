@@ -109,6 +109,7 @@ struct ScanArgs {
   const T* C;
   const float* D;
   const float* h0;  // initial forward state (Bs, ED, N) or nullptr for zero
+  const float* g0;  // bidirectional: reverse state entering at t = L-1 (Bs, ED, N), or nullptr for zero
   // step-size pre-processing: delta' = clamp(softplus?(delta + dt_bias), dt_min, dt_max)
   const float* dt_bias;  // (ED) or nullptr
   int dt_softplus;
@@ -480,9 +481,11 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
     const bool rev = BIDIR && sweep == 0;
     st.begin(b, L, t0, Lk, rev, BIDIR && sweep == 1);
-    // entering state: h0 for the forward sweep's first chunk, else zero
+    // entering state: h0 for the forward sweep's first chunk, g0 for the
+    // reverse sweep, else zero
     float4 init = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.h0 && !rev && kchunk == 0 && ch_ok) init = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
+    if (BIDIR && p.g0 && rev && ch_ok) init = *reinterpret_cast<const float4*>(p.g0 + (b * ED + e) * 16 + 4 * g);
     carry[0] = init.x, carry[1] = init.y, carry[2] = init.z, carry[3] = init.w;
     if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = init;
 
@@ -826,7 +829,7 @@ size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, 
 }
 
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-             const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
+             const float* h0, const float* g0, const ssm_scan_options* opts, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
              int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s) {
   int rc = check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
@@ -835,7 +838,7 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
   const void* z = opts ? opts->z : nullptr;
   if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
-  const void* ptrs[] = {x, delta, A, B, C, D, h0, dt_bias, z, y, h_last, g_first, ws};
+  const void* ptrs[] = {x, delta, A, B, C, D, h0, g0, dt_bias, z, y, h_last, g_first, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSM_ERR_UNSUPPORTED;
   size_t need = workspace_bytes(Bs, L, ED, N, dtype, bidir);
@@ -843,7 +846,7 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
 
   Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
                 rng(B, s->bc * s->elem), rng(C, s->bc * s->elem), rng(D, D ? ED * 4 : 0),
-                rng(h0, h0 ? s->state * 4 : 0), rng(dt_bias, dt_bias ? ED * 4 : 0),
+                rng(h0, h0 ? s->state * 4 : 0), rng(g0, g0 ? s->state * 4 : 0), rng(dt_bias, dt_bias ? ED * 4 : 0),
                 rng(z, z ? s->seq * s->elem : 0)};
   Range out[4];
   int nout = 0;
@@ -873,7 +876,7 @@ void launch_one(const ScanArgs<T>& a, int64_t nblk, size_t dyn, hipStream_t stre
 
 template <typename T>
 int launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
+                const float* h0, const float* g0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
                 hipStream_t stream) {
   const int64_t ngroups = (ED + 15) / 16;
   const SplitPlan sp = plan_split(Bs, L, ED, bidir, device_cus());
@@ -887,6 +890,7 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.C = static_cast<const T*>(C);
   a.D = D;
   a.h0 = h0;
+  a.g0 = bidir ? g0 : nullptr;
   a.dt_bias = opts ? opts->dt_bias : nullptr;
   a.dt_softplus = opts && opts->dt_softplus ? 1 : 0;
   a.dt_min = opts ? opts->dt_min : -INFINITY;
@@ -936,23 +940,24 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
 }
 
 int run(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-        const float* h0, const ssm_scan_options* opts, void* y,
+        const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
         float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* ws,
         size_t ws_bytes, void* stream, int bidir) {
   Sizes s;
-  int rc = validate(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
+  if (!bidir) g0 = nullptr;
+  int rc = validate(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.seq == 0) {
-    // nothing to scan. Over an empty sequence the forward state stays where it
-    // entered (h_last = h0, or zero) and the reverse state is zero.
-    const bool ok = fill_async(h_last, h0, s.state * 4, st) && fill_async(bidir ? g_first : nullptr, nullptr,
+    // nothing to scan. Over an empty sequence each state stays where it
+    // entered (h_last = h0, g_first = g0, or zero).
+    const bool ok = fill_async(h_last, h0, s.state * 4, st) && fill_async(bidir ? g_first : nullptr, g0,
                                                                           s.state * 4, st);
     return ok ? SSM_OK : SSM_ERR_LAUNCH;
   }
   if (dtype == SSM_F32)
-    return launch_scan<float>(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
-  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+    return launch_scan<float>(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
 }
 
 }  // namespace
@@ -1004,14 +1009,16 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
 int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const ssm_scan_options* opts, void* y, float* h_last, int64_t Bs, int64_t L,
                  int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return run(x, delta, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 0);
+  return run(x, delta, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace,
+             workspace_bytes, stream, 0);
 }
 
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
-                       float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  return run(x, delta, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes, stream, 1);
+                       const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
+                       float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes,
+             stream, 1);
 }
 
 int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -1027,7 +1034,7 @@ int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const
     const int r2 = scratch_on_current_device(&ws);
     if (r2 != SSM_OK) return r2;
   }
-  return run(x, delta, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, ws, need, stream, 0);
+  return run(x, delta, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, ws, need, stream, 0);
 }
 
 int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t Bs, int64_t L, int64_t ED,

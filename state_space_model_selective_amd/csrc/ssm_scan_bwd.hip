@@ -57,6 +57,7 @@ struct BwdArgs {
   const T* C;
   const float* D;    // or nullptr
   const float* h0;   // or nullptr
+  const float* dh_last;  // gradient of the final state (Bs, ED, N): the adjoint carry entering the last step, or nullptr
   // step-size options of the forward: delta' = clamp(softplus?(delta + dt_bias), dt_min, dt_max)
   const float* dt_bias;  // (ED) or nullptr
   int dt_softplus;
@@ -422,7 +423,12 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   double dA[4] = {0.0, 0.0, 0.0, 0.0};  // float32 within a round, float64 across rounds
   double dDacc = 0.0;
   float kcar[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint carry out of round 0 (wave 0)
-  if (wave == 0) fa.kc[R & 1][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // the adjoint carry entering the last round: the final state's gradient
+  // (padded steps past L have a = 1 and no output, so it reaches step L-1 unchanged)
+  if (wave == 0)
+    fa.kc[R & 1][lane] = (p.dh_last && ch_ok)
+                             ? *reinterpret_cast<const float4*>(p.dh_last + (b * ED + e) * 16 + 4 * g)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
   st.template prefetch<true>(p, R - 1);
   st.template commit<true>(p, tile[(R - 1) & 1]);
   __syncthreads();
@@ -766,11 +772,21 @@ size_t bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dty
   return gate ? gated_bytes(Bs, L, ED, N, dtype, bidir, s, lo.bytes, &off) : lo.bytes;
 }
 
+// The carried states of a call and their gradients: the reverse direction's
+// initial state g0 (bidirectional), the final states' gradients dh_last and
+// dg_first (bidirectional) given by the caller, and dg0 (bidirectional) out.
+struct StateArgs {
+  const float* g0;
+  const float* dh_last;
+  const float* dg_first;
+  float* dg0;
+};
+
 int bwd_validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const float* h0, const ssm_scan_options* opts, const void* dy, const void* dx, const void* ddelta,
                  const float* dA, const void* dB, const void* dC, const float* dD, const float* dh0,
-                 const float* ddt_bias, const void* dz, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
-                 const void* ws, size_t ws_bytes, bool bidir, BwdSizes* s, size_t* gate_off) {
+                 const float* ddt_bias, const void* dz, const StateArgs& sa, int64_t Bs, int64_t L, int64_t ED,
+                 int64_t N, int dtype, const void* ws, size_t ws_bytes, bool bidir, BwdSizes* s, size_t* gate_off) {
   int rc = bwd_check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
   if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
@@ -781,7 +797,8 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
   if ((s->seq > 0 && (!x || !delta || !dy || !dx || !ddelta || (z && !dz))) ||
       (s->bc > 0 && (!B || !C || !dB || !dC)) || (ED > 0 && (!A || !dA)))
     return SSM_ERR_NULL;
-  const void* ptrs[] = {x, delta, A, B, C, D, h0, dt_bias, z, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, ws};
+  const void* ptrs[] = {x,  delta, A,      B,        C,  D,  h0,       dt_bias,        z,     dy,    dx,
+                        ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, ws, sa.g0, sa.dh_last, sa.dg_first, sa.dg0};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   BwdLayout lo;
@@ -792,11 +809,13 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
   const Range in[] = {rng(x, s->seq * s->elem), rng(delta, s->seq * s->elem), rng(A, ED * N * 4),
                       rng(B, s->bc * s->elem),  rng(C, s->bc * s->elem),      rng(D, D ? ED * 4 : 0),
                       rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem), rng(dt_bias, dt_bias ? ED * 4 : 0),
-                      rng(z, z ? s->seq * s->elem : 0)};
+                      rng(z, z ? s->seq * s->elem : 0), rng(sa.g0, sa.g0 ? s->state * 4 : 0),
+                      rng(sa.dh_last, sa.dh_last ? s->state * 4 : 0), rng(sa.dg_first, sa.dg_first ? s->state * 4 : 0)};
   const Range out[] = {rng(dx, s->seq * s->elem), rng(ddelta, s->seq * s->elem), rng(dA, ED * N * 4),
                        rng(dB, s->bc * s->elem),  rng(dC, s->bc * s->elem),      rng(dD, dD ? ED * 4 : 0),
                        rng(dh0, dh0 ? s->state * 4 : 0), rng(ddt_bias, ddt_bias ? ED * 4 : 0),
-                       rng(dz, dz ? s->seq * s->elem : 0), rng(ws, static_cast<int64_t>(lo.bytes))};
+                       rng(dz, dz ? s->seq * s->elem : 0), rng(ws, static_cast<int64_t>(lo.bytes)),
+                       rng(sa.dg0, sa.dg0 ? s->state * 4 : 0)};
   constexpr int nout = sizeof(out) / sizeof(out[0]);
   for (int i = 0; i < nout; ++i) {
     if (out[i].hi == out[i].lo) continue;
@@ -826,8 +845,8 @@ void launch_bwd_kernel(const BwdArgs<T>& a, int64_t nblk, size_t dyn, bool vec, 
 template <typename T>
 int launch_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-               void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, int64_t Bs, int64_t L, int64_t ED,
-               void* ws, bool bidir, const float* dyf, hipStream_t stream) {
+               void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, const StateArgs& sa, int64_t Bs,
+               int64_t L, int64_t ED, void* ws, bool bidir, const float* dyf, hipStream_t stream) {
   const bool part_f32 = bidir && !std::is_same<T, float>::value;
   BwdLayout lo;
   bwd_layout(Bs, L, ED, &lo, bidir, part_f32);
@@ -842,6 +861,7 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.C = static_cast<const T*>(C);
   a.D = D;
   a.h0 = h0;
+  a.dh_last = sa.dh_last;
   a.dt_bias = opts ? opts->dt_bias : nullptr;
   a.dt_softplus = opts && opts->dt_softplus ? 1 : 0;
   a.dt_min = opts ? opts->dt_min : -INFINITY;
@@ -882,13 +902,15 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   launch_bwd_kernel<T, false>(a, nblk, dyn, vec, stream);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
   if (bidir) {
-    // the reverse-time scan: zero state at t = L-1, no D, its own halves of
-    // the partials, dx and ddelta added to the forward-time scan's (in order
-    // on the stream) and rounded once
+    // the reverse-time scan: from g0 (or zero) at t = L-1, no D, the adjoint
+    // entering from dg_first, its own halves of the partials, dx and ddelta
+    // added to the forward-time scan's (in order on the stream) and rounded
+    // once; its initial state's gradient is dg0
     BwdArgs<T> r = a;
     r.D = nullptr;
-    r.h0 = nullptr;
-    r.dh0 = nullptr;
+    r.h0 = sa.g0;
+    r.dh0 = sa.dg0;
+    r.dh_last = sa.dg_first;
     r.pB = a.pB + lo.ngroups * Bs * L * 16;
     r.pC = a.pC + lo.ngroups * Bs * L * 16;
     r.pA = a.pA + Bs * lo.EDp * 16;
@@ -915,12 +937,14 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
 
 int run_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
             const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-            void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
-            int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool bidir) {
+            void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, StateArgs sa, int64_t Bs,
+            int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+            bool bidir) {
   BwdSizes s;
   size_t gate_off = 0;
-  const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, Bs,
-                              L, ED, N, dtype, workspace, workspace_bytes, bidir, &s, &gate_off);
+  if (!bidir) sa.g0 = sa.dg_first = sa.dg0 = nullptr;
+  const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa,
+                              Bs, L, ED, N, dtype, workspace, workspace_bytes, bidir, &s, &gate_off);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   ssm_scan_options ungated{};
@@ -930,8 +954,8 @@ int run_bwd(const void* x, const void* delta, const float* A, const void* B, con
     // dy silu(z), then the backward of y' with that output gradient
     ungated = *opts;
     ungated.z = nullptr;
-    const int frc = bidir ? ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, &ungated, dz, nullptr, nullptr, Bs, L, ED,
-                                               N, dtype, workspace, gate_off, stream)
+    const int frc = bidir ? ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0, sa.g0, &ungated, dz, nullptr, nullptr, Bs,
+                                               L, ED, N, dtype, workspace, gate_off, stream)
                           : ssm_scan_fwd(x, delta, A, B, C, D, h0, &ungated, dz, nullptr, Bs, L, ED, N, dtype,
                                          workspace, gate_off, stream);
     if (frc != SSM_OK) return frc;
@@ -949,17 +973,19 @@ int run_bwd(const void* x, const void* delta, const float* A, const void* B, con
   }
   if (s.seq == 0) {
     // an empty output: every gradient is zero (dB and dC too when there are
-    // time steps but no channels)
+    // time steps but no channels), except that over zero steps each final
+    // state is its initial state, so dh0 = dh_last and dg0 = dg_first
     const bool ok = fill_async(dA, nullptr, ED * N * 4, st) && fill_async(dD, nullptr, ED * 4, st) &&
-                    fill_async(dh0, nullptr, s.state * 4, st) && fill_async(dB, nullptr, s.bc * s.elem, st) &&
+                    fill_async(dh0, sa.dh_last, s.state * 4, st) && fill_async(sa.dg0, sa.dg_first, s.state * 4, st) &&
+                    fill_async(dB, nullptr, s.bc * s.elem, st) &&
                     fill_async(dC, nullptr, s.bc * s.elem, st) && fill_async(ddt_bias, nullptr, ED * 4, st);
     return ok ? SSM_OK : SSM_ERR_LAUNCH;
   }
   if (dtype == SSM_F32)
-    return launch_bwd<float>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
-                             ED, workspace, bidir, dyf, st);
-  return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, Bs, L,
-                              ED, workspace, bidir, dyf, st);
+    return launch_bwd<float>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, sa, Bs,
+                             L, ED, workspace, bidir, dyf, st);
+  return launch_bwd<uint16_t>(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, sa, Bs,
+                              L, ED, workspace, bidir, dyf, st);
 }
 
 }  // namespace
@@ -975,20 +1001,23 @@ size_t ssm_scan_bidir_bwd_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int
 }
 
 int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const ssm_scan_options* opts, const void* dy, void* dx, void* ddelta, float* dA,
-                 void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
-                 int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, Bs, L, ED, N,
-                 dtype, workspace, workspace_bytes, stream, false);
+                 const float* h0, const ssm_scan_options* opts, const void* dy, const float* dh_last, void* dx,
+                 void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz,
+                 int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  const StateArgs sa{nullptr, dh_last, nullptr, nullptr};
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
+                 N, dtype, workspace, workspace_bytes, stream, false);
 }
 
 int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const float* h0, const ssm_scan_options* opts, const void* dy, void* dx,
-                       void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias,
-                       void* dz, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, Bs, L, ED, N,
-                 dtype, workspace, workspace_bytes, stream, true);
+                       const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, const void* dy,
+                       const float* dh_last, const float* dg_first, void* dx, void* ddelta, float* dA, void* dB,
+                       void* dC, float* dD, float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+                       int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const StateArgs sa{g0, dh_last, dg_first, dg0};
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
+                 N, dtype, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -52,6 +52,7 @@ struct SsdArgs {
   const T* C;
   const float* D;
   const float* h0;
+  const float* g0;  // bidirectional: reverse state entering at t = L-1, or nullptr
   T* y;
   float* h_last;
   // bidirectional scan: float32 partial of the reverse direction, (Bs, L, H,
@@ -213,13 +214,14 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   // partial, then the forward sweep adding it
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
   const bool rev = BIDIR && sweep == 0;
+  const float* const init = rev ? p.g0 : p.h0;  // the sweep's entering state (null: zero)
   f4 st[PBW];
 #pragma unroll
   for (int k = 0; k < PBW; ++k)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-      st[k][r] = p.h0 && !rev ? p.h0[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
+      st[k][r] = init ? init[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
       sm.S[pp][nn] = st[k][r];
     }
 
@@ -641,6 +643,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   // partial, then the forward sweep adding it
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
   const bool rev = BIDIR && sweep == 0;
+  const float* const init = rev ? p.g0 : p.h0;  // the sweep's entering state (null: zero)
   const float Dh = rev ? 0.f : Dfwd;
 
   // st[k][r] = S[p][n], p = 16 (spb + k) + li, n = 16 snb + 4 lk + r
@@ -649,7 +652,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   for (int k = 0; k < PBW; ++k) {
     const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[k][r] = p.h0 && !rev ? p.h0[((b * p.H + h) * kP + pp) * N + n0 + r] : 0.f;
+    for (int r = 0; r < 4; ++r) st[k][r] = init ? init[((b * p.H + h) * kP + pp) * N + n0 + r] : 0.f;
     store_state_bf16(sm, pp, n0, st[k]);
   }
 
@@ -808,7 +811,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
 }
 
 int ssd_validate(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-                 const float* h0, const ssm_scan_options* opts, const void* y, const float* h_last,
+                 const float* h0, const float* g0, const ssm_scan_options* opts, const void* y, const float* h_last,
                  const float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
                  int dtype) {
   // Bs and L may be zero (empty tensors); H, P, G and N are positive
@@ -827,13 +830,13 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
   const void* z = opts ? opts->z : nullptr;
   if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
-  const void* ptrs[] = {x, dt, A, B, C, D, h0, dt_bias, z, y, h_last, g_first};
+  const void* ptrs[] = {x, dt, A, B, C, D, h0, g0, dt_bias, z, y, h_last, g_first};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   const int64_t es = dtype == SSM_F32 ? 4 : 2;
   const Range in[] = {rng(x, seq * es), rng(dt, hd * es), rng(A, H * 4), rng(B, bc * es), rng(C, bc * es),
-                      rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(dt_bias, dt_bias ? H * 4 : 0),
-                      rng(z, z ? seq * es : 0)};
+                      rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(g0, g0 ? state * 4 : 0),
+                      rng(dt_bias, dt_bias ? H * 4 : 0), rng(z, z ? seq * es : 0)};
   const Range out[] = {rng(y, seq * es), rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0)};
   for (int i = 0; i < 3; ++i) {
     if (out[i].hi == out[i].lo) continue;
@@ -869,7 +872,7 @@ void launch_ssd_kernel(const SsdArgs<T>& a, int64_t N, dim3 grid, dim3 block, hi
 
 template <typename T>
 int launch_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-               const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, float* part,
+               const float* h0, const float* g0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, float* part,
                bool bidir, int64_t Bs, int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream) {
   SsdArgs<T> a;
   a.x = static_cast<const T*>(x);
@@ -879,6 +882,7 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   a.C = static_cast<const T*>(C);
   a.D = D;
   a.h0 = h0;
+  a.g0 = bidir ? g0 : nullptr;
   a.y = static_cast<T*>(y);
   a.h_last = h_last;
   a.part = part;
@@ -904,11 +908,10 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
-// An empty batch or sequence: nothing to scan. Over zero steps the forward
-// state stays where it entered (h_last = h0, or zero); the reverse state is
-// zero.
-int ssd_empty(const float* h0, float* h_last, float* g_first, int64_t state, hipStream_t stream) {
-  const bool ok = fill_async(h_last, h0, state * 4, stream) && fill_async(g_first, nullptr, state * 4, stream);
+// An empty batch or sequence: nothing to scan. Over zero steps each state
+// stays where it entered (h_last = h0, g_first = g0, or zero).
+int ssd_empty(const float* h0, const float* g0, float* h_last, float* g_first, int64_t state, hipStream_t stream) {
+  const bool ok = fill_async(h_last, h0, state * 4, stream) && fill_async(g_first, g0, state * 4, stream);
   return ok ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
@@ -918,13 +921,15 @@ extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const 
                            const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
                            int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
                            void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (Bs == 0 || L == 0) return ssd_empty(h0, h_last, nullptr, Bs * H * P * N, st);
+  if (Bs == 0 || L == 0) return ssd_empty(h0, nullptr, h_last, nullptr, Bs * H * P * N, st);
   if (dtype == SSM_F32)
-    return launch_ssd<float>(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
-  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N, st);
+    return launch_ssd<float>(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N,
+                             st);
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G,
+                              N, st);
 }
 
 extern "C" size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
@@ -933,17 +938,17 @@ extern "C" size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H
 }
 
 extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                                 const float* D, const float* h0, const ssm_scan_options* opts, void* y,
-                                 float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P,
+                                 const float* D, const float* h0, const float* g0, const ssm_scan_options* opts,
+                                 void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P,
                                  int64_t G, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
+  const int rc = ssd_validate(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (Bs == 0 || L == 0) return ssd_empty(h0, h_last, g_first, Bs * H * P * N, st);
+  if (Bs == 0 || L == 0) return ssd_empty(h0, g0, h_last, g_first, Bs * H * P * N, st);
   if (dtype == SSM_F32)
-    return launch_ssd<float>(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, static_cast<float*>(y), true, Bs, L, H,
-                             G, N, st);
+    return launch_ssd<float>(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, static_cast<float*>(y), true, Bs, L,
+                             H, G, N, st);
   const size_t need = ssd_bidir_ws_bytes(Bs, L, H, P, dtype);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SSM_ERR_WORKSPACE;
   // the workspace may not overlap any argument
@@ -952,11 +957,12 @@ extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, 
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
   const void* z = opts ? opts->z : nullptr;
   const Range args[] = {rng(x, seq * 2), rng(dt, hd * 2), rng(A, H * 4), rng(B, bc * 2), rng(C, bc * 2),
-                        rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(y, seq * 2),
+                        rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(g0, g0 ? state * 4 : 0),
+                        rng(y, seq * 2),
                         rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0),
                         rng(dt_bias, dt_bias ? H * 4 : 0), rng(z, z ? seq * 2 : 0)};
   for (const Range& r : args)
     if (r.hi > r.lo && overlap(ws, r)) return SSM_ERR_ALIAS;
-  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, opts, y, h_last, g_first, static_cast<float*>(workspace), true,
-                              Bs, L, H, G, N, st);
+  return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, static_cast<float*>(workspace),
+                              true, Bs, L, H, G, N, st);
 }

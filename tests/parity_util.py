@@ -40,7 +40,7 @@ def y_to_numpy(y):
     return y.double().cpu().numpy()
 
 
-def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False, h0=None, opts=None):
+def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=False, h0=None, opts=None, g0=None):
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -59,8 +59,9 @@ def run_gpu(inp, bidir=False, want_h=False, want_g=False, stream=None, D_none=Fa
         if kw.get("z") is not None:
             kw["z"] = to_device({"z": kw["z"]}, dev)["z"]
     if bidir:
+        g0t = None if g0 is None else torch.from_numpy(np.ascontiguousarray(g0, dtype=np.float32)).to(dev)
         y = ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, g_first=g,
-                                   stream=stream, h0=h0t, **kw)
+                                   stream=stream, h0=h0t, g0=g0t, **kw)
     else:
         y = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D, h_last=h, stream=stream, h0=h0t, **kw)
     torch.cuda.synchronize()
@@ -104,7 +105,8 @@ def gather_channels(y, chans, ED):
 
 
 def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None, bidir=False,
-                dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
+                dt_bias=None, dt_softplus=False, dt_limit=None, z=None, dh_last=None, g0=None, dg_first=None,
+                want_dg0=False):
     """ssm_scan_bwd (bidir: ssm_scan_bidir_bwd) on the GPU; every gradient as
     a float64 numpy array. dt_bias (numpy, float32) / dt_softplus / dt_limit
     are the step-size options; with dt_bias the result holds ddt_bias; z (like
@@ -132,23 +134,31 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
     if z is not None:
         zt = to_device(dict(z=z), dev)["z"]
         out["dz"] = torch.full_like(t["x"], float("nan"))
+    st = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    kw = dict(dh_last=st(dh_last))
+    if bidir:
+        kw.update(g0=st(g0), dg_first=st(dg_first), want_dg0=want_dg0)
+        if want_dg0:
+            out["dg0"] = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev)
     fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
     res = fn(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
              h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream, dt_bias=bias,
-             dt_softplus=dt_softplus, dt_limit=dt_limit, z=zt)
+             dt_softplus=dt_softplus, dt_limit=dt_limit, z=zt, **kw)
     torch.cuda.synchronize()
     return {k: y_to_numpy(v) for k, v in res.items()}
 
 
 def assert_grads_close(got, ref, dtype):
     """Every gradient the GPU returned against the oracle's. dx, ddelta, dB,
-    dC and dz carry the inputs' dtype; dA, dD, dh0 and ddt_bias are float32."""
+    dC and dz carry the inputs' dtype; dA, dD, dh0, dg0 and ddt_bias are
+    float32."""
     for k, v in got.items():
         tol = TOL[dtype] if k in ("dx", "ddelta", "dB", "dC", "dz") else TOL["f32"]
         assert_close(k, v, ref[k], tol)
 
 
-def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=False, want_g=False, opts=None):
+def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=False, want_g=False, opts=None,
+                g0=None):
     """ssm_ssd_fwd (or ssm_ssd_bidir_fwd) on the GPU: (y, h_last) as float64
     numpy arrays, and g_first as a third value for the bidirectional scan.
     opts: dt_bias / dt_softplus / dt_limit / z as numpy values or None."""
@@ -171,8 +181,9 @@ def run_gpu_ssd(inp, h0=None, want_h=False, D_none=False, stream=None, bidir=Fal
         if kw.get("z") is not None:
             kw["z"] = to_device({"z": kw["z"]}, dev)["z"]
     if bidir:
+        g0t = None if g0 is None else torch.from_numpy(np.ascontiguousarray(g0, dtype=np.float32)).to(dev)
         ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, g_first=gf, h0=h0t,
-                              stream=stream, **kw)
+                              g0=g0t, stream=stream, **kw)
     else:
         ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D, y=y, h_last=h, h0=h0t, stream=stream, **kw)
     torch.cuda.synchronize()

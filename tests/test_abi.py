@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
 # must fail validation before anything touches them. Where a GPU is present a
 # validation gap would launch a kernel on them, so these host-only checks are
 # skipped there (the GPU tests load and call the same library).
-P = [0x10000000 * (i + 1) for i in range(20)]
+P = [0x10000000 * (i + 1) for i in range(26)]
 
 pytestmark = pytest.mark.skipif(os.path.exists("/dev/kfd"),
                                 reason="calls the library with fake device addresses: host-only")
@@ -52,12 +52,21 @@ def fwd(**kw):
 
 
 def bidir(**kw):
-    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], h0=P[10], opts=None,
-                Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], h0=P[10], g0=P[15],
+                opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
     args.update(kw)
     return ssm.lib().ssm_scan_bidir_fwd(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"],
-                                        args["h0"], args["opts"], args["y"], args["h"], args["g"], args["Bs"], args["L"], args["ED"],
-                                        args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+                                        args["h0"], args["g0"], args["opts"], args["y"], args["h"], args["g"],
+                                        args["Bs"], args["L"], args["ED"], args["N"], args["dtype"], args["ws"],
+                                        args["ws_bytes"], None)
+
+
+def test_reverse_initial_state_arguments():
+    assert bidir(g0=P[15] + 4) == ssm.SSM_ERR_UNSUPPORTED     # misaligned
+    assert bidir(g=P[15]) == ssm.SSM_ERR_ALIAS                # g_first on top of g0
+    assert bidir(y=P[15] - 64) == ssm.SSM_ERR_ALIAS           # y running into g0
+    none = dict(x=None, delta=None, B=None, C=None, D=None, y=None, h=None, g=None, h0=None, g0=None)
+    assert bidir(**dict(none, Bs=0, ED=0)) == ssm.SSM_OK
 
 
 @pytest.mark.parametrize("name", ["x", "delta", "A", "B", "C", "y"])
@@ -162,15 +171,21 @@ def test_options_validation():
 
 
 BWD_PTRS = ["x", "delta", "A", "B", "C", "D", "h0", "opts", "dy", "dx", "ddelta", "dA", "dB", "dC", "dD", "dh0",
-            "ddt_bias", "dz", "ws"]
+            "ddt_bias", "dz", "ws", "dh_last", "g0", "dg_first", "dg0"]
+BWD_DEFAULT = {n: P[i] for i, n in enumerate(BWD_PTRS)}  # the default pointer of each argument
+# argument order of the two entry points
+BWD_ORDER = ["x", "delta", "A", "B", "C", "D", "h0", "opts", "dy", "dh_last", "dx", "ddelta", "dA", "dB", "dC", "dD",
+             "dh0", "ddt_bias", "dz"]
+BIDIR_BWD_ORDER = ["x", "delta", "A", "B", "C", "D", "h0", "g0", "opts", "dy", "dh_last", "dg_first", "dx", "ddelta",
+                   "dA", "dB", "dC", "dD", "dh0", "dg0", "ddt_bias", "dz"]
 
 
 def bwd(**kw):
-    args = {n: P[i] for i, n in enumerate(BWD_PTRS)}
+    args = dict(BWD_DEFAULT)
     args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32)  # (opts is read on the host)
     args["ws_bytes"] = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32)
     args.update(kw)
-    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_PTRS[:18]], args["Bs"], args["L"], args["ED"], args["N"],
+    return ssm.lib().ssm_scan_bwd(*[args[n] for n in BWD_ORDER], args["Bs"], args["L"], args["ED"], args["N"],
                                   args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -213,6 +228,9 @@ def test_bwd_validation():
     assert bwd(ddelta=P[9] + 256) == ssm.SSM_ERR_ALIAS    # ddelta inside dx
     assert bwd(dh0=P[6]) == ssm.SSM_ERR_ALIAS             # dh0 on top of h0
     assert bwd(ws=P[8]) == ssm.SSM_ERR_ALIAS              # workspace on top of dy
+    assert bwd(dh_last=P[19] + 8) == ssm.SSM_ERR_UNSUPPORTED   # misaligned final-state gradient
+    assert bwd(dh0=P[19]) == ssm.SSM_ERR_ALIAS            # dh0 on top of dh_last
+    assert bwd(dh_last=P[9]) == ssm.SSM_ERR_ALIAS         # dx on top of dh_last
 
 
 SSD_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "opts", "y", "h"]
@@ -239,7 +257,7 @@ def test_ssd_empty_inputs_are_valid():
     assert ssd(**dict(none, L=0)) == ssm.SSM_OK
     assert ssd(**dict(none, Bs=0)) == ssm.SSM_OK
     assert ssd(**dict(none, L=0, A=None)) == ssm.SSM_ERR_NULL   # A (H) is never empty
-    assert ssd_bidir(**dict(none, g=None, ws=None, ws_bytes=0, L=0)) == ssm.SSM_OK
+    assert ssd_bidir(**dict(none, g=None, g0=None, ws=None, ws_bytes=0, L=0)) == ssm.SSM_OK
 
 
 def test_ssd_validation():
@@ -256,9 +274,10 @@ def test_ssd_validation():
 
 
 SSD_BI_PTRS = ["x", "dt", "A", "B", "C", "D", "h0", "opts", "y", "h", "g"]
+SSD_BI_ORDER = ["x", "dt", "A", "B", "C", "D", "h0", "g0", "opts", "y", "h", "g"]
 
 
-BP = dict({n: P[i] for i, n in enumerate(SSD_BI_PTRS)}, ws=P[12])  # default pointers
+BP = dict({n: P[i] for i, n in enumerate(SSD_BI_PTRS)}, ws=P[12], g0=P[24])  # default pointers
 
 
 def ssd_bidir(**kw):
@@ -266,7 +285,7 @@ def ssd_bidir(**kw):
     args.update(opts=None, Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_BF16)
     args["ws_bytes"] = ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16)
     args.update(kw)
-    return ssm.lib().ssm_ssd_bidir_fwd(*[args[n] for n in SSD_BI_PTRS], args["Bs"], args["L"], args["H"], args["P"],
+    return ssm.lib().ssm_ssd_bidir_fwd(*[args[n] for n in SSD_BI_ORDER], args["Bs"], args["L"], args["H"], args["P"],
                                        args["G"], args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -293,6 +312,9 @@ def test_ssd_bidir_validation():
     assert ssd_bidir(g=BP["y"] + 64) == ssm.SSM_ERR_ALIAS          # g_first inside y
     assert ssd_bidir(ws=BP["y"]) == ssm.SSM_ERR_ALIAS              # workspace on top of y
     assert ssd_bidir(ws=BP["x"]) == ssm.SSM_ERR_ALIAS              # workspace on top of x
+    assert ssd_bidir(g0=BP["g0"] + 4) == ssm.SSM_ERR_UNSUPPORTED   # misaligned reverse initial state
+    assert ssd_bidir(g=BP["g0"]) == ssm.SSM_ERR_ALIAS              # g_first on top of g0
+    assert ssd_bidir(ws=BP["g0"]) == ssm.SSM_ERR_ALIAS             # workspace on top of g0
     # float32 needs no workspace: the reverse partial is kept in y itself
     assert ssd_bidir(dtype=ssm.SSM_F32, ws=None, ws_bytes=0, N=96) == ssm.SSM_ERR_UNSUPPORTED
 
@@ -318,11 +340,11 @@ def test_ssd_options_validation():
 
 
 def bidir_bwd(**kw):
-    args = {n: P[i] for i, n in enumerate(BWD_PTRS)}
+    args = dict(BWD_DEFAULT)
     args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_BF16)
     args["ws_bytes"] = ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
     args.update(kw)
-    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BWD_PTRS[:18]], args["Bs"], args["L"], args["ED"],
+    return ssm.lib().ssm_scan_bidir_bwd(*[args[n] for n in BIDIR_BWD_ORDER], args["Bs"], args["L"], args["ED"],
                                         args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
 
 
@@ -348,6 +370,11 @@ def test_bidir_bwd_validation():
     assert bidir_bwd(ws=None) == ssm.SSM_ERR_WORKSPACE
     assert bidir_bwd(ws_bytes=plain) == ssm.SSM_ERR_WORKSPACE   # the one-direction size is too small
     assert bidir_bwd(dx=P[0]) == ssm.SSM_ERR_ALIAS
+    assert bidir_bwd(dg0=P[20]) == ssm.SSM_ERR_ALIAS          # dg0 on top of g0
+    assert bidir_bwd(dg0=P[21]) == ssm.SSM_ERR_ALIAS          # dg0 on top of dg_first
+    assert bidir_bwd(dh0=P[22]) == ssm.SSM_ERR_ALIAS          # dh0 on top of dg0
+    assert bidir_bwd(g0=P[20] + 4) == ssm.SSM_ERR_UNSUPPORTED
+    assert bidir_bwd(dg_first=P[21] + 8) == ssm.SSM_ERR_UNSUPPORTED
     none = {n: None for n in BWD_PTRS}
     assert bidir_bwd(**dict(none, Bs=0, ED=0, ws_bytes=0)) == ssm.SSM_OK
 
