@@ -74,13 +74,18 @@ struct Vec4<uint16_t> {
 // log(1 + e^v) (as log1p(e^v) for accuracy at small e^v); the output gate is
 // y z sigmoid(z). bias points at the channel's (or head's) bias, or is null.
 // ---------------------------------------------------------------------------
+// 1 / v from the hardware reciprocal (v_rcp_f32, within 1 ulp): an IEEE
+// division costs about ten instructions more, on the staging threads'
+// critical path.
+__device__ __forceinline__ float rcp_fast(float v) { return __builtin_amdgcn_rcpf(v); }
+
 // log(1 + u) for u >= 0 from the hardware logarithm, accurate to a few ulp:
 // with w = 1 + u rounded, log(w) u / (w - 1) cancels the rounding of w
 // (D. Goldberg, "What every computer scientist should know about
 // floating-point arithmetic", 1991, section 4.1); u itself when w rounds to 1.
 __device__ __forceinline__ float log1p_pos(float u) {
   const float w = 1.f + u;
-  return w == 1.f ? u : __logf(w) * (u / (w - 1.f));
+  return w == 1.f ? u : __logf(w) * (u * rcp_fast(w - 1.f));
 }
 
 // e^x - 1 from the hardware exponential and logarithm (W. Kahan's method:
@@ -90,7 +95,7 @@ __device__ __forceinline__ float expm1_fast(float x) {
   const float v = __expf(x);
   if (v == 1.f) return x;
   const float vm = v - 1.f;
-  return vm == -1.f ? -1.f : vm * (x / __logf(v));
+  return vm == -1.f ? -1.f : vm * (x * rcp_fast(__logf(v)));
 }
 
 __device__ __forceinline__ float map_step(float d, const float* bias, int softplus, float lo, float hi) {
@@ -99,7 +104,9 @@ __device__ __forceinline__ float map_step(float d, const float* bias, int softpl
   return fminf(fmaxf(d, lo), hi);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+// z sigmoid(z) (where e^-z overflows, the reciprocal of the infinite
+// denominator is 0 and so is the result, as with a division)
+__device__ __forceinline__ float silu(float z) { return z * rcp_fast(1.f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------
 // Cross-lane operands (DPP). Lane q of a 16-lane row holds B_t[q] (or

@@ -164,10 +164,11 @@ struct alignas(16) FoldArea {
 
 enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
 
-// delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max)
+// delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max), with the
+// channel's bias (0 without one) already in a register
 template <typename T>
-__device__ __forceinline__ float step_size(const ScanArgs<T>& p, float d, int64_t e) {
-  return map_step(d, p.dt_bias ? p.dt_bias + e : nullptr, p.dt_softplus, p.dt_min, p.dt_max);
+__device__ __forceinline__ float step_size(const ScanArgs<T>& p, float d, float bias) {
+  return map_step(d + bias, nullptr, p.dt_softplus, p.dt_min, p.dt_max);
 }
 
 // Staging of one round: each thread owns TPT fixed (row, chunk) tasks of the
@@ -181,6 +182,7 @@ struct Stager {
   int row[TPT], chk[TPT];
   bool is_xd[TPT], chunk_ok[TPT], row_ok[TPT];
   float4 dval[TPT];              // D of the chunk's channels
+  float4 bval[TPT];              // dt_bias of the chunk's channels (0 without a bias), loaded once
   // prefetched data: loaded bits (VEC; widened at commit, so that the wave
   // does not wait for the loads at the prefetch), or widened values (element
   // by element loads of a ragged channel count)
@@ -210,6 +212,9 @@ struct Stager {
       const bool dd = is_xd[k] && p.D != nullptr;
       dval[k] = make_float4(dd && ce + 0 < ED ? p.D[ce + 0] : 0.f, dd && ce + 1 < ED ? p.D[ce + 1] : 0.f,
                             dd && ce + 2 < ED ? p.D[ce + 2] : 0.f, dd && ce + 3 < ED ? p.D[ce + 3] : 0.f);
+      const bool db = is_xd[k] && p.dt_bias != nullptr;
+      bval[k] = make_float4(db && ce + 0 < ED ? p.dt_bias[ce + 0] : 0.f, db && ce + 1 < ED ? p.dt_bias[ce + 1] : 0.f,
+                            db && ce + 2 < ED ? p.dt_bias[ce + 2] : 0.f, db && ce + 3 < ED ? p.dt_bias[ce + 3] : 0.f);
     }
   }
 
@@ -319,10 +324,10 @@ struct Stager {
           // padded rows and channels keep delta = 0 (a = 1, b = 0: no effect)
           const bool ok = row_ok[k] && chunk_ok[k];
           const int64_t ce = ce0 + c4;
-          dv.x = ok && ce + 0 < ED ? step_size(p, dv.x, ce + 0) : 0.f;
-          dv.y = ok && ce + 1 < ED ? step_size(p, dv.y, ce + 1) : 0.f;
-          dv.z = ok && ce + 2 < ED ? step_size(p, dv.z, ce + 2) : 0.f;
-          dv.w = ok && ce + 3 < ED ? step_size(p, dv.w, ce + 3) : 0.f;
+          dv.x = ok && ce + 0 < ED ? step_size(p, dv.x, bval[k].x) : 0.f;
+          dv.y = ok && ce + 1 < ED ? step_size(p, dv.y, bval[k].y) : 0.f;
+          dv.z = ok && ce + 2 < ED ? step_size(p, dv.z, bval[k].z) : 0.f;
+          dv.w = ok && ce + 3 < ED ? step_size(p, dv.w, bval[k].w) : 0.f;
         }
         if (GATE) {
           const float4 zv = val_z(k);

@@ -166,7 +166,9 @@ struct BwdStager {
   float4 ra, rb, rc;
   float4 bias4;  // OPTS: dt_bias of the task's channels
   int64_t b, e0, ED, L;
-  float4 dbacc = make_float4(0.f, 0.f, 0.f, 0.f);  // this task's raw step-size gradients, summed over its rounds
+  // this task's raw step-size gradients, summed over its rounds in float64
+  // (a float32 sum over thousands of rounds would lose the small terms)
+  double dbacc[4] = {0.0, 0.0, 0.0, 0.0};
 
   __device__ __forceinline__ void init(int tid, int64_t b_, int64_t e0_, int64_t ED_, int64_t L_) {
     int u = tid;
@@ -245,7 +247,10 @@ struct BwdStager {
       const float4 m = *reinterpret_cast<const float4*>(&tl.dt[row][c4]);
       gd = make_float4(gd.x * map_deriv(p, m.x), gd.y * map_deriv(p, m.y), gd.z * map_deriv(p, m.z),
                        gd.w * map_deriv(p, m.w));
-      dbacc = make_float4(dbacc.x + gd.x, dbacc.y + gd.y, dbacc.z + gd.z, dbacc.w + gd.w);
+      dbacc[0] += static_cast<double>(gd.x);
+      dbacc[1] += static_cast<double>(gd.y);
+      dbacc[2] += static_cast<double>(gd.z);
+      dbacc[3] += static_cast<double>(gd.w);
     }
     const int64_t ce = e0 + c4, off = (b * L + t) * ED + ce;
     if (VEC) {
@@ -596,10 +601,10 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     double* dbs = reinterpret_cast<double*>(&cs);  // [RT rows][16 channels]
     static_assert(sizeof(ColSums<RT>) >= sizeof(double) * RT * 16, "reduction area");
     if (st.is_xd) {
-      dbs[st.row * 16 + 4 * st.chk + 0] = st.dbacc.x;
-      dbs[st.row * 16 + 4 * st.chk + 1] = st.dbacc.y;
-      dbs[st.row * 16 + 4 * st.chk + 2] = st.dbacc.z;
-      dbs[st.row * 16 + 4 * st.chk + 3] = st.dbacc.w;
+      dbs[st.row * 16 + 4 * st.chk + 0] = st.dbacc[0];
+      dbs[st.row * 16 + 4 * st.chk + 1] = st.dbacc[1];
+      dbs[st.row * 16 + 4 * st.chk + 2] = st.dbacc[2];
+      dbs[st.row * 16 + 4 * st.chk + 3] = st.dbacc[3];
     }
     __syncthreads();
     if (tid < 16) {
