@@ -80,24 +80,29 @@ namespace {
 // chunks that run concurrently; chunk k hands its inclusive end state to
 // chunk k+1 through `state` and `flag`.
 //
-// Protocol. Each workgroup first takes a ticket (an atomic counter in this
-// header, cleared before the launch) and works on the chunk the ticket
-// names: tickets are numbered chunk-major (every chunk 0 of every channel
-// group, then every chunk 1, ...), so the predecessor of a chunk holds a
-// smaller ticket and has therefore already started, whichever workgroups the
-// hardware happens to dispatch first and whatever else runs on the device.
-// A started chunk finishes its main pass without waiting on anything, then
-// (chunk k > 0) waits for flag[k-1], reads state[k-1] (acquire), publishes
-// its own inclusive state and raises flag[k] (release); a chunk's wait
-// therefore only depends on earlier tickets, and every wait ends. The wait
-// is still bounded (a few seconds): if it ever gives up, `err` is set and
-// the chunk takes NaN as its entering state, so that its outputs, its
-// published state and every later chunk's become NaN rather than silently
+// Protocol. The chunks are dealt out through 8 ticket queues, one per XCD:
+// queue q holds the chunks of a contiguous range of channel groups, chunk-
+// major (chunk 0 of each of its groups, then chunk 1, ...). A workgroup
+// takes a ticket from the queue of the XCD it runs on (so that neighbouring
+// groups, which share 128-byte lines of x, delta and y, are served by one
+// L2), and only if that queue is exhausted from the next ones in turn. Every
+// queue is consumed in ticket order and a chunk's predecessor sits in the
+// same queue at an earlier ticket, so it has already started, whichever
+// workgroups the hardware dispatches first and to which XCD, and whatever
+// else runs on the device; there are as many workgroups as chunks, so every
+// chunk is taken. A started chunk finishes its main pass without waiting on
+// anything, then (chunk k > 0) waits for flag[k-1], reads state[k-1]
+// (acquire), publishes its own inclusive state and raises flag[k] (release);
+// a chunk's wait therefore only depends on earlier tickets, and every wait
+// ends. The wait is still bounded (a few seconds): if it ever gives up, `err`
+// is set and the chunk takes NaN as its entering state, so that its outputs,
+// its published state and every later chunk's become NaN rather than silently
 // wrong; ssm_scan_fwd_status() reports the error word to the host.
+constexpr int kQueues = 8;
 struct SplitHeader {
-  unsigned err;     // nonzero: a wait gave up (never expected)
-  unsigned ticket;  // next chunk ticket, in dispatch order
-  unsigned pad[62];
+  unsigned err;              // nonzero: a wait gave up (never expected)
+  unsigned ticket[kQueues];  // next ticket of each queue
+  unsigned pad[64 - 1 - kQueues];
 };
 
 template <typename T>
@@ -412,15 +417,30 @@ __device__ __forceinline__ bool wait_flag(int* flag, unsigned* err, unsigned spi
   }
 }
 
-// The chunk (chunk index, channel-group index) that split-sequence ticket tk
-// names: chunk-major, and within a chunk, when the group count is a multiple
-// of 8, the groups in the order that puts neighbouring groups (which share
-// 128-byte lines of x, delta and y) on the same XCD when tickets follow the
-// round-robin dispatch over the 8 XCDs (a bijection on the groups only then).
-__device__ __forceinline__ void split_chunk_of_ticket(int tk, int nbg, int64_t* kchunk, int64_t* bg) {
-  *kchunk = tk / nbg;
-  const int u = tk % nbg;
-  *bg = (nbg & 7) == 0 ? (u & 7) * (nbg >> 3) + (u >> 3) : u;
+// Queue q of the split-sequence chunks holds the groups [q nbg / 8,
+// (q + 1) nbg / 8), each in nchunks chunks, chunk-major.
+__device__ __forceinline__ int split_queue_start(int q, int nbg) { return q * nbg / kQueues; }
+
+// Takes a chunk for this workgroup (thread 0): a ticket from the queue of the
+// XCD it runs on, else from the following queues in turn. Returns the chunk
+// index and channel group, or false if every queue is exhausted (impossible
+// with one workgroup per chunk).
+__device__ __forceinline__ bool split_take_chunk(unsigned* tickets, int nbg, int nchunks, int64_t* kchunk,
+                                                 int64_t* bg) {
+  // XCC_ID hardware register (bits 3:0): the XCD this wave runs on
+  const unsigned xcc = static_cast<unsigned>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20));
+  for (int d = 0; d < kQueues; ++d) {
+    const int q = static_cast<int>((xcc + d) % kQueues);
+    const int g0 = split_queue_start(q, nbg), ng = split_queue_start(q + 1, nbg) - g0;
+    if (ng == 0) continue;
+    const unsigned j = __hip_atomic_fetch_add(&tickets[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (j < static_cast<unsigned>(ng * nchunks)) {
+      *kchunk = j / ng;
+      *bg = g0 + static_cast<int>(j % ng);
+      return true;
+    }
+  }
+  return false;
 }
 
 template <typename T, int SEG, int TS, bool BIDIR, bool VEC, bool SPLIT, bool GATE, int WPE = 3>
@@ -449,16 +469,26 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   // which (batch row, channel group) and, for a split sequence, which chunk.
   // Consecutive logical blocks share an XCD (its L2 serves the cache lines
   // that neighbouring channel groups share). A split sequence takes its chunk
-  // from a ticket (see SplitHeader): a chunk's predecessor holds an earlier
-  // ticket, so it has started and its state will be published.
+  // from a per-XCD ticket queue (see SplitHeader): a chunk's predecessor holds
+  // an earlier ticket of the same queue, so it has started and its state will
+  // be published.
   int64_t bg, kchunk = 0, t0 = 0, Lk = L;
   if constexpr (SPLIT) {
-    __shared__ int s_ticket;
-    if (tid == 0) s_ticket = static_cast<int>(__hip_atomic_fetch_add(&p.hdr->ticket, 1u, __ATOMIC_RELAXED,
-                                                                     __HIP_MEMORY_SCOPE_AGENT));
+    __shared__ int s_chunk[2];
+    if (tid == 0) {
+      int64_t k = 0, g = 0;
+      if (split_take_chunk(p.hdr->ticket, p.nblocks / p.nchunks, p.nchunks, &k, &g)) {
+        s_chunk[0] = static_cast<int>(k);
+        s_chunk[1] = static_cast<int>(g);
+      } else {
+        s_chunk[0] = -1;
+        __hip_atomic_fetch_or(&p.hdr->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     __syncthreads();
-    const int nbg = p.nblocks / p.nchunks;
-    split_chunk_of_ticket(s_ticket, nbg, &kchunk, &bg);
+    if (s_chunk[0] < 0) return;  // (uniform; cannot happen: as many workgroups as chunks)
+    kchunk = s_chunk[0];
+    bg = s_chunk[1];
     t0 = kchunk * p.chunk_len;
     Lk = L - t0 < p.chunk_len ? L - t0 : p.chunk_len;
   } else {

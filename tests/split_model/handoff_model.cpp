@@ -10,10 +10,15 @@
 // flag loads and stores, an acquire fence after the wait, a release fence
 // before the flag), random delays at every step, and fewer workers than
 // chunks (a workgroup only takes new work once it has finished its chunk).
+// The chunks are dealt out as the kernel deals them: 8 ticket queues (one
+// per XCD), queue q holding the groups [q nbg / 8, (q + 1) nbg / 8) chunk-
+// major; a worker takes from the queue of "its" XCD, else from the next ones.
 //
 //   handoff_model <order> <nbg> <nchunks> <workers> <seed> <spin_limit> <lost>
-//     order: "ticket"  chunks taken from an atomic counter, chunk-major (the
-//                      kernel's protocol)
+//     order: "ticket"  the queues, worker w on XCD w mod 8 (the kernel's
+//                      protocol)
+//            "skew"    the queues, every worker on XCD 0 (an uneven dispatch:
+//                      the other queues are only reached by the fallback)
 //            "static"  worker w takes blocks w, w + workers, ... in the
 //                      XCD-interleaved block order (a fixed assignment; its
 //                      predecessor may belong to a worker that is itself
@@ -21,7 +26,8 @@
 //     lost:  a chunk index (>= 0) whose workers never hand their state on
 //            (a lost workgroup), or -1
 //
-// Checks, per channel group: every inclusive state equals the sequential
+// Checks: every chunk is taken exactly once; per channel group, every
+// inclusive state equals the sequential
 // composition bit for bit (same operations in the same order), or is NaN
 // exactly for the chunks after a give-up; a give-up sets the error word.
 // Prints one line "ok ..." and exits 0, or prints the failure and exits 1.
@@ -45,16 +51,19 @@ struct Shared {
   int nbg = 0, nchunks = 0;
   unsigned spin_limit = 0;
   int lost = -1;
-  std::atomic<unsigned> ticket{0};
+  std::atomic<unsigned> ticket[8];
+  std::vector<std::atomic<int>> taken;  // times each chunk was taken
   std::atomic<unsigned> err{0};
   std::vector<std::atomic<int>> flag;
   std::vector<float> state;     // [slot][kStates], the hand-off buffer
   std::vector<float> A, H;      // chunk aggregates [slot][kStates]
   std::vector<float> incl;      // every chunk's inclusive state (checked afterwards)
   std::atomic<long> waits{0}, gave_up{0};
-  explicit Shared(int nslots) : flag(nslots), state(nslots * kStates), A(nslots * kStates), H(nslots * kStates),
-                                incl(nslots * kStates) {
+  explicit Shared(int nslots) : taken(nslots), flag(nslots), state(nslots * kStates), A(nslots * kStates),
+                                H(nslots * kStates), incl(nslots * kStates) {
     for (auto& f : flag) f.store(0, std::memory_order_relaxed);
+    for (auto& t : taken) t.store(0, std::memory_order_relaxed);
+    for (auto& t : ticket) t.store(0u, std::memory_order_relaxed);
   }
 };
 
@@ -68,17 +77,29 @@ void jitter(std::mt19937& rng) {
   std::this_thread::sleep_for(std::chrono::microseconds(rng() % 200));
 }
 
-// ticket -> (chunk, group): chunk-major, groups XCD-interleaved
-void chunk_of_ticket(int tk, int nbg, int* k, int* bg) {
-  *k = tk / nbg;
-  const int u = tk % nbg;
-  *bg = (nbg % 8 == 0) ? (u & 7) * (nbg >> 3) + (u >> 3) : u;
+int queue_start(int q, int nbg) { return q * nbg / 8; }
+
+// a chunk from the queue of XCD xcc, else from the following queues
+bool take_chunk(Shared& s, int xcc, int* k, int* bg) {
+  for (int d = 0; d < 8; ++d) {
+    const int q = (xcc + d) % 8;
+    const int g0 = queue_start(q, s.nbg), ng = queue_start(q + 1, s.nbg) - g0;
+    if (ng == 0) continue;
+    const unsigned j = s.ticket[q].fetch_add(1u, std::memory_order_relaxed);
+    if (j < static_cast<unsigned>(ng * s.nchunks)) {
+      *k = static_cast<int>(j) / ng;
+      *bg = g0 + static_cast<int>(j) % ng;
+      return true;
+    }
+  }
+  return false;
 }
 
 // one chunk: main pass (a delay), then the hand-off
 void run_chunk(Shared& s, int k, int bg, std::mt19937& rng) {
   jitter(rng);  // the chunk's main pass
   const int slot = bg * s.nchunks + k;
+  s.taken[slot].fetch_add(1, std::memory_order_relaxed);
   float hin[kStates];
   for (int j = 0; j < kStates; ++j) hin[j] = 0.f;
   if (k > 0) {
@@ -127,7 +148,8 @@ int main(int argc, char** argv) {
   const unsigned seed = static_cast<unsigned>(std::strtoul(argv[5], nullptr, 10));
   const unsigned spin = static_cast<unsigned>(std::strtoul(argv[6], nullptr, 10));
   const int lost = std::atoi(argv[7]);
-  if (nbg <= 0 || nchunks <= 0 || workers <= 0 || (order != "ticket" && order != "static")) return 2;
+  if (nbg <= 0 || nchunks <= 0 || workers <= 0 || (order != "ticket" && order != "skew" && order != "static"))
+    return 2;
   const int nslots = nbg * nchunks;
   Shared s(nslots);
   s.nbg = nbg;
@@ -142,14 +164,10 @@ int main(int argc, char** argv) {
   for (int w = 0; w < workers; ++w) {
     th.emplace_back([&, w] {
       std::mt19937 r(seed * 7919u + static_cast<unsigned>(w));
-      if (order == "ticket") {
-        for (;;) {
-          const unsigned t = s.ticket.fetch_add(1u, std::memory_order_relaxed);
-          if (t >= static_cast<unsigned>(nslots)) break;
-          int k, bg;
-          chunk_of_ticket(static_cast<int>(t), nbg, &k, &bg);
-          run_chunk(s, k, bg, r);
-        }
+      if (order != "static") {
+        const int xcc = order == "skew" ? 0 : w % 8;
+        int k, bg;
+        while (take_chunk(s, xcc, &k, &bg)) run_chunk(s, k, bg, r);
       } else {
         // fixed blocks, XCD-interleaved over all blocks, chunk-major after the remap
         for (int blk = w; blk < nslots; blk += workers) {
@@ -163,6 +181,11 @@ int main(int argc, char** argv) {
 
   // reference: the sequential composition, and which chunks must be NaN
   long mismatches = 0, nan_chunks = 0;
+  for (int i = 0; i < nslots; ++i)
+    if (s.taken[i].load() != 1) {
+      std::printf("FAIL chunk %d taken %d times\n", i, s.taken[i].load());
+      return 1;
+    }
   for (int bg = 0; bg < nbg; ++bg) {
     float ref[kStates];
     bool poisoned = false;

@@ -2,8 +2,10 @@
 for the one place where workgroups communicate).
 
 tests/split_model/handoff_model.cpp re-implements the protocol with
-std::thread workers in place of workgroups: chunk tickets from an atomic
-counter (chunk-major), a relaxed flag load with an acquire fence after the
+std::thread workers in place of workgroups: chunk tickets from 8 per-XCD
+queues (each chunk-major over a contiguous range of channel groups; a worker
+takes from its own XCD's queue, else from the next ones), a relaxed flag
+load with an acquire fence after the
 wait, a release fence before the flag store, the bounded wait that sets the
 error word and poisons the chunk with NaN when it gives up, random delays at
 every step, and fewer workers than chunks (a workgroup takes new work only
@@ -34,13 +36,16 @@ def run(model, order, nbg, nchunks, workers, seed, spin, lost=-1):
     return {k: (int(v) if v.lstrip("-").isdigit() else v) for k, v in fields.items()}
 
 
-# Ticket order: every wait ends, with any number of workers (down to one,
-# i.e. no two chunks ever resident together), under random delays.
+# Ticket order: every chunk is taken once and every wait ends, with any
+# number of workers (down to one, i.e. no two chunks ever resident together),
+# under random delays, and also when every worker reports the same XCD (the
+# other queues are then reached only by the fallback).
+@pytest.mark.parametrize("order", ["ticket", "skew"])
 @pytest.mark.parametrize("workers", [1, 2, 5, 16, 64])
-@pytest.mark.parametrize("nbg,nchunks", [(16, 6), (8, 24), (3, 7), (128, 6)])
-def test_ticket_order_never_gives_up(model, workers, nbg, nchunks):
+@pytest.mark.parametrize("nbg,nchunks", [(16, 6), (8, 24), (3, 7), (128, 6), (20, 5)])
+def test_ticket_order_never_gives_up(model, order, workers, nbg, nchunks):
     for seed in range(3):
-        r = run(model, "ticket", nbg, nchunks, workers, seed, 10 ** 9)
+        r = run(model, order, nbg, nchunks, workers, seed, 10 ** 9)
         assert r["gave_up"] == 0 and r["err"] == 0 and r["nan_chunks"] == 0
         assert r["waits"] == nbg * (nchunks - 1)
 
