@@ -19,53 +19,51 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 # ---------------------------------------------------------------------------
-# The pages' parallel scan, written from its description: an up-sweep that, at
-# each of log2(L) levels, views the live elements as pairs and folds the first
-# of each pair into the second, keeping the second elements; then a down-sweep
-# over levels k = log2(L)-1 .. 0 on the elements X[2^k-1 :: 2^k], which, for
-# every pair but the first, folds the previous pair's second element into the
-# pair's first element ("scan output is different between sequential and
-# parallel versions", the reduction code of the issue and the author's reply).
+# A parallel (tree) scan written from the definition of an inclusive scan with
+# an associative operator: combine neighbouring elements in pairs, scan the
+# half-length sequence of pair results recursively, then each odd position
+# takes its pair's scanned value and each even position (but the first)
+# combines the previous pair's scanned value with its own element. This is
+# the pairwise reduction followed by the fill-in that the page "scan output is
+# different between sequential and parallel versions" describes (its issue
+# text and the author's reply), organised as a recursion; its worked example
+# pins the 1-D (additive) case below. Power-of-two lengths only, as there.
 # ---------------------------------------------------------------------------
+def tree_scan(xs, combine):
+    """Inclusive scan of the list xs under an associative combine(earlier, later)."""
+    n = len(xs)
+    if n == 1:
+        return list(xs)
+    assert n % 2 == 0, "power-of-two lengths only"
+    pairs = [combine(xs[2 * i], xs[2 * i + 1]) for i in range(n // 2)]
+    scanned = tree_scan(pairs, combine)
+    out = [None] * n
+    out[0] = xs[0]
+    for i in range(n // 2):
+        out[2 * i + 1] = scanned[i]
+        if i > 0:
+            out[2 * i] = combine(scanned[i - 1], xs[2 * i])
+    return out
+
+
 def sweep_1d(values):
-    X = np.array(values, dtype=np.int64)
-    L = X.shape[0]
-    levels = int(np.log2(L))
-    assert 2 ** levels == L
-    Xa = X
-    for _ in range(levels):
-        Xa = Xa.reshape(-1, 2)
-        Xa[:, 1] += Xa[:, 0]
-        Xa = Xa[:, 1]
-    for k in range(levels - 1, -1, -1):
-        Xa = X[2 ** k - 1:L:2 ** k].reshape(-1, 2)
-        Xa[1:, 0] += Xa[:-1, 1]
-    return X
+    """The tree scan with addition: exact on integers."""
+    return np.array(tree_scan([int(v) for v in values], lambda u, v: u + v), dtype=np.int64)
 
 
 def sweep_pairs(a, b):
-    """Same sweep for the pair operator (a1,b1) then (a2,b2) -> (a1 a2, a2 b1 + b2).
+    """The tree scan of the pair operator (a1, b1) then (a2, b2) -> (a1 a2,
+    a2 b1 + b2): each pair is the affine map h -> a h + b, and the scan of
+    the maps gives h_t with h_{-1} = 0.
 
-    a, b: arrays with time on axis 0 (power-of-two length). Returns the
-    inclusive scan of b, i.e. h_t with h_{-1} = 0.
+    a, b: arrays with time on axis 0 (power-of-two length). Returns h (the
+    b part of the inclusive scan), in a's and b's dtype.
     """
-    A = np.array(a, dtype=np.float64, copy=True)
-    X = np.array(b, dtype=np.float64, copy=True)
-    L = X.shape[0]
-    levels = int(np.log2(L))
-    assert 2 ** levels == L
-    Aa, Xa = A, X
-    for _ in range(levels):
-        Aa = Aa.reshape((-1, 2) + Aa.shape[1:])
-        Xa = Xa.reshape((-1, 2) + Xa.shape[1:])
-        Xa[:, 1] = Aa[:, 1] * Xa[:, 0] + Xa[:, 1]
-        Aa[:, 1] = Aa[:, 1] * Aa[:, 0]
-        Aa, Xa = Aa[:, 1], Xa[:, 1]
-    for k in range(levels - 1, -1, -1):
-        Aa = A[2 ** k - 1:L:2 ** k].reshape((-1, 2) + A.shape[1:])
-        Xa = X[2 ** k - 1:L:2 ** k].reshape((-1, 2) + X.shape[1:])
-        Xa[1:, 0] = Aa[1:, 0] * Xa[:-1, 1] + Xa[1:, 0]
-    return X
+    a = np.asarray(a)
+    b = np.asarray(b)
+    combine = lambda e1, e2: (e1[0] * e2[0], e2[0] * e1[1] + e2[1])
+    scanned = tree_scan([(a[t], b[t]) for t in range(a.shape[0])], combine)
+    return np.stack([s[1] for s in scanned]).astype(np.result_type(a, b), copy=False)
 
 
 def discretise(x, delta, A, B):
