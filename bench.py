@@ -34,26 +34,28 @@ METRIC = "scan elements (Bs·L·ED·N)/s and achieved HBM GB/s vs MI355X peak"
 
 # MI355X published figures
 HBM_PEAK_GBPS = 8000.0
-CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
-# fp32 VALU issue slots per second (one non-packed lane-op per lane per clock)
-VALU_SLOTS_PER_S = CUS * SIMDS * LANES * CLOCK_GHZ * 1e9
-# issue slots one v_exp_f32 takes, in float32 FMA slots: the ratio of the two
-# issue rates that `bench.py --micro valu` measures (FMA 34.2 T, exp 17.9 T
-# lane-ops/s on the MI355X: 1.91; rounded to 2)
-EXP_SLOTS = 2.0
+CUS, SIMDS, CLOCK_GHZ = 256, 4, 2.4
+# float32 vector peak in FMA lane-ops per second: the published 157.3 TFLOP/s
+# counted as two flops per FMA, i.e. 32 FMA lanes per SIMD per clock
+# (256 CUs x 4 SIMDs x 32 x 2.4 GHz). `bench.py --micro valu` measures 65 T
+# non-packed FMA lane-ops/s with two or more waves per SIMD, 29 T with one.
+VALU_SLOTS_PER_S = CUS * SIMDS * 32 * CLOCK_GHZ * 1e9
+# FMA slots one v_exp_f32 costs: that peak over the measured exp rate
+# (19.3 T lane-ops/s at any occupancy): 4.07, rounded to 4
+EXP_SLOTS = 4.0
 # algorithmic VALU cost of one scan element: delta*A, (delta x)*B, the state
 # FMA, the C FMA (4 full-rate slots) + one v_exp_f32
 SLOTS_PER_ELEMENT = 4.0 + EXP_SLOTS
 # bidirectional: the exp and the two multiplies are shared by both
 # directions; 2 mul + exp + 2 x (state FMA + C FMA)
 SLOTS_PER_ELEMENT_BIDIR = 6.0 + EXP_SLOTS
-# backward: rebuild the state (delta*A, exp, (delta x)*B, state FMA: 5) and
-# the adjoint with its terms (g FMA, k = a g, dC and dB products, sum g B,
+# backward: rebuild the state (delta*A, (delta x)*B, state FMA: 3, + the exp)
+# and the adjoint with its terms (g FMA, k = a g, dC and dB products, sum g B,
 # q = g a h_{t-1} (2), sum A q, dA += delta q: 9)
-SLOTS_PER_ELEMENT_BWD = 14.0
-# bidirectional backward: both directions' 14, less the discretisation they
-# share (delta*A, exp, (delta x)*B: 4)
-SLOTS_PER_ELEMENT_BIDIR_BWD = 24.0
+SLOTS_PER_ELEMENT_BWD = 12.0 + EXP_SLOTS
+# bidirectional backward: both directions' 12, less the discretisation they
+# share (delta*A, (delta x)*B: 2), and one exp
+SLOTS_PER_ELEMENT_BIDIR_BWD = 22.0 + EXP_SLOTS
 
 
 def alg_bytes(w):
@@ -148,7 +150,7 @@ def cpu_baseline(inp, w, budget_s=20.0):
     # when the whole workload takes well under the budget, it is run several
     # times (at least min_s of CPU work in all) so that the rate is not one
     # short, noisy measurement
-    min_s = min(5.0, budget_s)
+    min_s = min(10.0, budget_s)
     reps, dt = 0, 0.0
     while reps == 0 or (chans is None and dt < min_s):
         t0 = time.perf_counter()
@@ -386,6 +388,7 @@ def micro_valu(args):
         "fma_lane_ops_per_s": fma,
         "exp_lane_ops_per_s": ex,
         "fma_frac_of_157_3_tflops": 2 * fma / 157.3e12,
+        "exp_slots_of_peak": VALU_SLOTS_PER_S / ex,
         "exp_slots_alone": fma / ex,
         "exp_slots_mixed_with_4_fma": fma / mixed - 4.0,
     }))
@@ -584,7 +587,7 @@ def main():
             "frac": achieved_slots / VALU_SLOTS_PER_S,
             "slots_per_element": slots,
             "exp_slots": EXP_SLOTS,
-            "peak_from": "256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, non-packed float32",
+            "peak_from": "published float32 vector 157.3 TFLOP/s = 78.6 T FMA lane-ops/s (256 CUs x 4 SIMDs x 32 x 2.4 GHz)",
         },
         "kernel_source_sha256_16": src_hash,
         "parity": parity,
