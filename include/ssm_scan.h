@@ -123,7 +123,10 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
  * resident, and other work may share the device). A hand-off wait is
  * bounded (about seven seconds); if it ever gives up, the chunk's outputs,
  * every later chunk's and h_last become NaN, and ssm_scan_fwd_status()
- * reports SSM_ERR_HANDOFF.
+ * reports SSM_ERR_HANDOFF. A later chunk adds the decayed entering state's
+ * contribution to the start of its outputs until every decay product
+ * prod a[n] is below 2^-40 (or the entering state is zero); the terms left
+ * out are below 2^-40 sum_n |C_t[n] h_in[n]|, under one float32 rounding.
  *   x, delta : (Bs, L, ED) of dtype        -- input sequence and step sizes
  *   A        : (ED, N) float32             -- state matrix (diagonal per channel)
  *   B, C     : (Bs, L, N) of dtype         -- input and output projections

@@ -169,6 +169,10 @@ struct alignas(16) FoldArea {
 
 enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
 
+// The split sequence's correction pass drops a carried term once its decay
+// product is below 2^-kCorrectionCut.
+constexpr float kCorrectionCut = 40.f;
+
 // delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max), with the
 // channel's bias (0 without one) already in a register
 template <typename T>
@@ -711,10 +715,14 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 
     // ---- correction: y_t += sum_n C_t[n] (prod_{s <= t} a_s[n]) h_in[n] ----
     // over the chunk from its start, with prod a = exp2(A log2e * cumulative
-    // delta) (float64 running sum). Once every carried product is exactly zero
-    // it stays zero if delta >= 0 and A <= 0 (checked as we go), and the pass
-    // stops there: the remaining terms are exact zeros.
+    // delta) (float64 running sum). With delta >= 0 and A <= 0 (checked as we
+    // go) the products only decay; once every one is below 2^-kCorrectionCut
+    // (or its h_in is zero) the pass stops. The terms it leaves out add at most
+    // 2^-kCorrectionCut sum_n |C_t[n] h_in[n]| to any y_t, far below one
+    // float32 rounding of that sum. A poisoned (NaN) h_in is carried to the
+    // chunk's end.
     bool mono = A2[0] <= 0.f && A2[1] <= 0.f && A2[2] <= 0.f && A2[3] <= 0.f;
+    const bool poisoned = hin[0] != hin[0] || hin[1] != hin[1] || hin[2] != hin[2] || hin[3] != hin[3];
     double base = 0.0;  // cumulative delta before the current round
     st.begin(b, L, t0, Lk, false, false);
     st.template prefetch<STAGE_CORRECT>(p, 0);
@@ -738,8 +746,11 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
         const float cum = static_cast<float>(base + static_cast<double>(pre));
         float w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_exp2f(A2[j] * cum) * hin[j];
-        alive = alive || w[0] != 0.f || w[1] != 0.f || w[2] != 0.f || w[3] != 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const float e2 = A2[j] * cum;
+          w[j] = __builtin_amdgcn_exp2f(e2) * hin[j];
+          alive = alive || (e2 > -kCorrectionCut && hin[j] != 0.f);
+        }
         const float cq = cur.cq[row][q];
         const float yp = dot_quad(cq, w);
         out.yq[g][row][ch] = yp;
@@ -748,7 +759,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       for (int i = (wave + 1) * TS; i < RT; ++i) rest += cur.dt[i][ch];
       base += static_cast<double>(pre + rest);
       if (r + 1 < rounds) st.template commit<STAGE_CORRECT>(p, nxt);
-      const int go_on = __syncthreads_or((alive || !mono) ? 1 : 0);
+      const int go_on = __syncthreads_or((alive || !mono || poisoned) ? 1 : 0);
       if (!go_on) {
         st.template store_out<STAGE_CORRECT>(p, r, cur, out);
         return;
