@@ -159,12 +159,12 @@ struct alignas(16) OutTile {
 };
 
 // Segment aggregates and the carry between rounds.
-template <int SEG>
+template <int SEG, bool SPLIT>
 struct alignas(16) FoldArea {
   float4 A[SEG][64];    // prod of a over the segment, per lane's 4 states
   float4 H[SEG][64];    // state at the segment's end, started from zero
   float4 carry[2][64];  // state after the round, by round parity
-  double sd[SEG][64];   // split sequence: sum of delta over each wave's segments
+  double sd[SPLIT ? SEG : 1][64];  // split sequence: sum of delta over each wave's segments
 };
 
 enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   __shared__ Tile<RT, GATE> tile[2];
   __shared__ OutTile<RT> out;
-  __shared__ FoldArea<SEG> fa;
+  __shared__ FoldArea<SEG, SPLIT> fa;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -910,14 +910,32 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
   return SSM_OK;
 }
 
+// LDS of one workgroup of the forward kernel
+template <bool GATE, bool SPLIT>
+constexpr size_t scan_lds_bytes() {
+  return sizeof(Tile<kRT, GATE>) * 2 + sizeof(OutTile<kRT>) + sizeof(FoldArea<kSEG, SPLIT>) + 16;
+}
+
+// A launch with more workgroups than 3 per compute unit (which is what the
+// gated, bidirectional and split kernels hold) runs the plain kernel built
+// for 4 per compute unit (at most 128 VGPRs, under 40 KB of LDS): the last
+// workgroups then start sooner (bf16 4x8192x5120: 861 -> 813 us).
 template <typename T, bool BIDIR, bool VEC, bool SPLIT>
-void launch_one(const ScanArgs<T>& a, int64_t nblk, size_t dyn, hipStream_t stream) {
+void launch_one(const ScanArgs<T>& a, int64_t nblk, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(nblk)), block(64 * kSEG);
+  const int ncu = device_cus();
+  if constexpr (!BIDIR && !SPLIT) {
+    if (!a.z && ncu > 0 && nblk > 3 * static_cast<int64_t>(ncu)) {
+      const size_t dyn = spread_lds(nblk, scan_lds_bytes<false, false>(), 4);
+      hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, false, VEC, false, false, 4>), grid, block, dyn, stream, a);
+      return;
+    }
+  }
+  const size_t dyn = spread_lds(nblk, scan_lds_bytes<true, SPLIT>(), 3);
   if (a.z)
-    hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT, true>), dim3(nblk), dim3(64 * kSEG), dyn,
-                       stream, a);
+    hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT, true>), grid, block, dyn, stream, a);
   else
-    hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT, false>), dim3(nblk), dim3(64 * kSEG), dyn,
-                       stream, a);
+    hipLaunchKernelGGL((scan_chunked_kernel<T, kSEG, kTS, BIDIR, VEC, SPLIT, false>), grid, block, dyn, stream, a);
 }
 
 template <typename T>
@@ -969,18 +987,16 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
     hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(std::min<int64_t>((words + 255) / 256, 1024))),
                        dim3(256), 0, stream, reinterpret_cast<unsigned*>(w), words);
   }
-  const size_t lds = sizeof(Tile<kRT, true>) * 2 + sizeof(OutTile<kRT>) + sizeof(FoldArea<kSEG>) + 16;
-  const size_t dyn = spread_lds(nblk, lds, 16 / kSEG);
   const bool vec = (ED % 4) == 0;
   if (bidir) {
-    if (vec) launch_one<T, true, true, false>(a, nblk, dyn, stream);
-    else launch_one<T, true, false, false>(a, nblk, dyn, stream);
+    if (vec) launch_one<T, true, true, false>(a, nblk, stream);
+    else launch_one<T, true, false, false>(a, nblk, stream);
   } else if (split) {
-    if (vec) launch_one<T, false, true, true>(a, nblk, dyn, stream);
-    else launch_one<T, false, false, true>(a, nblk, dyn, stream);
+    if (vec) launch_one<T, false, true, true>(a, nblk, stream);
+    else launch_one<T, false, false, true>(a, nblk, stream);
   } else {
-    if (vec) launch_one<T, false, true, false>(a, nblk, dyn, stream);
-    else launch_one<T, false, false, false>(a, nblk, dyn, stream);
+    if (vec) launch_one<T, false, true, false>(a, nblk, stream);
+    else launch_one<T, false, false, false>(a, nblk, stream);
   }
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }

@@ -90,6 +90,14 @@ def test_without_D():
     check_full(2, 100, 64, D_none=True, bidir=True, seed=9)
 
 
+@pytest.mark.parametrize("Bs,L,ED,dtype", [(2, 300, 8192, "f32"), (2, 301, 6150, "f32"), (3, 257, 5120, "bf16")])
+def test_more_workgroups_than_three_per_cu(Bs, L, ED, dtype):
+    # more than 768 (batch row, channel group) pairs: the launch takes the
+    # kernel built for four workgroups per compute unit (vectorised and, with
+    # ED not a multiple of 4, element-wise staging)
+    check_full(Bs, L, ED, dtype=dtype, seed=ED + L)
+
+
 def test_repeatable_bitwise():
     inp = synth.make_inputs(2, 777, 192, 16, "f32", seed=10)
     y1, h1, _ = run_gpu(inp, want_h=True)
