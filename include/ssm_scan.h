@@ -185,6 +185,14 @@ int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t B
  *             next piece's g_first.
  *   h_last  : (Bs, ED, N) float32 or NULL -- forward state after t = L-1
  *   g_first : (Bs, ED, N) float32 or NULL -- reverse state after t = 0
+ * Long sequences with little channel parallelism are split into chunks here
+ * too: every chunk runs both directions from its own entering states (zero
+ * inside the sequence), and a second kernel folds the chunks' aggregates
+ * into the states entering each chunk from either side, then corrects both
+ * ends of its output the way ssm_scan_fwd corrects a chunk's start (terms
+ * below 2^-40 of the carried state are left out). Nothing waits on another
+ * workgroup; the workspace (ssm_scan_workspace_bytes(..., bidir = 1)) holds
+ * the aggregates, after the bf16 scan's float32 partials.
  */
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                        const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, void* y,

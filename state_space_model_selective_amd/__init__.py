@@ -71,12 +71,22 @@ def build(verbose=False):
     _probe = None
 
 
+def _load_torch_runtime():
+    """Import torch before the library is loaded: the library's HIP runtime
+    dependency then binds to the runtime torch has loaded, so that one runtime
+    serves torch's memory and streams and the library's launches (loaded
+    first, the system runtime would take that name and torch's own would
+    fail to find a device)."""
+    import torch  # noqa: F401
+
+
 def lib():
     """The loaded C library; raises if it has not been built."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libssm_scan.so is not built (run __graft_entry__.build())")
+        _load_torch_runtime()
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
         L.ssm_scan_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ci]
@@ -115,6 +125,7 @@ def probe_lib():
     if _probe is None:
         if not os.path.exists(PROBE_LIB_PATH):
             raise RuntimeError("libssm_valu_probe.so is not built (run __graft_entry__.build())")
+        _load_torch_runtime()
         P = ctypes.CDLL(PROBE_LIB_PATH)
         P.ssm_probe_valu_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                             ctypes.c_void_p]

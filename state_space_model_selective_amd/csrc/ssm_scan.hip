@@ -138,6 +138,10 @@ struct ScanArgs {
   SplitHeader* hdr;
   int* flag;            // [bg * nchunks + k]
   float* state;         // [bg * nchunks + k][16 channels][16 states]
+  // bidirectional split: per chunk, the sum of delta per channel and the
+  // reverse sweep's start state (state: the forward sweep's end state)
+  double* sdsum;        // [bg * nchunks + k][16 channels]
+  float* gstate;        // [bg * nchunks + k][16 channels][16 states]
 };
 
 // Input tile of one round (double-buffered).
@@ -447,6 +451,71 @@ __device__ __forceinline__ bool split_take_chunk(unsigned* tickets, int nbg, int
   return false;
 }
 
+// ---- correction of a chunk's outputs for the state entering it ----------
+// Forward (rev = false): y_t += sum_n C_t[n] (prod_{s = t0 .. t} a_s[n]) h_in[n]
+// from the chunk's first step on; reverse (rev = true): the same with the
+// product over s = t .. t_end and the state entering at the chunk's last
+// step, from that step backwards. The product is exp2(A log2e * cumulative
+// delta) (a float64 running sum). With delta >= 0 and A <= 0 (checked as we
+// go) the products only decay; once every one is below 2^-kCorrectionCut (or
+// its h_in is zero) the pass stops. The terms it leaves out add at most
+// 2^-kCorrectionCut sum_n |C_t[n] h_in[n]| to any y_t, far below one float32
+// rounding of that sum. A poisoned (NaN) h_in is carried to the chunk's end.
+// The output gate, if any, multiplies the correction.
+template <typename T, int SEG, int TS, bool VEC, bool GATE, int TPT>
+__device__ void correct_pass(const ScanArgs<T>& p, Stager<T, SEG * TS, TPT, false, VEC, GATE>& st,
+                             Tile<SEG * TS, GATE> (&tile)[2], OutTile<SEG * TS>& out, int64_t b, int64_t t0,
+                             int64_t Lk, bool rev, const float (&hin)[4], const float (&A2)[4], int wave, int ch,
+                             int q, int g) {
+  constexpr int RT = SEG * TS;
+  const int64_t rounds = (Lk + RT - 1) / RT;
+  bool mono = A2[0] <= 0.f && A2[1] <= 0.f && A2[2] <= 0.f && A2[3] <= 0.f;
+  const bool poisoned = hin[0] != hin[0] || hin[1] != hin[1] || hin[2] != hin[2] || hin[3] != hin[3];
+  double base = 0.0;  // cumulative delta before the current round
+  st.begin(b, p.L, t0, Lk, rev, false);
+  st.template prefetch<STAGE_CORRECT>(p, 0);
+  st.template commit<STAGE_CORRECT>(p, tile[0]);
+  __syncthreads();
+  for (int64_t r = 0; r < rounds; ++r) {
+    Tile<RT, GATE>& cur = tile[r & 1];
+    Tile<RT, GATE>& nxt = tile[(r + 1) & 1];
+    if (r + 1 < rounds) st.template prefetch<STAGE_CORRECT>(p, r + 1);
+    if (r >= 1) st.template store_out<STAGE_CORRECT>(p, r - 1, nxt, out);
+    __syncthreads();  // the output tile is reused below
+    float pre = 0.f;  // delta of the round's rows before this wave's segment
+    for (int i = 0; i < wave * TS; ++i) pre += cur.dt[i][ch];
+    bool alive = false;
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+      const int row = wave * TS + i;
+      const float dt = cur.dt[row][ch];
+      mono = mono && dt >= 0.f;
+      pre += dt;
+      const float cum = static_cast<float>(base + static_cast<double>(pre));
+      float w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e2 = A2[j] * cum;
+        w[j] = __builtin_amdgcn_exp2f(e2) * hin[j];
+        alive = alive || (e2 > -kCorrectionCut && hin[j] != 0.f);
+      }
+      const float cq = cur.cq[row][q];
+      const float yp = dot_quad(cq, w);
+      out.yq[g][row][ch] = yp;
+    }
+    float rest = 0.f;  // rows after this wave's segment
+    for (int i = (wave + 1) * TS; i < RT; ++i) rest += cur.dt[i][ch];
+    base += static_cast<double>(pre + rest);
+    if (r + 1 < rounds) st.template commit<STAGE_CORRECT>(p, nxt);
+    const int go_on = __syncthreads_or((alive || !mono || poisoned) ? 1 : 0);
+    if (!go_on) {
+      st.template store_out<STAGE_CORRECT>(p, r, cur, out);
+      return;
+    }
+  }
+  st.template store_out<STAGE_CORRECT>(p, rounds - 1, tile[(rounds - 1) & 1], out);
+}
+
 template <typename T, int SEG, int TS, bool BIDIR, bool VEC, bool SPLIT, bool GATE, int WPE = 3>
 __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE))) void scan_chunked_kernel(
     const ScanArgs<T> p) {
@@ -455,7 +524,6 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   constexpr int TPT = (8 * RT) / NT;  // staging tasks per thread
   static_assert(TS % 8 == 0, "TS must be a multiple of 8");
   static_assert(TPT * NT == 8 * RT, "staging tasks must divide evenly");
-  static_assert(!(SPLIT && BIDIR), "the split-sequence scan is forward only");
   static_assert(!SPLIT || SEG > 1, "the split-sequence scan needs several segments");
 
   __shared__ Tile<RT, GATE> tile[2];
@@ -477,7 +545,17 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
   // an earlier ticket of the same queue, so it has started and its state will
   // be published.
   int64_t bg, kchunk = 0, t0 = 0, Lk = L;
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT && BIDIR) {
+    // the bidirectional split waits for nothing (a second kernel joins the
+    // chunks), so its chunks follow the block index, chunk-major
+    int64_t blk = blockIdx.x;
+    if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
+    const int64_t nbg = p.nblocks / p.nchunks;
+    kchunk = blk / nbg;
+    bg = blk % nbg;
+    t0 = kchunk * p.chunk_len;
+    Lk = L - t0 < p.chunk_len ? L - t0 : p.chunk_len;
+  } else if constexpr (SPLIT) {
     __shared__ int s_chunk[2];
     if (tid == 0) {
       int64_t k = 0, g = 0;
@@ -514,17 +592,20 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   Stager<T, RT, TPT, BIDIR, VEC, GATE> st;
   st.init(p, tid, e0);
-  double sd_total = 0.0;  // split sequence: sum of delta over this wave's segments
+  double sd_total = 0.0;  // split sequence: sum of delta over this wave's segments (of the last sweep)
   float carry[4];         // state after the last completed round (valid in wave SEG-1 after the sweep)
+  float gloc[4] = {0.f, 0.f, 0.f, 0.f};  // bidirectional split: the reverse sweep's end state
 
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
     const bool rev = BIDIR && sweep == 0;
     st.begin(b, L, t0, Lk, rev, BIDIR && sweep == 1);
+    sd_total = 0.0;
     // entering state: h0 for the forward sweep's first chunk, g0 for the
-    // reverse sweep, else zero
+    // reverse sweep's first (the sequence's last) chunk, else zero
     float4 init = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.h0 && !rev && kchunk == 0 && ch_ok) init = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
-    if (BIDIR && p.g0 && rev && ch_ok) init = *reinterpret_cast<const float4*>(p.g0 + (b * ED + e) * 16 + 4 * g);
+    if (BIDIR && p.g0 && rev && kchunk == p.nchunks - 1 && ch_ok)
+      init = *reinterpret_cast<const float4*>(p.g0 + (b * ED + e) * 16 + 4 * g);
     carry[0] = init.x, carry[1] = init.y, carry[2] = init.z, carry[3] = init.w;
     if (SEG > 1 && wave == SEG - 1) fa.carry[1][lane] = init;
 
@@ -666,11 +747,35 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       if (h_out && wave == SEG - 1 && ch_ok)
         *reinterpret_cast<float4*>(h_out + (b * ED + e) * 16 + 4 * g) =
             make_float4(carry[0], carry[1], carry[2], carry[3]);
-      if (BIDIR) __syncthreads();
+    } else if (rev) {
+      gloc[0] = carry[0], gloc[1] = carry[1], gloc[2] = carry[2], gloc[3] = carry[3];
     }
+    if (BIDIR) __syncthreads();
   }
 
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT && BIDIR) {
+    // ---- publish the chunk's aggregates: sum of delta (float64), the
+    // forward end state and the reverse start state, each from this chunk's
+    // entering state (zero, or h0 / g0 at the sequence's ends) ----
+    fa.sd[wave][lane] = sd_total;
+    __syncthreads();
+    if (wave == SEG - 1) {
+      const int64_t slot = bg * p.nchunks + kchunk;
+      if (g == 0) {
+        double sum = 0.0;
+#pragma unroll
+        for (int s2 = 0; s2 < SEG; ++s2) sum += fa.sd[s2][lane];
+        p.sdsum[slot * 16 + ch] = sum;
+      }
+      *reinterpret_cast<float4*>(p.state + slot * 256 + ch * 16 + 4 * g) =
+          make_float4(carry[0], carry[1], carry[2], carry[3]);
+      *reinterpret_cast<float4*>(p.gstate + slot * 256 + ch * 16 + 4 * g) =
+          make_float4(gloc[0], gloc[1], gloc[2], gloc[3]);
+    }
+    return;
+  }
+
+  if constexpr (SPLIT && !BIDIR) {
     // ---- hand the chunk's end state to the next chunk -------------------
     // chunk aggregate: prod of a over the chunk = exp2(A log2e * sum delta),
     // the sum taken in float64 over all waves' segments
@@ -713,60 +818,79 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
       hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
     }
 
-    // ---- correction: y_t += sum_n C_t[n] (prod_{s <= t} a_s[n]) h_in[n] ----
-    // over the chunk from its start, with prod a = exp2(A log2e * cumulative
-    // delta) (float64 running sum). With delta >= 0 and A <= 0 (checked as we
-    // go) the products only decay; once every one is below 2^-kCorrectionCut
-    // (or its h_in is zero) the pass stops. The terms it leaves out add at most
-    // 2^-kCorrectionCut sum_n |C_t[n] h_in[n]| to any y_t, far below one
-    // float32 rounding of that sum. A poisoned (NaN) h_in is carried to the
-    // chunk's end.
-    bool mono = A2[0] <= 0.f && A2[1] <= 0.f && A2[2] <= 0.f && A2[3] <= 0.f;
-    const bool poisoned = hin[0] != hin[0] || hin[1] != hin[1] || hin[2] != hin[2] || hin[3] != hin[3];
-    double base = 0.0;  // cumulative delta before the current round
-    st.begin(b, L, t0, Lk, false, false);
-    st.template prefetch<STAGE_CORRECT>(p, 0);
-    st.template commit<STAGE_CORRECT>(p, tile[0]);
-    __syncthreads();
-    for (int64_t r = 0; r < rounds; ++r) {
-      Tile<RT, GATE>& cur = tile[r & 1];
-      Tile<RT, GATE>& nxt = tile[(r + 1) & 1];
-      if (r + 1 < rounds) st.template prefetch<STAGE_CORRECT>(p, r + 1);
-      if (r >= 1) st.template store_out<STAGE_CORRECT>(p, r - 1, nxt, out);
-      __syncthreads();  // the output tile is reused below
-      float pre = 0.f;  // delta of the round's rows before this wave's segment
-      for (int i = 0; i < wave * TS; ++i) pre += cur.dt[i][ch];
-      bool alive = false;
-#pragma unroll
-      for (int i = 0; i < TS; ++i) {
-        const int row = wave * TS + i;
-        const float dt = cur.dt[row][ch];
-        mono = mono && dt >= 0.f;
-        pre += dt;
-        const float cum = static_cast<float>(base + static_cast<double>(pre));
-        float w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e2 = A2[j] * cum;
-          w[j] = __builtin_amdgcn_exp2f(e2) * hin[j];
-          alive = alive || (e2 > -kCorrectionCut && hin[j] != 0.f);
-        }
-        const float cq = cur.cq[row][q];
-        const float yp = dot_quad(cq, w);
-        out.yq[g][row][ch] = yp;
-      }
-      float rest = 0.f;  // rows after this wave's segment
-      for (int i = (wave + 1) * TS; i < RT; ++i) rest += cur.dt[i][ch];
-      base += static_cast<double>(pre + rest);
-      if (r + 1 < rounds) st.template commit<STAGE_CORRECT>(p, nxt);
-      const int go_on = __syncthreads_or((alive || !mono || poisoned) ? 1 : 0);
-      if (!go_on) {
-        st.template store_out<STAGE_CORRECT>(p, r, cur, out);
-        return;
-      }
-    }
-    st.template store_out<STAGE_CORRECT>(p, rounds - 1, tile[(rounds - 1) & 1], out);
+    correct_pass<T, SEG, TS, VEC, GATE>(p, st, tile, out, b, t0, Lk, false, hin, A2, wave, ch, q, g);
   }
+}
+
+// Second kernel of the bidirectional split scan: one workgroup per (batch
+// row, channel group, chunk) folds the chunks' aggregates into the states
+// entering its chunk from either side, h_in = fold over the chunks before it
+// (from h0) and g_in = fold over the chunks after it (from g0), writes h_last
+// (last chunk) and g_first (first chunk), and corrects the chunk's outputs:
+// the forward state's contribution from its first step on, the reverse
+// state's from its last step backwards (in that order, so that a short chunk
+// whose two corrections overlap adds both).
+template <typename T, int SEG, int TS, bool VEC, bool GATE>
+__global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) void scan_bidir_join_kernel(
+    const ScanArgs<T> p) {
+  constexpr int RT = SEG * TS;
+  constexpr int NT = 64 * SEG;
+  constexpr int TPT = (8 * RT) / NT;
+  __shared__ Tile<RT, GATE> tile[2];
+  __shared__ OutTile<RT> out;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 15;
+  const int g = q >> 2;
+  const int ch = ((lane >> 4) << 2) | (q & 3);
+  const int64_t L = p.L, ED = p.ED;
+  const int64_t nbg = p.nblocks / p.nchunks;
+  const int64_t kchunk = blockIdx.x / nbg, bg = blockIdx.x % nbg;
+  const int64_t K = p.nchunks;
+  const int64_t t0 = kchunk * p.chunk_len;
+  const int64_t Lk = L - t0 < p.chunk_len ? L - t0 : p.chunk_len;
+  const int64_t b = bg / p.ngroups;
+  const int64_t e0 = (bg % p.ngroups) * 16;
+  const int64_t e = e0 + ch;
+  const bool ch_ok = e < ED;
+  const int64_t ec = ch_ok ? e : ED - 1;
+  float A2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) A2[j] = p.A[ec * 16 + 4 * g + j] * kLog2e;
+
+  // fold: state = prod(a over chunk j) * state + chunk j's own state
+  auto fold = [&](float (&v)[4], const float* states, int64_t j) {
+    const int64_t slot = bg * K + j;
+    const float sdc = static_cast<float>(p.sdsum[slot * 16 + ch]);
+    const float4 hj = *reinterpret_cast<const float4*>(states + slot * 256 + ch * 16 + 4 * g);
+    const float hv[4] = {hj.x, hj.y, hj.z, hj.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[i] * sdc), v[i], hv[i]);
+  };
+  float hin[4] = {0.f, 0.f, 0.f, 0.f}, gin[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t j = 0; j < kchunk; ++j) fold(hin, p.state, j);
+  for (int64_t j = K - 1; j > kchunk; --j) fold(gin, p.gstate, j);
+  if (wave == 0 && ch_ok) {
+    if (kchunk == K - 1 && p.h_last) {
+      float v[4] = {hin[0], hin[1], hin[2], hin[3]};
+      fold(v, p.state, kchunk);
+      *reinterpret_cast<float4*>(p.h_last + (b * ED + e) * 16 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (kchunk == 0 && p.g_first) {
+      float v[4] = {gin[0], gin[1], gin[2], gin[3]};
+      fold(v, p.gstate, kchunk);
+      *reinterpret_cast<float4*>(p.g_first + (b * ED + e) * 16 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+
+  Stager<T, RT, TPT, false, VEC, GATE> st;
+  st.init(p, tid, e0);
+  if (kchunk > 0) correct_pass<T, SEG, TS, VEC, GATE>(p, st, tile, out, b, t0, Lk, false, hin, A2, wave, ch, q, g);
+  // the forward correction's stores of y are read back by the reverse one
+  __syncthreads();
+  if (kchunk < K - 1) correct_pass<T, SEG, TS, VEC, GATE>(p, st, tile, out, b, t0, Lk, true, gin, A2, wave, ch, q, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -818,16 +942,19 @@ int split_blocks_per_cu() {
   return std::min(best, n);
 }
 
-// How the forward scan splits a sequence across workgroups: when there are
-// fewer than two (batch row, 16-channel group) pairs per compute unit, cut
-// the sequence into chunks (each at least 16 rounds long) so that about three
-// workgroups per CU are in flight, and never more than fit on the device at
-// once (a chunk waits for its predecessor, which must therefore be running).
+// How a scan splits a sequence across workgroups: when there are fewer than
+// two (batch row, 16-channel group) pairs per compute unit, cut the sequence
+// into chunks (each at least 16 rounds long) so that about three workgroups
+// per CU are in flight. The forward scan hands states from chunk to chunk
+// inside the kernel (tickets make that safe whatever is resident); the
+// bidirectional scan joins its chunks in a second kernel.
 struct SplitPlan {
   int64_t nbg;        // (batch row, channel group) pairs
   int64_t nchunks;    // 1: no split
   int64_t chunk_len;
-  size_t flag_off, state_off, bytes;  // workspace layout
+  // workspace layout. Forward: header, flags, states. Bidirectional: the
+  // delta sums, the forward end states and the reverse start states.
+  size_t flag_off, state_off, sd_off, gstate_off, bytes;
 };
 
 // Iterations of a hand-off wait before it gives up (s_sleep 4 each: about
@@ -848,7 +975,7 @@ SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
   sp.nbg = Bs * ((ED + 15) / 16);
   sp.nchunks = 1;
   sp.chunk_len = L;
-  if (!bidir && ncu > 0 && sp.nbg < 2 * static_cast<int64_t>(ncu)) {
+  if (ncu > 0 && sp.nbg < 2 * static_cast<int64_t>(ncu)) {
     const int64_t per_cu = std::min<int64_t>(3, split_blocks_per_cu());  // workgroups resident per CU
     const int64_t want = per_cu * static_cast<int64_t>(ncu) / sp.nbg;
     const int64_t k = std::min<int64_t>(want, L / (16 * kRT));
@@ -858,7 +985,13 @@ SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
       sp.nchunks = (L + len - 1) / len;
     }
   }
-  if (sp.nchunks > 1) {
+  const size_t nslot = static_cast<size_t>(sp.nbg * sp.nchunks);
+  if (sp.nchunks > 1 && bidir) {
+    sp.sd_off = 0;
+    sp.state_off = (nslot * 16 * 8 + 255) & ~static_cast<size_t>(255);
+    sp.gstate_off = sp.state_off + nslot * 256 * 4;
+    sp.bytes = sp.gstate_off + nslot * 256 * 4;
+  } else if (sp.nchunks > 1) {
     sp.flag_off = sizeof(SplitHeader);
     sp.state_off = (sp.flag_off + static_cast<size_t>(sp.nbg * sp.nchunks) * 4 + 255) & ~static_cast<size_t>(255);
     sp.bytes = sp.state_off + static_cast<size_t>(sp.nbg * sp.nchunks) * 256 * 4;
@@ -866,12 +999,16 @@ SplitPlan plan_split(int64_t Bs, int64_t L, int64_t ED, int bidir, int ncu) {
   return sp;
 }
 
+// the bidirectional bf16 scan keeps its reverse-time partial sums in float32
+// at the start of the workspace; a split plan's buffers follow
+size_t partial_bytes(int64_t seq, int dtype, int bidir) {
+  return (bidir && dtype == SSM_BF16) ? (static_cast<size_t>(seq) * 4 + 255) & ~static_cast<size_t>(255) : 0;
+}
+
 size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, int bidir) {
   Sizes s;
   if (check_sizes(Bs, L, ED, N, dtype, &s) != SSM_OK || s.seq == 0) return 0;
-  // the bidirectional bf16 scan keeps its reverse-time partial sums in float32
-  if (bidir && dtype == SSM_BF16) return static_cast<size_t>(s.seq) * 4;
-  return plan_split(Bs, L, ED, bidir, device_cus()).bytes;
+  return partial_bytes(s.seq, dtype, bidir) + plan_split(Bs, L, ED, bidir, device_cus()).bytes;
 }
 
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
@@ -977,8 +1114,15 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.hdr = nullptr;
   a.flag = nullptr;
   a.state = nullptr;
+  a.sdsum = nullptr;
+  a.gstate = nullptr;
   const bool split = sp.nchunks > 1;
-  if (split) {
+  if (split && bidir) {
+    char* w = static_cast<char*>(ws) + partial_bytes(Bs * L * ED, std::is_same<T, float>::value ? SSM_F32 : SSM_BF16, 1);
+    a.sdsum = reinterpret_cast<double*>(w + sp.sd_off);
+    a.state = reinterpret_cast<float*>(w + sp.state_off);
+    a.gstate = reinterpret_cast<float*>(w + sp.gstate_off);
+  } else if (split) {
     char* w = static_cast<char*>(ws);
     a.hdr = reinterpret_cast<SplitHeader*>(w);
     a.flag = reinterpret_cast<int*>(w + sp.flag_off);
@@ -988,7 +1132,20 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
                        dim3(256), 0, stream, reinterpret_cast<unsigned*>(w), words);
   }
   const bool vec = (ED % 4) == 0;
-  if (bidir) {
+  if (bidir && split) {
+    // both directions of every chunk from its own entering states, then the
+    // join: entering states from the chunks' aggregates, and corrections
+    if (vec) launch_one<T, true, true, true>(a, nblk, stream);
+    else launch_one<T, true, false, true>(a, nblk, stream);
+    const dim3 grid(static_cast<unsigned>(nblk)), block(64 * kSEG);
+    if (a.z) {
+      if (vec) hipLaunchKernelGGL((scan_bidir_join_kernel<T, kSEG, kTS, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((scan_bidir_join_kernel<T, kSEG, kTS, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((scan_bidir_join_kernel<T, kSEG, kTS, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((scan_bidir_join_kernel<T, kSEG, kTS, false, false>), grid, block, 0, stream, a);
+    }
+  } else if (bidir) {
     if (vec) launch_one<T, true, true, false>(a, nblk, stream);
     else launch_one<T, true, false, false>(a, nblk, stream);
   } else if (split) {

@@ -407,3 +407,20 @@ def test_gated_backward_workspace(bidir, dtype):
     assert gated >= plain + 2 * 300 * 64 * 4
     assert gated < plain + 2 * 300 * 64 * 4 + 1024
     assert q(0, 300, 64, 16, dtype, gate=True) == 0
+
+
+def test_one_hip_runtime_whatever_the_call_order():
+    # The library is loaded with torch's HIP runtime already in the process,
+    # so that both use one runtime: a library call made before any torch call
+    # must not bring in a second (torch would then find no device).
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import state_space_model_selective_amd as ssm\n"
+            "ssm.ssm_scan_workspace_bytes(1, 64, 64, 16)\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout

@@ -126,6 +126,64 @@ def test_split_sequence(Bs, L, ED, dtype):
     check_full(Bs, L, ED, dtype=dtype, seed=L + ED)
 
 
+# The bidirectional scan splits such sequences too: every chunk runs both
+# directions from its own entering states (zero inside the sequence), then a
+# second kernel folds the chunks' aggregates into the states entering each
+# chunk from either side and corrects both ends of its output.
+
+@pytest.mark.parametrize("Bs,L,ED,dtype", [(1, 3000, 64, "f32"), (1, 5000, 42, "f32"), (2, 4096, 32, "bf16"),
+                                           (1, 20000, 128, "f32")])
+def test_bidirectional_split_sequence(Bs, L, ED, dtype):
+    import state_space_model_selective_amd as ssm
+    split = ssm.ssm_scan_workspace_bytes(Bs, L, ED, 16, ssm.SSM_F32 if dtype == "f32" else ssm.SSM_BF16, bidir=1)
+    plain = 0 if dtype == "f32" else -(-Bs * L * ED * 4 // 256) * 256
+    assert split > plain, "this shape is expected to split the sequence"
+    log("case bidir split Bs=%d L=%d ED=%d %s" % (Bs, L, ED, dtype))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=L + ED + 1)
+    h0 = (0.5 * synth.normal(L, 70, (Bs, ED, 16))).astype(np.float32)
+    g0 = (0.5 * synth.normal(L, 71, (Bs, ED, 16))).astype(np.float32)
+    for states in (False, True):
+        kw = dict(h0=h0, g0=g0) if states else {}
+        y, h, g = run_gpu(inp, bidir=True, want_h=True, want_g=True, **kw)
+        y_ref, h_ref, g_ref = oracle.scan(**inp, bidir=True, want_h_last=True, want_g_first=True, **kw)
+        assert_close("y", y, y_ref, TOL[dtype])
+        assert_close("h_last", h, h_ref, TOL["f32"])
+        assert_close("g_first", g, g_ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bidirectional_split_with_options_and_gate(dtype):
+    log("case bidir split, options %s" % dtype)
+    inp, opts = options_inputs(1, 4500, 48, dtype, seed=44)
+    y, h, g = run_gpu(inp, bidir=True, want_h=True, want_g=True, opts=opts)
+    y_ref, h_ref, g_ref = oracle.scan(**inp, bidir=True, want_h_last=True, want_g_first=True, **opts)
+    assert_close("y", y, y_ref, TOL[dtype])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+    assert_close("g_first", g, g_ref, TOL["f32"])
+
+
+def test_bidirectional_split_slow_decay_and_negative_steps():
+    # corrections that run over whole chunks from both ends (tiny steps, A = 0
+    # for some states), and mixed-sign step sizes (no early stop)
+    log("case bidir split, slow decay / mixed sign")
+    inp = synth.make_inputs(1, 6000, 64, 16, "f32", seed=23)
+    inp["delta"] = (inp["delta"] * 1e-3).astype(np.float32)
+    inp["A"][:, :3] = 0.0
+    y, h, g = run_gpu(inp, bidir=True, want_h=True, want_g=True)
+    y_ref, h_ref, g_ref = oracle.scan(**inp, bidir=True, want_h_last=True, want_g_first=True)
+    assert_close("y", y, y_ref, TOL["f32"])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+    assert_close("g_first", g, g_ref, TOL["f32"])
+    inp = synth.make_inputs(1, 4000, 64, 16, "f32", seed=24)
+    sign = np.where(synth.uniform(24, 9, inp["delta"].shape, 0, 1) < 0.1, -1.0, 1.0).astype(np.float32)
+    inp["delta"] = (inp["delta"] * sign).astype(np.float32)
+    y, h, g = run_gpu(inp, bidir=True, want_h=True, want_g=True)
+    y_ref, h_ref, g_ref = oracle.scan(**inp, bidir=True, want_h_last=True, want_g_first=True)
+    assert_close("y", y, y_ref, TOL["f32"])
+    assert_close("h_last", h, h_ref, TOL["f32"])
+    assert_close("g_first", g, g_ref, TOL["f32"])
+
+
 def test_split_sequence_slow_decay_and_no_decay():
     # tiny step sizes (the carried state decays over the whole chunk) and
     # A = 0 for some states (no decay at all): the correction runs to the end
