@@ -45,6 +45,9 @@ WORKLOADS = {
     "fwd_bf16_Bs4_L8192_ED5120_N16": dict(Bs=4, L=8192, ED=5120, N=16, dtype="bf16", bidir=False, h_last=False),
     "fwd_f32_Bs1_L131072_ED2048_N16": dict(Bs=1, L=131072, ED=2048, N=16, dtype="f32", bidir=False, h_last=False),
     "bidir_f32_Bs8_L4096_ED1536_N16": dict(Bs=8, L=4096, ED=1536, N=16, dtype="f32", bidir=True, h_last=False),
+    # the long sequence, bidirectional (split into chunks joined by a second kernel)
+    "bidir_f32_Bs1_L131072_ED2048_N16": dict(Bs=1, L=131072, ED=2048, N=16, dtype="f32", bidir=True,
+                                             h_last=True),
     # backward pass (all gradients, dy ~ N(0, 1)) at the forward training shape
     "bwd_f32_Bs8_L1024_ED1536_N16": dict(Bs=8, L=1024, ED=1536, N=16, dtype="f32", bidir=False, h_last=False,
                                          bwd=True),

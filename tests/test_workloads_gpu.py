@@ -54,6 +54,10 @@ def test_bidirectional_8x4096x1536():
     run_workload("bidir_f32_Bs8_L4096_ED1536_N16", 256)
 
 
+def test_bidirectional_long_sequence_131072():
+    run_workload("bidir_f32_Bs1_L131072_ED2048_N16", 64)
+
+
 def run_bwd_workload(name):
     from parity_util import assert_grads_close, run_gpu_bwd
     w = synth.WORKLOADS[name]
