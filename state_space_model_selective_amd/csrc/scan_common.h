@@ -79,23 +79,31 @@ struct Vec4<uint16_t> {
 // critical path.
 __device__ __forceinline__ float rcp_fast(float v) { return __builtin_amdgcn_rcpf(v); }
 
+// log(v) for a normal positive v: the hardware base-2 logarithm (v_log_f32)
+// times ln 2, a few ulp. (The library logf adds a rescaling for denormal
+// arguments and an extra-precise ln 2 product: a dozen more instructions,
+// on the staging threads' critical path.)
+__device__ __forceinline__ float log_fast(float v) { return __builtin_amdgcn_logf(v) * 0.6931471805599453f; }
+
 // log(1 + u) for u >= 0 from the hardware logarithm, accurate to a few ulp:
 // with w = 1 + u rounded, log(w) u / (w - 1) cancels the rounding of w
 // (D. Goldberg, "What every computer scientist should know about
 // floating-point arithmetic", 1991, section 4.1); u itself when w rounds to 1.
+// (w >= 1 is never denormal.)
 __device__ __forceinline__ float log1p_pos(float u) {
   const float w = 1.f + u;
-  return w == 1.f ? u : __logf(w) * (u * rcp_fast(w - 1.f));
+  return w == 1.f ? u : log_fast(w) * (u * rcp_fast(w - 1.f));
 }
 
 // e^x - 1 from the hardware exponential and logarithm (W. Kahan's method:
 // with v = e^x rounded, (v - 1) x / log(v) cancels the rounding of v); x
-// itself when v rounds to 1, -1 when v rounds to 0.
+// itself when v rounds to 1, -1 when v rounds to 0. Used with x <= 0, where
+// v in (0, 1]: v below the normal range makes (v - 1) round to -1 first.
 __device__ __forceinline__ float expm1_fast(float x) {
   const float v = __expf(x);
   if (v == 1.f) return x;
   const float vm = v - 1.f;
-  return vm == -1.f ? -1.f : vm * (x * rcp_fast(__logf(v)));
+  return vm == -1.f ? -1.f : vm * (x * rcp_fast(log_fast(v)));
 }
 
 __device__ __forceinline__ float map_step(float d, const float* bias, int softplus, float lo, float hi) {
