@@ -87,6 +87,14 @@ struct BwdArgs {
   float* part_dd;
   const float* acc_dx;
   const float* acc_dd;
+  // split sequence (nchunks > 1): chunk k of a (batch row, channel group)
+  // covers the sweep's virtual steps [k chunk_len, (k + 1) chunk_len); the
+  // chunk aggregates of bwd_chunk_agg_kernel give the states entering it
+  int nchunks;
+  int64_t chunk_len;
+  double* agg_sd;   // [bg * nchunks + k][16 channels]: sum of delta' over the chunk
+  float* agg_h;     // [bg * nchunks + k][16][16]: forward state at the chunk's end, from zero
+  float* agg_k;     // [bg * nchunks + k][16][16]: adjoint at the chunk's start, from zero after it
 };
 
 template <int RT>
@@ -166,25 +174,28 @@ struct BwdStager {
   float4 ra, rb, rc;
   float4 bias4;  // OPTS: dt_bias of the task's channels
   int64_t b, e0, ED, L;
+  int64_t tv0, tv1;  // the virtual steps [tv0, tv1) of this workgroup's chunk (the whole sweep unless split)
   // this task's raw step-size gradients, summed over its rounds in float64
   // (a float32 sum over thousands of rounds would lose the small terms)
   double dbacc[4] = {0.0, 0.0, 0.0, 0.0};
 
-  __device__ __forceinline__ void init(int tid, int64_t b_, int64_t e0_, int64_t ED_, int64_t L_) {
+  __device__ __forceinline__ void init(int tid, int64_t b_, int64_t e0_, int64_t ED_, int64_t L_, int64_t tv0_,
+                                       int64_t tv1_) {
     int u = tid;
     is_xd = u < 4 * RT;
     if (!is_xd) u -= 4 * RT;
     row = u >> 2;
     chk = u & 3;
     b = b_, e0 = e0_, ED = ED_, L = L_;
+    tv0 = tv0_, tv1 = tv1_;
     chunk_ok = !is_xd || e0 + 4 * chk < ED;
   }
 
-  // global -> registers for round rr; WITH_ADJ also loads dy and C
+  // global -> registers for round rr of the chunk; WITH_ADJ also loads dy and C
   template <bool WITH_ADJ>
   __device__ __forceinline__ void prefetch(const BwdArgs<T>& p, int64_t rr) {
-    const int64_t tv = rr * RT + row;
-    row_ok = tv < L;
+    const int64_t tv = tv0 + rr * RT + row;
+    row_ok = tv < tv1;
     const int64_t t = REV ? L - 1 - tv : tv;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), bb = a, cc = a;
     if (row_ok && chunk_ok) {
@@ -236,8 +247,8 @@ struct BwdStager {
   }
 
   __device__ __forceinline__ void store_grads(const BwdArgs<T>& p, const BwdTile<RT>& tl, int64_t rr) {
-    const int64_t tv = rr * RT + row;
-    if (!is_xd || tv >= L || !chunk_ok) return;
+    const int64_t tv = tv0 + rr * RT + row;
+    if (!is_xd || tv >= tv1 || !chunk_ok) return;
     const int64_t t = REV ? L - 1 - tv : tv;
     const int c4 = 4 * chk;
     float4 gx = *reinterpret_cast<const float4*>(&tl.xv[row][c4]);
@@ -317,10 +328,10 @@ struct BwdStager {
 // dB / dC partials of round rr (their column sums are in cs) -> workspace
 template <typename T, int RT, bool REV>
 __device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums<RT>& cs, int tid, int64_t b,
-                                              int64_t grp, int64_t rr) {
+                                              int64_t grp, int64_t tv0, int64_t tv1, int64_t rr) {
   const int tt = tid >> 3, qq = (tid >> 2) & 1, n4 = 4 * (tid & 3);
-  const int64_t tv = rr * RT + tt;
-  if (tv >= p.L) return;
+  const int64_t tv = tv0 + rr * RT + tt;
+  if (tv >= tv1) return;
   const int64_t t = REV ? p.L - 1 - tv : tv;
   float4 s = *reinterpret_cast<const float4*>(&cs.v[tt][0][qq][n4]);
 #pragma unroll
@@ -330,6 +341,137 @@ __device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums
   }
   float* dst = qq ? p.pC : p.pB;
   *reinterpret_cast<float4*>(dst + ((grp * p.Bs + b) * p.L + t) * 16 + n4) = s;
+}
+
+// The states entering chunk kchunk of a split sweep: the forward state
+// h (on entry: h0, or zero) folded through chunks 0 .. kchunk-1, and the
+// adjoint k (on entry: dh_last, or zero) folded through chunks nchunks-1 down
+// to kchunk+1, each as s = exp2(A log2e sum delta') s + s_chunk in chunk order.
+template <typename T>
+__device__ void chunk_entry_states(const BwdArgs<T>& p, int64_t bg, int64_t kchunk, int ch, int g,
+                                   const float (&A2)[4], float (&h)[4], float (&k)[4]) {
+  const int64_t K = p.nchunks;
+  auto fold = [&](float (&v)[4], const float* agg, int64_t j) {
+    const int64_t slot = bg * K + j;
+    const float sdc = static_cast<float>(p.agg_sd[slot * 16 + ch]);
+    const float4 a = *reinterpret_cast<const float4*>(agg + slot * 256 + ch * 16 + 4 * g);
+    const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[i] * sdc), v[i], av[i]);
+  };
+#pragma unroll 4
+  for (int64_t j = 0; j < kchunk; ++j) fold(h, p.agg_h, j);
+#pragma unroll 4
+  for (int64_t j = K - 1; j > kchunk; --j) fold(k, p.agg_k, j);
+}
+
+// First pass of a split sweep: per (batch row, channel group, chunk), the
+// chunk's aggregates from zero states: the sum of delta' over its steps
+// (float64), the forward state at its end and the adjoint at its start,
+// k = sum_t (prod_{s = t0 .. t} a_s) (dy_t C_t) (each a product of a and the
+// adjoint's own input, accumulated along the chunk). The second pass
+// (scan_bwd_kernel) folds them into the states entering each chunk.
+template <typename T, int SEG, int TS, bool VEC, bool REV, bool OPTS>
+__global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) void bwd_chunk_agg_kernel(
+    const BwdArgs<T> p) {
+  constexpr int RT = SEG * TS;
+  static_assert(SEG * 64 == 8 * RT, "one staging task per thread");
+  __shared__ BwdTile<RT> tile[2];
+  __shared__ BwdFold<SEG> fa;
+  __shared__ float sds[SEG][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 15;
+  const int g = q >> 2;
+  const int c = q & 3;
+  const int ch = ((lane >> 4) << 2) | c;
+  const int64_t L = p.L, ED = p.ED;
+  int blk = blockIdx.x;
+  if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
+  const int64_t nbg = p.nblocks / p.nchunks;
+  const int64_t kchunk = blk / nbg, bg = blk % nbg;
+  const int64_t b = bg / p.ngroups;
+  const int64_t e0 = (bg % p.ngroups) * 16;
+  const int64_t tv0 = kchunk * p.chunk_len;
+  const int64_t tv1 = L - tv0 < p.chunk_len ? L : tv0 + p.chunk_len;
+  const int64_t R = (tv1 - tv0 + RT - 1) / RT;
+  const int64_t e = e0 + ch;
+  const int64_t ec = e < ED ? e : ED - 1;
+  float A2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) A2[j] = p.A[ec * 16 + 4 * g + j] * kLog2e;
+
+  BwdStager<T, RT, VEC, REV, OPTS> st;
+  st.init(tid, b, e0, ED, L, tv0, tv1);
+  st.load_bias(p);
+  float hc[4] = {0.f, 0.f, 0.f, 0.f};  // forward state (wave SEG-1)
+  float kc[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint at the chunk's start, so far (wave SEG-1)
+  double sdc = 0.0;                    // sum of delta' before the current segment (wave SEG-1)
+  st.template prefetch<true>(p, 0);
+  st.template commit<true>(p, tile[0]);
+  __syncthreads();
+  for (int64_t r = 0; r < R; ++r) {
+    rotate_priority(r, p.rot_ncu);
+    BwdTile<RT>& cur = tile[r & 1];
+    BwdTile<RT>& nxt = tile[(r + 1) & 1];
+    if (r + 1 < R) st.template prefetch<true>(p, r + 1);
+    // this wave's segment from zero: the forward end state, and the adjoint
+    // at the segment's start (backwards over its steps)
+    float av[TS][4], hl[4] = {0.f, 0.f, 0.f, 0.f}, kl[4] = {0.f, 0.f, 0.f, 0.f}, sd = 0.f;
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+      const int row = wave * TS + i;
+      const float dt = cur.dt[row][ch], dxv = dt * cur.xv[row][ch];
+      const float bq = cur.bc[row][q].x;
+      sd += dt;
+      const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
+        hl[j] = __builtin_fmaf(av[i][j], hl[j], dxv * bb[j]);
+      }
+    }
+#pragma unroll
+    for (int i = TS - 1; i >= 0; --i) {
+      const int row = wave * TS + i;
+      add_c_dy(kl, cur.bc[row][q].y, cur.dy[row][ch]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kl[j] *= av[i][j];
+    }
+    fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
+                                   __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
+    fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+    fa.K[wave][lane] = make_float4(kl[0], kl[1], kl[2], kl[3]);
+    sds[wave][lane] = sd;
+    __syncthreads();
+    if (wave == SEG - 1) {
+      for (int k = 0; k < SEG; ++k) {
+        // the segment's adjoint reaches the chunk's start through every step
+        // before it: the product from the float64 sum of delta' so far
+        const float cum = static_cast<float>(sdc);
+        const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane], Kk = fa.K[k][lane];
+        kc[0] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[0] * cum), Kk.x, kc[0]);
+        kc[1] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[1] * cum), Kk.y, kc[1]);
+        kc[2] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[2] * cum), Kk.z, kc[2]);
+        kc[3] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[3] * cum), Kk.w, kc[3]);
+        hc[0] = __builtin_fmaf(Ak.x, hc[0], Hk.x);
+        hc[1] = __builtin_fmaf(Ak.y, hc[1], Hk.y);
+        hc[2] = __builtin_fmaf(Ak.z, hc[2], Hk.z);
+        hc[3] = __builtin_fmaf(Ak.w, hc[3], Hk.w);
+        sdc += static_cast<double>(sds[k][lane]);
+      }
+    }
+    if (r + 1 < R) st.template commit<true>(p, nxt);
+    __syncthreads();
+  }
+  if (wave == SEG - 1) {
+    const int64_t slot = bg * p.nchunks + kchunk;
+    if (g == 0) p.agg_sd[slot * 16 + ch] = sdc;
+    *reinterpret_cast<float4*>(p.agg_h + slot * 256 + ch * 16 + 4 * g) = make_float4(hc[0], hc[1], hc[2], hc[3]);
+    *reinterpret_cast<float4*>(p.agg_k + slot * 256 + ch * 16 + 4 * g) = make_float4(kc[0], kc[1], kc[2], kc[3]);
+  }
 }
 
 template <typename T, int SEG, int TS, bool VEC, bool REV, bool OPTS>
@@ -354,10 +496,20 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
 
   int blk = blockIdx.x;
   if (p.remap) blk = (blk & 7) * (p.nblocks >> 3) + (blk >> 3);
-  const int64_t b = blk / p.ngroups;
-  const int64_t grp = blk % p.ngroups;
+  // (batch row, channel group) and, for a split sequence, the chunk
+  int64_t bg = blk, kchunk = 0;
+  if (p.nchunks > 1) {
+    const int64_t nbg = p.nblocks / p.nchunks;
+    kchunk = blk / nbg;
+    bg = blk % nbg;
+  }
+  const int64_t b = bg / p.ngroups;
+  const int64_t grp = bg % p.ngroups;
   const int64_t e0 = grp * 16;
-  const int64_t R = p.rounds;
+  const int64_t tv0 = kchunk * p.chunk_len;                      // the chunk's virtual steps [tv0, tv1)
+  const int64_t tv1 = L - tv0 < p.chunk_len ? L : tv0 + p.chunk_len;
+  const int64_t R = (tv1 - tv0 + RT - 1) / RT;                   // rounds of the chunk
+  const int64_t r0 = tv0 / RT;                                   // its first round in the sweep
 
   const int64_t e = e0 + ch;
   const bool ch_ok = e < ED;
@@ -371,18 +523,29 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   const float Dv = (p.D && ch_ok) ? p.D[e] : 0.f;
 
   BwdStager<T, RT, VEC, REV, OPTS> st;
-  st.init(tid, b, e0, ED, L);
+  st.init(tid, b, e0, ED, L, tv0, tv1);
   st.load_bias(p);
-  // checkpoint of round rr for this lane's 4 states
-  auto ck = [&](int64_t rr) { return p.ckpt + ((b * R + rr) * p.EDp + e) * 16 + 4 * g; };
+  // checkpoint of round rr of the chunk for this lane's 4 states
+  auto ck = [&](int64_t rr) { return p.ckpt + ((b * p.rounds + r0 + rr) * p.EDp + e) * 16 + 4 * g; };
+
+  // the states entering the chunk: the forward state before its first step
+  // (h0 at the sweep's start) and the adjoint after its last step (dh_last
+  // at the sweep's end); a later (earlier) chunk folds the aggregates of the
+  // chunks before (after) it onto them
+  float hstart[4] = {0.f, 0.f, 0.f, 0.f}, kend[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.h0 && ch_ok) {
+    const float4 v = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
+    hstart[0] = v.x, hstart[1] = v.y, hstart[2] = v.z, hstart[3] = v.w;
+  }
+  if (p.dh_last && ch_ok) {
+    const float4 v = *reinterpret_cast<const float4*>(p.dh_last + (b * ED + e) * 16 + 4 * g);
+    kend[0] = v.x, kend[1] = v.y, kend[2] = v.z, kend[3] = v.w;
+  }
+  if (p.nchunks > 1) chunk_entry_states(p, bg, kchunk, ch, g, A2, hstart, kend);
 
   // ---- sweep 1: forward round aggregates -> checkpoints --------------------
   if (R > 1) {
-    float hc[4] = {0.f, 0.f, 0.f, 0.f};  // state entering the round (wave SEG-1)
-    if (p.h0 && ch_ok) {
-      const float4 v = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
-      hc[0] = v.x, hc[1] = v.y, hc[2] = v.z, hc[3] = v.w;
-    }
+    float hc[4] = {hstart[0], hstart[1], hstart[2], hstart[3]};  // state entering the round (wave SEG-1)
     st.template prefetch<false>(p, 0);
     st.template commit<false>(p, tile[0]);
     __syncthreads();
@@ -430,10 +593,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   float kcar[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint carry out of round 0 (wave 0)
   // the adjoint carry entering the last round: the final state's gradient
   // (padded steps past L have a = 1 and no output, so it reaches step L-1 unchanged)
-  if (wave == 0)
-    fa.kc[R & 1][lane] = (p.dh_last && ch_ok)
-                             ? *reinterpret_cast<const float4*>(p.dh_last + (b * ED + e) * 16 + 4 * g)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  if (wave == 0) fa.kc[R & 1][lane] = make_float4(kend[0], kend[1], kend[2], kend[3]);
   st.template prefetch<true>(p, R - 1);
   st.template commit<true>(p, tile[(R - 1) & 1]);
   __syncthreads();
@@ -443,7 +603,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     BwdTile<RT>& nxt = tile[(r + 1) & 1];  // round r-1 has the other parity
     if (r >= 1) st.template prefetch<true>(p, r - 1);
     if (r + 1 < R) {
-      store_colsums<T, RT, REV>(p, cs, tid, b, grp, r + 1);
+      store_colsums<T, RT, REV>(p, cs, tid, b, grp, tv0, tv1, r + 1);
       st.store_grads(p, nxt, r + 1);  // dx, ddelta of round r+1 (tile of the same parity)
     }
 
@@ -471,12 +631,9 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     __syncthreads();
 
     // state entering the segment: the round's checkpoint through segments 0 .. wave-1
-    float hin[4] = {0.f, 0.f, 0.f, 0.f};
+    float hin[4] = {hstart[0], hstart[1], hstart[2], hstart[3]};
     if (r > 0) {
       const float4 v = *reinterpret_cast<const float4*>(ck(r));
-      hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
-    } else if (p.h0 && ch_ok) {
-      const float4 v = *reinterpret_cast<const float4*>(p.h0 + (b * ED + e) * 16 + 4 * g);
       hin[0] = v.x, hin[1] = v.y, hin[2] = v.z, hin[3] = v.w;
     }
     for (int k = 0; k < wave; ++k) {
@@ -573,12 +730,14 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     if (r >= 1) st.template commit<true>(p, nxt);
     __syncthreads();
   }
-  store_colsums<T, RT, REV>(p, cs, tid, b, grp, 0);
+  store_colsums<T, RT, REV>(p, cs, tid, b, grp, tv0, tv1, 0);
   st.store_grads(p, tile[0], 0);
 
   // ---- per-workgroup results ----------------------------------------------
-  if (p.dh0 && wave == 0 && ch_ok)
+  // (a later chunk's entering-state gradient stays inside the sweep)
+  if (p.dh0 && kchunk == 0 && wave == 0 && ch_ok)
     *reinterpret_cast<float4*>(p.dh0 + (b * ED + e) * 16 + 4 * g) = make_float4(kcar[0], kcar[1], kcar[2], kcar[3]);
+  const int64_t prow = b * p.nchunks + kchunk;  // partial row of dA, dD, ddt_bias
   // dA and dD: sums over the waves' segments, then one partial per batch row
   double* red = reinterpret_cast<double*>(&fa);  // [SEG][5][64]; the fold area is free now
   static_assert(sizeof(BwdFold<SEG>) >= sizeof(double) * SEG * 5 * 64, "reduction area");
@@ -591,8 +750,8 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     for (int j = 0; j < 5; ++j) {
       double s = red[j * 64 + lane];
       for (int k = 1; k < SEG; ++k) s += red[(k * 5 + j) * 64 + lane];
-      if (j < 4) p.pA[(b * p.EDp + e) * 16 + 4 * g + j] = s;
-      else if (g == 0) p.pD[b * p.EDp + e] = s;
+      if (j < 4) p.pA[(prow * p.EDp + e) * 16 + 4 * g + j] = s;
+      else if (g == 0) p.pD[prow * p.EDp + e] = s;
     }
   }
   // ddt_bias: the step-size tasks' sums, added over the round's rows in row
@@ -610,7 +769,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     if (tid < 16) {
       double s = 0.0;
       for (int r = 0; r < RT; ++r) s += dbs[r * 16 + tid];
-      p.pDB[b * p.EDp + e0 + tid] = s;
+      p.pDB[prow * p.EDp + e0 + tid] = s;
     }
   }
 }
@@ -699,7 +858,8 @@ __global__ void gate_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ 
 // ---------------------------------------------------------------------------
 struct BwdLayout {
   int64_t rounds, ngroups, EDp;
-  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, pDB_off, part_off, bytes;
+  int64_t nchunks, chunk_len;  // split sweep: chunks per (batch row, channel group) and their length
+  size_t ckpt_off, pB_off, pC_off, pA_off, pD_off, pDB_off, part_off, agg_off, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -713,11 +873,26 @@ bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo, bool bidir = f
   lo->rounds = (L + kBRT - 1) / kBRT;
   lo->ngroups = (ED + 15) / 16;
   lo->EDp = lo->ngroups * 16;
+  // A long sweep with fewer than two (batch row, channel group) pairs per
+  // compute unit is cut into chunks (each at least 16 rounds, about three
+  // workgroups per CU in all), as the forward scan does.
+  lo->nchunks = 1;
+  lo->chunk_len = L;
+  const int64_t nbg = Bs * lo->ngroups, ncu = device_cus();
+  if (ncu > 0 && nbg > 0 && nbg < 2 * ncu) {
+    const int64_t k = std::min<int64_t>(3 * ncu / nbg, L / (16 * kBRT));
+    if (k >= 2) {
+      lo->chunk_len = ((L + k - 1) / k + kBRT - 1) / kBRT * kBRT;
+      lo->nchunks = (L + lo->chunk_len - 1) / lo->chunk_len;
+    }
+  }
+  const int64_t rows = Bs * lo->nchunks;  // dA / dD / ddt_bias partial rows per direction
   // every count below is checked against overflow of size_t arithmetic
   const double total = 4.0 * (static_cast<double>(Bs) * lo->rounds * lo->EDp * 16 +
-                              2.0 * dirs * lo->ngroups * Bs * L * 16 + 2.0 * dirs * Bs * lo->EDp * 18 +
-                              (part_f32 ? 2.0 * Bs * L * ED : 0.0)) +
-                       6 * 256.0;
+                              2.0 * dirs * lo->ngroups * Bs * L * 16 + 2.0 * dirs * rows * lo->EDp * 18 +
+                              (part_f32 ? 2.0 * Bs * L * ED : 0.0) +
+                              (lo->nchunks > 1 ? dirs * 544.0 * nbg * lo->nchunks : 0.0)) +
+                       7 * 256.0;
   if (total > 9.0e18) return false;
   size_t off = 0;
   lo->ckpt_off = off;
@@ -727,13 +902,17 @@ bool bwd_layout(int64_t Bs, int64_t L, int64_t ED, BwdLayout* lo, bool bidir = f
   lo->pC_off = off;
   off = align256(off + static_cast<size_t>(dirs * lo->ngroups * Bs * L * 16) * 4);
   lo->pA_off = off;
-  off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp * 16) * 8);
+  off = align256(off + static_cast<size_t>(dirs * rows * lo->EDp * 16) * 8);
   lo->pD_off = off;
-  off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp) * 8);
+  off = align256(off + static_cast<size_t>(dirs * rows * lo->EDp) * 8);
   lo->pDB_off = off;
-  off = align256(off + static_cast<size_t>(dirs * Bs * lo->EDp) * 8);
+  off = align256(off + static_cast<size_t>(dirs * rows * lo->EDp) * 8);
   lo->part_off = off;
   if (part_f32) off = align256(off + static_cast<size_t>(2 * Bs * L * ED) * 4);
+  // chunk aggregates per direction: [slot][16] float64 sums of delta', then
+  // [slot][16][16] forward end states and [slot][16][16] adjoint start states
+  lo->agg_off = off;
+  if (lo->nchunks > 1) off = align256(off + static_cast<size_t>(dirs * nbg * lo->nchunks) * (16 * 8 + 2 * 256 * 4));
   lo->bytes = off;
   return true;
 }
@@ -834,6 +1013,20 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
 
 template <typename T, bool REV>
 void launch_bwd_kernel(const BwdArgs<T>& a, int64_t nblk, size_t dyn, bool vec, hipStream_t stream) {
+  if (a.nchunks > 1) {
+    // the chunks' aggregates first (same grid; the launch order on the stream joins them)
+    if (a.dt_pre) {
+      if (vec)
+        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, true, REV, true>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, false, REV, true>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
+    } else {
+      if (vec)
+        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, true, REV, false>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, false, REV, false>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
+    }
+  }
   if (a.dt_pre) {
     if (vec)
       hipLaunchKernelGGL((scan_bwd_kernel<T, kBSEG, kBTS, true, REV, true>), dim3(nblk), dim3(64 * kBSEG), dyn, stream, a);
@@ -855,8 +1048,10 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   const bool part_f32 = bidir && !std::is_same<T, float>::value;
   BwdLayout lo;
   bwd_layout(Bs, L, ED, &lo, bidir, part_f32);
-  const int64_t nblk = Bs * lo.ngroups;
+  const int64_t nbg = Bs * lo.ngroups;
+  const int64_t nblk = nbg * lo.nchunks;
   if (nblk > INT32_MAX / 2) return SSM_ERR_DIM;
+  const int64_t rows = Bs * lo.nchunks;  // dA / dD / ddt_bias partial rows per direction
   char* w = static_cast<char*>(ws);
   BwdArgs<T> a;
   a.x = static_cast<const T*>(x);
@@ -900,6 +1095,13 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.part_dd = part_f32 ? part + Bs * L * ED : nullptr;
   a.acc_dx = nullptr;
   a.acc_dd = nullptr;
+  a.nchunks = static_cast<int>(lo.nchunks);
+  a.chunk_len = lo.chunk_len;
+  const size_t nslot = static_cast<size_t>(nbg * lo.nchunks);
+  char* agg = w + lo.agg_off;
+  a.agg_sd = lo.nchunks > 1 ? reinterpret_cast<double*>(agg) : nullptr;
+  a.agg_h = lo.nchunks > 1 ? reinterpret_cast<float*>(agg + nslot * 16 * 8) : nullptr;
+  a.agg_k = lo.nchunks > 1 ? a.agg_h + nslot * 256 : nullptr;
 
   const size_t lds = sizeof(BwdTile<kBRT>) * 2 + sizeof(ColSums<kBRT>) + sizeof(BwdFold<kBSEG>) + 16;
   const size_t dyn = spread_lds(nblk, lds, 16 / kBSEG);
@@ -918,9 +1120,16 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
     r.dh_last = sa.dg_first;
     r.pB = a.pB + lo.ngroups * Bs * L * 16;
     r.pC = a.pC + lo.ngroups * Bs * L * 16;
-    r.pA = a.pA + Bs * lo.EDp * 16;
-    r.pD = a.pD + Bs * lo.EDp;
-    r.pDB = a.pDB ? a.pDB + Bs * lo.EDp : nullptr;
+    r.pA = a.pA + rows * lo.EDp * 16;
+    r.pD = a.pD + rows * lo.EDp;
+    r.pDB = a.pDB ? a.pDB + rows * lo.EDp : nullptr;
+    if (lo.nchunks > 1) {
+      // the reverse-time scan's own chunk aggregates
+      char* agg_r = agg + nslot * (16 * 8 + 2 * 256 * 4);
+      r.agg_sd = reinterpret_cast<double*>(agg_r);
+      r.agg_h = reinterpret_cast<float*>(agg_r + nslot * 16 * 8);
+      r.agg_k = r.agg_h + nslot * 256;
+    }
     r.part_dx = nullptr;
     r.part_dd = nullptr;
     r.acc_dx = part_f32 ? a.part_dx : static_cast<const float*>(dx);
@@ -936,7 +1145,7 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
                      static_cast<int>(bidir ? 2 * lo.ngroups : lo.ngroups));
   if (hipGetLastError() != hipSuccess) return SSM_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_reduce_ad_kernel, dim3(static_cast<unsigned>((ED * 18 + 255) / 256)), dim3(256), 0, stream,
-                     a.pA, a.pD, a.pDB, dA, dD, ddt_bias, bidir ? 2 * Bs : Bs, Bs, ED, lo.EDp);
+                     a.pA, a.pD, a.pDB, dA, dD, ddt_bias, bidir ? 2 * rows : rows, rows, ED, lo.EDp);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
 }
 

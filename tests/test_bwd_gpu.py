@@ -241,3 +241,58 @@ def test_gate_training_shape():
     # (Bs 8, L 1024, ED 1536), bf16, with every option
     _, opts = options_inputs(8, 1024, 1536, "bf16", seed=13)
     check_options(8, 1024, 1536, "bf16", 13, opts)
+
+
+# ---- split sweeps: long sequences with few channel groups --------------------
+# Such sweeps are cut into chunks: a first kernel forms each chunk's
+# aggregates from zero states (the sum of its step sizes, the forward state at
+# its end, the adjoint at its start), then every chunk runs the backward of
+# its own steps from the states folded in from the chunks on either side.
+
+@pytest.mark.parametrize("Bs,L,ED,dtype,bidir", [(1, 3000, 64, "f32", False), (1, 5000, 42, "f32", False),
+                                                 (2, 4096, 32, "bf16", False), (1, 3000, 64, "f32", True),
+                                                 (2, 4096, 32, "bf16", True)])
+def test_split_sweep(Bs, L, ED, dtype, bidir):
+    log("bwd split case Bs=%d L=%d ED=%d dtype=%s bidir=%s" % (Bs, L, ED, dtype, bidir))
+    seed = L + ED + (7 if bidir else 0)
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=seed)
+    dy = synth.make_output_grad(Bs, L, ED, dtype, seed=seed)
+    h0 = synth.normal(seed, 79, (Bs, ED, 16))
+    dhl = synth.normal(seed, 80, (Bs, ED, 16))
+    kw = dict(g0=synth.normal(seed, 81, (Bs, ED, 16)), dg_first=synth.normal(seed, 82, (Bs, ED, 16))) \
+        if bidir else {}
+    got = run_gpu_bwd(inp, dy, h0=h0, want_dh0=True, bidir=bidir, dh_last=dhl, want_dg0=bidir, **kw)
+    ref = oracle.scan_bwd(**inp, dy=dy, h0=h0, bidir=bidir, dh_last=dhl, **kw)
+    assert_grads_close(got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype,bidir", [("f32", False), ("bf16", False), ("f32", True)])
+def test_split_sweep_with_options_and_gate(dtype, bidir):
+    _, opts = options_inputs(1, 4500, 48, dtype, seed=45)
+    check_options(1, 4500, 48, dtype, 45, opts, bidir=bidir, h0=True)
+
+
+@pytest.mark.parametrize("case", ["no_decay_exact", "full_decay", "zero_steps"])
+def test_split_sweep_degenerate_inputs(case):
+    # Carries over whole chunks: A = 0 with unit steps and inputs in {-1, 0, 1},
+    # where every state, adjoint and gradient is an integer that float32 holds
+    # exactly, whatever the order of the sums (with real-valued inputs and no
+    # decay over thousands of steps, float32 rounding of the growing sums alone
+    # exceeds the tolerance on ddelta where it cancels, split or not: the
+    # short unsplit cases above cover those inputs); no carries at all (a
+    # underflows to 0); zero steps at every other time.
+    log("bwd split degenerate case %s" % case)
+    L, ED = 2200, 48
+    if case == "no_decay_exact":
+        inp = synth.make_inputs(1, L, ED, 16, "f32", seed=16)
+        tern = lambda stream, shape: np.sign(np.round(synth.normal(16, stream, shape))).astype(np.float32)
+        inp.update(x=tern(40, (1, L, ED)), B=tern(41, (1, L, 16)), C=tern(42, (1, L, 16)),
+                   delta=np.ones((1, L, ED), np.float32), A=np.zeros((ED, 16), np.float32),
+                   D=np.round(inp["D"]).astype(np.float32))
+        dy = tern(43, (1, L, ED))
+    else:
+        inp = degenerate_inputs(case, Bs=1, L=L, ED=ED)
+        dy = synth.make_output_grad(1, L, ED, "f32", seed=16)
+    got = run_gpu_bwd(inp, dy, want_dD=True, want_dh0=True)
+    ref = oracle.scan_bwd(**inp, dy=dy)
+    assert_grads_close(got, ref, "f32")
