@@ -77,5 +77,9 @@ def test_backward_bf16_4x8192x5120():
     run_bwd_workload("bwd_bf16_Bs4_L8192_ED5120_N16")
 
 
+def test_backward_long_sequence_131072():
+    run_bwd_workload("bwd_f32_Bs1_L131072_ED2048_N16")
+
+
 def test_backward_bidirectional_8x4096x1536():
     run_bwd_workload("bwd_bidir_f32_Bs8_L4096_ED1536_N16")
