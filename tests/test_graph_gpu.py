@@ -123,3 +123,42 @@ def test_bidirectional_backward_bf16_graph():
     replay_check("bidirectional backward bf16", lambda: ssm.ssm_scan_bidir_bwd(
         t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=out, workspace=ws),
         [out[k] for k in ("dx", "ddelta", "dA", "dB", "dC", "dD")])
+
+
+def test_bidirectional_split_sequence_graph():
+    # the split bidirectional scan: the chunk kernel and the join kernel
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 1, 6000, 64, 16
+    need = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32, True)
+    assert need > 0, "this shape should split the bidirectional scan"
+    dev = torch.device("cuda:0")
+    t = to_device(synth.make_inputs(Bs, L, ED, N, "f32", seed=75), dev)
+    y = torch.empty_like(t["x"])
+    h = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev)
+    gf = torch.empty((Bs, ED, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    replay_check("bidirectional, split sequence", lambda: ssm.ssm_scan_bidir_fwd(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=y, h_last=h, g_first=gf, workspace=ws), [y, h, gf])
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_backward_split_sweep_graph(bidir):
+    # the chunk-aggregate kernel, the chunked backward and the reductions
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 1, 4000, 48, 16
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(Bs, L, ED, N, "f32", seed=76)
+    t = to_device(dict(inp, dy=synth.make_output_grad(Bs, L, ED, "f32", seed=76)), dev)
+    out = {"dx": torch.empty_like(t["x"]), "ddelta": torch.empty_like(t["x"]), "dA": torch.empty_like(t["A"]),
+           "dB": torch.empty_like(t["B"]), "dC": torch.empty_like(t["B"]),
+           "dD": torch.empty((ED,), dtype=torch.float32, device=dev),
+           "dh0": torch.empty((Bs, ED, N), dtype=torch.float32, device=dev)}
+    fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
+    need = (ssm.ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm.ssm_scan_bwd_workspace_bytes)(
+        Bs, L, ED, N, ssm.SSM_F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    replay_check("backward, split sweep, bidir=%s" % bidir, lambda: fn(
+        t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=out, workspace=ws, want_dh0=True),
+        [out[k] for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")])
