@@ -239,18 +239,18 @@ def bench_ssd(args, name):
         t["y"] = torch.empty_like(t["x"])
         sets.append(t)
     stream = torch.cuda.current_stream(dev)
-    ws = None
-    if bidir:
-        dcode = ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16
-        need = ssm.ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dcode)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+    # the workspace (a split sequence's range states; the bidirectional bf16
+    # scan's partials) is allocated once, outside the timed region
+    dcode = ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16
+    need = (ssm.ssm_ssd_bidir_workspace_bytes if bidir else ssm.ssm_ssd_workspace_bytes)(Bs, L, H, P, dcode)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
 
     def step(t):
         if bidir:
             ssm.ssm_ssd_bidir_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], workspace=ws,
                                   stream=stream)
         else:
-            ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], stream=stream)
+            ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=t["y"], workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         step(sets[i % nsets])

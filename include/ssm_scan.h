@@ -322,12 +322,25 @@ int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const v
  * instructions, with x, B and C as given and each float32 operand (the
  * decayed C B^T, the state, the decay-weighted B) split into a high and a
  * low bf16 part, so every product is within 2^-17 of its float32 value; y is
- * rounded to nearest even. No workspace. Conventions, alignment and error codes as
- * ssm_scan_fwd (SSM_ERR_DIM also when H is not a multiple of G).
+ * rounded to nearest even.
+ *   workspace : device memory of ssm_ssd_workspace_bytes(...) bytes, owned by
+ *               the caller; NULL when that is zero. With fewer (batch row,
+ *               head) pairs than compute units each sequence is cut into
+ *               ranges of whole 32-step chunks: a first pass forms every
+ *               range's end state from zero, the second runs every range
+ *               from the state folded in from the ranges before it; the
+ *               workspace holds those states (it needs no initialisation,
+ *               may not overlap an argument, and holds nothing of interest
+ *               after the call). SSM_ERR_WORKSPACE if it is needed and
+ *               missing or too small.
+ * Conventions, alignment and error codes as ssm_scan_fwd (SSM_ERR_DIM also
+ * when H is not a multiple of G).
  */
+size_t ssm_ssd_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype);
 int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                 const float* h0, const ssm_scan_options* opts, void* y, float* h_last, int64_t Bs, int64_t L,
-                int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* stream);
+                int64_t H, int64_t P, int64_t G, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /*
  * Bidirectional multi-head scan (Bi-Mamba2 on the multi-head form): the
@@ -346,11 +359,14 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
  *               at t = L-1 (zero if NULL; resumes the reverse direction from
  *               the next piece's g_first, as h0 resumes the forward one)
  *   g_first   : (Bs, H, P, N) float32, or NULL -- g after t = 0
- *   workspace : device memory of ssm_ssd_bidir_workspace_bytes(...) bytes for
- *               bfloat16 (the reverse direction's float32 partial of y; it
- *               may not overlap an argument); not used for float32 (the
- *               partial goes through y). Owned by the caller.
- * SSM_ERR_WORKSPACE if a bfloat16 call has no or too small a workspace.
+ *   workspace : device memory of ssm_ssd_bidir_workspace_bytes(...) bytes:
+ *               for bfloat16 the reverse direction's float32 partial of y
+ *               (float32 puts it through y), and for a split sequence (as in
+ *               ssm_ssd_fwd) both directions' range states; the reverse
+ *               sweep of a split sequence runs in a launch of its own before
+ *               the forward one. It may not overlap an argument; owned by
+ *               the caller; NULL when the size is zero.
+ * SSM_ERR_WORKSPACE if a needed workspace is missing or too small.
  * Otherwise conventions, numerics and error codes as ssm_ssd_fwd.
  */
 size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype);

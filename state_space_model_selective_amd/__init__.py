@@ -107,7 +107,9 @@ def lib():
         L.ssm_scan_bidir_bwd_workspace_bytes.restype = sz
         L.ssm_scan_bidir_bwd.argtypes = [vp] * 22 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_bwd.restype = ci
-        L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp]
+        L.ssm_ssd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+        L.ssm_ssd_workspace_bytes.restype = sz
+        L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp, sz, vp]
         L.ssm_ssd_fwd.restype = ci
         L.ssm_ssd_bidir_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
         L.ssm_ssd_bidir_workspace_bytes.restype = sz
@@ -486,30 +488,40 @@ def _ssd_args(where, x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace, out
     return Bs, L, H, P, G, N
 
 
+def ssm_ssd_workspace_bytes(Bs, L, H, P, dtype=SSM_F32):
+    """Workspace bytes of ssm_ssd_fwd on the current device (nonzero when the
+    sequences are split into ranges: fewer (batch row, head) pairs than
+    compute units)."""
+    return lib().ssm_ssd_workspace_bytes(Bs, L, H, P, dtype)
+
+
 def ssm_ssd_fwd(x, dt, A, B, C, D=None, y=None, h_last=None, h0=None, stream=None, dt_bias=None,
-                dt_softplus=False, dt_limit=None, z=None):
+                dt_softplus=False, dt_limit=None, z=None, workspace=None):
     """Multi-head selective scan: x (Bs, L, H, P), dt (Bs, L, H), A (H,),
     B and C (Bs, L, G, N), D (H,) or None, h0 (Bs, H, P, N) or None.
     dt_bias (H,) / dt_softplus / dt_limit pre-process dt, z (like x) gates
     the output. Returns y (Bs, L, H, P); the final state goes to h_last if
-    given."""
+    given. A workspace (uint8, ssm_ssd_workspace_bytes) is allocated when
+    needed and not given."""
     import torch
-    Bs, L, H, P, G, N = _ssd_args("ssm_ssd_fwd", x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, None,
+    Bs, L, H, P, G, N = _ssd_args("ssm_ssd_fwd", x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
                                   [("y", y, "seq"), ("h_last", h_last, "state")])
     dtc = _dtype_code(x)
     if y is None:
         y = torch.empty_like(x)
+    workspace, wsb = _workspace(workspace, lib().ssm_ssd_workspace_bytes(Bs, L, H, P, dtc), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
     rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts), _ptr(y),
-                           _ptr(h_last), Bs, L, H, P, G, N, dtc, _stream(x, stream))
+                           _ptr(h_last), Bs, L, H, P, G, N, dtc, _ptr(workspace), wsb, _stream(x, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")
     return y
 
 
 def ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtype=SSM_F32):
-    """Workspace bytes of ssm_ssd_bidir_fwd (SSM_F32: none, SSM_BF16: the
-    reverse sweep's float32 partial output)."""
+    """Workspace bytes of ssm_ssd_bidir_fwd on the current device (SSM_BF16:
+    the reverse sweep's float32 partial output; a split sequence: both
+    sweeps' range states)."""
     return lib().ssm_ssd_bidir_workspace_bytes(Bs, L, H, P, dtype)
 
 

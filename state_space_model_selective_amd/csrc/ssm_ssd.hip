@@ -69,6 +69,15 @@ struct SsdArgs {
   const T* z;
   int64_t L, H, G;
   int nblocks;  // workgroups of the launch
+  // split sequence: each (batch row, head) in nranges ranges of range_chunks
+  // chunks; range j starts from the state folded in from ranges 0 .. j-1 of
+  // its sweep (agg_S, agg_cs: per (range, batch row, head), a range's end
+  // state from zero and A times its sum of step sizes)
+  int nranges;
+  int64_t range_chunks;
+  int sweep_sel;   // -1: every sweep of the kernel; 0: the reverse sweep only; 1: the forward sweep only
+  float* agg_S;    // [(j * Bs H + bh)][P][N] (the sweep's own array)
+  double* agg_cs;  // [(j * Bs H + bh)]
 };
 
 // Workgroups are dealt to the 8 XCDs in turn (block i to XCD i mod 8). The
@@ -80,6 +89,45 @@ __device__ __forceinline__ int64_t xcd_local_block(int nblocks) {
   const int64_t blk = blockIdx.x;
   if (nblocks % 8 != 0) return blk;
   return (blk & 7) * (nblocks >> 3) + (blk >> 3);
+}
+
+// The (batch row, head) and, for a split sequence, the range of block i: in
+// the order of xcd_local_block, range-major, so that the heads of a batch
+// row's range (which share B and C) sit on one XCD.
+struct SsdBlock {
+  int bh, range, c0, c1;  // chunks [c0, c1) of the sweep (fewer than 2^31: L < 2^36)
+};
+template <typename T>
+__device__ __forceinline__ SsdBlock ssd_block(const SsdArgs<T>& p) {
+  SsdBlock r;
+  const int blk = static_cast<int>(xcd_local_block(p.nblocks));
+  const int nbh = p.nblocks / p.nranges;
+  const int nchunks = static_cast<int>((p.L + 31) / 32);
+  const int rc = static_cast<int>(p.range_chunks);
+  r.range = __builtin_amdgcn_readfirstlane(blk / nbh);
+  r.bh = __builtin_amdgcn_readfirstlane(blk % nbh);
+  r.c0 = r.range * rc;
+  r.c1 = r.c0 + rc < nchunks ? r.c0 + rc : nchunks;
+  return r;
+}
+
+// Between the two passes of a split sequence: every range's end state from
+// zero (agg_S) becomes, in place, the state entering that range: the sweep's
+// initial state (init: (Bs, H, P, N), or zero) folded through the ranges
+// before it, s = e^{cs_i} s + S_i, in range order. One thread per state
+// element of a (batch row, head).
+__global__ void ssd_join_kernel(float* agg_S, const double* agg_cs, const float* init, int64_t nbh, int64_t nranges,
+                                int64_t PN) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= nbh * PN) return;
+  const int64_t bh = i / PN, e = i % PN;
+  float run = init ? init[i] : 0.f;
+  for (int64_t j = 0; j < nranges; ++j) {
+    const int64_t slot = j * nbh + bh;
+    const float own = agg_S[slot * PN + e];
+    agg_S[slot * PN + e] = run;
+    run = __builtin_fmaf(__expf(static_cast<float>(agg_cs[slot])), run, own);
+  }
 }
 
 // step size of the head whose bias (or null) is given, after the options
@@ -181,10 +229,13 @@ struct SsdStager {
   }
 };
 
-template <typename T, int N, bool BIDIR, bool GATE>
+// AGG: the first pass of a split sequence (the ranges' end states from zero
+// and their decays; no output).
+template <typename T, int N, bool BIDIR, bool GATE, bool AGG = false>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p) {
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
+  static_assert(!(AGG && (BIDIR || GATE)), "the aggregate pass runs one sweep, no gate");
   constexpr int NB = N / 16;          // state column blocks
   constexpr int PBW = 4 * NB / 8;     // state row blocks per wave (its column block is wave % NB)
 
@@ -194,13 +245,13 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lk = lane >> 4;  // operand row / column and k index
-  const int64_t bh = xcd_local_block(p.nblocks);
+  const SsdBlock blk = ssd_block(p);
+  const int64_t bh = blk.bh;
   const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.f;
   const float* const bias = p.dt_bias ? p.dt_bias + h : nullptr;
-  const int64_t nchunks = (p.L + kQ - 1) / kQ;
 
   // output block of this wave: t-block ytb (16 steps) x head-channel block ypb
   const int ytb = wave >> 2, ypb = wave & 3;
@@ -211,9 +262,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const int mtb = mblk == 0 ? 0 : 1, msb = mblk == 2 ? 1 : 0;
 
   // BIDIR: a reverse sweep (zero initial state, no D x) storing a float32
-  // partial, then the forward sweep adding it
+  // partial, then the forward sweep adding it (a split sequence runs them in
+  // separate launches: sweep_sel)
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
-  const bool rev = BIDIR && sweep == 0;
+  if (BIDIR && p.sweep_sel >= 0 && sweep != p.sweep_sel) continue;  // (uniform)
+  const bool rev = BIDIR ? sweep == 0 : p.sweep_sel == 0;
   const float* const init = rev ? p.g0 : p.h0;  // the sweep's entering state (null: zero)
   f4 st[PBW];
 #pragma unroll
@@ -221,17 +274,24 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-      st[k][r] = init ? init[((b * p.H + h) * kP + pp) * N + nn] : 0.f;
-      sm.S[pp][nn] = st[k][r];
+      float v = 0.f;
+      if (!AGG) {
+        // a range of a split sequence starts from its joined entering state
+        if (p.nranges > 1) v = p.agg_S[((blk.range * (p.nblocks / p.nranges) + bh) * kP + pp) * N + nn];
+        else if (init) v = init[((b * p.H + h) * kP + pp) * N + nn];
+      }
+      st[k][r] = v;
+      if (!AGG) sm.S[pp][nn] = v;
     }
+  double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
 
   SsdStager<T, N> stg;
-  stg.load(p, tid, b, h, g, 0, rev);
+  stg.load(p, tid, b, h, g, blk.c0 * kQ, rev);
   stg.commit(sm, 0, tid);
   __syncthreads();
 
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int cur = c & 1;
+  for (int64_t c = blk.c0; c < blk.c1; ++c) {
+    const int cur = (c - blk.c0) & 1;
     const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
     // decay of the chunk: cs_t, e^{cs_t}, the state-update weights (ahead of
     // the next chunk's loads, whose registers are live from there on)
@@ -252,7 +312,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
       sm.w[lane] = __expf(cse - cst) * sm.dt[cur][lane];
       if (lane == 0) sm.cs_end = cse;
     }
-    if (c + 1 < nchunks) stg.load(p, tid, b, h, g, t0 + kQ, rev);
+    if (c + 1 < blk.c1) stg.load(p, tid, b, h, g, t0 + kQ, rev);
     // forward sweep of the bidirectional scan: the reverse partial of this
     // chunk's output rows, for the store at the chunk's end
     float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -263,10 +323,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     if (GATE && !rev) zr = load_gate(p, tid, b, h, t0);
 
     __syncthreads();
+    if (AGG && tid == 0) cs_sum += static_cast<double>(sm.cs_end);
 
     // C B^T on the causal blocks, each half of the sum over n by one wave,
     // masked and decayed into M[half]
-    if (wave < 6) {
+    if (!AGG && wave < 6) {
       // operands first (all LDS reads in flight together), then the products
       constexpr int K = N / 8;
       float ca[K], cb[K];
@@ -293,8 +354,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     }
 
     // inter-chunk output diag(e^{cs}) C S_in^T for the wave's output block
-    f4 y;
-    {
+    f4 y = {0.f, 0.f, 0.f, 0.f};
+    if (!AGG) {
       constexpr int K = N / 4;
       float ca[K], sb[K];
 #pragma unroll
@@ -316,7 +377,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 
     // intra-chunk output M X (causal: s-blocks up to the t-block); the
     // t-block 0 waves use the first half of the operands only
-    {
+    if (!AGG) {
       float ma[8], xb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -332,8 +393,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
         for (int j = 4; j < 8; ++j) y = mfma4(ma[j], xb[j], y);
       }
     }
+    if (!AGG) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Y[16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
+      for (int r = 0; r < 4; ++r) sm.Y[16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
+    }
 
     // state update S = e^{cs_end} S + (X w)^T B for the wave's blocks
     const float dec = __expf(sm.cs_end);
@@ -356,15 +419,17 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
         for (int k = 0; k < PBW; ++k) st[k] = mfma4(xa[j][k], bo[j], st[k]);
     }
     __syncthreads();  // every read of S_in and of this chunk's tiles is done; Y complete
+    if (!AGG) {
 #pragma unroll
-    for (int k = 0; k < PBW; ++k)
+      for (int k = 0; k < PBW; ++k)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.S[16 * (spb + k) + 4 * lk + r][16 * snb + li] = st[k][r];
+        for (int r = 0; r < 4; ++r) sm.S[16 * (spb + k) + 4 * lk + r][16 * snb + li] = st[k][r];
+    }
     // the next chunk's tiles (waits for its loads), then this chunk's output:
     // the store is the last memory operation of the chunk, so no later wait
     // for the loads has to wait for it as well
-    if (c + 1 < nchunks) stg.commit(sm, cur ^ 1, tid);
-    {
+    if (c + 1 < blk.c1) stg.commit(sm, cur ^ 1, tid);
+    if (!AGG) {
       // 4 consecutive head channels per thread: y + D x (+ the reverse
       // partial) -> y, or the reverse sweep's partial -> part
       const int t = tid >> 4, c4 = (tid & 15) * 4;
@@ -385,15 +450,28 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     __syncthreads();
   }
 
-  float* const fin = rev ? p.g_first : p.h_last;
-  if (fin) {
+  if (AGG) {
+    // the range's end state from zero and its decay exponent
+    const int64_t slot = blk.range * (p.nblocks / p.nranges) + bh;
 #pragma unroll
     for (int k = 0; k < PBW; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-        fin[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
+        p.agg_S[(slot * kP + pp) * N + nn] = st[k][r];
       }
+    if (tid == 0) p.agg_cs[slot] = cs_sum;
+  } else {
+    float* const fin = rev ? p.g_first : p.h_last;
+    if (fin && blk.range == p.nranges - 1) {
+#pragma unroll
+      for (int k = 0; k < PBW; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
+          fin[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
+        }
+    }
   }
   }  // sweep
 }
@@ -610,10 +688,11 @@ __device__ __forceinline__ void store_state_bf16(SsdSmemBf<N>& sm, int pp, int n
   *reinterpret_cast<uint2*>(&sm.S[1][pp][n0]) = make_uint2(l01, l23);
 }
 
-template <int N, bool BIDIR, bool GATE>
+template <int N, bool BIDIR, bool GATE, bool AGG = false>
 __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs<uint16_t> p) {
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
+  static_assert(!(AGG && (BIDIR || GATE)), "the aggregate pass runs one sweep, no gate");
   constexpr int NB = N / 16;       // state column blocks
   constexpr int PBW = 4 * NB / 8;  // state row blocks per wave (its column block is wave % NB)
   constexpr int KN = N / 32;       // products over n: instructions per 16 x 16 block
@@ -624,13 +703,14 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lk = lane >> 4;
-  const int64_t bh = xcd_local_block(p.nblocks);
+  const SsdBlock blk = ssd_block(p);
+  const int64_t bh = blk.bh;
   const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
   const float Dfwd = p.D ? p.D[h] : 0.f;
   const float* const bias = p.dt_bias ? p.dt_bias + h : nullptr;
-  const int64_t nchunks = (p.L + kQ - 1) / kQ;
+  const int64_t c0 = blk.c0, c1 = blk.c1;  // the chunks of this workgroup's range
 
   const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
   const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
@@ -640,9 +720,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   for (int i = tid; i < 2 * kQ * SsdSmemBf<N>::TP; i += 64 * kWaves) (&sm.M[0][0][0])[i] = 0;
 
   // BIDIR: a reverse sweep (zero initial state, no D x) storing a float32
-  // partial, then the forward sweep adding it
+  // partial, then the forward sweep adding it (a split sequence runs them in
+  // separate launches: sweep_sel)
   for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
-  const bool rev = BIDIR && sweep == 0;
+  if (BIDIR && p.sweep_sel >= 0 && sweep != p.sweep_sel) continue;  // (uniform)
+  const bool rev = BIDIR ? sweep == 0 : p.sweep_sel == 0;
   const float* const init = rev ? p.g0 : p.h0;  // the sweep's entering state (null: zero)
   const float Dh = rev ? 0.f : Dfwd;
 
@@ -652,45 +734,55 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
   for (int k = 0; k < PBW; ++k) {
     const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[k][r] = init ? init[((b * p.H + h) * kP + pp) * N + n0 + r] : 0.f;
-    store_state_bf16(sm, pp, n0, st[k]);
+    for (int r = 0; r < 4; ++r) {
+      float v = 0.f;
+      if (!AGG) {
+        // a range of a split sequence starts from its joined entering state
+        if (p.nranges > 1) v = p.agg_S[((blk.range * (p.nblocks / p.nranges) + bh) * kP + pp) * N + n0 + r];
+        else if (init) v = init[((b * p.H + h) * kP + pp) * N + n0 + r];
+      }
+      st[k][r] = v;
+    }
+    if (!AGG) store_state_bf16(sm, pp, n0, st[k]);
   }
+  double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
 
   // two stagers: while chunk c is computed, chunk c + 1 waits in one of them
   // (loaded during chunk c - 1, committed at the end of chunk c) and chunk
   // c + 2 is loaded into the other
   SsdStagerBf<N> stg0, stg1;
-  stg0.load(p, tid, b, h, g, 0, rev);
+  stg0.load(p, tid, b, h, g, c0 * kQ, rev);
   stg0.commit(p, bias, sm, 0, tid);
   if (wave == kWaves - 1) chunk_decay(sm, 0, Ah, lane, stg0.dt_value(p, bias));
-  if (nchunks > 1) stg1.load(p, tid, b, h, g, kQ, rev);
+  if (c0 + 1 < c1) stg1.load(p, tid, b, h, g, (c0 + 1) * kQ, rev);
   // forward sweep of the bidirectional scan: the reverse partial of the chunk
   // whose output is stored next, one chunk ahead of its store
   float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pv_prev = pv;
-  if (BIDIR && !rev) pv = load_partial(p, tid, b, h, 0);
+  if (BIDIR && !rev) pv = load_partial(p, tid, b, h, c0 * kQ);
   // the gate of those rows, the same way (forward sweep only)
   uint2 zr = make_uint2(0u, 0u), zr_prev = zr;
-  if (GATE && !rev) zr = load_gate(p, tid, b, h, 0);
+  if (GATE && !rev) zr = load_gate(p, tid, b, h, c0 * kQ);
   __syncthreads();
 
   // one chunk: ld receives chunk c + 2, cm holds chunk c + 1
   auto chunk = [&](const int64_t c, SsdStagerBf<N>& ld, const SsdStagerBf<N>& cm) {
-    const int cur = c & 1, nxt = cur ^ 1;
+    const int cur = (c - c0) & 1, nxt = cur ^ 1;
     const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
-    if (c + 2 < nchunks) ld.load(p, tid, b, h, g, t0 + 2 * kQ, rev);
+    if (c + 2 < c1) ld.load(p, tid, b, h, g, t0 + 2 * kQ, rev);
 
     // ---- phase 1 ----
-    if (c > 0) store_y_bf16<GATE>(p, sm.Y[nxt], tid, b, h, t0 - kQ, rev, pv_prev, zr_prev);
+    if (!AGG && c > c0) store_y_bf16<GATE>(p, sm.Y[nxt], tid, b, h, t0 - kQ, rev, pv_prev, zr_prev);
     if (BIDIR && !rev) {
       pv_prev = pv;
-      if (c + 1 < nchunks) pv = load_partial(p, tid, b, h, t0 + kQ);
+      if (c + 1 < c1) pv = load_partial(p, tid, b, h, t0 + kQ);
     }
     if (GATE && !rev) {
       zr_prev = zr;
-      if (c + 1 < nchunks) zr = load_gate(p, tid, b, h, t0 + kQ);
+      if (c + 1 < c1) zr = load_gate(p, tid, b, h, t0 + kQ);
     }
+    if (AGG && tid == 0) cs_sum += static_cast<double>(sm.cs_end[cur]);
 
-    if (wave < 3) {
+    if (!AGG && wave < 3) {
       // causal block of C B^T, masked and decayed: M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t,
       // as the block of B C^T: register r of the lane is s = 16 msb + 4 lk + r, t = 16 mtb + li
       uint4 bb[KN], cc[KN];
@@ -718,8 +810,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
     }
 
     // inter-chunk output of the wave's block: diag(e^{cs}) C S_in^T
-    f4 y;
-    {
+    f4 y = {0.f, 0.f, 0.f, 0.f};
+    if (!AGG) {
       uint4 ca[KN], sh[KN], sl[KN];
 #pragma unroll
       for (int j = 0; j < KN; ++j) {
@@ -769,7 +861,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
     __syncthreads();  // M complete; every read of S_in done
 
     // ---- phase 2 ----
-    {
+    if (!AGG) {
       // intra-chunk output M X (M is zero above the diagonal), then + D x
       const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[0][16 * ytb + li][8 * lk]);
       const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[1][16 * ytb + li][8 * lk]);
@@ -784,26 +876,37 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.Y[cur][16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
     }
+    if (!AGG) {
 #pragma unroll
-    for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
-    if (c + 1 < nchunks) {
+      for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
+    }
+    if (c + 1 < c1) {
       cm.commit(p, bias, sm, nxt, tid);
       if (wave == kWaves - 1) chunk_decay(sm, nxt, Ah, lane, cm.dt_value(p, bias));
     }
     __syncthreads();
   };
-  for (int64_t c = 0; c < nchunks; c += 2) {
+  for (int64_t c = c0; c < c1; c += 2) {
     chunk(c, stg0, stg1);
-    if (c + 1 < nchunks) chunk(c + 1, stg1, stg0);
+    if (c + 1 < c1) chunk(c + 1, stg1, stg0);
   }
-  store_y_bf16<GATE>(p, sm.Y[(nchunks - 1) & 1], tid, b, h, (nchunks - 1) * kQ, rev, pv_prev, zr_prev);
-
-  float* const fin = rev ? p.g_first : p.h_last;
-  if (fin) {
+  if (AGG) {
+    // the range's end state from zero and its decay exponent
+    const int64_t slot = blk.range * (p.nblocks / p.nranges) + bh;
 #pragma unroll
     for (int k = 0; k < PBW; ++k)
-      *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+      *reinterpret_cast<float4*>(p.agg_S + (slot * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
           make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
+    if (tid == 0) p.agg_cs[slot] = cs_sum;
+  } else {
+    store_y_bf16<GATE>(p, sm.Y[(c1 - 1 - c0) & 1], tid, b, h, (c1 - 1) * kQ, rev, pv_prev, zr_prev);
+    float* const fin = rev ? p.g_first : p.h_last;
+    if (fin && blk.range == p.nranges - 1) {
+#pragma unroll
+      for (int k = 0; k < PBW; ++k)
+        *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+            make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
+    }
   }
   // the forward sweep reuses the LDS tiles and reads the partial just stored
   if (BIDIR && rev) __syncthreads();
@@ -826,7 +929,7 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
   if (H % G != 0) return SSM_ERR_DIM;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (P != kP || (N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
-  if (Bs * H > INT32_MAX) return SSM_ERR_DIM;
+  if (Bs * H > INT32_MAX || L >= (int64_t{1} << 36)) return SSM_ERR_DIM;
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
   const void* z = opts ? opts->z : nullptr;
   if (opts && !(opts->dt_min <= opts->dt_max)) return SSM_ERR_ARG;  // also catches NaN
@@ -852,28 +955,68 @@ int ssd_validate(const void* x, const void* dt, const float* A, const void* B, c
 // float32, into the workspace for bf16. Another wave of the same workgroup
 // reads each value in the forward sweep; the workgroup barrier that ends the
 // reverse sweep orders the stores before those loads.
-size_t ssd_bidir_ws_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
-  if (dtype != SSM_BF16) return 0;
+// How a multi-head scan splits its sequences: one workgroup per (batch row,
+// head) holds a compute unit (its LDS), so with fewer pairs than CUs each
+// sweep is cut into ranges of whole chunks (at least 8 chunks each), about one
+// workgroup per CU in all. A first pass (the AGG kernels) forms every range's
+// end state from zero and its decay exponent; the second runs every range
+// from the state folded in from the ranges before it. Nothing waits on
+// another workgroup.
+struct SsdPlan {
+  int64_t nranges, range_chunks;
+  size_t agg_bytes;  // per sweep: end states (sized for N = 128) and decay exponents
+};
+
+SsdPlan ssd_plan(int64_t Bs, int64_t L, int64_t H) {
+  SsdPlan sp{};
+  const int64_t nbh = Bs * H, nchunks = (L + kQ - 1) / kQ, ncu = device_cus();
+  sp.nranges = 1;
+  sp.range_chunks = nchunks;
+  if (ncu > 0 && nbh > 0 && nbh < ncu) {
+    const int64_t k = std::min<int64_t>(ncu / nbh, nchunks / 8);
+    if (k >= 2) {
+      sp.range_chunks = (nchunks + k - 1) / k;
+      sp.nranges = (nchunks + sp.range_chunks - 1) / sp.range_chunks;
+    }
+  }
+  if (sp.nranges > 1) {
+    const size_t slots = static_cast<size_t>(nbh * sp.nranges);
+    sp.agg_bytes = ((slots * kP * 128 * 4 + 255) & ~static_cast<size_t>(255)) + ((slots * 8 + 255) & ~static_cast<size_t>(255));
+  }
+  return sp;
+}
+
+// workspace: [float32 partials of the bidirectional bf16 scan] [split plan:
+// the forward sweep's aggregates] [the reverse sweep's aggregates]
+size_t ssd_partial_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype, bool bidir) {
+  if (!bidir || dtype != SSM_BF16) return 0;
   int64_t n;
   if (!mul_ok(Bs, L, &n) || !mul_ok(n, H, &n) || !mul_ok(n, P, &n) || n > INT64_MAX / 8) return 0;
   return (static_cast<size_t>(n) * 4 + 255) & ~static_cast<size_t>(255);
 }
 
-template <typename T, bool BIDIR, bool GATE>
+size_t ssd_ws_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype, bool bidir) {
+  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0 || Bs * H > INT32_MAX / 64) return 0;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+  const SsdPlan sp = ssd_plan(Bs, L, H);
+  return ssd_partial_bytes(Bs, L, H, P, dtype, bidir) + (bidir ? 2 : 1) * sp.agg_bytes;
+}
+
+template <typename T, bool BIDIR, bool GATE, bool AGG = false>
 void launch_ssd_kernel(const SsdArgs<T>& a, int64_t N, dim3 grid, dim3 block, hipStream_t stream) {
   if constexpr (std::is_same<T, uint16_t>::value) {
-    if (N == 128) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, BIDIR, GATE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, BIDIR, GATE>), grid, block, 0, stream, a);
+    if (N == 128) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
   } else {
-    if (N == 128) hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, BIDIR, GATE>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, BIDIR, GATE>), grid, block, 0, stream, a);
+    if (N == 128) hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
   }
 }
 
 template <typename T>
 int launch_ssd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                const float* h0, const float* g0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, float* part,
-               bool bidir, int64_t Bs, int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream) {
+               bool bidir, int64_t Bs, int64_t L, int64_t H, int64_t G, int64_t N, void* ws, hipStream_t stream) {
   SsdArgs<T> a;
   a.x = static_cast<const T*>(x);
   a.dt = static_cast<const T*>(dt);
@@ -896,8 +1039,46 @@ int launch_ssd(const void* x, const void* dt, const float* A, const void* B, con
   a.L = L;
   a.H = H;
   a.G = G;
-  a.nblocks = static_cast<int>(Bs * H);
-  const dim3 grid(static_cast<unsigned>(Bs * H)), block(64 * kWaves);
+  const SsdPlan sp = ssd_plan(Bs, L, H);
+  a.nranges = static_cast<int>(sp.nranges);
+  a.range_chunks = sp.range_chunks;
+  a.sweep_sel = -1;
+  a.agg_S = nullptr;
+  a.agg_cs = nullptr;
+  a.nblocks = static_cast<int>(Bs * H * sp.nranges);
+  const dim3 grid(static_cast<unsigned>(a.nblocks)), block(64 * kWaves);
+  if (sp.nranges > 1) {
+    // the sweeps' aggregates (forward, then reverse), then every range from
+    // its folded entering state; the bidirectional scan stores the reverse
+    // sweep's partials in a launch of their own before the forward sweep
+    // reads them
+    const size_t slots = static_cast<size_t>(Bs * H * sp.nranges);
+    const size_t s_bytes = (slots * kP * 128 * 4 + 255) & ~static_cast<size_t>(255);
+    char* w = static_cast<char*>(ws) + ssd_partial_bytes(Bs, L, H, kP, std::is_same<T, float>::value ? SSM_F32 : SSM_BF16, bidir);
+    const int64_t nbh = Bs * H, PN = kP * N;
+    const dim3 jgrid(static_cast<unsigned>((nbh * PN + 255) / 256)), jblock(256);
+    SsdArgs<T> fw = a, rv = a;
+    fw.agg_S = reinterpret_cast<float*>(w);
+    fw.agg_cs = reinterpret_cast<double*>(w + s_bytes);
+    fw.sweep_sel = 1;
+    launch_ssd_kernel<T, false, false, true>(fw, N, grid, block, stream);
+    hipLaunchKernelGGL(ssd_join_kernel, jgrid, jblock, 0, stream, fw.agg_S, fw.agg_cs, h0, nbh, sp.nranges, PN);
+    if (bidir) {
+      rv.agg_S = reinterpret_cast<float*>(w + sp.agg_bytes);
+      rv.agg_cs = reinterpret_cast<double*>(w + sp.agg_bytes + s_bytes);
+      rv.sweep_sel = 0;
+      launch_ssd_kernel<T, false, false, true>(rv, N, grid, block, stream);
+      hipLaunchKernelGGL(ssd_join_kernel, jgrid, jblock, 0, stream, rv.agg_S, rv.agg_cs, g0, nbh, sp.nranges, PN);
+      if (rv.z) launch_ssd_kernel<T, true, true>(rv, N, grid, block, stream);
+      else launch_ssd_kernel<T, true, false>(rv, N, grid, block, stream);
+      if (fw.z) launch_ssd_kernel<T, true, true>(fw, N, grid, block, stream);
+      else launch_ssd_kernel<T, true, false>(fw, N, grid, block, stream);
+    } else {
+      if (fw.z) launch_ssd_kernel<T, false, true>(fw, N, grid, block, stream);
+      else launch_ssd_kernel<T, false, false>(fw, N, grid, block, stream);
+    }
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+  }
   if (bidir) {
     if (a.z) launch_ssd_kernel<T, true, true>(a, N, grid, block, stream);
     else launch_ssd_kernel<T, true, false>(a, N, grid, block, stream);
@@ -915,26 +1096,54 @@ int ssd_empty(const float* h0, const float* g0, float* h_last, float* g_first, i
   return ok ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
+// The workspace may not overlap any argument.
+int ssd_check_workspace(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                        const float* h0, const float* g0, const ssm_scan_options* opts, const void* y,
+                        const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P,
+                        int64_t G, int64_t N, int dtype, const void* workspace, size_t workspace_bytes, size_t need) {
+  if (need == 0) return SSM_OK;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SSM_ERR_WORKSPACE;
+  const int64_t es = dtype == SSM_F32 ? 4 : 2;
+  const int64_t seq = Bs * L * H * P, hd = Bs * L * H, bc = Bs * L * G * N, state = Bs * H * P * N;
+  const Range ws = rng(workspace, static_cast<int64_t>(need));
+  const float* dt_bias = opts ? opts->dt_bias : nullptr;
+  const void* z = opts ? opts->z : nullptr;
+  const Range args[] = {rng(x, seq * es), rng(dt, hd * es), rng(A, H * 4), rng(B, bc * es), rng(C, bc * es),
+                        rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(g0, g0 ? state * 4 : 0),
+                        rng(y, seq * es),
+                        rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0),
+                        rng(dt_bias, dt_bias ? H * 4 : 0), rng(z, z ? seq * es : 0)};
+  for (const Range& r : args)
+    if (r.hi > r.lo && overlap(ws, r)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
 }  // namespace
+
+extern "C" size_t ssm_ssd_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
+  return ssd_ws_bytes(Bs, L, H, P, dtype, false);
+}
 
 extern "C" int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                            const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
                            int64_t Bs, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
-                           void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = ssd_validate(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (Bs == 0 || L == 0) return ssd_empty(h0, nullptr, h_last, nullptr, Bs * H * P * N, st);
+  rc = ssd_check_workspace(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, H, P, G, N, dtype,
+                           workspace, workspace_bytes, ssd_ws_bytes(Bs, L, H, P, dtype, false));
+  if (rc != SSM_OK) return rc;
   if (dtype == SSM_F32)
     return launch_ssd<float>(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G, N,
-                             st);
+                             workspace, st);
   return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, nullptr, false, Bs, L, H, G,
-                              N, st);
+                              N, workspace, st);
 }
 
 extern "C" size_t ssm_ssd_bidir_workspace_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype) {
-  if (Bs <= 0 || L <= 0 || H <= 0 || P <= 0) return 0;
-  return ssd_bidir_ws_bytes(Bs, L, H, P, dtype);
+  return ssd_ws_bytes(Bs, L, H, P, dtype, true);
 }
 
 extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
@@ -942,27 +1151,16 @@ extern "C" int ssm_ssd_bidir_fwd(const void* x, const void* dt, const float* A, 
                                  void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t H, int64_t P,
                                  int64_t G, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  const int rc = ssd_validate(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
+  int rc = ssd_validate(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (Bs == 0 || L == 0) return ssd_empty(h0, g0, h_last, g_first, Bs * H * P * N, st);
+  rc = ssd_check_workspace(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, H, P, G, N, dtype, workspace,
+                           workspace_bytes, ssd_ws_bytes(Bs, L, H, P, dtype, true));
+  if (rc != SSM_OK) return rc;
   if (dtype == SSM_F32)
     return launch_ssd<float>(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, static_cast<float*>(y), true, Bs, L,
-                             H, G, N, st);
-  const size_t need = ssd_bidir_ws_bytes(Bs, L, H, P, dtype);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SSM_ERR_WORKSPACE;
-  // the workspace may not overlap any argument
-  int64_t seq = Bs * L * H * P, hd = Bs * L * H, bc = Bs * L * G * N, state = Bs * H * P * N;
-  const Range ws = rng(workspace, static_cast<int64_t>(need));
-  const float* dt_bias = opts ? opts->dt_bias : nullptr;
-  const void* z = opts ? opts->z : nullptr;
-  const Range args[] = {rng(x, seq * 2), rng(dt, hd * 2), rng(A, H * 4), rng(B, bc * 2), rng(C, bc * 2),
-                        rng(D, D ? H * 4 : 0), rng(h0, h0 ? state * 4 : 0), rng(g0, g0 ? state * 4 : 0),
-                        rng(y, seq * 2),
-                        rng(h_last, h_last ? state * 4 : 0), rng(g_first, g_first ? state * 4 : 0),
-                        rng(dt_bias, dt_bias ? H * 4 : 0), rng(z, z ? seq * 2 : 0)};
-  for (const Range& r : args)
-    if (r.hi > r.lo && overlap(ws, r)) return SSM_ERR_ALIAS;
+                             H, G, N, workspace, st);
   return launch_ssd<uint16_t>(x, dt, A, B, C, D, h0, g0, opts, y, h_last, g_first, static_cast<float*>(workspace),
-                              true, Bs, L, H, G, N, st);
+                              true, Bs, L, H, G, N, workspace, st);
 }

@@ -244,7 +244,7 @@ def ssd(**kw):
     args.update(opts=None, Bs=2, L=64, H=4, P=64, G=1, N=128, dtype=ssm.SSM_F32)
     args.update(kw)
     return ssm.lib().ssm_ssd_fwd(*[args[n] for n in SSD_PTRS], args["Bs"], args["L"], args["H"], args["P"],
-                                 args["G"], args["N"], args["dtype"], None)
+                                 args["G"], args["N"], args["dtype"], args.get("ws"), args.get("ws_bytes", 0), None)
 
 
 @pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
@@ -291,9 +291,12 @@ def ssd_bidir(**kw):
 
 def test_ssd_bidir_workspace_size():
     # the reverse sweep's float32 partial output, one value per element of y
+    # (no device here: no split plan, so nothing else)
     assert ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16) >= 4 * 2 * 64 * 4 * 64
     assert ssm.ssm_ssd_bidir_workspace_bytes(2, 64, 4, 64, ssm.SSM_F32) == 0
     assert ssm.ssm_ssd_bidir_workspace_bytes(0, 64, 4, 64, ssm.SSM_BF16) == 0
+    assert ssm.ssm_ssd_workspace_bytes(2, 64, 4, 64, ssm.SSM_F32) == 0
+    assert ssm.ssm_ssd_workspace_bytes(2, 64, 4, 64, ssm.SSM_BF16) == 0
 
 
 @pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])

@@ -201,3 +201,35 @@ def test_empty_inputs(Bs, L, dtype):
     assert_close("y bidir", y, y_ref, TOL[dtype])
     assert_close("h_last bidir", h, h_ref, TOL["f32"])
     assert_close("g_first", g, g_ref, TOL["f32"])
+
+
+# ---- split sequences: fewer (batch row, head) pairs than compute units -------
+# Each sweep is cut into ranges of whole chunks: a first pass forms every
+# range's end state from zero, a small kernel folds them into the state
+# entering each range (from h0 / g0), and every range then runs from it.
+
+@pytest.mark.parametrize("Bs,L,H,G,N,dtype,bidir", [
+    (1, 3000, 3, 1, 128, "f32", False), (1, 3000, 3, 1, 128, "bf16", False), (2, 2100, 2, 2, 64, "bf16", False),
+    (1, 2600, 2, 1, 64, "f32", False), (1, 3000, 3, 1, 128, "f32", True), (1, 2600, 4, 2, 128, "bf16", True)])
+def test_split_sequence(Bs, L, H, G, N, dtype, bidir):
+    import state_space_model_selective_amd as ssm
+    code = ssm.SSM_F32 if dtype == "f32" else ssm.SSM_BF16
+    need = (ssm.ssm_ssd_bidir_workspace_bytes if bidir else ssm.ssm_ssd_workspace_bytes)(Bs, L, H, 64, code)
+    plain = -(-Bs * L * H * 64 * 4 // 256) * 256 if (bidir and dtype == "bf16") else 0
+    assert need > plain, "this shape is expected to split its sequences"
+    seed = L + H + N
+    log("ssd split case Bs=%d L=%d H=%d G=%d N=%d %s bidir=%s" % (Bs, L, H, G, N, dtype, bidir))
+    inp = synth.make_ssd_inputs(Bs, L, H, 64, G, N, dtype, seed=seed)
+    h0 = synth.normal(seed, 95, (Bs, H, 64, N))
+    g0 = synth.normal(seed, 96, (Bs, H, 64, N)) if bidir else None
+    out = run_gpu_ssd(inp, h0=h0, want_h=True, want_g=bidir, bidir=bidir, g0=g0)
+    ref = oracle.ssd(**inp, h0=h0, g0=g0, bidir=bidir, want_h_last=True, want_g_first=bidir)
+    assert_close("y", out[0], ref[0], TOL[dtype])
+    assert_close("h_last", out[1], ref[1], TOL["f32"])
+    if bidir:
+        assert_close("g_first", out[2], ref[2], TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype,bidir", [("f32", False), ("bf16", False), ("bf16", True)])
+def test_split_sequence_with_options(dtype, bidir):
+    check_options(1, 2500, 2, 1, 128, dtype, seed=64, bidir=bidir, h0=True)
