@@ -162,3 +162,24 @@ def test_backward_split_sweep_graph(bidir):
     replay_check("backward, split sweep, bidir=%s" % bidir, lambda: fn(
         t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=out, workspace=ws, want_dh0=True),
         [out[k] for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dh0")])
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_multi_head_split_sequence_graph(bidir):
+    # the aggregate pass, the join kernel and the ranges (the bidirectional
+    # scan with its reverse sweep in a launch of its own)
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, H, P, G, N = 1, 2600, 2, 64, 1, 128
+    dtype = "bf16" if bidir else "f32"
+    code = ssm.SSM_BF16 if bidir else ssm.SSM_F32
+    need = (ssm.ssm_ssd_bidir_workspace_bytes if bidir else ssm.ssm_ssd_workspace_bytes)(Bs, L, H, P, code)
+    assert need > (Bs * L * H * P * 4 if bidir else 0), "this shape should split its sequences"
+    dev = torch.device("cuda:0")
+    t = to_device(synth.make_ssd_inputs(Bs, L, H, P, G, N, dtype, seed=77), dev)
+    y = torch.empty_like(t["x"])
+    h = torch.empty((Bs, H, P, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    fn = ssm.ssm_ssd_bidir_fwd if bidir else ssm.ssm_ssd_fwd
+    replay_check("multi-head split sequence, bidir=%s" % bidir, lambda: fn(
+        t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=y, h_last=h, workspace=ws), [y, h])
