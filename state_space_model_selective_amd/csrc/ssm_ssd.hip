@@ -42,6 +42,10 @@ namespace {
 constexpr int kQ = 32;       // chunk length
 constexpr int kP = 64;       // head channels (headdim)
 constexpr int kWaves = 8;
+// bf16 kernel: compute waves and staging waves
+constexpr int kMainBf = 8;
+constexpr int kStageBf = 4;
+constexpr int kWavesBf = kMainBf + kStageBf;
 
 template <typename T>
 struct SsdArgs {
@@ -134,6 +138,13 @@ __global__ void ssd_join_kernel(float* agg_S, const double* agg_cs, const float*
 template <typename T>
 __device__ __forceinline__ float ssd_step(const SsdArgs<T>& p, float d, const float* bias) {
   return p.dt_pre ? map_step(d, bias, p.dt_softplus, p.dt_min, p.dt_max) : d;
+}
+// the same with the head's bias held in a register (0 when there is none)
+template <typename T>
+__device__ __forceinline__ float ssd_step_v(const SsdArgs<T>& p, float d, float bias) {
+  if (!p.dt_pre) return d;
+  if (p.dt_bias) d += bias;
+  return map_step(d, nullptr, p.dt_softplus, p.dt_min, p.dt_max);
 }
 
 // gate of 4 consecutive head channels of the row at time t (zero-filled bits
@@ -494,18 +505,25 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 // n-contiguous tiles (C[t][n], B[s][n], S[p][n]); products over the chunk's
 // steps read s-contiguous ones (M[t][s], x transposed to Xt[p][s]).
 //
-// Per chunk, two barriers:
-//   phase 1  store y of the previous chunk; the three causal 16 x 16 blocks
-//            of C B^T (waves 0..2, computed as B C^T so that a lane holds 4
-//            consecutive s of one t) -> masked, decayed M (bf16 pair); every
-//            wave: its 16 x 16 block of diag(e^{cs}) C S_in^T and the update
-//            of its state blocks, S^T = e^{cs_end} S^T + (w B)^T X (so that a
-//            lane holds 4 consecutive n of one p)
-//   phase 2  M X added to the output block, + D x -> Y (float32, by chunk
-//            parity); bf16 pair copy of the new state (8-byte stores); the
-//            next chunk's tiles (prefetched into registers during phase 1);
-//            its decays by the last wave, a prefix sum over the lanes (DPP)
-//            of the step sizes that wave loaded
+// Twelve waves: eight compute waves own the state and the output blocks and
+// run only products over LDS tiles; four staging waves move data and form
+// each chunk's masked C B^T, so that this work overlaps the products instead
+// of adding to them. Two of the staging waves only load and commit tiles
+// (16-byte global loads into registers, one chunk ahead), the other two only
+// store y; a wave that waits for its loads then has no stores outstanding
+// (stores count in the same counter). Per chunk, two barriers:
+//   phase 1  compute waves: their 16 x 16 block of diag(e^{cs}) C S_in^T and
+//            the update of their state blocks, S^T = e^{cs_end} S^T +
+//            (w B)^T X (so that a lane holds 4 consecutive n of one p).
+//            Staging waves: the chunk's three causal 16 x 16 blocks of C B^T
+//            (computed as B C^T so that a lane holds 4 consecutive s of one
+//            t) -> masked, decayed M (bf16 pair); store y of the previous
+//            chunk; issue the loads of the next chunk
+//   phase 2  compute waves: M X added to the output block, + D x -> Y
+//            (float32, by chunk parity); bf16 pair copy of the new state
+//            (8-byte stores). Loading waves: commit the next chunk's tiles
+//            and form its decays (the last loading wave: a prefix sum over
+//            the lanes (DPP) of the step sizes it loaded)
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -547,7 +565,7 @@ struct alignas(16) SsdSmemBf {
   uint16_t B[2][kQ][NP];   // B chunk [s][n]
   uint16_t Xt[2][kP][TP];  // x chunk, transposed [p][s]
   uint16_t S[2][kP][NP];   // state entering the chunk [p][n]: high, low bf16 part
-  uint16_t M[2][kQ][TP];   // masked, decayed C B^T [t][s]: high, low part
+  uint16_t M[2][2][kQ][TP];  // masked, decayed C B^T [t][s] by chunk parity: high, low part
   float Y[2][kQ][kP + 4];  // y of a chunk (with D x), by chunk parity
   float dt[2][kQ];
   float cs[2][kQ];         // A * inclusive cumulative dt within the chunk
@@ -556,67 +574,85 @@ struct alignas(16) SsdSmemBf {
   float cs_end[2];
 };
 
-template <int N>
+template <int N, int NT>
 struct SsdStagerBf {
-  static constexpr int kXT = kQ * kP / 4 / (64 * kWaves);  // x tasks per thread
-  static constexpr int kBT = kQ * N / 4 / (64 * kWaves);   // B (and C) tasks per thread
-  uint2 rx[kXT], rb[kBT], rc[kBT];
+  static constexpr int kXT = kQ * kP / 8 / NT;  // x tasks (8 head channels of a row) per loading thread
+  static constexpr int kBT = kQ * N / 8 / NT;   // B (and C) tasks (8 states of a row) per loading thread
+  static constexpr int kDtWave = NT / 64 - 1;   // the loading wave whose lanes 0 .. kQ-1 load the step sizes
+  static constexpr int kBRows = NT / (N / 8);   // rows between a thread's B tasks
+  static_assert(NT % kQ == 0 && NT % (N / 8) == 0 && kXT >= 1 && kBT >= 1, "task split");
+  uint4 rx[kXT], rb[kBT], rc[kBT];
   uint16_t rdt;
-  bool vx[kXT], vb[kBT], vdt;
+  bool vx, vb[kBT], vdt;
+  // element offsets of the thread's first task rows in the next chunk to
+  // load; sbr: from one B row to the next in the sweep's order (negative in
+  // a reverse sweep); sx, sb, sd: from one chunk to the next
+  int64_t ox, ob, od;
+  int64_t sbr, sx, sb, sd;
 
-  // rows tau0 .. tau0 + kQ - 1 of the sweep (rev: time L - 1 - tau)
-  __device__ __forceinline__ void load(const SsdArgs<uint16_t>& p, int tid, int64_t b, int64_t h, int64_t g,
+  // the first chunk to load starts at sweep row tau0 (st: the loading
+  // thread's index, 0 .. NT-1). Task k of x is row st % kQ, head channels
+  // 8 (st / kQ + k NT / kQ) ..; task k of B and C is row st / (N / 8) +
+  // k kBRows, states 8 (st % (N / 8)) ..
+  __device__ __forceinline__ void init(const SsdArgs<uint16_t>& p, int st, int64_t b, int64_t h, int64_t g,
                                        int64_t tau0, bool rev) {
+    const int64_t dir = rev ? -1 : 1;
+    ox = ((b * p.L + sweep_time(tau0 + st % kQ, p.L, rev)) * p.H + h) * kP + (st / kQ) * 8;
+    ob = ((b * p.L + sweep_time(tau0 + st / (N / 8), p.L, rev)) * p.G + g) * N + (st % (N / 8)) * 8;
+    od = (b * p.L + sweep_time(tau0 + (st & (kQ - 1)), p.L, rev)) * p.H + h;
+    sbr = dir * p.G * N;
+    sx = dir * kQ * p.H * kP;
+    sb = kQ * sbr;
+    sd = dir * kQ * p.H;
+  }
+
+  // the chunk of sweep rows tau0 .. tau0 + kQ - 1 (the next one after the
+  // previous load); rows at or past L are not read
+  __device__ __forceinline__ void load(const SsdArgs<uint16_t>& p, int st, int64_t tau0) {
+    vx = tau0 + st % kQ < p.L;
 #pragma unroll
-    for (int k = 0; k < kXT; ++k) {
-      // rows along the lanes, so that the transposed stores of the commit
-      // fall on distinct banks
-      const int u = tid + k * 64 * kWaves, row = u % kQ, c4 = (u / kQ) * 4;
-      const int64_t tau = tau0 + row;
-      vx[k] = tau < p.L;
-      const int64_t t = sweep_time(vx[k] ? tau : p.L - 1, p.L, rev);
-      rx[k] = *reinterpret_cast<const uint2*>(p.x + ((b * p.L + t) * p.H + h) * kP + c4);
-    }
+    for (int k = 0; k < kXT; ++k)
+      rx[k] = vx ? *reinterpret_cast<const uint4*>(p.x + ox + k * (NT / kQ) * 8) : make_uint4(0u, 0u, 0u, 0u);
+    ox += sx;
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
-      const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
-      const int64_t tau = tau0 + row;
-      vb[k] = tau < p.L;
-      const int64_t off = ((b * p.L + sweep_time(vb[k] ? tau : p.L - 1, p.L, rev)) * p.G + g) * N + c4;
-      rb[k] = *reinterpret_cast<const uint2*>(p.B + off);
-      rc[k] = *reinterpret_cast<const uint2*>(p.C + off);
+      vb[k] = tau0 + st / (N / 8) + k * kBRows < p.L;
+      const int64_t off = ob + k * kBRows * sbr;
+      rb[k] = vb[k] ? *reinterpret_cast<const uint4*>(p.B + off) : make_uint4(0u, 0u, 0u, 0u);
+      rc[k] = vb[k] ? *reinterpret_cast<const uint4*>(p.C + off) : make_uint4(0u, 0u, 0u, 0u);
     }
-    // step sizes: lanes 0 .. kQ-1 of the last wave
-    const int64_t td = tau0 + (tid & (kQ - 1));
-    vdt = (tid >> 6) == kWaves - 1 && (tid & 63) < kQ && td < p.L;
-    rdt = p.dt[(b * p.L + sweep_time(td < p.L ? td : p.L - 1, p.L, rev)) * p.H + h];
+    ob += sb;
+    vdt = (st >> 6) == kDtWave && (st & 63) < kQ && tau0 + (st & (kQ - 1)) < p.L;
+    rdt = vdt ? p.dt[od] : uint16_t{0};
+    od += sd;
   }
 
   // step size of this lane's row (zero past L or outside the dt task)
   // (rows past L keep dt = 0 whatever the options would make of it)
-  __device__ __forceinline__ float dt_value(const SsdArgs<uint16_t>& p, const float* bias) const {
-    return vdt ? ssd_step(p, to_f32(rdt), bias) : 0.f;
+  __device__ __forceinline__ float dt_value(const SsdArgs<uint16_t>& p, float bias) const {
+    return vdt ? ssd_step_v(p, to_f32(rdt), bias) : 0.f;
   }
 
   // rows at or past L are zero (dt = 0: a = 1 and no input)
-  __device__ __forceinline__ void commit(const SsdArgs<uint16_t>& p, const float* bias, SsdSmemBf<N>& sm, int buf,
-                                         int tid) const {
+  __device__ __forceinline__ void commit(const SsdArgs<uint16_t>& p, float bias, SsdSmemBf<N>& sm, int buf,
+                                         int st) const {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
-      const int u = tid + k * 64 * kWaves, row = u % kQ, c4 = (u / kQ) * 4;
-      const uint2 v = vx[k] ? rx[k] : make_uint2(0u, 0u);
-      sm.Xt[buf][c4 + 0][row] = static_cast<uint16_t>(v.x);
-      sm.Xt[buf][c4 + 1][row] = static_cast<uint16_t>(v.x >> 16);
-      sm.Xt[buf][c4 + 2][row] = static_cast<uint16_t>(v.y);
-      sm.Xt[buf][c4 + 3][row] = static_cast<uint16_t>(v.y >> 16);
+      const int row = st % kQ, c8 = (st / kQ + k * (NT / kQ)) * 8;
+      const uint32_t w[4] = {rx[k].x, rx[k].y, rx[k].z, rx[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sm.Xt[buf][c8 + 2 * j][row] = static_cast<uint16_t>(w[j]);
+        sm.Xt[buf][c8 + 2 * j + 1][row] = static_cast<uint16_t>(w[j] >> 16);
+      }
     }
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
-      const int u = tid + k * 64 * kWaves, row = u / (N / 4), c4 = (u % (N / 4)) * 4;
-      *reinterpret_cast<uint2*>(&sm.B[buf][row][c4]) = vb[k] ? rb[k] : make_uint2(0u, 0u);
-      *reinterpret_cast<uint2*>(&sm.C[buf][row][c4]) = vb[k] ? rc[k] : make_uint2(0u, 0u);
+      const int row = st / (N / 8) + k * kBRows, c8 = (st % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(&sm.B[buf][row][c8]) = rb[k];
+      *reinterpret_cast<uint4*>(&sm.C[buf][row][c8]) = rc[k];
     }
-    if ((tid >> 6) == kWaves - 1 && (tid & 63) < kQ) sm.dt[buf][tid & 63] = dt_value(p, bias);
+    if ((st >> 6) == kDtWave && (st & 63) < kQ) sm.dt[buf][st & 63] = dt_value(p, bias);
   }
 };
 
@@ -650,30 +686,36 @@ __device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah,
   }
 }
 
-// rows t0 .. t0 + kQ - 1 of the sweep (those before L), 4 head channels per
-// thread: y (+ the reverse partial pv), times the gate -> y, or, in the
-// reverse sweep, the float32 partial -> part
+// rows t0 .. t0 + kQ - 1 of the sweep (those before L) by the 128 threads
+// of the store waves, rows st / 16 + 8 i (i < 4), 4 head channels each: y
+// (+ the reverse partial pv), times the gate -> y, or, in the reverse sweep,
+// the float32 partial -> part
 template <bool GATE>
-__device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const float (&Y)[kQ][kP + 4], int tid,
-                                             int64_t b, int64_t h, int64_t t0, bool rev, float4 pv, uint2 zr) {
-  const int t = tid >> 4, c4 = (tid & 15) * 4;
-  if (t0 + t < p.L) {
-    const float4 v = *reinterpret_cast<const float4*>(&Y[t][c4]);
-    const int64_t row = (b * p.L + sweep_time(t0 + t, p.L, rev)) * p.H + h;
-    if (rev)
-      *reinterpret_cast<float4*>(p.part + row * kP + c4) = v;
-    else {
-      float4 o = make_float4(v.x + pv.x, v.y + pv.y, v.z + pv.z, v.w + pv.w);
-      if (GATE) o = gated(o, Vec4<uint16_t>::widen(zr));
-      *reinterpret_cast<uint2*>(p.y + row * kP + c4) = make_uint2(pack_bf16(o.x, o.y), pack_bf16(o.z, o.w));
+__device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const float (&Y)[kQ][kP + 4], int st,
+                                             int64_t b, int64_t h, int64_t t0, bool rev, const float4 (&pv)[4],
+                                             const uint2 (&zr)[4]) {
+  const int c4 = (st & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = (st >> 4) + 8 * i;
+    if (t0 + t < p.L) {
+      const float4 v = *reinterpret_cast<const float4*>(&Y[t][c4]);
+      const int64_t row = (b * p.L + sweep_time(t0 + t, p.L, rev)) * p.H + h;
+      if (rev)
+        *reinterpret_cast<float4*>(p.part + row * kP + c4) = v;
+      else {
+        float4 o = make_float4(v.x + pv[i].x, v.y + pv[i].y, v.z + pv[i].z, v.w + pv[i].w);
+        if (GATE) o = gated(o, Vec4<uint16_t>::widen(zr[i]));
+        *reinterpret_cast<uint2*>(p.y + row * kP + c4) = make_uint2(pack_bf16(o.x, o.y), pack_bf16(o.z, o.w));
+      }
     }
   }
 }
 
-// the reverse partial of sweep rows t0 .. t0 + kQ - 1 for this thread's store
-__device__ __forceinline__ float4 load_partial(const SsdArgs<uint16_t>& p, int tid, int64_t b, int64_t h,
+// the reverse partial of sweep row t0 + st / 16 for a store thread
+__device__ __forceinline__ float4 load_partial(const SsdArgs<uint16_t>& p, int st, int64_t b, int64_t h,
                                                int64_t t0) {
-  const int t = tid >> 4, c4 = (tid & 15) * 4;
+  const int t = st >> 4, c4 = (st & 15) * 4;
   if (t0 + t >= p.L) return make_float4(0.f, 0.f, 0.f, 0.f);
   return *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + t) * p.H + h) * kP + c4);
 }
@@ -688,116 +730,176 @@ __device__ __forceinline__ void store_state_bf16(SsdSmemBf<N>& sm, int pp, int n
   *reinterpret_cast<uint2*>(&sm.S[1][pp][n0]) = make_uint2(l01, l23);
 }
 
-template <int N, bool BIDIR, bool GATE, bool AGG = false>
-__global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs<uint16_t> p) {
-  static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
-  static_assert(N == 64 || N == 128, "state sizes");
-  static_assert(!(AGG && (BIDIR || GATE)), "the aggregate pass runs one sweep, no gate");
+// One sweep of the bf16 kernel over the chunks [blk.c0, blk.c1) of a
+// (batch row, head): REV runs in decreasing time (chunk k of the sweep holds
+// times L-1-32k .. L-32-32k) from g0, else in increasing time from h0.
+template <int N, bool BIDIR, bool GATE, bool AGG, bool REV>
+__device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSmemBf<N>& sm, const SsdBlock& blk,
+                                               float Dfwd, float bias) {
   constexpr int NB = N / 16;       // state column blocks
-  constexpr int PBW = 4 * NB / 8;  // state row blocks per wave (its column block is wave % NB)
+  constexpr int PBW = 4 * NB / 8;  // state row blocks per compute wave (its column block is wave % NB)
   constexpr int KN = N / 32;       // products over n: instructions per 16 x 16 block
-
-  __shared__ SsdSmemBf<N> sm;
-
+  constexpr bool rev = REV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lk = lane >> 4;
-  const SsdBlock blk = ssd_block(p);
   const int64_t bh = blk.bh;
   const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t g = h / (p.H / p.G);
   const float Ah = p.A[h];
-  const float Dfwd = p.D ? p.D[h] : 0.f;
-  const float* const bias = p.dt_bias ? p.dt_bias + h : nullptr;
-  const int64_t c0 = blk.c0, c1 = blk.c1;  // the chunks of this workgroup's range
-
-  const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
-  const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
-  const int mtb = wave == 0 ? 0 : 1, msb = wave == 2 ? 1 : 0;  // causal C B^T block of waves 0..2
-
-  // the block t < 16, s >= 16 of M stays zero (future steps)
-  for (int i = tid; i < 2 * kQ * SsdSmemBf<N>::TP; i += 64 * kWaves) (&sm.M[0][0][0])[i] = 0;
-
-  // BIDIR: a reverse sweep (zero initial state, no D x) storing a float32
-  // partial, then the forward sweep adding it (a split sequence runs them in
-  // separate launches: sweep_sel)
-  for (int sweep = 0; sweep < (BIDIR ? 2 : 1); ++sweep) {
-  if (BIDIR && p.sweep_sel >= 0 && sweep != p.sweep_sel) continue;  // (uniform)
-  const bool rev = BIDIR ? sweep == 0 : p.sweep_sel == 0;
+  const int64_t c0 = blk.c0, c1 = blk.c1;
   const float* const init = rev ? p.g0 : p.h0;  // the sweep's entering state (null: zero)
   const float Dh = rev ? 0.f : Dfwd;
 
-  // st[k][r] = S[p][n], p = 16 (spb + k) + li, n = 16 snb + 4 lk + r
-  f4 st[PBW];
+  // Both roles run the same chunk loop with the same two barriers per chunk.
+  if (wave < kMainBf) {
+    // ================= compute waves =================
+    const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
+    const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
+
+    // st[k][r] = S[p][n], p = 16 (spb + k) + li, n = 16 snb + 4 lk + r
+    f4 st[PBW];
 #pragma unroll
-  for (int k = 0; k < PBW; ++k) {
-    const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
+    for (int k = 0; k < PBW; ++k) {
+      const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = 0.f;
-      if (!AGG) {
-        // a range of a split sequence starts from its joined entering state
-        if (p.nranges > 1) v = p.agg_S[((blk.range * (p.nblocks / p.nranges) + bh) * kP + pp) * N + n0 + r];
-        else if (init) v = init[((b * p.H + h) * kP + pp) * N + n0 + r];
+      for (int r = 0; r < 4; ++r) {
+        float v = 0.f;
+        if (!AGG) {
+          // a range of a split sequence starts from its joined entering state
+          if (p.nranges > 1) v = p.agg_S[((blk.range * (p.nblocks / p.nranges) + bh) * kP + pp) * N + n0 + r];
+          else if (init) v = init[((b * p.H + h) * kP + pp) * N + n0 + r];
+        }
+        st[k][r] = v;
       }
-      st[k][r] = v;
+      if (!AGG) store_state_bf16(sm, pp, n0, st[k]);
     }
-    if (!AGG) store_state_bf16(sm, pp, n0, st[k]);
-  }
-  double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
+    double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
+    __syncthreads();
 
-  // two stagers: while chunk c is computed, chunk c + 1 waits in one of them
-  // (loaded during chunk c - 1, committed at the end of chunk c) and chunk
-  // c + 2 is loaded into the other
-  SsdStagerBf<N> stg0, stg1;
-  stg0.load(p, tid, b, h, g, c0 * kQ, rev);
-  stg0.commit(p, bias, sm, 0, tid);
-  if (wave == kWaves - 1) chunk_decay(sm, 0, Ah, lane, stg0.dt_value(p, bias));
-  if (c0 + 1 < c1) stg1.load(p, tid, b, h, g, (c0 + 1) * kQ, rev);
-  // forward sweep of the bidirectional scan: the reverse partial of the chunk
-  // whose output is stored next, one chunk ahead of its store
-  float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pv_prev = pv;
-  if (BIDIR && !rev) pv = load_partial(p, tid, b, h, c0 * kQ);
-  // the gate of those rows, the same way (forward sweep only)
-  uint2 zr = make_uint2(0u, 0u), zr_prev = zr;
-  if (GATE && !rev) zr = load_gate(p, tid, b, h, c0 * kQ);
-  __syncthreads();
+    for (int64_t c = c0; c < c1; ++c) {
+      const int cur = (c - c0) & 1;
+      // ---- phase 1 ----
+      if (AGG && tid == 0) cs_sum += static_cast<double>(sm.cs_end[cur]);
 
-  // one chunk: ld receives chunk c + 2, cm holds chunk c + 1
-  auto chunk = [&](const int64_t c, SsdStagerBf<N>& ld, const SsdStagerBf<N>& cm) {
-    const int cur = (c - c0) & 1, nxt = cur ^ 1;
-    const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
-    if (c + 2 < c1) ld.load(p, tid, b, h, g, t0 + 2 * kQ, rev);
+      // inter-chunk output of the wave's block: diag(e^{cs}) C S_in^T
+      f4 y = {0.f, 0.f, 0.f, 0.f};
+      if (!AGG) {
+        uint4 ca[KN], sh[KN], sl[KN];
+#pragma unroll
+        for (int j = 0; j < KN; ++j) {
+          ca[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * ytb + li][32 * j + 8 * lk]);
+          sh[j] = *reinterpret_cast<const uint4*>(&sm.S[0][16 * ypb + li][32 * j + 8 * lk]);
+          sl[j] = *reinterpret_cast<const uint4*>(&sm.S[1][16 * ypb + li][32 * j + 8 * lk]);
+        }
+        f4 a = {0.f, 0.f, 0.f, 0.f}, a2 = a;
+#pragma unroll
+        for (int j = 0; j < KN; ++j) {
+          a = mfma_bf16(ca[j], sh[j], a);
+          a2 = mfma_bf16(ca[j], sl[j], a2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = (a[r] + a2[r]) * sm.ecs[cur][16 * ytb + 4 * lk + r];
+      }
 
-    // ---- phase 1 ----
-    if (!AGG && c > c0) store_y_bf16<GATE>(p, sm.Y[nxt], tid, b, h, t0 - kQ, rev, pv_prev, zr_prev);
-    if (BIDIR && !rev) {
-      pv_prev = pv;
-      if (c + 1 < c1) pv = load_partial(p, tid, b, h, t0 + kQ);
+      // state update of the wave's blocks: S^T = e^{cs_end} S^T + (w B)^T X
+      {
+        const float dec = __expf(sm.cs_end[cur]);
+#pragma unroll
+        for (int k = 0; k < PBW; ++k) st[k] *= dec;
+        // operand A: (w B)^T[n][s] = w_s B[s][n] for n = 16 snb + li. The sum
+        // over s does not depend on which k slot holds which s as long as both
+        // operands agree: the lane's 8 slots hold s = 4 lk .. 4 lk + 3 and
+        // 16 + 4 lk .. 16 + 4 lk + 3, so that the lanes' column reads of B fall
+        // on rows 4 apart (distinct LDS banks).
+        uint32_t bhi[4], blo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s0 = (i < 2 ? 0 : 16) + 4 * lk + 2 * (i & 1);
+          const float b0 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0][16 * snb + li]) << 16);
+          const float b1 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0 + 1][16 * snb + li]) << 16);
+          split_pack_bf16(b0 * sm.w[cur][s0], b1 * sm.w[cur][s0 + 1], bhi[i], blo[i]);
+        }
+        const uint4 boh = make_uint4(bhi[0], bhi[1], bhi[2], bhi[3]), bol = make_uint4(blo[0], blo[1], blo[2], blo[3]);
+#pragma unroll
+        for (int k = 0; k < PBW; ++k) {
+          // operand B: X[s][p] = Xt[p][s], p = 16 (spb + k) + li, the same s slots
+          const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][4 * lk]);
+          const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][16 + 4 * lk]);
+          const uint4 xa = make_uint4(x0.x, x0.y, x1.x, x1.y);
+          st[k] = mfma_bf16(boh, xa, st[k]);
+          st[k] = mfma_bf16(bol, xa, st[k]);
+        }
+      }
+      __syncthreads();  // the next chunk's tiles committed; every read of S_in done
+
+      // ---- phase 2 ----
+      if (!AGG) {
+        // intra-chunk output M X (M is zero above the diagonal), then + D x
+        const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[cur][0][16 * ytb + li][8 * lk]);
+        const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[cur][1][16 * ytb + li][8 * lk]);
+        const uint4 xb = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * ypb + li][8 * lk]);
+        y = mfma_bf16(mh, xb, y);
+        y = mfma_bf16(ml, xb, y);
+        const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * ypb + li][16 * ytb + 4 * lk]);
+        y[0] += Dh * bf_lo(xv.x);
+        y[1] += Dh * bf_hi(xv.x);
+        y[2] += Dh * bf_lo(xv.y);
+        y[3] += Dh * bf_hi(xv.y);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.Y[cur][16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
+#pragma unroll
+        for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
+      }
+      __syncthreads();
     }
-    if (GATE && !rev) {
-      zr_prev = zr;
-      if (c + 1 < c1) zr = load_gate(p, tid, b, h, t0 + kQ);
+    if (AGG) {
+      // the range's end state from zero and its decay exponent
+      const int64_t slot = blk.range * (p.nblocks / p.nranges) + bh;
+#pragma unroll
+      for (int k = 0; k < PBW; ++k)
+        *reinterpret_cast<float4*>(p.agg_S + (slot * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+            make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
+      if (tid == 0) p.agg_cs[slot] = cs_sum;
+    } else {
+      float* const fin = rev ? p.g_first : p.h_last;
+      if (fin && blk.range == p.nranges - 1) {
+#pragma unroll
+        for (int k = 0; k < PBW; ++k)
+          *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+              make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
+      }
     }
-    if (AGG && tid == 0) cs_sum += static_cast<double>(sm.cs_end[cur]);
+  } else {
+    // ================= staging waves =================
+    // Waves 0, 1 of them store y (and load what the stores add: the reverse
+    // partial, the gate); waves 2, 3 load and commit the chunks' tiles; a
+    // wave that waits for loads has no stores outstanding. Waves 0..2 also
+    // form the causal C B^T blocks, the last the decays.
+    const int sw = wave - kMainBf;                 // staging wave 0 .. kStageBf-1
+    const bool loader = sw >= 2;
+    const int lt = tid - 64 * (kMainBf + 2);       // loading thread 0 .. 127
+    const int stt = tid - 64 * kMainBf;            // store thread 0 .. 127
+    const int mtb = sw == 0 ? 0 : 1, msb = sw == 2 ? 1 : 0;  // causal C B^T block of staging waves 0..2
 
-    if (!AGG && wave < 3) {
-      // causal block of C B^T, masked and decayed: M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t,
-      // as the block of B C^T: register r of the lane is s = 16 msb + 4 lk + r, t = 16 mtb + li
+    // causal block of C B^T of chunk buffer buf, masked and decayed: M[t][s]
+    // = (C_t . B_s) e^{cs_t - cs_s} dt_s, s <= t, as the block of B C^T:
+    // register r of the lane is s = 16 msb + 4 lk + r, t = 16 mtb + li
+    auto causal_block = [&](const int buf) {
       uint4 bb[KN], cc[KN];
 #pragma unroll
       for (int j = 0; j < KN; ++j) {
-        bb[j] = *reinterpret_cast<const uint4*>(&sm.B[cur][16 * msb + li][32 * j + 8 * lk]);
-        cc[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * mtb + li][32 * j + 8 * lk]);
+        bb[j] = *reinterpret_cast<const uint4*>(&sm.B[buf][16 * msb + li][32 * j + 8 * lk]);
+        cc[j] = *reinterpret_cast<const uint4*>(&sm.C[buf][16 * mtb + li][32 * j + 8 * lk]);
       }
       f4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KN; ++j) a = mfma_bf16(bb[j], cc[j], a);
       const int t = 16 * mtb + li, s0 = 16 * msb + 4 * lk;
-      const float cst = sm.cs[cur][t];
-      const float4 css = *reinterpret_cast<const float4*>(&sm.cs[cur][s0]);
-      const float4 dts = *reinterpret_cast<const float4*>(&sm.dt[cur][s0]);
+      const float cst = sm.cs[buf][t];
+      const float4 css = *reinterpret_cast<const float4*>(&sm.cs[buf][s0]);
+      const float4 dts = *reinterpret_cast<const float4*>(&sm.dt[buf][s0]);
       const float m0 = s0 + 0 <= t ? a[0] * __expf(cst - css.x) * dts.x : 0.f;
       const float m1 = s0 + 1 <= t ? a[1] * __expf(cst - css.y) * dts.y : 0.f;
       const float m2 = s0 + 2 <= t ? a[2] * __expf(cst - css.z) * dts.z : 0.f;
@@ -805,112 +907,106 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_bf16_kernel(const SsdArgs
       uint32_t h01, l01, h23, l23;
       split_pack_bf16(m0, m1, h01, l01);
       split_pack_bf16(m2, m3, h23, l23);
-      *reinterpret_cast<uint2*>(&sm.M[0][t][s0]) = make_uint2(h01, h23);
-      *reinterpret_cast<uint2*>(&sm.M[1][t][s0]) = make_uint2(l01, l23);
-    }
+      *reinterpret_cast<uint2*>(&sm.M[buf][0][t][s0]) = make_uint2(h01, h23);
+      *reinterpret_cast<uint2*>(&sm.M[buf][1][t][s0]) = make_uint2(l01, l23);
+    };
 
-    // inter-chunk output of the wave's block: diag(e^{cs}) C S_in^T
-    f4 y = {0.f, 0.f, 0.f, 0.f};
-    if (!AGG) {
-      uint4 ca[KN], sh[KN], sl[KN];
-#pragma unroll
-      for (int j = 0; j < KN; ++j) {
-        ca[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * ytb + li][32 * j + 8 * lk]);
-        sh[j] = *reinterpret_cast<const uint4*>(&sm.S[0][16 * ypb + li][32 * j + 8 * lk]);
-        sl[j] = *reinterpret_cast<const uint4*>(&sm.S[1][16 * ypb + li][32 * j + 8 * lk]);
+    if (loader) {
+      // one stager: it holds chunk c + 1 from its loads (issued during chunk
+      // c - 1) to its commit (during chunk c), and receives chunk c + 2 right
+      // after that commit
+      SsdStagerBf<N, 128> stg;
+      stg.init(p, lt, b, h, g, c0 * kQ, rev);
+      stg.load(p, lt, c0 * kQ);
+      stg.commit(p, bias, sm, 0, lt);
+      if (sw == kStageBf - 1) chunk_decay(sm, 0, Ah, lane, stg.dt_value(p, bias));
+      __syncthreads();
+      for (int64_t c = c0; c < c1; ++c) {
+        const int cur = (c - c0) & 1, nxt = cur ^ 1;
+        // ---- phase 1: the chunk's M; the loads of the next chunk ----
+        if (!AGG && sw == 2) causal_block(cur);
+        if (c + 1 < c1) stg.load(p, lt, (c + 1) * kQ);
+        __syncthreads();
+        // ---- phase 2: the next chunk's tiles and decays ----
+        if (c + 1 < c1) {
+          stg.commit(p, bias, sm, nxt, lt);
+          if (sw == kStageBf - 1) chunk_decay(sm, nxt, Ah, lane, stg.dt_value(p, bias));
+        }
+        __syncthreads();
       }
-      f4 a = {0.f, 0.f, 0.f, 0.f}, a2 = a;
-#pragma unroll
-      for (int j = 0; j < KN; ++j) {
-        a = mfma_bf16(ca[j], sh[j], a);
-        a2 = mfma_bf16(ca[j], sl[j], a2);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = (a[r] + a2[r]) * sm.ecs[cur][16 * ytb + 4 * lk + r];
-    }
-
-    // state update of the wave's blocks: S^T = e^{cs_end} S^T + (w B)^T X
-    {
-      const float dec = __expf(sm.cs_end[cur]);
-#pragma unroll
-      for (int k = 0; k < PBW; ++k) st[k] *= dec;
-      // operand A: (w B)^T[n][s] = w_s B[s][n] for n = 16 snb + li. The sum
-      // over s does not depend on which k slot holds which s as long as both
-      // operands agree: the lane's 8 slots hold s = 4 lk .. 4 lk + 3 and
-      // 16 + 4 lk .. 16 + 4 lk + 3, so that the lanes' column reads of B fall
-      // on rows 4 apart (distinct LDS banks).
-      uint32_t bh[4], bl[4];
+    } else {
+      // forward sweep of the bidirectional scan: the reverse partial of the
+      // chunk whose output is stored next, one chunk ahead of its store; the
+      // gate of those rows the same way (forward sweep only)
+      float4 pv[4], pv_prev[4];
+      uint2 zr[4], zr_prev[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s0 = (i < 2 ? 0 : 16) + 4 * lk + 2 * (i & 1);
-        const float b0 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0][16 * snb + li]) << 16);
-        const float b1 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0 + 1][16 * snb + li]) << 16);
-        split_pack_bf16(b0 * sm.w[cur][s0], b1 * sm.w[cur][s0 + 1], bh[i], bl[i]);
+        pv[i] = pv_prev[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        zr[i] = zr_prev[i] = make_uint2(0u, 0u);
       }
-      const uint4 boh = make_uint4(bh[0], bh[1], bh[2], bh[3]), bol = make_uint4(bl[0], bl[1], bl[2], bl[3]);
-#pragma unroll
-      for (int k = 0; k < PBW; ++k) {
-        // operand B: X[s][p] = Xt[p][s], p = 16 (spb + k) + li, the same s slots
-        const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][4 * lk]);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][16 + 4 * lk]);
-        const uint4 xa = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        st[k] = mfma_bf16(boh, xa, st[k]);
-        st[k] = mfma_bf16(bol, xa, st[k]);
+      if (BIDIR && !rev)
+        for (int i = 0; i < 4; ++i) pv[i] = load_partial(p, stt, b, h, c0 * kQ + 8 * i);
+      if (GATE && !rev)
+        for (int i = 0; i < 4; ++i) zr[i] = load_gate(p, stt, b, h, c0 * kQ + 8 * i);
+      __syncthreads();
+      for (int64_t c = c0; c < c1; ++c) {
+        const int cur = (c - c0) & 1, nxt = cur ^ 1;
+        const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
+        // ---- phase 1: the chunk's M; y of the previous chunk ----
+        if (!AGG) causal_block(cur);
+        if (!AGG && c > c0) store_y_bf16<GATE>(p, sm.Y[nxt], stt, b, h, t0 - kQ, rev, pv_prev, zr_prev);
+        if (BIDIR && !rev) {
+          for (int i = 0; i < 4; ++i) pv_prev[i] = pv[i];
+          if (c + 1 < c1)
+            for (int i = 0; i < 4; ++i) pv[i] = load_partial(p, stt, b, h, t0 + kQ + 8 * i);
+        }
+        if (GATE && !rev) {
+          for (int i = 0; i < 4; ++i) zr_prev[i] = zr[i];
+          if (c + 1 < c1)
+            for (int i = 0; i < 4; ++i) zr[i] = load_gate(p, stt, b, h, t0 + kQ + 8 * i);
+        }
+        __syncthreads();
+        __syncthreads();
       }
+      if (!AGG) store_y_bf16<GATE>(p, sm.Y[(c1 - 1 - c0) & 1], stt, b, h, (c1 - 1) * kQ, rev, pv_prev, zr_prev);
     }
-    __syncthreads();  // M complete; every read of S_in done
+  }
+}
 
-    // ---- phase 2 ----
-    if (!AGG) {
-      // intra-chunk output M X (M is zero above the diagonal), then + D x
-      const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[0][16 * ytb + li][8 * lk]);
-      const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[1][16 * ytb + li][8 * lk]);
-      const uint4 xb = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * ypb + li][8 * lk]);
-      y = mfma_bf16(mh, xb, y);
-      y = mfma_bf16(ml, xb, y);
-      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * ypb + li][16 * ytb + 4 * lk]);
-      y[0] += Dh * bf_lo(xv.x);
-      y[1] += Dh * bf_hi(xv.x);
-      y[2] += Dh * bf_lo(xv.y);
-      y[3] += Dh * bf_hi(xv.y);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.Y[cur][16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
+template <int N, bool BIDIR, bool GATE, bool AGG = false>
+__global__ __launch_bounds__(64 * kWavesBf) void ssd_fwd_bf16_kernel(const SsdArgs<uint16_t> p) {
+  static_assert(kQ == 32 && kP == 64 && kMainBf == 8 && kStageBf == 4, "work split below assumes these sizes");
+  static_assert(N == 64 || N == 128, "state sizes");
+  static_assert(!(AGG && (BIDIR || GATE)), "the aggregate pass runs one sweep, no gate");
+
+  __shared__ SsdSmemBf<N> sm;
+
+  const SsdBlock blk = ssd_block(p);
+  const int64_t h = blk.bh % p.H;
+  const float Dfwd = p.D ? p.D[h] : 0.f;
+  const float bias = p.dt_bias ? p.dt_bias[h] : 0.f;  // the head's step-size bias (0: none), in a register
+
+  // the block t < 16, s >= 16 of M stays zero (future steps)
+  for (int i = threadIdx.x; i < 4 * kQ * SsdSmemBf<N>::TP; i += 64 * kWavesBf) (&sm.M[0][0][0][0])[i] = 0;
+
+  // BIDIR: a reverse sweep (zero initial state, no D x) storing a float32
+  // partial, then the forward sweep adding it (a split sequence runs them in
+  // separate launches: sweep_sel). Without BIDIR, sweep_sel 0 selects the
+  // reverse sweep: only the aggregate pass of a split bidirectional scan
+  // runs that way.
+  if (BIDIR) {
+    if (p.sweep_sel != 1) {
+      ssd_bf16_sweep<N, BIDIR, GATE, AGG, true>(p, sm, blk, Dfwd, bias);
+      // the forward sweep reuses the LDS tiles and reads the partial just stored
+      __syncthreads();
     }
-    if (!AGG) {
-#pragma unroll
-      for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
-    }
-    if (c + 1 < c1) {
-      cm.commit(p, bias, sm, nxt, tid);
-      if (wave == kWaves - 1) chunk_decay(sm, nxt, Ah, lane, cm.dt_value(p, bias));
-    }
-    __syncthreads();
-  };
-  for (int64_t c = c0; c < c1; c += 2) {
-    chunk(c, stg0, stg1);
-    if (c + 1 < c1) chunk(c + 1, stg1, stg0);
-  }
-  if (AGG) {
-    // the range's end state from zero and its decay exponent
-    const int64_t slot = blk.range * (p.nblocks / p.nranges) + bh;
-#pragma unroll
-    for (int k = 0; k < PBW; ++k)
-      *reinterpret_cast<float4*>(p.agg_S + (slot * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
-          make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
-    if (tid == 0) p.agg_cs[slot] = cs_sum;
+    if (p.sweep_sel != 0) ssd_bf16_sweep<N, BIDIR, GATE, AGG, false>(p, sm, blk, Dfwd, bias);
+  } else if (AGG && p.sweep_sel == 0) {
+    ssd_bf16_sweep<N, BIDIR, GATE, AGG, true>(p, sm, blk, Dfwd, bias);
   } else {
-    store_y_bf16<GATE>(p, sm.Y[(c1 - 1 - c0) & 1], tid, b, h, (c1 - 1) * kQ, rev, pv_prev, zr_prev);
-    float* const fin = rev ? p.g_first : p.h_last;
-    if (fin && blk.range == p.nranges - 1) {
-#pragma unroll
-      for (int k = 0; k < PBW; ++k)
-        *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
-            make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
-    }
+    ssd_bf16_sweep<N, BIDIR, GATE, AGG, false>(p, sm, blk, Dfwd, bias);
   }
-  // the forward sweep reuses the LDS tiles and reads the partial just stored
-  if (BIDIR && rev) __syncthreads();
-  }  // sweep
 }
 
 int ssd_validate(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
@@ -1005,8 +1101,9 @@ size_t ssd_ws_bytes(int64_t Bs, int64_t L, int64_t H, int64_t P, int dtype, bool
 template <typename T, bool BIDIR, bool GATE, bool AGG = false>
 void launch_ssd_kernel(const SsdArgs<T>& a, int64_t N, dim3 grid, dim3 block, hipStream_t stream) {
   if constexpr (std::is_same<T, uint16_t>::value) {
-    if (N == 128) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
+    const dim3 bblock(64 * kWavesBf);
+    if (N == 128) hipLaunchKernelGGL((ssd_fwd_bf16_kernel<128, BIDIR, GATE, AGG>), grid, bblock, 0, stream, a);
+    else hipLaunchKernelGGL((ssd_fwd_bf16_kernel<64, BIDIR, GATE, AGG>), grid, bblock, 0, stream, a);
   } else {
     if (N == 128) hipLaunchKernelGGL((ssd_fwd_kernel<T, 128, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((ssd_fwd_kernel<T, 64, BIDIR, GATE, AGG>), grid, block, 0, stream, a);
