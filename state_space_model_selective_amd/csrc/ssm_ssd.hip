@@ -509,9 +509,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 // run only products over LDS tiles; four staging waves move data and form
 // each chunk's masked C B^T, so that this work overlaps the products instead
 // of adding to them. Two of the staging waves only load and commit tiles
-// (16-byte global loads into registers, one chunk ahead), the other two only
-// store y; a wave that waits for its loads then has no stores outstanding
-// (stores count in the same counter). Per chunk, two barriers:
+// (16-byte global loads into registers in phase 1, committed in phase 2),
+// the other two only store y; a wave that waits for its loads then has no
+// stores outstanding (stores count in the same counter). Per chunk, two
+// barriers:
 //   phase 1  compute waves: their 16 x 16 block of diag(e^{cs}) C S_in^T and
 //            the update of their state blocks, S^T = e^{cs_end} S^T +
 //            (w B)^T X (so that a lane holds 4 consecutive n of one p).
@@ -912,9 +913,9 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
     };
 
     if (loader) {
-      // one stager: it holds chunk c + 1 from its loads (issued during chunk
-      // c - 1) to its commit (during chunk c), and receives chunk c + 2 right
-      // after that commit
+      // one stager: the next chunk's tiles are loaded during phase 1 and
+      // committed in phase 2 of the same chunk (with two stagers a chunk
+      // ahead the compiler's waits took in the newest loads as well)
       SsdStagerBf<N, 128> stg;
       stg.init(p, lt, b, h, g, c0 * kQ, rev);
       stg.load(p, lt, c0 * kQ);
