@@ -557,8 +557,8 @@ struct alignas(16) SsdSmemBf {
   // Row pitches (elements). With lanes on rows and 16-byte column blocks, a
   // 16-byte read is free of bank conflicts when the pitch in bytes is 32 mod
   // 64, an 8-byte access when it is 16 mod 64 (measured on gfx950): C is
-  // only read 16 bytes at a time; B, the state copy and x also take 8-byte
-  // stores or reads.
+  // only read and written 16 bytes at a time; the state copy and Xt also
+  // take 8-byte stores or reads, and B 2-byte column reads (rows 4 apart).
   static constexpr int NPC = N + 16;  // C
   static constexpr int NP = N + 8;    // B and the state copy
   static constexpr int TP = kQ + 8;   // the s-contiguous tiles
