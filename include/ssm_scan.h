@@ -142,6 +142,31 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
                  int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Round checkpoints: the scan state entering every 32-step round, for a
+ * backward pass that then skips its own forward sweep. Like the forward of
+ * the Bi-Mamba2 autograd function in "Some questions of Bi-Mamba2 and Hydra"
+ * (the MambaChunkScanCombinedFn listing), which returns the per-chunk states
+ * and keeps the forward's products for the backward to read.
+ * ssm_scan_ckpt_bytes: bytes of the checkpoint buffer for these sizes,
+ * (Bs, ceil(L / 32), 16 ceil(ED / 16), 16) float32 (channels padded to a
+ * multiple of 16; N must be 16, else 0), 0 for invalid sizes.
+ * ssm_scan_fwd_ckpt: ssm_scan_fwd (same arguments, results and errors) that
+ * also writes ckpt[b][r][e][n] = h_{32 r - 1}[b, e, n], the state after the
+ * first 32 r steps, for rounds r >= 1 (entries of round 0 are not written;
+ * padded channels get their zero state). A split sequence's checkpoints
+ * take the entering state's carried contribution with the same 2^-40 cut
+ * as its outputs. ckpt: device buffer of at least ckpt_bytes >=
+ * ssm_scan_ckpt_bytes(...) bytes, aligned to 16 bytes, overlapping no other
+ * argument (SSM_ERR_NULL if NULL with data to scan, SSM_ERR_WORKSPACE if
+ * too small, SSM_ERR_ALIAS if it overlaps).
+ */
+size_t ssm_scan_ckpt_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N);
+int ssm_scan_fwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D, const float* h0, const ssm_scan_options* opts, void* y, float* h_last,
+                      float* ckpt, size_t ckpt_bytes, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward selective scan that allocates nothing and takes no workspace, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc). Arguments, results
@@ -260,6 +285,22 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz,
                  int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * ssm_scan_bwd given the round checkpoints that ssm_scan_fwd_ckpt wrote for
+ * the same inputs (x, delta, A, B, C, h0 and the step-size options): the
+ * backward then skips its own forward sweep over the sequence. ckpt (read
+ * only; at least ckpt_bytes >= ssm_scan_ckpt_bytes(...) bytes, aligned to 16
+ * bytes, overlapping no output or the workspace) is required: NULL with
+ * data to scan is SSM_ERR_NULL. Other arguments, results, workspace and
+ * errors as ssm_scan_bwd; checkpoints of other inputs give wrong gradients
+ * (no error).
+ */
+int ssm_scan_bwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D, const float* h0, const ssm_scan_options* opts, const void* dy,
+                      const float* dh_last, const float* ckpt, size_t ckpt_bytes, void* dx, void* ddelta, float* dA,
+                      void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+                      int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward pass of the bidirectional scan: the gradients of L = sum(dy * y)

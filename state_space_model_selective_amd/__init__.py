@@ -95,6 +95,12 @@ def lib():
         L.ssm_scan_fwd.restype = ci
         L.ssm_scan_bidir_fwd.argtypes = [vp] * 12 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_fwd.restype = ci
+        L.ssm_scan_ckpt_bytes.argtypes = [i64] * 4
+        L.ssm_scan_ckpt_bytes.restype = sz
+        L.ssm_scan_fwd_ckpt.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_fwd_ckpt.restype = ci
+        L.ssm_scan_bwd_ckpt.argtypes = [vp] * 11 + [sz] + [vp] * 9 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bwd_ckpt.restype = ci
         L.ssm_scan_fwd_status.argtypes = [vp, sz] + [i64] * 4 + [ci, vp]
         L.ssm_scan_fwd_status.restype = ci
         L.ssm_scan_fwd_noalloc.argtypes = [vp] * 10 + [i64] * 4 + [ci, vp]
@@ -234,7 +240,7 @@ def _scan_args(where, x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
     """Validates the per-channel scan's arguments; returns (checker, dims).
     outs: (name, tensor, kind[, required]) with kind 'seq' (like x), 'bc'
     (like B), 'state' (Bs, ED, N) float32, 'ed' (ED,) float32, 'a' (ED, N)
-    float32."""
+    float32, 'ckpt' the round checkpoints (float32)."""
     import torch
     a = _Args(where, x, 3)
     Bs, L, ED = (int(v) for v in x.shape)
@@ -249,7 +255,7 @@ def _scan_args(where, x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
     a.check("z", z, (Bs, L, ED))
     a.limit(dt_limit)
     shapes = {"seq": ((Bs, L, ED), None), "bc": ((Bs, L, N), None), "state": ((Bs, ED, N), f32),
-              "ed": ((ED,), f32), "a": ((ED, N), f32)}
+              "ed": ((ED,), f32), "a": ((ED, N), f32), "ckpt": (ssm_scan_ckpt_shape(Bs, L, ED), f32)}
     for name, t, kind, *req in outs:
         shp, dt = shapes[kind]
         a.check(name, t, shp, dt, required=bool(req and req[0]))
@@ -285,24 +291,35 @@ def _stream(x, stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def ssm_scan_ckpt_shape(Bs, L, ED):
+    """Shape of the round checkpoints (float32): (Bs, ceil(L / 32), 16 ceil(ED / 16), 16)."""
+    return (Bs, (L + 31) // 32, (ED + 15) // 16 * 16, 16)
+
+
 def ssm_scan_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, workspace=None, stream=None, h0=None,
-                 dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
+                 dt_bias=None, dt_softplus=False, dt_limit=None, z=None, ckpt=None):
     """y = selective_scan(x, delta, A, B, C, D) from initial state h0 (zero if None);
     optionally the final state into h_last. dt_bias / dt_softplus / dt_limit
-    pre-process delta, z gates the output (y * silu(z))."""
+    pre-process delta, z gates the output (y * silu(z)). With ckpt (a float32
+    tensor of ssm_scan_ckpt_shape(Bs, L, ED)) the state entering every
+    32-step round is written there as well (ssm_scan_fwd_ckpt), for
+    ssm_scan_bwd(..., ckpt=ckpt)."""
+    import torch
     _, (Bs, L, ED, N) = _scan_args("ssm_scan_fwd", x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
-                                   [("y", y, "seq"), ("h_last", h_last, "state")])
+                                   [("y", y, "seq"), ("h_last", h_last, "state"), ("ckpt", ckpt, "ckpt")])
     dt = _dtype_code(x)
     if y is None:
-        import torch
         y = torch.empty_like(x)
     workspace, ws_bytes = _workspace(workspace, ssm_scan_workspace_bytes(Bs, L, ED, N, dt, False), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
-    rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
-                            _ptr(y), _ptr(h_last),
-                            Bs, L, ED, N, dt, _ptr(workspace), ws_bytes, _stream(x, stream))
+    head = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts), _ptr(y), _ptr(h_last))
+    tail = (Bs, L, ED, N, dt, _ptr(workspace), ws_bytes, _stream(x, stream))
+    if ckpt is None:
+        rc = lib().ssm_scan_fwd(*head, *tail)
+    else:
+        rc = lib().ssm_scan_fwd_ckpt(*head, _ptr(ckpt), ckpt.numel() * 4, *tail)
     if rc != SSM_OK:
-        raise SSMError(rc, "ssm_scan_fwd")
+        raise SSMError(rc, "ssm_scan_fwd_ckpt" if ckpt is not None else "ssm_scan_fwd")
     return y
 
 
@@ -377,7 +394,7 @@ def ssm_scan_bidir_bwd_workspace_bytes(Bs, L, ED, N, dtype=SSM_F32, gate=False):
 
 
 def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias, dt_softplus,
-         dt_limit, want_ddt_bias, z, dh_last=None, g0=None, dg_first=None, want_dg0=False):
+         dt_limit, want_ddt_bias, z, dh_last=None, g0=None, dg_first=None, want_dg0=False, ckpt=None):
     import torch
     where = "ssm_scan_bidir_bwd" if bidir else "ssm_scan_bwd"
     o = dict(out or {})
@@ -390,7 +407,8 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
             raise ValueError("%s: unknown output %r" % (where, k))
     a, (Bs, L, ED, N) = _scan_args(where, x, delta, A, B, C, D, h0, dt_bias, dt_limit, z, workspace,
                                    [("dy", dy, "seq", True), ("dh_last", dh_last, "state"), ("g0", g0, "state"),
-                                    ("dg_first", dg_first, "state")] + [(k, v, known[k]) for k, v in o.items()])
+                                    ("dg_first", dg_first, "state"), ("ckpt", ckpt, "ckpt")] +
+                                   [(k, v, known[k]) for k, v in o.items()])
     if not bidir and (g0 is not None or dg_first is not None):
         raise ValueError("%s: g0 and dg_first belong to the bidirectional scan" % where)
     dt = _dtype_code(x)
@@ -421,6 +439,11 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
         rc = lib().ssm_scan_bidir_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0),
                                       _byref(opts), _ptr(dy), _ptr(dh_last), _ptr(dg_first), *grads,
                                       _ptr(o.get("dg0")), *tail)
+    elif ckpt is not None:
+        where = "ssm_scan_bwd_ckpt"
+        rc = lib().ssm_scan_bwd_ckpt(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                                     _byref(opts), _ptr(dy), _ptr(dh_last), _ptr(ckpt), ckpt.numel() * 4, *grads,
+                                     *tail)
     else:
         rc = lib().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _byref(opts),
                                 _ptr(dy), _ptr(dh_last), *grads, *tail)
@@ -431,7 +454,7 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
 
 def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
                  stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None,
-                 dh_last=None):
+                 dh_last=None, ckpt=None):
     """Gradients of sum(dy * y) (+ sum(dh_last * h_last) when dh_last, the
     final state's gradient, is given) for y = ssm_scan_fwd(x, delta, A, B,
     C, D, h0=h0, dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit,
@@ -441,10 +464,12 @@ def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False
     (like A), dB, dC (like B), dD (ED,) float32 if want_dD, dh0 (Bs, ED, N)
     float32 if want_dh0, ddt_bias (ED,) float32 if dt_bias is given or
     want_ddt_bias, dz (like x) if z is given. Tensors given in ``out`` (same
-    keys) are written instead of new ones.
+    keys) are written instead of new ones. ckpt: the round checkpoints that
+    ssm_scan_fwd(..., ckpt=ckpt) wrote for the same inputs (the backward
+    then skips its own forward sweep; ssm_scan_bwd_ckpt).
     """
     return _bwd(False, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias,
-                dt_softplus, dt_limit, want_ddt_bias, z, dh_last=dh_last)
+                dt_softplus, dt_limit, want_ddt_bias, z, dh_last=dh_last, ckpt=ckpt)
 
 
 def ssm_scan_bidir_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,

@@ -142,6 +142,10 @@ struct ScanArgs {
   // reverse sweep's start state (state: the forward sweep's end state)
   double* sdsum;        // [bg * nchunks + k][16 channels]
   float* gstate;        // [bg * nchunks + k][16 channels][16 states]
+  // round checkpoints (forward scans only, or nullptr): the state entering
+  // every round of kRT steps, [Bs][ck_rounds][ck_EDp][16], round 0 not written
+  float* ckpt;
+  int64_t ck_rounds, ck_EDp;
 };
 
 // Input tile of one round (double-buffered).
@@ -481,6 +485,19 @@ __device__ void correct_pass(const ScanArgs<T>& p, Stager<T, SEG * TS, TPT, fals
     Tile<RT, GATE>& nxt = tile[(r + 1) & 1];
     if (r + 1 < rounds) st.template prefetch<STAGE_CORRECT>(p, r + 1);
     if (r >= 1) st.template store_out<STAGE_CORRECT>(p, r - 1, nxt, out);
+    if (p.ckpt && !rev && wave == 0) {
+      // the checkpoint of this round: the main pass's state (from zero at the
+      // chunk's start) plus the entering state carried to the round's start;
+      // the chunk's first round is the entering state itself
+      float* ck = p.ckpt + ((b * p.ck_rounds + t0 / RT + r) * p.ck_EDp + st.ce0 + ch) * 16 + 4 * g;
+      float4 v = r == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(ck);
+      const float cb = static_cast<float>(base);
+      v.x = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[0] * cb), hin[0], v.x);
+      v.y = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[1] * cb), hin[1], v.y);
+      v.z = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[2] * cb), hin[2], v.z);
+      v.w = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[3] * cb), hin[3], v.w);
+      *reinterpret_cast<float4*>(ck) = v;
+    }
     __syncthreads();  // the output tile is reused below
     float pre = 0.f;  // delta of the round's rows before this wave's segment
     for (int i = 0; i < wave * TS; ++i) pre += cur.dt[i][ch];
@@ -727,8 +744,15 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
             for (int j = 0; j < 4; ++j) hin[j] = __builtin_fmaf(av[i][j], hin[j], bv[i][j]);
             out.yq[g][row][ch] = dot_quad(cq, hin);
           }
-          // the last segment's end state is the round's carry
-          if (seg == SEG - 1) fa.carry[r & 1][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
+          // the last segment's end state is the round's carry, and the
+          // checkpoint of the chunk's next round (all 16 lanes of a group,
+          // padded channels too: their state is their zero entering state)
+          if (seg == SEG - 1) {
+            fa.carry[r & 1][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
+            if (!BIDIR && p.ckpt && r + 1 < rounds)
+              *reinterpret_cast<float4*>(p.ckpt + ((b * p.ck_rounds + t0 / RT + r + 1) * p.ck_EDp + e) * 16 + 4 * g) =
+                  make_float4(hin[0], hin[1], hin[2], hin[3]);
+          }
         }
       }
 
@@ -1011,11 +1035,29 @@ size_t workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, 
   return partial_bytes(s.seq, dtype, bidir) + plan_split(Bs, L, ED, bidir, device_cus()).bytes;
 }
 
+// Bytes of the round checkpoints (Bs, ceil(L / kRT), 16 ceil(ED / 16), 16)
+// float32, or 0 when the sizes overflow
+size_t ckpt_bytes(int64_t Bs, int64_t L, int64_t ED) {
+  if (Bs < 0 || L < 0 || ED < 0) return 0;
+  int64_t t;
+  const int64_t rounds = (L + 31) / 32, EDp = (ED + 15) / 16 * 16;
+  if (!mul_nn(Bs, rounds, &t) || !mul_nn(t, EDp, &t) || !mul_nn(t, 16, &t) || t > INT64_MAX / 4) return 0;
+  return static_cast<size_t>(t) * 4;
+}
+
 int validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
              const float* h0, const float* g0, const ssm_scan_options* opts, const void* y, const float* h_last, const float* g_first, int64_t Bs, int64_t L, int64_t ED,
-             int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s) {
+             int64_t N, int dtype, const void* ws, size_t ws_bytes, int bidir, Sizes* s, bool want_ck = false,
+             const void* ckpt = nullptr, size_t ck_bytes = 0) {
   int rc = check_sizes(Bs, L, ED, N, dtype, s);
   if (rc != SSM_OK) return rc;
+  const size_t ck_need = want_ck && s->seq > 0 ? ckpt_bytes(Bs, L, ED) : 0;
+  if (want_ck && s->seq > 0) {
+    if (ck_need == 0) return SSM_ERR_DIM;
+    if (!ckpt) return SSM_ERR_NULL;
+    if (!aligned16(ckpt)) return SSM_ERR_UNSUPPORTED;
+    if (ck_bytes < ck_need) return SSM_ERR_WORKSPACE;
+  }
   // a buffer with no elements may be NULL
   if ((s->seq > 0 && (!x || !delta || !y)) || (s->bc > 0 && (!B || !C)) || (ED > 0 && !A)) return SSM_ERR_NULL;
   const float* dt_bias = opts ? opts->dt_bias : nullptr;
@@ -1031,12 +1073,13 @@ int validate(const void* x, const void* delta, const float* A, const void* B, co
                 rng(B, s->bc * s->elem), rng(C, s->bc * s->elem), rng(D, D ? ED * 4 : 0),
                 rng(h0, h0 ? s->state * 4 : 0), rng(g0, g0 ? s->state * 4 : 0), rng(dt_bias, dt_bias ? ED * 4 : 0),
                 rng(z, z ? s->seq * s->elem : 0)};
-  Range out[4];
+  Range out[5];
   int nout = 0;
   out[nout++] = rng(y, s->seq * s->elem);
   if (h_last) out[nout++] = rng(h_last, s->state * 4);
   if (g_first) out[nout++] = rng(g_first, s->state * 4);
   if (need > 0) out[nout++] = rng(ws, static_cast<int64_t>(need));
+  if (ck_need > 0) out[nout++] = rng(ckpt, static_cast<int64_t>(ck_need));
   for (int i = 0; i < nout; ++i) {
     if (out[i].hi == out[i].lo) continue;
     for (const Range& r : in)
@@ -1078,7 +1121,7 @@ void launch_one(const ScanArgs<T>& a, int64_t nblk, hipStream_t stream) {
 template <typename T>
 int launch_scan(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                 const float* h0, const float* g0, const ssm_scan_options* opts, void* y, float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int bidir, void* ws,
-                hipStream_t stream) {
+                hipStream_t stream, float* ckpt = nullptr) {
   const int64_t ngroups = (ED + 15) / 16;
   const SplitPlan sp = plan_split(Bs, L, ED, bidir, device_cus());
   const int64_t nblk = sp.nbg * sp.nchunks;
@@ -1116,6 +1159,9 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.state = nullptr;
   a.sdsum = nullptr;
   a.gstate = nullptr;
+  a.ckpt = bidir ? nullptr : ckpt;
+  a.ck_rounds = (L + kRT - 1) / kRT;
+  a.ck_EDp = ngroups * 16;
   const bool split = sp.nchunks > 1;
   if (split && bidir) {
     char* w = static_cast<char*>(ws) + partial_bytes(Bs * L * ED, std::is_same<T, float>::value ? SSM_F32 : SSM_BF16, 1);
@@ -1161,10 +1207,11 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
 int run(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
         const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
         float* h_last, float* g_first, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* ws,
-        size_t ws_bytes, void* stream, int bidir) {
+        size_t ws_bytes, void* stream, int bidir, bool want_ck = false, float* ckpt = nullptr, size_t ck_bytes = 0) {
   Sizes s;
   if (!bidir) g0 = nullptr;
-  int rc = validate(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s);
+  int rc = validate(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, ws, ws_bytes, bidir, &s,
+                    want_ck, ckpt, ck_bytes);
   if (rc != SSM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.seq == 0) {
@@ -1174,9 +1221,10 @@ int run(const void* x, const void* delta, const float* A, const void* B, const v
                                                                           s.state * 4, st);
     return ok ? SSM_OK : SSM_ERR_LAUNCH;
   }
+  float* ck = want_ck ? ckpt : nullptr;
   if (dtype == SSM_F32)
-    return launch_scan<float>(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
-  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st);
+    return launch_scan<float>(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st, ck);
+  return launch_scan<uint16_t>(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, bidir, ws, st, ck);
 }
 
 }  // namespace
@@ -1230,6 +1278,19 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
                  int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return run(x, delta, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace,
              workspace_bytes, stream, 0);
+}
+
+size_t ssm_scan_ckpt_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N) {
+  if (N != 16) return 0;
+  return ckpt_bytes(Bs, L, ED);
+}
+
+int ssm_scan_fwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                      const float* h0, const ssm_scan_options* opts, void* y, float* h_last, float* ckpt,
+                      size_t ckpt_bytes, int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, nullptr, opts, y, h_last, nullptr, Bs, L, ED, N, dtype, workspace,
+             workspace_bytes, stream, 0, true, ckpt, ckpt_bytes);
 }
 
 int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,

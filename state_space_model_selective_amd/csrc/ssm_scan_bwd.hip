@@ -70,6 +70,7 @@ struct BwdArgs {
   T* ddl;
   float* dh0;        // or nullptr
   float* ckpt;       // [Bs][rounds][EDp][16]: state entering each round (round 0 unused)
+  int ck_given;      // the caller's checkpoints (of the forward scan): the first sweep is skipped
   float* pB;         // [ngroups][Bs][L][16]: dB partial of each channel group
   float* pC;         // same for dC
   double* pA;        // [Bs][EDp][16]: dA partial of each batch row
@@ -544,7 +545,8 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   if (p.nchunks > 1) chunk_entry_states(p, bg, kchunk, ch, g, A2, hstart, kend);
 
   // ---- sweep 1: forward round aggregates -> checkpoints --------------------
-  if (R > 1) {
+  // (not when the caller passes the forward scan's checkpoints)
+  if (R > 1 && !p.ck_given) {
     float hc[4] = {hstart[0], hstart[1], hstart[2], hstart[3]};  // state entering the round (wave SEG-1)
     st.template prefetch<false>(p, 0);
     st.template commit<false>(p, tile[0]);
@@ -964,6 +966,8 @@ struct StateArgs {
   const float* dh_last;
   const float* dg_first;
   float* dg0;
+  const float* ckpt;  // the forward scan's round checkpoints, or nullptr
+  size_t ck_bytes;
 };
 
 int bwd_validate(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
@@ -987,6 +991,10 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
     if (q && !aligned16(q)) return SSM_ERR_UNSUPPORTED;
   BwdLayout lo;
   if (!bwd_layout(Bs, L, ED, &lo, bidir, bidir && dtype == SSM_BF16)) return SSM_ERR_DIM;
+  // the forward scan's checkpoints: (Bs, rounds, 16 ceil(ED / 16), 16) float32
+  const int64_t ck_need = sa.ckpt && s->seq > 0 ? Bs * lo.rounds * lo.EDp * 16 * 4 : 0;
+  if (sa.ckpt && !aligned16(sa.ckpt)) return SSM_ERR_UNSUPPORTED;
+  if (ck_need > 0 && sa.ck_bytes < static_cast<size_t>(ck_need)) return SSM_ERR_WORKSPACE;
   if (s->seq == 0) lo.bytes = 0;  // nothing is scanned: no workspace
   else if (z) lo.bytes = gated_bytes(Bs, L, ED, N, dtype, bidir, *s, lo.bytes, gate_off);
   if (lo.bytes > 0 && (!ws || ws_bytes < lo.bytes)) return SSM_ERR_WORKSPACE;
@@ -994,7 +1002,8 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
                       rng(B, s->bc * s->elem),  rng(C, s->bc * s->elem),      rng(D, D ? ED * 4 : 0),
                       rng(h0, h0 ? s->state * 4 : 0), rng(dy, s->seq * s->elem), rng(dt_bias, dt_bias ? ED * 4 : 0),
                       rng(z, z ? s->seq * s->elem : 0), rng(sa.g0, sa.g0 ? s->state * 4 : 0),
-                      rng(sa.dh_last, sa.dh_last ? s->state * 4 : 0), rng(sa.dg_first, sa.dg_first ? s->state * 4 : 0)};
+                      rng(sa.dh_last, sa.dh_last ? s->state * 4 : 0), rng(sa.dg_first, sa.dg_first ? s->state * 4 : 0),
+                      rng(sa.ckpt, ck_need)};
   const Range out[] = {rng(dx, s->seq * s->elem), rng(ddelta, s->seq * s->elem), rng(dA, ED * N * 4),
                        rng(dB, s->bc * s->elem),  rng(dC, s->bc * s->elem),      rng(dD, dD ? ED * 4 : 0),
                        rng(dh0, dh0 ? s->state * 4 : 0), rng(ddt_bias, ddt_bias ? ED * 4 : 0),
@@ -1076,7 +1085,9 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
   a.dx = static_cast<T*>(dx);
   a.ddl = static_cast<T*>(ddelta);
   a.dh0 = dh0;
-  a.ckpt = reinterpret_cast<float*>(w + lo.ckpt_off);
+  // the kernels only read checkpoints that the caller passes
+  a.ckpt = sa.ckpt ? const_cast<float*>(sa.ckpt) : reinterpret_cast<float*>(w + lo.ckpt_off);
+  a.ck_given = sa.ckpt ? 1 : 0;
   a.pB = reinterpret_cast<float*>(w + lo.pB_off);
   a.pC = reinterpret_cast<float*>(w + lo.pC_off);
   a.pA = reinterpret_cast<double*>(w + lo.pA_off);
@@ -1157,6 +1168,7 @@ int run_bwd(const void* x, const void* delta, const float* A, const void* B, con
   BwdSizes s;
   size_t gate_off = 0;
   if (!bidir) sa.g0 = sa.dg_first = sa.dg0 = nullptr;
+  if (bidir) sa.ckpt = nullptr;
   const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa,
                               Bs, L, ED, N, dtype, workspace, workspace_bytes, bidir, &s, &gate_off);
   if (rc != SSM_OK) return rc;
@@ -1219,7 +1231,20 @@ int ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B
                  void* ddelta, float* dA, void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz,
                  int64_t Bs, int64_t L, int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream) {
-  const StateArgs sa{nullptr, dh_last, nullptr, nullptr};
+  const StateArgs sa{nullptr, dh_last, nullptr, nullptr, nullptr, 0};
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
+                 N, dtype, workspace, workspace_bytes, stream, false);
+}
+
+int ssm_scan_bwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D, const float* h0, const ssm_scan_options* opts, const void* dy,
+                      const float* dh_last, const float* ckpt, size_t ckpt_bytes, void* dx, void* ddelta, float* dA,
+                      void* dB, void* dC, float* dD, float* dh0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
+                      int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  // a NULL ckpt is an error here (ssm_scan_bwd is the call without one),
+  // unless there is nothing to scan
+  if (!ckpt && Bs > 0 && L > 0 && ED > 0) return SSM_ERR_NULL;
+  const StateArgs sa{nullptr, dh_last, nullptr, nullptr, ckpt, ckpt_bytes};
   return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
                  N, dtype, workspace, workspace_bytes, stream, false);
 }
@@ -1229,7 +1254,7 @@ int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const v
                        const float* dh_last, const float* dg_first, void* dx, void* ddelta, float* dA, void* dB,
                        void* dC, float* dD, float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
                        int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const StateArgs sa{g0, dh_last, dg_first, dg0};
+  const StateArgs sa{g0, dh_last, dg_first, dg0, nullptr, 0};
   return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
                  N, dtype, workspace, workspace_bytes, stream, true);
 }

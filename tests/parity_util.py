@@ -106,11 +106,13 @@ def gather_channels(y, chans, ED):
 
 def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, stream=None, bidir=False,
                 dt_bias=None, dt_softplus=False, dt_limit=None, z=None, dh_last=None, g0=None, dg_first=None,
-                want_dg0=False):
+                want_dg0=False, use_ckpt=False):
     """ssm_scan_bwd (bidir: ssm_scan_bidir_bwd) on the GPU; every gradient as
     a float64 numpy array. dt_bias (numpy, float32) / dt_softplus / dt_limit
     are the step-size options; with dt_bias the result holds ddt_bias; z (like
-    x) is the output gate, and the result then holds dz."""
+    x) is the output gate, and the result then holds dz. use_ckpt: run the
+    forward with round checkpoints (NaN-filled first) and pass them to the
+    backward (ssm_scan_fwd_ckpt, ssm_scan_bwd_ckpt)."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -140,6 +142,11 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
         kw.update(g0=st(g0), dg_first=st(dg_first), want_dg0=want_dg0)
         if want_dg0:
             out["dg0"] = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev)
+    if use_ckpt:
+        ck = torch.full(ssm.ssm_scan_ckpt_shape(Bs, L, ED), float("nan"), dtype=torch.float32, device=dev)
+        ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], h0=h0t,
+                         dt_bias=bias, dt_softplus=dt_softplus, dt_limit=dt_limit, z=zt, ckpt=ck, stream=stream)
+        kw["ckpt"] = ck
     fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
     res = fn(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],
              h0=h0t, want_dD=want_dD, want_dh0=want_dh0, out=out, stream=stream, dt_bias=bias,

@@ -427,3 +427,71 @@ def test_one_hip_runtime_whatever_the_call_order():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def fwd_ckpt(**kw):
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], h0=P[10], ck=P[20], opts=None,
+                Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args["ck_bytes"] = ssm.lib().ssm_scan_ckpt_bytes(2, 64, 64, 16)
+    args.update(kw)
+    return ssm.lib().ssm_scan_fwd_ckpt(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                                       args["h0"], args["opts"], args["y"], args["h"], args["ck"], args["ck_bytes"],
+                                       args["Bs"], args["L"], args["ED"], args["N"], args["dtype"], args["ws"],
+                                       args["ws_bytes"], None)
+
+
+def test_checkpoint_bytes():
+    q = ssm.lib().ssm_scan_ckpt_bytes
+    # (Bs, ceil(L / 32), 16 ceil(ED / 16), 16) float32
+    assert q(2, 64, 64, 16) == 2 * 2 * 64 * 16 * 4
+    assert q(3, 65, 20, 16) == 3 * 3 * 32 * 16 * 4
+    assert q(1, 1, 1, 16) == 16 * 16 * 4
+    assert q(2, 0, 64, 16) == 0 and q(0, 64, 64, 16) == 0
+    assert q(2, 64, 64, 8) == 0                     # N other than 16
+    assert q(1, 1 << 62, 1 << 20, 16) == 0          # overflow
+    assert ssm.ssm_scan_ckpt_shape(3, 65, 20) == (3, 3, 32, 16)
+
+
+def test_forward_checkpoint_validation():
+    assert fwd_ckpt(ck=None) == ssm.SSM_ERR_NULL
+    assert fwd_ckpt(ck=P[20] + 8) == ssm.SSM_ERR_UNSUPPORTED       # misaligned
+    assert fwd_ckpt(ck_bytes=1024) == ssm.SSM_ERR_WORKSPACE         # too small
+    assert fwd_ckpt(ck=P[0]) == ssm.SSM_ERR_ALIAS                   # on top of x
+    assert fwd_ckpt(ck=P[6] + 256) == ssm.SSM_ERR_ALIAS             # inside y
+    none = dict(x=None, delta=None, B=None, C=None, D=None, y=None, h=None, h0=None, ck=None)
+    assert fwd_ckpt(**dict(none, Bs=0, ED=0)) == ssm.SSM_OK         # nothing to scan: no checkpoints
+
+
+def bwd_ckpt(**kw):
+    args = dict(BWD_DEFAULT)
+    args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32, ck=P[24])
+    args["ws_bytes"] = ssm.ssm_scan_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_F32)
+    args["ck_bytes"] = ssm.lib().ssm_scan_ckpt_bytes(2, 64, 64, 16)
+    args.update(kw)
+    head = [args[n] for n in BWD_ORDER[:10]]
+    tail = [args[n] for n in BWD_ORDER[10:]]
+    return ssm.lib().ssm_scan_bwd_ckpt(*head, args["ck"], args["ck_bytes"], *tail, args["Bs"], args["L"], args["ED"],
+                                       args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+def test_backward_checkpoint_validation():
+    assert bwd_ckpt(ck=None) == ssm.SSM_ERR_NULL
+    assert bwd_ckpt(ck=P[24] + 4) == ssm.SSM_ERR_UNSUPPORTED       # misaligned
+    assert bwd_ckpt(ck_bytes=64) == ssm.SSM_ERR_WORKSPACE          # too small
+    assert bwd_ckpt(ck=P[9]) == ssm.SSM_ERR_ALIAS                  # dx on top of the checkpoints
+    assert bwd_ckpt(ck=P[18]) == ssm.SSM_ERR_ALIAS                 # the workspace on top of them
+    none = {n: None for n in BWD_PTRS}
+    assert bwd_ckpt(**dict(none, ck=None, Bs=0, ED=0, ws_bytes=0)) == ssm.SSM_OK
+
+
+def test_binding_checks_checkpoint_tensors():
+    import torch
+    x = torch.zeros(2, 40, 20)
+    d, B, C = torch.zeros(2, 40, 20), torch.zeros(2, 40, 16), torch.zeros(2, 40, 16)
+    A = torch.zeros(20, 16)
+    with pytest.raises(ValueError, match="ckpt must have shape"):
+        ssm.ssm_scan_fwd(x, d, A, B, C, ckpt=torch.zeros(2, 2, 20, 16))
+    with pytest.raises(TypeError, match="ckpt must be torch.float32"):
+        ssm.ssm_scan_fwd(x, d, A, B, C, ckpt=torch.zeros(2, 2, 32, 16, dtype=torch.float64))
+    with pytest.raises(TypeError):
+        ssm.ssm_scan_bwd(x, d, A, B, C, None, x, ckpt=torch.zeros(2, 2, 32, 16, dtype=torch.bfloat16))
