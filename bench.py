@@ -3,7 +3,9 @@
 One step = one full pass of the scan (discretise, scan over L, C-contraction,
 D skip term, final state) over one batch of synthetic input already resident in
 device memory; for a backward workload, one full backward pass (every
-gradient). Three input sets are rotated so that consecutive steps do not
+gradient); for a training-step workload, the forward pass that also keeps the
+state entering every 32-step round, then the backward pass that reads those
+states instead of rebuilding them. Three input sets are rotated so that consecutive steps do not
 re-read a working set left in the 256 MB last-level cache.
 
 Prints ONE JSON line. `value` is scan elements (Bs*L*ED*N) per second;
@@ -61,10 +63,13 @@ SLOTS_PER_ELEMENT_BIDIR_BWD = 22.0 + EXP_SLOTS
 def alg_bytes(w):
     s = 4 if w["dtype"] == "f32" else 2
     Bs, L, ED, N = w["Bs"], w["L"], w["ED"], w["N"]
+    b = Bs * L * ED * (2 * s + s) + 2 * Bs * L * N * s + 4 * ED * N + 4 * ED
     if w.get("bwd"):
         # read x, delta, dy, B, C, A, D; write dx, ddelta, dB, dC, dA, dD
-        return Bs * L * ED * 5 * s + 4 * Bs * L * N * s + 2 * (4 * ED * N + 4 * ED)
-    b = Bs * L * ED * (2 * s + s) + 2 * Bs * L * N * s + 4 * ED * N + 4 * ED
+        # (a training step adds the forward's bytes; the round states it
+        # keeps for the backward are not counted)
+        bb = Bs * L * ED * 5 * s + 4 * Bs * L * N * s + 2 * (4 * ED * N + 4 * ED)
+        return bb + (b if w.get("train") else 0)
     if w.get("h_last"):
         b += 4 * Bs * ED * N
     return b
@@ -73,6 +78,7 @@ def alg_bytes(w):
 KERNEL_SOURCES = {
     "fwd": ("scan_common.h", "ssm_scan.hip"),
     "bwd": ("scan_common.h", "ssm_scan_bwd.hip"),
+    "train": ("scan_common.h", "ssm_scan.hip", "ssm_scan_bwd.hip"),
     "ssd": ("scan_common.h", "ssm_ssd.hip"),
 }
 
@@ -80,6 +86,8 @@ KERNEL_SOURCES = {
 def kernel_family(workload):
     if workload.startswith("bwd"):
         return "bwd"
+    if workload.startswith("train"):
+        return "train"
     if workload.startswith("ssd"):
         return "ssd"
     return "fwd"
@@ -167,32 +175,40 @@ def cpu_baseline(inp, w, budget_s=20.0):
 
 
 def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
-    """The oracle's backward pass on the first batch rows of the workload (as
-    many as fit the time budget, at least one)."""
+    """The oracle's backward pass (for a training step: its forward pass, then
+    its backward pass) on the first batch rows of the workload (as many as fit
+    the time budget, at least one)."""
     import numpy as np
     import oracle
     threads = oracle_threads()
     Bs = w["Bs"]
+    train = bool(w.get("train"))
 
     def rows(k):
         sub = {n: (v[:k] if v.ndim == 3 else v) for n, v in inp.items()}
         return sub, dy[:k]
 
+    def run(sub, dys):
+        y = oracle.scan(**sub, nthreads=threads)[0] if train else None
+        ref = oracle.scan_bwd(**sub, dy=dys, bidir=bidir, nthreads=threads)
+        return ref if y is None else dict(ref, y=y)
+
     bidir = bool(w["bidir"])
     sub, dys = rows(1)
     t0 = time.perf_counter()
-    ref = oracle.scan_bwd(**sub, dy=dys, bidir=bidir, nthreads=threads)
+    ref = run(sub, dys)
     dt = max(time.perf_counter() - t0, 1e-6)
     k = int(min(Bs, max(1, budget_s / dt)))
     if k > 1:
         sub, dys = rows(k)
         t0 = time.perf_counter()
-        ref = oracle.scan_bwd(**sub, dy=dys, bidir=bidir, nthreads=threads)
+        ref = run(sub, dys)
         dt = time.perf_counter() - t0
     E = k * w["L"] * w["ED"] * w["N"]
     sample = ("all %d batch rows" % Bs) if k == Bs else ("%d of %d batch rows" % (k, Bs))
+    what = "fp64 forward scan, then forward states + adjoint" if train else "fp64 forward states + adjoint"
     return dict(value=E / dt, unit="scan elements/s", **cpu_fields(threads), kind="oracle",
-                sample=sample + " (fp64 forward states + adjoint, %.2f s)" % dt), ref, k
+                sample=sample + " (%s, %.2f s)" % (what, dt)), ref, k
 
 
 # dense fp32 matrix-core peak of the MI355X (the multi-head scan's products run there)
@@ -451,6 +467,7 @@ def main():
 
     nsets = 3
     bwd = bool(w.get("bwd"))
+    train = bool(w.get("train"))
     dcode = ssm.SSM_F32 if w["dtype"] == "f32" else ssm.SSM_BF16
     host_sets, sets = [], []
     for i in range(nsets):
@@ -465,6 +482,11 @@ def main():
                         "dC": torch.empty_like(t["C"]), "dD": torch.empty_like(t["D"])}
             need = (ssm.ssm_scan_bidir_bwd_workspace_bytes if w["bidir"] else ssm.ssm_scan_bwd_workspace_bytes)(
                 Bs, L, ED, N, dcode)
+            if train:
+                t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
+                t["ck"] = torch.empty(ssm.ssm_scan_ckpt_shape(Bs, L, ED), dtype=torch.float32, device=dev)
+                fneed = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, dcode, False)
+                t["fws"] = torch.empty(fneed, dtype=torch.uint8, device=dev) if fneed else None
         else:
             host_sets.append(inp if i == 0 else None)
             t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
@@ -476,7 +498,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(t):
-        if bwd:
+        if train:
+            ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], workspace=t["fws"],
+                             ckpt=t["ck"], stream=stream)
+            ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
+                             workspace=t["ws"], ckpt=t["ck"], stream=stream)
+        elif bwd:
             (ssm.ssm_scan_bidir_bwd if w["bidir"] else ssm.ssm_scan_bwd)(
                              t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
                              workspace=t["ws"], stream=stream)
@@ -512,7 +539,9 @@ def main():
     kernel_elem_rate = E / avg_launch_s
     # bidirectional: the exp and the two multiplies are shared by both
     # directions; algorithmic cost 2 mul + exp + 2 x (state FMA + C FMA) = 8
-    if bwd:
+    if train:
+        slots = SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD
+    elif bwd:
         slots = SLOTS_PER_ELEMENT_BIDIR_BWD if w["bidir"] else SLOTS_PER_ELEMENT_BWD
     else:
         slots = SLOTS_PER_ELEMENT_BIDIR if w["bidir"] else SLOTS_PER_ELEMENT
@@ -530,11 +559,13 @@ def main():
         torch.cuda.synchronize()
         tol = 1e-4 if w["dtype"] == "f32" else 2e-2
         rel = 0.0
-        for name in ("dx", "ddelta", "dB", "dC"):
-            got = sets[0]["out"][name][:k].float().cpu().numpy().astype(np.float64)
+        names = ("y", "dx", "ddelta", "dB", "dC") if train else ("dx", "ddelta", "dB", "dC")
+        for name in names:
+            src = sets[0]["y"] if name == "y" else sets[0]["out"][name]
+            got = src[:k].float().cpu().numpy().astype(np.float64)
             rel = max(rel, float(np.max(np.abs(got - ref[name]) / (1 + np.abs(ref[name])))))
         parity = dict(max_rel_err=rel, tol=tol, passed=bool(rel <= tol),
-                      checked="dx, ddelta, dB, dC of the sampled batch rows")
+                      checked=", ".join(names) + " of the sampled batch rows")
     elif not args.no_cpu:
         cpu, y_ref, chans = cpu_baseline(host_sets[0], w)
         step(sets[0])
@@ -564,7 +595,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; x,B,C,D ~ N(0,1), delta log-uniform [1e-3,1e-1], "
                 "A[e,n] = -(n+1)" + ("; dy ~ N(0,1)" if bwd else "") + "); 3 input sets rotated",
         "config": {"workload": args.workload, "Bs": Bs, "L": L, "ED": ED, "N": N, "bidir": w["bidir"],
-                   "h_last": w["h_last"], "backward": bwd, "parallelism": "single GPU"},
+                   "h_last": w["h_last"], "backward": bwd, "training_step": train, "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
             "achieved": bytes_alg / avg_launch_s / 1e9,
@@ -574,7 +605,10 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": bytes_alg,
             "kernel_avg_us": avg_launch_s * 1e6,
-            "timed": (("whole backward step: the scan kernel (once per direction) and the two small kernels "
+            "timed": (("whole training step: the forward scan kernel (writing the round states), the backward "
+                       "scan kernel and the two small kernels that add up the dB/dC and dA/dD partial sums")
+                      if train else
+                      ("whole backward step: the scan kernel (once per direction) and the two small kernels "
                        "that add up the dB/dC and dA/dD partial sums") if bwd else
                       "the scan kernel (one launch per step)"),
         },

@@ -59,6 +59,14 @@ WORKLOADS = {
     # backward pass of the bidirectional scan at its forward shape
     "bwd_bidir_f32_Bs8_L4096_ED1536_N16": dict(Bs=8, L=4096, ED=1536, N=16, dtype="f32", bidir=True,
                                                h_last=False, bwd=True),
+    # a training step: the forward pass (y, and the state entering every
+    # 32-step round kept for the backward) followed by the backward pass
+    "train_f32_Bs8_L1024_ED1536_N16": dict(Bs=8, L=1024, ED=1536, N=16, dtype="f32", bidir=False, h_last=False,
+                                           bwd=True, train=True),
+    "train_bf16_Bs4_L8192_ED5120_N16": dict(Bs=4, L=8192, ED=5120, N=16, dtype="bf16", bidir=False,
+                                            h_last=False, bwd=True, train=True),
+    "train_f32_Bs1_L131072_ED2048_N16": dict(Bs=1, L=131072, ED=2048, N=16, dtype="f32", bidir=False,
+                                             h_last=False, bwd=True, train=True),
 }
 
 # Multi-head (SSD) workloads: batch 32, seqlen 400, 8 heads is the shape the

@@ -83,3 +83,28 @@ def test_backward_long_sequence_131072():
 
 def test_backward_bidirectional_8x4096x1536():
     run_bwd_workload("bwd_bidir_f32_Bs8_L4096_ED1536_N16")
+
+
+def run_train_workload(name):
+    """The training step: the forward scan keeps the round states, the
+    backward reads them; every gradient against the oracle's adjoint."""
+    from parity_util import assert_grads_close, run_gpu_bwd
+    w = synth.WORKLOADS[name]
+    log("training-step workload %s" % name)
+    inp = synth.workload_inputs(name, seed=0)
+    dy = synth.make_output_grad(w["Bs"], w["L"], w["ED"], w["dtype"], seed=0)
+    got = run_gpu_bwd(inp, dy, want_dh0=True, use_ckpt=True)
+    ref = oracle.scan_bwd(**inp, dy=dy)
+    assert_grads_close(got, ref, w["dtype"])
+
+
+def test_training_step_fp32_8x1024x1536():
+    run_train_workload("train_f32_Bs8_L1024_ED1536_N16")
+
+
+def test_training_step_bf16_4x8192x5120():
+    run_train_workload("train_bf16_Bs4_L8192_ED5120_N16")
+
+
+def test_training_step_long_sequence_131072():
+    run_train_workload("train_f32_Bs1_L131072_ED2048_N16")
