@@ -192,8 +192,9 @@ struct BwdStager {
     chunk_ok = !is_xd || e0 + 4 * chk < ED;
   }
 
-  // global -> registers for round rr of the chunk; WITH_ADJ also loads dy and C
-  template <bool WITH_ADJ>
+  // global -> registers for round rr of the chunk; WITH_ADJ also loads dy and
+  // C; without WITH_FWD, x and B are not loaded (their slots hold zeros)
+  template <bool WITH_ADJ, bool WITH_FWD = true>
   __device__ __forceinline__ void prefetch(const BwdArgs<T>& p, int64_t rr) {
     const int64_t tv = tv0 + rr * RT + row;
     row_ok = tv < tv1;
@@ -202,18 +203,19 @@ struct BwdStager {
     if (row_ok && chunk_ok) {
       if (!is_xd) {
         const int64_t off = (b * L + t) * 16 + 4 * chk;
-        a = Vec4<T>::load(p.B + off);
+        if (WITH_FWD) a = Vec4<T>::load(p.B + off);
         if (WITH_ADJ) bb = Vec4<T>::load(p.C + off);
       } else {
         const int64_t ce = e0 + 4 * chk;
         const int64_t off = (b * L + t) * ED + ce;
         if (VEC) {
-          a = Vec4<T>::load(p.x + off);
+          if (WITH_FWD) a = Vec4<T>::load(p.x + off);
           bb = Vec4<T>::load(p.dl + off);
           if (WITH_ADJ) cc = (OPTS && p.dyf) ? Vec4<float>::load(p.dyf + off) : Vec4<T>::load(p.dy + off);
         } else {
-          a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
-                          ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
+          if (WITH_FWD)
+            a = make_float4(to_f32(p.x[off]), ce + 1 < ED ? to_f32(p.x[off + 1]) : 0.f,
+                            ce + 2 < ED ? to_f32(p.x[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.x[off + 3]) : 0.f);
           bb = make_float4(to_f32(p.dl[off]), ce + 1 < ED ? to_f32(p.dl[off + 1]) : 0.f,
                            ce + 2 < ED ? to_f32(p.dl[off + 2]) : 0.f, ce + 3 < ED ? to_f32(p.dl[off + 3]) : 0.f);
           if (WITH_ADJ && OPTS && p.dyf)
@@ -348,6 +350,9 @@ __device__ __forceinline__ void store_colsums(const BwdArgs<T>& p, const ColSums
 // h (on entry: h0, or zero) folded through chunks 0 .. kchunk-1, and the
 // adjoint k (on entry: dh_last, or zero) folded through chunks nchunks-1 down
 // to kchunk+1, each as s = exp2(A log2e sum delta') s + s_chunk in chunk order.
+// Given the forward scan's checkpoints, the aggregates hold no forward state
+// and h is left as it is (the caller takes the checkpoint of the chunk's
+// first round instead).
 template <typename T>
 __device__ void chunk_entry_states(const BwdArgs<T>& p, int64_t bg, int64_t kchunk, int ch, int g,
                                    const float (&A2)[4], float (&h)[4], float (&k)[4]) {
@@ -360,8 +365,10 @@ __device__ void chunk_entry_states(const BwdArgs<T>& p, int64_t bg, int64_t kchu
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[i] * sdc), v[i], av[i]);
   };
+  if (!p.ck_given) {
 #pragma unroll 4
-  for (int64_t j = 0; j < kchunk; ++j) fold(h, p.agg_h, j);
+    for (int64_t j = 0; j < kchunk; ++j) fold(h, p.agg_h, j);
+  }
 #pragma unroll 4
   for (int64_t j = K - 1; j > kchunk; --j) fold(k, p.agg_k, j);
 }
@@ -372,7 +379,9 @@ __device__ void chunk_entry_states(const BwdArgs<T>& p, int64_t bg, int64_t kchu
 // k = sum_t (prod_{s = t0 .. t} a_s) (dy_t C_t) (each a product of a and the
 // adjoint's own input, accumulated along the chunk). The second pass
 // (scan_bwd_kernel) folds them into the states entering each chunk.
-template <typename T, int SEG, int TS, bool VEC, bool REV, bool OPTS>
+// FWD = false (the forward scan's checkpoints give the forward states): the
+// adjoint and the step sums only, without loading x and B.
+template <typename T, int SEG, int TS, bool VEC, bool REV, bool OPTS, bool FWD>
 __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) void bwd_chunk_agg_kernel(
     const BwdArgs<T> p) {
   constexpr int RT = SEG * TS;
@@ -410,28 +419,30 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   float hc[4] = {0.f, 0.f, 0.f, 0.f};  // forward state (wave SEG-1)
   float kc[4] = {0.f, 0.f, 0.f, 0.f};  // adjoint at the chunk's start, so far (wave SEG-1)
   double sdc = 0.0;                    // sum of delta' before the current segment (wave SEG-1)
-  st.template prefetch<true>(p, 0);
+  st.template prefetch<true, FWD>(p, 0);
   st.template commit<true>(p, tile[0]);
   __syncthreads();
   for (int64_t r = 0; r < R; ++r) {
     rotate_priority(r, p.rot_ncu);
     BwdTile<RT>& cur = tile[r & 1];
     BwdTile<RT>& nxt = tile[(r + 1) & 1];
-    if (r + 1 < R) st.template prefetch<true>(p, r + 1);
+    if (r + 1 < R) st.template prefetch<true, FWD>(p, r + 1);
     // this wave's segment from zero: the forward end state, and the adjoint
     // at the segment's start (backwards over its steps)
     float av[TS][4], hl[4] = {0.f, 0.f, 0.f, 0.f}, kl[4] = {0.f, 0.f, 0.f, 0.f}, sd = 0.f;
 #pragma unroll
     for (int i = 0; i < TS; ++i) {
       const int row = wave * TS + i;
-      const float dt = cur.dt[row][ch], dxv = dt * cur.xv[row][ch];
-      const float bq = cur.bc[row][q].x;
+      const float dt = cur.dt[row][ch];
       sd += dt;
-      const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
-        hl[j] = __builtin_fmaf(av[i][j], hl[j], dxv * bb[j]);
+      for (int j = 0; j < 4; ++j) av[i][j] = __builtin_amdgcn_exp2f(dt * A2[j]);
+      if constexpr (FWD) {
+        const float dxv = dt * cur.xv[row][ch];
+        const float bq = cur.bc[row][q].x;
+        const float bb[4] = {quad_bcast<0>(bq), quad_bcast<1>(bq), quad_bcast<2>(bq), quad_bcast<3>(bq)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hl[j] = __builtin_fmaf(av[i][j], hl[j], dxv * bb[j]);
       }
     }
 #pragma unroll
@@ -441,9 +452,11 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int j = 0; j < 4; ++j) kl[j] *= av[i][j];
     }
-    fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
-                                   __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
-    fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+    if constexpr (FWD) {
+      fa.A[wave][lane] = make_float4(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd),
+                                     __builtin_amdgcn_exp2f(A2[2] * sd), __builtin_amdgcn_exp2f(A2[3] * sd));
+      fa.H[wave][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+    }
     fa.K[wave][lane] = make_float4(kl[0], kl[1], kl[2], kl[3]);
     sds[wave][lane] = sd;
     __syncthreads();
@@ -452,15 +465,18 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
         // the segment's adjoint reaches the chunk's start through every step
         // before it: the product from the float64 sum of delta' so far
         const float cum = static_cast<float>(sdc);
-        const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane], Kk = fa.K[k][lane];
+        const float4 Kk = fa.K[k][lane];
         kc[0] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[0] * cum), Kk.x, kc[0]);
         kc[1] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[1] * cum), Kk.y, kc[1]);
         kc[2] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[2] * cum), Kk.z, kc[2]);
         kc[3] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[3] * cum), Kk.w, kc[3]);
-        hc[0] = __builtin_fmaf(Ak.x, hc[0], Hk.x);
-        hc[1] = __builtin_fmaf(Ak.y, hc[1], Hk.y);
-        hc[2] = __builtin_fmaf(Ak.z, hc[2], Hk.z);
-        hc[3] = __builtin_fmaf(Ak.w, hc[3], Hk.w);
+        if constexpr (FWD) {
+          const float4 Ak = fa.A[k][lane], Hk = fa.H[k][lane];
+          hc[0] = __builtin_fmaf(Ak.x, hc[0], Hk.x);
+          hc[1] = __builtin_fmaf(Ak.y, hc[1], Hk.y);
+          hc[2] = __builtin_fmaf(Ak.z, hc[2], Hk.z);
+          hc[3] = __builtin_fmaf(Ak.w, hc[3], Hk.w);
+        }
         sdc += static_cast<double>(sds[k][lane]);
       }
     }
@@ -470,7 +486,8 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
   if (wave == SEG - 1) {
     const int64_t slot = bg * p.nchunks + kchunk;
     if (g == 0) p.agg_sd[slot * 16 + ch] = sdc;
-    *reinterpret_cast<float4*>(p.agg_h + slot * 256 + ch * 16 + 4 * g) = make_float4(hc[0], hc[1], hc[2], hc[3]);
+    if (FWD)
+      *reinterpret_cast<float4*>(p.agg_h + slot * 256 + ch * 16 + 4 * g) = make_float4(hc[0], hc[1], hc[2], hc[3]);
     *reinterpret_cast<float4*>(p.agg_k + slot * 256 + ch * 16 + 4 * g) = make_float4(kc[0], kc[1], kc[2], kc[3]);
   }
 }
@@ -543,6 +560,12 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(3))) v
     kend[0] = v.x, kend[1] = v.y, kend[2] = v.z, kend[3] = v.w;
   }
   if (p.nchunks > 1) chunk_entry_states(p, bg, kchunk, ch, g, A2, hstart, kend);
+  if (p.ck_given && kchunk > 0) {
+    // the forward scan's checkpoint of the chunk's first round (chunks start
+    // on round boundaries)
+    const float4 v = *reinterpret_cast<const float4*>(ck(0));
+    hstart[0] = v.x, hstart[1] = v.y, hstart[2] = v.z, hstart[3] = v.w;
+  }
 
   // ---- sweep 1: forward round aggregates -> checkpoints --------------------
   // (not when the caller passes the forward scan's checkpoints)
@@ -1020,21 +1043,34 @@ int bwd_validate(const void* x, const void* delta, const float* A, const void* B
   return SSM_OK;
 }
 
+template <typename T, bool REV, bool FWD>
+void launch_agg(const BwdArgs<T>& a, int64_t nblk, bool vec, hipStream_t stream) {
+  if (a.dt_pre) {
+    if (vec)
+      hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, true, REV, true, FWD>), dim3(nblk), dim3(64 * kBSEG), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, false, REV, true, FWD>), dim3(nblk), dim3(64 * kBSEG),
+                         0, stream, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, true, REV, false, FWD>), dim3(nblk), dim3(64 * kBSEG),
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, false, REV, false, FWD>), dim3(nblk), dim3(64 * kBSEG),
+                         0, stream, a);
+  }
+}
+
 template <typename T, bool REV>
 void launch_bwd_kernel(const BwdArgs<T>& a, int64_t nblk, size_t dyn, bool vec, hipStream_t stream) {
   if (a.nchunks > 1) {
-    // the chunks' aggregates first (same grid; the launch order on the stream joins them)
-    if (a.dt_pre) {
-      if (vec)
-        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, true, REV, true>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
-      else
-        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, false, REV, true>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
-    } else {
-      if (vec)
-        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, true, REV, false>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
-      else
-        hipLaunchKernelGGL((bwd_chunk_agg_kernel<T, kBSEG, kBTS, false, REV, false>), dim3(nblk), dim3(64 * kBSEG), 0, stream, a);
-    }
+    // the chunks' aggregates first (same grid; the launch order on the stream
+    // joins them); with the forward scan's checkpoints, the adjoint's only
+    if (a.ck_given)
+      launch_agg<T, REV, false>(a, nblk, vec, stream);
+    else
+      launch_agg<T, REV, true>(a, nblk, vec, stream);
   }
   if (a.dt_pre) {
     if (vec)
