@@ -492,39 +492,43 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 // instruction, v_mfma_f32_16x16x32_bf16 (float32 accumulation; 16 times the
 // float32 instruction's rate). C, B and x are bf16 already and enter exactly.
 // The float32 operands -- the decayed, masked C B^T, the state (kept float32
-// in registers; its LDS copy is the operand) and the decay-weighted B of the
-// state update -- are split into a high and a low bf16 part, v = hi + lo with
-// hi = bf16(v) and lo = bf16(v - hi) (round to nearest even), and each product
-// takes both parts: the operand error is then below 2^-17 |v|, so the state
-// and the output keep float32-level accuracy.
+// in the accumulators, which are also its operand) and the decay-weighted x
+// of the state update -- are split into a high and a low bf16 part, v = hi +
+// lo with hi = bf16(v) and lo = bf16(v - hi) (round to nearest even), and
+// each product takes both parts: the operand error is then below 2^-17 |v|,
+// so the state and the output keep float32-level accuracy.
 //
 // Operand layout (16 x 16 x 32, one wave): lane l supplies the 8 consecutive
 // k = 8 (l / 16) .. 8 (l / 16) + 7 of row l % 16 of A and of column l % 16 of
 // B, i.e. one 16-byte read of a k-contiguous LDS row; result register r of
 // lane l is D[4 (l / 16) + r][l % 16]. Products over the state index n read
-// n-contiguous tiles (C[t][n], B[s][n], S[p][n]); products over the chunk's
-// steps read s-contiguous ones (M[t][s], x transposed to Xt[p][s]).
+// n-contiguous tiles (C[t][n], B[s][n]); products over the chunk's steps
+// read s-contiguous ones (M[t][s], x transposed to Xt[p][s]). Two result
+// tiles whose registers hold the state's n = 32 g + 8 (l / 16) + 0..3 and
+// + 4..7 are together the operand B of a product over n with C[t][32 g ..]
+// read as usual, so the state never leaves the registers.
 //
 // Twelve waves: eight compute waves own the state and the output blocks and
-// run only products over LDS tiles; four staging waves move data and form
-// each chunk's masked C B^T, so that this work overlaps the products instead
-// of adding to them. Two of the staging waves only load and commit tiles
+// run only products; four staging waves move data and form each chunk's
+// masked C B^T, so that this work overlaps the products instead of adding to
+// them. Two of the staging waves only load and commit tiles
 // (16-byte global loads into registers in phase 1, committed in phase 2),
 // the other two only store y; a wave that waits for its loads then has no
 // stores outstanding (stores count in the same counter). Per chunk, two
 // barriers:
-//   phase 1  compute waves: their 16 x 16 block of diag(e^{cs}) C S_in^T and
-//            the update of their state blocks, S^T = e^{cs_end} S^T +
-//            (w B)^T X (so that a lane holds 4 consecutive n of one p).
+//   phase 1  compute waves: diag(e^{cs}) C S_in^T over the wave's half of
+//            the states for both 16-step blocks (one goes to LDS for the
+//            wave that owns it), and the update of the wave's state tiles,
+//            S^T = e^{cs_end} S^T + B^T (w X) (so that a lane holds 4
+//            consecutive n of one p).
 //            Staging waves: the chunk's three causal 16 x 16 blocks of C B^T
 //            (computed as B C^T so that a lane holds 4 consecutive s of one
 //            t) -> masked, decayed M (bf16 pair); store y of the previous
 //            chunk; issue the loads of the next chunk
-//   phase 2  compute waves: M X added to the output block, + D x -> Y
-//            (float32, by chunk parity); bf16 pair copy of the new state
-//            (8-byte stores). Loading waves: commit the next chunk's tiles
-//            and form its decays (the last loading wave: a prefix sum over
-//            the lanes (DPP) of the step sizes it loaded)
+//   phase 2  compute waves: the other half's C S_in^T block, M X, + D x
+//            -> Y (float32, by chunk parity). Loading waves: commit the next
+//            chunk's tiles and form its decays (the last loading wave: a
+//            prefix sum over the lanes (DPP) of the step sizes it loaded)
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -557,17 +561,19 @@ struct alignas(16) SsdSmemBf {
   // Row pitches (elements). With lanes on rows and 16-byte column blocks, a
   // 16-byte read is free of bank conflicts when the pitch in bytes is 32 mod
   // 64, an 8-byte access when it is 16 mod 64 (measured on gfx950): C is
-  // only read and written 16 bytes at a time; the state copy and Xt also
-  // take 8-byte stores or reads, and B 2-byte column reads (rows 4 apart).
+  // only read and written 16 bytes at a time; Xt also takes 8-byte reads,
+  // and B 2-byte column reads (rows 4 apart).
   static constexpr int NPC = N + 16;  // C
-  static constexpr int NP = N + 8;    // B and the state copy
+  static constexpr int NP = N + 8;    // B
   static constexpr int TP = kQ + 8;   // the s-contiguous tiles
   uint16_t C[2][kQ][NPC];  // C chunk [t][n]
   uint16_t B[2][kQ][NP];   // B chunk [s][n]
   uint16_t Xt[2][kP][TP];  // x chunk, transposed [p][s]
-  uint16_t S[2][kP][NP];   // state entering the chunk [p][n]: high, low bf16 part
   uint16_t M[2][2][kQ][TP];  // masked, decayed C B^T [t][s] by chunk parity: high, low part
   float Y[2][kQ][kP + 4];  // y of a chunk (with D x), by chunk parity
+  // the inter-chunk output block (t-block, p-block) over one half of the
+  // states, [p][t] within the block, from the wave that does not own it
+  float Yx[2][4][16][24];
   float dt[2][kQ];
   float cs[2][kQ];         // A * inclusive cumulative dt within the chunk
   float ecs[2][kQ];        // e^{cs_t}
@@ -721,25 +727,13 @@ __device__ __forceinline__ float4 load_partial(const SsdArgs<uint16_t>& p, int s
   return *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + t) * p.H + h) * kP + c4);
 }
 
-// S[p][n0 .. n0+3] (high and low bf16 parts) from 4 float32 values
-template <int N>
-__device__ __forceinline__ void store_state_bf16(SsdSmemBf<N>& sm, int pp, int n0, f4 v) {
-  uint32_t h01, l01, h23, l23;
-  split_pack_bf16(v[0], v[1], h01, l01);
-  split_pack_bf16(v[2], v[3], h23, l23);
-  *reinterpret_cast<uint2*>(&sm.S[0][pp][n0]) = make_uint2(h01, h23);
-  *reinterpret_cast<uint2*>(&sm.S[1][pp][n0]) = make_uint2(l01, l23);
-}
-
 // One sweep of the bf16 kernel over the chunks [blk.c0, blk.c1) of a
 // (batch row, head): REV runs in decreasing time (chunk k of the sweep holds
 // times L-1-32k .. L-32-32k) from g0, else in increasing time from h0.
 template <int N, bool BIDIR, bool GATE, bool AGG, bool REV>
 __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSmemBf<N>& sm, const SsdBlock& blk,
                                                float Dfwd, float bias) {
-  constexpr int NB = N / 16;       // state column blocks
-  constexpr int PBW = 4 * NB / 8;  // state row blocks per compute wave (its column block is wave % NB)
-  constexpr int KN = N / 32;       // products over n: instructions per 16 x 16 block
+  constexpr int KN = N / 32;  // products over n: instructions per 16 x 16 block
   constexpr bool rev = REV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -756,14 +750,24 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
   // Both roles run the same chunk loop with the same two barriers per chunk.
   if (wave < kMainBf) {
     // ================= compute waves =================
-    const int ytb = wave >> 2, ypb = wave & 3;           // output block (t-block, p-block)
-    const int snb = wave % NB, spb = (wave / NB) * PBW;  // state blocks
+    // Wave (pb, nh) owns the state columns p = 16 pb .. 16 pb + 15 for half nh
+    // of the states n, in accumulators, and the output block (t-block nh,
+    // p-block pb). State tile k = 2 kg + ab: register r of lane (li, lk) is
+    // S[n][p], p = 16 pb + li, n = N/2 nh + 32 kg + 8 lk + 4 ab + r. Its two
+    // tiles of group kg, read as one register row, are then the operand B
+    // (k = n, column p) of a product over n: lane (li, lk) holds n = 32 kg' +
+    // 8 lk .. 8 lk + 7, the same k order as a 16-byte read of C[t][n]. The
+    // state is its own operand: no copy of it goes through LDS.
+    constexpr int KG = N / 64;    // 32-state groups per half
+    constexpr int NTL = 2 * KG;   // state tiles per wave
+    const int pb = wave & 3, nh = wave >> 2;
+    const int pp = 16 * pb + li;
+    auto tile_n0 = [&](int k) { return (N / 2) * nh + 32 * (k >> 1) + 8 * lk + 4 * (k & 1); };
 
-    // st[k][r] = S[p][n], p = 16 (spb + k) + li, n = 16 snb + 4 lk + r
-    f4 st[PBW];
+    f4 st[NTL];
 #pragma unroll
-    for (int k = 0; k < PBW; ++k) {
-      const int pp = 16 * (spb + k) + li, n0 = 16 * snb + 4 * lk;
+    for (int k = 0; k < NTL; ++k) {
+      const int n0 = tile_n0(k);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = 0.f;
@@ -774,7 +778,6 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         }
         st[k][r] = v;
       }
-      if (!AGG) store_state_bf16(sm, pp, n0, st[k]);
     }
     double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
     __syncthreads();
@@ -784,74 +787,95 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
       // ---- phase 1 ----
       if (AGG && tid == 0) cs_sum += static_cast<double>(sm.cs_end[cur]);
 
-      // inter-chunk output of the wave's block: diag(e^{cs}) C S_in^T
+      // inter-chunk output over this half of the states, both t-blocks:
+      // diag(e^{cs}) C S_in^T; the partner wave (pb, 1 - nh) gets the block
+      // it owns, this wave keeps its own
       f4 y = {0.f, 0.f, 0.f, 0.f};
       if (!AGG) {
-        uint4 ca[KN], sh[KN], sl[KN];
+        uint4 sh[KG], sl[KG];
 #pragma unroll
-        for (int j = 0; j < KN; ++j) {
-          ca[j] = *reinterpret_cast<const uint4*>(&sm.C[cur][16 * ytb + li][32 * j + 8 * lk]);
-          sh[j] = *reinterpret_cast<const uint4*>(&sm.S[0][16 * ypb + li][32 * j + 8 * lk]);
-          sl[j] = *reinterpret_cast<const uint4*>(&sm.S[1][16 * ypb + li][32 * j + 8 * lk]);
-        }
-        f4 a = {0.f, 0.f, 0.f, 0.f}, a2 = a;
-#pragma unroll
-        for (int j = 0; j < KN; ++j) {
-          a = mfma_bf16(ca[j], sh[j], a);
-          a2 = mfma_bf16(ca[j], sl[j], a2);
+        for (int kg = 0; kg < KG; ++kg) {
+          uint32_t h0a, l0a, h1a, l1a, h0b, l0b, h1b, l1b;
+          split_pack_bf16(st[2 * kg][0], st[2 * kg][1], h0a, l0a);
+          split_pack_bf16(st[2 * kg][2], st[2 * kg][3], h1a, l1a);
+          split_pack_bf16(st[2 * kg + 1][0], st[2 * kg + 1][1], h0b, l0b);
+          split_pack_bf16(st[2 * kg + 1][2], st[2 * kg + 1][3], h1b, l1b);
+          sh[kg] = make_uint4(h0a, h1a, h0b, h1b);
+          sl[kg] = make_uint4(l0a, l1a, l0b, l1b);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (a[r] + a2[r]) * sm.ecs[cur][16 * ytb + 4 * lk + r];
+        for (int tb = 0; tb < 2; ++tb) {
+          f4 a = {0.f, 0.f, 0.f, 0.f}, a2 = a;
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg) {
+            const uint4 ca =
+                *reinterpret_cast<const uint4*>(&sm.C[cur][16 * tb + li][(N / 2) * nh + 32 * kg + 8 * lk]);
+            a = mfma_bf16(ca, sh[kg], a);
+            a2 = mfma_bf16(ca, sl[kg], a2);
+          }
+          const float4 e = *reinterpret_cast<const float4*>(&sm.ecs[cur][16 * tb + 4 * lk]);
+          const f4 v = {(a[0] + a2[0]) * e.x, (a[1] + a2[1]) * e.y, (a[2] + a2[2]) * e.z, (a[3] + a2[3]) * e.w};
+          if (tb == nh) y = v;
+          else *reinterpret_cast<float4*>(&sm.Yx[tb][pb][li][4 * lk]) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
 
-      // state update of the wave's blocks: S^T = e^{cs_end} S^T + (w B)^T X
+      // state update: S^T = e^{cs_end} S^T + B^T (w X), the weights on x
       {
         const float dec = __expf(sm.cs_end[cur]);
 #pragma unroll
-        for (int k = 0; k < PBW; ++k) st[k] *= dec;
-        // operand A: (w B)^T[n][s] = w_s B[s][n] for n = 16 snb + li. The sum
-        // over s does not depend on which k slot holds which s as long as both
-        // operands agree: the lane's 8 slots hold s = 4 lk .. 4 lk + 3 and
-        // 16 + 4 lk .. 16 + 4 lk + 3, so that the lanes' column reads of B fall
-        // on rows 4 apart (distinct LDS banks).
-        uint32_t bhi[4], blo[4];
+        for (int k = 0; k < NTL; ++k) st[k] *= dec;
+        // operand B: w_s X[s][p] for p = pp. The sum over s does not depend on
+        // which k slot holds which s as long as both operands agree: the lane's
+        // 8 slots hold s = 4 lk .. 4 lk + 3 and 16 + 4 lk .. 16 + 4 lk + 3, so
+        // that the lanes' column reads of B fall on rows 4 apart (distinct LDS
+        // banks).
+        const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][pp][4 * lk]);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][pp][16 + 4 * lk]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[cur][4 * lk]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[cur][16 + 4 * lk]);
+        uint32_t xh[4], xl[4];
+        split_pack_bf16(bf_lo(x0.x) * w0.x, bf_hi(x0.x) * w0.y, xh[0], xl[0]);
+        split_pack_bf16(bf_lo(x0.y) * w0.z, bf_hi(x0.y) * w0.w, xh[1], xl[1]);
+        split_pack_bf16(bf_lo(x1.x) * w1.x, bf_hi(x1.x) * w1.y, xh[2], xl[2]);
+        split_pack_bf16(bf_lo(x1.y) * w1.z, bf_hi(x1.y) * w1.w, xh[3], xl[3]);
+        const uint4 xoh = make_uint4(xh[0], xh[1], xh[2], xh[3]), xol = make_uint4(xl[0], xl[1], xl[2], xl[3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s0 = (i < 2 ? 0 : 16) + 4 * lk + 2 * (i & 1);
-          const float b0 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0][16 * snb + li]) << 16);
-          const float b1 = __uint_as_float(static_cast<uint32_t>(sm.B[cur][s0 + 1][16 * snb + li]) << 16);
-          split_pack_bf16(b0 * sm.w[cur][s0], b1 * sm.w[cur][s0 + 1], bhi[i], blo[i]);
-        }
-        const uint4 boh = make_uint4(bhi[0], bhi[1], bhi[2], bhi[3]), bol = make_uint4(blo[0], blo[1], blo[2], blo[3]);
+        for (int k = 0; k < NTL; ++k) {
+          // operand A: B^T[n][s] = B[s][n] for the tile's row li, n = N/2 nh +
+          // 32 kg + 8 (li / 4) + 4 ab + li % 4 (the row order of the tile)
+          const int nr = (N / 2) * nh + 32 * (k >> 1) + 8 * (li >> 2) + 4 * (k & 1) + (li & 3);
+          uint32_t bt[4];
 #pragma unroll
-        for (int k = 0; k < PBW; ++k) {
-          // operand B: X[s][p] = Xt[p][s], p = 16 (spb + k) + li, the same s slots
-          const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][4 * lk]);
-          const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * (spb + k) + li][16 + 4 * lk]);
-          const uint4 xa = make_uint4(x0.x, x0.y, x1.x, x1.y);
-          st[k] = mfma_bf16(boh, xa, st[k]);
-          st[k] = mfma_bf16(bol, xa, st[k]);
+          for (int i = 0; i < 4; ++i) {
+            const int s0 = (i < 2 ? 0 : 16) + 4 * lk + 2 * (i & 1);
+            bt[i] = static_cast<uint32_t>(sm.B[cur][s0][nr]) | (static_cast<uint32_t>(sm.B[cur][s0 + 1][nr]) << 16);
+          }
+          const uint4 ba = make_uint4(bt[0], bt[1], bt[2], bt[3]);
+          st[k] = mfma_bf16(ba, xoh, st[k]);
+          st[k] = mfma_bf16(ba, xol, st[k]);
         }
       }
-      __syncthreads();  // the next chunk's tiles committed; every read of S_in done
+      __syncthreads();  // the next chunk's tiles committed; the partner's block written
 
       // ---- phase 2 ----
       if (!AGG) {
-        // intra-chunk output M X (M is zero above the diagonal), then + D x
-        const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[cur][0][16 * ytb + li][8 * lk]);
-        const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[cur][1][16 * ytb + li][8 * lk]);
-        const uint4 xb = *reinterpret_cast<const uint4*>(&sm.Xt[cur][16 * ypb + li][8 * lk]);
+        // the partner's half of the inter-chunk block, then M X (M is zero
+        // above the diagonal) and D x
+        const float4 o = *reinterpret_cast<const float4*>(&sm.Yx[nh][pb][li][4 * lk]);
+        y[0] += o.x, y[1] += o.y, y[2] += o.z, y[3] += o.w;
+        const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[cur][0][16 * nh + li][8 * lk]);
+        const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[cur][1][16 * nh + li][8 * lk]);
+        const uint4 xb = *reinterpret_cast<const uint4*>(&sm.Xt[cur][pp][8 * lk]);
         y = mfma_bf16(mh, xb, y);
         y = mfma_bf16(ml, xb, y);
-        const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xt[cur][16 * ypb + li][16 * ytb + 4 * lk]);
+        const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xt[cur][pp][16 * nh + 4 * lk]);
         y[0] += Dh * bf_lo(xv.x);
         y[1] += Dh * bf_hi(xv.x);
         y[2] += Dh * bf_lo(xv.y);
         y[3] += Dh * bf_hi(xv.y);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.Y[cur][16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
-#pragma unroll
-        for (int k = 0; k < PBW; ++k) store_state_bf16(sm, 16 * (spb + k) + li, 16 * snb + 4 * lk, st[k]);
+        for (int r = 0; r < 4; ++r) sm.Y[cur][16 * nh + 4 * lk + r][pp] = y[r];
       }
       __syncthreads();
     }
@@ -859,16 +883,16 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
       // the range's end state from zero and its decay exponent
       const int64_t slot = blk.range * (p.nblocks / p.nranges) + bh;
 #pragma unroll
-      for (int k = 0; k < PBW; ++k)
-        *reinterpret_cast<float4*>(p.agg_S + (slot * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+      for (int k = 0; k < NTL; ++k)
+        *reinterpret_cast<float4*>(p.agg_S + (slot * kP + pp) * N + tile_n0(k)) =
             make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
       if (tid == 0) p.agg_cs[slot] = cs_sum;
     } else {
       float* const fin = rev ? p.g_first : p.h_last;
       if (fin && blk.range == p.nranges - 1) {
 #pragma unroll
-        for (int k = 0; k < PBW; ++k)
-          *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + 16 * (spb + k) + li) * N + 16 * snb + 4 * lk) =
+        for (int k = 0; k < NTL; ++k)
+          *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + pp) * N + tile_n0(k)) =
               make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
       }
     }
