@@ -503,7 +503,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 // B, i.e. one 16-byte read of a k-contiguous LDS row; result register r of
 // lane l is D[4 (l / 16) + r][l % 16]. Products over the state index n read
 // n-contiguous tiles (C[t][n], B[s][n]); products over the chunk's steps
-// read s-contiguous ones (M[t][s], x transposed to Xt[p][s]). Two result
+// read M[t][s] as it is and x[s][p], B[s][n] by transposing reads. Two result
 // tiles whose registers hold the state's n = 32 g + 8 (l / 16) + 0..3 and
 // + 4..7 are together the operand B of a product over n with C[t][32 g ..]
 // read as usual, so the state never leaves the registers.
@@ -554,6 +554,18 @@ __device__ __forceinline__ void split_pack_bf16(float a, float b, uint32_t& hi, 
   lo = pack_bf16(a - static_cast<float>(h[0]), b - static_cast<float>(h[1]));
 }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+// Transposing LDS read of 16-bit elements (gfx950): within each group of 16
+// lanes, lane i receives as element j the element i % 4 of the 8 bytes that
+// lane 4 j + i / 4 of its group addresses (checked on the GPU with a probe).
+// So if lane 4 j + q addresses 4 consecutive columns 4 q .. 4 q + 3 of row
+// r0 + j of a row-major tile, lane i receives column i of rows r0 .. r0 + 3:
+// a k-contiguous operand read from a tile stored the other way round.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr16(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 template <int N>
@@ -561,14 +573,15 @@ struct alignas(16) SsdSmemBf {
   // Row pitches (elements). With lanes on rows and 16-byte column blocks, a
   // 16-byte read is free of bank conflicts when the pitch in bytes is 32 mod
   // 64, an 8-byte access when it is 16 mod 64 (measured on gfx950): C is
-  // only read and written 16 bytes at a time; Xt also takes 8-byte reads,
-  // and B 2-byte column reads (rows 4 apart).
+  // only read and written 16 bytes at a time; B and x also take 8-byte
+  // transposing reads.
   static constexpr int NPC = N + 16;  // C
   static constexpr int NP = N + 8;    // B
   static constexpr int TP = kQ + 8;   // the s-contiguous tiles
+  static constexpr int XP = kP + 8;   // x
   uint16_t C[2][kQ][NPC];  // C chunk [t][n]
   uint16_t B[2][kQ][NP];   // B chunk [s][n]
-  uint16_t Xt[2][kP][TP];  // x chunk, transposed [p][s]
+  uint16_t X[2][kQ][XP];   // x chunk [s][p]
   uint16_t M[2][2][kQ][TP];  // masked, decayed C B^T [t][s] by chunk parity: high, low part
   float Y[2][kQ][kP + 4];  // y of a chunk (with D x), by chunk parity
   // the inter-chunk output block (t-block, p-block) over one half of the
@@ -646,12 +659,7 @@ struct SsdStagerBf {
 #pragma unroll
     for (int k = 0; k < kXT; ++k) {
       const int row = st % kQ, c8 = (st / kQ + k * (NT / kQ)) * 8;
-      const uint32_t w[4] = {rx[k].x, rx[k].y, rx[k].z, rx[k].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sm.Xt[buf][c8 + 2 * j][row] = static_cast<uint16_t>(w[j]);
-        sm.Xt[buf][c8 + 2 * j + 1][row] = static_cast<uint16_t>(w[j] >> 16);
-      }
+      *reinterpret_cast<uint4*>(&sm.X[buf][row][c8]) = rx[k];
     }
 #pragma unroll
     for (int k = 0; k < kBT; ++k) {
@@ -821,37 +829,33 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
       }
 
       // state update: S^T = e^{cs_end} S^T + B^T (w X), the weights on x
+      uint2 xs0, xs1;  // x[8 lk .. 8 lk + 7][pp], the k slots of the products over s
       {
         const float dec = __expf(sm.cs_end[cur]);
 #pragma unroll
         for (int k = 0; k < NTL; ++k) st[k] *= dec;
-        // operand B: w_s X[s][p] for p = pp. The sum over s does not depend on
-        // which k slot holds which s as long as both operands agree: the lane's
-        // 8 slots hold s = 4 lk .. 4 lk + 3 and 16 + 4 lk .. 16 + 4 lk + 3, so
-        // that the lanes' column reads of B fall on rows 4 apart (distinct LDS
-        // banks).
-        const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][pp][4 * lk]);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.Xt[cur][pp][16 + 4 * lk]);
-        const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[cur][4 * lk]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[cur][16 + 4 * lk]);
+        // operand B: w_s X[s][p] for p = pp, s = 8 lk .. 8 lk + 7 (the k slots
+        // of the lane), by two transposing reads of x (kept for M X below)
+        xs0 = read_tr16(&sm.X[cur][8 * lk + (li >> 2)][16 * pb + 4 * (li & 3)]);
+        xs1 = read_tr16(&sm.X[cur][8 * lk + 4 + (li >> 2)][16 * pb + 4 * (li & 3)]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[cur][8 * lk]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[cur][8 * lk + 4]);
         uint32_t xh[4], xl[4];
-        split_pack_bf16(bf_lo(x0.x) * w0.x, bf_hi(x0.x) * w0.y, xh[0], xl[0]);
-        split_pack_bf16(bf_lo(x0.y) * w0.z, bf_hi(x0.y) * w0.w, xh[1], xl[1]);
-        split_pack_bf16(bf_lo(x1.x) * w1.x, bf_hi(x1.x) * w1.y, xh[2], xl[2]);
-        split_pack_bf16(bf_lo(x1.y) * w1.z, bf_hi(x1.y) * w1.w, xh[3], xl[3]);
+        split_pack_bf16(bf_lo(xs0.x) * w0.x, bf_hi(xs0.x) * w0.y, xh[0], xl[0]);
+        split_pack_bf16(bf_lo(xs0.y) * w0.z, bf_hi(xs0.y) * w0.w, xh[1], xl[1]);
+        split_pack_bf16(bf_lo(xs1.x) * w1.x, bf_hi(xs1.x) * w1.y, xh[2], xl[2]);
+        split_pack_bf16(bf_lo(xs1.y) * w1.z, bf_hi(xs1.y) * w1.w, xh[3], xl[3]);
         const uint4 xoh = make_uint4(xh[0], xh[1], xh[2], xh[3]), xol = make_uint4(xl[0], xl[1], xl[2], xl[3]);
 #pragma unroll
         for (int k = 0; k < NTL; ++k) {
-          // operand A: B^T[n][s] = B[s][n] for the tile's row li, n = N/2 nh +
-          // 32 kg + 8 (li / 4) + 4 ab + li % 4 (the row order of the tile)
-          const int nr = (N / 2) * nh + 32 * (k >> 1) + 8 * (li >> 2) + 4 * (k & 1) + (li & 3);
-          uint32_t bt[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int s0 = (i < 2 ? 0 : 16) + 4 * lk + 2 * (i & 1);
-            bt[i] = static_cast<uint32_t>(sm.B[cur][s0][nr]) | (static_cast<uint32_t>(sm.B[cur][s0 + 1][nr]) << 16);
-          }
-          const uint4 ba = make_uint4(bt[0], bt[1], bt[2], bt[3]);
+          // operand A: B^T[n][s] = B[s][n] for the tile's rows, n = N/2 nh +
+          // 32 kg + 8 (li / 4) + 4 ab + li % 4 for lane row li, by two
+          // transposing reads (lane li's address: row 8 lk + li / 4 (+ 4),
+          // columns from the tile row order's 4-column group li % 4)
+          const int nc = (N / 2) * nh + 32 * (k >> 1) + 8 * (li & 3) + 4 * (k & 1);
+          const uint2 b0 = read_tr16(&sm.B[cur][8 * lk + (li >> 2)][nc]);
+          const uint2 b1 = read_tr16(&sm.B[cur][8 * lk + 4 + (li >> 2)][nc]);
+          const uint4 ba = make_uint4(b0.x, b0.y, b1.x, b1.y);
           st[k] = mfma_bf16(ba, xoh, st[k]);
           st[k] = mfma_bf16(ba, xol, st[k]);
         }
@@ -866,10 +870,11 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         y[0] += o.x, y[1] += o.y, y[2] += o.z, y[3] += o.w;
         const uint4 mh = *reinterpret_cast<const uint4*>(&sm.M[cur][0][16 * nh + li][8 * lk]);
         const uint4 ml = *reinterpret_cast<const uint4*>(&sm.M[cur][1][16 * nh + li][8 * lk]);
-        const uint4 xb = *reinterpret_cast<const uint4*>(&sm.Xt[cur][pp][8 * lk]);
+        const uint4 xb = make_uint4(xs0.x, xs0.y, xs1.x, xs1.y);
         y = mfma_bf16(mh, xb, y);
         y = mfma_bf16(ml, xb, y);
-        const uint2 xv = *reinterpret_cast<const uint2*>(&sm.Xt[cur][pp][16 * nh + 4 * lk]);
+        // x[16 nh + 4 lk + r][pp] for the lane's output rows r
+        const uint2 xv = read_tr16(&sm.X[cur][16 * nh + 4 * lk + (li >> 2)][16 * pb + 4 * (li & 3)]);
         y[0] += Dh * bf_lo(xv.x);
         y[1] += Dh * bf_hi(xv.x);
         y[2] += Dh * bf_lo(xv.y);
