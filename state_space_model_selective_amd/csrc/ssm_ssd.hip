@@ -549,9 +549,9 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = bf16_bits(v - static_cast<float>(h));
 }
 __device__ __forceinline__ void split_pack_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = pack_bf16(a - static_cast<float>(h[0]), b - static_cast<float>(h[1]));
+  hi = pack_bf16(a, b);
+  // the high parts back as float32 from the packed pair (a shift and a mask)
+  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 // Transposing LDS read of 16-bit elements (gfx950): within each group of 16
@@ -813,16 +813,16 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          f4 a = {0.f, 0.f, 0.f, 0.f}, a2 = a;
+          f4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kg = 0; kg < KG; ++kg) {
             const uint4 ca =
                 *reinterpret_cast<const uint4*>(&sm.C[cur][16 * tb + li][(N / 2) * nh + 32 * kg + 8 * lk]);
             a = mfma_bf16(ca, sh[kg], a);
-            a2 = mfma_bf16(ca, sl[kg], a2);
+            a = mfma_bf16(ca, sl[kg], a);
           }
           const float4 e = *reinterpret_cast<const float4*>(&sm.ecs[cur][16 * tb + 4 * lk]);
-          const f4 v = {(a[0] + a2[0]) * e.x, (a[1] + a2[1]) * e.y, (a[2] + a2[2]) * e.z, (a[3] + a2[3]) * e.w};
+          const f4 v = {a[0] * e.x, a[1] * e.y, a[2] * e.z, a[3] * e.w};
           if (tb == nh) y = v;
           else *reinterpret_cast<float4*>(&sm.Yx[tb][pb][li][4 * lk]) = make_float4(v[0], v[1], v[2], v[3]);
         }
