@@ -169,7 +169,9 @@ struct alignas(16) SsdSmem {
   float X[2][kQ][kP + 16];   // x chunk, row padded so that 4 consecutive rows hit different banks
   float Bm[2][kQ][N + 4];    // B chunk
   float Cm[2][kQ][N + 4];    // C chunk
-  float S[kP][N + 4];        // state entering the chunk (operand of C S^T)
+  // the inter-chunk output block (t-block, p-block) over one half of the
+  // states, [p][t] within the block, from the wave that does not own it
+  float Yx[2][4][16][20];
   float M[2][kQ][kQ + 4];    // masked, decayed C B^T: two halves of the sum over n
   float Y[kQ][kP + 4];       // output of the chunk before D x
   float dt[2][kQ];
@@ -247,8 +249,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   static_assert(kQ == 32 && kP == 64 && kWaves == 8, "work split below assumes these sizes");
   static_assert(N == 64 || N == 128, "state sizes");
   static_assert(!(AGG && (BIDIR || GATE)), "the aggregate pass runs one sweep, no gate");
-  constexpr int NB = N / 16;          // state column blocks
-  constexpr int PBW = 4 * NB / 8;     // state row blocks per wave (its column block is wave % NB)
+  constexpr int NTL = N / 32;         // state tiles per wave (16 states each)
 
   __shared__ SsdSmem<N> sm;
 
@@ -264,10 +265,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   const float Dh = p.D ? p.D[h] : 0.f;
   const float* const bias = p.dt_bias ? p.dt_bias + h : nullptr;
 
-  // output block of this wave: t-block ytb (16 steps) x head-channel block ypb
+  // output block of this wave: t-block ytb (16 steps) x head-channel block
+  // ypb. The wave's state: head channels p = 16 ypb .. 16 ypb + 15, states n
+  // in half ytb of N, as NTL accumulator tiles S[n][p] (n the row): register
+  // r of lane (li, lk) in tile k is n = N/2 ytb + 16 k + 4 lk + r, p = 16 ypb
+  // + li. Register r of a tile is then, as it stands, the operand B (k = n,
+  // column p) of one 16 x 16 x 4 product over n, so C S^T takes the state
+  // from the accumulators and no copy of it goes through LDS.
   const int ytb = wave >> 2, ypb = wave & 3;
-  // state blocks of this wave: rows 16 (spb + k), k < PBW, column block snb
-  const int snb = wave % NB, spb = (wave / NB) * PBW;
+  const int pp = 16 * ypb + li;
+  auto tile_n0 = [&](int k) { return (N / 2) * ytb + 16 * k + 4 * lk; };
   // C B^T task: causal block (0,0), (1,0) or (1,1), half of the sum over n
   const int mblk = wave >> 1, mhalf = wave & 1;
   const int mtb = mblk == 0 ? 0 : 1, msb = mblk == 2 ? 1 : 0;
@@ -279,21 +286,20 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
   if (BIDIR && p.sweep_sel >= 0 && sweep != p.sweep_sel) continue;  // (uniform)
   const bool rev = BIDIR ? sweep == 0 : p.sweep_sel == 0;
   const float* const init = rev ? p.g0 : p.h0;  // the sweep's entering state (null: zero)
-  f4 st[PBW];
+  f4 st[NTL];
 #pragma unroll
-  for (int k = 0; k < PBW; ++k)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-      float v = 0.f;
-      if (!AGG) {
-        // a range of a split sequence starts from its joined entering state
-        if (p.nranges > 1) v = p.agg_S[((blk.range * (p.nblocks / p.nranges) + bh) * kP + pp) * N + nn];
-        else if (init) v = init[((b * p.H + h) * kP + pp) * N + nn];
-      }
-      st[k][r] = v;
-      if (!AGG) sm.S[pp][nn] = v;
+  for (int k = 0; k < NTL; ++k) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!AGG) {
+      // a range of a split sequence starts from its joined entering state
+      if (p.nranges > 1)
+        v = *reinterpret_cast<const float4*>(
+            p.agg_S + ((blk.range * (p.nblocks / p.nranges) + bh) * kP + pp) * N + tile_n0(k));
+      else if (init)
+        v = *reinterpret_cast<const float4*>(init + ((b * p.H + h) * kP + pp) * N + tile_n0(k));
     }
+    st[k][0] = v.x, st[k][1] = v.y, st[k][2] = v.z, st[k][3] = v.w;
+  }
   double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
 
   SsdStager<T, N> stg;
@@ -364,27 +370,35 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
       }
     }
 
-    // inter-chunk output diag(e^{cs}) C S_in^T for the wave's output block
+    // inter-chunk output diag(e^{cs}) C S_in^T over the wave's half of the
+    // states, for both t-blocks: the wave keeps its own block and hands the
+    // other to its partner (same p-block, other half) through LDS
     f4 y = {0.f, 0.f, 0.f, 0.f};
     if (!AGG) {
-      constexpr int K = N / 4;
-      float ca[K], sb[K];
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        ca[j] = sm.Cm[cur][16 * ytb + li][4 * j + lk];
-        sb[j] = sm.S[16 * ypb + li][4 * j + lk];
+      for (int tb = 0; tb < 2; ++tb) {
+        float4 ca[NTL];
+#pragma unroll
+        for (int k = 0; k < NTL; ++k) ca[k] = *reinterpret_cast<const float4*>(&sm.Cm[cur][16 * tb + li][tile_n0(k)]);
+        f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+        for (int k = 0; k < NTL; ++k) {
+          a0 = mfma4(ca[k].x, st[k][0], a0);
+          a1 = mfma4(ca[k].y, st[k][1], a1);
+          a0 = mfma4(ca[k].z, st[k][2], a0);
+          a1 = mfma4(ca[k].w, st[k][3], a1);
+        }
+        const float4 e = *reinterpret_cast<const float4*>(&sm.ecs[16 * tb + 4 * lk]);
+        const f4 v = {(a0[0] + a1[0]) * e.x, (a0[1] + a1[1]) * e.y, (a0[2] + a1[2]) * e.z, (a0[3] + a1[3]) * e.w};
+        if (tb == ytb) y = v;
+        else *reinterpret_cast<float4*>(&sm.Yx[tb][ypb][li][4 * lk]) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-      for (int j = 0; j < K; j += 2) {
-        a0 = mfma4(ca[j], sb[j], a0);
-        a1 = mfma4(ca[j + 1], sb[j + 1], a1);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = (a0[r] + a1[r]) * sm.ecs[16 * ytb + 4 * lk + r];
     }
-    __syncthreads();  // M complete
+    __syncthreads();  // M and the partner's block complete
+    if (!AGG) {
+      const float4 o = *reinterpret_cast<const float4*>(&sm.Yx[ytb][ypb][li][4 * lk]);
+      y[0] += o.x, y[1] += o.y, y[2] += o.z, y[3] += o.w;
+    }
 
     // intra-chunk output M X (causal: s-blocks up to the t-block); the
     // t-block 0 waves use the first half of the operands only
@@ -409,33 +423,28 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
       for (int r = 0; r < 4; ++r) sm.Y[16 * ytb + 4 * lk + r][16 * ypb + li] = y[r];
     }
 
-    // state update S = e^{cs_end} S + (X w)^T B for the wave's blocks
+    // state update S^T = e^{cs_end} S^T + B^T (w X) for the wave's tiles:
+    // operand A B[s][n] (row n of the tile: 16 k + li of its half), operand
+    // B w_s X[s][p]
     const float dec = __expf(sm.cs_end);
 #pragma unroll
-    for (int k = 0; k < PBW; ++k) st[k] *= dec;
+    for (int k = 0; k < NTL; ++k) st[k] *= dec;
     {
-      float bo[kQ / 4], xa[kQ / 4][PBW];
+      float bo[kQ / 4][NTL], xa[kQ / 4];
 #pragma unroll
       for (int j = 0; j < kQ / 4; ++j) {
         const int s0 = 4 * j;
-        bo[j] = sm.Bm[cur][s0 + lk][16 * snb + li];
-        const float wv = sm.w[s0 + lk];
+        xa[j] = sm.X[cur][s0 + lk][pp] * sm.w[s0 + lk];
 #pragma unroll
-        for (int k = 0; k < PBW; ++k) xa[j][k] = sm.X[cur][s0 + lk][16 * (spb + k) + li] * wv;
+        for (int k = 0; k < NTL; ++k) bo[j][k] = sm.Bm[cur][s0 + lk][(N / 2) * ytb + 16 * k + li];
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < kQ / 4; ++j)
 #pragma unroll
-        for (int k = 0; k < PBW; ++k) st[k] = mfma4(xa[j][k], bo[j], st[k]);
+        for (int k = 0; k < NTL; ++k) st[k] = mfma4(bo[j][k], xa[j], st[k]);
     }
-    __syncthreads();  // every read of S_in and of this chunk's tiles is done; Y complete
-    if (!AGG) {
-#pragma unroll
-      for (int k = 0; k < PBW; ++k)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.S[16 * (spb + k) + 4 * lk + r][16 * snb + li] = st[k][r];
-    }
+    __syncthreads();  // every read of this chunk's tiles and of the exchange is done; Y complete
     // the next chunk's tiles (waits for its loads), then this chunk's output:
     // the store is the last memory operation of the chunk, so no later wait
     // for the loads has to wait for it as well
@@ -465,23 +474,17 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
     // the range's end state from zero and its decay exponent
     const int64_t slot = blk.range * (p.nblocks / p.nranges) + bh;
 #pragma unroll
-    for (int k = 0; k < PBW; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-        p.agg_S[(slot * kP + pp) * N + nn] = st[k][r];
-      }
+    for (int k = 0; k < NTL; ++k)
+      *reinterpret_cast<float4*>(p.agg_S + (slot * kP + pp) * N + tile_n0(k)) =
+          make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
     if (tid == 0) p.agg_cs[slot] = cs_sum;
   } else {
     float* const fin = rev ? p.g_first : p.h_last;
     if (fin && blk.range == p.nranges - 1) {
 #pragma unroll
-      for (int k = 0; k < PBW; ++k)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pp = 16 * (spb + k) + 4 * lk + r, nn = 16 * snb + li;
-          fin[((b * p.H + h) * kP + pp) * N + nn] = st[k][r];
-        }
+      for (int k = 0; k < NTL; ++k)
+        *reinterpret_cast<float4*>(fin + ((b * p.H + h) * kP + pp) * N + tile_n0(k)) =
+            make_float4(st[k][0], st[k][1], st[k][2], st[k][3]);
     }
   }
   }  // sweep
