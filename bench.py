@@ -189,7 +189,7 @@ def cpu_baseline_bwd(inp, dy, w, budget_s=20.0):
         return sub, dy[:k]
 
     def run(sub, dys):
-        y = oracle.scan(**sub, nthreads=threads)[0] if train else None
+        y = oracle.scan(**sub, bidir=bidir, nthreads=threads)[0] if train else None
         ref = oracle.scan_bwd(**sub, dy=dys, bidir=bidir, nthreads=threads)
         return ref if y is None else dict(ref, y=y)
 
@@ -485,7 +485,7 @@ def main():
             if train:
                 t["y"] = torch.empty((Bs, L, ED), dtype=tdt, device=dev)
                 t["ck"] = torch.empty(ssm.ssm_scan_ckpt_shape(Bs, L, ED), dtype=torch.float32, device=dev)
-                fneed = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, dcode, False)
+                fneed = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, dcode, w["bidir"])
                 t["fws"] = torch.empty(fneed, dtype=torch.uint8, device=dev) if fneed else None
         else:
             host_sets.append(inp if i == 0 else None)
@@ -499,10 +499,12 @@ def main():
 
     def step(t):
         if train:
-            ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], workspace=t["fws"],
-                             ckpt=t["ck"], stream=stream)
-            ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
-                             workspace=t["ws"], ckpt=t["ck"], stream=stream)
+            (ssm.ssm_scan_bidir_fwd if w["bidir"] else ssm.ssm_scan_fwd)(
+                t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], y=t["y"], workspace=t["fws"], ckpt=t["ck"],
+                stream=stream)
+            (ssm.ssm_scan_bidir_bwd if w["bidir"] else ssm.ssm_scan_bwd)(
+                t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"], workspace=t["ws"],
+                ckpt=t["ck"], stream=stream)
         elif bwd:
             (ssm.ssm_scan_bidir_bwd if w["bidir"] else ssm.ssm_scan_bwd)(
                              t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["dy"], out=t["out"],
@@ -540,7 +542,8 @@ def main():
     # bidirectional: the exp and the two multiplies are shared by both
     # directions; algorithmic cost 2 mul + exp + 2 x (state FMA + C FMA) = 8
     if train:
-        slots = SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD
+        slots = (SLOTS_PER_ELEMENT_BIDIR + SLOTS_PER_ELEMENT_BIDIR_BWD) if w["bidir"] else \
+            (SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD)
     elif bwd:
         slots = SLOTS_PER_ELEMENT_BIDIR_BWD if w["bidir"] else SLOTS_PER_ELEMENT_BWD
     else:
@@ -605,8 +608,9 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": bytes_alg,
             "kernel_avg_us": avg_launch_s * 1e6,
-            "timed": (("whole training step: the forward scan kernel (writing the round states), the backward "
-                       "scan kernel and the two small kernels that add up the dB/dC and dA/dD partial sums")
+            "timed": (("whole training step: the forward scan's kernels (writing the round states), the backward "
+                       "scan kernel (once per direction) and the two small kernels that add up the dB/dC and dA/dD "
+                       "partial sums")
                       if train else
                       ("whole backward step: the scan kernel (once per direction) and the two small kernels "
                        "that add up the dB/dC and dA/dD partial sums") if bwd else

@@ -225,6 +225,19 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssm_scan_bidir_fwd (same arguments, results and errors) that also writes
+ * the forward direction's round checkpoints, exactly as ssm_scan_fwd_ckpt
+ * does for the same inputs: ckpt[b][r][e][n] = h_{32 r - 1}[b, e, n] of the
+ * forward scan from h0, for rounds r >= 1 (the reverse direction's states
+ * are not kept). Same ckpt sizes, alignment and errors as ssm_scan_fwd_ckpt;
+ * for ssm_scan_bidir_bwd_ckpt.
+ */
+int ssm_scan_bidir_fwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
+                            float* h_last, float* g_first, float* ckpt, size_t ckpt_bytes, int64_t Bs, int64_t L,
+                            int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass of the forward scan: the gradients of L = sum(dy * y) for
  * y = ssm_scan_fwd(x, delta, A, B, C, D, h0, opts = NULL). This is the step
  * that follows the forward in the autograd function of "Some questions of
@@ -332,6 +345,23 @@ int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const v
                        const float* dh_last, const float* dg_first, void* dx, void* ddelta, float* dA, void* dB,
                        void* dC, float* dD, float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
                        int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_scan_bidir_bwd given the forward direction's round checkpoints that
+ * ssm_scan_bidir_fwd_ckpt (or ssm_scan_fwd_ckpt) wrote for the same x,
+ * delta, A, B, C, h0 and options: the forward-time half of the backward then
+ * skips its own forward sweep; the reverse-time half keeps it. ckpt (read
+ * only) is required (NULL with data to scan: SSM_ERR_NULL); sizes,
+ * alignment and overlap rules as ssm_scan_bwd_ckpt; other arguments,
+ * results, workspace and errors as ssm_scan_bidir_bwd. Checkpoints of other
+ * inputs give wrong gradients (no error).
+ */
+int ssm_scan_bidir_bwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const float* h0, const float* g0, const ssm_scan_options* opts,
+                            const void* dy, const float* dh_last, const float* dg_first, const float* ckpt,
+                            size_t ckpt_bytes, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                            float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L, int64_t ED,
+                            int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Multi-head (Mamba-2 / SSD) selective scan, in the layout of the chunked

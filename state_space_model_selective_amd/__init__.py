@@ -113,6 +113,10 @@ def lib():
         L.ssm_scan_bidir_bwd_workspace_bytes.restype = sz
         L.ssm_scan_bidir_bwd.argtypes = [vp] * 22 + [i64] * 4 + [ci, vp, sz, vp]
         L.ssm_scan_bidir_bwd.restype = ci
+        L.ssm_scan_bidir_fwd_ckpt.argtypes = [vp] * 13 + [sz] + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_fwd_ckpt.restype = ci
+        L.ssm_scan_bidir_bwd_ckpt.argtypes = [vp] * 13 + [sz] + [vp] * 10 + [i64] * 4 + [ci, vp, sz, vp]
+        L.ssm_scan_bidir_bwd_ckpt.restype = ci
         L.ssm_ssd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
         L.ssm_ssd_workspace_bytes.restype = sz
         L.ssm_ssd_fwd.argtypes = [vp] * 10 + [i64] * 6 + [ci, vp, sz, vp]
@@ -363,25 +367,32 @@ def ssm_scan_fwd_status(x, A, workspace, stream=None):
 
 
 def ssm_scan_bidir_fwd(x, delta, A, B, C, D=None, y=None, h_last=None, g_first=None, workspace=None,
-                       stream=None, h0=None, g0=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
+                       stream=None, h0=None, g0=None, dt_bias=None, dt_softplus=False, dt_limit=None, z=None,
+                       ckpt=None):
     """y = forward scan (from h0, zero if None) + reverse-time scan (from g0
     at the last step, zero if None; shared weights, read in place) + D x,
-    with the same options as ssm_scan_fwd."""
+    with the same options as ssm_scan_fwd. With ckpt (float32, of
+    ssm_scan_ckpt_shape(Bs, L, ED)) the forward direction's round states are
+    written there as well (ssm_scan_bidir_fwd_ckpt), for
+    ssm_scan_bidir_bwd(..., ckpt=ckpt)."""
     _, (Bs, L, ED, N) = _scan_args("ssm_scan_bidir_fwd", x, delta, A, B, C, D, h0, dt_bias, dt_limit, z,
                                    workspace, [("g0", g0, "state"), ("y", y, "seq"), ("h_last", h_last, "state"),
-                                               ("g_first", g_first, "state")])
+                                               ("g_first", g_first, "state"), ("ckpt", ckpt, "ckpt")])
     dt = _dtype_code(x)
     if y is None:
         import torch
         y = torch.empty_like(x)
     workspace, ws_bytes = _workspace(workspace, ssm_scan_workspace_bytes(Bs, L, ED, N, dt, True), x.device)
     opts = _options(dt_bias, dt_softplus, dt_limit, z)
-    rc = lib().ssm_scan_bidir_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0),
-                                  _byref(opts), _ptr(y),
-                                  _ptr(h_last), _ptr(g_first), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
-                                  _stream(x, stream))
+    head = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0), _byref(opts), _ptr(y),
+            _ptr(h_last), _ptr(g_first))
+    tail = (Bs, L, ED, N, dt, _ptr(workspace), ws_bytes, _stream(x, stream))
+    if ckpt is None:
+        rc = lib().ssm_scan_bidir_fwd(*head, *tail)
+    else:
+        rc = lib().ssm_scan_bidir_fwd_ckpt(*head, _ptr(ckpt), ckpt.numel() * 4, *tail)
     if rc != SSM_OK:
-        raise SSMError(rc, "ssm_scan_bidir_fwd")
+        raise SSMError(rc, "ssm_scan_bidir_fwd_ckpt" if ckpt is not None else "ssm_scan_bidir_fwd")
     return y
 
 
@@ -435,7 +446,12 @@ def _bwd(bidir, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace,
              _ptr(o.get("dh0")))
     tail = (_ptr(o.get("ddt_bias")), _ptr(o.get("dz")), Bs, L, ED, N, dt, _ptr(workspace), ws_bytes,
             _stream(x, stream))
-    if bidir:
+    if bidir and ckpt is not None:
+        where = "ssm_scan_bidir_bwd_ckpt"
+        rc = lib().ssm_scan_bidir_bwd_ckpt(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                                           _ptr(g0), _byref(opts), _ptr(dy), _ptr(dh_last), _ptr(dg_first),
+                                           _ptr(ckpt), ckpt.numel() * 4, *grads, _ptr(o.get("dg0")), *tail)
+    elif bidir:
         rc = lib().ssm_scan_bidir_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(g0),
                                       _byref(opts), _ptr(dy), _ptr(dh_last), _ptr(dg_first), *grads,
                                       _ptr(o.get("dg0")), *tail)
@@ -474,15 +490,17 @@ def ssm_scan_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False
 
 def ssm_scan_bidir_bwd(x, delta, A, B, C, D, dy, h0=None, want_dD=True, want_dh0=False, out=None, workspace=None,
                        stream=None, dt_bias=None, dt_softplus=False, dt_limit=None, want_ddt_bias=False, z=None,
-                       g0=None, dh_last=None, dg_first=None, want_dg0=False):
+                       g0=None, dh_last=None, dg_first=None, want_dg0=False, ckpt=None):
     """Gradients of sum(dy * y) (+ sum(dh_last * h_last) + sum(dg_first *
     g_first) for the final states' gradients when given) for y =
     ssm_scan_bidir_fwd(x, delta, A, B, C, D, h0=h0, g0=g0, <step-size
     options>, z=z), with the outputs of ssm_scan_bwd and dg0 (the gradient of
-    g0) if want_dg0."""
+    g0) if want_dg0. ckpt: the forward direction's round checkpoints that
+    ssm_scan_bidir_fwd(..., ckpt=ckpt) wrote for the same inputs
+    (ssm_scan_bidir_bwd_ckpt)."""
     return _bwd(True, x, delta, A, B, C, D, dy, h0, want_dD, want_dh0, out, workspace, stream, dt_bias,
                 dt_softplus, dt_limit, want_ddt_bias, z, dh_last=dh_last, g0=g0, dg_first=dg_first,
-                want_dg0=want_dg0)
+                want_dg0=want_dg0, ckpt=ckpt)
 
 
 def _ssd_args(where, x, dt, A, B, C, D, h0, dt_bias, dt_limit, z, workspace, outs):

@@ -749,7 +749,7 @@ __global__ __launch_bounds__(64 * SEG) __attribute__((amdgpu_waves_per_eu(WPE)))
           // padded channels too: their state is their zero entering state)
           if (seg == SEG - 1) {
             fa.carry[r & 1][lane] = make_float4(hin[0], hin[1], hin[2], hin[3]);
-            if (!BIDIR && p.ckpt && r + 1 < rounds)
+            if (!rev && p.ckpt && r + 1 < rounds)
               *reinterpret_cast<float4*>(p.ckpt + ((b * p.ck_rounds + t0 / RT + r + 1) * p.ck_EDp + e) * 16 + 4 * g) =
                   make_float4(hin[0], hin[1], hin[2], hin[3]);
           }
@@ -1159,7 +1159,7 @@ int launch_scan(const void* x, const void* delta, const float* A, const void* B,
   a.state = nullptr;
   a.sdsum = nullptr;
   a.gstate = nullptr;
-  a.ckpt = bidir ? nullptr : ckpt;
+  a.ckpt = ckpt;  // the forward direction's round states (both scans)
   a.ck_rounds = (L + kRT - 1) / kRT;
   a.ck_EDp = ngroups * 16;
   const bool split = sp.nchunks > 1;
@@ -1299,6 +1299,14 @@ int ssm_scan_bidir_fwd(const void* x, const void* delta, const float* A, const v
                        void* workspace, size_t workspace_bytes, void* stream) {
   return run(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes,
              stream, 1);
+}
+
+int ssm_scan_bidir_fwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const float* h0, const float* g0, const ssm_scan_options* opts, void* y,
+                            float* h_last, float* g_first, float* ckpt, size_t ckpt_bytes, int64_t Bs, int64_t L,
+                            int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(x, delta, A, B, C, D, h0, g0, opts, y, h_last, g_first, Bs, L, ED, N, dtype, workspace, workspace_bytes,
+             stream, 1, true, ckpt, ckpt_bytes);
 }
 
 int ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,

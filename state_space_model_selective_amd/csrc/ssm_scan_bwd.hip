@@ -1161,6 +1161,10 @@ int launch_bwd(const void* x, const void* delta, const float* A, const void* B, 
     // added to the forward-time scan's (in order on the stream) and rounded
     // once; its initial state's gradient is dg0
     BwdArgs<T> r = a;
+    // the caller's checkpoints are the forward direction's; this scan keeps
+    // its own first sweep and workspace checkpoints
+    r.ckpt = reinterpret_cast<float*>(w + lo.ckpt_off);
+    r.ck_given = 0;
     r.D = nullptr;
     r.h0 = sa.g0;
     r.dh0 = sa.dg0;
@@ -1204,7 +1208,6 @@ int run_bwd(const void* x, const void* delta, const float* A, const void* B, con
   BwdSizes s;
   size_t gate_off = 0;
   if (!bidir) sa.g0 = sa.dg_first = sa.dg0 = nullptr;
-  if (bidir) sa.ckpt = nullptr;
   const int rc = bwd_validate(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa,
                               Bs, L, ED, N, dtype, workspace, workspace_bytes, bidir, &s, &gate_off);
   if (rc != SSM_OK) return rc;
@@ -1291,6 +1294,18 @@ int ssm_scan_bidir_bwd(const void* x, const void* delta, const float* A, const v
                        void* dC, float* dD, float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L,
                        int64_t ED, int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   const StateArgs sa{g0, dh_last, dg_first, dg0, nullptr, 0};
+  return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
+                 N, dtype, workspace, workspace_bytes, stream, true);
+}
+
+int ssm_scan_bidir_bwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                            const float* D, const float* h0, const float* g0, const ssm_scan_options* opts,
+                            const void* dy, const float* dh_last, const float* dg_first, const float* ckpt,
+                            size_t ckpt_bytes, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                            float* dh0, float* dg0, float* ddt_bias, void* dz, int64_t Bs, int64_t L, int64_t ED,
+                            int64_t N, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ckpt && Bs > 0 && L > 0 && ED > 0) return SSM_ERR_NULL;
+  const StateArgs sa{g0, dh_last, dg_first, dg0, ckpt, ckpt_bytes};
   return run_bwd(x, delta, A, B, C, D, h0, opts, dy, dx, ddelta, dA, dB, dC, dD, dh0, ddt_bias, dz, sa, Bs, L, ED,
                  N, dtype, workspace, workspace_bytes, stream, true);
 }

@@ -67,6 +67,10 @@ WORKLOADS = {
                                             h_last=False, bwd=True, train=True),
     "train_f32_Bs1_L131072_ED2048_N16": dict(Bs=1, L=131072, ED=2048, N=16, dtype="f32", bidir=False,
                                              h_last=False, bwd=True, train=True),
+    # the bidirectional scan's training step (the forward direction's round
+    # states kept by the bidirectional forward)
+    "train_bidir_f32_Bs8_L4096_ED1536_N16": dict(Bs=8, L=4096, ED=1536, N=16, dtype="f32", bidir=True,
+                                                 h_last=False, bwd=True, train=True),
 }
 
 # Multi-head (SSD) workloads: batch 32, seqlen 400, 8 heads is the shape the

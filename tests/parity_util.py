@@ -111,8 +111,8 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
     a float64 numpy array. dt_bias (numpy, float32) / dt_softplus / dt_limit
     are the step-size options; with dt_bias the result holds ddt_bias; z (like
     x) is the output gate, and the result then holds dz. use_ckpt: run the
-    forward with round checkpoints (NaN-filled first) and pass them to the
-    backward (ssm_scan_fwd_ckpt, ssm_scan_bwd_ckpt)."""
+    forward (bidir: the bidirectional forward) with round checkpoints
+    (NaN-filled first) and pass them to the backward."""
     import torch
     import state_space_model_selective_amd as ssm
     dev = torch.device("cuda:0")
@@ -144,8 +144,12 @@ def run_gpu_bwd(inp, dy, h0=None, D_none=False, want_dD=True, want_dh0=False, st
             out["dg0"] = torch.full((Bs, ED, N), float("nan"), dtype=torch.float32, device=dev)
     if use_ckpt:
         ck = torch.full(ssm.ssm_scan_ckpt_shape(Bs, L, ED), float("nan"), dtype=torch.float32, device=dev)
-        ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], h0=h0t,
-                         dt_bias=bias, dt_softplus=dt_softplus, dt_limit=dt_limit, z=zt, ckpt=ck, stream=stream)
+        fargs = (t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"])
+        fkw = dict(h0=h0t, dt_bias=bias, dt_softplus=dt_softplus, dt_limit=dt_limit, z=zt, ckpt=ck, stream=stream)
+        if bidir:
+            ssm.ssm_scan_bidir_fwd(*fargs, g0=kw["g0"], **fkw)
+        else:
+            ssm.ssm_scan_fwd(*fargs, **fkw)
         kw["ckpt"] = ck
     fn = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
     res = fn(t["x"], t["delta"], t["A"], t["B"], t["C"], None if D_none else t["D"], t["dy"],

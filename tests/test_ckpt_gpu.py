@@ -143,3 +143,69 @@ def test_backward_with_checkpoints_split_sequence():
     got = run_gpu_bwd(inp, dy, want_dh0=True, use_ckpt=True)
     ref = oracle.scan_bwd(**inp, dy=dy)
     assert_grads_close(got, ref, "f32")
+
+
+# ---- the bidirectional scan: the forward direction's checkpoints ------------
+
+def run_bidir_fwd_ckpt(inp, h0=None, g0=None, opts=None):
+    import torch
+    import state_space_model_selective_amd as ssm
+    dev = torch.device("cuda:0")
+    t = to_device(inp, dev)
+    Bs, L, ED = inp["x"].shape
+    ck = torch.full(ssm.ssm_scan_ckpt_shape(Bs, L, ED), float("nan"), dtype=torch.float32, device=dev)
+    st = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    kw = dict(opts or {})
+    if kw.get("dt_bias") is not None:
+        kw["dt_bias"] = st(kw["dt_bias"])
+    y = ssm.ssm_scan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], h0=st(h0), g0=st(g0), ckpt=ck,
+                               **kw)
+    torch.cuda.synchronize()
+    return y_to_numpy(y), ck.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("Bs,L,ED,dtype", [(2, 200, 48, "f32"), (2, 257, 40, "bf16"), (1, 9001, 32, "f32"),
+                                           (1, 3000, 64, "f32")])
+def test_bidir_forward_checkpoints(Bs, L, ED, dtype):
+    """The forward direction's states after each prefix, from h0, whatever
+    the reverse direction starts from; split shapes take their corrections
+    in the join kernel. y is the plain bidirectional forward's, bit for bit."""
+    log("ckpt bidir forward Bs=%d L=%d ED=%d %s" % (Bs, L, ED, dtype))
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=L + 1)
+    h0 = synth.normal(L, 79, (Bs, ED, 16))
+    g0 = synth.normal(L, 80, (Bs, ED, 16))
+    y, ck = run_bidir_fwd_ckpt(inp, h0=h0, g0=g0)
+    R = (L + 31) // 32
+    assert not np.isnan(ck[:, 1:]).any(), "a checkpoint was not written"
+    chans = sample_channels(Bs, ED, 8, seed=L)
+    for r in sorted({1, 2, R // 3, R // 2 + 1, R - 1}):
+        if not 1 <= r < R:
+            continue
+        pre = {k: inp[k][:, :32 * r] for k in ("x", "delta", "B", "C")}
+        _, h, _ = oracle.scan(**pre, A=inp["A"], D=inp["D"], h0=h0, want_h_last=True, chans=chans)
+        got = np.stack([ck[c // ED, r, c % ED] for c in chans])
+        assert_close("ckpt round %d" % r, got, h, TOL["f32"])
+    y0, _, _ = run_gpu(inp, bidir=True, h0=h0, g0=g0)
+    np.testing.assert_array_equal(y, y0)
+
+
+@pytest.mark.parametrize("Bs,L,ED,dtype", [(2, 200, 48, "f32"), (2, 300, 96, "bf16"), (1, 3000, 64, "f32")])
+def test_bidir_backward_with_checkpoints(Bs, L, ED, dtype):
+    log("ckpt bidir bwd Bs=%d L=%d ED=%d %s" % (Bs, L, ED, dtype))
+    seed = L + ED + 3
+    inp = synth.make_inputs(Bs, L, ED, 16, dtype, seed=seed)
+    dy = synth.make_output_grad(Bs, L, ED, dtype, seed=seed)
+    h0 = synth.normal(seed, 79, (Bs, ED, 16))
+    kw = dict(g0=synth.normal(seed, 81, (Bs, ED, 16)), dg_first=synth.normal(seed, 82, (Bs, ED, 16)))
+    dhl = synth.normal(seed, 80, (Bs, ED, 16))
+    got = run_gpu_bwd(inp, dy, h0=h0, want_dh0=True, bidir=True, dh_last=dhl, want_dg0=True, use_ckpt=True, **kw)
+    ref = oracle.scan_bwd(**inp, dy=dy, h0=h0, bidir=True, dh_last=dhl, **kw)
+    assert_grads_close(got, ref, dtype)
+
+
+def test_bidir_backward_with_checkpoints_options_and_gate():
+    inp, opts = options_inputs(2, 200, 48, "f32", seed=11)
+    dy = synth.make_output_grad(2, 200, 48, "f32", seed=11)
+    got = run_gpu_bwd(inp, dy, want_dh0=True, bidir=True, use_ckpt=True, **opts)
+    ref = oracle.scan_bwd(**inp, dy=dy, bidir=True, **opts)
+    assert_grads_close(got, ref, "f32")

@@ -93,8 +93,8 @@ def run_train_workload(name):
     log("training-step workload %s" % name)
     inp = synth.workload_inputs(name, seed=0)
     dy = synth.make_output_grad(w["Bs"], w["L"], w["ED"], w["dtype"], seed=0)
-    got = run_gpu_bwd(inp, dy, want_dh0=True, use_ckpt=True)
-    ref = oracle.scan_bwd(**inp, dy=dy)
+    got = run_gpu_bwd(inp, dy, want_dh0=True, use_ckpt=True, bidir=w["bidir"])
+    ref = oracle.scan_bwd(**inp, dy=dy, bidir=w["bidir"])
     assert_grads_close(got, ref, w["dtype"])
 
 
@@ -108,3 +108,7 @@ def test_training_step_bf16_4x8192x5120():
 
 def test_training_step_long_sequence_131072():
     run_train_workload("train_f32_Bs1_L131072_ED2048_N16")
+
+
+def test_training_step_bidirectional_8x4096x1536():
+    run_train_workload("train_bidir_f32_Bs8_L4096_ED1536_N16")
