@@ -125,8 +125,8 @@ size_t ssm_scan_workspace_bytes(int64_t Bs, int64_t L, int64_t ED, int64_t N, in
  * every later chunk's and h_last become NaN, and ssm_scan_fwd_status()
  * reports SSM_ERR_HANDOFF. A later chunk adds the decayed entering state's
  * contribution to the start of its outputs until every decay product
- * prod a[n] is below 2^-40 (or the entering state is zero); the terms left
- * out are below 2^-40 sum_n |C_t[n] h_in[n]|, under one float32 rounding.
+ * prod a[n] is below 2^-30 (or the entering state is zero); the terms left
+ * out are below 2^-30 sum_n |C_t[n] h_in[n]|, under one float32 rounding.
  *   x, delta : (Bs, L, ED) of dtype        -- input sequence and step sizes
  *   A        : (ED, N) float32             -- state matrix (diagonal per channel)
  *   B, C     : (Bs, L, N) of dtype         -- input and output projections
@@ -154,7 +154,7 @@ int ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B
  * also writes ckpt[b][r][e][n] = h_{32 r - 1}[b, e, n], the state after the
  * first 32 r steps, for rounds r >= 1 (entries of round 0 are not written;
  * padded channels get their zero state). A split sequence's checkpoints
- * take the entering state's carried contribution with the same 2^-40 cut
+ * take the entering state's carried contribution with the same 2^-30 cut
  * as its outputs. ckpt: device buffer of at least ckpt_bytes >=
  * ssm_scan_ckpt_bytes(...) bytes, aligned to 16 bytes, overlapping no other
  * argument (SSM_ERR_NULL if NULL with data to scan, SSM_ERR_WORKSPACE if
@@ -215,7 +215,7 @@ int ssm_scan_fwd_status(const void* workspace, size_t workspace_bytes, int64_t B
  * inside the sequence), and a second kernel folds the chunks' aggregates
  * into the states entering each chunk from either side, then corrects both
  * ends of its output the way ssm_scan_fwd corrects a chunk's start (terms
- * below 2^-40 of the carried state are left out). Nothing waits on another
+ * below 2^-30 of the carried state are left out). Nothing waits on another
  * workgroup; the workspace (ssm_scan_workspace_bytes(..., bidir = 1)) holds
  * the aggregates, after the bf16 scan's float32 partials.
  */

@@ -178,8 +178,9 @@ struct alignas(16) FoldArea {
 enum { STAGE_SCAN = 0, STAGE_CORRECT = 1 };
 
 // The split sequence's correction pass drops a carried term once its decay
-// product is below 2^-kCorrectionCut.
-constexpr float kCorrectionCut = 40.f;
+// product is below 2^-kCorrectionCut: what it leaves out is 2^6 below the
+// float32 rounding of the sum it would be added to.
+constexpr float kCorrectionCut = 30.f;
 
 // delta' = clamp(softplus?(delta + dt_bias[e]), dt_min, dt_max), with the
 // channel's bias (0 without one) already in a register
