@@ -495,3 +495,61 @@ def test_binding_checks_checkpoint_tensors():
         ssm.ssm_scan_fwd(x, d, A, B, C, ckpt=torch.zeros(2, 2, 32, 16, dtype=torch.float64))
     with pytest.raises(TypeError):
         ssm.ssm_scan_bwd(x, d, A, B, C, None, x, ckpt=torch.zeros(2, 2, 32, 16, dtype=torch.bfloat16))
+
+
+def bidir_fwd_ckpt(**kw):
+    args = dict(x=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=P[5], y=P[6], h=P[7], g=P[8], h0=P[10], g0=P[15],
+                ck=P[20], opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_F32, ws=None, ws_bytes=0)
+    args["ck_bytes"] = ssm.lib().ssm_scan_ckpt_bytes(2, 64, 64, 16)
+    args.update(kw)
+    return ssm.lib().ssm_scan_bidir_fwd_ckpt(args["x"], args["delta"], args["A"], args["B"], args["C"], args["D"],
+                                             args["h0"], args["g0"], args["opts"], args["y"], args["h"], args["g"],
+                                             args["ck"], args["ck_bytes"], args["Bs"], args["L"], args["ED"],
+                                             args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bidir_forward_checkpoint_validation():
+    assert bidir_fwd_ckpt(ck=None) == ssm.SSM_ERR_NULL
+    assert bidir_fwd_ckpt(ck=P[20] + 8) == ssm.SSM_ERR_UNSUPPORTED       # misaligned
+    assert bidir_fwd_ckpt(ck_bytes=1024) == ssm.SSM_ERR_WORKSPACE         # too small
+    assert bidir_fwd_ckpt(ck=P[15]) == ssm.SSM_ERR_ALIAS                  # on top of g0
+    assert bidir_fwd_ckpt(ck=P[8] + 256) == ssm.SSM_ERR_ALIAS             # inside g_first
+    none = dict(x=None, delta=None, B=None, C=None, D=None, y=None, h=None, g=None, h0=None, g0=None, ck=None)
+    assert bidir_fwd_ckpt(**dict(none, Bs=0, ED=0)) == ssm.SSM_OK         # nothing to scan: no checkpoints
+
+
+def bidir_bwd_ckpt(**kw):
+    args = dict(BWD_DEFAULT)
+    args.update(opts=None, Bs=2, L=64, ED=64, N=16, dtype=ssm.SSM_BF16, ck=P[24])
+    args["ws_bytes"] = ssm.ssm_scan_bidir_bwd_workspace_bytes(2, 64, 64, 16, ssm.SSM_BF16)
+    args["ck_bytes"] = ssm.lib().ssm_scan_ckpt_bytes(2, 64, 64, 16)
+    args.update(kw)
+    head = [args[n] for n in BIDIR_BWD_ORDER[:12]]
+    tail = [args[n] for n in BIDIR_BWD_ORDER[12:]]
+    return ssm.lib().ssm_scan_bidir_bwd_ckpt(*head, args["ck"], args["ck_bytes"], *tail, args["Bs"], args["L"],
+                                             args["ED"], args["N"], args["dtype"], args["ws"], args["ws_bytes"], None)
+
+
+def test_bidir_backward_checkpoint_validation():
+    assert BIDIR_BWD_ORDER[11] == "dg_first" and BIDIR_BWD_ORDER[12] == "dx"
+    assert bidir_bwd_ckpt(ck=None) == ssm.SSM_ERR_NULL
+    assert bidir_bwd_ckpt(ck=P[24] + 4) == ssm.SSM_ERR_UNSUPPORTED       # misaligned
+    assert bidir_bwd_ckpt(ck_bytes=64) == ssm.SSM_ERR_WORKSPACE          # too small
+    assert bidir_bwd_ckpt(ck=P[9]) == ssm.SSM_ERR_ALIAS                  # dx on top of the checkpoints
+    assert bidir_bwd_ckpt(ck=P[22]) == ssm.SSM_ERR_ALIAS                 # dg0 on top of them
+    assert bidir_bwd_ckpt(ck=P[18]) == ssm.SSM_ERR_ALIAS                 # the workspace on top of them
+    none = {n: None for n in BWD_PTRS}
+    assert bidir_bwd_ckpt(**dict(none, ck=None, Bs=0, ED=0, ws_bytes=0)) == ssm.SSM_OK
+
+
+def test_binding_checks_bidir_checkpoint_tensors():
+    import torch
+    x = torch.zeros(2, 40, 20)
+    d, B, C = torch.zeros(2, 40, 20), torch.zeros(2, 40, 16), torch.zeros(2, 40, 16)
+    A = torch.zeros(20, 16)
+    with pytest.raises(ValueError, match="ckpt must have shape"):
+        ssm.ssm_scan_bidir_fwd(x, d, A, B, C, ckpt=torch.zeros(2, 2, 20, 16))
+    with pytest.raises(TypeError, match="ckpt must be torch.float32"):
+        ssm.ssm_scan_bidir_fwd(x, d, A, B, C, ckpt=torch.zeros(2, 2, 32, 16, dtype=torch.float64))
+    with pytest.raises(TypeError):
+        ssm.ssm_scan_bidir_bwd(x, d, A, B, C, None, x, ckpt=torch.zeros(2, 2, 32, 16, dtype=torch.bfloat16))
