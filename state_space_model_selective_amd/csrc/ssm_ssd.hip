@@ -746,6 +746,9 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
                                                float Dfwd, float bias) {
   constexpr int KN = N / 32;  // products over n: instructions per 16 x 16 block
   constexpr bool rev = REV;
+  // the plain forward scan (no reverse partial, no gate): the compute waves
+  // store y straight from their accumulators (no Y tile, no store waves' work)
+  constexpr bool kDirectY = !BIDIR && !GATE && !REV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -882,8 +885,17 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         y[1] += Dh * bf_hi(xv.x);
         y[2] += Dh * bf_lo(xv.y);
         y[3] += Dh * bf_hi(xv.y);
+        if constexpr (kDirectY) {
+          // the plain scan stores its block itself: rows 4 lk + r of the
+          // wave's t-block, head channel pp, rounded once to bf16
+          const int64_t tb0 = c * kQ + 16 * nh + 4 * lk;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.Y[cur][16 * nh + 4 * lk + r][pp] = y[r];
+          for (int r = 0; r < 4; ++r)
+            if (tb0 + r < p.L) p.y[((b * p.L + tb0 + r) * p.H + h) * kP + pp] = bf16_bits(y[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.Y[cur][16 * nh + 4 * lk + r][pp] = y[r];
+        }
       }
       __syncthreads();
     }
@@ -988,7 +1000,7 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
         // ---- phase 1: the chunk's M; y of the previous chunk ----
         if (!AGG) causal_block(cur);
-        if (!AGG && c > c0) store_y_bf16<GATE>(p, sm.Y[nxt], stt, b, h, t0 - kQ, rev, pv_prev, zr_prev);
+        if (!AGG && !kDirectY && c > c0) store_y_bf16<GATE>(p, sm.Y[nxt], stt, b, h, t0 - kQ, rev, pv_prev, zr_prev);
         if (BIDIR && !rev) {
           for (int i = 0; i < 4; ++i) pv_prev[i] = pv[i];
           if (c + 1 < c1)
@@ -1002,7 +1014,8 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         __syncthreads();
         __syncthreads();
       }
-      if (!AGG) store_y_bf16<GATE>(p, sm.Y[(c1 - 1 - c0) & 1], stt, b, h, (c1 - 1) * kQ, rev, pv_prev, zr_prev);
+      if (!AGG && !kDirectY)
+        store_y_bf16<GATE>(p, sm.Y[(c1 - 1 - c0) & 1], stt, b, h, (c1 - 1) * kQ, rev, pv_prev, zr_prev);
     }
   }
 }
