@@ -511,27 +511,28 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_fwd_kernel(const SsdArgs<T> p
 // + 4..7 are together the operand B of a product over n with C[t][32 g ..]
 // read as usual, so the state never leaves the registers.
 //
-// Twelve waves: eight compute waves own the state and the output blocks and
-// run only products; four staging waves move data and form each chunk's
-// masked C B^T, so that this work overlaps the products instead of adding to
-// them. Two of the staging waves only load and commit tiles
-// (16-byte global loads into registers in phase 1, committed in phase 2),
-// the other two only store y; a wave that waits for its loads then has no
-// stores outstanding (stores count in the same counter). Per chunk, two
-// barriers:
+// Twelve waves: eight compute waves own the state and the output blocks,
+// run the products and store the output; four staging waves move data and
+// form each chunk's masked C B^T, so that this work overlaps the products
+// instead of adding to them. Two of the staging waves load and commit tiles
+// (16-byte global loads into registers in phase 1, committed in phase 2);
+// they issue no stores, so their waits for loads never wait for stores
+// (both count in the same counter). Per chunk, two barriers:
 //   phase 1  compute waves: diag(e^{cs}) C S_in^T over the wave's half of
 //            the states for both 16-step blocks (one goes to LDS for the
 //            wave that owns it), and the update of the wave's state tiles,
 //            S^T = e^{cs_end} S^T + B^T (w X) (so that a lane holds 4
-//            consecutive n of one p).
+//            consecutive n of one p); loads of what the output adds (the
+//            reverse partial, the gate).
 //            Staging waves: the chunk's three causal 16 x 16 blocks of C B^T
 //            (computed as B C^T so that a lane holds 4 consecutive s of one
-//            t) -> masked, decayed M (bf16 pair); store y of the previous
-//            chunk; issue the loads of the next chunk
+//            t) -> masked, decayed M (bf16 pair); issue the loads of the
+//            next chunk
 //   phase 2  compute waves: the other half's C S_in^T block, M X, + D x
-//            -> Y (float32, by chunk parity). Loading waves: commit the next
-//            chunk's tiles and form its decays (the last loading wave: a
-//            prefix sum over the lanes (DPP) of the step sizes it loaded)
+//            -> y (or the reverse sweep's float32 partial), stored from the
+//            registers. Loading waves: commit the next chunk's tiles and form
+//            its decays (the last loading wave: a prefix sum over the lanes
+//            (DPP) of the step sizes it loaded)
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -586,7 +587,6 @@ struct alignas(16) SsdSmemBf {
   uint16_t B[2][kQ][NP];   // B chunk [s][n]
   uint16_t X[2][kQ][XP];   // x chunk [s][p]
   uint16_t M[2][2][kQ][TP];  // masked, decayed C B^T [t][s] by chunk parity: high, low part
-  float Y[2][kQ][kP + 4];  // y of a chunk (with D x), by chunk parity
   // the inter-chunk output block (t-block, p-block) over one half of the
   // states, [p][t] within the block, from the wave that does not own it
   float Yx[2][4][16][24];
@@ -704,40 +704,6 @@ __device__ __forceinline__ void chunk_decay(SsdSmemBf<N>& sm, int buf, float Ah,
   }
 }
 
-// rows t0 .. t0 + kQ - 1 of the sweep (those before L) by the 128 threads
-// of the store waves, rows st / 16 + 8 i (i < 4), 4 head channels each: y
-// (+ the reverse partial pv), times the gate -> y, or, in the reverse sweep,
-// the float32 partial -> part
-template <bool GATE>
-__device__ __forceinline__ void store_y_bf16(const SsdArgs<uint16_t>& p, const float (&Y)[kQ][kP + 4], int st,
-                                             int64_t b, int64_t h, int64_t t0, bool rev, const float4 (&pv)[4],
-                                             const uint2 (&zr)[4]) {
-  const int c4 = (st & 15) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = (st >> 4) + 8 * i;
-    if (t0 + t < p.L) {
-      const float4 v = *reinterpret_cast<const float4*>(&Y[t][c4]);
-      const int64_t row = (b * p.L + sweep_time(t0 + t, p.L, rev)) * p.H + h;
-      if (rev)
-        *reinterpret_cast<float4*>(p.part + row * kP + c4) = v;
-      else {
-        float4 o = make_float4(v.x + pv[i].x, v.y + pv[i].y, v.z + pv[i].z, v.w + pv[i].w);
-        if (GATE) o = gated(o, Vec4<uint16_t>::widen(zr[i]));
-        *reinterpret_cast<uint2*>(p.y + row * kP + c4) = make_uint2(pack_bf16(o.x, o.y), pack_bf16(o.z, o.w));
-      }
-    }
-  }
-}
-
-// the reverse partial of sweep row t0 + st / 16 for a store thread
-__device__ __forceinline__ float4 load_partial(const SsdArgs<uint16_t>& p, int st, int64_t b, int64_t h,
-                                               int64_t t0) {
-  const int t = st >> 4, c4 = (st & 15) * 4;
-  if (t0 + t >= p.L) return make_float4(0.f, 0.f, 0.f, 0.f);
-  return *reinterpret_cast<const float4*>(p.part + ((b * p.L + t0 + t) * p.H + h) * kP + c4);
-}
-
 // One sweep of the bf16 kernel over the chunks [blk.c0, blk.c1) of a
 // (batch row, head): REV runs in decreasing time (chunk k of the sweep holds
 // times L-1-32k .. L-32-32k) from g0, else in increasing time from h0.
@@ -746,9 +712,6 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
                                                float Dfwd, float bias) {
   constexpr int KN = N / 32;  // products over n: instructions per 16 x 16 block
   constexpr bool rev = REV;
-  // the plain forward scan (no reverse partial, no gate): the compute waves
-  // store y straight from their accumulators (no Y tile, no store waves' work)
-  constexpr bool kDirectY = !BIDIR && !GATE && !REV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -794,12 +757,38 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
       }
     }
     double cs_sum = 0.0;  // AGG: A times the range's sum of step sizes (thread 0)
+    // what the output of chunk cc adds (the reverse partial, the gate of the
+    // lane's rows), into pvn / zn
+    float pvn[4] = {0.f, 0.f, 0.f, 0.f}, zn[4] = {0.f, 0.f, 0.f, 0.f};
+    auto load_adds = [&](int64_t cc) {
+      if constexpr (!AGG && !REV && (BIDIR || GATE)) {
+        const int64_t t = cc * kQ + 16 * nh + 4 * lk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t + r < p.L) {
+            const int64_t o = ((b * p.L + t + r) * p.H + h) * kP + pp;
+            if (BIDIR) pvn[r] = p.part[o];
+            if (GATE) zn[r] = to_f32(p.z[o]);
+          }
+      }
+    };
+    load_adds(c0);
     __syncthreads();
 
     for (int64_t c = c0; c < c1; ++c) {
       const int cur = (c - c0) & 1;
       // ---- phase 1 ----
       if (AGG && tid == 0) cs_sum += static_cast<double>(sm.cs_end[cur]);
+
+      // the lane's 4 output rows: sweep rows tau0 .. tau0 + 3 (those before L),
+      // head channel pp. The forward sweep of the bidirectional scan adds the
+      // reverse sweep's partial of those rows and the gated form multiplies
+      // by silu(z): both are loaded a chunk ahead of their use
+      const int64_t tau0 = c * kQ + 16 * nh + 4 * lk;
+      float pvv[4], zv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pvv[r] = pvn[r], zv[r] = zn[r];
+      if (c + 1 < c1) load_adds(c + 1);
 
       // inter-chunk output over this half of the states, both t-blocks:
       // diag(e^{cs}) C S_in^T; the partner wave (pb, 1 - nh) gets the block
@@ -885,17 +874,21 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         y[1] += Dh * bf_hi(xv.x);
         y[2] += Dh * bf_lo(xv.y);
         y[3] += Dh * bf_hi(xv.y);
-        if constexpr (kDirectY) {
-          // the plain scan stores its block itself: rows 4 lk + r of the
-          // wave's t-block, head channel pp, rounded once to bf16
-          const int64_t tb0 = c * kQ + 16 * nh + 4 * lk;
+        // the wave stores its block itself: the reverse sweep its float32
+        // partial, the forward sweep y (+ the partial, times the gate) rounded
+        // once to bf16
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (tb0 + r < p.L) p.y[((b * p.L + tb0 + r) * p.H + h) * kP + pp] = bf16_bits(y[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.Y[cur][16 * nh + 4 * lk + r][pp] = y[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (tau0 + r < p.L) {
+            const int64_t o = ((b * p.L + sweep_time(tau0 + r, p.L, rev)) * p.H + h) * kP + pp;
+            if (rev) {
+              p.part[o] = y[r];
+            } else {
+              float v = y[r] + pvv[r];
+              if (GATE) v *= silu(zv[r]);
+              p.y[o] = bf16_bits(v);
+            }
+          }
       }
       __syncthreads();
     }
@@ -918,14 +911,13 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
     }
   } else {
     // ================= staging waves =================
-    // Waves 0, 1 of them store y (and load what the stores add: the reverse
-    // partial, the gate); waves 2, 3 load and commit the chunks' tiles; a
-    // wave that waits for loads has no stores outstanding. Waves 0..2 also
-    // form the causal C B^T blocks, the last the decays.
+    // Waves 0..2 of them form the causal C B^T blocks; waves 2, 3 load and
+    // commit the chunks' tiles, the last also forms the decays. (The compute
+    // waves store the output, so no wave that waits for loads has stores
+    // outstanding: stores count in the same wait counter.)
     const int sw = wave - kMainBf;                 // staging wave 0 .. kStageBf-1
     const bool loader = sw >= 2;
     const int lt = tid - 64 * (kMainBf + 2);       // loading thread 0 .. 127
-    const int stt = tid - 64 * kMainBf;            // store thread 0 .. 127
     const int mtb = sw == 0 ? 0 : 1, msb = sw == 2 ? 1 : 0;  // causal C B^T block of staging waves 0..2
 
     // causal block of C B^T of chunk buffer buf, masked and decayed: M[t][s]
@@ -980,42 +972,14 @@ __device__ __forceinline__ void ssd_bf16_sweep(const SsdArgs<uint16_t>& p, SsdSm
         __syncthreads();
       }
     } else {
-      // forward sweep of the bidirectional scan: the reverse partial of the
-      // chunk whose output is stored next, one chunk ahead of its store; the
-      // gate of those rows the same way (forward sweep only)
-      float4 pv[4], pv_prev[4];
-      uint2 zr[4], zr_prev[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = pv_prev[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        zr[i] = zr_prev[i] = make_uint2(0u, 0u);
-      }
-      if (BIDIR && !rev)
-        for (int i = 0; i < 4; ++i) pv[i] = load_partial(p, stt, b, h, c0 * kQ + 8 * i);
-      if (GATE && !rev)
-        for (int i = 0; i < 4; ++i) zr[i] = load_gate(p, stt, b, h, c0 * kQ + 8 * i);
       __syncthreads();
       for (int64_t c = c0; c < c1; ++c) {
-        const int cur = (c - c0) & 1, nxt = cur ^ 1;
-        const int64_t t0 = c * kQ;  // first step of the chunk in the sweep's order
-        // ---- phase 1: the chunk's M; y of the previous chunk ----
+        const int cur = (c - c0) & 1;
+        // ---- phase 1: the chunk's M ----
         if (!AGG) causal_block(cur);
-        if (!AGG && !kDirectY && c > c0) store_y_bf16<GATE>(p, sm.Y[nxt], stt, b, h, t0 - kQ, rev, pv_prev, zr_prev);
-        if (BIDIR && !rev) {
-          for (int i = 0; i < 4; ++i) pv_prev[i] = pv[i];
-          if (c + 1 < c1)
-            for (int i = 0; i < 4; ++i) pv[i] = load_partial(p, stt, b, h, t0 + kQ + 8 * i);
-        }
-        if (GATE && !rev) {
-          for (int i = 0; i < 4; ++i) zr_prev[i] = zr[i];
-          if (c + 1 < c1)
-            for (int i = 0; i < 4; ++i) zr[i] = load_gate(p, stt, b, h, t0 + kQ + 8 * i);
-        }
         __syncthreads();
         __syncthreads();
       }
-      if (!AGG && !kDirectY)
-        store_y_bf16<GATE>(p, sm.Y[(c1 - 1 - c0) & 1], stt, b, h, (c1 - 1) * kQ, rev, pv_prev, zr_prev);
     }
   }
 }
