@@ -183,3 +183,36 @@ def test_multi_head_split_sequence_graph(bidir):
     fn = ssm.ssm_ssd_bidir_fwd if bidir else ssm.ssm_ssd_fwd
     replay_check("multi-head split sequence, bidir=%s" % bidir, lambda: fn(
         t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], y=y, h_last=h, workspace=ws), [y, h])
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_training_step_pair_graph(bidir):
+    """The forward that keeps the round states and the backward that reads
+    them, captured together (split sequences, so the forward's workspace
+    clear and the backward's aggregate pass are in the graph too)."""
+    import torch
+    import state_space_model_selective_amd as ssm
+    Bs, L, ED, N = 1, 8192, 64, 16
+    dev = torch.device("cuda:0")
+    t = to_device(synth.make_inputs(Bs, L, ED, N, "f32", seed=72), dev)
+    dy = to_device(dict(dy=synth.make_output_grad(Bs, L, ED, "f32", seed=72)), dev)["dy"]
+    y = torch.empty_like(t["x"])
+    ck = torch.empty(ssm.ssm_scan_ckpt_shape(Bs, L, ED), dtype=torch.float32, device=dev)
+    fneed = ssm.ssm_scan_workspace_bytes(Bs, L, ED, N, ssm.SSM_F32, bidir)
+    fws = torch.empty(max(fneed, 1), dtype=torch.uint8, device=dev) if fneed else None
+    bneed = (ssm.ssm_scan_bidir_bwd_workspace_bytes if bidir else ssm.ssm_scan_bwd_workspace_bytes)(
+        Bs, L, ED, N, ssm.SSM_F32)
+    bws = torch.empty(bneed, dtype=torch.uint8, device=dev)
+    out = {k: torch.empty_like(v) for k, v in (("dx", t["x"]), ("ddelta", t["x"]), ("dA", t["A"]), ("dB", t["B"]),
+                                               ("dC", t["C"]))}
+    out["dD"] = torch.empty((ED,), dtype=torch.float32, device=dev)
+    args = (t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"])
+    fwd = ssm.ssm_scan_bidir_fwd if bidir else ssm.ssm_scan_fwd
+    bwd = ssm.ssm_scan_bidir_bwd if bidir else ssm.ssm_scan_bwd
+
+    def step():
+        fwd(*args, y=y, workspace=fws, ckpt=ck)
+        bwd(*args, dy, out=out, workspace=bws, ckpt=ck)
+
+    # (the checkpoints are an intermediate: their round 0 is never written)
+    replay_check("training step, bidir=%s" % bidir, step, [y] + [out[k] for k in sorted(out)])
