@@ -816,8 +816,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const int per = (ngroups + 3) / 4;
   const int g0 = quarter * per, g1 = min(ngroups, g0 + per);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (ok) {
+  // the groups in order either way; more loads in flight pay off only for
+  // long quarters
+  if (ok && g1 - g0 >= 32) {
 #pragma unroll 16
+    for (int gi = g0; gi < g1; ++gi) {
+      const float4 v = src[gi * n4];
+      s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
+    }
+  } else if (ok) {
+#pragma unroll 8
     for (int gi = g0; gi < g1; ++gi) {
       const float4 v = src[gi * n4];
       s = make_float4(s.x + v.x, s.y + v.y, s.z + v.z, s.w + v.w);
