@@ -13,11 +13,11 @@
 // inside the chunk and S_in the state entering it,
 //   Y   = M X + diag(e^{cs}) C S_in^T,     M[t][s] = (C_t . B_s) e^{cs_t - cs_s} dt_s  (s <= t)
 //   S_out = e^{cs_end} S_in + sum_s X_s^T (e^{cs_end - cs_s} dt_s) B_s
-// which the matrix cores compute. One workgroup of 8 waves owns one (batch
-// row, head), keeps the head's 64 x N state on chip for the whole sequence
-// (registers for the update, an LDS copy for the output product) and walks
-// the chunks in order; the next chunk's inputs are loaded into registers
-// while the current one is computed (double-buffered LDS tiles).
+// which the matrix cores compute. One workgroup owns one (batch row, head),
+// keeps the head's 64 x N state in matrix-core accumulators for the whole
+// sequence (the accumulators are also the operand of the output product)
+// and walks the chunks in order; the next chunk's inputs are loaded into
+// registers while the current one is computed (double-buffered LDS tiles).
 //
 // Two kernels: float32 inputs (ssd_fwd_kernel, below) on
 // v_mfma_f32_16x16x4f32 with float32 operands and accumulation; bfloat16
